@@ -1,0 +1,332 @@
+"""Benchmark of libgemm355 on one MI355X: TFLOP/s = 2MNK/t of C = alpha*A@B + beta*C.
+
+One "step" is one library call over the whole path (for f16r: the operand
+rounding passes and the GEMM).  The headline workload is the f32 GEMM at
+M = N = K = 4096 (alpha 1, beta 0); the line also carries the beta = 1 run and
+the f16r GEMM at 8192^3 (alpha 0.75, beta -0.25), each with its fraction of the
+matrix-core roof re-measured on this chip (the Matrix Multiplication lab,
+"Part 1 -- the two roofs, again"), and the CPU oracle timed on host cores.
+
+Protocol (the lab's helpers): every result is checked against the oracle before
+it is timed; clocks are settled with synchronised calls for a quarter second;
+then exactly --steps calls are timed between two device synchronisations, with
+an event pair around every call on the stream the library launches on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--workloads a,b,...] [--no-tune] [--json-out path]
+Prints progress on stderr and ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s (2MNK/t) at 4096^3 f32 and 8192^3 f16r/f32acc; % of MFMA peak"
+PRIMARY = "f32_4096_a1_b0"
+SCORED = ["f32_4096_a1_b0", "f32_4096_a1_b1", "f16r_8192_a0.75_b-0.25"]
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
+PEAK_TFLOPS = {"f32": 157.3, "f16r": 2500.0}
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workloads", default=",".join(SCORED))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tune", action="store_true")
+    ap.add_argument("--no-roofs", action="store_true")
+    ap.add_argument("--roof-seconds", type=float, default=2.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--json-out", default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gemm_tiled_amd as g
+    from workloads import WORKLOADS, sample_indices, workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), "
+        f"{props.multi_processor_count} CUs; libgemm355 {g.version()}")
+
+    # ------------------------------------------------------------------ roofs
+    roofs = {}
+    if not args.no_roofs:
+        roofs = measure_roofs(g, torch, dev, args.roof_seconds)
+        log(f"measured roofs: {json.dumps(roofs)}")
+
+    # -------------------------------------------------------------- workloads
+    names = [n for n in args.workloads.split(",") if n]
+    runs = {}
+    for name in names:
+        w = WORKLOADS[name]
+        runs[name] = bench_workload(g, torch, dev, w, args, roofs, workload_inputs,
+                                    sample_indices)
+
+    primary = PRIMARY if PRIMARY in runs else names[0]
+    pr = runs[primary]
+    w = WORKLOADS[primary]
+
+    # --------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds, workload_inputs)
+
+    line = {
+        "metric": METRIC,
+        "value": pr["tflops_job"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pr["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.mode == "f32" else "f16r/f32acc",
+        "data": "synthetic (seeded uniform/normal matrices; no dataset)",
+        "config": {"workload": primary, "mode": w.mode, "M": w.M, "N": w.N, "K": w.K,
+                   "alpha": w.alpha, "beta": w.beta, "tile": pr["tile"]},
+        "roofline": pr["roofline"],
+        "cpu_baseline": cpu,
+        "measured_roof": roofs or None,
+        "frac_of_measured_roof": pr.get("frac_of_measured_roof"),
+        "workloads": runs,
+    }
+    text = json.dumps(line)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(text + "\n")
+    print(text, flush=True)
+
+
+def measure_roofs(g, torch, dev, seconds):
+    import ctypes
+
+    L = g.lib()
+    out = {}
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    blocks = 256 * 4   # four workgroups of four waves per CU
+    sink = torch.empty(blocks * 256, device=dev, dtype=torch.float32)
+    for mode, name in ((0, "f32"), (1, "f16r")):
+        iters = 2000 if mode == 0 else 4000
+        flops = ctypes.c_double(0)
+
+        def launch():
+            st = L.gemm355_roof_mfma(mode, iters, blocks, ctypes.c_void_p(sink.data_ptr()),
+                                     ctypes.byref(flops), sp)
+            if st != 0:
+                raise g.Gemm355Error(st, "gemm355_roof_mfma")
+
+        launch()
+        torch.cuda.synchronize()
+        # sustained: back-to-back launches for `seconds`, synchronising every 4 calls
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            launch()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+        e_ev.record()
+        e_ev.synchronize()
+        t = s_ev.elapsed_time(e_ev) / 1e3 / n
+        out[f"mfma_{name}_tflops"] = flops.value / t / 1e12
+        out[f"mfma_{name}_published_tflops"] = PEAK_TFLOPS[name]
+    # HBM read roof: 4 GiB, beyond the 256 MB last-level cache
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, device=dev, dtype=torch.float32)
+    sink1 = torch.zeros(1, device=dev, dtype=torch.float32)
+
+    def read():
+        st = L.gemm355_roof_hbm(ctypes.c_void_p(buf.data_ptr()), nbytes, 256 * 8,
+                                ctypes.c_void_p(sink1.data_ptr()), sp)
+        if st != 0:
+            raise g.Gemm355Error(st, "gemm355_roof_hbm")
+
+    t = steady(read, torch, 0.5)
+    out["hbm_read_gbs"] = nbytes / t / 1e9
+    out["hbm_published_gbs"] = PEAK_HBM_GBS
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
+def steady(fn, torch, seconds=0.5, min_calls=3):
+    """Median seconds per call after settling (the lab's steady())."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds / 2:
+        fn()
+        torch.cuda.synchronize()
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts, t0 = [], time.perf_counter()
+    while time.perf_counter() - t0 < seconds or len(ts) < min_calls:
+        s_ev.record()
+        fn()
+        e_ev.record()
+        e_ev.synchronize()
+        ts.append(s_ev.elapsed_time(e_ev) / 1e3)
+    return float(np.median(ts))
+
+
+def bench_workload(g, torch, dev, w, args, roofs, workload_inputs, sample_indices):
+    import oracle   # correctness check before timing (CPU, test infrastructure)
+
+    log(f"{w.name}: generating inputs")
+    A, B, C = workload_inputs(w)
+    tA = torch.from_numpy(A).to(dev)
+    tB = torch.from_numpy(B).to(dev)
+    tC0 = torch.from_numpy(C).to(dev)
+    tC = tC0.clone()
+    fn = g.gemm_f32 if w.mode == "f32" else g.gemm_f16r_f32acc
+
+    if not args.no_tune:
+        log(f"{w.name}: tuning")
+        g.tune(w.mode, tA, tB, tC, beta=w.beta)
+    tile = g.get_config(w.mode, w.M, w.N, w.K, beta=w.beta)
+    log(f"{w.name}: tile {tile}")
+
+    # correctness first: one call on a fresh C, sampled oracle elements
+    fn(tA, tB, tC, w.alpha, w.beta)
+    torch.cuda.synchronize()
+    got = tC.cpu().numpy()
+    r, c = sample_indices(w.M, w.N, 2048, seed=1)
+    ref, W = oracle.entries(w.mode, A, B, C, w.alpha, w.beta, r, c)
+    err = np.abs(got[r, c].astype(np.float64) - ref)
+    ratio = float(np.max(err / np.where(W > 0, W, 1.0)))
+    ok = bool(np.all(err <= oracle.TOL[w.mode] * W))
+    log(f"{w.name}: parity on {r.size} sampled elements: max err/W {ratio:.3e} "
+        f"(bound {oracle.TOL[w.mode]:.0e}) -> {'ok' if ok else 'FAIL'}")
+    if not ok:
+        raise SystemExit(f"{w.name}: result outside the parity bound; not timing it")
+    del got
+
+    stream = torch.cuda.current_stream()
+    call = lambda: fn(tA, tB, tC, w.alpha, w.beta)   # noqa: E731  (C drifts; timing is data-independent)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    # settle the clocks (synchronised calls, a quarter second)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.25:
+        call()
+        torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ev, e_ev in evs:
+        s_ev.record(stream)
+        call()
+        e_ev.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([s.elapsed_time(e) / 1e3 for s, e in evs])
+    gpu_total = float(per.sum())
+
+    flops = w.flops
+    tflops_job = flops * args.steps / wall / 1e12
+    tflops_med = flops / float(np.median(per)) / 1e12
+    avg = float(per.mean())
+    achieved = flops / avg / 1e12
+    peak = PEAK_TFLOPS[w.mode]
+    roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "kernel": "gemm_f32_kernel" if w.mode == "f32" else
+            "round_a + round_bt + gemm_f16_kernel (whole call)",
+            "per_launch_flops": flops}
+    res = {
+        "mode": w.mode, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
+        "tile": tile,
+        "ms_per_step": wall / args.steps * 1e3,
+        "ms_median_call": float(np.median(per)) * 1e3,
+        "ms_mean_call": avg * 1e3,
+        "gpu_busy_frac": gpu_total / wall,
+        "tflops_job": tflops_job,
+        "tflops_median_call": tflops_med,
+        "parity_max_ratio_sampled": ratio,
+        "roofline": roof,
+    }
+    key = "mfma_f32_tflops" if w.mode == "f32" else "mfma_f16r_tflops"
+    if roofs.get(key):
+        res["frac_of_measured_roof"] = round(tflops_med / roofs[key], 4)
+    log(f"{w.name}: {tflops_job:.2f} TFLOP/s over {args.steps} steps "
+        f"({res['ms_per_step']:.4f} ms/step, median call {res['ms_median_call']:.4f} ms, "
+        f"{tflops_med:.2f} TFLOP/s median); frac of published peak {roof['frac']:.3f}"
+        + (f", of measured roof {res['frac_of_measured_roof']:.3f}" if "frac_of_measured_roof" in res
+           else ""))
+    del tA, tB, tC, tC0
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, target_seconds, workload_inputs):
+    """The oracle as it stands, on a band of output rows of the same workload,
+    sized to about target_seconds of CPU time; throughput in TFLOP/s."""
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    os.environ["OMP_NUM_THREADS"] = str(threads)
+    A, B, C = workload_inputs(w)
+    probe = 16
+    t0 = time.perf_counter()
+    oracle.check(w.mode, A, B, C, w.alpha, w.beta, C, rows=(0, probe))
+    t_probe = time.perf_counter() - t0
+    rows = int(min(w.M, max(probe, probe * target_seconds / max(t_probe, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.check(w.mode, A, B, C, w.alpha, w.beta, C, rows=(0, rows))
+    t = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    res = {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{rows} of {w.M} output rows of {w.name} (float64 triple loop incl. "
+                     f"operand widening), {t:.1f} s", "cpu": cpu_model}
+    log(f"cpu baseline: {res['value'] * 1e3:.2f} GFLOP/s on {threads} threads ({res['sample']})")
+    return res
+
+
+if __name__ == "__main__":
+    main()

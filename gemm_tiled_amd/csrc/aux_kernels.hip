@@ -1,0 +1,133 @@
+// aux_kernels.hip -- the beta-only update and the measurement kernels.
+#include "internal.hpp"
+
+namespace g355 {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// C = beta*C, or C = 0 when beta == 0 (C is then not read).  One thread per
+// element of a row segment; rows are independent, so a 2-D grid walks them.
+__global__ __launch_bounds__(256) void scale_c_kernel(float* __restrict__ C, int64_t ldc, int M,
+                                                      int N, float beta) {
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= N) return;
+    for (int row = blockIdx.y; row < M; row += gridDim.y) {
+        float* c = C + (int64_t)row * ldc + col;
+        *c = (beta == 0.f) ? 0.f : beta * *c;
+    }
+}
+
+// Matrix-core roofs (the lab's "Part 1": a kernel of nothing but independent
+// multiply-adds).  Each wave keeps 8 independent accumulator blocks so the
+// matrix unit never waits on a previous result.
+__global__ __launch_bounds__(256) void roof_mfma_f32_kernel(int64_t iters, float* sink) {
+    const float a = 1e-3f * (threadIdx.x & 7), b = 1e-3f * (threadIdx.x >> 3);
+    f32x16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[i], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[i][e];
+    sink[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void roof_mfma_f16_kernel(int64_t iters, float* sink) {
+    f16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = static_cast<_Float16>(1e-3f * ((threadIdx.x + e) & 7));
+        b[e] = static_cast<_Float16>(1e-3f * ((threadIdx.x >> 3) + e));
+    }
+    f32x16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[i], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[i][e];
+    sink[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+// HBM read roof (the lab's streaming read): grid-stride 16-byte loads.
+__global__ __launch_bounds__(256) void roof_hbm_kernel(const float4* __restrict__ x, int64_t n4,
+                                                       float* sink) {
+    float acc = 0.f;
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        const float4 v = x[i];
+        acc += v.x + v.y + v.z + v.w;
+    }
+    if (acc == 1234.5f) sink[0] = acc;   // never true for the data used; keeps the loads
+}
+
+__global__ __launch_bounds__(256) void copy_f32_kernel(const float4* __restrict__ src,
+                                                       float4* __restrict__ dst, int64_t n4) {
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+        dst[i] = src[i];
+}
+
+__global__ void copy_tail_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                 int64_t from, int64_t n) {
+    const int64_t i = from + threadIdx.x;
+    if (i < n) dst[i] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_scale_c(float* C, int64_t ldc, int M, int N, float beta, hipStream_t s) {
+    const unsigned gx = static_cast<unsigned>((N + 255) / 256);
+    const unsigned gy = static_cast<unsigned>(M < 4096 ? M : 4096);
+    scale_c_kernel<<<dim3(gx, gy), 256, 0, s>>>(C, ldc, M, N, beta);
+    return hipGetLastError();
+}
+
+hipError_t launch_roof_mfma(int mode, int64_t iters, int blocks, float* sink, double* flops,
+                            hipStream_t s) {
+    const double waves = static_cast<double>(blocks) * 4.0;
+    if (mode == GEMM355_MODE_F32) {
+        roof_mfma_f32_kernel<<<blocks, 256, 0, s>>>(iters, sink);
+        *flops = waves * static_cast<double>(iters) * 8.0 * (2.0 * 32 * 32 * 2);
+    } else {
+        roof_mfma_f16_kernel<<<blocks, 256, 0, s>>>(iters, sink);
+        *flops = waves * static_cast<double>(iters) * 8.0 * (2.0 * 32 * 32 * 16);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_roof_hbm(const void* buf, int64_t bytes, int blocks, float* sink,
+                           hipStream_t s) {
+    roof_hbm_kernel<<<blocks, 256, 0, s>>>(static_cast<const float4*>(buf), bytes / 16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s) {
+    const int64_t n4 = n / 4;
+    if (n4 > 0) {
+        const int64_t want = (n4 + 255) / 256;
+        const int blocks = static_cast<int>(want < 16384 ? want : 16384);
+        copy_f32_kernel<<<blocks, 256, 0, s>>>(reinterpret_cast<const float4*>(src),
+                                               reinterpret_cast<float4*>(dst), n4);
+    }
+    if (n4 * 4 < n) copy_tail_kernel<<<1, 64, 0, s>>>(src, dst, n4 * 4, n);
+    return hipGetLastError();
+}
+
+}  // namespace g355

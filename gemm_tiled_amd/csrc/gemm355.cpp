@@ -1,0 +1,663 @@
+// gemm355.cpp -- host side of libgemm355: argument checks, the special
+// cases, tile selection (pin > tuned > heuristic), the f16r workspace, the
+// per-shape autotuner and its cache, and the exported C ABI.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cctype>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "gemm355.h"
+#include "internal.hpp"
+
+namespace g355 {
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1024;   // kernels index tiles with int
+
+// ---------------------------------------------------------------------------
+// Logging (GEMM355_LOG=debug prints every choice of tile and path).
+// ---------------------------------------------------------------------------
+bool log_debug() {
+    static const bool on = [] {
+        const char* v = std::getenv("GEMM355_LOG");
+        return v && (std::strcmp(v, "debug") == 0 || std::strcmp(v, "1") == 0);
+    }();
+    return on;
+}
+
+const char* mode_name(int mode) { return mode == GEMM355_MODE_F32 ? "f32" : "f16r"; }
+
+// ---------------------------------------------------------------------------
+// Instances and configuration strings.
+// ---------------------------------------------------------------------------
+std::vector<TileConfig> configs_of(int mode) {
+    std::vector<TileConfig> out;
+    int n = 0;
+    if (mode == GEMM355_MODE_F32) {
+        const F32Instance* t = f32_instances(&n);
+        for (int i = 0; i < n; ++i) out.push_back(t[i].cfg);
+    } else {
+        const F16Instance* t = f16_instances(&n);
+        for (int i = 0; i < n; ++i) out.push_back(t[i].cfg);
+    }
+    return out;
+}
+
+std::string format_config(const TileConfig& c) {
+    char b[128];
+    std::snprintf(b, sizeof b, "BM=%d BN=%d BK=%d WM=%d WN=%d GM=%d", c.bm, c.bn, c.bk, c.wm,
+                  c.wn, c.gm);
+    return b;
+}
+
+// Parse "KEY=VALUE ..." into the first compiled instance matching every given
+// key.  Returns false on a syntax error, an unknown key or no match.
+bool parse_config(int mode, const char* spec, TileConfig* out) {
+    int want[6] = {-1, -1, -1, -1, -1, -1};   // bm bn bk wm wn gm
+    const char* p = spec;
+    bool any = false;
+    while (*p) {
+        while (*p && std::isspace(static_cast<unsigned char>(*p))) ++p;
+        if (!*p) break;
+        const char* k0 = p;
+        while (*p && *p != '=' && !std::isspace(static_cast<unsigned char>(*p))) ++p;
+        if (*p != '=') return false;
+        std::string key(k0, p - k0);
+        ++p;
+        char* end = nullptr;
+        const long v = std::strtol(p, &end, 10);
+        if (end == p || v <= 0 || v > 4096) return false;
+        if (*end && !std::isspace(static_cast<unsigned char>(*end))) return false;
+        p = end;
+        for (auto& ch : key) ch = static_cast<char>(std::toupper(static_cast<unsigned char>(ch)));
+        int slot = -1;
+        if (key == "BM" || key == "TILE_M") slot = 0;
+        else if (key == "BN" || key == "TILE_N") slot = 1;
+        else if (key == "BK" || key == "TILE_K") slot = 2;
+        else if (key == "WM") slot = 3;
+        else if (key == "WN") slot = 4;
+        else if (key == "GM") slot = 5;
+        if (slot < 0) return false;
+        want[slot] = static_cast<int>(v);
+        any = true;
+    }
+    if (!any) return false;
+    for (const TileConfig& c : configs_of(mode)) {
+        const int have[6] = {c.bm, c.bn, c.bk, c.wm, c.wn, c.gm};
+        bool ok = true;
+        for (int i = 0; i < 6; ++i)
+            if (want[i] >= 0 && want[i] != have[i]) ok = false;
+        if (ok) {
+            *out = c;
+            return true;
+        }
+    }
+    return false;
+}
+
+// ---------------------------------------------------------------------------
+// Pins, tuned cache.
+// ---------------------------------------------------------------------------
+struct Key {
+    int mode;
+    int64_t M, N, K;
+    int vec_a, vec_b, beta0;
+    bool operator<(const Key& o) const {
+        return std::tie(mode, M, N, K, vec_a, vec_b, beta0) <
+               std::tie(o.mode, o.M, o.N, o.K, o.vec_a, o.vec_b, o.beta0);
+    }
+};
+
+struct State {
+    std::mutex mu;
+    bool env_read = false;
+    bool pin_set[2] = {false, false};
+    bool pin_bad[2] = {false, false};   // an invalid pin from the environment
+    TileConfig pin[2];
+    std::map<Key, TileConfig> cache;
+    std::string cache_path;
+};
+
+State& state() {
+    static State s;
+    return s;
+}
+
+size_t load_cache_locked(State& st, const char* path);
+
+void read_env_locked(State& st) {
+    if (st.env_read) return;
+    st.env_read = true;
+    const char* names[2] = {"GEMM355_CONFIG_F32", "GEMM355_CONFIG_F16R"};
+    for (int m = 0; m < 2; ++m) {
+        const char* v = std::getenv(names[m]);
+        if (!v || !*v) continue;
+        TileConfig c;
+        if (parse_config(m, v, &c)) {
+            st.pin[m] = c;
+            st.pin_set[m] = true;
+        } else {
+            st.pin_bad[m] = true;
+            std::fprintf(stderr, "[gemm355] %s=\"%s\" names no compiled configuration\n",
+                         names[m], v);
+        }
+    }
+    const char* path = std::getenv("GEMM355_TUNE_CACHE");
+    if (path && *path) {
+        st.cache_path = path;
+        load_cache_locked(st, path);
+    }
+}
+
+bool vec_ok(const float* p, int64_t ld) {
+    return (ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(p) & 15) == 0);
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Heuristic when nothing is pinned or tuned: estimate the time of each
+// instance as (rounds of workgroups over 256 CUs) x (work per tile) / (reuse
+// efficiency of the tile), the trade-off of the phobos "Tuning" section:
+// larger tiles reuse more, but leave fewer workgroups to fill the chip.
+TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K) {
+    const std::vector<TileConfig> all = configs_of(mode);
+    double best = 1e300;
+    TileConfig pick = all.front();
+    for (const TileConfig& c : all) {
+        const double tiles = static_cast<double>((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+        const double per_cu = (c.bm * c.bn >= 256 * 128) ? 1.0 : 2.0;
+        const double rounds = std::ceil(tiles / (256.0 * per_cu));
+        const double reuse = static_cast<double>(c.bm) * c.bn / (c.bm + c.bn);   // flop per loaded element
+        const double eff = reuse / (reuse + 24.0);
+        const double kpad = static_cast<double>(round_up(K, c.bk));
+        const double cost = rounds * per_cu * c.bm * c.bn * kpad / eff;
+        if (cost < best * 0.999) {
+            best = cost;
+            pick = c;
+        }
+    }
+    return pick;
+}
+
+enum class Source { Pin, Tuned, Heuristic };
+
+int select_config(int mode, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                  const float* B, int64_t ldb, float beta, TileConfig* out, Source* src) {
+    State& st = state();
+    std::lock_guard<std::mutex> lock(st.mu);
+    read_env_locked(st);
+    if (st.pin_bad[mode] && !st.pin_set[mode]) return GEMM355_ERR_CONFIG;
+    if (st.pin_set[mode]) {
+        *out = st.pin[mode];
+        *src = Source::Pin;
+        return 0;
+    }
+    const Key key{mode, M, N, K, vec_ok(A, lda), vec_ok(B, ldb), beta == 0.f};
+    auto it = st.cache.find(key);
+    if (it != st.cache.end()) {
+        *out = it->second;
+        *src = Source::Tuned;
+        return 0;
+    }
+    *out = heuristic(mode, M, N, K);
+    *src = Source::Heuristic;
+    return 0;
+}
+
+// ---------------------------------------------------------------------------
+// The f16r workspace: one device buffer per (device, stream), grown on demand.
+// Calls on one stream run in order, so they can share it.
+// ---------------------------------------------------------------------------
+struct WsKey {
+    int dev;
+    hipStream_t s;
+    bool operator<(const WsKey& o) const { return std::tie(dev, s) < std::tie(o.dev, o.s); }
+};
+struct Ws {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<WsKey, Ws> g_ws;
+
+hipError_t workspace(hipStream_t s, size_t bytes, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    Ws& w = g_ws[WsKey{dev, s}];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            // earlier work on this stream may still read the old buffer
+            e = hipStreamSynchronize(s);
+            if (e != hipSuccess) return e;
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        e = hipMalloc(&w.ptr, bytes);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return e;
+        }
+        w.bytes = bytes;
+    }
+    *out = w.ptr;
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Argument checks (BLAS xerbla numbering) and the dispatch of one call.
+// ---------------------------------------------------------------------------
+int check_args(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
+               const float* B, int64_t ldb, const float* C, int64_t ldc) {
+    if (M < 0 || M > kMaxDim) return -1;
+    if (N < 0 || N > kMaxDim) return -2;
+    if (K < 0 || K > kMaxDim) return -3;
+    const bool product = M > 0 && N > 0 && K > 0 && alpha != 0.f;
+    if (product && A == nullptr) return -5;
+    if (lda < std::max<int64_t>(1, K)) return -6;
+    if (product && B == nullptr) return -7;
+    if (ldb < std::max<int64_t>(1, N)) return -8;
+    if (M > 0 && N > 0 && C == nullptr) return -10;
+    if (ldc < std::max<int64_t>(1, N)) return -11;
+    return 0;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? 0 : static_cast<int>(e); }
+
+int launch_with(const TileConfig& cfg, int64_t M, int64_t N, int64_t K, float alpha,
+                const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                int64_t ldc, hipStream_t s) {
+    const int tiles_m = static_cast<int>((M + cfg.bm - 1) / cfg.bm);
+    const int tiles_n = static_cast<int>((N + cfg.bn - 1) / cfg.bn);
+    if (cfg.mode == GEMM355_MODE_F32) {
+        int n = 0;
+        const F32Instance* t = f32_instances(&n);
+        for (int i = 0; i < n; ++i) {
+            if (!(t[i].cfg == cfg)) continue;
+            F32Args a{A, B, C, lda, ldb, ldc, static_cast<int>(M), static_cast<int>(N),
+                      static_cast<int>(K), alpha, beta, tiles_m, tiles_n};
+            F32Variant v;
+            v.vec = vec_ok(A, lda) && vec_ok(B, ldb);
+            v.masked = !v.vec || (M % cfg.bm) || (N % cfg.bn) || (K % cfg.bk);
+            if (log_debug())
+                std::fprintf(stderr, "[gemm355] f32 M=%lld N=%lld K=%lld %s path=%s%s\n",
+                             (long long)M, (long long)N, (long long)K, format_config(cfg).c_str(),
+                             v.masked ? "masked" : "aligned", v.vec ? "" : " scalar-loads");
+            return status_of(t[i].launch(a, v, s));
+        }
+        return GEMM355_ERR_CONFIG;
+    }
+    int n = 0;
+    const F16Instance* t = f16_instances(&n);
+    for (int i = 0; i < n; ++i) {
+        if (!(t[i].cfg == cfg)) continue;
+        const int64_t mp = round_up(M, 256), np = round_up(N, 256), kp = round_up(K, 64);
+        void* ws = nullptr;
+        hipError_t e = workspace(s, static_cast<size_t>((mp + np) * kp) * 2, &ws);
+        if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
+        uint16_t* A16 = static_cast<uint16_t*>(ws);
+        uint16_t* B16t = A16 + mp * kp;
+        e = launch_round_a(A, lda, static_cast<int>(M), static_cast<int>(K), A16, mp, kp, s);
+        if (e != hipSuccess) return status_of(e);
+        e = launch_round_bt(B, ldb, static_cast<int>(K), static_cast<int>(N), B16t, np, kp, s);
+        if (e != hipSuccess) return status_of(e);
+        F16Args a{A16, B16t, C, kp, ldc, static_cast<int>(M), static_cast<int>(N), alpha, beta,
+                  tiles_m, tiles_n};
+        if (log_debug())
+            std::fprintf(stderr, "[gemm355] f16r M=%lld N=%lld K=%lld %s path=%s\n",
+                         (long long)M, (long long)N, (long long)K, format_config(cfg).c_str(),
+                         ((M % cfg.bm) || (N % cfg.bn)) ? "masked-store" : "aligned");
+        return status_of(t[i].launch(a, s));
+    }
+    return GEMM355_ERR_CONFIG;
+}
+
+int gemm(int mode, int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
+         const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream,
+         const TileConfig* force) {
+    const int bad = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (bad) return bad;
+    if (M == 0 || N == 0) return 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0 || alpha == 0.f) {
+        if (log_debug())
+            std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld path=beta-only\n",
+                         mode_name(mode), (long long)M, (long long)N, (long long)K);
+        return status_of(launch_scale_c(C, ldc, static_cast<int>(M), static_cast<int>(N), beta, s));
+    }
+    TileConfig cfg;
+    if (force) {
+        cfg = *force;
+    } else {
+        Source src;
+        const int rc = select_config(mode, M, N, K, A, lda, B, ldb, beta, &cfg, &src);
+        if (rc) return rc;
+    }
+    return launch_with(cfg, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+}
+
+// ---------------------------------------------------------------------------
+// Tuning cache file: one entry per line,
+//   <mode> <M> <N> <K> <vec_a> <vec_b> <beta0> BM=.. BN=.. BK=.. WM=.. WN=.. GM=..
+// ---------------------------------------------------------------------------
+size_t load_cache_locked(State& st, const char* path) {
+    FILE* f = std::fopen(path, "r");
+    if (!f) return 0;
+    char line[512];
+    size_t n = 0;
+    while (std::fgets(line, sizeof line, f)) {
+        char mode_s[16];
+        long long M, N, K;
+        int va, vb, b0, off = 0;
+        if (std::sscanf(line, "%15s %lld %lld %lld %d %d %d %n", mode_s, &M, &N, &K, &va, &vb,
+                        &b0, &off) != 7)
+            continue;
+        int mode = -1;
+        if (std::strcmp(mode_s, "f32") == 0) mode = GEMM355_MODE_F32;
+        if (std::strcmp(mode_s, "f16r") == 0) mode = GEMM355_MODE_F16R;
+        if (mode < 0 || M < 0 || N < 0 || K < 0) continue;
+        std::string rest(line + off);
+        while (!rest.empty() && (rest.back() == '\n' || rest.back() == '\r')) rest.pop_back();
+        TileConfig c;
+        if (!parse_config(mode, rest.c_str(), &c)) continue;
+        st.cache[Key{mode, M, N, K, va != 0, vb != 0, b0 != 0}] = c;
+        ++n;
+    }
+    std::fclose(f);
+    return n;
+}
+
+int save_cache_locked(State& st, const char* path) {
+    if (!path || !*path) return GEMM355_ERR_BUFFER;
+    const std::string tmp = std::string(path) + ".tmp";
+    FILE* f = std::fopen(tmp.c_str(), "w");
+    if (!f) return GEMM355_ERR_BUFFER;
+    int n = 0;
+    for (const auto& kv : st.cache) {
+        const Key& k = kv.first;
+        std::fprintf(f, "%s %lld %lld %lld %d %d %d %s\n", mode_name(k.mode), (long long)k.M,
+                     (long long)k.N, (long long)k.K, k.vec_a, k.vec_b, k.beta0,
+                     format_config(kv.second).c_str());
+        ++n;
+    }
+    std::fclose(f);
+    if (std::rename(tmp.c_str(), path) != 0) return GEMM355_ERR_BUFFER;
+    return n;
+}
+
+// ---------------------------------------------------------------------------
+// The autotuner (phobos docs, "gemm, f32", section "Tuning"): stage 1 times
+// every compiled configuration a few times and drops those that fail; stage 2
+// re-times the fastest few over shuffled rounds, one launch of each per round,
+// so the finalists see the same clocks (the lab's sweep() helper).
+// ---------------------------------------------------------------------------
+struct Timed {
+    TileConfig cfg;
+    std::vector<float> ms;
+    float median() const {
+        std::vector<float> v = ms;
+        std::sort(v.begin(), v.end());
+        return v.empty() ? 1e30f : v[v.size() / 2];
+    }
+};
+
+int time_once(const TileConfig& cfg, int64_t M, int64_t N, int64_t K, const float* A,
+              int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
+              hipStream_t s, hipEvent_t e0, hipEvent_t e1, float* ms) {
+    hipError_t e = hipEventRecord(e0, s);
+    if (e != hipSuccess) return status_of(e);
+    int rc = gemm(cfg.mode, M, N, K, 1.0f, A, lda, B, ldb, beta, C, ldc, s, &cfg);
+    if (rc) return rc;
+    e = hipEventRecord(e1, s);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(ms, e0, e1);
+    return status_of(e);
+}
+
+int tune(int mode, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+         int64_t ldb, float beta, int64_t ldc, void* stream) {
+    if (mode != GEMM355_MODE_F32 && mode != GEMM355_MODE_F16R) return GEMM355_ERR_MODE;
+    float* C = nullptr;
+    // a stand-in C pointer for the argument check; the real scratch comes next
+    const int bad = check_args(M, N, K, 1.0f, A, lda, B, ldb,
+                               reinterpret_cast<const float*>(uintptr_t{16}), ldc);
+    if (bad) return bad;
+    if (M == 0 || N == 0 || K == 0) return 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMalloc(&C, static_cast<size_t>(M) * ldc * sizeof(float));
+    if (e != hipSuccess) return GEMM355_ERR_ALLOC;
+    e = hipMemsetAsync(C, 0, static_cast<size_t>(M) * ldc * sizeof(float), s);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (e == hipSuccess) e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    int rc = status_of(e);
+    std::vector<Timed> ok;
+    if (rc == 0) {
+        for (const TileConfig& cfg : configs_of(mode)) {
+            Timed t{cfg, {}};
+            float ms = 0.f;
+            int r = time_once(cfg, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, &ms);  // warm-up
+            for (int i = 0; i < 3 && r == 0; ++i) {
+                r = time_once(cfg, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, &ms);
+                if (r == 0) t.ms.push_back(ms);
+            }
+            if (r != 0) {
+                (void)hipGetLastError();   // a failing candidate is skipped
+                if (log_debug())
+                    std::fprintf(stderr, "[gemm355] tune: %s failed (%d), skipped\n",
+                                 format_config(cfg).c_str(), r);
+                continue;
+            }
+            ok.push_back(t);
+        }
+        std::sort(ok.begin(), ok.end(),
+                  [](const Timed& a, const Timed& b) { return a.median() < b.median(); });
+        if (ok.size() > 4) ok.resize(4);
+        for (Timed& t : ok) t.ms.clear();
+        uint64_t lcg = 0x9E3779B97F4A7C15ull;
+        std::vector<size_t> order(ok.size());
+        for (int round = 0; round < 12 && !ok.empty(); ++round) {
+            for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+            for (size_t i = order.size(); i > 1; --i) {   // Fisher-Yates with an LCG
+                lcg = lcg * 6364136223846793005ull + 1442695040888963407ull;
+                std::swap(order[i - 1], order[(lcg >> 33) % i]);
+            }
+            for (size_t i : order) {
+                float ms = 0.f;
+                if (time_once(ok[i].cfg, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, &ms) == 0)
+                    ok[i].ms.push_back(ms);
+            }
+        }
+        if (ok.empty()) {
+            rc = GEMM355_ERR_CONFIG;
+        } else {
+            const Timed* best = &ok[0];
+            for (const Timed& t : ok)
+                if (t.median() < best->median()) best = &t;
+            if (log_debug())
+                for (const Timed& t : ok)
+                    std::fprintf(stderr, "[gemm355] tune %s M=%lld N=%lld K=%lld %s: %.4f ms%s\n",
+                                 mode_name(mode), (long long)M, (long long)N, (long long)K,
+                                 format_config(t.cfg).c_str(), t.median(),
+                                 &t == best ? "  <- chosen" : "");
+            State& st = state();
+            std::lock_guard<std::mutex> lock(st.mu);
+            read_env_locked(st);
+            st.cache[Key{mode, M, N, K, vec_ok(A, lda), vec_ok(B, ldb), beta == 0.f}] = best->cfg;
+            if (!st.cache_path.empty()) save_cache_locked(st, st.cache_path.c_str());
+        }
+    }
+    (void)hipStreamSynchronize(s);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    (void)hipFree(C);
+    return rc;
+}
+
+int copy_out(const std::string& s, char* buf, size_t len) {
+    if (!buf || len == 0) return GEMM355_ERR_BUFFER;
+    if (s.size() + 1 > len) {
+        std::memcpy(buf, s.data(), len - 1);
+        buf[len - 1] = '\0';
+        return GEMM355_ERR_BUFFER;
+    }
+    std::memcpy(buf, s.c_str(), s.size() + 1);
+    return 0;
+}
+
+}  // namespace
+}  // namespace g355
+
+using namespace g355;
+
+extern "C" {
+
+int gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
+             const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream) {
+    return gemm(GEMM355_MODE_F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, nullptr);
+}
+
+int gemm_f16r_f32acc(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
+                     const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
+                     void* stream) {
+    return gemm(GEMM355_MODE_F16R, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, nullptr);
+}
+
+int gemm355_tune(int mode, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                 const float* B, int64_t ldb, float beta, int64_t ldc, void* stream) {
+    return tune(mode, M, N, K, A, lda, B, ldb, beta, ldc, stream);
+}
+
+int gemm355_get_config(int mode, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                       int64_t ldc, float beta, char* buf, size_t len) {
+    if (mode != GEMM355_MODE_F32 && mode != GEMM355_MODE_F16R) return GEMM355_ERR_MODE;
+    const float* aligned = reinterpret_cast<const float*>(uintptr_t{256});
+    const int bad = check_args(M, N, K, 1.0f, aligned, lda, aligned, ldb, aligned, ldc);
+    if (bad) return bad;
+    TileConfig cfg;
+    Source src;
+    const int rc = select_config(mode, M, N, K, aligned, lda, aligned, ldb, beta, &cfg, &src);
+    if (rc) return rc;
+    const char* sname = src == Source::Pin ? "pin" : src == Source::Tuned ? "tuned" : "heuristic";
+    return copy_out(format_config(cfg) + " source=" + sname, buf, len);
+}
+
+int gemm355_set_config(int mode, const char* spec) {
+    if (mode != GEMM355_MODE_F32 && mode != GEMM355_MODE_F16R) return GEMM355_ERR_MODE;
+    State& st = state();
+    std::lock_guard<std::mutex> lock(st.mu);
+    read_env_locked(st);
+    if (!spec || !*spec) {
+        st.pin_set[mode] = false;
+        st.pin_bad[mode] = false;
+        return 0;
+    }
+    TileConfig c;
+    if (!parse_config(mode, spec, &c)) return GEMM355_ERR_CONFIG;
+    st.pin[mode] = c;
+    st.pin_set[mode] = true;
+    st.pin_bad[mode] = false;
+    return 0;
+}
+
+int gemm355_parse_config(int mode, const char* spec, char* buf, size_t len) {
+    if (mode != GEMM355_MODE_F32 && mode != GEMM355_MODE_F16R) return GEMM355_ERR_MODE;
+    TileConfig c;
+    if (!spec || !parse_config(mode, spec, &c)) return GEMM355_ERR_CONFIG;
+    return copy_out(format_config(c), buf, len);
+}
+
+int gemm355_list_configs(int mode, char* buf, size_t len) {
+    if (mode != GEMM355_MODE_F32 && mode != GEMM355_MODE_F16R) return GEMM355_ERR_MODE;
+    std::string all;
+    const std::vector<TileConfig> cs = configs_of(mode);
+    for (const TileConfig& c : cs) all += format_config(c) + "\n";
+    const int rc = copy_out(all, buf, len);
+    return rc ? rc : static_cast<int>(cs.size());
+}
+
+int gemm355_cache_load(const char* path) {
+    State& st = state();
+    std::lock_guard<std::mutex> lock(st.mu);
+    read_env_locked(st);
+    if (!path || !*path) return GEMM355_ERR_BUFFER;
+    st.cache_path = path;
+    return static_cast<int>(load_cache_locked(st, path));
+}
+
+int gemm355_cache_save(const char* path) {
+    State& st = state();
+    std::lock_guard<std::mutex> lock(st.mu);
+    read_env_locked(st);
+    if (path && *path) st.cache_path = path;
+    return save_cache_locked(st, st.cache_path.c_str());
+}
+
+void gemm355_cache_clear(void) {
+    State& st = state();
+    std::lock_guard<std::mutex> lock(st.mu);
+    read_env_locked(st);
+    st.cache.clear();
+}
+
+const char* gemm355_strerror(int status) {
+    switch (status) {
+        case 0: return "success";
+        case -1: return "invalid argument 1 (M)";
+        case -2: return "invalid argument 2 (N)";
+        case -3: return "invalid argument 3 (K)";
+        case -5: return "invalid argument 5 (A is NULL)";
+        case -6: return "invalid argument 6 (lda < max(1, K))";
+        case -7: return "invalid argument 7 (B is NULL)";
+        case -8: return "invalid argument 8 (ldb < max(1, N))";
+        case -10: return "invalid argument 10 (C is NULL)";
+        case -11: return "invalid argument 11 (ldc < max(1, N))";
+        case GEMM355_ERR_CONFIG: return "tile configuration unknown or not compiled";
+        case GEMM355_ERR_ALLOC: return "device allocation failed";
+        case GEMM355_ERR_MODE: return "unknown mode";
+        case GEMM355_ERR_BUFFER: return "output buffer too small or file error";
+        case GEMM355_ERR_INTERNAL: return "internal error";
+        default: break;
+    }
+    if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));
+    return "unknown status";
+}
+
+const char* gemm355_version(void) { return "0.1.0"; }
+
+int gemm355_roof_mfma(int mode, int64_t iters, int blocks, float* sink, double* flops_out,
+                      void* stream) {
+    if (mode != GEMM355_MODE_F32 && mode != GEMM355_MODE_F16R) return GEMM355_ERR_MODE;
+    if (iters < 1 || blocks < 1 || !sink || !flops_out) return GEMM355_ERR_BUFFER;
+    return status_of(
+        launch_roof_mfma(mode, iters, blocks, sink, flops_out, static_cast<hipStream_t>(stream)));
+}
+
+int gemm355_roof_hbm(const void* buf, int64_t bytes, int blocks, float* sink, void* stream) {
+    if (!buf || !sink || bytes < 16 || bytes % 16 || blocks < 1 ||
+        (reinterpret_cast<uintptr_t>(buf) & 15))
+        return GEMM355_ERR_BUFFER;
+    return status_of(launch_roof_hbm(buf, bytes, blocks, sink, static_cast<hipStream_t>(stream)));
+}
+
+int gemm355_copy_f32(const float* src, float* dst, int64_t n, void* stream) {
+    if (n < 0 || ((!src || !dst) && n > 0)) return GEMM355_ERR_BUFFER;
+    if (n == 0) return 0;
+    if ((reinterpret_cast<uintptr_t>(src) & 15) || (reinterpret_cast<uintptr_t>(dst) & 15))
+        return GEMM355_ERR_BUFFER;
+    return status_of(launch_copy_f32(src, dst, n, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// internal.hpp -- declarations shared by the kernels and the host side of
+// libgemm355.  Not part of the public ABI (include/gemm355.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "gemm355.h"
+
+namespace g355 {
+
+// One tile configuration: the workgroup owns a BM x BN tile of C and walks K
+// in steps of BK; its WM x WN wavefronts of 64 lanes split the tile; GM tile
+// rows form one group of the rasterised tile order (L2 reuse).
+struct TileConfig {
+    int mode;  // GEMM355_MODE_*
+    int bm, bn, bk, wm, wn, gm;
+    int threads() const { return wm * wn * 64; }
+    bool operator==(const TileConfig& o) const {
+        return mode == o.mode && bm == o.bm && bn == o.bn && bk == o.bk && wm == o.wm &&
+               wn == o.wn && gm == o.gm;
+    }
+};
+
+// Arguments of one f32 GEMM launch.
+struct F32Args {
+    const float* A;
+    const float* B;
+    float* C;
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+    float alpha, beta;
+    int tiles_m, tiles_n;
+};
+
+// Arguments of one f16 GEMM launch on rounded, padded operands:
+// A16 is Mp x Kp (row-major), B16t is Np x Kp (B transposed), both binary16,
+// zero outside the logical M x K and K x N.
+struct F16Args {
+    const uint16_t* A16;
+    const uint16_t* B16t;
+    float* C;
+    int64_t kp;   // padded K, row stride of A16 and B16t (elements)
+    int64_t ldc;
+    int M, N;
+    float alpha, beta;
+    int tiles_m, tiles_n;
+};
+
+// Which variant of a compiled configuration a launch needs.
+struct F32Variant {
+    bool masked;  // some of M, N, K is not a tile multiple
+    bool vec;     // 16-byte global loads are legal (lda, ldb % 4 == 0, aligned pointers)
+};
+
+using F32Launch = hipError_t (*)(const F32Args&, F32Variant, hipStream_t);
+using F16Launch = hipError_t (*)(const F16Args&, hipStream_t);
+
+struct F32Instance {
+    TileConfig cfg;
+    F32Launch launch;
+};
+struct F16Instance {
+    TileConfig cfg;
+    F16Launch launch;
+};
+
+// Tables of compiled instances (defined in the kernel translation units).
+const F32Instance* f32_instances(int* count);
+const F16Instance* f16_instances(int* count);
+
+// Rounding/padding passes of the f16r mode.
+hipError_t launch_round_a(const float* A, int64_t lda, int M, int K, uint16_t* A16, int64_t mp,
+                          int64_t kp, hipStream_t s);
+hipError_t launch_round_bt(const float* B, int64_t ldb, int K, int N, uint16_t* B16t,
+                           int64_t np, int64_t kp, hipStream_t s);
+
+// C = beta*C (beta == 0: C = 0 without reading it).
+hipError_t launch_scale_c(float* C, int64_t ldc, int M, int N, float beta, hipStream_t s);
+
+// Measurement kernels.
+hipError_t launch_roof_mfma(int mode, int64_t iters, int blocks, float* sink, double* flops,
+                            hipStream_t s);
+hipError_t launch_roof_hbm(const void* buf, int64_t bytes, int blocks, float* sink,
+                           hipStream_t s);
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
+
+// The workgroup -> tile mapping used by every GEMM kernel.  Consecutive
+// workgroup ids are dealt to the 8 XCDs of the chip in turn; the remap gives
+// each XCD one contiguous run of the rasterised order, so the tiles that
+// share an XCD's L2 also share A rows and B columns.  Within the run, tiles
+// go down GM tile rows before moving one tile column right.
+__device__ __forceinline__ void tile_of_block(int g, int G, int tiles_m, int tiles_n, int gm,
+                                              int& tm, int& tn) {
+    const int xcd = g & 7;
+    const int q = G >> 3, r = G & 7;
+    const int gg = xcd * q + (xcd < r ? xcd : r) + (g >> 3);
+    const int per_group = gm * tiles_n;
+    const int group = gg / per_group;
+    const int first_m = group * gm;
+    const int rows = min(tiles_m - first_m, gm);
+    const int in_group = gg - group * per_group;
+    tm = first_m + in_group % rows;
+    tn = in_group / rows;
+}
+
+}  // namespace g355

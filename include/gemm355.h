@@ -1,0 +1,180 @@
+/*
+ * gemm355.h -- C ABI of libgemm355, a GEMM library for the AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (phobos docs, page "gemm, f32", opening paragraph and section
+ * "The epilogue"):
+ *
+ *     C = alpha * A @ B + beta * C
+ *
+ * with A an M x K, B a K x N and C an M x N matrix of f32, alpha and beta f32
+ * scalars.  The f16r mode (phobos docs, page "gemm on tensor cores", section
+ * "What changes") rounds every element of A and B to IEEE binary16 (round to
+ * nearest, ties to even, subnormals kept) before multiplying and accumulates
+ * the products in f32; C, alpha and beta stay f32.
+ *
+ * Layout and ownership (both modes):
+ *   - all matrices are row-major: A[i*lda + k], B[k*ldb + j], C[i*ldc + j];
+ *   - A, B and C are device pointers owned by the caller; A and B are only
+ *     read; C is read (unless beta == 0) and written in place; C must not
+ *     overlap A or B;
+ *   - alpha and beta are host values passed by value.
+ *
+ * Execution:
+ *   - the work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns without waiting for it;
+ *   - the f16r mode writes the rounded operands into a device workspace that
+ *     the library allocates on first use and keeps per (device, stream); calls
+ *     on one stream are ordered and share it; calls on different streams use
+ *     different workspaces;
+ *   - every call is thread-safe.
+ *
+ * Special cases, decided on the host before any launch:
+ *   - M == 0 or N == 0: nothing to do, returns 0;
+ *   - K == 0 or alpha == 0: C = beta * C, A and B are not read;
+ *   - beta == 0: C is only written, never read (NaN in C does not survive).
+ *
+ * Return value:
+ *   0              success (the work is enqueued);
+ *   -p (p = 1..11)  argument p is invalid (1 M, 2 N, 3 K, 5 A, 6 lda, 7 B,
+ *                  8 ldb, 10 C, 11 ldc), as in BLAS's xerbla convention;
+ *                  nothing is launched and C is untouched;
+ *   GEMM355_ERR_*  (below -100) a library-level failure;
+ *   > 0            a hipError_t reported by the HIP runtime at launch.  Faults
+ *                  inside a kernel surface at the caller's next synchronisation.
+ */
+#ifndef GEMM355_H
+#define GEMM355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GEMM355_MODE_F32 0  /* plain f32 operands, f32 accumulation */
+#define GEMM355_MODE_F16R 1 /* operands rounded to binary16 (RNE), f32 accumulation */
+
+#define GEMM355_OK 0
+#define GEMM355_ERR_CONFIG (-101)   /* tile configuration unknown or not compiled */
+#define GEMM355_ERR_ALLOC (-102)    /* workspace or scratch allocation failed */
+#define GEMM355_ERR_MODE (-103)     /* mode is neither F32 nor F16R */
+#define GEMM355_ERR_BUFFER (-104)   /* output buffer too small */
+#define GEMM355_ERR_INTERNAL (-105) /* no kernel instance fits (library bug) */
+
+/*
+ * C = alpha*A@B + beta*C in f32.  Arguments:
+ *   M, N, K   matrix sizes, each >= 0;
+ *   A         device pointer to M x K f32, row stride lda >= max(1, K);
+ *   B         device pointer to K x N f32, row stride ldb >= max(1, N);
+ *   C         device pointer to M x N f32, row stride ldc >= max(1, N);
+ *   stream    hipStream_t to enqueue on (NULL = default stream).
+ * A and B may be NULL only when M*K (resp. K*N) is 0 or alpha == 0; C may be
+ * NULL only when M*N is 0.
+ */
+int gemm_f32(int64_t M, int64_t N, int64_t K, float alpha,
+             const float* A, int64_t lda, const float* B, int64_t ldb,
+             float beta, float* C, int64_t ldc, void* stream);
+
+/*
+ * The same operation with A and B rounded to binary16 (round to nearest even)
+ * and the products accumulated in f32 (phobos docs, "gemm on tensor cores",
+ * section "What changes").  Arguments and return values as gemm_f32.
+ */
+int gemm_f16r_f32acc(int64_t M, int64_t N, int64_t K, float alpha,
+                     const float* A, int64_t lda, const float* B, int64_t ldb,
+                     float beta, float* C, int64_t ldc, void* stream);
+
+/*
+ * Per-shape tile autotuning (phobos docs, "gemm, f32", section "Tuning": time
+ * every configuration briefly, skip those that fail, then re-time the fastest
+ * few over interleaved rounds under the same clocks).  Runs the candidates on
+ * the caller's A and B and on a scratch C the library allocates and frees
+ * (the caller's C is not touched), synchronises `stream`, and stores the
+ * winner in the per-shape cache used by later calls with the same key
+ * (mode, M, N, K, alignment class of lda/ldb/ldc and pointers, beta == 0).
+ * `beta` only selects the key and the epilogue variant timed.
+ * Returns 0, a negative argument/library error, or a positive hipError_t.
+ */
+int gemm355_tune(int mode, int64_t M, int64_t N, int64_t K,
+                 const float* A, int64_t lda, const float* B, int64_t ldb,
+                 float beta, int64_t ldc, void* stream);
+
+/*
+ * The tile configuration a call with these arguments would use, written as
+ * "BM=.. BN=.. BK=.. WM=.. WN=.. GM=.." plus " source=pin|tuned|heuristic"
+ * into buf (NUL-terminated, at most len bytes).  Host only; no GPU call.
+ */
+int gemm355_get_config(int mode, int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldb, int64_t ldc, float beta,
+                       char* buf, size_t len);
+
+/*
+ * Pin one tile configuration for every later call of `mode`, skipping the
+ * search (phobos docs, "gemm, f32", section "Tuning", the pinned run).
+ * Grammar: space-separated KEY=VALUE with keys BM|TILE_M, BN|TILE_N,
+ * BK|TILE_K, WM, WN, GM; omitted keys take the first compiled instance that
+ * matches the given ones.  NULL or "" clears the pin.  The environment
+ * variables GEMM355_CONFIG_F32 / GEMM355_CONFIG_F16R set the initial pin.
+ * Returns 0 or GEMM355_ERR_CONFIG (the pin is then unchanged).  Host only.
+ */
+int gemm355_set_config(int mode, const char* spec);
+
+/*
+ * Parse `spec` (grammar as gemm355_set_config) and write the canonical form of
+ * the compiled instance it names into buf.  Returns 0 or GEMM355_ERR_CONFIG.
+ * Host only.
+ */
+int gemm355_parse_config(int mode, const char* spec, char* buf, size_t len);
+
+/*
+ * Newline-separated canonical forms of every compiled tile configuration of
+ * `mode`.  Returns the number of configurations, or a negative error.
+ * Host only.
+ */
+int gemm355_list_configs(int mode, char* buf, size_t len);
+
+/* Load (path != NULL) or save (path == NULL: to the same path) the per-shape
+ * tuning cache as text.  Lines that do not parse or name unknown instances
+ * are ignored.  Returns the number of entries read/written, or a negative
+ * error.  Host only. */
+int gemm355_cache_load(const char* path);
+int gemm355_cache_save(const char* path);
+/* Drop every tuned entry.  Host only. */
+void gemm355_cache_clear(void);
+
+/* Text for a status code returned by this library.  Never NULL. */
+const char* gemm355_strerror(int status);
+
+/* Library version string, e.g. "0.1.0". */
+const char* gemm355_version(void);
+
+/*
+ * Measurement kernels for the roofs the GEMM is judged against (the
+ * Matrix Multiplication lab, "Part 1 -- the two roofs, again": a kernel of
+ * nothing but independent multiply-adds, and a streaming read).
+ *
+ * gemm355_roof_mfma: enqueue `blocks` workgroups of 256 threads, each wave
+ * issuing `iters` rounds of 8 independent matrix instructions of the mode
+ * (F32: 32x32x2 f32; F16R: 32x32x16 f16 with f32 accumulators) into `sink`
+ * (device, >= blocks*256 floats).  *flops_out receives the flop count of the
+ * launch (2*m*n*k per instruction).
+ *
+ * gemm355_roof_hbm: enqueue a grid-stride 16-byte read of `bytes` bytes
+ * (multiple of 16) from device pointer `buf`, with `blocks` workgroups of 256
+ * threads; `sink` is a device float written only to keep the loads alive.
+ *
+ * gemm355_copy_f32: enqueue dst[i] = src[i] for n floats (a plain copy
+ * kernel of known traffic, for calibrating hardware byte counters).
+ */
+int gemm355_roof_mfma(int mode, int64_t iters, int blocks, float* sink, double* flops_out,
+                      void* stream);
+int gemm355_roof_hbm(const void* buf, int64_t bytes, int blocks, float* sink, void* stream);
+int gemm355_copy_f32(const float* src, float* dst, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM355_H */

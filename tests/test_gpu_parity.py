@@ -1,0 +1,279 @@
+"""GPU parity tests: the HIP path through the C ABI against the CPU oracle.
+
+Bound (both modes): |C_gpu - C_ref| <= tol * W elementwise, with
+W = |alpha|*(|r(A)||r(B)|)_ij + |beta||C_ij| and tol = 1e-5 (f32), 4e-5 (f16r).
+Small shapes are checked element by element over the whole output; the full
+workload sizes are checked on bands of whole rows at both edges plus sampled
+elements the oracle computes one by one, and through properties that hold at
+any size (exact small-integer results, identity, alpha = 0, determinism).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import WORKLOADS, make_inputs, sample_indices, small_integers, workload_inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():   # collected on CPU-only hosts, never run there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gemm_tiled_amd as g  # noqa: E402
+from tests.gpu_helpers import pinned, run, say, to_device  # noqa: E402
+
+TOL = oracle.TOL
+MODES = ["f32", "f16r"]
+
+
+def assert_parity(mode, A, B, C, alpha, beta, got, rows=None):
+    st = oracle.check(mode, A, B, C, alpha, beta, got, rows=rows)
+    assert st["n_fail"] == 0, st
+    return st
+
+
+def assert_sampled(mode, A, B, C, alpha, beta, got, n=4096, seed=1):
+    M, N = got.shape
+    r, c = sample_indices(M, N, n, seed)
+    ref, W = oracle.entries(mode, A, B, C, alpha, beta, r, c)
+    err = np.abs(got[r, c].astype(np.float64) - ref)
+    bad = ~(err <= TOL[mode] * W)
+    assert not bad.any(), (int(bad.sum()), r[bad][:5], c[bad][:5])
+    return float(np.max(err / np.where(W > 0, W, 1.0)))
+
+
+# ---------------------------------------------------------------------------
+# Every compiled tile configuration, aligned and ragged (the tuner may pick any
+# of them, so each must be right on its own).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", MODES)
+def test_every_config_aligned_and_ragged(mode):
+    shapes = [
+        (512, 512, 256, {}),                                    # whole tiles
+        (300, 200, 150, {}),                                    # ragged in M, N, K
+        (257, 129, 67, {"lda": 68, "ldb": 132, "ldc": 131}),    # ragged, padded lds
+        (129, 77, 45, {"lda": 47, "ldb": 79, "ldc": 77}),       # odd lds: 4-byte rows
+    ]
+    for cfg in g.list_configs(mode):
+        for (M, N, K, lds) in shapes:
+            A, B, C = make_inputs(M, N, K, "uniform", seed=11, **lds)
+            say(f"[parity] {mode} {cfg} {M}x{N}x{K} {lds}")
+            with pinned(mode, cfg):
+                got = run(mode, A, B, C, 1.5, 0.5)
+            assert_parity(mode, A, B, C, 1.5, 0.5, got)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads, at their full sizes, with the library's own choice of
+# configuration (heuristic) and after tuning.
+# ---------------------------------------------------------------------------
+
+def test_workload_f32_256():
+    w = WORKLOADS["f32_256_a1.5_b0.5"]
+    A, B, C = workload_inputs(w)
+    say(f"[parity] {w.name}")
+    got = run(w.mode, A, B, C, w.alpha, w.beta)
+    assert_parity(w.mode, A, B, C, w.alpha, w.beta, got)
+
+
+@pytest.mark.parametrize("name", ["f32_4096_a1_b0", "f32_4096_a1_b1", "f16r_4096_a1_b0.5",
+                                  "f32_4000x4097x4093_a2_b-1"])
+def test_workload_full_size(name):
+    w = WORKLOADS[name]
+    A, B, C = workload_inputs(w)
+    say(f"[parity] {w.name} {g.get_config(w.mode, w.M, w.N, w.K, beta=w.beta)}")
+    got = run(w.mode, A, B, C, w.alpha, w.beta)
+    assert np.isfinite(got).all()
+    assert_parity(w.mode, A, B, C, w.alpha, w.beta, got, rows=(0, 96))
+    assert_parity(w.mode, A, B, C, w.alpha, w.beta, got, rows=(w.M - 96, w.M))
+    assert_sampled(w.mode, A, B, C, w.alpha, w.beta, got)
+
+
+def test_workload_f16r_8192():
+    w = WORKLOADS["f16r_8192_a0.75_b-0.25"]
+    A, B, C = workload_inputs(w)
+    say(f"[parity] {w.name} {g.get_config(w.mode, w.M, w.N, w.K, beta=w.beta)}")
+    got = run(w.mode, A, B, C, w.alpha, w.beta)
+    assert np.isfinite(got).all()
+    assert_parity(w.mode, A, B, C, w.alpha, w.beta, got, rows=(0, 32))
+    assert_parity(w.mode, A, B, C, w.alpha, w.beta, got, rows=(w.M - 32, w.M))
+    assert_sampled(w.mode, A, B, C, w.alpha, w.beta, got, n=4096)
+
+
+# ---------------------------------------------------------------------------
+# Exact results: small integers make every partial sum exact in f32 in any
+# order, so the GPU must match the exact product bit for bit (both modes: the
+# integers are exact in f16 too).  The exact product comes from a float64
+# matrix product, exact here because every partial sum is below 2^53.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode,M,N,K,lds", [
+    ("f32", 256, 256, 256, {}),
+    ("f16r", 256, 256, 256, {}),
+    ("f32", 4096, 4096, 4096, {}),
+    ("f16r", 4096, 4096, 4096, {}),
+    ("f32", 4000, 4097, 4093, {}),
+    ("f16r", 4000, 4097, 4093, {}),
+    ("f32", 1000, 999, 1001, {"lda": 1004, "ldb": 1001, "ldc": 1003}),
+])
+def test_small_integers_exact(mode, M, N, K, lds):
+    A, B, C = small_integers(M, N, K, seed=5, **lds)
+    exact_p = A.astype(np.float64) @ B.astype(np.float64)
+    for alpha, beta in ((1.0, 1.0), (2.0, -1.0), (-1.0, 0.5), (0.5, 0.0)):
+        say(f"[exact] {mode} {M}x{N}x{K} {lds} alpha={alpha} beta={beta}")
+        got = run(mode, A, B, C, alpha, beta)
+        exp = (alpha * exact_p + beta * C.astype(np.float64)).astype(np.float32)
+        assert np.array_equal(got, exp), f"{int((got != exp).sum())} elements differ"
+
+
+# ---------------------------------------------------------------------------
+# Closed forms.
+# ---------------------------------------------------------------------------
+
+def _rounding_probe_matrix(rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal(size=(rows, cols)).astype(np.float32)
+    specials = np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, -(1 + 2 ** -11), 2 ** -24, 2 ** -25,
+                         1.5 * 2 ** -24, 2.5 * 2 ** -24, 2 ** -14 - 2 ** -25, 65504.0, 65519.0,
+                         -65519.0, 0.1, -0.3, 1e-6, 3.0e-5, 6.0e-8], dtype=np.float32)
+    X.ravel()[: specials.size] = specials
+    # plus a band of values right at f16 ties across many binades
+    tie = (np.float32(1.0) + np.float32(2 ** -11)) * (2.0 ** rng.integers(-14, 15, size=cols))
+    X[-1, :] = tie.astype(np.float32) * rng.choice([-1, 1], size=cols)
+    return X
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("n,N", [(64, 96), (300, 517)])
+def test_identity_returns_the_rounded_operand(mode, n, N):
+    """A = I: C = r(B) exactly at alpha=1, beta=0; B = I likewise gives r(A).
+    In f16r mode r is round-to-nearest-even to binary16, checked bit for bit
+    against numpy's conversion, including ties and subnormals."""
+    B = _rounding_probe_matrix(n, N, seed=1)
+    I = np.eye(n, dtype=np.float32)
+    say(f"[identity] {mode} A=I {n}x{N}")
+    got = run(mode, I, B, np.zeros((n, N), np.float32), 1.0, 0.0)
+    exp = B.astype(np.float16).astype(np.float32) if mode == "f16r" else B
+    # a signed zero may come back as +0 (adding zero products); compare with -0 folded to +0
+    assert np.array_equal((got + np.float32(0)).view(np.uint32),
+                          (exp + np.float32(0)).view(np.uint32))
+    A = _rounding_probe_matrix(N, n, seed=2)
+    say(f"[identity] {mode} B=I {N}x{n}")
+    got = run(mode, A, I, np.zeros((N, n), np.float32), 1.0, 0.0)
+    exp = A.astype(np.float16).astype(np.float32) if mode == "f16r" else A
+    assert np.array_equal((got + np.float32(0)).view(np.uint32),
+                          (exp + np.float32(0)).view(np.uint32))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_alpha_zero_and_k_zero_scale_c_exactly(mode):
+    A, B, C = make_inputs(333, 444, 55, "normal", seed=3)
+    say(f"[closed form] {mode} alpha=0")
+    got = run(mode, A, B, C, 0.0, -0.75)
+    assert np.array_equal(got, (np.float32(-0.75) * C).astype(np.float32))
+    # K = 0: the product term is empty; A and B are not read (NULL is valid)
+    tC = to_device(C)
+    say(f"[closed form] {mode} K=0")
+    fn = g.lib().gemm_f32 if mode == "f32" else g.lib().gemm_f16r_f32acc
+    st = fn(333, 444, 0, 1.0, None, 1, None, 444, 2.0, tC.data_ptr(), tC.stride(0), None)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert np.array_equal(tC.cpu().numpy(), (np.float32(2.0) * C).astype(np.float32))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_beta_zero_does_not_read_c(mode):
+    A, B, _ = make_inputs(300, 260, 70, "uniform", seed=4)
+    C = np.full((300, 260), np.nan, dtype=np.float32)
+    C[::3, ::5] = np.inf
+    say(f"[closed form] {mode} beta=0 with NaN/inf in C")
+    got = run(mode, A, B, C, 1.25, 0.0)
+    assert np.isfinite(got).all()
+    assert_parity(mode, A, B, C, 1.25, 0.0, got)
+    # alpha = 0 and beta = 0: zeros, C not read
+    got = run(mode, A, B, C, 0.0, 0.0)
+    assert np.array_equal(got, np.zeros_like(got))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_all_ones_a_gives_column_sums(mode):
+    rng = np.random.default_rng(6)
+    M, N, K = 200, 333, 1000
+    B = rng.integers(-100, 101, size=(K, N)).astype(np.float32)
+    A = np.ones((M, K), dtype=np.float32)
+    say(f"[closed form] {mode} all-ones A")
+    got = run(mode, A, B, np.zeros((M, N), np.float32), 1.0, 0.0)
+    colsum = B.astype(np.int64).sum(axis=0).astype(np.float32)
+    assert np.array_equal(got, np.broadcast_to(colsum, (M, N)))
+
+
+# ---------------------------------------------------------------------------
+# Edge cases and brute force on tiny shapes.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_shapes_against_the_oracle(mode):
+    dims = [1, 2, 3, 5, 7, 8, 31, 33]
+    for M in dims:
+        for N in dims:
+            for K in (1, 2, 3, 7, 17):
+                A, B, C = make_inputs(M, N, K, "normal", seed=M * 1000 + N * 10 + K)
+                say(f"[tiny] {mode} {M}x{N}x{K}")
+                got = run(mode, A, B, C, 0.75, -0.25)
+                assert_parity(mode, A, B, C, 0.75, -0.25, got)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_empty_output_leaves_c_alone(mode):
+    fn = g.lib().gemm_f32 if mode == "f32" else g.lib().gemm_f16r_f32acc
+    tC = torch.full((4, 4), 7.0, device="cuda:0")
+    say(f"[edge] {mode} M=0 / N=0")
+    assert fn(0, 4, 4, 1.0, None, 4, None, 4, 0.0, tC.data_ptr(), 4, None) == 0
+    assert fn(4, 0, 4, 1.0, None, 4, None, 1, 0.0, tC.data_ptr(), 4, None) == 0
+    torch.cuda.synchronize()
+    assert bool((tC == 7.0).all())
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_bitwise_deterministic(mode):
+    A, B, C = make_inputs(1024, 768, 1000, "normal", seed=8)
+    say(f"[determinism] {mode}")
+    first = run(mode, A, B, C, 1.0, 1.0)
+    for _ in range(3):
+        again = run(mode, A, B, C, 1.0, 1.0)
+        assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_non_default_stream(mode):
+    A, B, C = make_inputs(640, 384, 512, "uniform", seed=9)
+    s = torch.cuda.Stream()
+    tA, tB, tC = to_device(A), to_device(B), to_device(C)
+    torch.cuda.synchronize()
+    say(f"[stream] {mode}")
+    with torch.cuda.stream(s):
+        g.gemm(mode, tA, tB, tC, 1.0, 0.5)
+    s.synchronize()
+    assert_parity(mode, A, B, C, 1.0, 0.5, tC.cpu().numpy())
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_tuner_leaves_c_alone_and_its_choice_is_correct(mode):
+    M, N, K = 1536, 1280, 1024
+    A, B, C = make_inputs(M, N, K, "uniform", seed=10)
+    tA, tB, tC = to_device(A), to_device(B), to_device(C)
+    g.cache_clear()
+    try:
+        say(f"[tune] {mode} {M}x{N}x{K}")
+        g.tune(mode, tA, tB, tC, beta=0.5)
+        assert np.array_equal(tC.cpu().numpy(), C)
+        cfg = g.get_config(mode, M, N, K, beta=0.5)
+        assert cfg.endswith("source=tuned"), cfg
+        g.gemm(mode, tA, tB, tC, 1.0, 0.5)
+        torch.cuda.synchronize()
+        assert_parity(mode, A, B, C, 1.0, 0.5, tC.cpu().numpy())
+    finally:
+        g.cache_clear()
