@@ -55,15 +55,15 @@ std::vector<TileConfig> configs_of(int mode) {
 
 std::string format_config(const TileConfig& c) {
     char b[128];
-    std::snprintf(b, sizeof b, "BM=%d BN=%d BK=%d WM=%d WN=%d GM=%d", c.bm, c.bn, c.bk, c.wm,
-                  c.wn, c.gm);
+    std::snprintf(b, sizeof b, "BM=%d BN=%d BK=%d ST=%d WM=%d WN=%d GM=%d", c.bm, c.bn, c.bk,
+                  c.st, c.wm, c.wn, c.gm);
     return b;
 }
 
 // Parse "KEY=VALUE ..." into the first compiled instance matching every given
 // key.  Returns false on a syntax error, an unknown key or no match.
 bool parse_config(int mode, const char* spec, TileConfig* out) {
-    int want[6] = {-1, -1, -1, -1, -1, -1};   // bm bn bk wm wn gm
+    int want[7] = {-1, -1, -1, -1, -1, -1, -1};   // bm bn bk wm wn gm st
     const char* p = spec;
     bool any = false;
     while (*p) {
@@ -87,15 +87,16 @@ bool parse_config(int mode, const char* spec, TileConfig* out) {
         else if (key == "WM") slot = 3;
         else if (key == "WN") slot = 4;
         else if (key == "GM") slot = 5;
+        else if (key == "ST" || key == "STAGES") slot = 6;
         if (slot < 0) return false;
         want[slot] = static_cast<int>(v);
         any = true;
     }
     if (!any) return false;
     for (const TileConfig& c : configs_of(mode)) {
-        const int have[6] = {c.bm, c.bn, c.bk, c.wm, c.wn, c.gm};
+        const int have[7] = {c.bm, c.bn, c.bk, c.wm, c.wn, c.gm, c.st};
         bool ok = true;
-        for (int i = 0; i < 6; ++i)
+        for (int i = 0; i < 7; ++i)
             if (want[i] >= 0 && want[i] != have[i]) ok = false;
         if (ok) {
             *out = c;
@@ -309,12 +310,12 @@ int launch_with(const TileConfig& cfg, int64_t M, int64_t N, int64_t K, float al
         if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
         uint16_t* A16 = static_cast<uint16_t*>(ws);
         uint16_t* B16t = A16 + mp * kp;
-        e = launch_round_a(A, lda, static_cast<int>(M), static_cast<int>(K), A16, mp, kp, s);
+        e = launch_pack_a(A, lda, static_cast<int>(M), static_cast<int>(K), A16, mp, kp, s);
         if (e != hipSuccess) return status_of(e);
-        e = launch_round_bt(B, ldb, static_cast<int>(K), static_cast<int>(N), B16t, np, kp, s);
+        e = launch_pack_bt(B, ldb, static_cast<int>(K), static_cast<int>(N), B16t, np, kp, s);
         if (e != hipSuccess) return status_of(e);
-        F16Args a{A16, B16t, C, kp, ldc, static_cast<int>(M), static_cast<int>(N), alpha, beta,
-                  tiles_m, tiles_n};
+        F16Args a{A16, B16t, C, kp / 64, ldc, static_cast<int>(M), static_cast<int>(N), alpha,
+                  beta, tiles_m, tiles_n};
         if (log_debug())
             std::fprintf(stderr, "[gemm355] f16r M=%lld N=%lld K=%lld %s path=%s\n",
                          (long long)M, (long long)N, (long long)K, format_config(cfg).c_str(),

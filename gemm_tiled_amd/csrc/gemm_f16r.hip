@@ -4,13 +4,16 @@
 //
 // The phobos docs page "gemm on tensor cores" (section "What changes") keeps
 // the f32 kernel line for line and only moves dot onto the matrix units with
-// operands rounded to f16.  Here the rounding is a pass of its own: A is
-// rounded into a row-major binary16 copy and B into a transposed binary16 copy
-// (each row holds one column of B, k contiguous), both zero-padded to whole
-// tiles.  The GEMM kernel then reads two k-contiguous operands with 16-byte
-// loads, half the bytes of the f32 source, with no masks on its loads; only the
-// epilogue is masked.  The zero padding is the masked-edge rule of the
-// Matrix Multiplication lab's tiled kernels (out-of-range operands load as 0).
+// operands rounded to f16.  Here the rounding is a pass of its own that also
+// packs each operand panel-major: A, and B transposed (so both are k
+// contiguous), are cut into blocks of 256 rows x 64 k, and each block is
+// stored as one contiguous 32 KB run that is already the shared-memory image
+// the GEMM kernel multiplies from.  Filling a panel is then a straight copy of
+// contiguous kilobytes (one stream per panel instead of 256 rows scattered
+// one row pitch apart), and the zero padding of partial blocks is the masked
+// edge rule of the Matrix Multiplication lab's tiled kernels (out-of-range
+// operands load as 0), so the GEMM loads carry no masks; only its epilogue is
+// masked.
 #include "internal.hpp"
 
 namespace g355 {
@@ -18,7 +21,7 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Two f32 -> two binary16, round to nearest even (a C++ conversion to
 // _Float16 is correctly rounded in the default rounding mode), packed.
@@ -28,19 +31,43 @@ __device__ __forceinline__ uint32_t pack_rn(float lo, float hi) {
 }
 
 // ----------------------------------------------------------------------------
-// A -> A16: row-major, Mp x Kp, zero outside M x K.  One thread writes 8
-// consecutive k of one row (16 bytes).
+// Packed operand layout.  Rows (of A, or columns of B) are grouped in blocks
+// of kPackRows, depth in blocks of kPackK = 64.  Block (xb, kb) starts at
+// element ((xb * nkb) + kb) * kPackRows * kPackK.  Inside it, row r holds its
+// 64 values as 8 chunks of 8, logical chunk c at position c ^ swz(r):
+//   swz(r) = (r / 2) % 8.
+// A 16-byte shared-memory read is served 16 lanes at a time from 64 four-byte
+// banks (256 bytes); the 16 lanes of a fragment read take 16 consecutive rows
+// at one logical chunk, and with 128-byte rows the swizzle puts them in 16
+// different 16-byte slots.
 // ----------------------------------------------------------------------------
+constexpr int kPackRows = 256;
+constexpr int kPackK = 64;
+constexpr int kBlockElems = kPackRows * kPackK;
+
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ int64_t packed_offset(int64_t x, int kb, int c, int64_t nkb) {
+    const int64_t xb = x / kPackRows;
+    const int r = static_cast<int>(x - xb * kPackRows);
+    return ((xb * nkb + kb) * kPackRows + r) * kPackK + ((c ^ swz(r)) << 3);
+}
+
+// A -> packed A16 (Mp rows, zero outside M x K).  One thread converts 8
+// consecutive k of one row (16 bytes out); consecutive threads walk along the
+// row of A, so the f32 reads stream.
 template <bool VEC>
-__global__ __launch_bounds__(256) void round_a_kernel(const float* __restrict__ A, int64_t lda,
-                                                      int M, int K, uint16_t* __restrict__ A16,
-                                                      int64_t mp, int64_t kp) {
-    const int64_t k8s = kp / 8;
-    const int64_t units = mp * k8s;
+__global__ __launch_bounds__(256) void pack_a_kernel(const float* __restrict__ A, int64_t lda,
+                                                     int M, int K, uint16_t* __restrict__ A16,
+                                                     int64_t mp, int64_t nkb) {
+    const int64_t units = mp * nkb * 8;
     for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < units;
          u += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = u / k8s;
-        const int k = static_cast<int>(u - r * k8s) * 8;
+        const int64_t q = u >> 3;
+        const int c = static_cast<int>(u & 7);
+        const int64_t r = q / nkb;
+        const int kb = static_cast<int>(q - r * nkb);
+        const int k = kb * kPackK + c * 8;
         float v[8];
         if (r < M && VEC && k + 7 < K) {
             const float4* src = reinterpret_cast<const float4*>(A + r * lda + k);
@@ -56,25 +83,24 @@ __global__ __launch_bounds__(256) void round_a_kernel(const float* __restrict__ 
         o.y = pack_rn(v[2], v[3]);
         o.z = pack_rn(v[4], v[5]);
         o.w = pack_rn(v[6], v[7]);
-        *reinterpret_cast<uint4*>(A16 + r * kp + k) = o;
+        *reinterpret_cast<uint4*>(A16 + packed_offset(r, kb, c, nkb)) = o;
     }
 }
 
-// ----------------------------------------------------------------------------
-// B -> B16t: B16t[n][k] = rn(B[k][n]), Np x Kp, zero outside.  A 64 x 64 block
-// of B is read along n (coalesced), rounded, transposed through LDS and written
-// along k (coalesced).
-// ----------------------------------------------------------------------------
+// B -> packed B16t (B transposed: Np rows of K, zero outside).  A 64 (k) x 64
+// (n) block of B is read along n (coalesced), rounded, transposed through LDS
+// and written as 64 packed rows of one depth block.
 constexpr int kTB = 64;        // transpose block edge
 constexpr int kTS = kTB + 2;   // LDS row stride in halves
 
 template <bool VEC>
-__global__ __launch_bounds__(256) void round_bt_kernel(const float* __restrict__ B, int64_t ldb,
-                                                       int K, int N, uint16_t* __restrict__ B16t,
-                                                       int64_t kp) {
+__global__ __launch_bounds__(256) void pack_bt_kernel(const float* __restrict__ B, int64_t ldb,
+                                                      int K, int N, uint16_t* __restrict__ B16t,
+                                                      int64_t nkb) {
     __shared__ uint16_t t[kTB * kTS];   // t[k][n]
     const int n0 = blockIdx.x * kTB;
-    const int k0 = blockIdx.y * kTB;
+    const int kb = blockIdx.y;
+    const int k0 = kb * kPackK;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -102,94 +128,162 @@ __global__ __launch_bounds__(256) void round_bt_kernel(const float* __restrict__
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int u = tid + j * 256;
-        const int n = u >> 3, k8 = (u & 7) * 8;
+        const int n = u >> 3, c = u & 7;
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            w[e] = static_cast<uint32_t>(t[(k8 + 2 * e) * kTS + n]) |
-                   (static_cast<uint32_t>(t[(k8 + 2 * e + 1) * kTS + n]) << 16);
-        *reinterpret_cast<uint4*>(B16t + (int64_t)(n0 + n) * kp + k0 + k8) =
+            w[e] = static_cast<uint32_t>(t[(c * 8 + 2 * e) * kTS + n]) |
+                   (static_cast<uint32_t>(t[(c * 8 + 2 * e + 1) * kTS + n]) << 16);
+        *reinterpret_cast<uint4*>(B16t + packed_offset(n0 + n, kb, c, nkb)) =
             make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
 // ----------------------------------------------------------------------------
-// The f16 GEMM on the rounded operands.
+// The f16 GEMM on the packed operands.
+//
+// A stage holds the BK = 64 deep panels of A (BM rows) and B (BN columns) of
+// one k step, in the packed image: 128 bytes per row.  The stages form a ring
+// of ST buffers in LDS, filled by direct global->LDS loads
+// (global_load_lds_dwordx4): one wave instruction copies one contiguous
+// kilobyte of a packed block into the same kilobyte of the stage without
+// passing through registers.  Fills run ST-1 panels ahead of the panel being
+// multiplied.  The stages are separate LDS arrays and the K loop is unrolled
+// by ST, so every read names its stage statically and the compiler does not
+// wait for fills of other stages before it.
 // ----------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN>
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const f16x8 lds_f16x8;
+typedef __attribute__((address_space(1))) void glb_void;
+
+template <int BM, int BN, int ST, int WM, int WN>
 struct F16Shape {
-    static constexpr int NT = WM * WN * 64;
+    static constexpr int BK = kPackK;
+    static constexpr int NW = WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 32, FN = TN / 32;
-    static constexpr int KH = BK / 2;        // k per lane half per panel
-    static constexpr int KSTEPS = BK / 16;   // matrix instructions per block per panel
-    // Both panels are stored n- or m-major with k contiguous; rows padded by 8
-    // halves so the 16-byte reads of 16 consecutive rows hit distinct banks.
-    static constexpr int AS = BK + 8;
-    static constexpr int A_STAGE = BM * AS;
-    static constexpr int B_STAGE = BN * AS;
-    static constexpr int LDS_HALVES = 2 * (A_STAGE + B_STAGE);
-    static constexpr int A_LD = BM * BK / 8 / NT;   // 16-byte loads per thread per panel
-    static constexpr int B_LD = BN * BK / 8 / NT;
+    static constexpr int ROW = BK * 2;              // bytes per panel row
+    static constexpr int KSTEPS = BK / 16;          // matrix instructions per block per panel
+    static constexpr int A_BYTES = BM * ROW;
+    static constexpr int STAGE = (BM + BN) * ROW;   // bytes per stage
+    static constexpr int A_INS = A_BYTES / 1024 / NW;   // fill instructions per wave per stage
+    static constexpr int B_INS = BN * ROW / 1024 / NW;
+    static constexpr int FILLS = A_INS + B_INS;
+    static_assert(ST >= 2 && ST <= 3, "2 or 3 stages");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(BK % 16 == 0 && 64 % BK == 0, "BK must be 16, 32 or 64");
-    static_assert(256 % BM == 0 && 256 % BN == 0, "operands are padded to multiples of 256");
-    static_assert((BM * BK / 8) % NT == 0 && (BN * BK / 8) % NT == 0, "panel split");
-    static_assert(LDS_HALVES * 2 <= 160 * 1024, "LDS budget of one CU");
+    static_assert(A_INS * 1024 * NW == A_BYTES && B_INS * 1024 * NW == BN * ROW,
+                  "kilobytes of a panel split evenly over the waves");
+    static_assert(kPackRows % BM == 0 && kPackRows % BN == 0, "tiles nest in packed blocks");
+    static_assert(ST * STAGE <= 160 * 1024, "LDS budget of one CU");
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int GM, bool MASKED>
+// s_waitcnt vmcnt(N) with N a compile-time constant (at most 63).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for the panel ring.  __syncthreads() carries a workgroup
+// fence, for which the compiler waits until every outstanding global->LDS fill
+// of the wave has landed; that would cap the ring at one panel in flight.  The
+// ring orders its fills itself (wait_vmcnt before this barrier), so a bare
+// s_barrier suffices; this wave's own LDS reads are drained first so no other
+// wave can refill a stage under them, and the asm is a compiler memory barrier.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int BM, int BN, int ST, int WM, int WN, int GM, bool RS, bool MASKED>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
-    using S = F16Shape<BM, BN, BK, WM, WN>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_HALVES];
-    uint16_t* const As = smem;                    // [2][BM][AS]
-    uint16_t* const Bs = smem + 2 * S::A_STAGE;   // [2][BN][AS]
+    using S = F16Shape<BM, BN, ST, WM, WN>;
+    __shared__ __attribute__((aligned(1024))) unsigned char ring0[S::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char ring1[S::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char ring2[ST > 2 ? S::STAGE : 16];
 
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / WN, wc = wave % WN;
     const int h = lane >> 5;
     const int r32 = lane & 31;
+    const int64_t nkb = p.nkb;
 
-    const int64_t kp = p.kp;
-    const uint16_t* __restrict__ A = p.A16 + (int64_t)m0 * kp;
-    const uint16_t* __restrict__ B = p.B16t + (int64_t)n0 * kp;
+    // Panel kt of this tile's A rows is the BM-row slice at row m0 % 256 of
+    // packed block (m0 / 256, kt); consecutive kt are consecutive blocks.
+    const unsigned char* a_src =
+        reinterpret_cast<const unsigned char*>(
+            p.A16 + ((int64_t)(m0 / kPackRows) * nkb * kPackRows + m0 % kPackRows) * kPackK) +
+        wave * 1024 + lane * 16;
+    const unsigned char* b_src =
+        reinterpret_cast<const unsigned char*>(
+            p.B16t + ((int64_t)(n0 / kPackRows) * nkb * kPackRows + n0 % kPackRows) * kPackK) +
+        wave * 1024 + lane * 16;
+    constexpr int64_t kBlockBytes = int64_t{kBlockElems} * 2;
 
-    uint4 ra[S::A_LD], rb[S::B_LD];
-    auto load_panels = [&](int k0) {
+    auto fill = [&](unsigned char* stage, int kt) __attribute__((always_inline)) {
+        lds_u8* as = (lds_u8*)(stage) + wave * 1024;
+        lds_u8* bs = (lds_u8*)(stage) + S::A_BYTES + wave * 1024;
+        const int64_t kofs = (int64_t)kt * kBlockBytes;
 #pragma unroll
-        for (int i = 0; i < S::A_LD; ++i) {
-            const int idx = tid + i * S::NT;
-            const int r = idx / (BK / 8), c = (idx % (BK / 8)) * 8;
-            ra[i] = *reinterpret_cast<const uint4*>(A + (int64_t)r * kp + k0 + c);
-        }
+        for (int j = 0; j < S::A_INS; ++j)
+            __builtin_amdgcn_global_load_lds((glb_void*)(a_src + kofs + j * S::NW * 1024),
+                                             reinterpret_cast<lds_void*>(as + j * S::NW * 1024),
+                                             16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < S::B_LD; ++i) {
-            const int idx = tid + i * S::NT;
-            const int r = idx / (BK / 8), c = (idx % (BK / 8)) * 8;
-            rb[i] = *reinterpret_cast<const uint4*>(B + (int64_t)r * kp + k0 + c);
-        }
+        for (int j = 0; j < S::B_INS; ++j)
+            __builtin_amdgcn_global_load_lds((glb_void*)(b_src + kofs + j * S::NW * 1024),
+                                             reinterpret_cast<lds_void*>(bs + j * S::NW * 1024),
+                                             16, 0, 0);
     };
-    auto store_panels = [&](int stage) {
-        uint16_t* as = As + stage * S::A_STAGE;
-        uint16_t* bs = Bs + stage * S::B_STAGE;
+
+    // Register-staged fills (RS): the same kilobytes go through VGPRs --
+    // load(kt) issues the 16-byte global loads of panel kt into `stg`,
+    // commit(stage) writes them to the same offsets of the stage.
+    u32x4 stg[RS ? S::FILLS : 1];
+    auto load = [&](int kt) __attribute__((always_inline)) {
+        const int64_t kofs = (int64_t)kt * kBlockBytes;
 #pragma unroll
-        for (int i = 0; i < S::A_LD; ++i) {
-            const int idx = tid + i * S::NT;
-            const int r = idx / (BK / 8), c = (idx % (BK / 8)) * 8;
-            *reinterpret_cast<uint4*>(as + r * S::AS + c) = ra[i];
-        }
+        for (int j = 0; j < S::A_INS; ++j)
+            stg[j] = *reinterpret_cast<const u32x4*>(a_src + kofs + j * S::NW * 1024);
 #pragma unroll
-        for (int i = 0; i < S::B_LD; ++i) {
-            const int idx = tid + i * S::NT;
-            const int r = idx / (BK / 8), c = (idx % (BK / 8)) * 8;
-            *reinterpret_cast<uint4*>(bs + r * S::AS + c) = rb[i];
-        }
+        for (int j = 0; j < S::B_INS; ++j)
+            stg[S::A_INS + j] = *reinterpret_cast<const u32x4*>(b_src + kofs + j * S::NW * 1024);
+    };
+    auto commit = [&](unsigned char* stage) __attribute__((always_inline)) {
+        lds_u8* as = (lds_u8*)(stage) + wave * 1024 + lane * 16;
+        lds_u8* bs = (lds_u8*)(stage) + S::A_BYTES + wave * 1024 + lane * 16;
+#pragma unroll
+        for (int j = 0; j < S::A_INS; ++j)
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(as + j * S::NW * 1024) =
+                stg[j];
+#pragma unroll
+        for (int j = 0; j < S::B_INS; ++j)
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(bs + j * S::NW * 1024) =
+                stg[S::A_INS + j];
+    };
+
+    // Fragment reads: lane (h, r32) of block i reads row r32 of the block at
+    // logical chunk h*4 + ks (lane half h feeds k in [32h, 32h+32) of the
+    // panel, 8 per instruction, to A and B alike).  Blocks start at multiples
+    // of 32 rows (of 16 within the packed block), so the row's swizzle key is
+    // swz(r32).
+    const int sw = swz(r32);
+    const int a_row0 = (wr * S::TM + r32) * S::ROW;
+    const int b_row0 = S::A_BYTES + (wc * S::TN + r32) * S::ROW;
+    auto frags = [&](const unsigned char* stage, int ks, f16x8 (&a)[S::FM], f16x8 (&b)[S::FN]) {
+        const lds_u8* base = (const lds_u8*)(stage);
+        const int chunk = ((h * S::KSTEPS + ks) ^ sw) << 4;
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i)
+            a[i] = *reinterpret_cast<lds_f16x8*>(base + a_row0 + i * 32 * S::ROW + chunk);
+#pragma unroll
+        for (int j = 0; j < S::FN; ++j)
+            b[j] = *reinterpret_cast<lds_f16x8*>(base + b_row0 + j * 32 * S::ROW + chunk);
     };
 
     f32x16 acc[S::FM][S::FN];
@@ -200,87 +294,142 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    const int nk = static_cast<int>(kp / BK);
-    load_panels(0);
-    store_panels(0);
-    __syncthreads();
+    constexpr int NMF = S::FM * S::FN;
+    constexpr int NFR = S::FM + S::FN;
+    const int nk = static_cast<int>(nkb);
+    auto stage_of = [&](int i) __attribute__((always_inline)) -> unsigned char* { return i == 0 ? ring0 : i == 1 ? ring1 : ring2; };
 
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) load_panels((kt + 1) * BK);
-
-        // Lane half h feeds k in [h*KH, (h+1)*KH) of the panel, 8 per
-        // instruction, to A and B alike.
-        const uint16_t* as = As + cur * S::A_STAGE;
-        const uint16_t* bs = Bs + cur * S::B_STAGE;
+    // Multiply one stage: fragments of step ks+1 are read while step ks
+    // multiplies.
+    auto multiply = [&](const unsigned char* cur) __attribute__((always_inline)) {
+        f16x8 a[2][S::FM], b[2][S::FN];
+        frags(cur, 0, a[0], b[0]);
 #pragma unroll
         for (int ks = 0; ks < S::KSTEPS; ++ks) {
-            f16x8 a[S::FM], b[S::FN];
-#pragma unroll
-            for (int i = 0; i < S::FM; ++i)
-                a[i] = *reinterpret_cast<const f16x8*>(
-                    as + (wr * S::TM + i * 32 + r32) * S::AS + h * S::KH + ks * 8);
-#pragma unroll
-            for (int j = 0; j < S::FN; ++j)
-                b[j] = *reinterpret_cast<const f16x8*>(
-                    bs + (wc * S::TN + j * 32 + r32) * S::AS + h * S::KH + ks * 8);
+            if (ks + 1 < S::KSTEPS) frags(cur, ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
 #pragma unroll
             for (int i = 0; i < S::FM; ++i)
 #pragma unroll
                 for (int j = 0; j < S::FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0,
-                                                                        0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks & 1][i], b[ks & 1][j],
+                                                                        acc[i][j], 0, 0, 0);
         }
+    };
 
-        if (more) store_panels(cur ^ 1);
-        __syncthreads();
-    }
+    if constexpr (!RS) {
+        // One panel: fill panel kt+ST-1 into the stage freed by panel kt-1
+        // (every wave passed the barrier after reading it), multiply the
+        // current stage, then wait until panel kt+1 has landed -- the fills of
+        // later panels may stay in flight -- and for every other wave.  Fills
+        // past the last panel reload the last panel into a stage nobody reads
+        // again, so the wave's count of outstanding fills is the same at every
+        // step and the step is one basic block, which the group barriers below
+        // order: fills, then the first fragments, then one matrix instruction
+        // after another with the next step's fragment reads between them.
+        auto panel = [&](const unsigned char* cur, unsigned char* freed, int kt_fill) __attribute__((always_inline)) {
+            fill(freed, kt_fill);
+            multiply(cur);
+            __builtin_amdgcn_sched_group_barrier(0x020, S::FILLS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NFR, 0);
+#pragma unroll
+            for (int ks = 0; ks < S::KSTEPS; ++ks) {
+#pragma unroll
+                for (int m = 0; m < NMF; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (ks + 1 < S::KSTEPS && m < NFR)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+            wait_vmcnt<(ST - 2) * S::FILLS>();
+            ring_barrier();
+        };
 
-    // Epilogue: C = alpha*acc + beta*C; element e of lane l of a 32x32 block
-    // is row 8*(e/4) + 4*(l/32) + e%4, column l%32.
-    const float alpha = p.alpha, beta = p.beta;
+        // Prologue: panels 0 .. ST-2 into stages 0 .. ST-2, then wait for panel 0.
 #pragma unroll
-    for (int i = 0; i < S::FM; ++i) {
+        for (int i = 0; i + 1 < ST; ++i) fill(stage_of(i), min(i, nk - 1));
+        wait_vmcnt<(ST - 2) * S::FILLS>();
+        ring_barrier();
+
+        for (int kt = 0; kt < nk; kt += ST) {
 #pragma unroll
-        for (int j = 0; j < S::FN; ++j) {
-            const int col = n0 + wc * S::TN + j * 32 + r32;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wr * S::TM + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (MASKED && (row >= p.M || col >= p.N)) continue;
-                float* c = p.C + (int64_t)row * p.ldc + col;
-                float v = alpha * acc[i][j][e];
-                if (beta != 0.f) v += beta * *c;
-                *c = v;
+            for (int u = 0; u < ST; ++u) {
+                if (u == 0 || kt + u < nk)
+                    panel(stage_of(u), stage_of((u + ST - 1) % ST), min(kt + u + ST - 1, nk - 1));
             }
         }
+        wait_vmcnt<0>();   // no fill may still be landing in LDS when the workgroup ends
+    } else {
+        // Register-staged ring of two stages: while stage kt%2 is multiplied,
+        // panel kt+1 (loaded into registers during the previous panel) is
+        // written to the other stage, then the loads of panel kt+2 are issued.
+        // The group barriers spread the writes and the loads between the
+        // matrix instructions of the second and third step.
+        static_assert(ST == 2, "the register-staged ring has two stages");
+        auto panel = [&](const unsigned char* cur, unsigned char* next, int kt_load) __attribute__((always_inline)) {
+            multiply(cur);
+            commit(next);
+            load(kt_load);
+            __builtin_amdgcn_sched_group_barrier(0x100, NFR, 0);
+#pragma unroll
+            for (int ks = 0; ks < S::KSTEPS; ++ks) {
+#pragma unroll
+                for (int m = 0; m < NMF; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (ks + 1 < S::KSTEPS && m < NFR)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if (ks == 1 && m < S::FILLS) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                    if (ks == 2 && m < S::FILLS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+            }
+            ring_barrier();
+        };
+        load(0);
+        commit(ring0);
+        load(min(1, nk - 1));
+        ring_barrier();
+        for (int kt = 0; kt < nk; kt += 2) {
+            panel(ring0, ring1, min(kt + 2, nk - 1));
+            if (kt + 1 < nk) panel(ring1, ring0, min(kt + 3, nk - 1));
+        }
+        wait_vmcnt<0>();
     }
+
+    // Epilogue: C = alpha*acc + beta*C over this wave's part of the tile.
+    store_tile<S::FM, S::FN, MASKED>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N,
+                                     p.alpha, p.beta, lane);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int GM>
+template <int BM, int BN, int ST, int WM, int WN, int GM, bool RS>
 hipError_t launch_f16(const F16Args& a, hipStream_t s) {
     const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
     const bool masked = (a.M % BM) != 0 || (a.N % BN) != 0;
     if (masked)
-        gemm_f16_kernel<BM, BN, BK, WM, WN, GM, true><<<grid, block, 0, s>>>(a);
+        gemm_f16_kernel<BM, BN, ST, WM, WN, GM, RS, true><<<grid, block, 0, s>>>(a);
     else
-        gemm_f16_kernel<BM, BN, BK, WM, WN, GM, false><<<grid, block, 0, s>>>(a);
+        gemm_f16_kernel<BM, BN, ST, WM, WN, GM, RS, false><<<grid, block, 0, s>>>(a);
     return hipGetLastError();
 }
 
-#define F16_INSTANCE(BM, BN, BK, WM, WN, GM) \
-    {{GEMM355_MODE_F16R, BM, BN, BK, WM, WN, GM}, &launch_f16<BM, BN, BK, WM, WN, GM>}
+// ST = 1 in a configuration names the register-staged two-stage ring (one
+// stage in LDS is written from registers while the other is multiplied).
+#define F16_INSTANCE(BM, BN, ST, WM, WN, GM) \
+    {{GEMM355_MODE_F16R, BM, BN, kPackK, ST, WM, WN, GM},       \
+     &launch_f16<BM, BN, (ST == 1 ? 2 : ST), WM, WN, GM, ST == 1>}
 
 const F16Instance kF16Instances[] = {
-    F16_INSTANCE(256, 256, 64, 2, 2, 8),
-    F16_INSTANCE(256, 256, 32, 2, 2, 8),
-    F16_INSTANCE(256, 128, 64, 2, 2, 8),
-    F16_INSTANCE(128, 256, 64, 2, 2, 8),
-    F16_INSTANCE(128, 128, 64, 2, 2, 8),
-    F16_INSTANCE(128, 128, 32, 2, 2, 8),
-    F16_INSTANCE(128, 64, 64, 2, 2, 8),
-    F16_INSTANCE(64, 64, 64, 2, 2, 8),
+    F16_INSTANCE(256, 256, 1, 4, 2, 8),
+    F16_INSTANCE(256, 256, 1, 2, 4, 8),
+    F16_INSTANCE(128, 128, 1, 2, 2, 8),
+    F16_INSTANCE(256, 256, 2, 4, 2, 8),
+    F16_INSTANCE(256, 256, 2, 2, 4, 8),
+    F16_INSTANCE(256, 128, 3, 2, 2, 8),
+    F16_INSTANCE(256, 128, 2, 2, 2, 8),
+    F16_INSTANCE(256, 128, 3, 4, 2, 8),
+    F16_INSTANCE(128, 256, 3, 2, 2, 8),
+    F16_INSTANCE(128, 128, 2, 2, 2, 8),
+    F16_INSTANCE(128, 128, 3, 2, 2, 8),
+    F16_INSTANCE(128, 64, 2, 2, 2, 8),
+    F16_INSTANCE(64, 64, 2, 2, 2, 8),
 };
 
 }  // namespace
@@ -290,27 +439,29 @@ const F16Instance* f16_instances(int* count) {
     return kF16Instances;
 }
 
-hipError_t launch_round_a(const float* A, int64_t lda, int M, int K, uint16_t* A16, int64_t mp,
-                          int64_t kp, hipStream_t s) {
-    const int64_t units = mp * (kp / 8);
+hipError_t launch_pack_a(const float* A, int64_t lda, int M, int K, uint16_t* A16, int64_t mp,
+                         int64_t kp, hipStream_t s) {
+    const int64_t nkb = kp / kPackK;
+    const int64_t units = mp * nkb * 8;
     const int64_t want = (units + 255) / 256;
     const int blocks = static_cast<int>(want < 8192 ? (want > 0 ? want : 1) : 8192);
     const bool vec = (lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(A) & 15) == 0);
     if (vec)
-        round_a_kernel<true><<<blocks, 256, 0, s>>>(A, lda, M, K, A16, mp, kp);
+        pack_a_kernel<true><<<blocks, 256, 0, s>>>(A, lda, M, K, A16, mp, nkb);
     else
-        round_a_kernel<false><<<blocks, 256, 0, s>>>(A, lda, M, K, A16, mp, kp);
+        pack_a_kernel<false><<<blocks, 256, 0, s>>>(A, lda, M, K, A16, mp, nkb);
     return hipGetLastError();
 }
 
-hipError_t launch_round_bt(const float* B, int64_t ldb, int K, int N, uint16_t* B16t, int64_t np,
-                           int64_t kp, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>(np / kTB), static_cast<unsigned>(kp / kTB));
+hipError_t launch_pack_bt(const float* B, int64_t ldb, int K, int N, uint16_t* B16t, int64_t np,
+                          int64_t kp, hipStream_t s) {
+    const int64_t nkb = kp / kPackK;
+    const dim3 grid(static_cast<unsigned>(np / kTB), static_cast<unsigned>(nkb));
     const bool vec = (ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(B) & 15) == 0);
     if (vec)
-        round_bt_kernel<true><<<grid, 256, 0, s>>>(B, ldb, K, N, B16t, kp);
+        pack_bt_kernel<true><<<grid, 256, 0, s>>>(B, ldb, K, N, B16t, nkb);
     else
-        round_bt_kernel<false><<<grid, 256, 0, s>>>(B, ldb, K, N, B16t, kp);
+        pack_bt_kernel<false><<<grid, 256, 0, s>>>(B, ldb, K, N, B16t, nkb);
     return hipGetLastError();
 }
 

@@ -18,7 +18,6 @@
 namespace g355 {
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <int BM, int BN, int BK, int WM, int WN>
 struct F32Shape {
@@ -198,26 +197,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_kernel(F32Args p) {
         __syncthreads();
     }
 
-    // Epilogue: C = alpha*acc + beta*C over the tile.  Accumulator element e
-    // of lane l in a 32x32 block sits at row 8*(e/4) + 4*(l/32) + e%4 and
-    // column l%32.
-    const float alpha = p.alpha, beta = p.beta;
-#pragma unroll
-    for (int i = 0; i < S::FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < S::FN; ++j) {
-            const int col = n0 + wc * S::TN + j * 32 + r32;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wr * S::TM + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (MASKED && (row >= p.M || col >= p.N)) continue;
-                float* c = p.C + (int64_t)row * p.ldc + col;
-                float v = alpha * acc[i][j][e];
-                if (beta != 0.f) v += beta * *c;
-                *c = v;
-            }
-        }
-    }
+    // Epilogue: C = alpha*acc + beta*C over this wave's part of the tile.
+    store_tile<S::FM, S::FN, MASKED>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N,
+                                     p.alpha, p.beta, lane);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int GM>
@@ -234,7 +216,7 @@ hipError_t launch_f32(const F32Args& a, F32Variant v, hipStream_t s) {
 }
 
 #define F32_INSTANCE(BM, BN, BK, WM, WN, GM) \
-    {{GEMM355_MODE_F32, BM, BN, BK, WM, WN, GM}, &launch_f32<BM, BN, BK, WM, WN, GM>}
+    {{GEMM355_MODE_F32, BM, BN, BK, 2, WM, WN, GM}, &launch_f32<BM, BN, BK, WM, WN, GM>}
 
 const F32Instance kF32Instances[] = {
     F32_INSTANCE(256, 256, 16, 2, 2, 8),

@@ -11,15 +11,16 @@
 namespace g355 {
 
 // One tile configuration: the workgroup owns a BM x BN tile of C and walks K
-// in steps of BK; its WM x WN wavefronts of 64 lanes split the tile; GM tile
-// rows form one group of the rasterised tile order (L2 reuse).
+// in steps of BK through a ring of ST shared-memory stages; its WM x WN
+// wavefronts of 64 lanes split the tile; GM tile rows form one group of the
+// rasterised tile order (L2 reuse).
 struct TileConfig {
     int mode;  // GEMM355_MODE_*
-    int bm, bn, bk, wm, wn, gm;
+    int bm, bn, bk, st, wm, wn, gm;
     int threads() const { return wm * wn * 64; }
     bool operator==(const TileConfig& o) const {
-        return mode == o.mode && bm == o.bm && bn == o.bn && bk == o.bk && wm == o.wm &&
-               wn == o.wn && gm == o.gm;
+        return mode == o.mode && bm == o.bm && bn == o.bn && bk == o.bk && st == o.st &&
+               wm == o.wm && wn == o.wn && gm == o.gm;
     }
 };
 
@@ -34,14 +35,15 @@ struct F32Args {
     int tiles_m, tiles_n;
 };
 
-// Arguments of one f16 GEMM launch on rounded, padded operands:
-// A16 is Mp x Kp (row-major), B16t is Np x Kp (B transposed), both binary16,
-// zero outside the logical M x K and K x N.
+// Arguments of one f16 GEMM launch on rounded, packed operands: A16 holds A
+// and B16t holds B transposed (k contiguous), both binary16 in the packed
+// panel-major layout of gemm_f16r.hip (blocks of 256 rows x 64 k, zero outside
+// the logical matrices).
 struct F16Args {
     const uint16_t* A16;
     const uint16_t* B16t;
     float* C;
-    int64_t kp;   // padded K, row stride of A16 and B16t (elements)
+    int64_t nkb;  // depth blocks of 64 (padded K / 64)
     int64_t ldc;
     int M, N;
     float alpha, beta;
@@ -70,11 +72,12 @@ struct F16Instance {
 const F32Instance* f32_instances(int* count);
 const F16Instance* f16_instances(int* count);
 
-// Rounding/padding passes of the f16r mode.
-hipError_t launch_round_a(const float* A, int64_t lda, int M, int K, uint16_t* A16, int64_t mp,
-                          int64_t kp, hipStream_t s);
-hipError_t launch_round_bt(const float* B, int64_t ldb, int K, int N, uint16_t* B16t,
-                           int64_t np, int64_t kp, hipStream_t s);
+// Rounding and packing passes of the f16r mode: A (M x K) into Mp x Kp and B
+// (K x N) transposed into Np x Kp, Mp, Np multiples of 256, Kp of 64.
+hipError_t launch_pack_a(const float* A, int64_t lda, int M, int K, uint16_t* A16, int64_t mp,
+                         int64_t kp, hipStream_t s);
+hipError_t launch_pack_bt(const float* B, int64_t ldb, int K, int N, uint16_t* B16t,
+                          int64_t np, int64_t kp, hipStream_t s);
 
 // C = beta*C (beta == 0: C = 0 without reading it).
 hipError_t launch_scale_c(float* C, int64_t ldc, int M, int N, float beta, hipStream_t s);
@@ -103,6 +106,53 @@ __device__ __forceinline__ void tile_of_block(int g, int G, int tiles_m, int til
     const int in_group = gg - group * per_group;
     tm = first_m + in_group % rows;
     tn = in_group / rows;
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Epilogue shared by the GEMM kernels (phobos docs, "gemm, f32", section "The
+// epilogue": C = alpha*acc + beta*C over the tile, C read in place).  A wave
+// holds FM x FN accumulator blocks of 32x32; element e of lane l in a block
+// sits at row 8*(e/4) + 4*(l/32) + e%4, column l%32, so one store instruction
+// writes two 128-byte row segments.  beta == 0 never reads C.  Otherwise the
+// 16 loads of a block are issued together before its 16 stores, so a wave
+// waits for memory once per block rather than once per element.
+// MASKED guards every access with row < M and col < N.
+template <int FM, int FN, bool MASKED>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* __restrict__ C,
+                                           int64_t ldc, int row0, int col0, int M, int N,
+                                           float alpha, float beta, int lane) {
+    const int h = lane >> 5, r32 = lane & 31;
+    auto row_of = [&](int i, int e) { return row0 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3); };
+    auto col_of = [&](int j) { return col0 + j * 32 + r32; };
+    auto inside = [&](int row, int col) { return !MASKED || (row < M && col < N); };
+    if (beta == 0.f) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = row_of(i, e), col = col_of(j);
+                    if (inside(row, col)) C[(int64_t)row * ldc + col] = alpha * acc[i][j][e];
+                }
+        return;
+    }
+#pragma unroll
+    for (int b = 0; b < FM * FN; ++b) {
+        const int i = b / FN, j = b % FN;
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = row_of(i, e), col = col_of(j);
+            v[e] = inside(row, col) ? C[(int64_t)row * ldc + col] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = row_of(i, e), col = col_of(j);
+            if (inside(row, col)) C[(int64_t)row * ldc + col] = alpha * acc[i][j][e] + beta * v[e];
+        }
+    }
 }
 
 }  // namespace g355

@@ -103,7 +103,7 @@ int gemm355_tune(int mode, int64_t M, int64_t N, int64_t K,
 
 /*
  * The tile configuration a call with these arguments would use, written as
- * "BM=.. BN=.. BK=.. WM=.. WN=.. GM=.." plus " source=pin|tuned|heuristic"
+ * "BM=.. BN=.. BK=.. ST=.. WM=.. WN=.. GM=.." plus " source=pin|tuned|heuristic"
  * into buf (NUL-terminated, at most len bytes).  Host only; no GPU call.
  */
 int gemm355_get_config(int mode, int64_t M, int64_t N, int64_t K,
@@ -114,7 +114,7 @@ int gemm355_get_config(int mode, int64_t M, int64_t N, int64_t K,
  * Pin one tile configuration for every later call of `mode`, skipping the
  * search (phobos docs, "gemm, f32", section "Tuning", the pinned run).
  * Grammar: space-separated KEY=VALUE with keys BM|TILE_M, BN|TILE_N,
- * BK|TILE_K, WM, WN, GM; omitted keys take the first compiled instance that
+ * BK|TILE_K, ST|STAGES, WM, WN, GM; omitted keys take the first compiled instance that
  * matches the given ones.  NULL or "" clears the pin.  The environment
  * variables GEMM355_CONFIG_F32 / GEMM355_CONFIG_F16R set the initial pin.
  * Returns 0 or GEMM355_ERR_CONFIG (the pin is then unchanged).  Host only.
