@@ -56,7 +56,22 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB copy kernel (byte-counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="DIR", default=None,
+                    help="write a markdown summary of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="summarise FETCH_SIZE / WRITE_SIZE runs into an HBM-traffic table")
+    ap.add_argument("--out", default=None, help="output file of the --summarize-* modes")
+    ap.add_argument("--cmd", default="", help="the command that produced the profile")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, args.cmd)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.out, args.cmd)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -79,6 +94,9 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), "
         f"{props.multi_processor_count} CUs; libgemm355 {g.version()}")
+
+    if args.calibrate_copy:
+        copy_calibration(g, torch, dev)
 
     # ------------------------------------------------------------------ roofs
     roofs = {}
@@ -282,6 +300,10 @@ def bench_workload(g, torch, dev, w, args, roofs, workload_inputs, sample_indice
         "parity_max_ratio_sampled": ratio,
         "roofline": roof,
     }
+    tr = committed_traffic(w.mode, w.name, tile)
+    if tr is not None:
+        roof["traffic"] = tr["traffic_bytes_per_launch"]
+        roof["traffic_source"] = tr["source"]
     key = "mfma_f32_tflops" if w.mode == "f32" else "mfma_f16r_tflops"
     if roofs.get(key):
         res["frac_of_measured_roof"] = round(tflops_med / roofs[key], 4)
@@ -296,21 +318,29 @@ def bench_workload(g, torch, dev, w, args, roofs, workload_inputs, sample_indice
 
 
 def cpu_baseline(w, target_seconds, workload_inputs):
-    """The oracle as it stands, on a band of output rows of the same workload,
-    sized to about target_seconds of CPU time; throughput in TFLOP/s."""
+    """The oracle as it stands, timed on the host cores over the whole workload
+    when that fits in ~30 s, else over a band of output rows sized to about
+    target_seconds; throughput in TFLOP/s (2*rows*N*K / t)."""
     import oracle
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
     os.environ["OMP_NUM_THREADS"] = str(threads)
     A, B, C = workload_inputs(w)
-    probe = 16
-    t0 = time.perf_counter()
-    oracle.check(w.mode, A, B, C, w.alpha, w.beta, C, rows=(0, probe))
-    t_probe = time.perf_counter() - t0
-    rows = int(min(w.M, max(probe, probe * target_seconds / max(t_probe, 1e-3))))
-    t0 = time.perf_counter()
-    oracle.check(w.mode, A, B, C, w.alpha, w.beta, C, rows=(0, rows))
-    t = time.perf_counter() - t0
+
+    def timed(rows):
+        t0 = time.perf_counter()
+        oracle.check(w.mode, A, B, C, w.alpha, w.beta, C, rows=(0, rows))
+        return time.perf_counter() - t0
+
+    # per-row cost from two probes (the widening of A and B is a fixed cost)
+    t16, t64 = timed(16), timed(64)
+    per_row = max((t64 - t16) / 48.0, 1e-6)
+    fixed = max(t16 - 16 * per_row, 0.0)
+    if fixed + per_row * w.M <= 30.0:
+        rows = w.M
+    else:
+        rows = int(min(w.M, max(64, (target_seconds - fixed) / per_row)))
+    t = timed(rows)
     flops = 2.0 * rows * w.N * w.K
     cpu_model = ""
     try:
@@ -321,11 +351,163 @@ def cpu_baseline(w, target_seconds, workload_inputs):
                     break
     except OSError:
         pass
+    what = "the whole workload" if rows == w.M else f"{rows} of {w.M} output rows"
     res = {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-           "sample": f"{rows} of {w.M} output rows of {w.name} (float64 triple loop incl. "
-                     f"operand widening), {t:.1f} s", "cpu": cpu_model}
+           "sample": f"{what} of {w.name} (float64 triple loop incl. operand widening and "
+                     f"the bound), {t:.1f} s", "cpu": cpu_model}
     log(f"cpu baseline: {res['value'] * 1e3:.2f} GFLOP/s on {threads} threads ({res['sample']})")
     return res
+
+
+# ---------------------------------------------------------------------------
+# Profile evidence: byte-counter calibration, committed summaries.
+# ---------------------------------------------------------------------------
+COPY_BYTES = 256 << 20          # one direction of the calibration copy
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "f32": ["gemm_tiled_amd/csrc/gemm_f32.hip", "gemm_tiled_amd/csrc/internal.hpp"],
+    "f16r": ["gemm_tiled_amd/csrc/gemm_f16r.hip", "gemm_tiled_amd/csrc/internal.hpp"],
+}
+
+
+def copy_calibration(g, torch, dev):
+    """A plain copy of COPY_BYTES (read) into COPY_BYTES (write), 5 launches:
+    the kernel whose FETCH_SIZE / WRITE_SIZE calibrate the byte counters."""
+    import ctypes
+    n = COPY_BYTES // 4
+    src = torch.ones(n, device=dev, dtype=torch.float32)
+    dst = torch.empty(n, device=dev, dtype=torch.float32)
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(5):
+        st = g.lib().gemm355_copy_f32(ctypes.c_void_p(src.data_ptr()),
+                                      ctypes.c_void_p(dst.data_ptr()), n, sp)
+        if st != 0:
+            raise g.Gemm355Error(st, "gemm355_copy_f32")
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"calibration copy: 5 x {COPY_BYTES >> 20} MiB")
+
+
+def source_hash(mode):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[mode]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(mode, workload, tile):
+    """HBM bytes per launch from the committed counter summary of this
+    workload and tile, if it was taken on the current kernel sources; else None."""
+    import glob
+    import re
+    for path in glob.glob(os.path.join(PROFILES, "*traffic*.md")):
+        text = open(path).read()
+        m = re.search(r"```json\n(.*?)\n```", text, re.S)
+        if not m:
+            continue
+        try:
+            d = json.loads(m.group(1))
+        except ValueError:
+            continue
+        if d.get("workload") != workload or d.get("mode") != mode:
+            continue
+        if d.get("tile", "").split(" source=")[0] != tile.split(" source=")[0]:
+            continue
+        if d.get("source_hash") != source_hash(mode):
+            return None          # the kernel changed since the counters were taken
+        return {"traffic_bytes_per_launch": d["traffic_bytes_per_launch"],
+                "source": os.path.relpath(path, ROOT)}
+    return None
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_trace(directory, out, cmd):
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    if not rows:
+        raise SystemExit(f"no kernel_stats.csv under {directory}")
+    lines = ["# Kernel trace summary", "", "Command:", "", "```", cmd, "```", "",
+             "| kernel | calls | average us | min us | max us | share of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        name = r["Name"].replace("|", "/")
+        lines.append(f"| `{name[:150]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    text = "\n".join(lines) + "\n"
+    _write(out, text)
+
+
+def _per_dispatch(rows, counter):
+    import collections
+    per = collections.defaultdict(float)
+    names = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+        names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    by_kernel = collections.defaultdict(list)
+    for d, v in per.items():
+        by_kernel[names[d]].append(v)
+    return {k: (sum(v) / len(v), len(v)) for k, v in by_kernel.items()}
+
+
+def summarize_pmc(fetch_dir, write_dir, out, cmd):
+    fetch = _per_dispatch(_csv_rows(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    write = _per_dispatch(_csv_rows(write_dir, "counter_collection.csv"), "WRITE_SIZE")
+    copy_f = [v[0] for k, v in fetch.items() if "copy_f32_kernel" in k]
+    copy_w = [v[0] for k, v in write.items() if "copy_f32_kernel" in k]
+    if not copy_f or not copy_w:
+        raise SystemExit("no calibration copy kernel in the counter runs (--calibrate-copy)")
+    kib = COPY_BYTES / 1024
+    f_fac, w_fac = kib / copy_f[0], kib / copy_w[0]
+    lines = ["# HBM traffic per launch (FETCH_SIZE, WRITE_SIZE)", "", "Commands:", "", "```",
+             cmd, "```", "",
+             f"Calibration: the plain copy of {COPY_BYTES >> 20} MiB read FETCH_SIZE "
+             f"{copy_f[0]:.0f} KiB and WRITE_SIZE {copy_w[0]:.0f} KiB per launch against "
+             f"{kib:.0f} KiB moved each way, so the factors are {f_fac:.4f} (fetch) and "
+             f"{w_fac:.4f} (write).", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | calibrated bytes |",
+             "|---|---:|---:|---:|"]
+    best = None
+    for k in sorted(set(fetch) | set(write)):
+        fb = fetch.get(k, (0.0, 0))[0] * f_fac * 1024
+        wb = write.get(k, (0.0, 0))[0] * w_fac * 1024
+        lines.append(f"| `{k[:150]}` | {fetch.get(k, (0.0, 0))[0]:.0f} | "
+                     f"{write.get(k, (0.0, 0))[0]:.0f} | {fb + wb:.4g} |")
+        calls = fetch.get(k, (0.0, 0))[1]
+        if "gemm_" in k and (best is None or calls > best[2]):
+            best = (k, fb + wb, calls)
+    text = "\n".join(lines) + "\n"
+    if best is not None:
+        mode = "f32" if "gemm_f32" in best[0] else "f16r"
+        meta = {"workload": os.environ.get("TRAFFIC_WORKLOAD", ""),
+                "tile": os.environ.get("TRAFFIC_TILE", ""), "mode": mode, "kernel": best[0],
+                "traffic_bytes_per_launch": best[1], "source_hash": source_hash(mode),
+                "fetch_factor": f_fac, "write_factor": w_fac}
+        text += "\nMachine-readable (read by bench.py while the kernel sources are unchanged):\n"
+        text += "\n```json\n" + json.dumps(meta) + "\n```\n"
+    _write(out, text)
+
+
+def _write(out, text):
+    if out:
+        with open(out, "w") as f:
+            f.write(text)
+    print(text)
 
 
 if __name__ == "__main__":
