@@ -14,6 +14,8 @@
 // edge rule of the Matrix Multiplication lab's tiled kernels (out-of-range
 // operands load as 0), so the GEMM loads carry no masks; only its epilogue is
 // masked.
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace g355 {
@@ -22,6 +24,7 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Two f32 -> two binary16, round to nearest even (a C++ conversion to
 // _Float16 is correctly rounded in the default rounding mode), packed.
@@ -70,8 +73,10 @@ __global__ __launch_bounds__(256) void pack_a_kernel(const float* __restrict__ A
         const int k = kb * kPackK + c * 8;
         float v[8];
         if (r < M && VEC && k + 7 < K) {
-            const float4* src = reinterpret_cast<const float4*>(A + r * lda + k);
-            const float4 x = src[0], y = src[1];
+            // the f32 source is read once: non-temporal, so it does not evict
+            // the packed operands from the caches
+            const f32x4* src = reinterpret_cast<const f32x4*>(A + r * lda + k);
+            const f32x4 x = __builtin_nontemporal_load(src), y = __builtin_nontemporal_load(src + 1);
             v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
             v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
         } else {
@@ -109,7 +114,8 @@ __global__ __launch_bounds__(256) void pack_bt_kernel(const float* __restrict__ 
         const int k = k0 + kr, n = n0 + nq;
         float v[4];
         if (k < K && VEC && n + 3 < N) {
-            const float4 x = *reinterpret_cast<const float4*>(B + (int64_t)k * ldb + n);
+            const f32x4 x =
+                __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(B + (int64_t)k * ldb + n));
             v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
         } else {
 #pragma unroll
@@ -286,13 +292,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
             b[j] = *reinterpret_cast<lds_f16x8*>(base + b_row0 + j * 32 * S::ROW + chunk);
     };
 
+    // The accumulators get their first value from the first matrix
+    // instruction of the first panel, with an inline-constant zero as its
+    // addend, so they are born in the accumulation registers instead of being
+    // zeroed in general registers and copied over.
     f32x16 acc[S::FM][S::FN];
-#pragma unroll
-    for (int i = 0; i < S::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < S::FN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    using first_panel = std::true_type;
+    using later_panel = std::false_type;
 
     constexpr int NMF = S::FM * S::FN;
     constexpr int NFR = S::FM + S::FN;
@@ -301,9 +307,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
 
     // Multiply one stage: fragments of step ks+1 are read while step ks
     // multiplies.
-    auto multiply = [&](const unsigned char* cur) __attribute__((always_inline)) {
+    auto multiply = [&](const unsigned char* cur, auto first) __attribute__((always_inline)) {
         f16x8 a[2][S::FM], b[2][S::FN];
         frags(cur, 0, a[0], b[0]);
+        const f32x16 zero = {};
 #pragma unroll
         for (int ks = 0; ks < S::KSTEPS; ++ks) {
             if (ks + 1 < S::KSTEPS) frags(cur, ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
@@ -311,8 +318,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
             for (int i = 0; i < S::FM; ++i)
 #pragma unroll
                 for (int j = 0; j < S::FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks & 1][i], b[ks & 1][j],
-                                                                        acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        a[ks & 1][i], b[ks & 1][j],
+                        (decltype(first)::value && ks == 0) ? zero : acc[i][j], 0, 0, 0);
         }
     };
 
@@ -326,9 +334,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
         // step and the step is one basic block, which the group barriers below
         // order: fills, then the first fragments, then one matrix instruction
         // after another with the next step's fragment reads between them.
-        auto panel = [&](const unsigned char* cur, unsigned char* freed, int kt_fill) __attribute__((always_inline)) {
+        auto panel = [&](const unsigned char* cur, unsigned char* freed, int kt_fill,
+                         auto first) __attribute__((always_inline)) {
             fill(freed, kt_fill);
-            multiply(cur);
+            multiply(cur, first);
             __builtin_amdgcn_sched_group_barrier(0x020, S::FILLS, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, NFR, 0);
 #pragma unroll
@@ -350,11 +359,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
         wait_vmcnt<(ST - 2) * S::FILLS>();
         ring_barrier();
 
-        for (int kt = 0; kt < nk; kt += ST) {
+        panel(stage_of(0), stage_of(ST - 1), min(ST - 1, nk - 1), first_panel{});
+#pragma unroll
+        for (int u = 1; u < ST; ++u)
+            if (u < nk) panel(stage_of(u), stage_of(u - 1), min(u + ST - 1, nk - 1), later_panel{});
+        for (int kt = ST; kt < nk; kt += ST) {
 #pragma unroll
             for (int u = 0; u < ST; ++u) {
                 if (u == 0 || kt + u < nk)
-                    panel(stage_of(u), stage_of((u + ST - 1) % ST), min(kt + u + ST - 1, nk - 1));
+                    panel(stage_of(u), stage_of((u + ST - 1) % ST), min(kt + u + ST - 1, nk - 1),
+                          later_panel{});
             }
         }
         wait_vmcnt<0>();   // no fill may still be landing in LDS when the workgroup ends
@@ -365,8 +379,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
         // The group barriers spread the writes and the loads between the
         // matrix instructions of the second and third step.
         static_assert(ST == 2, "the register-staged ring has two stages");
-        auto panel = [&](const unsigned char* cur, unsigned char* next, int kt_load) __attribute__((always_inline)) {
-            multiply(cur);
+        auto panel = [&](const unsigned char* cur, unsigned char* next, int kt_load,
+                         auto first) __attribute__((always_inline)) {
+            multiply(cur, first);
             commit(next);
             load(kt_load);
             __builtin_amdgcn_sched_group_barrier(0x100, NFR, 0);
@@ -387,9 +402,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
         commit(ring0);
         load(min(1, nk - 1));
         ring_barrier();
-        for (int kt = 0; kt < nk; kt += 2) {
-            panel(ring0, ring1, min(kt + 2, nk - 1));
-            if (kt + 1 < nk) panel(ring1, ring0, min(kt + 3, nk - 1));
+        panel(ring0, ring1, min(2, nk - 1), first_panel{});
+        if (1 < nk) panel(ring1, ring0, min(3, nk - 1), later_panel{});
+        for (int kt = 2; kt < nk; kt += 2) {
+            panel(ring0, ring1, min(kt + 2, nk - 1), later_panel{});
+            if (kt + 1 < nk) panel(ring1, ring0, min(kt + 3, nk - 1), later_panel{});
         }
         wait_vmcnt<0>();
     }

@@ -116,7 +116,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // sits at row 8*(e/4) + 4*(l/32) + e%4, column l%32, so one store instruction
 // writes two 128-byte row segments.  beta == 0 never reads C.  Otherwise the
 // 16 loads of a block are issued together before its 16 stores, so a wave
-// waits for memory once per block rather than once per element.
+// waits for memory once per block rather than once per element.  C is touched
+// exactly once, so its loads and stores are non-temporal: they do not evict
+// the operand panels other workgroups are still re-reading from the caches.
 // MASKED guards every access with row < M and col < N.
 template <int FM, int FN, bool MASKED>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* __restrict__ C,
@@ -134,7 +136,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int row = row_of(i, e), col = col_of(j);
-                    if (inside(row, col)) C[(int64_t)row * ldc + col] = alpha * acc[i][j][e];
+                    if (inside(row, col))
+                        __builtin_nontemporal_store(alpha * acc[i][j][e], C + (int64_t)row * ldc + col);
                 }
         return;
     }
@@ -145,13 +148,18 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int row = row_of(i, e), col = col_of(j);
-            v[e] = inside(row, col) ? C[(int64_t)row * ldc + col] : 0.f;
+            v[e] = inside(row, col) ? __builtin_nontemporal_load(C + (int64_t)row * ldc + col) : 0.f;
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int row = row_of(i, e), col = col_of(j);
-            if (inside(row, col)) C[(int64_t)row * ldc + col] = alpha * acc[i][j][e] + beta * v[e];
+            if (inside(row, col))
+                __builtin_nontemporal_store(alpha * acc[i][j][e] + beta * v[e],
+                                            C + (int64_t)row * ldc + col);
         }
+        // keep the compiler from hoisting every block's loads above the first
+        // stores (that would need FM*FN*16 live registers)
+        asm volatile("" ::: "memory");
     }
 }
 
