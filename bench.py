@@ -286,7 +286,7 @@ def bench_workload(g, torch, dev, w, args, roofs, workload_inputs, sample_indice
     roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": None,
             "kernel": "gemm_f32_kernel" if w.mode == "f32" else
-            "pack_a + pack_bt + gemm_f16_kernel (whole call)",
+            "pack_kernel + gemm_f16_kernel (whole call)",
             "per_launch_flops": flops}
     res = {
         "mode": w.mode, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,

@@ -310,9 +310,8 @@ int launch_with(const TileConfig& cfg, int64_t M, int64_t N, int64_t K, float al
         if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
         uint16_t* A16 = static_cast<uint16_t*>(ws);
         uint16_t* B16t = A16 + mp * kp;
-        e = launch_pack_a(A, lda, static_cast<int>(M), static_cast<int>(K), A16, mp, kp, s);
-        if (e != hipSuccess) return status_of(e);
-        e = launch_pack_bt(B, ldb, static_cast<int>(K), static_cast<int>(N), B16t, np, kp, s);
+        e = launch_pack(A, lda, B, ldb, static_cast<int>(M), static_cast<int>(N),
+                        static_cast<int>(K), A16, B16t, mp, np, kp, s);
         if (e != hipSuccess) return status_of(e);
         F16Args a{A16, B16t, C, kp / 64, ldc, static_cast<int>(M), static_cast<int>(N), alpha,
                   beta, tiles_m, tiles_n};

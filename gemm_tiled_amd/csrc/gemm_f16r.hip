@@ -56,40 +56,54 @@ __device__ __forceinline__ int64_t packed_offset(int64_t x, int kb, int c, int64
     return ((xb * nkb + kb) * kPackRows + r) * kPackK + ((c ^ swz(r)) << 3);
 }
 
-// A -> packed A16 (Mp rows, zero outside M x K).  One thread converts 8
-// consecutive k of one row (16 bytes out); consecutive threads walk along the
-// row of A, so the f32 reads stream.
+// Both operands are packed by one launch: the first a_blocks workgroups pack A,
+// the rest pack B^T, so the two streams share the memory system and the tail
+// of one overlaps the start of the other.
+struct PackArgs {
+    const float* A;
+    int64_t lda;
+    const float* B;
+    int64_t ldb;
+    uint16_t* A16;
+    uint16_t* B16t;
+    int64_t mp, nkb;
+    int M, N, K;
+    int a_blocks;   // workgroups packing A
+    int b_cols;     // Np / 64
+};
+
+constexpr int kAUnitsPerThread = 8;
+constexpr int kAUnitsPerBlock = 256 * kAUnitsPerThread;
+
+// A -> packed A16 (Mp rows, zero outside M x K).  One unit converts 8
+// consecutive k of one row (16 bytes out); consecutive threads take
+// consecutive units along the row of A, so the f32 reads stream.
 template <bool VEC>
-__global__ __launch_bounds__(256) void pack_a_kernel(const float* __restrict__ A, int64_t lda,
-                                                     int M, int K, uint16_t* __restrict__ A16,
-                                                     int64_t mp, int64_t nkb) {
-    const int64_t units = mp * nkb * 8;
-    for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < units;
-         u += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t q = u >> 3;
-        const int c = static_cast<int>(u & 7);
-        const int64_t r = q / nkb;
-        const int kb = static_cast<int>(q - r * nkb);
-        const int k = kb * kPackK + c * 8;
-        float v[8];
-        if (r < M && VEC && k + 7 < K) {
-            // the f32 source is read once: non-temporal, so it does not evict
-            // the packed operands from the caches
-            const f32x4* src = reinterpret_cast<const f32x4*>(A + r * lda + k);
-            const f32x4 x = __builtin_nontemporal_load(src), y = __builtin_nontemporal_load(src + 1);
-            v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-            v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
-        } else {
+__device__ __forceinline__ void pack_a_unit(const PackArgs& p, int64_t u) {
+    const int64_t q = u >> 3;
+    const int c = static_cast<int>(u & 7);
+    const int64_t r = q / p.nkb;
+    const int kb = static_cast<int>(q - r * p.nkb);
+    const int k = kb * kPackK + c * 8;
+    const float* A = p.A;
+    float v[8];
+    if (r < p.M && VEC && k + 7 < p.K) {
+        // the f32 source is read once: non-temporal, so it does not evict the
+        // packed operands from the caches
+        const f32x4* src = reinterpret_cast<const f32x4*>(A + r * p.lda + k);
+        const f32x4 x = __builtin_nontemporal_load(src), y = __builtin_nontemporal_load(src + 1);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+    } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (r < M && k + e < K) ? A[r * lda + k + e] : 0.f;
-        }
-        uint4 o;
-        o.x = pack_rn(v[0], v[1]);
-        o.y = pack_rn(v[2], v[3]);
-        o.z = pack_rn(v[4], v[5]);
-        o.w = pack_rn(v[6], v[7]);
-        *reinterpret_cast<uint4*>(A16 + packed_offset(r, kb, c, nkb)) = o;
+        for (int e = 0; e < 8; ++e) v[e] = (r < p.M && k + e < p.K) ? A[r * p.lda + k + e] : 0.f;
     }
+    uint4 o;
+    o.x = pack_rn(v[0], v[1]);
+    o.y = pack_rn(v[2], v[3]);
+    o.z = pack_rn(v[4], v[5]);
+    o.w = pack_rn(v[6], v[7]);
+    *reinterpret_cast<uint4*>(p.A16 + packed_offset(r, kb, c, p.nkb)) = o;
 }
 
 // B -> packed B16t (B transposed: Np rows of K, zero outside).  A 64 (k) x 64
@@ -99,28 +113,25 @@ constexpr int kTB = 64;        // transpose block edge
 constexpr int kTS = kTB + 2;   // LDS row stride in halves
 
 template <bool VEC>
-__global__ __launch_bounds__(256) void pack_bt_kernel(const float* __restrict__ B, int64_t ldb,
-                                                      int K, int N, uint16_t* __restrict__ B16t,
-                                                      int64_t nkb) {
-    __shared__ uint16_t t[kTB * kTS];   // t[k][n]
-    const int n0 = blockIdx.x * kTB;
-    const int kb = blockIdx.y;
+__device__ __forceinline__ void pack_bt_block(const PackArgs& p, int bx, int kb, uint16_t* t) {
+    const int n0 = bx * kTB;
     const int k0 = kb * kPackK;
     const int tid = threadIdx.x;
+    const float* B = p.B;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int idx = tid + i * 256;
         const int kr = idx >> 4, nq = (idx & 15) * 4;
         const int k = k0 + kr, n = n0 + nq;
         float v[4];
-        if (k < K && VEC && n + 3 < N) {
+        if (k < p.K && VEC && n + 3 < p.N) {
             const f32x4 x =
-                __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(B + (int64_t)k * ldb + n));
+                __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(B + (int64_t)k * p.ldb + n));
             v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                v[e] = (k < K && n + e < N) ? B[(int64_t)k * ldb + n + e] : 0.f;
+                v[e] = (k < p.K && n + e < p.N) ? B[(int64_t)k * p.ldb + n + e] : 0.f;
         }
         const uint32_t p01 = pack_rn(v[0], v[1]);
         const uint32_t p23 = pack_rn(v[2], v[3]);
@@ -140,8 +151,25 @@ __global__ __launch_bounds__(256) void pack_bt_kernel(const float* __restrict__ 
         for (int e = 0; e < 4; ++e)
             w[e] = static_cast<uint32_t>(t[(c * 8 + 2 * e) * kTS + n]) |
                    (static_cast<uint32_t>(t[(c * 8 + 2 * e + 1) * kTS + n]) << 16);
-        *reinterpret_cast<uint4*>(B16t + packed_offset(n0 + n, kb, c, nkb)) =
+        *reinterpret_cast<uint4*>(p.B16t + packed_offset(n0 + n, kb, c, p.nkb)) =
             make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+template <bool VA, bool VB>
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs p) {
+    __shared__ uint16_t t[kTB * kTS];   // transpose tile of the B blocks
+    if (static_cast<int>(blockIdx.x) < p.a_blocks) {
+        const int64_t units = p.mp * p.nkb * 8;
+        const int64_t u0 = (int64_t)blockIdx.x * kAUnitsPerBlock + threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < kAUnitsPerThread; ++i) {
+            const int64_t u = u0 + i * 256;
+            if (u < units) pack_a_unit<VA>(p, u);
+        }
+    } else {
+        const int b = static_cast<int>(blockIdx.x) - p.a_blocks;
+        pack_bt_block<VB>(p, b % p.b_cols, b / p.b_cols, t);
     }
 }
 
@@ -376,8 +404,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
         // Register-staged ring of two stages: while stage kt%2 is multiplied,
         // panel kt+1 (loaded into registers during the previous panel) is
         // written to the other stage, then the loads of panel kt+2 are issued.
-        // The group barriers spread the writes and the loads between the
-        // matrix instructions of the second and third step.
+        // The group barriers spread the writes between the matrix
+        // instructions of the first step and the loads between those of the
+        // second, so the loads have most of a panel to arrive.
         static_assert(ST == 2, "the register-staged ring has two stages");
         auto panel = [&](const unsigned char* cur, unsigned char* next, int kt_load,
                          auto first) __attribute__((always_inline)) {
@@ -392,8 +421,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     if (ks + 1 < S::KSTEPS && m < NFR)
                         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    if (ks == 1 && m < S::FILLS) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-                    if (ks == 2 && m < S::FILLS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    if (ks == 0 && m < S::FILLS) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                    if (ks == 1 && m < S::FILLS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 }
             }
             ring_barrier();
@@ -456,29 +485,33 @@ const F16Instance* f16_instances(int* count) {
     return kF16Instances;
 }
 
-hipError_t launch_pack_a(const float* A, int64_t lda, int M, int K, uint16_t* A16, int64_t mp,
-                         int64_t kp, hipStream_t s) {
-    const int64_t nkb = kp / kPackK;
-    const int64_t units = mp * nkb * 8;
-    const int64_t want = (units + 255) / 256;
-    const int blocks = static_cast<int>(want < 8192 ? (want > 0 ? want : 1) : 8192);
-    const bool vec = (lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(A) & 15) == 0);
-    if (vec)
-        pack_a_kernel<true><<<blocks, 256, 0, s>>>(A, lda, M, K, A16, mp, nkb);
-    else
-        pack_a_kernel<false><<<blocks, 256, 0, s>>>(A, lda, M, K, A16, mp, nkb);
-    return hipGetLastError();
-}
-
-hipError_t launch_pack_bt(const float* B, int64_t ldb, int K, int N, uint16_t* B16t, int64_t np,
-                          int64_t kp, hipStream_t s) {
-    const int64_t nkb = kp / kPackK;
-    const dim3 grid(static_cast<unsigned>(np / kTB), static_cast<unsigned>(nkb));
-    const bool vec = (ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(B) & 15) == 0);
-    if (vec)
-        pack_bt_kernel<true><<<grid, 256, 0, s>>>(B, ldb, K, N, B16t, nkb);
-    else
-        pack_bt_kernel<false><<<grid, 256, 0, s>>>(B, ldb, K, N, B16t, nkb);
+hipError_t launch_pack(const float* A, int64_t lda, const float* B, int64_t ldb, int M, int N,
+                       int K, uint16_t* A16, uint16_t* B16t, int64_t mp, int64_t np, int64_t kp,
+                       hipStream_t s) {
+    PackArgs p;
+    p.A = A;
+    p.lda = lda;
+    p.B = B;
+    p.ldb = ldb;
+    p.A16 = A16;
+    p.B16t = B16t;
+    p.mp = mp;
+    p.nkb = kp / kPackK;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    const int64_t a_units = mp * p.nkb * 8;
+    p.a_blocks = static_cast<int>((a_units + kAUnitsPerBlock - 1) / kAUnitsPerBlock);
+    p.b_cols = static_cast<int>(np / kTB);
+    const int64_t blocks = p.a_blocks + (int64_t)p.b_cols * p.nkb;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const bool va = (lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(A) & 15) == 0);
+    const bool vb = (ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(B) & 15) == 0);
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (va && vb) pack_kernel<true, true><<<grid, 256, 0, s>>>(p);
+    else if (va) pack_kernel<true, false><<<grid, 256, 0, s>>>(p);
+    else if (vb) pack_kernel<false, true><<<grid, 256, 0, s>>>(p);
+    else pack_kernel<false, false><<<grid, 256, 0, s>>>(p);
     return hipGetLastError();
 }
 

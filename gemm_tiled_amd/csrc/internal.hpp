@@ -72,12 +72,12 @@ struct F16Instance {
 const F32Instance* f32_instances(int* count);
 const F16Instance* f16_instances(int* count);
 
-// Rounding and packing passes of the f16r mode: A (M x K) into Mp x Kp and B
-// (K x N) transposed into Np x Kp, Mp, Np multiples of 256, Kp of 64.
-hipError_t launch_pack_a(const float* A, int64_t lda, int M, int K, uint16_t* A16, int64_t mp,
-                         int64_t kp, hipStream_t s);
-hipError_t launch_pack_bt(const float* B, int64_t ldb, int K, int N, uint16_t* B16t,
-                          int64_t np, int64_t kp, hipStream_t s);
+// Rounding and packing pass of the f16r mode: A (M x K) into Mp x Kp and B
+// (K x N) transposed into Np x Kp, Mp, Np multiples of 256, Kp of 64, in one
+// launch.
+hipError_t launch_pack(const float* A, int64_t lda, const float* B, int64_t ldb, int M, int N,
+                       int K, uint16_t* A16, uint16_t* B16t, int64_t mp, int64_t np, int64_t kp,
+                       hipStream_t s);
 
 // C = beta*C (beta == 0: C = 0 without reading it).
 hipError_t launch_scale_c(float* C, int64_t ldc, int M, int N, float beta, hipStream_t s);
