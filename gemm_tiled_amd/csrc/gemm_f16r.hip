@@ -212,6 +212,11 @@ struct F16Shape {
     static_assert(ST * STAGE <= 160 * 1024, "LDS budget of one CU");
 };
 
+// Word 3 of a raw buffer descriptor on gfx9-family GPUs: 32-bit data format
+// (a zero format would make every load return zero), no swizzle, no index
+// stride; bounds are checked against the record count in bytes.
+constexpr int kBufferFlags = 0x00020000;
+
 // s_waitcnt vmcnt(N) with N a compile-time constant (at most 63).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -249,14 +254,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
 
     // Panel kt of this tile's A rows is the BM-row slice at row m0 % 256 of
     // packed block (m0 / 256, kt); consecutive kt are consecutive blocks.
-    const unsigned char* a_src =
-        reinterpret_cast<const unsigned char*>(
-            p.A16 + ((int64_t)(m0 / kPackRows) * nkb * kPackRows + m0 % kPackRows) * kPackK) +
-        wave * 1024 + lane * 16;
-    const unsigned char* b_src =
-        reinterpret_cast<const unsigned char*>(
-            p.B16t + ((int64_t)(n0 / kPackRows) * nkb * kPackRows + n0 % kPackRows) * kPackK) +
-        wave * 1024 + lane * 16;
+    const unsigned char* a_tile = reinterpret_cast<const unsigned char*>(
+        p.A16 + ((int64_t)(m0 / kPackRows) * nkb * kPackRows + m0 % kPackRows) * kPackK);
+    const unsigned char* b_tile = reinterpret_cast<const unsigned char*>(
+        p.B16t + ((int64_t)(n0 / kPackRows) * nkb * kPackRows + n0 % kPackRows) * kPackK);
+    const int lane_ofs = wave * 1024 + lane * 16;
+    const unsigned char* a_src = a_tile + lane_ofs;
+    const unsigned char* b_src = b_tile + lane_ofs;
     constexpr int64_t kBlockBytes = int64_t{kBlockElems} * 2;
 
     auto fill = [&](unsigned char* stage, int kt) __attribute__((always_inline)) {
@@ -276,17 +280,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
     };
 
     // Register-staged fills (RS): the same kilobytes go through VGPRs --
-    // load(kt) issues the 16-byte global loads of panel kt into `stg`,
-    // commit(stage) writes them to the same offsets of the stage.
+    // load(kt) issues the 16-byte loads of panel kt into `stg`, commit(stage)
+    // writes them to the same offsets of the stage.  The loads are buffer
+    // loads: the panel's base address lives in a scalar descriptor (rebuilt
+    // per panel with scalar arithmetic) whose record count is exactly the
+    // panel's bytes, and every load of the wave shares one 32-bit lane offset,
+    // so no 64-bit vector address is formed per load.
     u32x4 stg[RS ? S::FILLS : 1];
     auto load = [&](int kt) __attribute__((always_inline)) {
         const int64_t kofs = (int64_t)kt * kBlockBytes;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a_tile + kofs), (short)0, S::A_BYTES, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(b_tile + kofs), (short)0, BN * S::ROW, kBufferFlags);
 #pragma unroll
         for (int j = 0; j < S::A_INS; ++j)
-            stg[j] = *reinterpret_cast<const u32x4*>(a_src + kofs + j * S::NW * 1024);
+            stg[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, lane_ofs, j * S::NW * 1024, 0);
 #pragma unroll
         for (int j = 0; j < S::B_INS; ++j)
-            stg[S::A_INS + j] = *reinterpret_cast<const u32x4*>(b_src + kofs + j * S::NW * 1024);
+            stg[S::A_INS + j] = __builtin_amdgcn_raw_buffer_load_b128(rb, lane_ofs, j * S::NW * 1024, 0);
     };
     auto commit = [&](unsigned char* stage) __attribute__((always_inline)) {
         lds_u8* as = (lds_u8*)(stage) + wave * 1024 + lane * 16;
