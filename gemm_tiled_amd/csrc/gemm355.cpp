@@ -311,9 +311,9 @@ int launch_with(const TileConfig& cfg, int64_t M, int64_t N, int64_t K, float al
         uint16_t* A16 = static_cast<uint16_t*>(ws);
         uint16_t* B16t = A16 + mp * kp;
         e = launch_pack(A, lda, B, ldb, static_cast<int>(M), static_cast<int>(N),
-                        static_cast<int>(K), A16, B16t, mp, np, kp, s);
+                        static_cast<int>(K), A16, B16t, mp, np, kp, cfg.bk, s);
         if (e != hipSuccess) return status_of(e);
-        F16Args a{A16, B16t, C, kp / 64, ldc, static_cast<int>(M), static_cast<int>(N), alpha,
+        F16Args a{A16, B16t, C, kp / cfg.bk, ldc, static_cast<int>(M), static_cast<int>(N), alpha,
                   beta, tiles_m, tiles_n};
         if (log_debug())
             std::fprintf(stderr, "[gemm355] f16r M=%lld N=%lld K=%lld %s path=%s\n",

@@ -35,25 +35,34 @@ __device__ __forceinline__ uint32_t pack_rn(float lo, float hi) {
 
 // ----------------------------------------------------------------------------
 // Packed operand layout.  Rows (of A, or columns of B) are grouped in blocks
-// of kPackRows, depth in blocks of kPackK = 64.  Block (xb, kb) starts at
-// element ((xb * nkb) + kb) * kPackRows * kPackK.  Inside it, row r holds its
-// 64 values as 8 chunks of 8, logical chunk c at position c ^ swz(r):
-//   swz(r) = (r / 2) % 8.
+// of kPackRows, depth in blocks of D values (D = 64 or 32, the depth of the
+// panel the GEMM configuration multiplies from).  Block (xb, kb) starts at
+// element ((xb * nkb) + kb) * kPackRows * D.  Inside it, row r holds its D
+// values as D/8 chunks of 8, logical chunk c at position c ^ swz(r), where the
+// key runs through all D/8 chunk positions as r steps through the rows that
+// share one 256-byte window of shared-memory banks:
+//   D = 64 (128-byte rows, 2 per window): swz(r) = (r / 2) % 8
+//   D = 32 ( 64-byte rows, 4 per window): swz(r) = (r / 4) % 4
 // A 16-byte shared-memory read is served 16 lanes at a time from 64 four-byte
 // banks (256 bytes); the 16 lanes of a fragment read take 16 consecutive rows
-// at one logical chunk, and with 128-byte rows the swizzle puts them in 16
-// different 16-byte slots.
+// at one logical chunk, and the swizzle puts them in 16 different 16-byte
+// slots.
 // ----------------------------------------------------------------------------
 constexpr int kPackRows = 256;
-constexpr int kPackK = 64;
-constexpr int kBlockElems = kPackRows * kPackK;
+constexpr int kPackK = 64;   // the padded depth is a multiple of this for every D
 
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    static_assert(D == 32 || D == 64, "panel depth");
+    constexpr int cpr = D / 8;             // chunks per row
+    return (r / (16 / cpr)) % cpr;
+}
 
+template <int D>
 __device__ __forceinline__ int64_t packed_offset(int64_t x, int kb, int c, int64_t nkb) {
     const int64_t xb = x / kPackRows;
     const int r = static_cast<int>(x - xb * kPackRows);
-    return ((xb * nkb + kb) * kPackRows + r) * kPackK + ((c ^ swz(r)) << 3);
+    return ((xb * nkb + kb) * kPackRows + r) * D + ((c ^ swz<D>(r)) << 3);
 }
 
 // Both operands are packed by one launch: the first a_blocks workgroups pack A,
@@ -66,7 +75,7 @@ struct PackArgs {
     int64_t ldb;
     uint16_t* A16;
     uint16_t* B16t;
-    int64_t mp, nkb;
+    int64_t mp, nkb;   // padded rows of A; depth blocks of D
     int M, N, K;
     int a_blocks;   // workgroups packing A
     int b_cols;     // Np / 64
@@ -76,15 +85,21 @@ constexpr int kAUnitsPerThread = 8;
 constexpr int kAUnitsPerBlock = 256 * kAUnitsPerThread;
 
 // A -> packed A16 (Mp rows, zero outside M x K).  One unit converts 8
-// consecutive k of one row (16 bytes out); consecutive threads take
-// consecutive units along the row of A, so the f32 reads stream.
-template <bool VEC>
+// consecutive k of one row into one 16-byte chunk of the packed image, and
+// units are numbered in the order of the packed image, so consecutive threads
+// write consecutive bytes (whole 128-byte lines) and the D/8 threads of one
+// packed row read D consecutive floats of one row of A.
+template <int D, bool VEC>
 __device__ __forceinline__ void pack_a_unit(const PackArgs& p, int64_t u) {
-    const int64_t q = u >> 3;
-    const int c = static_cast<int>(u & 7);
-    const int64_t r = q / p.nkb;
-    const int kb = static_cast<int>(q - r * p.nkb);
-    const int k = kb * kPackK + c * 8;
+    constexpr int cpr = D / 8;
+    const int64_t q = u / cpr;                       // packed row: (block, row in block)
+    const int pc = static_cast<int>(u - q * cpr);    // physical chunk
+    const int64_t blk = q / kPackRows;
+    const int rin = static_cast<int>(q - blk * kPackRows);
+    const int64_t xb = blk / p.nkb;
+    const int kb = static_cast<int>(blk - xb * p.nkb);
+    const int64_t r = xb * kPackRows + rin;
+    const int k = kb * D + ((pc ^ swz<D>(rin)) << 3);
     const float* A = p.A;
     float v[8];
     if (r < p.M && VEC && k + 7 < p.K) {
@@ -103,19 +118,19 @@ __device__ __forceinline__ void pack_a_unit(const PackArgs& p, int64_t u) {
     o.y = pack_rn(v[2], v[3]);
     o.z = pack_rn(v[4], v[5]);
     o.w = pack_rn(v[6], v[7]);
-    *reinterpret_cast<uint4*>(p.A16 + packed_offset(r, kb, c, p.nkb)) = o;
+    *reinterpret_cast<uint4*>(p.A16 + u * 8) = o;
 }
 
 // B -> packed B16t (B transposed: Np rows of K, zero outside).  A 64 (k) x 64
 // (n) block of B is read along n (coalesced), rounded, transposed through LDS
-// and written as 64 packed rows of one depth block.
+// and written as 64 packed rows of the 64 / D depth blocks it covers.
 constexpr int kTB = 64;        // transpose block edge
 constexpr int kTS = kTB + 2;   // LDS row stride in halves
 
-template <bool VEC>
-__device__ __forceinline__ void pack_bt_block(const PackArgs& p, int bx, int kb, uint16_t* t) {
+template <int D, bool VEC>
+__device__ __forceinline__ void pack_bt_block(const PackArgs& p, int bx, int kt, uint16_t* t) {
     const int n0 = bx * kTB;
-    const int k0 = kb * kPackK;
+    const int k0 = kt * kTB;
     const int tid = threadIdx.x;
     const float* B = p.B;
 #pragma unroll
@@ -151,25 +166,27 @@ __device__ __forceinline__ void pack_bt_block(const PackArgs& p, int bx, int kb,
         for (int e = 0; e < 4; ++e)
             w[e] = static_cast<uint32_t>(t[(c * 8 + 2 * e) * kTS + n]) |
                    (static_cast<uint32_t>(t[(c * 8 + 2 * e + 1) * kTS + n]) << 16);
-        *reinterpret_cast<uint4*>(p.B16t + packed_offset(n0 + n, kb, c, p.nkb)) =
+        constexpr int cpr = D / 8;
+        const int kb = kt * (kTB / D) + c / cpr;
+        *reinterpret_cast<uint4*>(p.B16t + packed_offset<D>(n0 + n, kb, c % cpr, p.nkb)) =
             make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
-template <bool VA, bool VB>
+template <int D, bool VA, bool VB>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs p) {
     __shared__ uint16_t t[kTB * kTS];   // transpose tile of the B blocks
     if (static_cast<int>(blockIdx.x) < p.a_blocks) {
-        const int64_t units = p.mp * p.nkb * 8;
+        const int64_t units = p.mp * p.nkb * (D / 8);
         const int64_t u0 = (int64_t)blockIdx.x * kAUnitsPerBlock + threadIdx.x;
 #pragma unroll
         for (int i = 0; i < kAUnitsPerThread; ++i) {
             const int64_t u = u0 + i * 256;
-            if (u < units) pack_a_unit<VA>(p, u);
+            if (u < units) pack_a_unit<D, VA>(p, u);
         }
     } else {
         const int b = static_cast<int>(blockIdx.x) - p.a_blocks;
-        pack_bt_block<VB>(p, b % p.b_cols, b / p.b_cols, t);
+        pack_bt_block<D, VB>(p, b % p.b_cols, b / p.b_cols, t);
     }
 }
 
@@ -182,9 +199,8 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs p) {
 // (global_load_lds_dwordx4): one wave instruction copies one contiguous
 // kilobyte of a packed block into the same kilobyte of the stage without
 // passing through registers.  Fills run ST-1 panels ahead of the panel being
-// multiplied.  The stages are separate LDS arrays and the K loop is unrolled
-// by ST, so every read names its stage statically and the compiler does not
-// wait for fills of other stages before it.
+// multiplied.  The K loop is unrolled by ST, so every stage is named
+// statically (a fixed shared-memory address).
 // ----------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -234,6 +250,23 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// One direct global->LDS copy of a wave: lane l copies the 16 bytes at `src`
+// (its own address) to LDS byte address lds_base + 16 l.  Written as assembly
+// so that the compiler does not track these copies: it cannot always tell
+// which stage a shared-memory read may alias and would then wait for every
+// copy in flight before the read, which serialises the ring.  The ring waits
+// for its copies itself (wait_vmcnt before each barrier).  M0 carries the
+// wave's LDS base (the compiler writes it before the statement); the copy
+// needs one wait state after a write of M0.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds_base) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_base)
+                 : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* generic_lds_ptr) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)(generic_lds_ptr)));
+}
+
 template <int BM, int BN, int ST, int WM, int WN, int GM, bool RS, bool MASKED>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
     using S = F16Shape<BM, BN, ST, WM, WN>;
@@ -261,22 +294,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
     const int lane_ofs = wave * 1024 + lane * 16;
     const unsigned char* a_src = a_tile + lane_ofs;
     const unsigned char* b_src = b_tile + lane_ofs;
-    constexpr int64_t kBlockBytes = int64_t{kBlockElems} * 2;
+    constexpr int64_t kBlockBytes = int64_t{kPackRows} * kPackK * 2;
 
     auto fill = [&](unsigned char* stage, int kt) __attribute__((always_inline)) {
-        lds_u8* as = (lds_u8*)(stage) + wave * 1024;
-        lds_u8* bs = (lds_u8*)(stage) + S::A_BYTES + wave * 1024;
+        const uint32_t as = __builtin_amdgcn_readfirstlane(lds_addr(stage) + wave * 1024);
+        const uint32_t bs = as + S::A_BYTES;
         const int64_t kofs = (int64_t)kt * kBlockBytes;
 #pragma unroll
         for (int j = 0; j < S::A_INS; ++j)
-            __builtin_amdgcn_global_load_lds((glb_void*)(a_src + kofs + j * S::NW * 1024),
-                                             reinterpret_cast<lds_void*>(as + j * S::NW * 1024),
-                                             16, 0, 0);
+            lds_copy16(a_src + kofs + j * S::NW * 1024, as + j * S::NW * 1024);
 #pragma unroll
         for (int j = 0; j < S::B_INS; ++j)
-            __builtin_amdgcn_global_load_lds((glb_void*)(b_src + kofs + j * S::NW * 1024),
-                                             reinterpret_cast<lds_void*>(bs + j * S::NW * 1024),
-                                             16, 0, 0);
+            lds_copy16(b_src + kofs + j * S::NW * 1024, bs + j * S::NW * 1024);
     };
 
     // Register-staged fills (RS): the same kilobytes go through VGPRs --
@@ -318,7 +347,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
     // panel, 8 per instruction, to A and B alike).  Blocks start at multiples
     // of 32 rows (of 16 within the packed block), so the row's swizzle key is
     // swz(r32).
-    const int sw = swz(r32);
+    const int sw = swz<kPackK>(r32);
     const int a_row0 = (wr * S::TM + r32) * S::ROW;
     const int b_row0 = S::A_BYTES + (wc * S::TN + r32) * S::ROW;
     auto frags = [&](const unsigned char* stage, int ks, f16x8 (&a)[S::FM], f16x8 (&b)[S::FN]) {
@@ -457,6 +486,189 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
                                      p.alpha, p.beta, lane);
 }
 
+// ----------------------------------------------------------------------------
+// The half-depth ring.  Panels are BK = 32 deep (64 bytes per row, packed
+// blocks of depth 32), and NS of them (up to 5 x 32 KB for a 256 x 256 tile,
+// all of a CU's shared memory) form a ring filled direct from the packed
+// blocks, so NS - 1 panels -- up to two 64-deep steps of the full-depth ring
+// -- are in flight while one is multiplied; the fills then have several
+// microseconds to arrive from the memory-side cache when they miss in L2.
+//
+// One panel is two steps of 16 k.  The barrier sits between them: step 0
+// multiplies fragments read before it, while this wave reads the fragments of
+// step 1 and issues its fills of the panel NS - 1 ahead; then the wave waits
+// for its fills of the next panel, passes the barrier (every wave's fills of
+// the next panel have landed, every wave has read all of this one), and step 1
+// multiplies while the first fragments of the next panel are read.  So the
+// matrix instructions after a barrier never wait for shared memory.
+// ----------------------------------------------------------------------------
+template <int BM, int BN, int NS, int WM, int WN>
+struct RingShape {
+    static constexpr int BK = 32;
+    static constexpr int NW = WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int ROW = BK * 2;              // bytes per panel row
+    static constexpr int A_BYTES = BM * ROW;
+    static constexpr int STAGE = (BM + BN) * ROW;   // bytes per stage
+    static constexpr int A_INS = A_BYTES / 1024 / NW;   // fill instructions per wave per panel
+    static constexpr int B_INS = BN * ROW / 1024 / NW;
+    static constexpr int FILLS = A_INS + B_INS;
+    static_assert(NS >= 3 && NS <= 5, "3 to 5 stages");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(A_INS >= 1 && B_INS >= 1 && A_INS * 1024 * NW == A_BYTES &&
+                      B_INS * 1024 * NW == BN * ROW,
+                  "kilobytes of a panel split evenly over the waves");
+    static_assert(kPackRows % BM == 0 && kPackRows % BN == 0, "tiles nest in packed blocks");
+    static_assert(NS * STAGE <= 160 * 1024, "LDS budget of one CU");
+    static_assert((NS - 2) * FILLS < 64, "vmcnt range");
+};
+
+template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_f16_ring_kernel(F16Args p) {
+    using S = RingShape<BM, BN, NS, WM, WN>;
+    constexpr int D = S::BK;
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[S::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[S::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[S::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[NS > 3 ? S::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char st4[NS > 4 ? S::STAGE : 16];
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave / WN, wc = wave % WN;
+    const int h = lane >> 5;
+    const int r32 = lane & 31;
+    const int nk = static_cast<int>(p.nkb);
+
+    // Panel kt of this tile's A rows is the BM-row slice at row m0 % 256 of
+    // packed block (m0 / 256, kt); consecutive kt are consecutive blocks.
+    const int lane_ofs = wave * 1024 + lane * 16;
+    const unsigned char* a_src = reinterpret_cast<const unsigned char*>(
+        p.A16 + ((int64_t)(m0 / kPackRows) * p.nkb * kPackRows + m0 % kPackRows) * D) + lane_ofs;
+    const unsigned char* b_src = reinterpret_cast<const unsigned char*>(
+        p.B16t + ((int64_t)(n0 / kPackRows) * p.nkb * kPackRows + n0 % kPackRows) * D) + lane_ofs;
+    constexpr int64_t kBlockBytes = int64_t{kPackRows} * D * 2;
+
+    auto stage_of = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+        return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : i == 3 ? st3 : st4;
+    };
+    auto fill = [&](unsigned char* stage, int kt) __attribute__((always_inline)) {
+        const uint32_t as = __builtin_amdgcn_readfirstlane(lds_addr(stage) + wave * 1024);
+        const uint32_t bs = as + S::A_BYTES;
+        const int64_t kofs = (int64_t)kt * kBlockBytes;
+#pragma unroll
+        for (int j = 0; j < S::A_INS; ++j)
+            lds_copy16(a_src + kofs + j * S::NW * 1024, as + j * S::NW * 1024);
+#pragma unroll
+        for (int j = 0; j < S::B_INS; ++j)
+            lds_copy16(b_src + kofs + j * S::NW * 1024, bs + j * S::NW * 1024);
+    };
+
+    // Fragment reads: lane (h, r32) of block i reads row r32 of the block at
+    // logical chunk 2h + ks (lane half h feeds k in [16h, 16h + 16) of the
+    // panel, 8 per instruction, to A and B alike).  Blocks start at multiples
+    // of 32 rows, a whole number of swizzle periods, so the key is swz(r32).
+    const int sw = swz<D>(r32);
+    const int a_row0 = (wr * S::TM + r32) * S::ROW;
+    const int b_row0 = S::A_BYTES + (wc * S::TN + r32) * S::ROW;
+    f16x8 fa[2][S::FM], fb[2][S::FN];
+    auto frags = [&](const unsigned char* stage, int ks) __attribute__((always_inline)) {
+        const lds_u8* base = (const lds_u8*)(stage);
+        const int chunk = ((h * 2 + ks) ^ sw) << 4;
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i)
+            fa[ks][i] = *reinterpret_cast<lds_f16x8*>(base + a_row0 + i * 32 * S::ROW + chunk);
+#pragma unroll
+        for (int j = 0; j < S::FN; ++j)
+            fb[ks][j] = *reinterpret_cast<lds_f16x8*>(base + b_row0 + j * 32 * S::ROW + chunk);
+    };
+
+    // The accumulators get their first value from the first matrix
+    // instruction, with an inline-constant zero as its addend.
+    f32x16 acc[S::FM][S::FN];
+    constexpr int NMF = S::FM * S::FN;
+    constexpr int NFR = S::FM + S::FN;
+    auto mfmas = [&](int ks, auto first) __attribute__((always_inline)) {
+        const f32x16 zero = {};
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < S::FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    fa[ks][i], fb[ks][j], decltype(first)::value ? zero : acc[i][j], 0, 0, 0);
+    };
+    // one matrix instruction, then one fragment read, while reads remain
+    auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < NMF; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (m < NFR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+
+    // One panel in stage `cur`: fill panel kt_fill into `freed` (the stage of
+    // the previous panel, which every wave finished reading before the last
+    // barrier), step 0 beside the reads of step 1, wait for this wave's fills
+    // of the next panel, barrier, step 1 beside the first reads of `next`.
+    // Fills past the last panel reload the last panel into a stage nobody
+    // reads again, so the count of outstanding fills is the same every panel.
+    auto panel = [&](const unsigned char* cur, unsigned char* freed, const unsigned char* next,
+                     int kt_fill, auto first) __attribute__((always_inline)) {
+        fill(freed, kt_fill);
+        frags(cur, 1);
+        mfmas(0, first);
+        __builtin_amdgcn_sched_group_barrier(0x020, S::FILLS, 0);
+        interleave();
+        wait_vmcnt<(NS - 2) * S::FILLS>();
+        ring_barrier();
+        frags(next, 0);
+        mfmas(1, std::false_type{});
+        interleave();
+    };
+
+    // Prologue: panels 0 .. NS-2 into stages 0 .. NS-2; wait for panel 0.
+#pragma unroll
+    for (int i = 0; i + 1 < NS; ++i) fill(stage_of(i), min(i, nk - 1));
+    wait_vmcnt<(NS - 2) * S::FILLS>();
+    ring_barrier();
+    frags(stage_of(0), 0);
+
+    panel(stage_of(0), stage_of(NS - 1), stage_of(1), min(NS - 1, nk - 1), std::true_type{});
+#pragma unroll
+    for (int u = 1; u < NS; ++u)
+        if (u < nk)
+            panel(stage_of(u), stage_of(u - 1), stage_of((u + 1) % NS), min(u + NS - 1, nk - 1),
+                  std::false_type{});
+    for (int kt = NS; kt < nk; kt += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            if (u == 0 || kt + u < nk)
+                panel(stage_of(u), stage_of((u + NS - 1) % NS), stage_of((u + 1) % NS),
+                      min(kt + u + NS - 1, nk - 1), std::false_type{});
+        }
+    }
+    wait_vmcnt<0>();   // no fill may still be landing in LDS when the workgroup ends
+
+    store_tile<S::FM, S::FN, MASKED>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N,
+                                     p.alpha, p.beta, lane);
+}
+
+template <int BM, int BN, int NS, int WM, int WN, int GM>
+hipError_t launch_f16_ring(const F16Args& a, hipStream_t s) {
+    const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
+    const bool masked = (a.M % BM) != 0 || (a.N % BN) != 0;
+    if (masked)
+        gemm_f16_ring_kernel<BM, BN, NS, WM, WN, GM, true><<<grid, block, 0, s>>>(a);
+    else
+        gemm_f16_ring_kernel<BM, BN, NS, WM, WN, GM, false><<<grid, block, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int ST, int WM, int WN, int GM, bool RS>
 hipError_t launch_f16(const F16Args& a, hipStream_t s) {
     const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
@@ -474,7 +686,17 @@ hipError_t launch_f16(const F16Args& a, hipStream_t s) {
     {{GEMM355_MODE_F16R, BM, BN, kPackK, ST, WM, WN, GM},       \
      &launch_f16<BM, BN, (ST == 1 ? 2 : ST), WM, WN, GM, ST == 1>}
 
+// Half-depth ring configurations: BK = 32, ST = NS stages.
+#define F16_RING_INSTANCE(BM, BN, NS, WM, WN, GM) \
+    {{GEMM355_MODE_F16R, BM, BN, 32, NS, WM, WN, GM}, &launch_f16_ring<BM, BN, NS, WM, WN, GM>}
+
 const F16Instance kF16Instances[] = {
+    F16_RING_INSTANCE(256, 256, 5, 4, 2, 8),
+    F16_RING_INSTANCE(256, 256, 5, 2, 4, 8),
+    F16_RING_INSTANCE(256, 256, 4, 4, 2, 8),
+    F16_RING_INSTANCE(256, 256, 4, 2, 4, 8),
+    F16_RING_INSTANCE(256, 256, 5, 2, 2, 8),
+    F16_RING_INSTANCE(128, 128, 5, 2, 2, 8),
     F16_INSTANCE(256, 256, 1, 4, 2, 8),
     F16_INSTANCE(256, 256, 1, 2, 4, 8),
     F16_INSTANCE(128, 128, 1, 2, 2, 8),
@@ -499,7 +721,10 @@ const F16Instance* f16_instances(int* count) {
 
 hipError_t launch_pack(const float* A, int64_t lda, const float* B, int64_t ldb, int M, int N,
                        int K, uint16_t* A16, uint16_t* B16t, int64_t mp, int64_t np, int64_t kp,
-                       hipStream_t s) {
+                       int depth, hipStream_t s) {
+    if ((depth != 32 && depth != 64) || kp % kPackK != 0 || mp % kPackRows != 0 ||
+        np % kPackRows != 0)
+        return hipErrorInvalidValue;
     PackArgs p;
     p.A = A;
     p.lda = lda;
@@ -508,22 +733,27 @@ hipError_t launch_pack(const float* A, int64_t lda, const float* B, int64_t ldb,
     p.A16 = A16;
     p.B16t = B16t;
     p.mp = mp;
-    p.nkb = kp / kPackK;
+    p.nkb = kp / depth;
     p.M = M;
     p.N = N;
     p.K = K;
-    const int64_t a_units = mp * p.nkb * 8;
+    const int64_t a_units = mp * (kp / 8);
     p.a_blocks = static_cast<int>((a_units + kAUnitsPerBlock - 1) / kAUnitsPerBlock);
     p.b_cols = static_cast<int>(np / kTB);
-    const int64_t blocks = p.a_blocks + (int64_t)p.b_cols * p.nkb;
+    const int64_t blocks = p.a_blocks + (int64_t)p.b_cols * (kp / kTB);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool va = (lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(A) & 15) == 0);
     const bool vb = (ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(B) & 15) == 0);
     const dim3 grid(static_cast<unsigned>(blocks));
-    if (va && vb) pack_kernel<true, true><<<grid, 256, 0, s>>>(p);
-    else if (va) pack_kernel<true, false><<<grid, 256, 0, s>>>(p);
-    else if (vb) pack_kernel<false, true><<<grid, 256, 0, s>>>(p);
-    else pack_kernel<false, false><<<grid, 256, 0, s>>>(p);
+    auto go = [&](auto d) {
+        constexpr int D = decltype(d)::value;
+        if (va && vb) pack_kernel<D, true, true><<<grid, 256, 0, s>>>(p);
+        else if (va) pack_kernel<D, true, false><<<grid, 256, 0, s>>>(p);
+        else if (vb) pack_kernel<D, false, true><<<grid, 256, 0, s>>>(p);
+        else pack_kernel<D, false, false><<<grid, 256, 0, s>>>(p);
+    };
+    if (depth == 32) go(std::integral_constant<int, 32>{});
+    else go(std::integral_constant<int, 64>{});
     return hipGetLastError();
 }
 

@@ -37,13 +37,13 @@ struct F32Args {
 
 // Arguments of one f16 GEMM launch on rounded, packed operands: A16 holds A
 // and B16t holds B transposed (k contiguous), both binary16 in the packed
-// panel-major layout of gemm_f16r.hip (blocks of 256 rows x 64 k, zero outside
-// the logical matrices).
+// panel-major layout of gemm_f16r.hip (blocks of 256 rows x BK k, BK the
+// configuration's panel depth, zero outside the logical matrices).
 struct F16Args {
     const uint16_t* A16;
     const uint16_t* B16t;
     float* C;
-    int64_t nkb;  // depth blocks of 64 (padded K / 64)
+    int64_t nkb;  // depth blocks of BK (padded K / BK)
     int64_t ldc;
     int M, N;
     float alpha, beta;
@@ -74,10 +74,10 @@ const F16Instance* f16_instances(int* count);
 
 // Rounding and packing pass of the f16r mode: A (M x K) into Mp x Kp and B
 // (K x N) transposed into Np x Kp, Mp, Np multiples of 256, Kp of 64, in one
-// launch.
+// launch, in depth blocks of `depth` (32 or 64) values.
 hipError_t launch_pack(const float* A, int64_t lda, const float* B, int64_t ldb, int M, int N,
                        int K, uint16_t* A16, uint16_t* B16t, int64_t mp, int64_t np, int64_t kp,
-                       hipStream_t s);
+                       int depth, hipStream_t s);
 
 // C = beta*C (beta == 0: C = 0 without reading it).
 hipError_t launch_scale_c(float* C, int64_t ldc, int M, int N, float beta, hipStream_t s);
