@@ -64,6 +64,10 @@ def main():
                     help="summarise FETCH_SIZE / WRITE_SIZE runs into an HBM-traffic table")
     ap.add_argument("--out", default=None, help="output file of the --summarize-* modes")
     ap.add_argument("--cmd", default="", help="the command that produced the profile")
+    ap.add_argument("--sweep", metavar="OUT_MD", default=None,
+                    help="shape and alignment sweep of both modes (sizes 128..8192, n = "
+                         "4088..4104 and 2048..2304, fixed-tile steps); markdown to OUT_MD")
+    ap.add_argument("--sweep-repeats", type=int, default=3)
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -97,6 +101,10 @@ def main():
 
     if args.calibrate_copy:
         copy_calibration(g, torch, dev)
+
+    if args.sweep:
+        shape_sweep(g, torch, dev, args.sweep, args.sweep_repeats)
+        return
 
     # ------------------------------------------------------------------ roofs
     roofs = {}
@@ -360,12 +368,137 @@ def cpu_baseline(w, target_seconds, workload_inputs):
 
 
 # ---------------------------------------------------------------------------
+# Shape and alignment sweep (the Matrix Multiplication lab, "Part 5 -- cuBLAS,
+# and what shape does to it": a size sweep, the one-element steps around 2048
+# and 4096, and the same steps for a tiling that cannot change).
+# ---------------------------------------------------------------------------
+SWEEP_SIZES = [128, 256, 512, 1024, 1536, 2048, 3072, 4096, 6144, 8192]
+SWEEP_QUANT = list(range(4088, 4105)) + [2048, 2049, 2056, 2064, 2080, 2112, 2176, 2304]
+SWEEP_FIXED = [2048, 2049, 4096, 4097]
+FIXED_TILE = {"f32": "BM=128 BN=128 BK=32 ST=2 WM=2 WN=2 GM=8",
+              "f16r": "BM=128 BN=128 BK=64 ST=1 WM=2 WN=2 GM=8"}
+
+
+def _tile_fields(tile):
+    return {k: int(v) for k, v in (t.split("=") for t in tile.split() if "=" in t and
+                                    t.split("=")[1].isdigit())}
+
+
+def _path_of(mode, n, tile):
+    """Which variant a square n^3 call with this tile runs (dense, 16-byte aligned rows)."""
+    t = _tile_fields(tile)
+    if mode == "f32":
+        ragged = n % t["BM"] or n % t["BN"] or n % t["BK"]
+        return ("masked" if ragged else "aligned") + ("" if n % 4 == 0 else ", 4-byte loads")
+    return "masked store" if (n % t["BM"] or n % t["BN"]) else "aligned"
+
+
+def shape_sweep(g, torch, dev, out, repeats):
+    import random
+
+    import oracle
+    from workloads import make_inputs, sample_indices
+
+    cases = [(mode, n, "tuned") for mode in ("f32", "f16r")
+             for n in sorted(set(SWEEP_SIZES + SWEEP_QUANT))]
+    cases += [(mode, n, "fixed") for mode in ("f32", "f16r") for n in SWEEP_FIXED]
+    inputs = {}
+    for n in sorted({c[1] for c in cases}):
+        A, B, C = make_inputs(n, n, n, "normal", seed=n)
+        r, c = sample_indices(n, n, 256, seed=2)
+        refs = {mode: oracle.entries(mode, A, B, C, 1.0, 0.0, r, c) for mode in ("f32", "f16r")}
+        inputs[n] = (torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev),
+                     torch.from_numpy(C).to(dev), r, c, refs)
+        del A, B, C
+    log(f"sweep: {len(cases)} cases, {repeats} shuffled rounds")
+
+    tiles, calls = {}, {}
+    for case in cases:
+        mode, n, kind = case
+        tA, tB, tC, r, c, refs = inputs[n]
+        fn = g.gemm_f32 if mode == "f32" else g.gemm_f16r_f32acc
+        if kind == "tuned":
+            g.tune(mode, tA, tB, tC, beta=0.0)
+            tiles[case] = g.get_config(mode, n, n, n, beta=0.0)
+            call = (lambda fn=fn, tA=tA, tB=tB, tC=tC: fn(tA, tB, tC, 1.0, 0.0))
+        else:
+            tiles[case] = FIXED_TILE[mode] + " source=pin"
+
+            def call(fn=fn, tA=tA, tB=tB, tC=tC, mode=mode):
+                g.set_config(mode, FIXED_TILE[mode])
+                try:
+                    fn(tA, tB, tC, 1.0, 0.0)
+                finally:
+                    g.set_config(mode, None)
+        # correctness first: sampled elements against the oracle (beta = 0: C is not read)
+        call()
+        torch.cuda.synchronize()
+        got = tC[torch.as_tensor(r, device=dev), torch.as_tensor(c, device=dev)].cpu().numpy()
+        ref, W = refs[mode]
+        err = np.abs(got.astype(np.float64) - ref)
+        if not np.all(err <= oracle.TOL[mode] * W):
+            raise SystemExit(f"sweep {case}: outside the parity bound")
+        calls[case] = call
+
+    times = {case: [] for case in cases}
+    rng = random.Random(0)
+    for rnd in range(repeats):
+        order = list(cases)
+        rng.shuffle(order)
+        for case in order:
+            times[case].append(steady(calls[case], torch, seconds=0.3))
+        log(f"sweep: round {rnd + 1} of {repeats} done")
+
+    rows = []
+    for case in cases:
+        mode, n, kind = case
+        ts = times[case]
+        med = float(np.median(ts))
+        rows.append({"mode": mode, "n": n, "kind": kind, "tile": tiles[case].split(" source=")[0],
+                     "path": _path_of(mode, n, tiles[case]), "seconds": med,
+                     "seconds_min": min(ts), "seconds_max": max(ts),
+                     "tflops": 2.0 * n ** 3 / med / 1e12})
+    by = {(r["mode"], r["n"], r["kind"]): r for r in rows}
+
+    def step(mode, kind, a, b):
+        ra, rb = by[(mode, a, kind)], by[(mode, b, kind)]
+        return 100 * (rb["seconds"] / ra["seconds"] - 1), 100 * (1 - rb["tflops"] / ra["tflops"])
+
+    lines = ["# Shape and alignment sweep (both modes, one MI355X)", "",
+             "Command:", "", "```", "python bench.py --sweep profiles/sweep_shapes.md", "```", "",
+             "Square n x n x n, A, B, C iid N(0,1) (seed n), alpha = 1, beta = 0.  Every case is "
+             "checked against the oracle on 256 sampled elements before it is timed; each time "
+             f"is the median of {repeats} shuffled rounds of the lab's steady() (0.3 s each).  "
+             "`tuned` lets the library's tuner pick the tile per shape; `fixed` pins one 128 x 128 "
+             "tile, so its step isolates the cost of the ragged edge.", ""]
+    lines += ["## One-element steps", "", "| mode | tiling | 2048 -> 2049 time | 4096 -> 4097 time |",
+              "|---|---|---:|---:|"]
+    for mode in ("f32", "f16r"):
+        for kind in ("tuned", "fixed"):
+            a, b = step(mode, kind, 2048, 2049), step(mode, kind, 4096, 4097)
+            lines.append(f"| {mode} | {kind} | {a[0]:+.1f}% | {b[0]:+.1f}% |")
+    for title, sel in (("## Size sweep", lambda r: r["n"] in SWEEP_SIZES and r["kind"] == "tuned"),
+                       ("## Near 2048 and 4096", lambda r: r["n"] in SWEEP_QUANT and
+                        r["kind"] == "tuned"),
+                       ("## Fixed 128 x 128 tile", lambda r: r["kind"] == "fixed")):
+        lines += ["", title, "", "| mode | n | TFLOP/s | min..max ms | tile | path |",
+                  "|---|---:|---:|---|---|---|"]
+        for r in sorted(filter(sel, rows), key=lambda r: (r["mode"], r["n"])):
+            lines.append(f"| {r['mode']} | {r['n']} | {r['tflops']:.1f} | "
+                         f"{r['seconds_min'] * 1e3:.3f}..{r['seconds_max'] * 1e3:.3f} | "
+                         f"{r['tile']} | {r['path']} |")
+    lines += ["", "```json", json.dumps(rows), "```", ""]
+    _write(out, "\n".join(lines))
+
+
+# ---------------------------------------------------------------------------
 # Profile evidence: byte-counter calibration, committed summaries.
 # ---------------------------------------------------------------------------
 COPY_BYTES = 256 << 20          # one direction of the calibration copy
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
-    "f32": ["gemm_tiled_amd/csrc/gemm_f32.hip", "gemm_tiled_amd/csrc/internal.hpp"],
+    "f32": ["gemm_tiled_amd/csrc/gemm_f32.hip", "gemm_tiled_amd/csrc/f32_kernel.hpp",
+            "gemm_tiled_amd/csrc/internal.hpp"],
     "f16r": ["gemm_tiled_amd/csrc/gemm_f16r.hip", "gemm_tiled_amd/csrc/internal.hpp"],
 }
 

@@ -37,10 +37,18 @@ EXPORTS = {
     "gemm_f32": (ctypes.c_int, [_i64, _i64, _i64, _f32, _p, _i64, _p, _i64, _f32, _p, _i64, _p]),
     "gemm_f16r_f32acc": (ctypes.c_int,
                          [_i64, _i64, _i64, _f32, _p, _i64, _p, _i64, _f32, _p, _i64, _p]),
+    "gemm_f32_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _f32, _p, _i64,
+                                   _p, _i64, _f32, _p, _i64, _p]),
+    "gemm_f16r_f32acc_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _f32, _p,
+                                           _i64, _p, _i64, _f32, _p, _i64, _p]),
     "gemm355_tune": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p, _i64, _f32,
                                     _i64, _p]),
+    "gemm355_tune_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64, _i64,
+                                       _p, _i64, _p, _i64, _f32, _i64, _p]),
     "gemm355_get_config": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _i64,
                                           _f32, _p, ctypes.c_size_t]),
+    "gemm355_get_config_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64,
+                                             _i64, _i64, _i64, _i64, _f32, _p, ctypes.c_size_t]),
     "gemm355_set_config": (ctypes.c_int, [ctypes.c_int, _cp]),
     "gemm355_parse_config": (ctypes.c_int, [ctypes.c_int, _cp, _p, ctypes.c_size_t]),
     "gemm355_list_configs": (ctypes.c_int, [ctypes.c_int, _p, ctypes.c_size_t]),
@@ -124,50 +132,69 @@ def _matrix(t, name, rows=None, cols=None):
     return ld
 
 
-def gemm(mode, A, B, C, alpha=1.0, beta=0.0, stream=None):
-    """C = alpha*A@B + beta*C in place, on torch's current stream (or `stream`)."""
-    M, K = A.shape
-    N = B.shape[1]
-    lda = _matrix(A, "A", M, K)
-    ldb = _matrix(B, "B", K, N)
+def _operands(A, B, C, transa, transb):
+    """Shapes and leading dimensions of one call: A is stored M x K (K x M when
+    transa), B K x N (N x K when transb)."""
+    if transa:
+        K, M = A.shape
+    else:
+        M, K = A.shape
+    N = B.shape[0] if transb else B.shape[1]
+    lda = _matrix(A, "A", *((K, M) if transa else (M, K)))
+    ldb = _matrix(B, "B", *((N, K) if transb else (K, N)))
     ldc = _matrix(C, "C", M, N)
+    return M, N, K, lda, ldb, ldc
+
+
+def gemm(mode, A, B, C, alpha=1.0, beta=0.0, stream=None, transa=False, transb=False):
+    """C = alpha*op(A)@op(B) + beta*C in place, on torch's current stream (or
+    `stream`); op(X) = X, or X transposed when transa / transb (A then holds
+    K x M, B N x K, both row-major)."""
+    M, N, K, lda, ldb, ldc = _operands(A, B, C, transa, transb)
     if (A.numel() and A.device != C.device) or (B.numel() and B.device != C.device):
         raise ValueError("A, B and C must be on the same device")
-    fn = lib().gemm_f32 if _mode(mode) == MODE_F32 else lib().gemm_f16r_f32acc
-    st = fn(M, N, K, float(alpha), A.data_ptr() or None, lda, B.data_ptr() or None, ldb,
-            float(beta), C.data_ptr() or None, ldc, _stream_ptr(stream))
+    ptrs = (float(alpha), A.data_ptr() or None, lda, B.data_ptr() or None, ldb, float(beta),
+            C.data_ptr() or None, ldc, _stream_ptr(stream))
+    f32 = _mode(mode) == MODE_F32
+    if transa or transb:
+        name = "gemm_f32_ex" if f32 else "gemm_f16r_f32acc_ex"
+        st = getattr(lib(), name)(int(bool(transa)), int(bool(transb)), M, N, K, *ptrs)
+    else:
+        name = "gemm_f32" if f32 else "gemm_f16r_f32acc"
+        st = getattr(lib(), name)(M, N, K, *ptrs)
     if st != 0:
-        raise Gemm355Error(st, "gemm_f32" if _mode(mode) == MODE_F32 else "gemm_f16r_f32acc")
+        raise Gemm355Error(st, name)
     return C
 
 
-def gemm_f32(A, B, C, alpha=1.0, beta=0.0, stream=None):
-    return gemm(MODE_F32, A, B, C, alpha, beta, stream)
+def gemm_f32(A, B, C, alpha=1.0, beta=0.0, stream=None, transa=False, transb=False):
+    return gemm(MODE_F32, A, B, C, alpha, beta, stream, transa, transb)
 
 
-def gemm_f16r_f32acc(A, B, C, alpha=1.0, beta=0.0, stream=None):
-    return gemm(MODE_F16R, A, B, C, alpha, beta, stream)
+def gemm_f16r_f32acc(A, B, C, alpha=1.0, beta=0.0, stream=None, transa=False, transb=False):
+    return gemm(MODE_F16R, A, B, C, alpha, beta, stream, transa, transb)
 
 
-def tune(mode, A, B, C, beta=0.0, stream=None):
-    """Autotune the tile configuration for this call's shape; C is not touched."""
-    M, K = A.shape
-    N = B.shape[1]
-    lda = _matrix(A, "A", M, K)
-    ldb = _matrix(B, "B", K, N)
-    ldc = _matrix(C, "C", M, N)
-    st = lib().gemm355_tune(_mode(mode), M, N, K, A.data_ptr() or None, lda,
-                            B.data_ptr() or None, ldb, float(beta), ldc, _stream_ptr(stream))
+def tune(mode, A, B, C, beta=0.0, stream=None, transa=False, transb=False):
+    """Autotune the tile configuration for this call's shape and layout; C is
+    not touched."""
+    M, N, K, lda, ldb, ldc = _operands(A, B, C, transa, transb)
+    st = lib().gemm355_tune_ex(_mode(mode), int(bool(transa)), int(bool(transb)), M, N, K,
+                               A.data_ptr() or None, lda, B.data_ptr() or None, ldb, float(beta),
+                               ldc, _stream_ptr(stream))
     if st != 0:
-        raise Gemm355Error(st, "gemm355_tune")
+        raise Gemm355Error(st, "gemm355_tune_ex")
 
 
-def get_config(mode, M, N, K, lda=None, ldb=None, ldc=None, beta=0.0) -> str:
+def get_config(mode, M, N, K, lda=None, ldb=None, ldc=None, beta=0.0, transa=False,
+               transb=False) -> str:
     buf = ctypes.create_string_buffer(256)
-    st = lib().gemm355_get_config(_mode(mode), M, N, K, lda or max(K, 1), ldb or max(N, 1),
-                                  ldc or max(N, 1), float(beta), buf, 256)
+    lda = lda or max(M if transa else K, 1)
+    ldb = ldb or max(K if transb else N, 1)
+    st = lib().gemm355_get_config_ex(_mode(mode), int(bool(transa)), int(bool(transb)), M, N, K,
+                                     lda, ldb, ldc or max(N, 1), float(beta), buf, 256)
     if st != 0:
-        raise Gemm355Error(st, "gemm355_get_config")
+        raise Gemm355Error(st, "gemm355_get_config_ex")
     return buf.value.decode()
 
 

@@ -113,11 +113,24 @@ struct Key {
     int mode;
     int64_t M, N, K;
     int vec_a, vec_b, beta0;
+    int trans;   // operand layouts: bit 0 op(A) = A^T, bit 1 op(B) = B^T
     bool operator<(const Key& o) const {
-        return std::tie(mode, M, N, K, vec_a, vec_b, beta0) <
-               std::tie(o.mode, o.M, o.N, o.K, o.vec_a, o.vec_b, o.beta0);
+        return std::tie(mode, M, N, K, vec_a, vec_b, beta0, trans) <
+               std::tie(o.mode, o.M, o.N, o.K, o.vec_a, o.vec_b, o.beta0, o.trans);
     }
 };
+
+// The cache and log name of a mode and layout: "f32", "f32:TN" (op(A) = A^T),
+// "f16r:NT" (op(B) = B^T), ...
+std::string layout_name(int mode, int trans) {
+    std::string s = mode == GEMM355_MODE_F32 ? "f32" : "f16r";
+    if (trans) {
+        s += ':';
+        s += (trans & 1) ? 'T' : 'N';
+        s += (trans & 2) ? 'T' : 'N';
+    }
+    return s;
+}
 
 struct State {
     std::mutex mu;
@@ -192,8 +205,9 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K) {
 
 enum class Source { Pin, Tuned, Heuristic };
 
-int select_config(int mode, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
-                  const float* B, int64_t ldb, float beta, TileConfig* out, Source* src) {
+int select_config(int mode, int trans, int64_t M, int64_t N, int64_t K, const float* A,
+                  int64_t lda, const float* B, int64_t ldb, float beta, TileConfig* out,
+                  Source* src) {
     State& st = state();
     std::lock_guard<std::mutex> lock(st.mu);
     read_env_locked(st);
@@ -203,7 +217,7 @@ int select_config(int mode, int64_t M, int64_t N, int64_t K, const float* A, int
         *src = Source::Pin;
         return 0;
     }
-    const Key key{mode, M, N, K, vec_ok(A, lda), vec_ok(B, ldb), beta == 0.f};
+    const Key key{mode, M, N, K, vec_ok(A, lda), vec_ok(B, ldb), beta == 0.f, trans};
     auto it = st.cache.find(key);
     if (it != st.cache.end()) {
         *out = it->second;
@@ -260,16 +274,20 @@ hipError_t workspace(hipStream_t s, size_t bytes, void** out) {
 // ---------------------------------------------------------------------------
 // Argument checks (BLAS xerbla numbering) and the dispatch of one call.
 // ---------------------------------------------------------------------------
-int check_args(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
-               const float* B, int64_t ldb, const float* C, int64_t ldc) {
+// Arguments are numbered as in gemm_f32: 1 M, 2 N, 3 K, 5 A, 6 lda, 7 B,
+// 8 ldb, 10 C, 11 ldc (the _ex entry points add 2 and number transa, transb
+// 1 and 2).  A is stored M x K (K x M when op(A) = A^T), B K x N (N x K).
+int check_args(int trans, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+               int64_t lda, const float* B, int64_t ldb, const float* C, int64_t ldc) {
     if (M < 0 || M > kMaxDim) return -1;
     if (N < 0 || N > kMaxDim) return -2;
     if (K < 0 || K > kMaxDim) return -3;
     const bool product = M > 0 && N > 0 && K > 0 && alpha != 0.f;
+    const int64_t a_row = (trans & 1) ? M : K, b_row = (trans & 2) ? K : N;
     if (product && A == nullptr) return -5;
-    if (lda < std::max<int64_t>(1, K)) return -6;
+    if (lda < std::max<int64_t>(1, a_row)) return -6;
     if (product && B == nullptr) return -7;
-    if (ldb < std::max<int64_t>(1, N)) return -8;
+    if (ldb < std::max<int64_t>(1, b_row)) return -8;
     if (M > 0 && N > 0 && C == nullptr) return -10;
     if (ldc < std::max<int64_t>(1, N)) return -11;
     return 0;
@@ -277,7 +295,7 @@ int check_args(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int
 
 int status_of(hipError_t e) { return e == hipSuccess ? 0 : static_cast<int>(e); }
 
-int launch_with(const TileConfig& cfg, int64_t M, int64_t N, int64_t K, float alpha,
+int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
                 int64_t ldc, hipStream_t s) {
     const int tiles_m = static_cast<int>((M + cfg.bm - 1) / cfg.bm);
@@ -291,10 +309,13 @@ int launch_with(const TileConfig& cfg, int64_t M, int64_t N, int64_t K, float al
                       static_cast<int>(K), alpha, beta, tiles_m, tiles_n};
             F32Variant v;
             v.vec = vec_ok(A, lda) && vec_ok(B, ldb);
+            v.ta = (trans & 1) != 0;
+            v.tb = (trans & 2) != 0;
             v.masked = !v.vec || (M % cfg.bm) || (N % cfg.bn) || (K % cfg.bk);
             if (log_debug())
-                std::fprintf(stderr, "[gemm355] f32 M=%lld N=%lld K=%lld %s path=%s%s\n",
-                             (long long)M, (long long)N, (long long)K, format_config(cfg).c_str(),
+                std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=%s%s\n",
+                             layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
+                             (long long)K, format_config(cfg).c_str(),
                              v.masked ? "masked" : "aligned", v.vec ? "" : " scalar-loads");
             return status_of(t[i].launch(a, v, s));
         }
@@ -310,24 +331,26 @@ int launch_with(const TileConfig& cfg, int64_t M, int64_t N, int64_t K, float al
         if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
         uint16_t* A16 = static_cast<uint16_t*>(ws);
         uint16_t* B16t = A16 + mp * kp;
-        e = launch_pack(A, lda, B, ldb, static_cast<int>(M), static_cast<int>(N),
-                        static_cast<int>(K), A16, B16t, mp, np, kp, cfg.bk, s);
+        e = launch_pack(A, lda, (trans & 1) != 0, B, ldb, (trans & 2) != 0, static_cast<int>(M),
+                        static_cast<int>(N), static_cast<int>(K), A16, B16t, mp, np, kp, cfg.bk,
+                        s);
         if (e != hipSuccess) return status_of(e);
         F16Args a{A16, B16t, C, kp / cfg.bk, ldc, static_cast<int>(M), static_cast<int>(N), alpha,
                   beta, tiles_m, tiles_n};
         if (log_debug())
-            std::fprintf(stderr, "[gemm355] f16r M=%lld N=%lld K=%lld %s path=%s\n",
-                         (long long)M, (long long)N, (long long)K, format_config(cfg).c_str(),
+            std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=%s\n",
+                         layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
+                         (long long)K, format_config(cfg).c_str(),
                          ((M % cfg.bm) || (N % cfg.bn)) ? "masked-store" : "aligned");
         return status_of(t[i].launch(a, s));
     }
     return GEMM355_ERR_CONFIG;
 }
 
-int gemm(int mode, int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
-         const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream,
+int gemm(int mode, int trans, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+         int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream,
          const TileConfig* force) {
-    const int bad = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    const int bad = check_args(trans, M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (bad) return bad;
     if (M == 0 || N == 0) return 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -342,10 +365,10 @@ int gemm(int mode, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
         cfg = *force;
     } else {
         Source src;
-        const int rc = select_config(mode, M, N, K, A, lda, B, ldb, beta, &cfg, &src);
+        const int rc = select_config(mode, trans, M, N, K, A, lda, B, ldb, beta, &cfg, &src);
         if (rc) return rc;
     }
-    return launch_with(cfg, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    return launch_with(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -364,15 +387,20 @@ size_t load_cache_locked(State& st, const char* path) {
         if (std::sscanf(line, "%15s %lld %lld %lld %d %d %d %n", mode_s, &M, &N, &K, &va, &vb,
                         &b0, &off) != 7)
             continue;
-        int mode = -1;
-        if (std::strcmp(mode_s, "f32") == 0) mode = GEMM355_MODE_F32;
-        if (std::strcmp(mode_s, "f16r") == 0) mode = GEMM355_MODE_F16R;
+        int mode = -1, trans = -1;
+        for (int m = 0; m < 2 && mode < 0; ++m)
+            for (int t = 0; t < 4; ++t)
+                if (layout_name(m, t) == mode_s) {
+                    mode = m;
+                    trans = t;
+                    break;
+                }
         if (mode < 0 || M < 0 || N < 0 || K < 0) continue;
         std::string rest(line + off);
         while (!rest.empty() && (rest.back() == '\n' || rest.back() == '\r')) rest.pop_back();
         TileConfig c;
         if (!parse_config(mode, rest.c_str(), &c)) continue;
-        st.cache[Key{mode, M, N, K, va != 0, vb != 0, b0 != 0}] = c;
+        st.cache[Key{mode, M, N, K, va != 0, vb != 0, b0 != 0, trans}] = c;
         ++n;
     }
     std::fclose(f);
@@ -387,7 +415,8 @@ int save_cache_locked(State& st, const char* path) {
     int n = 0;
     for (const auto& kv : st.cache) {
         const Key& k = kv.first;
-        std::fprintf(f, "%s %lld %lld %lld %d %d %d %s\n", mode_name(k.mode), (long long)k.M,
+        std::fprintf(f, "%s %lld %lld %lld %d %d %d %s\n", layout_name(k.mode, k.trans).c_str(),
+                     (long long)k.M,
                      (long long)k.N, (long long)k.K, k.vec_a, k.vec_b, k.beta0,
                      format_config(kv.second).c_str());
         ++n;
@@ -413,12 +442,12 @@ struct Timed {
     }
 };
 
-int time_once(const TileConfig& cfg, int64_t M, int64_t N, int64_t K, const float* A,
+int time_once(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, const float* A,
               int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
               hipStream_t s, hipEvent_t e0, hipEvent_t e1, float* ms) {
     hipError_t e = hipEventRecord(e0, s);
     if (e != hipSuccess) return status_of(e);
-    int rc = gemm(cfg.mode, M, N, K, 1.0f, A, lda, B, ldb, beta, C, ldc, s, &cfg);
+    int rc = gemm(cfg.mode, trans, M, N, K, 1.0f, A, lda, B, ldb, beta, C, ldc, s, &cfg);
     if (rc) return rc;
     e = hipEventRecord(e1, s);
     if (e == hipSuccess) e = hipEventSynchronize(e1);
@@ -426,12 +455,12 @@ int time_once(const TileConfig& cfg, int64_t M, int64_t N, int64_t K, const floa
     return status_of(e);
 }
 
-int tune(int mode, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
-         int64_t ldb, float beta, int64_t ldc, void* stream) {
+int tune(int mode, int trans, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+         const float* B, int64_t ldb, float beta, int64_t ldc, void* stream) {
     if (mode != GEMM355_MODE_F32 && mode != GEMM355_MODE_F16R) return GEMM355_ERR_MODE;
     float* C = nullptr;
     // a stand-in C pointer for the argument check; the real scratch comes next
-    const int bad = check_args(M, N, K, 1.0f, A, lda, B, ldb,
+    const int bad = check_args(trans, M, N, K, 1.0f, A, lda, B, ldb,
                                reinterpret_cast<const float*>(uintptr_t{16}), ldc);
     if (bad) return bad;
     if (M == 0 || N == 0 || K == 0) return 0;
@@ -448,9 +477,9 @@ int tune(int mode, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
         for (const TileConfig& cfg : configs_of(mode)) {
             Timed t{cfg, {}};
             float ms = 0.f;
-            int r = time_once(cfg, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, &ms);  // warm-up
+            int r = time_once(cfg, trans, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, &ms);  // warm-up
             for (int i = 0; i < 3 && r == 0; ++i) {
-                r = time_once(cfg, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, &ms);
+                r = time_once(cfg, trans, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, &ms);
                 if (r == 0) t.ms.push_back(ms);
             }
             if (r != 0) {
@@ -476,7 +505,7 @@ int tune(int mode, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
             }
             for (size_t i : order) {
                 float ms = 0.f;
-                if (time_once(ok[i].cfg, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, &ms) == 0)
+                if (time_once(ok[i].cfg, trans, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, &ms) == 0)
                     ok[i].ms.push_back(ms);
             }
         }
@@ -489,13 +518,14 @@ int tune(int mode, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
             if (log_debug())
                 for (const Timed& t : ok)
                     std::fprintf(stderr, "[gemm355] tune %s M=%lld N=%lld K=%lld %s: %.4f ms%s\n",
-                                 mode_name(mode), (long long)M, (long long)N, (long long)K,
+                                 layout_name(mode, trans).c_str(), (long long)M, (long long)N, (long long)K,
                                  format_config(t.cfg).c_str(), t.median(),
                                  &t == best ? "  <- chosen" : "");
             State& st = state();
             std::lock_guard<std::mutex> lock(st.mu);
             read_env_locked(st);
-            st.cache[Key{mode, M, N, K, vec_ok(A, lda), vec_ok(B, ldb), beta == 0.f}] = best->cfg;
+            st.cache[Key{mode, M, N, K, vec_ok(A, lda), vec_ok(B, ldb), beta == 0.f, trans}] =
+                best->cfg;
             if (!st.cache_path.empty()) save_cache_locked(st, st.cache_path.c_str());
         }
     }
@@ -526,32 +556,88 @@ extern "C" {
 
 int gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
              const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream) {
-    return gemm(GEMM355_MODE_F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, nullptr);
+    return gemm(GEMM355_MODE_F32, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                nullptr);
 }
 
 int gemm_f16r_f32acc(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
                      const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
                      void* stream) {
-    return gemm(GEMM355_MODE_F16R, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, nullptr);
+    return gemm(GEMM355_MODE_F16R, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The _ex entry points: transa, transb must be 0 or 1 (codes -1, -2); the
+// other argument codes move up by two (BLAS sgemm numbering).
+int trans_of(int transa, int transb, int* trans) {
+    if (transa != 0 && transa != 1) return -1;
+    if (transb != 0 && transb != 1) return -2;
+    *trans = transa | (transb << 1);
+    return 0;
+}
+int shift_ex(int rc) { return rc < 0 && rc > -100 ? rc - 2 : rc; }
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
+                const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                int64_t ldc, void* stream) {
+    int trans = 0;
+    if (const int bad = trans_of(transa, transb, &trans)) return bad;
+    return shift_ex(gemm(GEMM355_MODE_F32, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         stream, nullptr));
+}
+
+int gemm_f16r_f32acc_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
+                        const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                        float* C, int64_t ldc, void* stream) {
+    int trans = 0;
+    if (const int bad = trans_of(transa, transb, &trans)) return bad;
+    return shift_ex(gemm(GEMM355_MODE_F16R, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         stream, nullptr));
 }
 
 int gemm355_tune(int mode, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                  const float* B, int64_t ldb, float beta, int64_t ldc, void* stream) {
-    return tune(mode, M, N, K, A, lda, B, ldb, beta, ldc, stream);
+    return tune(mode, 0, M, N, K, A, lda, B, ldb, beta, ldc, stream);
+}
+
+int gemm355_tune_ex(int mode, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                    const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                    int64_t ldc, void* stream) {
+    int trans = 0;
+    if (const int bad = trans_of(transa, transb, &trans)) return bad;
+    return shift_ex(tune(mode, trans, M, N, K, A, lda, B, ldb, beta, ldc, stream));
+}
+
+int gemm355_get_config_ex(int mode, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                          int64_t lda, int64_t ldb, int64_t ldc, float beta, char* buf,
+                          size_t len) {
+    if (mode != GEMM355_MODE_F32 && mode != GEMM355_MODE_F16R) return GEMM355_ERR_MODE;
+    int trans = 0;
+    if (const int bad = trans_of(transa, transb, &trans)) return bad;
+    const float* aligned = reinterpret_cast<const float*>(uintptr_t{256});
+    const int bad = check_args(trans, M, N, K, 1.0f, aligned, lda, aligned, ldb, aligned, ldc);
+    if (bad) return shift_ex(bad);
+    TileConfig cfg;
+    Source src;
+    const int rc =
+        select_config(mode, trans, M, N, K, aligned, lda, aligned, ldb, beta, &cfg, &src);
+    if (rc) return rc;
+    const char* sname = src == Source::Pin ? "pin" : src == Source::Tuned ? "tuned" : "heuristic";
+    return copy_out(format_config(cfg) + " source=" + sname, buf, len);
 }
 
 int gemm355_get_config(int mode, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                        int64_t ldc, float beta, char* buf, size_t len) {
-    if (mode != GEMM355_MODE_F32 && mode != GEMM355_MODE_F16R) return GEMM355_ERR_MODE;
-    const float* aligned = reinterpret_cast<const float*>(uintptr_t{256});
-    const int bad = check_args(M, N, K, 1.0f, aligned, lda, aligned, ldb, aligned, ldc);
-    if (bad) return bad;
-    TileConfig cfg;
-    Source src;
-    const int rc = select_config(mode, M, N, K, aligned, lda, aligned, ldb, beta, &cfg, &src);
-    if (rc) return rc;
-    const char* sname = src == Source::Pin ? "pin" : src == Source::Tuned ? "tuned" : "heuristic";
-    return copy_out(format_config(cfg) + " source=" + sname, buf, len);
+    const int rc = gemm355_get_config_ex(mode, 0, 0, M, N, K, lda, ldb, ldc, beta, buf, len);
+    return rc < 0 && rc > -100 ? rc + 2 : rc;
 }
 
 int gemm355_set_config(int mode, const char* spec) {

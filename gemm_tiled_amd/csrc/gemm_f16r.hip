@@ -65,92 +65,119 @@ __device__ __forceinline__ int64_t packed_offset(int64_t x, int kb, int c, int64
     return ((xb * nkb + kb) * kPackRows + r) * D + ((c ^ swz<D>(r)) << 3);
 }
 
-// Both operands are packed by one launch: the first a_blocks workgroups pack A,
-// the rest pack B^T, so the two streams share the memory system and the tail
-// of one overlaps the start of the other.
-struct PackArgs {
-    const float* A;
-    int64_t lda;
-    const float* B;
-    int64_t ldb;
-    uint16_t* A16;
-    uint16_t* B16t;
-    int64_t mp, nkb;   // padded rows of A; depth blocks of D
-    int M, N, K;
-    int a_blocks;   // workgroups packing A
-    int b_cols;     // Np / 64
+// One operand of the packing pass: the packed image `dst` (rows x Kp, in
+// blocks of 256 rows x D) is filled from the f32 array `src` with leading
+// dimension `ld`, holding the operand either with k contiguous (`direct`: row
+// x of the image is row x of src, as A is stored, or B^T) or with the rows of
+// the image contiguous (transposing: row x of the image is column x of src,
+// as B is stored, or A^T).
+struct PackOperand {
+    const float* src;
+    int64_t ld;
+    uint16_t* dst;
+    int64_t rows_p;   // padded rows of the image (multiple of 256)
+    int rows;         // logical rows (M for A, N for B)
+    int blocks;       // workgroups of this operand
 };
 
-constexpr int kAUnitsPerThread = 8;
-constexpr int kAUnitsPerBlock = 256 * kAUnitsPerThread;
+// Both operands are packed by one launch: the first a.blocks workgroups pack
+// A, the rest B, so the two streams share the memory system and the tail of
+// one overlaps the start of the other.
+struct PackArgs {
+    PackOperand a, b;
+    int64_t nkb;   // depth blocks of D
+    int K;
+};
 
-// A -> packed A16 (Mp rows, zero outside M x K).  One unit converts 8
-// consecutive k of one row into one 16-byte chunk of the packed image, and
-// units are numbered in the order of the packed image, so consecutive threads
-// write consecutive bytes (whole 128-byte lines) and the D/8 threads of one
-// packed row read D consecutive floats of one row of A.
+constexpr int kUnitsPerThread = 8;
+constexpr int kUnitsPerBlock = 256 * kUnitsPerThread;
+constexpr int kTB = 64;        // transpose block edge
+constexpr int kTS = kTB + 2;   // LDS row stride in halves
+
+// Direct packing.  One unit converts 8 consecutive k of one row into one
+// 16-byte chunk of the packed image, and units are numbered in the order of
+// the packed image, so consecutive threads write consecutive bytes (whole
+// 128-byte lines) and the D/8 threads of one packed row read D consecutive
+// floats of one source row.
 template <int D, bool VEC>
-__device__ __forceinline__ void pack_a_unit(const PackArgs& p, int64_t u) {
+__device__ __forceinline__ void pack_unit(const PackOperand& o, int64_t nkb, int K, int64_t u) {
     constexpr int cpr = D / 8;
     const int64_t q = u / cpr;                       // packed row: (block, row in block)
     const int pc = static_cast<int>(u - q * cpr);    // physical chunk
     const int64_t blk = q / kPackRows;
     const int rin = static_cast<int>(q - blk * kPackRows);
-    const int64_t xb = blk / p.nkb;
-    const int kb = static_cast<int>(blk - xb * p.nkb);
+    const int64_t xb = blk / nkb;
+    const int kb = static_cast<int>(blk - xb * nkb);
     const int64_t r = xb * kPackRows + rin;
     const int k = kb * D + ((pc ^ swz<D>(rin)) << 3);
-    const float* A = p.A;
+    const float* X = o.src;
     float v[8];
-    if (r < p.M && VEC && k + 7 < p.K) {
+    if (r < o.rows && VEC && k + 7 < K) {
         // the f32 source is read once: non-temporal, so it does not evict the
         // packed operands from the caches
-        const f32x4* src = reinterpret_cast<const f32x4*>(A + r * p.lda + k);
+        const f32x4* src = reinterpret_cast<const f32x4*>(X + r * o.ld + k);
         const f32x4 x = __builtin_nontemporal_load(src), y = __builtin_nontemporal_load(src + 1);
         v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
         v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+    } else if (r < o.rows && k + 7 < K) {
+        // a row that starts on any 4-byte boundary: 16-byte global loads
+        // need only 4-byte alignment here
+        __builtin_memcpy(v, X + r * o.ld + k, sizeof v);
     } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (r < p.M && k + e < p.K) ? A[r * p.lda + k + e] : 0.f;
+        for (int e = 0; e < 8; ++e) v[e] = (r < o.rows && k + e < K) ? X[r * o.ld + k + e] : 0.f;
     }
-    uint4 o;
-    o.x = pack_rn(v[0], v[1]);
-    o.y = pack_rn(v[2], v[3]);
-    o.z = pack_rn(v[4], v[5]);
-    o.w = pack_rn(v[6], v[7]);
-    *reinterpret_cast<uint4*>(p.A16 + u * 8) = o;
+    uint4 w;
+    w.x = pack_rn(v[0], v[1]);
+    w.y = pack_rn(v[2], v[3]);
+    w.z = pack_rn(v[4], v[5]);
+    w.w = pack_rn(v[6], v[7]);
+    *reinterpret_cast<uint4*>(o.dst + u * 8) = w;
 }
 
-// B -> packed B16t (B transposed: Np rows of K, zero outside).  A 64 (k) x 64
-// (n) block of B is read along n (coalesced), rounded, transposed through LDS
-// and written as 64 packed rows of the 64 / D depth blocks it covers.
-constexpr int kTB = 64;        // transpose block edge
-constexpr int kTS = kTB + 2;   // LDS row stride in halves
-
 template <int D, bool VEC>
-__device__ __forceinline__ void pack_bt_block(const PackArgs& p, int bx, int kt, uint16_t* t) {
-    const int n0 = bx * kTB;
+__device__ __forceinline__ void pack_direct(const PackOperand& o, int64_t nkb, int K, int b) {
+    const int64_t units = o.rows_p * nkb * (D / 8);
+    const int64_t u0 = (int64_t)b * kUnitsPerBlock + threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kUnitsPerThread; ++i) {
+        const int64_t u = u0 + i * 256;
+        if (u < units) pack_unit<D, VEC>(o, nkb, K, u);
+    }
+}
+
+// Transposing packing.  A 64 (k) x 64 (image rows) block of the source is read
+// along its contiguous dimension (coalesced), rounded, transposed through LDS
+// and written as 64 packed rows of the 64 / D depth blocks it covers.
+template <int D, bool VEC>
+__device__ __forceinline__ void pack_transpose(const PackOperand& o, int64_t nkb, int K, int b,
+                                               uint16_t* t) {
+    const int cols = static_cast<int>(o.rows_p / kTB);
+    const int x0 = (b % cols) * kTB;
+    const int kt = b / cols;
     const int k0 = kt * kTB;
     const int tid = threadIdx.x;
-    const float* B = p.B;
+    const float* X = o.src;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int idx = tid + i * 256;
-        const int kr = idx >> 4, nq = (idx & 15) * 4;
-        const int k = k0 + kr, n = n0 + nq;
+        const int kr = idx >> 4, xq = (idx & 15) * 4;
+        const int k = k0 + kr, x = x0 + xq;
         float v[4];
-        if (k < p.K && VEC && n + 3 < p.N) {
-            const f32x4 x =
-                __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(B + (int64_t)k * p.ldb + n));
-            v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        if (k < K && VEC && x + 3 < o.rows) {
+            const f32x4 q =
+                __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(X + (int64_t)k * o.ld + x));
+            v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+        } else if (k < K && x + 3 < o.rows) {
+            __builtin_memcpy(v, X + (int64_t)k * o.ld + x, sizeof v);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                v[e] = (k < p.K && n + e < p.N) ? B[(int64_t)k * p.ldb + n + e] : 0.f;
+                v[e] = (k < K && x + e < o.rows) ? X[(int64_t)k * o.ld + x + e] : 0.f;
         }
         const uint32_t p01 = pack_rn(v[0], v[1]);
         const uint32_t p23 = pack_rn(v[2], v[3]);
-        uint16_t* row = t + kr * kTS + nq;
+        uint16_t* row = t + kr * kTS + xq;
         row[0] = static_cast<uint16_t>(p01 & 0xffffu);
         row[1] = static_cast<uint16_t>(p01 >> 16);
         row[2] = static_cast<uint16_t>(p23 & 0xffffu);
@@ -160,33 +187,36 @@ __device__ __forceinline__ void pack_bt_block(const PackArgs& p, int bx, int kt,
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int u = tid + j * 256;
-        const int n = u >> 3, c = u & 7;
+        const int x = u >> 3, c = u & 7;
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            w[e] = static_cast<uint32_t>(t[(c * 8 + 2 * e) * kTS + n]) |
-                   (static_cast<uint32_t>(t[(c * 8 + 2 * e + 1) * kTS + n]) << 16);
+            w[e] = static_cast<uint32_t>(t[(c * 8 + 2 * e) * kTS + x]) |
+                   (static_cast<uint32_t>(t[(c * 8 + 2 * e + 1) * kTS + x]) << 16);
         constexpr int cpr = D / 8;
         const int kb = kt * (kTB / D) + c / cpr;
-        *reinterpret_cast<uint4*>(p.B16t + packed_offset<D>(n0 + n, kb, c % cpr, p.nkb)) =
+        *reinterpret_cast<uint4*>(o.dst + packed_offset<D>(x0 + x, kb, c % cpr, nkb)) =
             make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
-template <int D, bool VA, bool VB>
+// Workgroups an operand needs: direct units, or 64 x 64 transpose blocks.
+inline int64_t pack_blocks(bool direct, int64_t rows_p, int64_t kp) {
+    return direct ? (rows_p * (kp / 8) + kUnitsPerBlock - 1) / kUnitsPerBlock
+                  : (rows_p / kTB) * (kp / kTB);
+}
+
+// DA / DB: the operand is packed directly (k contiguous in its source).
+template <int D, bool DA, bool DB, bool VA, bool VB>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs p) {
-    __shared__ uint16_t t[kTB * kTS];   // transpose tile of the B blocks
-    if (static_cast<int>(blockIdx.x) < p.a_blocks) {
-        const int64_t units = p.mp * p.nkb * (D / 8);
-        const int64_t u0 = (int64_t)blockIdx.x * kAUnitsPerBlock + threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < kAUnitsPerThread; ++i) {
-            const int64_t u = u0 + i * 256;
-            if (u < units) pack_a_unit<D, VA>(p, u);
-        }
+    __shared__ uint16_t t[kTB * kTS];   // transpose tile
+    const int b = static_cast<int>(blockIdx.x);
+    if (b < p.a.blocks) {
+        if (DA) pack_direct<D, VA>(p.a, p.nkb, p.K, b);
+        else pack_transpose<D, VA>(p.a, p.nkb, p.K, b, t);
     } else {
-        const int b = static_cast<int>(blockIdx.x) - p.a_blocks;
-        pack_bt_block<D, VB>(p, b % p.b_cols, b / p.b_cols, t);
+        if (DB) pack_direct<D, VB>(p.b, p.nkb, p.K, b - p.a.blocks);
+        else pack_transpose<D, VB>(p.b, p.nkb, p.K, b - p.a.blocks, t);
     }
 }
 
@@ -719,41 +749,45 @@ const F16Instance* f16_instances(int* count) {
     return kF16Instances;
 }
 
-hipError_t launch_pack(const float* A, int64_t lda, const float* B, int64_t ldb, int M, int N,
-                       int K, uint16_t* A16, uint16_t* B16t, int64_t mp, int64_t np, int64_t kp,
-                       int depth, hipStream_t s) {
+hipError_t launch_pack(const float* A, int64_t lda, bool ta, const float* B, int64_t ldb,
+                       bool tb, int M, int N, int K, uint16_t* A16, uint16_t* B16t, int64_t mp,
+                       int64_t np, int64_t kp, int depth, hipStream_t s) {
     if ((depth != 32 && depth != 64) || kp % kPackK != 0 || mp % kPackRows != 0 ||
         np % kPackRows != 0)
         return hipErrorInvalidValue;
+    // A (op(A) = A, k contiguous) packs directly, A^T transposes; B (K x N)
+    // transposes, B^T (N x K, k contiguous) packs directly.
+    const bool da = !ta, db = tb;
     PackArgs p;
-    p.A = A;
-    p.lda = lda;
-    p.B = B;
-    p.ldb = ldb;
-    p.A16 = A16;
-    p.B16t = B16t;
-    p.mp = mp;
+    p.a = PackOperand{A, lda, A16, mp, M, 0};
+    p.b = PackOperand{B, ldb, B16t, np, N, 0};
     p.nkb = kp / depth;
-    p.M = M;
-    p.N = N;
     p.K = K;
-    const int64_t a_units = mp * (kp / 8);
-    p.a_blocks = static_cast<int>((a_units + kAUnitsPerBlock - 1) / kAUnitsPerBlock);
-    p.b_cols = static_cast<int>(np / kTB);
-    const int64_t blocks = p.a_blocks + (int64_t)p.b_cols * (kp / kTB);
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int64_t ab = pack_blocks(da, mp, kp), bb = pack_blocks(db, np, kp);
+    if (ab + bb > 0x7fffffff) return hipErrorInvalidConfiguration;
+    p.a.blocks = static_cast<int>(ab);
+    p.b.blocks = static_cast<int>(bb);
     const bool va = (lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(A) & 15) == 0);
     const bool vb = (ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(B) & 15) == 0);
-    const dim3 grid(static_cast<unsigned>(blocks));
-    auto go = [&](auto d) {
-        constexpr int D = decltype(d)::value;
-        if (va && vb) pack_kernel<D, true, true><<<grid, 256, 0, s>>>(p);
-        else if (va) pack_kernel<D, true, false><<<grid, 256, 0, s>>>(p);
-        else if (vb) pack_kernel<D, false, true><<<grid, 256, 0, s>>>(p);
-        else pack_kernel<D, false, false><<<grid, 256, 0, s>>>(p);
+    const dim3 grid(static_cast<unsigned>(ab + bb));
+    auto go = [&](auto d, auto da_, auto db_) {
+        constexpr int DD = decltype(d)::value;
+        constexpr bool DA = decltype(da_)::value, DB = decltype(db_)::value;
+        if (va && vb) pack_kernel<DD, DA, DB, true, true><<<grid, 256, 0, s>>>(p);
+        else if (va) pack_kernel<DD, DA, DB, true, false><<<grid, 256, 0, s>>>(p);
+        else if (vb) pack_kernel<DD, DA, DB, false, true><<<grid, 256, 0, s>>>(p);
+        else pack_kernel<DD, DA, DB, false, false><<<grid, 256, 0, s>>>(p);
     };
-    if (depth == 32) go(std::integral_constant<int, 32>{});
-    else go(std::integral_constant<int, 64>{});
+    auto layouts = [&](auto d) {
+        using T = std::true_type;
+        using F = std::false_type;
+        if (da && !db) go(d, T{}, F{});          // A, B (the plain layout)
+        else if (!da && !db) go(d, F{}, F{});    // A^T, B
+        else if (da && db) go(d, T{}, T{});      // A, B^T
+        else go(d, F{}, T{});                    // A^T, B^T
+    };
+    if (depth == 32) layouts(std::integral_constant<int, 32>{});
+    else layouts(std::integral_constant<int, 64>{});
     return hipGetLastError();
 }
 

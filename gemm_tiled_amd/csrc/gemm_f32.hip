@@ -1,233 +1,23 @@
-// gemm_f32.hip -- C = alpha*A@B + beta*C on f32, contracted on the gfx950
-// matrix cores (v_mfma_f32_32x32x2_f32, full f32 precision).
-//
-// The structure follows the phobos docs page "gemm, f32": one output tile per
-// workgroup (section "One output tile per CTA"), a K loop over BK-deep panels
-// of A and B staged in shared memory by all threads and double-buffered so the
-// copy of the next pair overlaps the math on the current one (sections "The k
-// loop" and "The attributes", @pipeline), and the alpha/beta epilogue over the
-// same tile (section "The epilogue").  On gfx950 the tile is split over 64-lane
-// wavefronts, each owning a grid of 32x32 accumulator blocks.
-//
-// Masked variant (the default of the page's kernel without @aligned, and the
-// zero-fill rule of the Matrix Multiplication lab's shared-memory kernels):
-// out-of-range elements of A and B are loaded as zeros and stores outside
-// M x N are skipped.
-#include "internal.hpp"
+// gemm_f32.hip -- C = alpha*op(A)@op(B) + beta*C on f32, contracted on the
+// gfx950 matrix cores (v_mfma_f32_32x32x2_f32, full f32 precision).  The
+// kernel template is in f32_kernel.hpp; this unit compiles the plain layout
+// (op = identity) and holds the table of configurations, whose launches hand
+// the transposed layouts to gemm_f32_t.hip.
+#include "f32_kernel.hpp"
 
 namespace g355 {
 namespace {
 
-
-template <int BM, int BN, int BK, int WM, int WN>
-struct F32Shape {
-    static constexpr int NT = WM * WN * 64;
-    static constexpr int TM = BM / WM;   // rows of C per wave
-    static constexpr int TN = BN / WN;   // cols of C per wave
-    static constexpr int FM = TM / 32;   // 32x32 accumulator blocks per wave (rows)
-    static constexpr int FN = TN / 32;   // (cols)
-    static constexpr int KH = BK / 2;    // k values per lane half per panel
-    // A panel in LDS: BM rows of BK floats (k contiguous), padded so that the
-    // 16-byte reads of 8 consecutive rows hit distinct banks.
-    static constexpr int AS = BK + 4;
-    // B panel in LDS: BK rows of BN floats (n contiguous), padded so the two
-    // lane halves of a 32-bit read land on different bank halves.
-    static constexpr int BS = BN + 4;
-    static constexpr int A_STAGE = BM * AS;
-    static constexpr int B_STAGE = BK * BS;
-    static constexpr int LDS_FLOATS = 2 * (A_STAGE + B_STAGE);
-    static constexpr int A_LD = BM * BK / 4 / NT;  // float4 loads per thread per panel
-    static constexpr int B_LD = BK * BN / 4 / NT;
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
-    static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "panel split");
-    static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget of one CU");
-};
-
-// Load one float4 of a row-major matrix X at (r, c) .. (r, c+3).
-template <bool MASKED, bool VEC>
-__device__ __forceinline__ float4 load4(const float* __restrict__ X, int64_t ld, int r, int c,
-                                        int rows, int cols) {
-    if (!MASKED) {
-        return *reinterpret_cast<const float4*>(X + (int64_t)r * ld + c);
-    } else {
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < rows) {
-            const float* p = X + (int64_t)r * ld + c;
-            if (VEC && c + 3 < cols) {
-                v = *reinterpret_cast<const float4*>(p);
-            } else {
-                if (c + 0 < cols) v.x = p[0];
-                if (c + 1 < cols) v.y = p[1];
-                if (c + 2 < cols) v.z = p[2];
-                if (c + 3 < cols) v.w = p[3];
-            }
-        }
-        return v;
-    }
-}
-
-template <int BM, int BN, int BK, int WM, int WN, int GM, bool MASKED, bool VEC>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_f32_kernel(F32Args p) {
-    using S = F32Shape<BM, BN, BK, WM, WN>;
-    __shared__ __attribute__((aligned(16))) float smem[S::LDS_FLOATS];
-    float* const As = smem;                     // [2][BM][AS]
-    float* const Bs = smem + 2 * S::A_STAGE;    // [2][BK][BS]
-
-    int tm, tn;
-    tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wr = wave / WN, wc = wave % WN;
-    const int h = lane >> 5;    // lane half: which k sub-range this lane feeds
-    const int r32 = lane & 31;  // row (A) / column (B) of the 32x32 block
-
-    const float* __restrict__ A = p.A + (int64_t)m0 * p.lda;
-    const float* __restrict__ B = p.B + n0;
-    const int rows_a = p.M - m0;   // valid rows of this tile (masked variant)
-    const int cols_b = p.N - n0;
-
-    float4 ra[S::A_LD], rb[S::B_LD];
-
-    auto load_panels = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < S::A_LD; ++i) {
-            const int idx = tid + i * S::NT;
-            const int r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
-            ra[i] = load4<MASKED, VEC>(A, p.lda, r, k0 + c, rows_a, p.K);
-        }
-#pragma unroll
-        for (int i = 0; i < S::B_LD; ++i) {
-            const int idx = tid + i * S::NT;
-            const int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
-            // rows of B are k: valid while k0 + r < K; columns valid while < cols_b
-            float4 v;
-            if (!MASKED) {
-                v = *reinterpret_cast<const float4*>(B + (int64_t)(k0 + r) * p.ldb + c);
-            } else {
-                v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (k0 + r < p.K) {
-                    const float* q = B + (int64_t)(k0 + r) * p.ldb + c;
-                    if (VEC && c + 3 < cols_b) {
-                        v = *reinterpret_cast<const float4*>(q);
-                    } else {
-                        if (c + 0 < cols_b) v.x = q[0];
-                        if (c + 1 < cols_b) v.y = q[1];
-                        if (c + 2 < cols_b) v.z = q[2];
-                        if (c + 3 < cols_b) v.w = q[3];
-                    }
-                }
-            }
-            rb[i] = v;
-        }
-    };
-    auto store_panels = [&](int stage) {
-        float* as = As + stage * S::A_STAGE;
-        float* bs = Bs + stage * S::B_STAGE;
-#pragma unroll
-        for (int i = 0; i < S::A_LD; ++i) {
-            const int idx = tid + i * S::NT;
-            const int r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
-            *reinterpret_cast<float4*>(as + r * S::AS + c) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < S::B_LD; ++i) {
-            const int idx = tid + i * S::NT;
-            const int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
-            *reinterpret_cast<float4*>(bs + r * S::BS + c) = rb[i];
-        }
-    };
-
-    f32x16 acc[S::FM][S::FN];
-#pragma unroll
-    for (int i = 0; i < S::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < S::FN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-    const int nk = (p.K + BK - 1) / BK;
-    load_panels(0);
-    store_panels(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) load_panels((kt + 1) * BK);
-
-        // The panel pair in LDS: lane half h supplies k in [h*KH, (h+1)*KH) of
-        // the panel, one k per instruction, to both operands alike, so every
-        // instruction sums matching k of A and B.
-        const float* as = As + cur * S::A_STAGE;
-        const float* bs = Bs + cur * S::B_STAGE;
-        float a[S::FM][S::KH];
-        float b[S::FN][S::KH];
-#pragma unroll
-        for (int i = 0; i < S::FM; ++i) {
-            const float* src = as + (wr * S::TM + i * 32 + r32) * S::AS + h * S::KH;
-#pragma unroll
-            for (int q = 0; q < S::KH / 4; ++q) {
-                const float4 v = *reinterpret_cast<const float4*>(src + 4 * q);
-                a[i][4 * q + 0] = v.x;
-                a[i][4 * q + 1] = v.y;
-                a[i][4 * q + 2] = v.z;
-                a[i][4 * q + 3] = v.w;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < S::FN; ++j) {
-            const float* src = bs + (h * S::KH) * S::BS + wc * S::TN + j * 32 + r32;
-#pragma unroll
-            for (int s = 0; s < S::KH; ++s) b[j][s] = src[s * S::BS];
-        }
-#pragma unroll
-        for (int s = 0; s < S::KH; ++s)
-#pragma unroll
-            for (int i = 0; i < S::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < S::FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j],
-                                                                      0, 0, 0);
-
-        if (more) store_panels(cur ^ 1);
-        __syncthreads();
-    }
-
-    // Epilogue: C = alpha*acc + beta*C over this wave's part of the tile.
-    store_tile<S::FM, S::FN, MASKED>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N,
-                                     p.alpha, p.beta, lane);
-}
-
 template <int BM, int BN, int BK, int WM, int WN, int GM>
 hipError_t launch_f32(const F32Args& a, F32Variant v, hipStream_t s) {
-    const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
-    if (!v.masked) {
-        gemm_f32_kernel<BM, BN, BK, WM, WN, GM, false, true><<<grid, block, 0, s>>>(a);
-    } else if (v.vec) {
-        gemm_f32_kernel<BM, BN, BK, WM, WN, GM, true, true><<<grid, block, 0, s>>>(a);
-    } else {
-        gemm_f32_kernel<BM, BN, BK, WM, WN, GM, true, false><<<grid, block, 0, s>>>(a);
-    }
-    return hipGetLastError();
+    if (v.ta || v.tb) return launch_f32_transposed<BM, BN, BK, WM, WN, GM>(a, v, s);
+    return launch_f32_layout<BM, BN, BK, WM, WN, GM, false, false>(a, v, s);
 }
 
-#define F32_INSTANCE(BM, BN, BK, WM, WN, GM) \
-    {{GEMM355_MODE_F32, BM, BN, BK, 2, WM, WN, GM}, &launch_f32<BM, BN, BK, WM, WN, GM>}
+#define G355_F32_INSTANCE(BM, BN, BK, WM, WN, GM) \
+    {{GEMM355_MODE_F32, BM, BN, BK, 2, WM, WN, GM}, &launch_f32<BM, BN, BK, WM, WN, GM>},
 
-const F32Instance kF32Instances[] = {
-    F32_INSTANCE(256, 256, 16, 2, 2, 8),
-    F32_INSTANCE(256, 128, 16, 2, 2, 8),
-    F32_INSTANCE(128, 256, 16, 2, 2, 8),
-    F32_INSTANCE(128, 128, 16, 2, 2, 8),
-    F32_INSTANCE(128, 128, 32, 2, 2, 8),
-    F32_INSTANCE(128, 64, 16, 2, 2, 8),
-    F32_INSTANCE(64, 64, 16, 2, 2, 8),
-    F32_INSTANCE(64, 64, 32, 2, 2, 8),
-};
+const F32Instance kF32Instances[] = {G355_F32_CONFIGS(G355_F32_INSTANCE)};
 
 }  // namespace
 

@@ -54,6 +54,8 @@ struct F16Args {
 struct F32Variant {
     bool masked;  // some of M, N, K is not a tile multiple
     bool vec;     // 16-byte global loads are legal (lda, ldb % 4 == 0, aligned pointers)
+    bool ta = false;   // op(A) = A^T: A is stored K x M
+    bool tb = false;   // op(B) = B^T: B is stored N x K
 };
 
 using F32Launch = hipError_t (*)(const F32Args&, F32Variant, hipStream_t);
@@ -72,12 +74,13 @@ struct F16Instance {
 const F32Instance* f32_instances(int* count);
 const F16Instance* f16_instances(int* count);
 
-// Rounding and packing pass of the f16r mode: A (M x K) into Mp x Kp and B
-// (K x N) transposed into Np x Kp, Mp, Np multiples of 256, Kp of 64, in one
-// launch, in depth blocks of `depth` (32 or 64) values.
-hipError_t launch_pack(const float* A, int64_t lda, const float* B, int64_t ldb, int M, int N,
-                       int K, uint16_t* A16, uint16_t* B16t, int64_t mp, int64_t np, int64_t kp,
-                       int depth, hipStream_t s);
+// Rounding and packing pass of the f16r mode: op(A) (M x K) into Mp x Kp and
+// op(B) (K x N) transposed into Np x Kp, Mp, Np multiples of 256, Kp of 64, in
+// one launch, in depth blocks of `depth` (32 or 64) values.  ta: A is stored
+// K x M (op(A) = A^T); tb: B is stored N x K (op(B) = B^T).
+hipError_t launch_pack(const float* A, int64_t lda, bool ta, const float* B, int64_t ldb,
+                       bool tb, int M, int N, int K, uint16_t* A16, uint16_t* B16t, int64_t mp,
+                       int64_t np, int64_t kp, int depth, hipStream_t s);
 
 // C = beta*C (beta == 0: C = 0 without reading it).
 hipError_t launch_scale_c(float* C, int64_t ldc, int M, int N, float beta, hipStream_t s);

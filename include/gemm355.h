@@ -87,28 +87,62 @@ int gemm_f16r_f32acc(int64_t M, int64_t N, int64_t K, float alpha,
                      float beta, float* C, int64_t ldc, void* stream);
 
 /*
+ * Operand layouts (the Matrix Multiplication lab, "Part 5", the layout sweep;
+ * the transa/transb arguments of the BLAS GEMM interface the lab calls):
+ *
+ *     C = alpha * op(A) @ op(B) + beta * C
+ *
+ * with op(A) M x K and op(B) K x N:
+ *   transa = 0: A is stored M x K, A[i*lda + k], lda >= max(1, K);
+ *   transa = 1: A is stored K x M, op(A)[i][k] = A[k*lda + i], lda >= max(1, M);
+ *   transb = 0: B is stored K x N, B[k*ldb + j], ldb >= max(1, N);
+ *   transb = 1: B is stored N x K, op(B)[k][j] = B[j*ldb + k], ldb >= max(1, K).
+ * Everything else (ownership, stream, special cases, rounding of the f16r
+ * mode, which applies to the elements whatever their layout) is as for
+ * gemm_f32 / gemm_f16r_f32acc, which are the transa = transb = 0 case.
+ * Return codes follow BLAS sgemm's argument numbers: -1 transa, -2 transb
+ * (not 0 or 1), -3 M, -4 N, -5 K, -7 A, -8 lda, -9 B, -10 ldb, -12 C,
+ * -13 ldc; library errors and hipError_t values as gemm_f32.
+ */
+int gemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
+                const float* A, int64_t lda, const float* B, int64_t ldb,
+                float beta, float* C, int64_t ldc, void* stream);
+int gemm_f16r_f32acc_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
+                        const float* A, int64_t lda, const float* B, int64_t ldb,
+                        float beta, float* C, int64_t ldc, void* stream);
+
+/*
  * Per-shape tile autotuning (phobos docs, "gemm, f32", section "Tuning": time
  * every configuration briefly, skip those that fail, then re-time the fastest
  * few over interleaved rounds under the same clocks).  Runs the candidates on
  * the caller's A and B and on a scratch C the library allocates and frees
  * (the caller's C is not touched), synchronises `stream`, and stores the
  * winner in the per-shape cache used by later calls with the same key
- * (mode, M, N, K, alignment class of lda/ldb/ldc and pointers, beta == 0).
- * `beta` only selects the key and the epilogue variant timed.
- * Returns 0, a negative argument/library error, or a positive hipError_t.
+ * (mode, operand layout, M, N, K, alignment class of lda/ldb and pointers,
+ * beta == 0).  `beta` only selects the key and the epilogue variant timed.
+ * Returns 0, a negative argument code (numbered as the same argument of
+ * gemm_f32), a library error, or a positive hipError_t.  gemm355_tune_ex takes
+ * the operand layout as gemm_f32_ex and numbers its argument codes as there.
  */
 int gemm355_tune(int mode, int64_t M, int64_t N, int64_t K,
                  const float* A, int64_t lda, const float* B, int64_t ldb,
                  float beta, int64_t ldc, void* stream);
+int gemm355_tune_ex(int mode, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                    const float* A, int64_t lda, const float* B, int64_t ldb,
+                    float beta, int64_t ldc, void* stream);
 
 /*
  * The tile configuration a call with these arguments would use, written as
  * "BM=.. BN=.. BK=.. ST=.. WM=.. WN=.. GM=.." plus " source=pin|tuned|heuristic"
  * into buf (NUL-terminated, at most len bytes).  Host only; no GPU call.
+ * gemm355_get_config_ex: the same for the operand layout (transa, transb).
  */
 int gemm355_get_config(int mode, int64_t M, int64_t N, int64_t K,
                        int64_t lda, int64_t ldb, int64_t ldc, float beta,
                        char* buf, size_t len);
+int gemm355_get_config_ex(int mode, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                          int64_t lda, int64_t ldb, int64_t ldc, float beta,
+                          char* buf, size_t len);
 
 /*
  * Pin one tile configuration for every later call of `mode`, skipping the

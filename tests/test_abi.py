@@ -74,6 +74,64 @@ def test_argument_checks_follow_xerbla_numbering(name):
     assert _call(fn, 4, 4, 0, lda=0) == -6
 
 
+def _call_ex(fn, ta, tb, M, N, K, A=FAKE, lda=None, B=FAKE, ldb=None, C=FAKE, ldc=None):
+    lda = max(M if ta else K, 1) if lda is None else lda
+    ldb = max(K if tb else N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return fn(ta, tb, M, N, K, 1.0, A, lda, B, ldb, 0.0, C, ldc, None)
+
+
+@pytest.mark.parametrize("name", ["gemm_f32_ex", "gemm_f16r_f32acc_ex"])
+def test_layout_argument_checks_follow_sgemm_numbering(name):
+    """op(A) = A^T is stored K x M (lda >= M), op(B) = B^T N x K (ldb >= K);
+    codes are BLAS sgemm's argument numbers."""
+    fn = getattr(g.lib(), name)
+    assert _call_ex(fn, 2, 0, 4, 4, 4) == -1
+    assert _call_ex(fn, 0, -1, 4, 4, 4) == -2
+    assert _call_ex(fn, 0, 0, -1, 4, 4) == -3
+    assert _call_ex(fn, 1, 0, 4, -1, 4) == -4
+    assert _call_ex(fn, 0, 1, 4, 4, -1) == -5
+    assert _call_ex(fn, 1, 1, 4, 4, 4, A=None) == -7
+    assert _call_ex(fn, 0, 0, 4, 4, 8, lda=7) == -8
+    # transposed A: the row of the stored array has M elements
+    assert _call_ex(fn, 1, 0, 8, 4, 4, lda=7) == -8
+    assert _call_ex(fn, 1, 1, 4, 4, 4, B=None) == -9
+    assert _call_ex(fn, 0, 1, 4, 4, 8, ldb=7) == -10
+    assert _call_ex(fn, 0, 0, 4, 8, 4, ldb=7) == -10
+    assert _call_ex(fn, 0, 0, 4, 4, 4, C=None) == -12
+    assert _call_ex(fn, 1, 1, 4, 8, 4, ldc=7) == -13
+    # M == 0: nothing to do, whatever the layout
+    assert _call_ex(fn, 1, 1, 0, 5, 7, A=None, B=None, C=None) == 0
+
+
+def test_layout_configs_are_keyed_apart(tmp_path):
+    """The tuning cache keys the operand layout: a tuned transposed shape does
+    not leak into the plain layout of the same shape, and the cache file names
+    the layout after the mode ("f32:TN")."""
+    path = tmp_path / "tune.txt"
+    cfg = g.list_configs("f32")[-1]
+    path.write_text(f"f32:TN 2048 2048 2048 1 1 1 {cfg}\nf32:XY 64 64 64 1 1 1 {cfg}\n")
+    g.cache_clear()
+    try:
+        assert g.cache_load(str(path)) == 1
+        assert g.get_config("f32", 2048, 2048, 2048, transa=True) == cfg + " source=tuned"
+        assert g.get_config("f32", 2048, 2048, 2048).endswith("source=heuristic")
+        assert g.get_config("f32", 2048, 2048, 2048, transb=True).endswith("source=heuristic")
+        out = tmp_path / "saved.txt"
+        assert g.cache_save(str(out)) == 1
+        assert out.read_text().strip() == f"f32:TN 2048 2048 2048 1 1 1 {cfg}"
+    finally:
+        g.cache_clear()
+    # the plain-layout codes of get_config are unchanged by the _ex numbering
+    buf = ctypes.create_string_buffer(64)
+    assert g.lib().gemm355_get_config(0, 4, 4, 8, 7, 4, 4, 0.0, buf, 64) == -6
+    assert g.lib().gemm355_get_config_ex(0, 1, 0, 8, 4, 4, 7, 4, 4, 0.0, buf, 64) == -8
+    assert g.lib().gemm355_get_config_ex(0, 0, 3, 8, 4, 4, 4, 4, 4, 0.0, buf, 64) == -2
+    # transposed A with K > M: lda >= M suffices (host-only check, no launch)
+    assert g.lib().gemm355_get_config_ex(0, 1, 0, 8, 4, 16, 8, 4, 4, 0.0, buf, 64) == 0
+    assert g.lib().gemm355_get_config_ex(1, 1, 1, 8, 4, 16, 8, 16, 4, 0.0, buf, 64) == 0
+
+
 @pytest.mark.parametrize("name", ["gemm_f32", "gemm_f16r_f32acc"])
 def test_empty_output_returns_without_launch(name):
     fn = getattr(g.lib(), name)
