@@ -68,6 +68,9 @@ def main():
                     help="shape and alignment sweep of both modes (sizes 128..8192, n = "
                          "4088..4104 and 2048..2304, fixed-tile steps); markdown to OUT_MD")
     ap.add_argument("--sweep-repeats", type=int, default=3)
+    ap.add_argument("--skinny", metavar="OUT_MD", default=None,
+                    help="few-rows sweep (M = 1..2048 at K = N = 4096, both modes) against "
+                         "the HBM and matrix-core roofs; markdown to OUT_MD")
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -104,6 +107,9 @@ def main():
 
     if args.sweep:
         shape_sweep(g, torch, dev, args.sweep, args.sweep_repeats)
+        return
+    if args.skinny:
+        skinny_sweep(g, torch, dev, args.skinny, args.sweep_repeats)
         return
 
     # ------------------------------------------------------------------ roofs
@@ -389,7 +395,7 @@ def _path_of(mode, n, tile):
     t = _tile_fields(tile)
     if mode == "f32":
         ragged = n % t["BM"] or n % t["BN"] or n % t["BK"]
-        return ("masked" if ragged else "aligned") + ("" if n % 4 == 0 else ", 4-byte loads")
+        return ("masked" if ragged else "aligned") + ("" if n % 4 == 0 else ", rows 4-byte aligned")
     return "masked store" if (n % t["BM"] or n % t["BN"]) else "aligned"
 
 
@@ -488,6 +494,111 @@ def shape_sweep(g, torch, dev, out, repeats):
                          f"{r['seconds_min'] * 1e3:.3f}..{r['seconds_max'] * 1e3:.3f} | "
                          f"{r['tile']} | {r['path']} |")
     lines += ["", "```json", json.dumps(rows), "```", ""]
+    _write(out, "\n".join(lines))
+
+
+# ---------------------------------------------------------------------------
+# Few rows of C (the lab's "Part 5", the skinny shapes: M from 1 up at
+# K = N = 4096).  Arithmetic intensity I = 2MNK / (4(MK + KN + MN)) bytes of
+# f32 storage; below the ridge the HBM roof bounds the call.
+# ---------------------------------------------------------------------------
+SKINNY_M = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048]
+
+
+def skinny_sweep(g, torch, dev, out, repeats):
+    import random
+
+    import oracle
+    from workloads import make_inputs, sample_indices
+
+    roofs = measure_roofs(g, torch, dev, 1.0)
+    log(f"skinny: roofs {json.dumps(roofs)}")
+    K = N = 4096
+    _, B, _ = make_inputs(1, N, K, "normal", seed=4096)
+    tB = torch.from_numpy(B).to(dev)
+    cases = []
+    for M in SKINNY_M:
+        A = make_inputs(M, 1, K, "normal", seed=M)[0]       # M x K
+        C = make_inputs(M, N, 1, "normal", seed=M + 1)[2]   # M x N
+        r, c = sample_indices(M, N, 256, seed=3)
+        tA, tC = torch.from_numpy(A).to(dev), torch.from_numpy(C).to(dev)
+        for mode in ("f32", "f16r"):
+            ref, W = oracle.entries(mode, A, B, C, 1.0, 0.0, r, c)
+            for kind in ("tuned", "no split-K"):
+                cases.append((mode, M, kind, tA, tC, r, c, ref, W))
+    calls, tiles = {}, {}
+    for (mode, M, kind, tA, tC, r, c, ref, W) in cases:
+        fn = g.gemm_f32 if mode == "f32" else g.gemm_f16r_f32acc
+        key = (mode, M, kind)
+        if kind == "tuned":
+            g.tune(mode, tA, tB, tC, beta=0.0)
+            tiles[key] = g.get_config(mode, M, N, K, beta=0.0)
+            call = (lambda fn=fn, tA=tA, tC=tC: fn(tA, tB, tC, 1.0, 0.0))
+        else:
+            # the library's best configuration without split-K (tuned over the rest)
+            best, best_t = None, 1e30
+            for cfg in g.list_configs(mode):
+                if "KS=" in cfg:
+                    continue
+                g.set_config(mode, cfg)
+                try:
+                    t = steady(lambda fn=fn, tA=tA, tC=tC: fn(tA, tB, tC, 1.0, 0.0), torch, 0.05)
+                finally:
+                    g.set_config(mode, None)
+                if t < best_t:
+                    best, best_t = cfg, t
+            tiles[key] = best
+
+            def call(fn=fn, tA=tA, tC=tC, mode=mode, cfg=best):
+                g.set_config(mode, cfg)
+                try:
+                    fn(tA, tB, tC, 1.0, 0.0)
+                finally:
+                    g.set_config(mode, None)
+        call()
+        torch.cuda.synchronize()
+        got = tC[torch.as_tensor(r, device=dev), torch.as_tensor(c, device=dev)].cpu().numpy()
+        if not np.all(np.abs(got.astype(np.float64) - ref) <= oracle.TOL[mode] * W):
+            raise SystemExit(f"skinny {key}: outside the parity bound")
+        calls[key] = call
+    times = {k: [] for k in calls}
+    rng = random.Random(1)
+    for rnd in range(repeats):
+        order = list(calls)
+        rng.shuffle(order)
+        for k in order:
+            times[k].append(steady(calls[k], torch, seconds=0.2))
+        log(f"skinny: round {rnd + 1} of {repeats} done")
+    rows = []
+    hbm = roofs["hbm_read_gbs"] * 1e9
+    for (mode, M, kind), ts in times.items():
+        t = float(np.median(ts))
+        flops = 2.0 * M * N * K
+        nbytes = 4.0 * (M * K + K * N + M * N)
+        intensity = flops / nbytes
+        mfma = roofs["mfma_f32_tflops" if mode == "f32" else "mfma_f16r_tflops"] * 1e12
+        roof = min(mfma, intensity * hbm)
+        rows.append({"mode": mode, "M": M, "kind": kind, "tile": tiles[(mode, M, kind)].split(
+            " source=")[0], "seconds": t, "tflops": flops / t / 1e12,
+            "gbs": nbytes / t / 1e9, "intensity": intensity, "roof_tflops": roof / 1e12,
+            "bound": "hbm" if intensity * hbm < mfma else "mfma", "frac_of_roof": flops / t / roof})
+    lines = ["# Few rows of C: M = 1 .. 2048 at K = N = 4096 (both modes, one MI355X)", "",
+             "Command:", "", "```", "python bench.py --skinny profiles/skinny_m.md", "```", "",
+             "A (M x K), B (K x N), C iid N(0,1); alpha = 1, beta = 0.  Every case is checked "
+             "against the oracle on 256 sampled elements before it is timed; the time is the "
+             f"median of {repeats} shuffled rounds of steady() (0.2 s).  Bytes are the f32 "
+             "storage the call must move at least once, 4(MK + KN + MN); the roof is "
+             "min(measured matrix-core roof of the mode, intensity x measured HBM read roof "
+             f"{roofs['hbm_read_gbs']:.0f} GB/s).  `tuned` is the library's own choice (the "
+             "split-K configuration is one of the candidates); `no split-K` is the fastest "
+             "configuration without it.", "",
+             "| mode | M | choice | TFLOP/s | GB/s | FLOP/B | bound | of roof | tile |",
+             "|---|---:|---|---:|---:|---:|---|---:|---|"]
+    for r_ in sorted(rows, key=lambda r_: (r_["mode"], r_["M"], r_["kind"])):
+        lines.append(f"| {r_['mode']} | {r_['M']} | {r_['kind']} | {r_['tflops']:.2f} | "
+                     f"{r_['gbs']:.0f} | {r_['intensity']:.1f} | {r_['bound']} | "
+                     f"{r_['frac_of_roof']:.2f} | {r_['tile']} |")
+    lines += ["", "```json", json.dumps({"roofs": roofs, "rows": rows}), "```", ""]
     _write(out, "\n".join(lines))
 
 

@@ -19,6 +19,32 @@ __global__ __launch_bounds__(256) void scale_c_kernel(float* __restrict__ C, int
     }
 }
 
+// Second pass of the split-K configuration: C = alpha * (P[0] + P[1] + ...) +
+// beta * C, the slices summed in order; beta == 0 does not read C.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int S,
+                                                            int M, int N, float alpha, float beta,
+                                                            float* __restrict__ C, int64_t ldc) {
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= N) return;
+    const int64_t slice = static_cast<int64_t>(M) * N;
+    for (int row = blockIdx.y; row < M; row += gridDim.y) {
+        const float* p = P + static_cast<int64_t>(row) * N + col;
+        float* c = C + static_cast<int64_t>(row) * ldc + col;
+        const float old = (beta == 0.f) ? 0.f : *c;
+        // eight slices' loads in flight at a time, added in slice order
+        float sum = 0.f;
+        for (int z0 = 0; z0 < S; z0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = (z0 + u < S) ? p[(z0 + u) * slice] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (z0 + u < S) sum += v[u];
+        }
+        *c = (beta == 0.f) ? alpha * sum : alpha * sum + beta * old;
+    }
+}
+
 // Matrix-core roofs (the lab's "Part 1": a kernel of nothing but independent
 // multiply-adds).  Each wave keeps 8 independent accumulator blocks so the
 // matrix unit never waits on a previous result.
@@ -91,6 +117,14 @@ __global__ void copy_tail_kernel(const float* __restrict__ src, float* __restric
 }
 
 }  // namespace
+
+hipError_t launch_splitk_reduce(const float* P, int S, int M, int N, float alpha, float beta,
+                                float* C, int64_t ldc, hipStream_t s) {
+    const unsigned gx = static_cast<unsigned>((N + 255) / 256);
+    const unsigned gy = static_cast<unsigned>(M < 4096 ? M : 4096);
+    splitk_reduce_kernel<<<dim3(gx, gy), 256, 0, s>>>(P, S, M, N, alpha, beta, C, ldc);
+    return hipGetLastError();
+}
 
 hipError_t launch_scale_c(float* C, int64_t ldc, int M, int N, float beta, hipStream_t s) {
     const unsigned gx = static_cast<unsigned>((N + 255) / 256);

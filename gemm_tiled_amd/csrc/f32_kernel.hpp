@@ -93,7 +93,13 @@ __device__ __forceinline__ float4 load4(const float* __restrict__ X, int64_t ld,
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int GM, bool MASKED, bool VEC, bool TA, bool TB>
+// SPLIT: this workgroup covers the K slice blockIdx.y (see F32Args) and
+// stores its raw partial tile.  R16: operands are rounded to binary16 (round
+// to nearest even) as they are staged; the f32 matrix instruction then
+// multiplies binary16 values exactly and accumulates in f32, which is the
+// f16r mode's arithmetic.
+template <int BM, int BN, int BK, int WM, int WN, int GM, bool MASKED, bool VEC, bool TA, bool TB,
+          bool SPLIT = false, bool R16 = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_kernel(F32Args p) {
     using S = F32Shape<BM, BN, BK, WM, WN, TA, TB>;
     __shared__ __attribute__((aligned(16))) float smem[S::LDS_FLOATS];
@@ -117,6 +123,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_kernel(F32Args p) {
     const float* __restrict__ B = TB ? p.B + (int64_t)n0 * p.ldb : p.B + n0;
     const int rows_a = p.M - m0;   // valid rows of op(A) in this tile (masked variant)
     const int cols_b = p.N - n0;   // valid columns of op(B)
+    // the K range of this workgroup: everything, or one slice
+    const int k_lo = SPLIT ? static_cast<int>(blockIdx.y) * p.ksplit : 0;
+    const int k_hi = SPLIT ? min(p.K, k_lo + p.ksplit) : p.K;
 
     float4 ra[S::A_LD], rb[S::B_LD];
 
@@ -128,10 +137,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_kernel(F32Args p) {
             const int idx = tid + i * S::NT;
             if (!TA) {   // BM rows (m) of BK contiguous k
                 const int r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
-                ra[i] = load4<MASKED, VEC>(A, p.lda, r, k0 + c, rows_a, p.K);
+                ra[i] = load4<MASKED, VEC>(A, p.lda, r, k0 + c, rows_a, k_hi);
             } else {     // BK rows (k) of BM contiguous m
                 const int r = idx / (BM / 4), c = (idx % (BM / 4)) * 4;
-                ra[i] = load4<MASKED, VEC>(A, p.lda, k0 + r, c, p.K, rows_a);
+                ra[i] = load4<MASKED, VEC>(A, p.lda, k0 + r, c, k_hi, rows_a);
             }
         }
 #pragma unroll
@@ -139,16 +148,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_kernel(F32Args p) {
             const int idx = tid + i * S::NT;
             if (!TB) {   // BK rows (k) of BN contiguous n
                 const int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
-                rb[i] = load4<MASKED, VEC>(B, p.ldb, k0 + r, c, p.K, cols_b);
+                rb[i] = load4<MASKED, VEC>(B, p.ldb, k0 + r, c, k_hi, cols_b);
             } else {     // BN rows (n) of BK contiguous k
                 const int r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
-                rb[i] = load4<MASKED, VEC>(B, p.ldb, r, k0 + c, cols_b, p.K);
+                rb[i] = load4<MASKED, VEC>(B, p.ldb, r, k0 + c, cols_b, k_hi);
             }
+        }
+    };
+    auto round16 = [](float4& v) {
+        if (R16) {
+            v.x = static_cast<float>(static_cast<_Float16>(v.x));
+            v.y = static_cast<float>(static_cast<_Float16>(v.y));
+            v.z = static_cast<float>(static_cast<_Float16>(v.z));
+            v.w = static_cast<float>(static_cast<_Float16>(v.w));
         }
     };
     auto store_panels = [&](int stage) {
         float* as = As + stage * S::A_STAGE;
         float* bs = Bs + stage * S::B_STAGE;
+#pragma unroll
+        for (int i = 0; i < S::A_LD; ++i) round16(ra[i]);
+#pragma unroll
+        for (int i = 0; i < S::B_LD; ++i) round16(rb[i]);
 #pragma unroll
         for (int i = 0; i < S::A_LD; ++i) {
             const int idx = tid + i * S::NT;
@@ -173,15 +194,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_kernel(F32Args p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    const int nk = (p.K + BK - 1) / BK;
-    load_panels(0);
+    const int nk = (k_hi - k_lo + BK - 1) / BK;
+    load_panels(k_lo);
     store_panels(0);
     __syncthreads();
 
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         const bool more = kt + 1 < nk;
-        if (more) load_panels((kt + 1) * BK);
+        if (more) load_panels(k_lo + (kt + 1) * BK);
 
         // The panel pair in LDS: lane half h supplies k in [h*KH, (h+1)*KH) of
         // the panel, one k per instruction, to both operands alike, so every
@@ -241,6 +262,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_kernel(F32Args p) {
         __syncthreads();
     }
 
+    if (SPLIT) {
+        // the raw partial tile of this slice (1 * acc is exact; beta = 0 reads nothing)
+        float* P = p.C + static_cast<int64_t>(blockIdx.y) * p.M * p.ldc;
+        store_tile<S::FM, S::FN, MASKED>(acc, P, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M,
+                                         p.N, 1.0f, 0.0f, lane);
+        return;
+    }
     // Epilogue: C = alpha*acc + beta*C over this wave's part of the tile.
     store_tile<S::FM, S::FN, MASKED>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N,
                                      p.alpha, p.beta, lane);

@@ -37,6 +37,16 @@ bool log_debug() {
 
 const char* mode_name(int mode) { return mode == GEMM355_MODE_F32 ? "f32" : "f16r"; }
 
+// Up to this many rows of C the heuristic picks the split-K configuration.
+constexpr int64_t kSplitKRows = 64;
+// Compute units of the MI355X (gfx950).
+constexpr int64_t kCUs = 256;
+// Workgroups a split-K launch aims for (three per CU), the least k per slice,
+// and the most bytes its partial tiles may take in the workspace.
+constexpr int64_t kSplitKTarget = 3 * kCUs;
+constexpr int64_t kSplitKMinDepth = 128;
+constexpr int64_t kSplitKMaxBytes = int64_t{1} << 30;
+
 // ---------------------------------------------------------------------------
 // Instances and configuration strings.
 // ---------------------------------------------------------------------------
@@ -50,6 +60,7 @@ std::vector<TileConfig> configs_of(int mode) {
         const F16Instance* t = f16_instances(&n);
         for (int i = 0; i < n; ++i) out.push_back(t[i].cfg);
     }
+    out.push_back(splitk_config(mode));
     return out;
 }
 
@@ -57,13 +68,17 @@ std::string format_config(const TileConfig& c) {
     char b[128];
     std::snprintf(b, sizeof b, "BM=%d BN=%d BK=%d ST=%d WM=%d WN=%d GM=%d", c.bm, c.bn, c.bk,
                   c.st, c.wm, c.wn, c.gm);
-    return b;
+    std::string out = b;
+    if (c.ks) out += " KS=" + std::to_string(c.ks);
+    return out;
 }
 
 // Parse "KEY=VALUE ..." into the first compiled instance matching every given
 // key.  Returns false on a syntax error, an unknown key or no match.
 bool parse_config(int mode, const char* spec, TileConfig* out) {
-    int want[7] = {-1, -1, -1, -1, -1, -1, -1};   // bm bn bk wm wn gm st
+    // bm bn bk wm wn gm st ks; an absent key matches any value, except KS,
+    // whose absence means the configurations without split-K (KS = 0)
+    int want[8] = {-1, -1, -1, -1, -1, -1, -1, 0};
     const char* p = spec;
     bool any = false;
     while (*p) {
@@ -76,7 +91,7 @@ bool parse_config(int mode, const char* spec, TileConfig* out) {
         ++p;
         char* end = nullptr;
         const long v = std::strtol(p, &end, 10);
-        if (end == p || v <= 0 || v > 4096) return false;
+        if (end == p || v < 0 || v > 4096) return false;
         if (*end && !std::isspace(static_cast<unsigned char>(*end))) return false;
         p = end;
         for (auto& ch : key) ch = static_cast<char>(std::toupper(static_cast<unsigned char>(ch)));
@@ -88,15 +103,16 @@ bool parse_config(int mode, const char* spec, TileConfig* out) {
         else if (key == "WN") slot = 4;
         else if (key == "GM") slot = 5;
         else if (key == "ST" || key == "STAGES") slot = 6;
-        if (slot < 0) return false;
+        else if (key == "KS" || key == "SPLITK") slot = 7;
+        if (slot < 0 || (v == 0 && slot != 7)) return false;
         want[slot] = static_cast<int>(v);
         any = true;
     }
     if (!any) return false;
     for (const TileConfig& c : configs_of(mode)) {
-        const int have[7] = {c.bm, c.bn, c.bk, c.wm, c.wn, c.gm, c.st};
+        const int have[8] = {c.bm, c.bn, c.bk, c.wm, c.wn, c.gm, c.st, c.ks};
         bool ok = true;
-        for (int i = 0; i < 7; ++i)
+        for (int i = 0; i < 8; ++i)
             if (want[i] >= 0 && want[i] != have[i]) ok = false;
         if (ok) {
             *out = c;
@@ -184,10 +200,13 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // efficiency of the tile), the trade-off of the phobos "Tuning" section:
 // larger tiles reuse more, but leave fewer workgroups to fill the chip.
 TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K) {
+    // a few rows of C: the split-K configuration (memory-bound, too few tiles)
+    if (M <= kSplitKRows) return splitk_config(mode);
     const std::vector<TileConfig> all = configs_of(mode);
     double best = 1e300;
     TileConfig pick = all.front();
     for (const TileConfig& c : all) {
+        if (c.ks) continue;
         const double tiles = static_cast<double>((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         const double per_cu = (c.bm * c.bn >= 256 * 128) ? 1.0 : 2.0;
         const double rounds = std::ceil(tiles / (256.0 * per_cu));
@@ -295,9 +314,55 @@ int check_args(int trans, int64_t M, int64_t N, int64_t K, float alpha, const fl
 
 int status_of(hipError_t e) { return e == hipSuccess ? 0 : static_cast<int>(e); }
 
+// The split-K configuration: slices of K chosen so that tiles x slices reaches
+// kSplitKTarget workgroups, each slice at least kSplitKMinDepth deep (a
+// multiple of BK), the partial tiles within kSplitKMaxBytes.  One slice runs
+// the normal epilogue; more go through the workspace and the reduction.
+int launch_splitk(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
+                  const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                  int64_t ldc, hipStream_t s) {
+    const int tiles_m = static_cast<int>((M + cfg.bm - 1) / cfg.bm);
+    const int tiles_n = static_cast<int>((N + cfg.bn - 1) / cfg.bn);
+    const int64_t tiles = int64_t{tiles_m} * tiles_n;
+    int64_t slices = std::max<int64_t>(1, (kSplitKTarget + tiles - 1) / tiles);
+    slices = std::min(slices, std::max<int64_t>(1, K / kSplitKMinDepth));
+    slices = std::min(slices, std::max<int64_t>(1, kSplitKMaxBytes / (M * N * 4)));
+    int64_t depth = round_up((K + slices - 1) / slices, cfg.bk);
+    slices = (K + depth - 1) / depth;
+    F32Args a{A, B, C, lda, ldb, ldc, static_cast<int>(M), static_cast<int>(N),
+              static_cast<int>(K), alpha, beta, tiles_m, tiles_n};
+    F32Variant v;
+    v.vec = vec_ok(A, lda) && vec_ok(B, ldb);
+    // every slice but the last is a whole number of BK-deep panels, and so is
+    // the last one when K is
+    v.masked = !v.vec || (M % cfg.bm) || (N % cfg.bn) || (K % cfg.bk);
+    v.ta = (trans & 1) != 0;
+    v.tb = (trans & 2) != 0;
+    v.r16 = cfg.mode == GEMM355_MODE_F16R;
+    if (log_debug())
+        std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=split-K x%lld (k %lld)%s\n",
+                     layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
+                     (long long)K, format_config(cfg).c_str(), (long long)slices,
+                     (long long)depth, v.masked ? " masked" : "");
+    if (slices == 1) return status_of(launch_f32_splitk(a, v, s));
+    void* ws = nullptr;
+    hipError_t e = workspace(s, static_cast<size_t>(slices * M * N) * 4, &ws);
+    if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
+    a.C = static_cast<float*>(ws);
+    a.ldc = N;
+    a.ksplit = static_cast<int>(depth);
+    // the slices of a ragged split write partial tiles masked to M x N
+    e = launch_f32_splitk(a, v, s);
+    if (e != hipSuccess) return status_of(e);
+    return status_of(launch_splitk_reduce(static_cast<const float*>(ws), static_cast<int>(slices),
+                                          static_cast<int>(M), static_cast<int>(N), alpha, beta,
+                                          C, ldc, s));
+}
+
 int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
                 int64_t ldc, hipStream_t s) {
+    if (cfg.ks) return launch_splitk(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
     const int tiles_m = static_cast<int>((M + cfg.bm - 1) / cfg.bm);
     const int tiles_n = static_cast<int>((N + cfg.bn - 1) / cfg.bn);
     if (cfg.mode == GEMM355_MODE_F32) {

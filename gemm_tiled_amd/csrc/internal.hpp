@@ -14,17 +14,24 @@ namespace g355 {
 // in steps of BK through a ring of ST shared-memory stages; its WM x WN
 // wavefronts of 64 lanes split the tile; GM tile rows form one group of the
 // rasterised tile order (L2 reuse).
+// KS = 1 names the split-K configuration for few rows of C (the f32 kernel
+// over slices of K, partial tiles summed by a second pass; in the f16r mode it
+// rounds the operands as it loads them, with no packing pass).
 struct TileConfig {
     int mode;  // GEMM355_MODE_*
     int bm, bn, bk, st, wm, wn, gm;
+    int ks = 0;
     int threads() const { return wm * wn * 64; }
     bool operator==(const TileConfig& o) const {
         return mode == o.mode && bm == o.bm && bn == o.bn && bk == o.bk && st == o.st &&
-               wm == o.wm && wn == o.wn && gm == o.gm;
+               wm == o.wm && wn == o.wn && gm == o.gm && ks == o.ks;
     }
 };
 
 // Arguments of one f32 GEMM launch.
+// A and B as stored (see F32Variant::ta, tb).  In a split-K launch, slice z
+// (blockIdx.y) of the K range [z*ksplit, (z+1)*ksplit) writes its partial
+// product to C + z*M*ldc, and alpha, beta are applied by the reduction.
 struct F32Args {
     const float* A;
     const float* B;
@@ -33,6 +40,7 @@ struct F32Args {
     int M, N, K;
     float alpha, beta;
     int tiles_m, tiles_n;
+    int ksplit = 0;   // k per slice (multiple of BK); 0 = no split
 };
 
 // Arguments of one f16 GEMM launch on rounded, packed operands: A16 holds A
@@ -56,6 +64,7 @@ struct F32Variant {
     bool vec;     // 16-byte global loads are legal (lda, ldb % 4 == 0, aligned pointers)
     bool ta = false;   // op(A) = A^T: A is stored K x M
     bool tb = false;   // op(B) = B^T: B is stored N x K
+    bool r16 = false;  // round A and B to binary16 (RNE) on load: the f16r mode
 };
 
 using F32Launch = hipError_t (*)(const F32Args&, F32Variant, hipStream_t);
@@ -84,6 +93,15 @@ hipError_t launch_pack(const float* A, int64_t lda, bool ta, const float* B, int
 
 // C = beta*C (beta == 0: C = 0 without reading it).
 hipError_t launch_scale_c(float* C, int64_t ldc, int M, int N, float beta, hipStream_t s);
+
+// The split-K reduction: C = alpha * sum_{z < S} P[z] + beta * C, slices
+// summed in order z = 0, 1, ... (P: S slices of M x N, dense).
+hipError_t launch_splitk_reduce(const float* P, int S, int M, int N, float alpha, float beta,
+                                float* C, int64_t ldc, hipStream_t s);
+
+// The split-K configuration of a mode (KS = 1) and its launch.
+TileConfig splitk_config(int mode);
+hipError_t launch_f32_splitk(const F32Args& a, F32Variant v, hipStream_t s);
 
 // Measurement kernels.
 hipError_t launch_roof_mfma(int mode, int64_t iters, int blocks, float* sink, double* flops,

@@ -104,6 +104,54 @@ def test_workload_f16r_8192():
 
 
 # ---------------------------------------------------------------------------
+# The split-K configuration (KS=1) for few rows of C: K is cut into slices
+# whose partial tiles a second pass adds in order, then alpha and beta.  With
+# K = 4096 (or the ragged 4093) and a handful of tiles, every case below runs
+# several slices.  In the f16r mode it rounds the operands as it loads them.
+# ---------------------------------------------------------------------------
+
+SPLITK = "BM=32 BN=128 BK=32 KS=1"
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("M,N,K,lds", [
+    (1, 4096, 4096, {}),
+    (7, 1000, 4093, {}),
+    (64, 4096, 4096, {}),
+    (33, 515, 2049, {"lda": 2051, "ldb": 517, "ldc": 516}),   # odd lds, ragged everything
+])
+def test_splitk_against_the_oracle(mode, M, N, K, lds):
+    A, B, C = make_inputs(M, N, K, "normal", seed=12, **lds)
+    with pinned(mode, SPLITK):
+        say(f"[split-K] {mode} {M}x{N}x{K} {lds}")
+        got = run(mode, A, B, C, 1.25, -0.5)
+        again = run(mode, A, B, C, 1.25, -0.5)
+    assert_parity(mode, A, B, C, 1.25, -0.5, got)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))   # fixed slice order
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_splitk_small_integers_exact_and_beta_zero(mode):
+    M, N, K = 5, 4096, 4096
+    A, B, C = small_integers(M, N, K, seed=13)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned(mode, SPLITK):
+        say(f"[split-K exact] {mode} {M}x{N}x{K}")
+        got = run(mode, A, B, C, -2.0, 0.5)
+        assert np.array_equal(got, (-2.0 * exact + 0.5 * C.astype(np.float64)).astype(np.float32))
+        Cn = np.full((M, N), np.nan, dtype=np.float32)
+        got = run(mode, A, B, Cn, 1.0, 0.0)
+        assert np.array_equal(got, exact.astype(np.float32))
+
+
+def test_splitk_is_the_default_for_few_rows():
+    for mode in MODES:
+        assert g.get_config(mode, 16, 4096, 4096).startswith("BM=32 BN=128 BK=32")
+        assert "KS=1" in g.get_config(mode, 16, 4096, 4096)
+        assert "KS=1" not in g.get_config(mode, 4096, 4096, 4096)
+
+
+# ---------------------------------------------------------------------------
 # Exact results: small integers make every partial sum exact in f32 in any
 # order, so the GPU must match the exact product bit for bit (both modes: the
 # integers are exact in f16 too).  The exact product comes from a float64
