@@ -68,6 +68,9 @@ def main():
                     help="shape and alignment sweep of both modes (sizes 128..8192, n = "
                          "4088..4104 and 2048..2304, fixed-tile steps); markdown to OUT_MD")
     ap.add_argument("--sweep-repeats", type=int, default=3)
+    ap.add_argument("--precision", metavar="OUT_MD", default=None,
+                    help="precision study (the lab's Part 4): f32, f16r and f16r with binary16 "
+                         "output against float64 of the unrounded inputs; markdown to OUT_MD")
     ap.add_argument("--skinny", metavar="OUT_MD", default=None,
                     help="few-rows sweep (M = 1..2048 at K = N = 4096, both modes) against "
                          "the HBM and matrix-core roofs; markdown to OUT_MD")
@@ -110,6 +113,9 @@ def main():
         return
     if args.skinny:
         skinny_sweep(g, torch, dev, args.skinny, args.sweep_repeats)
+        return
+    if args.precision:
+        precision_study(g, torch, dev, args.precision)
         return
 
     # ------------------------------------------------------------------ roofs
@@ -493,6 +499,73 @@ def shape_sweep(g, torch, dev, out, repeats):
             lines.append(f"| {r['mode']} | {r['n']} | {r['tflops']:.1f} | "
                          f"{r['seconds_min'] * 1e3:.3f}..{r['seconds_max'] * 1e3:.3f} | "
                          f"{r['tile']} | {r['path']} |")
+    lines += ["", "```json", json.dumps(rows), "```", ""]
+    _write(out, "\n".join(lines))
+
+
+# ---------------------------------------------------------------------------
+# Precision (the Matrix Multiplication lab, "Part 4 -- precision"): A, B =
+# U[0,1) - 0.5, C = A@B; each variant against the float64 product of the
+# UNROUNDED inputs, as the lab's normalised max error (max|err| / max|ref|)
+# and relative Frobenius error, beside its speed and bytes per element of C.
+# ---------------------------------------------------------------------------
+PRECISION_SIZES = [2048, 4096]
+
+
+def precision_study(g, torch, dev, out):
+    import oracle
+    from workloads import make_inputs
+
+    rows = []
+    for n in PRECISION_SIZES:
+        A, B, _ = make_inputs(n, n, n, "centered", seed=0)
+        zeros = np.zeros((n, n), dtype=np.float32)
+        tA, tB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+        tC = torch.zeros((n, n), device=dev, dtype=torch.float32)
+        tC16 = torch.zeros((n, n), device=dev, dtype=torch.float16)
+        variants = [
+            ("f32", 4, lambda: g.gemm_f32(tA, tB, tC, 1.0, 0.0), tC),
+            ("f16r (f32 output)", 4, lambda: g.gemm_f16r_f32acc(tA, tB, tC, 1.0, 0.0), tC),
+            ("f16r, f16 output", 2, lambda: g.gemm_f16r_f16out(tA, tB, tC16, 1.0, 0.0), tC16),
+        ]
+        for label, nbytes, fn, dst in variants:
+            fn()
+            torch.cuda.synchronize()
+            got = dst.float().cpu().numpy()
+            # against the float64 product of the unrounded inputs (the f32 reference)
+            vs64 = oracle.check("f32", A, B, zeros, 1.0, 0.0, got, tol=1.0)
+            # and against the float64 product of the binary16-rounded inputs
+            vsr = oracle.check("f16r", A, B, zeros, 1.0, 0.0, got, tol=1.0)
+            t = steady(fn, torch, 0.5)
+            rows.append({"n": n, "variant": label, "seconds": t,
+                         "tflops": 2.0 * n ** 3 / t / 1e12, "bytes_per_element": nbytes,
+                         "err_max_norm": vs64["err_max_norm"], "err_fro": vs64["err_fro"],
+                         "err_max_norm_vs_rounded": vsr["err_max_norm"],
+                         "err_fro_vs_rounded": vsr["err_fro"]})
+            log(f"precision n={n} {label}: {rows[-1]['tflops']:.1f} TFLOP/s, "
+                f"max {vs64['err_max_norm']:.2e}, Frobenius {vs64['err_fro']:.2e}")
+        del tA, tB, tC, tC16
+        torch.cuda.empty_cache()
+    for r_ in rows:
+        base = next(x for x in rows if x["n"] == r_["n"] and x["variant"] == "f32")
+        r_["speedup_vs_f32"] = r_["tflops"] / base["tflops"]
+    lines = ["# Precision: f32, f16r and f16r with binary16 output (one MI355X)", "",
+             "Command:", "", "```", "python bench.py --precision profiles/precision.md", "```", "",
+             "A, B = U[0,1) - 0.5 (float32, seed 0), C = A @ B (alpha 1, beta 0).  Errors against "
+             "the float64 product of the unrounded inputs, computed by the oracle: normalised "
+             "max error max|C - ref| / max|ref| and relative Frobenius error "
+             "||C - ref|| / ||ref||.  The last two columns measure the same against the float64 "
+             "product of the binary16-rounded inputs, which separates the rounding of the "
+             "operands (and of the output) from the f32 accumulation.  Times: steady(), "
+             "median over 0.5 s.", "",
+             "| n | variant | TFLOP/s | speedup vs f32 | bytes/element of C | max err (norm.) | "
+             "Frobenius | max err vs rounded inputs | Frobenius vs rounded inputs |",
+             "|---:|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for r_ in rows:
+        lines.append(f"| {r_['n']} | {r_['variant']} | {r_['tflops']:.1f} | "
+                     f"{r_['speedup_vs_f32']:.2f} | {r_['bytes_per_element']} | "
+                     f"{r_['err_max_norm']:.2e} | {r_['err_fro']:.2e} | "
+                     f"{r_['err_max_norm_vs_rounded']:.2e} | {r_['err_fro_vs_rounded']:.2e} |")
     lines += ["", "```json", json.dumps(rows), "```", ""]
     _write(out, "\n".join(lines))
 

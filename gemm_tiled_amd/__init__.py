@@ -41,6 +41,8 @@ EXPORTS = {
                                    _p, _i64, _f32, _p, _i64, _p]),
     "gemm_f16r_f32acc_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _f32, _p,
                                            _i64, _p, _i64, _f32, _p, _i64, _p]),
+    "gemm_f16r_f16out": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _f32, _p,
+                                        _i64, _p, _i64, _f32, _p, _i64, _p]),
     "gemm355_tune": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p, _i64, _f32,
                                     _i64, _p]),
     "gemm355_tune_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64, _i64,
@@ -173,6 +175,28 @@ def gemm_f32(A, B, C, alpha=1.0, beta=0.0, stream=None, transa=False, transb=Fal
 
 def gemm_f16r_f32acc(A, B, C, alpha=1.0, beta=0.0, stream=None, transa=False, transb=False):
     return gemm(MODE_F16R, A, B, C, alpha, beta, stream, transa, transb)
+
+
+def gemm_f16r_f16out(A, B, C16, alpha=1.0, beta=0.0, stream=None, transa=False, transb=False):
+    """C16 = alpha*op(A)@op(B) + beta*C16 with A, B float32 (rounded to binary16
+    inside) and C16 a float16 tensor (row-major), the result rounded to
+    nearest even."""
+    import torch
+    if not isinstance(C16, torch.Tensor) or C16.dtype != torch.float16 or C16.dim() != 2:
+        raise TypeError("C16 must be a 2-D float16 tensor")
+    M, N = C16.shape
+    if C16.is_cuda is False or (N > 1 and C16.stride(1) != 1):
+        raise ValueError("C16 must be a row-major tensor on the GPU")
+    ldc = C16.stride(0) if M > 1 else max(N, 1)
+    K = A.shape[0] if transa else A.shape[1]
+    lda = _matrix(A, "A", *((K, M) if transa else (M, K)))
+    ldb = _matrix(B, "B", *((N, K) if transb else (K, N)))
+    st = lib().gemm_f16r_f16out(int(bool(transa)), int(bool(transb)), M, N, K, float(alpha),
+                                A.data_ptr() or None, lda, B.data_ptr() or None, ldb, float(beta),
+                                C16.data_ptr() or None, ldc, _stream_ptr(stream))
+    if st != 0:
+        raise Gemm355Error(st, "gemm_f16r_f16out")
+    return C16
 
 
 def tune(mode, A, B, C, beta=0.0, stream=None, transa=False, transb=False):

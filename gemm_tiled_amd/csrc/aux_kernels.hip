@@ -19,18 +19,42 @@ __global__ __launch_bounds__(256) void scale_c_kernel(float* __restrict__ C, int
     }
 }
 
+__device__ __forceinline__ float h2f(uint16_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+__device__ __forceinline__ uint16_t f2h(float x) {   // round to nearest even
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+// C = beta*C on binary16 storage (the f16-output variant's beta-only path).
+__global__ __launch_bounds__(256) void scale_c16_kernel(uint16_t* __restrict__ C, int64_t ldc,
+                                                        int M, int N, float beta) {
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= N) return;
+    for (int row = blockIdx.y; row < M; row += gridDim.y) {
+        uint16_t* c = C + (int64_t)row * ldc + col;
+        *c = (beta == 0.f) ? uint16_t{0} : f2h(beta * h2f(*c));
+    }
+}
+
 // Second pass of the split-K configuration: C = alpha * (P[0] + P[1] + ...) +
-// beta * C, the slices summed in order; beta == 0 does not read C.
+// beta * C, the slices summed in order; beta == 0 does not read C.  OUT
+// is float, or uint16_t for binary16 storage (rounded to nearest even).
+template <typename OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int S,
                                                             int M, int N, float alpha, float beta,
-                                                            float* __restrict__ C, int64_t ldc) {
+                                                            OUT* __restrict__ C, int64_t ldc) {
     const int col = blockIdx.x * 256 + threadIdx.x;
     if (col >= N) return;
     const int64_t slice = static_cast<int64_t>(M) * N;
     for (int row = blockIdx.y; row < M; row += gridDim.y) {
         const float* p = P + static_cast<int64_t>(row) * N + col;
-        float* c = C + static_cast<int64_t>(row) * ldc + col;
-        const float old = (beta == 0.f) ? 0.f : *c;
+        OUT* c = C + static_cast<int64_t>(row) * ldc + col;
+        float old = 0.f;
+        if (beta != 0.f) {
+            if constexpr (sizeof(OUT) == 2) old = h2f(*c);
+            else old = *c;
+        }
         // eight slices' loads in flight at a time, added in slice order
         float sum = 0.f;
         for (int z0 = 0; z0 < S; z0 += 8) {
@@ -41,7 +65,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
             for (int u = 0; u < 8; ++u)
                 if (z0 + u < S) sum += v[u];
         }
-        *c = (beta == 0.f) ? alpha * sum : alpha * sum + beta * old;
+        const float r = (beta == 0.f) ? alpha * sum : __builtin_fmaf(alpha, sum, beta * old);
+        if constexpr (sizeof(OUT) == 2) *c = f2h(r);
+        else *c = r;
     }
 }
 
@@ -122,7 +148,22 @@ hipError_t launch_splitk_reduce(const float* P, int S, int M, int N, float alpha
                                 float* C, int64_t ldc, hipStream_t s) {
     const unsigned gx = static_cast<unsigned>((N + 255) / 256);
     const unsigned gy = static_cast<unsigned>(M < 4096 ? M : 4096);
-    splitk_reduce_kernel<<<dim3(gx, gy), 256, 0, s>>>(P, S, M, N, alpha, beta, C, ldc);
+    splitk_reduce_kernel<float><<<dim3(gx, gy), 256, 0, s>>>(P, S, M, N, alpha, beta, C, ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce16(const float* P, int S, int M, int N, float alpha, float beta,
+                                  uint16_t* C16, int64_t ldc, hipStream_t s) {
+    const unsigned gx = static_cast<unsigned>((N + 255) / 256);
+    const unsigned gy = static_cast<unsigned>(M < 4096 ? M : 4096);
+    splitk_reduce_kernel<uint16_t><<<dim3(gx, gy), 256, 0, s>>>(P, S, M, N, alpha, beta, C16, ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_c16(uint16_t* C16, int64_t ldc, int M, int N, float beta, hipStream_t s) {
+    const unsigned gx = static_cast<unsigned>((N + 255) / 256);
+    const unsigned gy = static_cast<unsigned>(M < 4096 ? M : 4096);
+    scale_c16_kernel<<<dim3(gx, gy), 256, 0, s>>>(C16, ldc, M, N, beta);
     return hipGetLastError();
 }
 

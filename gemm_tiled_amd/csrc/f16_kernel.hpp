@@ -1,0 +1,579 @@
+// f16_kernel.hpp -- the f16 GEMM kernel templates of libgemm355 (the f16r
+// mode on rounded, packed operands), shared by the translation unit of the
+// f32 output (gemm_f16r.hip, which also holds the rounding/packing pass and
+// the table of configurations) and that of the binary16 output
+// (gemm_f16r_o16.hip).  Not part of the public ABI.
+#pragma once
+
+#include <type_traits>
+
+#include "internal.hpp"
+
+namespace g355 {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ----------------------------------------------------------------------------
+// Packed operand layout.  Rows (of A, or columns of B) are grouped in blocks
+// of kPackRows, depth in blocks of D values (D = 64 or 32, the depth of the
+// panel the GEMM configuration multiplies from).  Block (xb, kb) starts at
+// element ((xb * nkb) + kb) * kPackRows * D.  Inside it, row r holds its D
+// values as D/8 chunks of 8, logical chunk c at position c ^ swz(r), where the
+// key runs through all D/8 chunk positions as r steps through the rows that
+// share one 256-byte window of shared-memory banks:
+//   D = 64 (128-byte rows, 2 per window): swz(r) = (r / 2) % 8
+//   D = 32 ( 64-byte rows, 4 per window): swz(r) = (r / 4) % 4
+// A 16-byte shared-memory read is served 16 lanes at a time from 64 four-byte
+// banks (256 bytes); the 16 lanes of a fragment read take 16 consecutive rows
+// at one logical chunk, and the swizzle puts them in 16 different 16-byte
+// slots.
+// ----------------------------------------------------------------------------
+constexpr int kPackRows = 256;
+constexpr int kPackK = 64;   // the padded depth is a multiple of this for every D
+
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    static_assert(D == 32 || D == 64, "panel depth");
+    constexpr int cpr = D / 8;             // chunks per row
+    return (r / (16 / cpr)) % cpr;
+}
+
+template <int D>
+__device__ __forceinline__ int64_t packed_offset(int64_t x, int kb, int c, int64_t nkb) {
+    const int64_t xb = x / kPackRows;
+    const int r = static_cast<int>(x - xb * kPackRows);
+    return ((xb * nkb + kb) * kPackRows + r) * D + ((c ^ swz<D>(r)) << 3);
+}
+
+// ----------------------------------------------------------------------------
+// The f16 GEMM on the packed operands.
+//
+// A stage holds the BK = 64 deep panels of A (BM rows) and B (BN columns) of
+// one k step, in the packed image: 128 bytes per row.  The stages form a ring
+// of ST buffers in LDS, filled by direct global->LDS loads
+// (global_load_lds_dwordx4): one wave instruction copies one contiguous
+// kilobyte of a packed block into the same kilobyte of the stage without
+// passing through registers.  Fills run ST-1 panels ahead of the panel being
+// multiplied.  The K loop is unrolled by ST, so every stage is named
+// statically (a fixed shared-memory address).
+// ----------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const f16x8 lds_f16x8;
+typedef __attribute__((address_space(1))) void glb_void;
+
+template <int BM, int BN, int ST, int WM, int WN>
+struct F16Shape {
+    static constexpr int BK = kPackK;
+    static constexpr int NW = WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int ROW = BK * 2;              // bytes per panel row
+    static constexpr int KSTEPS = BK / 16;          // matrix instructions per block per panel
+    static constexpr int A_BYTES = BM * ROW;
+    static constexpr int STAGE = (BM + BN) * ROW;   // bytes per stage
+    static constexpr int A_INS = A_BYTES / 1024 / NW;   // fill instructions per wave per stage
+    static constexpr int B_INS = BN * ROW / 1024 / NW;
+    static constexpr int FILLS = A_INS + B_INS;
+    static_assert(ST >= 2 && ST <= 3, "2 or 3 stages");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(A_INS * 1024 * NW == A_BYTES && B_INS * 1024 * NW == BN * ROW,
+                  "kilobytes of a panel split evenly over the waves");
+    static_assert(kPackRows % BM == 0 && kPackRows % BN == 0, "tiles nest in packed blocks");
+    static_assert(ST * STAGE <= 160 * 1024, "LDS budget of one CU");
+};
+
+// Word 3 of a raw buffer descriptor on gfx9-family GPUs: 32-bit data format
+// (a zero format would make every load return zero), no swizzle, no index
+// stride; bounds are checked against the record count in bytes.
+constexpr int kBufferFlags = 0x00020000;
+
+// s_waitcnt vmcnt(N) with N a compile-time constant (at most 63).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for the panel ring.  __syncthreads() carries a workgroup
+// fence, for which the compiler waits until every outstanding global->LDS fill
+// of the wave has landed; that would cap the ring at one panel in flight.  The
+// ring orders its fills itself (wait_vmcnt before this barrier), so a bare
+// s_barrier suffices; this wave's own LDS reads are drained first so no other
+// wave can refill a stage under them, and the asm is a compiler memory barrier.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One direct global->LDS copy of a wave: lane l copies the 16 bytes at `src`
+// (its own address) to LDS byte address lds_base + 16 l.  Written as assembly
+// so that the compiler does not track these copies: it cannot always tell
+// which stage a shared-memory read may alias and would then wait for every
+// copy in flight before the read, which serialises the ring.  The ring waits
+// for its copies itself (wait_vmcnt before each barrier).  M0 carries the
+// wave's LDS base (the compiler writes it before the statement); the copy
+// needs one wait state after a write of M0.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds_base) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_base)
+                 : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* generic_lds_ptr) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)(generic_lds_ptr)));
+}
+
+template <int BM, int BN, int ST, int WM, int WN, int GM, bool RS, bool MASKED, bool OUT16>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
+    using S = F16Shape<BM, BN, ST, WM, WN>;
+    __shared__ __attribute__((aligned(1024))) unsigned char ring0[S::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char ring1[S::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char ring2[ST > 2 ? S::STAGE : 16];
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave / WN, wc = wave % WN;
+    const int h = lane >> 5;
+    const int r32 = lane & 31;
+    const int64_t nkb = p.nkb;
+
+    // Panel kt of this tile's A rows is the BM-row slice at row m0 % 256 of
+    // packed block (m0 / 256, kt); consecutive kt are consecutive blocks.
+    const unsigned char* a_tile = reinterpret_cast<const unsigned char*>(
+        p.A16 + ((int64_t)(m0 / kPackRows) * nkb * kPackRows + m0 % kPackRows) * kPackK);
+    const unsigned char* b_tile = reinterpret_cast<const unsigned char*>(
+        p.B16t + ((int64_t)(n0 / kPackRows) * nkb * kPackRows + n0 % kPackRows) * kPackK);
+    const int lane_ofs = wave * 1024 + lane * 16;
+    const unsigned char* a_src = a_tile + lane_ofs;
+    const unsigned char* b_src = b_tile + lane_ofs;
+    constexpr int64_t kBlockBytes = int64_t{kPackRows} * kPackK * 2;
+
+    auto fill = [&](unsigned char* stage, int kt) __attribute__((always_inline)) {
+        const uint32_t as = __builtin_amdgcn_readfirstlane(lds_addr(stage) + wave * 1024);
+        const uint32_t bs = as + S::A_BYTES;
+        const int64_t kofs = (int64_t)kt * kBlockBytes;
+#pragma unroll
+        for (int j = 0; j < S::A_INS; ++j)
+            lds_copy16(a_src + kofs + j * S::NW * 1024, as + j * S::NW * 1024);
+#pragma unroll
+        for (int j = 0; j < S::B_INS; ++j)
+            lds_copy16(b_src + kofs + j * S::NW * 1024, bs + j * S::NW * 1024);
+    };
+
+    // Register-staged fills (RS): the same kilobytes go through VGPRs --
+    // load(kt) issues the 16-byte loads of panel kt into `stg`, commit(stage)
+    // writes them to the same offsets of the stage.  The loads are buffer
+    // loads: the panel's base address lives in a scalar descriptor (rebuilt
+    // per panel with scalar arithmetic) whose record count is exactly the
+    // panel's bytes, and every load of the wave shares one 32-bit lane offset,
+    // so no 64-bit vector address is formed per load.
+    u32x4 stg[RS ? S::FILLS : 1];
+    auto load = [&](int kt) __attribute__((always_inline)) {
+        const int64_t kofs = (int64_t)kt * kBlockBytes;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a_tile + kofs), (short)0, S::A_BYTES, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(b_tile + kofs), (short)0, BN * S::ROW, kBufferFlags);
+#pragma unroll
+        for (int j = 0; j < S::A_INS; ++j)
+            stg[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, lane_ofs, j * S::NW * 1024, 0);
+#pragma unroll
+        for (int j = 0; j < S::B_INS; ++j)
+            stg[S::A_INS + j] = __builtin_amdgcn_raw_buffer_load_b128(rb, lane_ofs, j * S::NW * 1024, 0);
+    };
+    auto commit = [&](unsigned char* stage) __attribute__((always_inline)) {
+        lds_u8* as = (lds_u8*)(stage) + wave * 1024 + lane * 16;
+        lds_u8* bs = (lds_u8*)(stage) + S::A_BYTES + wave * 1024 + lane * 16;
+#pragma unroll
+        for (int j = 0; j < S::A_INS; ++j)
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(as + j * S::NW * 1024) =
+                stg[j];
+#pragma unroll
+        for (int j = 0; j < S::B_INS; ++j)
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(bs + j * S::NW * 1024) =
+                stg[S::A_INS + j];
+    };
+
+    // Fragment reads: lane (h, r32) of block i reads row r32 of the block at
+    // logical chunk h*4 + ks (lane half h feeds k in [32h, 32h+32) of the
+    // panel, 8 per instruction, to A and B alike).  Blocks start at multiples
+    // of 32 rows (of 16 within the packed block), so the row's swizzle key is
+    // swz(r32).
+    const int sw = swz<kPackK>(r32);
+    const int a_row0 = (wr * S::TM + r32) * S::ROW;
+    const int b_row0 = S::A_BYTES + (wc * S::TN + r32) * S::ROW;
+    auto frags = [&](const unsigned char* stage, int ks, f16x8 (&a)[S::FM], f16x8 (&b)[S::FN]) {
+        const lds_u8* base = (const lds_u8*)(stage);
+        const int chunk = ((h * S::KSTEPS + ks) ^ sw) << 4;
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i)
+            a[i] = *reinterpret_cast<lds_f16x8*>(base + a_row0 + i * 32 * S::ROW + chunk);
+#pragma unroll
+        for (int j = 0; j < S::FN; ++j)
+            b[j] = *reinterpret_cast<lds_f16x8*>(base + b_row0 + j * 32 * S::ROW + chunk);
+    };
+
+    // The accumulators get their first value from the first matrix
+    // instruction of the first panel, with an inline-constant zero as its
+    // addend, so they are born in the accumulation registers instead of being
+    // zeroed in general registers and copied over.
+    f32x16 acc[S::FM][S::FN];
+    using first_panel = std::true_type;
+    using later_panel = std::false_type;
+
+    constexpr int NMF = S::FM * S::FN;
+    constexpr int NFR = S::FM + S::FN;
+    const int nk = static_cast<int>(nkb);
+    auto stage_of = [&](int i) __attribute__((always_inline)) -> unsigned char* { return i == 0 ? ring0 : i == 1 ? ring1 : ring2; };
+
+    // Multiply one stage: fragments of step ks+1 are read while step ks
+    // multiplies.
+    auto multiply = [&](const unsigned char* cur, auto first) __attribute__((always_inline)) {
+        f16x8 a[2][S::FM], b[2][S::FN];
+        frags(cur, 0, a[0], b[0]);
+        const f32x16 zero = {};
+#pragma unroll
+        for (int ks = 0; ks < S::KSTEPS; ++ks) {
+            if (ks + 1 < S::KSTEPS) frags(cur, ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
+#pragma unroll
+            for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < S::FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        a[ks & 1][i], b[ks & 1][j],
+                        (decltype(first)::value && ks == 0) ? zero : acc[i][j], 0, 0, 0);
+        }
+    };
+
+    if constexpr (!RS) {
+        // One panel: fill panel kt+ST-1 into the stage freed by panel kt-1
+        // (every wave passed the barrier after reading it), multiply the
+        // current stage, then wait until panel kt+1 has landed -- the fills of
+        // later panels may stay in flight -- and for every other wave.  Fills
+        // past the last panel reload the last panel into a stage nobody reads
+        // again, so the wave's count of outstanding fills is the same at every
+        // step and the step is one basic block, which the group barriers below
+        // order: fills, then the first fragments, then one matrix instruction
+        // after another with the next step's fragment reads between them.
+        auto panel = [&](const unsigned char* cur, unsigned char* freed, int kt_fill,
+                         auto first) __attribute__((always_inline)) {
+            fill(freed, kt_fill);
+            multiply(cur, first);
+            __builtin_amdgcn_sched_group_barrier(0x020, S::FILLS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NFR, 0);
+#pragma unroll
+            for (int ks = 0; ks < S::KSTEPS; ++ks) {
+#pragma unroll
+                for (int m = 0; m < NMF; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (ks + 1 < S::KSTEPS && m < NFR)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+            wait_vmcnt<(ST - 2) * S::FILLS>();
+            ring_barrier();
+        };
+
+        // Prologue: panels 0 .. ST-2 into stages 0 .. ST-2, then wait for panel 0.
+#pragma unroll
+        for (int i = 0; i + 1 < ST; ++i) fill(stage_of(i), min(i, nk - 1));
+        wait_vmcnt<(ST - 2) * S::FILLS>();
+        ring_barrier();
+
+        panel(stage_of(0), stage_of(ST - 1), min(ST - 1, nk - 1), first_panel{});
+#pragma unroll
+        for (int u = 1; u < ST; ++u)
+            if (u < nk) panel(stage_of(u), stage_of(u - 1), min(u + ST - 1, nk - 1), later_panel{});
+        for (int kt = ST; kt < nk; kt += ST) {
+#pragma unroll
+            for (int u = 0; u < ST; ++u) {
+                if (u == 0 || kt + u < nk)
+                    panel(stage_of(u), stage_of((u + ST - 1) % ST), min(kt + u + ST - 1, nk - 1),
+                          later_panel{});
+            }
+        }
+        wait_vmcnt<0>();   // no fill may still be landing in LDS when the workgroup ends
+    } else {
+        // Register-staged ring of two stages: while stage kt%2 is multiplied,
+        // panel kt+1 (loaded into registers during the previous panel) is
+        // written to the other stage, then the loads of panel kt+2 are issued.
+        // The group barriers spread the writes between the matrix
+        // instructions of the first step and the loads between those of the
+        // second, so the loads have most of a panel to arrive.
+        static_assert(ST == 2, "the register-staged ring has two stages");
+        auto panel = [&](const unsigned char* cur, unsigned char* next, int kt_load,
+                         auto first) __attribute__((always_inline)) {
+            multiply(cur, first);
+            commit(next);
+            load(kt_load);
+            __builtin_amdgcn_sched_group_barrier(0x100, NFR, 0);
+#pragma unroll
+            for (int ks = 0; ks < S::KSTEPS; ++ks) {
+#pragma unroll
+                for (int m = 0; m < NMF; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (ks + 1 < S::KSTEPS && m < NFR)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if (ks == 0 && m < S::FILLS) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                    if (ks == 1 && m < S::FILLS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+            }
+            ring_barrier();
+        };
+        load(0);
+        commit(ring0);
+        load(min(1, nk - 1));
+        ring_barrier();
+        panel(ring0, ring1, min(2, nk - 1), first_panel{});
+        if (1 < nk) panel(ring1, ring0, min(3, nk - 1), later_panel{});
+        for (int kt = 2; kt < nk; kt += 2) {
+            panel(ring0, ring1, min(kt + 2, nk - 1), later_panel{});
+            if (kt + 1 < nk) panel(ring1, ring0, min(kt + 3, nk - 1), later_panel{});
+        }
+        wait_vmcnt<0>();
+    }
+
+    // Epilogue: C = alpha*acc + beta*C over this wave's part of the tile.
+    if constexpr (OUT16)
+        store_tile16<S::FM, S::FN, MASKED>(acc, p.C16, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN,
+                                           p.M, p.N, p.alpha, p.beta, lane);
+    else
+        store_tile<S::FM, S::FN, MASKED>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M,
+                                         p.N, p.alpha, p.beta, lane);
+}
+
+// ----------------------------------------------------------------------------
+// The half-depth ring.  Panels are BK = 32 deep (64 bytes per row, packed
+// blocks of depth 32), and NS of them (up to 5 x 32 KB for a 256 x 256 tile,
+// all of a CU's shared memory) form a ring filled direct from the packed
+// blocks, so NS - 1 panels -- up to two 64-deep steps of the full-depth ring
+// -- are in flight while one is multiplied; the fills then have several
+// microseconds to arrive from the memory-side cache when they miss in L2.
+//
+// One panel is two steps of 16 k.  The barrier sits between them: step 0
+// multiplies fragments read before it, while this wave reads the fragments of
+// step 1 and issues its fills of the panel NS - 1 ahead; then the wave waits
+// for its fills of the next panel, passes the barrier (every wave's fills of
+// the next panel have landed, every wave has read all of this one), and step 1
+// multiplies while the first fragments of the next panel are read.  So the
+// matrix instructions after a barrier never wait for shared memory.
+// ----------------------------------------------------------------------------
+template <int BM, int BN, int NS, int WM, int WN>
+struct RingShape {
+    static constexpr int BK = 32;
+    static constexpr int NW = WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int ROW = BK * 2;              // bytes per panel row
+    static constexpr int A_BYTES = BM * ROW;
+    static constexpr int STAGE = (BM + BN) * ROW;   // bytes per stage
+    static constexpr int A_INS = A_BYTES / 1024 / NW;   // fill instructions per wave per panel
+    static constexpr int B_INS = BN * ROW / 1024 / NW;
+    static constexpr int FILLS = A_INS + B_INS;
+    static_assert(NS >= 3 && NS <= 5, "3 to 5 stages");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(A_INS >= 1 && B_INS >= 1 && A_INS * 1024 * NW == A_BYTES &&
+                      B_INS * 1024 * NW == BN * ROW,
+                  "kilobytes of a panel split evenly over the waves");
+    static_assert(kPackRows % BM == 0 && kPackRows % BN == 0, "tiles nest in packed blocks");
+    static_assert(NS * STAGE <= 160 * 1024, "LDS budget of one CU");
+    static_assert((NS - 2) * FILLS < 64, "vmcnt range");
+};
+
+template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED, bool OUT16>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_f16_ring_kernel(F16Args p) {
+    using S = RingShape<BM, BN, NS, WM, WN>;
+    constexpr int D = S::BK;
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[S::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[S::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[S::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[NS > 3 ? S::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char st4[NS > 4 ? S::STAGE : 16];
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave / WN, wc = wave % WN;
+    const int h = lane >> 5;
+    const int r32 = lane & 31;
+    const int nk = static_cast<int>(p.nkb);
+
+    // Panel kt of this tile's A rows is the BM-row slice at row m0 % 256 of
+    // packed block (m0 / 256, kt); consecutive kt are consecutive blocks.
+    const int lane_ofs = wave * 1024 + lane * 16;
+    const unsigned char* a_src = reinterpret_cast<const unsigned char*>(
+        p.A16 + ((int64_t)(m0 / kPackRows) * p.nkb * kPackRows + m0 % kPackRows) * D) + lane_ofs;
+    const unsigned char* b_src = reinterpret_cast<const unsigned char*>(
+        p.B16t + ((int64_t)(n0 / kPackRows) * p.nkb * kPackRows + n0 % kPackRows) * D) + lane_ofs;
+    constexpr int64_t kBlockBytes = int64_t{kPackRows} * D * 2;
+
+    auto stage_of = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+        return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : i == 3 ? st3 : st4;
+    };
+    auto fill = [&](unsigned char* stage, int kt) __attribute__((always_inline)) {
+        const uint32_t as = __builtin_amdgcn_readfirstlane(lds_addr(stage) + wave * 1024);
+        const uint32_t bs = as + S::A_BYTES;
+        const int64_t kofs = (int64_t)kt * kBlockBytes;
+#pragma unroll
+        for (int j = 0; j < S::A_INS; ++j)
+            lds_copy16(a_src + kofs + j * S::NW * 1024, as + j * S::NW * 1024);
+#pragma unroll
+        for (int j = 0; j < S::B_INS; ++j)
+            lds_copy16(b_src + kofs + j * S::NW * 1024, bs + j * S::NW * 1024);
+    };
+
+    // Fragment reads: lane (h, r32) of block i reads row r32 of the block at
+    // logical chunk 2h + ks (lane half h feeds k in [16h, 16h + 16) of the
+    // panel, 8 per instruction, to A and B alike).  Blocks start at multiples
+    // of 32 rows, a whole number of swizzle periods, so the key is swz(r32).
+    const int sw = swz<D>(r32);
+    const int a_row0 = (wr * S::TM + r32) * S::ROW;
+    const int b_row0 = S::A_BYTES + (wc * S::TN + r32) * S::ROW;
+    f16x8 fa[2][S::FM], fb[2][S::FN];
+    auto frags = [&](const unsigned char* stage, int ks) __attribute__((always_inline)) {
+        const lds_u8* base = (const lds_u8*)(stage);
+        const int chunk = ((h * 2 + ks) ^ sw) << 4;
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i)
+            fa[ks][i] = *reinterpret_cast<lds_f16x8*>(base + a_row0 + i * 32 * S::ROW + chunk);
+#pragma unroll
+        for (int j = 0; j < S::FN; ++j)
+            fb[ks][j] = *reinterpret_cast<lds_f16x8*>(base + b_row0 + j * 32 * S::ROW + chunk);
+    };
+
+    // The accumulators get their first value from the first matrix
+    // instruction, with an inline-constant zero as its addend.
+    f32x16 acc[S::FM][S::FN];
+    constexpr int NMF = S::FM * S::FN;
+    constexpr int NFR = S::FM + S::FN;
+    auto mfmas = [&](int ks, auto first) __attribute__((always_inline)) {
+        const f32x16 zero = {};
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < S::FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    fa[ks][i], fb[ks][j], decltype(first)::value ? zero : acc[i][j], 0, 0, 0);
+    };
+    // one matrix instruction, then one fragment read, while reads remain
+    auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < NMF; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (m < NFR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+
+    // One panel in stage `cur`: fill panel kt_fill into `freed` (the stage of
+    // the previous panel, which every wave finished reading before the last
+    // barrier), step 0 beside the reads of step 1, wait for this wave's fills
+    // of the next panel, barrier, step 1 beside the first reads of `next`.
+    // Fills past the last panel reload the last panel into a stage nobody
+    // reads again, so the count of outstanding fills is the same every panel.
+    auto panel = [&](const unsigned char* cur, unsigned char* freed, const unsigned char* next,
+                     int kt_fill, auto first) __attribute__((always_inline)) {
+        fill(freed, kt_fill);
+        frags(cur, 1);
+        mfmas(0, first);
+        __builtin_amdgcn_sched_group_barrier(0x020, S::FILLS, 0);
+        interleave();
+        wait_vmcnt<(NS - 2) * S::FILLS>();
+        ring_barrier();
+        frags(next, 0);
+        mfmas(1, std::false_type{});
+        interleave();
+    };
+
+    // Prologue: panels 0 .. NS-2 into stages 0 .. NS-2; wait for panel 0.
+#pragma unroll
+    for (int i = 0; i + 1 < NS; ++i) fill(stage_of(i), min(i, nk - 1));
+    wait_vmcnt<(NS - 2) * S::FILLS>();
+    ring_barrier();
+    frags(stage_of(0), 0);
+
+    panel(stage_of(0), stage_of(NS - 1), stage_of(1), min(NS - 1, nk - 1), std::true_type{});
+#pragma unroll
+    for (int u = 1; u < NS; ++u)
+        if (u < nk)
+            panel(stage_of(u), stage_of(u - 1), stage_of((u + 1) % NS), min(u + NS - 1, nk - 1),
+                  std::false_type{});
+    for (int kt = NS; kt < nk; kt += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            if (u == 0 || kt + u < nk)
+                panel(stage_of(u), stage_of((u + NS - 1) % NS), stage_of((u + 1) % NS),
+                      min(kt + u + NS - 1, nk - 1), std::false_type{});
+        }
+    }
+    wait_vmcnt<0>();   // no fill may still be landing in LDS when the workgroup ends
+
+    if constexpr (OUT16)
+        store_tile16<S::FM, S::FN, MASKED>(acc, p.C16, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN,
+                                           p.M, p.N, p.alpha, p.beta, lane);
+    else
+        store_tile<S::FM, S::FN, MASKED>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M,
+                                         p.N, p.alpha, p.beta, lane);
+}
+
+// One configuration, both masking variants, f32 (OUT16 false) or binary16 C.
+template <int BM, int BN, int NS, int WM, int WN, int GM, bool OUT16>
+hipError_t launch_f16_ring_out(const F16Args& a, hipStream_t s) {
+    const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
+    const bool masked = (a.M % BM) != 0 || (a.N % BN) != 0;
+    if (masked) gemm_f16_ring_kernel<BM, BN, NS, WM, WN, GM, true, OUT16><<<grid, block, 0, s>>>(a);
+    else gemm_f16_ring_kernel<BM, BN, NS, WM, WN, GM, false, OUT16><<<grid, block, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int ST, int WM, int WN, int GM, bool RS, bool OUT16>
+hipError_t launch_f16_out(const F16Args& a, hipStream_t s) {
+    const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
+    const bool masked = (a.M % BM) != 0 || (a.N % BN) != 0;
+    if (masked) gemm_f16_kernel<BM, BN, ST, WM, WN, GM, RS, true, OUT16><<<grid, block, 0, s>>>(a);
+    else gemm_f16_kernel<BM, BN, ST, WM, WN, GM, RS, false, OUT16><<<grid, block, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+// The binary16-output launches (defined in gemm_f16r_o16.hip).
+template <int BM, int BN, int NS, int WM, int WN, int GM>
+hipError_t launch_f16_ring_o16(const F16Args& a, hipStream_t s);
+template <int BM, int BN, int ST, int WM, int WN, int GM, bool RS>
+hipError_t launch_f16_o16(const F16Args& a, hipStream_t s);
+
+// Compiled f16 configurations.  Half-depth rings: X(BM, BN, NS, WM, WN, GM),
+// BK = 32, ST = NS stages.  Full-depth panels: Y(BM, BN, ST, WM, WN, GM),
+// BK = 64; ST = 1 in a configuration names the register-staged two-stage
+// ring (one stage in LDS is written from registers while the other is
+// multiplied), ST = 2 or 3 the direct-to-LDS ring of that many stages.
+#define G355_F16_RING_CONFIGS(X) \
+    X(256, 256, 5, 4, 2, 8)      \
+    X(256, 256, 5, 2, 4, 8)      \
+    X(256, 256, 4, 4, 2, 8)      \
+    X(256, 256, 4, 2, 4, 8)      \
+    X(256, 256, 5, 2, 2, 8)      \
+    X(128, 128, 5, 2, 2, 8)
+#define G355_F16_PANEL_CONFIGS(Y) \
+    Y(256, 256, 1, 4, 2, 8)       \
+    Y(256, 256, 1, 2, 4, 8)       \
+    Y(128, 128, 1, 2, 2, 8)       \
+    Y(256, 256, 2, 4, 2, 8)       \
+    Y(256, 256, 2, 2, 4, 8)       \
+    Y(256, 128, 3, 2, 2, 8)       \
+    Y(256, 128, 2, 2, 2, 8)       \
+    Y(256, 128, 3, 4, 2, 8)       \
+    Y(128, 256, 3, 2, 2, 8)       \
+    Y(128, 128, 2, 2, 2, 8)       \
+    Y(128, 128, 3, 2, 2, 8)       \
+    Y(128, 64, 2, 2, 2, 8)        \
+    Y(64, 64, 2, 2, 2, 8)
+
+}  // namespace g355

@@ -320,7 +320,7 @@ int status_of(hipError_t e) { return e == hipSuccess ? 0 : static_cast<int>(e); 
 // the normal epilogue; more go through the workspace and the reduction.
 int launch_splitk(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
                   const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
-                  int64_t ldc, hipStream_t s) {
+                  int64_t ldc, hipStream_t s, uint16_t* C16) {
     const int tiles_m = static_cast<int>((M + cfg.bm - 1) / cfg.bm);
     const int tiles_n = static_cast<int>((N + cfg.bn - 1) / cfg.bn);
     const int64_t tiles = int64_t{tiles_m} * tiles_n;
@@ -344,16 +344,21 @@ int launch_splitk(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_
                      layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
                      (long long)K, format_config(cfg).c_str(), (long long)slices,
                      (long long)depth, v.masked ? " masked" : "");
-    if (slices == 1) return status_of(launch_f32_splitk(a, v, s));
+    // binary16 output always goes through the reduction, which rounds
+    if (slices == 1 && !C16) return status_of(launch_f32_splitk(a, v, s));
     void* ws = nullptr;
     hipError_t e = workspace(s, static_cast<size_t>(slices * M * N) * 4, &ws);
     if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
     a.C = static_cast<float*>(ws);
     a.ldc = N;
-    a.ksplit = static_cast<int>(depth);
+    a.ksplit = static_cast<int>(depth);   // one slice too, when the output is binary16
     // the slices of a ragged split write partial tiles masked to M x N
     e = launch_f32_splitk(a, v, s);
     if (e != hipSuccess) return status_of(e);
+    if (C16)
+        return status_of(launch_splitk_reduce16(static_cast<const float*>(ws),
+                                                static_cast<int>(slices), static_cast<int>(M),
+                                                static_cast<int>(N), alpha, beta, C16, ldc, s));
     return status_of(launch_splitk_reduce(static_cast<const float*>(ws), static_cast<int>(slices),
                                           static_cast<int>(M), static_cast<int>(N), alpha, beta,
                                           C, ldc, s));
@@ -361,8 +366,9 @@ int launch_splitk(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_
 
 int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
-                int64_t ldc, hipStream_t s) {
-    if (cfg.ks) return launch_splitk(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+                int64_t ldc, hipStream_t s, uint16_t* C16) {
+    if (cfg.ks)
+        return launch_splitk(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
     const int tiles_m = static_cast<int>((M + cfg.bm - 1) / cfg.bm);
     const int tiles_n = static_cast<int>((N + cfg.bn - 1) / cfg.bn);
     if (cfg.mode == GEMM355_MODE_F32) {
@@ -402,27 +408,37 @@ int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
         if (e != hipSuccess) return status_of(e);
         F16Args a{A16, B16t, C, kp / cfg.bk, ldc, static_cast<int>(M), static_cast<int>(N), alpha,
                   beta, tiles_m, tiles_n};
+        a.C16 = C16;
         if (log_debug())
-            std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=%s\n",
+            std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=%s%s\n",
                          layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
                          (long long)K, format_config(cfg).c_str(),
-                         ((M % cfg.bm) || (N % cfg.bn)) ? "masked-store" : "aligned");
+                         ((M % cfg.bm) || (N % cfg.bn)) ? "masked-store" : "aligned",
+                         C16 ? " f16-out" : "");
         return status_of(t[i].launch(a, s));
     }
     return GEMM355_ERR_CONFIG;
 }
 
+// C16 != NULL: the f16-output variant (f16r mode only): C is stored as
+// binary16 in C16 and the f32 result is rounded to nearest even; C is unused.
 int gemm(int mode, int trans, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
          int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream,
-         const TileConfig* force) {
-    const int bad = check_args(trans, M, N, K, alpha, A, lda, B, ldb, C, ldc);
+         const TileConfig* force, uint16_t* C16) {
+    const float* c_arg = C16 ? reinterpret_cast<const float*>(C16) : C;
+    const int bad = check_args(trans, M, N, K, alpha, A, lda, B, ldb, c_arg, ldc);
     if (bad) return bad;
+    if (C16 && mode != GEMM355_MODE_F16R) return GEMM355_ERR_MODE;
     if (M == 0 || N == 0) return 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (K == 0 || alpha == 0.f) {
         if (log_debug())
-            std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld path=beta-only\n",
-                         mode_name(mode), (long long)M, (long long)N, (long long)K);
+            std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld path=beta-only%s\n",
+                         mode_name(mode), (long long)M, (long long)N, (long long)K,
+                         C16 ? " f16-out" : "");
+        if (C16)
+            return status_of(
+                launch_scale_c16(C16, ldc, static_cast<int>(M), static_cast<int>(N), beta, s));
         return status_of(launch_scale_c(C, ldc, static_cast<int>(M), static_cast<int>(N), beta, s));
     }
     TileConfig cfg;
@@ -433,7 +449,7 @@ int gemm(int mode, int trans, int64_t M, int64_t N, int64_t K, float alpha, cons
         const int rc = select_config(mode, trans, M, N, K, A, lda, B, ldb, beta, &cfg, &src);
         if (rc) return rc;
     }
-    return launch_with(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    return launch_with(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
 }
 
 // ---------------------------------------------------------------------------
@@ -512,7 +528,7 @@ int time_once(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K,
               hipStream_t s, hipEvent_t e0, hipEvent_t e1, float* ms) {
     hipError_t e = hipEventRecord(e0, s);
     if (e != hipSuccess) return status_of(e);
-    int rc = gemm(cfg.mode, trans, M, N, K, 1.0f, A, lda, B, ldb, beta, C, ldc, s, &cfg);
+    int rc = gemm(cfg.mode, trans, M, N, K, 1.0f, A, lda, B, ldb, beta, C, ldc, s, &cfg, nullptr);
     if (rc) return rc;
     e = hipEventRecord(e1, s);
     if (e == hipSuccess) e = hipEventSynchronize(e1);
@@ -622,14 +638,14 @@ extern "C" {
 int gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
              const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream) {
     return gemm(GEMM355_MODE_F32, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
-                nullptr);
+                nullptr, nullptr);
 }
 
 int gemm_f16r_f32acc(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
                      const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
                      void* stream) {
     return gemm(GEMM355_MODE_F16R, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
-                nullptr);
+                nullptr, nullptr);
 }
 
 }  // extern "C"
@@ -656,7 +672,7 @@ int gemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float a
     int trans = 0;
     if (const int bad = trans_of(transa, transb, &trans)) return bad;
     return shift_ex(gemm(GEMM355_MODE_F32, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
-                         stream, nullptr));
+                         stream, nullptr, nullptr));
 }
 
 int gemm_f16r_f32acc_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
@@ -665,7 +681,16 @@ int gemm_f16r_f32acc_ex(int transa, int transb, int64_t M, int64_t N, int64_t K,
     int trans = 0;
     if (const int bad = trans_of(transa, transb, &trans)) return bad;
     return shift_ex(gemm(GEMM355_MODE_F16R, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
-                         stream, nullptr));
+                         stream, nullptr, nullptr));
+}
+
+int gemm_f16r_f16out(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
+                     const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                     uint16_t* C16, int64_t ldc, void* stream) {
+    int trans = 0;
+    if (const int bad = trans_of(transa, transb, &trans)) return bad;
+    return shift_ex(gemm(GEMM355_MODE_F16R, trans, M, N, K, alpha, A, lda, B, ldb, beta, nullptr,
+                         ldc, stream, nullptr, C16));
 }
 
 int gemm355_tune(int mode, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,

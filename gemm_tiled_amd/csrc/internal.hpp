@@ -56,6 +56,7 @@ struct F16Args {
     int M, N;
     float alpha, beta;
     int tiles_m, tiles_n;
+    uint16_t* C16 = nullptr;   // binary16 output (then C is unused): the f16-output variant
 };
 
 // Which variant of a compiled configuration a launch needs.
@@ -91,13 +92,19 @@ hipError_t launch_pack(const float* A, int64_t lda, bool ta, const float* B, int
                        bool tb, int M, int N, int K, uint16_t* A16, uint16_t* B16t, int64_t mp,
                        int64_t np, int64_t kp, int depth, hipStream_t s);
 
-// C = beta*C (beta == 0: C = 0 without reading it).
+// C = beta*C (beta == 0: C = 0 without reading it); C16: the same on binary16
+// storage (rounded to nearest even).
 hipError_t launch_scale_c(float* C, int64_t ldc, int M, int N, float beta, hipStream_t s);
+hipError_t launch_scale_c16(uint16_t* C16, int64_t ldc, int M, int N, float beta, hipStream_t s);
 
 // The split-K reduction: C = alpha * sum_{z < S} P[z] + beta * C, slices
 // summed in order z = 0, 1, ... (P: S slices of M x N, dense).
 hipError_t launch_splitk_reduce(const float* P, int S, int M, int N, float alpha, float beta,
                                 float* C, int64_t ldc, hipStream_t s);
+// The same into binary16 storage C16 (read as binary16 when beta != 0, the
+// result rounded to nearest even).
+hipError_t launch_splitk_reduce16(const float* P, int S, int M, int N, float alpha, float beta,
+                                  uint16_t* C16, int64_t ldc, hipStream_t s);
 
 // The split-K configuration of a mode (KS = 1) and its launch.
 TileConfig splitk_config(int mode);
@@ -140,7 +147,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // waits for memory once per block rather than once per element.  C is touched
 // exactly once, so its loads and stores are non-temporal: they do not evict
 // the operand panels other workgroups are still re-reading from the caches.
-// MASKED guards every access with row < M and col < N.
+// MASKED guards every access with row < M and col < N.  The value is
+// fma(alpha, acc, beta*c) (one rounding for alpha*acc + beta*c), written out
+// so that every epilogue of the library computes the same f32 number.
 template <int FM, int FN, bool MASKED>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* __restrict__ C,
                                            int64_t ldc, int row0, int col0, int M, int N,
@@ -175,11 +184,44 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
         for (int e = 0; e < 16; ++e) {
             const int row = row_of(i, e), col = col_of(j);
             if (inside(row, col))
-                __builtin_nontemporal_store(alpha * acc[i][j][e] + beta * v[e],
+                __builtin_nontemporal_store(__builtin_fmaf(alpha, acc[i][j][e], beta * v[e]),
                                             C + (int64_t)row * ldc + col);
         }
         // keep the compiler from hoisting every block's loads above the first
         // stores (that would need FM*FN*16 live registers)
+        asm volatile("" ::: "memory");
+    }
+}
+
+// The epilogue of the f16-output variant: C16 holds binary16 bit patterns;
+// C = alpha*acc + beta*C is evaluated in f32 as in store_tile (C widened
+// exactly) and rounded to binary16 once, to nearest even.  Same tile walk.
+template <int FM, int FN, bool MASKED>
+__device__ __forceinline__ void store_tile16(const f32x16 (&acc)[FM][FN], uint16_t* __restrict__ C,
+                                             int64_t ldc, int row0, int col0, int M, int N,
+                                             float alpha, float beta, int lane) {
+    const int h = lane >> 5, r32 = lane & 31;
+    auto row_of = [&](int i, int e) { return row0 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3); };
+    auto col_of = [&](int j) { return col0 + j * 32 + r32; };
+    auto inside = [&](int row, int col) { return !MASKED || (row < M && col < N); };
+    auto to16 = [](float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); };
+    auto to32 = [](uint16_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); };
+#pragma unroll
+    for (int b = 0; b < FM * FN; ++b) {
+        const int i = b / FN, j = b % FN;
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = row_of(i, e), col = col_of(j);
+            v[e] = (beta != 0.f && inside(row, col)) ? to32(C[(int64_t)row * ldc + col]) : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = row_of(i, e), col = col_of(j);
+            if (inside(row, col))
+                C[(int64_t)row * ldc + col] = to16(
+                    beta == 0.f ? alpha * acc[i][j][e] : __builtin_fmaf(alpha, acc[i][j][e], beta * v[e]));
+        }
         asm volatile("" ::: "memory");
     }
 }

@@ -112,6 +112,21 @@ int gemm_f16r_f32acc_ex(int transa, int transb, int64_t M, int64_t N, int64_t K,
                         float beta, float* C, int64_t ldc, void* stream);
 
 /*
+ * The f16-output variant of the f16r mode (the Matrix Multiplication lab,
+ * "Part 4 -- precision": FP16 operands and an FP16 result, half the bytes per
+ * element of C): operands as in gemm_f16r_f32acc_ex (rounded to binary16,
+ * products accumulated in f32); C16 is a device pointer to M x N IEEE
+ * binary16 values (bit patterns, row stride ldc), read as binary16 when
+ * beta != 0; alpha*acc + beta*C is evaluated in f32 and rounded once to
+ * binary16, to nearest even (overflow to +-inf).  Arguments, special cases
+ * and return codes as gemm_f16r_f32acc_ex (C16 is argument 12).  Tile choice,
+ * pins and tuning are those of the f16r mode.
+ */
+int gemm_f16r_f16out(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
+                     const float* A, int64_t lda, const float* B, int64_t ldb,
+                     float beta, uint16_t* C16, int64_t ldc, void* stream);
+
+/*
  * Per-shape tile autotuning (phobos docs, "gemm, f32", section "Tuning": time
  * every configuration briefly, skip those that fail, then re-time the fastest
  * few over interleaved rounds under the same clocks).  Runs the candidates on

@@ -104,6 +104,15 @@ def test_layout_argument_checks_follow_sgemm_numbering(name):
     assert _call_ex(fn, 1, 1, 0, 5, 7, A=None, B=None, C=None) == 0
 
 
+def test_f16out_argument_checks():
+    fn = g.lib().gemm_f16r_f16out
+    assert _call_ex(fn, 3, 0, 4, 4, 4) == -1
+    assert _call_ex(fn, 0, 0, 4, 4, 8, lda=7) == -8
+    assert _call_ex(fn, 0, 0, 4, 4, 4, C=None) == -12
+    assert _call_ex(fn, 0, 0, 4, 8, 4, ldc=7) == -13
+    assert _call_ex(fn, 0, 0, 0, 8, 4, A=None, B=None, C=None) == 0
+
+
 def test_layout_configs_are_keyed_apart(tmp_path):
     """The tuning cache keys the operand layout: a tuned transposed shape does
     not leak into the plain layout of the same shape, and the cache file names

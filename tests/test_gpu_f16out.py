@@ -1,0 +1,94 @@
+"""GPU tests of the f16-output variant of the f16r mode (gemm_f16r_f16out):
+operands rounded to binary16, products accumulated in f32, C stored as
+binary16 and the f32 epilogue value rounded once to nearest even.
+
+Pins: the result is bit for bit numpy's float16 rounding of the f32-output
+call of the same configuration on the same inputs (the two compute the same f32
+value); it is inside the oracle's bound widened by half a binary16 ulp; small
+integers whose results are exact in binary16 come back exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_inputs, small_integers
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():   # collected on CPU-only hosts, never run there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gemm_tiled_amd as g  # noqa: E402
+from tests.gpu_helpers import pinned, run, say, to_device  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def run16(A, B, C16, alpha, beta):
+    tC = torch.from_numpy(C16.copy()).to(DEV)
+    g.gemm_f16r_f16out(to_device(A), to_device(B), tC, alpha, beta)
+    torch.cuda.synchronize()
+    return tC.cpu().numpy()
+
+
+def inside_bound(A, B, C16, alpha, beta, got16, rows=None):
+    """|C16 - Cref| <= 4e-5 W + 2^-11 (|Cref| + 4e-5 W) + 2^-25: the f16r bound
+    plus the final rounding to binary16 (half an ulp, relative 2^-11, or 2^-25
+    among subnormals)."""
+    C = C16.astype(np.float32)
+    r0, r1 = rows or (0, C.shape[0])
+    ref, W = oracle.gemm("f16r", A[r0:r1], B, C[r0:r1], alpha, beta)
+    err = np.abs(got16[r0:r1].astype(np.float64) - ref)
+    tol = oracle.TOL["f16r"] * W
+    return np.all(err <= tol + 2.0 ** -11 * (np.abs(ref) + tol) + 2.0 ** -25)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 200, 150), (512, 512, 256), (1000, 999, 1001)])
+def test_f16out_is_the_rounded_f32_result(M, N, K):
+    A, B, C = make_inputs(M, N, K, "normal", seed=31)
+    C16 = C.astype(np.float16)
+    for alpha, beta in ((1.0, 0.0), (0.75, -0.25)):
+        cfg = g.get_config("f16r", M, N, K, beta=beta).split(" source=")[0]
+        with pinned("f16r", cfg):
+            say(f"[f16-out] {M}x{N}x{K} {cfg} alpha={alpha} beta={beta}")
+            got16 = run16(A, B, C16, alpha, beta)
+            got32 = run("f16r", A, B, C16.astype(np.float32), alpha, beta)
+        assert np.array_equal(got16.view(np.uint16), got32.astype(np.float16).view(np.uint16))
+        assert inside_bound(A, B, C16, alpha, beta, got16)
+
+
+def test_f16out_every_config():
+    M, N, K = 257, 129, 67
+    A, B, C = make_inputs(M, N, K, "uniform", seed=32)
+    C16 = C.astype(np.float16)
+    for cfg in g.list_configs("f16r"):
+        with pinned("f16r", cfg):
+            say(f"[f16-out] every config {cfg}")
+            got16 = run16(A, B, C16, 1.5, 0.5)
+        assert inside_bound(A, B, C16, 1.5, 0.5, got16), cfg
+
+
+def test_f16out_small_integers_exact():
+    # entries in [-2, 2], K = 100: |result| <= 2 * 400 + 2 * 2 < 2048, exact in binary16
+    M, N, K = 700, 600, 100
+    A, B, C = small_integers(M, N, K, lo=-2, hi=2, seed=33)
+    exact = 2.0 * (A.astype(np.float64) @ B.astype(np.float64)) - 1.0 * C.astype(np.float64)
+    say(f"[f16-out exact] {M}x{N}x{K}")
+    got16 = run16(A, B, C.astype(np.float16), 2.0, -1.0)
+    assert np.array_equal(got16.astype(np.float64), exact)
+
+
+def test_f16out_beta_only_and_few_rows():
+    A, B, C = make_inputs(16, 4096, 4096, "normal", seed=34)
+    C16 = C.astype(np.float16)
+    say("[f16-out] alpha = 0")
+    got16 = run16(A, B, C16, 0.0, -0.5)
+    assert np.array_equal(got16.view(np.uint16),
+                          (np.float32(-0.5) * C16.astype(np.float32)).astype(np.float16).view(np.uint16))
+    say("[f16-out] split-K, 16 rows")
+    assert "KS=1" in g.get_config("f16r", 16, 4096, 4096, beta=0.25)
+    got16 = run16(A, B, C16, 1.0, 0.25)
+    assert inside_bound(A, B, C16, 1.0, 0.25, got16)

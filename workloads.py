@@ -8,7 +8,8 @@ matrices with a fixed seed), so these generators are the workload.
 
 Recipe: ``numpy.random.default_rng(seed)``, draw A, then B, then C, each in
 float64 at its full (M,K), (K,N), (M,N) shape, cast to float32.  Distributions
-are ``uniform(-1, 1)`` or ``standard_normal``.  With padded leading dimensions
+are ``uniform(-1, 1)``, ``standard_normal``, or ``centered`` (U[0,1) - 0.5, the
+inputs of the lab's precision study).  With padded leading dimensions
 the matrix is drawn at its logical shape and placed into a larger zero buffer.
 """
 from __future__ import annotations
@@ -57,6 +58,8 @@ WORKLOADS = {
 def _draw(rng, dist, shape):
     if dist == "uniform":
         return rng.uniform(-1.0, 1.0, size=shape)
+    if dist == "centered":          # the lab's precision inputs: U[0,1) - 0.5
+        return rng.random(size=shape) - 0.5
     if dist == "normal":
         return rng.standard_normal(size=shape)
     if dist == "ones":
