@@ -308,6 +308,37 @@ def test_non_default_stream(mode):
     assert_parity(mode, A, B, C, 1.0, 0.5, tC.cpu().numpy())
 
 
+@pytest.mark.parametrize("mode,M,K", [("f32", 640, 512), ("f16r", 640, 512), ("f16r", 16, 4096),
+                                      ("f32", 16, 4096)])
+def test_graph_capture_replays(mode, M, K):
+    """The calls enqueue kernels only (no allocation once the stream's workspace
+    exists, no memset), so they can be captured into a HIP graph; every replay,
+    with eager work and synchronisations in between, matches the eager call bit
+    for bit.  M = 16 takes the split-K path (partials + reduction)."""
+    N = 384
+    A, B, C = make_inputs(M, N, K, "uniform", seed=14)
+    tA, tB, tC = to_device(A), to_device(B), to_device(C)
+    C0 = tC.clone()
+    s = torch.cuda.Stream()
+    say(f"[graph] {mode} {M}x{N}x{K} {g.get_config(mode, M, N, K, beta=0.5)}")
+    with torch.cuda.stream(s):
+        g.gemm(mode, tA, tB, tC, 1.25, 0.5)          # eager; creates the stream's workspace
+    s.synchronize()
+    eager = tC.clone()
+    graph = torch.cuda.CUDAGraph()
+    tC.copy_(C0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s):
+        g.gemm(mode, tA, tB, tC, 1.25, 0.5)
+    for _ in range(3):
+        tC.copy_(C0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tC, eager)
+    assert_parity(mode, A, B, C, 1.25, 0.5, tC.cpu().numpy())
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_tuner_leaves_c_alone_and_its_choice_is_correct(mode):
     M, N, K = 1536, 1280, 1024
