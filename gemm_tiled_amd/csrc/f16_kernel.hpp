@@ -6,6 +6,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "internal.hpp"
 
@@ -356,20 +357,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(F16Args p) {
 // -- are in flight while one is multiplied; the fills then have several
 // microseconds to arrive from the memory-side cache when they miss in L2.
 //
-// One panel is two steps of 16 k.  The barrier sits between them: step 0
-// multiplies fragments read before it, while this wave reads the fragments of
-// step 1 and issues its fills of the panel NS - 1 ahead; then the wave waits
-// for its fills of the next panel, passes the barrier (every wave's fills of
-// the next panel have landed, every wave has read all of this one), and step 1
-// multiplies while the first fragments of the next panel are read.  So the
-// matrix instructions after a barrier never wait for shared memory.
+// The matrix instruction is v_mfma_f32_16x16x32_f16: one panel is one step of
+// 32 k for every 16 x 16 block of the wave tile.  For the same flops it moves
+// half the accumulator bytes of the 32x32x16 form through the register file
+// per instruction, and on this GPU, whose f16 GEMMs run at the power limit,
+// that measured about 4% faster at 8192^3.  The wave tile is GFM x GFN blocks;
+// the A fragments of rows 0..H-1 (H = GFM/2) and all B fragments of a panel
+// are read before it starts.  First half: rows 0..H-1 are multiplied while the
+// A fragments of rows H.. are read and this wave's fills of the panel NS - 1
+// ahead are issued.  Then the wave waits for its fills of the next panel and
+// passes the barrier (every wave's fills of the next panel have landed, every
+// wave has read all of this one).  Second half: rows H.. are multiplied while
+// the next panel's B fragments (into the other of two buffers) and A rows
+// 0..H-1 are read.  So the matrix instructions never wait for shared memory
+// right after a barrier.
 // ----------------------------------------------------------------------------
 template <int BM, int BN, int NS, int WM, int WN>
 struct RingShape {
     static constexpr int BK = 32;
     static constexpr int NW = WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;
-    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int GFM = TM / 16, GFN = TN / 16;   // 16 x 16 blocks per wave
+    static constexpr int H = GFM / 2;
     static constexpr int ROW = BK * 2;              // bytes per panel row
     static constexpr int A_BYTES = BM * ROW;
     static constexpr int STAGE = (BM + BN) * ROW;   // bytes per stage
@@ -377,7 +386,7 @@ struct RingShape {
     static constexpr int B_INS = BN * ROW / 1024 / NW;
     static constexpr int FILLS = A_INS + B_INS;
     static_assert(NS >= 3 && NS <= 5, "3 to 5 stages");
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(TM % 32 == 0 && TN % 16 == 0, "wave tile must be an even number of block rows");
     static_assert(A_INS >= 1 && B_INS >= 1 && A_INS * 1024 * NW == A_BYTES &&
                       B_INS * 1024 * NW == BN * ROW,
                   "kilobytes of a panel split evenly over the waves");
@@ -386,10 +395,81 @@ struct RingShape {
     static_assert((NS - 2) * FILLS < 64, "vmcnt range");
 };
 
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Epilogue of the 16 x 16 blocks: element e of lane l in block (i, j) sits at
+// row 16 i + 4 (l / 16) + e, column 16 j + l % 16.  Same value as store_tile,
+// fma(alpha, acc, beta*c), for f32 or binary16 C (read widened, rounded once
+// to nearest even).  beta == 0 never reads C.  With beta != 0 the loads of a
+// row of blocks are issued before the stores of the previous row.
+template <int FM, int FN, bool MASKED, bool OUT16, typename CT>
+__device__ __forceinline__ void store_tile_m16(const f32x4 (&acc)[FM][FN], CT* __restrict__ C,
+                                               int64_t ldc, int row0, int col0, int M, int N,
+                                               float alpha, float beta, int lane) {
+    const int q = lane >> 4, r16 = lane & 15;
+    auto row_of = [&](int i, int e) { return row0 + i * 16 + 4 * q + e; };
+    auto col_of = [&](int j) { return col0 + j * 16 + r16; };
+    auto inside = [&](int row, int col) { return !MASKED || (row < M && col < N); };
+    auto ld = [&](int row, int col) -> float {
+        if constexpr (OUT16)
+            return static_cast<float>(__builtin_bit_cast(_Float16, C[(int64_t)row * ldc + col]));
+        else
+            return __builtin_nontemporal_load(C + (int64_t)row * ldc + col);
+    };
+    auto st = [&](int row, int col, float v) {
+        if constexpr (OUT16)
+            C[(int64_t)row * ldc + col] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+        else
+            __builtin_nontemporal_store(v, C + (int64_t)row * ldc + col);
+    };
+    if (beta == 0.f) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (inside(row_of(i, e), col_of(j)))
+                        st(row_of(i, e), col_of(j), alpha * acc[i][j][e]);
+        return;
+    }
+    float v[2][FN * 4];
+    auto load_row = [&](int i, float(&d)[FN * 4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                d[j * 4 + e] = inside(row_of(i, e), col_of(j)) ? ld(row_of(i, e), col_of(j)) : 0.f;
+    };
+    load_row(0, v[0]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        if (i + 1 < FM) load_row(i + 1, v[(i + 1) & 1]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (inside(row_of(i, e), col_of(j)))
+                    st(row_of(i, e), col_of(j),
+                       __builtin_fmaf(alpha, acc[i][j][e], beta * v[i & 1][j * 4 + e]));
+        asm volatile("" ::: "memory");
+    }
+}
+
 template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED, bool OUT16>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_ring_kernel(F16Args p) {
     using S = RingShape<BM, BN, NS, WM, WN>;
     constexpr int D = S::BK;
+    constexpr int GFM = S::GFM, GFN = S::GFN, H = S::H;
+    constexpr int U = 2 * NS;   // panels per unrolled step: every stage, both B buffers
     __shared__ __attribute__((aligned(1024))) unsigned char st0[S::STAGE];
     __shared__ __attribute__((aligned(1024))) unsigned char st1[S::STAGE];
     __shared__ __attribute__((aligned(1024))) unsigned char st2[S::STAGE];
@@ -403,8 +483,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_ring_kernel(F16Args p) 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / WN, wc = wave % WN;
-    const int h = lane >> 5;
-    const int r32 = lane & 31;
     const int nk = static_cast<int>(p.nkb);
 
     // Panel kt of this tile's A rows is the BM-row slice at row m0 % 256 of
@@ -431,97 +509,106 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_ring_kernel(F16Args p) 
             lds_copy16(b_src + kofs + j * S::NW * 1024, bs + j * S::NW * 1024);
     };
 
-    // Fragment reads: lane (h, r32) of block i reads row r32 of the block at
-    // logical chunk 2h + ks (lane half h feeds k in [16h, 16h + 16) of the
-    // panel, 8 per instruction, to A and B alike).  Blocks start at multiples
-    // of 32 rows, a whole number of swizzle periods, so the key is swz(r32).
-    const int sw = swz<D>(r32);
-    const int a_row0 = (wr * S::TM + r32) * S::ROW;
-    const int b_row0 = S::A_BYTES + (wc * S::TN + r32) * S::ROW;
-    f16x8 fa[2][S::FM], fb[2][S::FN];
-    auto frags = [&](const unsigned char* stage, int ks) __attribute__((always_inline)) {
-        const lds_u8* base = (const lds_u8*)(stage);
-        const int chunk = ((h * 2 + ks) ^ sw) << 4;
-#pragma unroll
-        for (int i = 0; i < S::FM; ++i)
-            fa[ks][i] = *reinterpret_cast<lds_f16x8*>(base + a_row0 + i * 32 * S::ROW + chunk);
-#pragma unroll
-        for (int j = 0; j < S::FN; ++j)
-            fb[ks][j] = *reinterpret_cast<lds_f16x8*>(base + b_row0 + j * 32 * S::ROW + chunk);
+    // Fragment reads: lane (q, r16) reads row r16 of a 16-row block at logical
+    // chunk q, the 8 k values [8q, 8q + 8) of the panel, to A and B alike.
+    // Blocks start at multiples of 16 rows, a whole swizzle period, so the key
+    // is swz(r16); the 16 lanes of a quarter hit 16 different 16-byte slots.
+    const int r16 = lane & 15, q = lane >> 4;
+    const int chunk = (q ^ swz<D>(r16)) << 4;
+    const int a_row0 = (wr * S::TM + r16) * S::ROW + chunk;
+    const int b_row0 = S::A_BYTES + (wc * S::TN + r16) * S::ROW + chunk;
+    f16x8 fa[GFM], fb[2][GFN];
+    auto read_a = [&](const unsigned char* stage, int i) __attribute__((always_inline)) {
+        fa[i] = *reinterpret_cast<lds_f16x8*>((const lds_u8*)(stage) + a_row0 + i * 16 * S::ROW);
+    };
+    auto read_b = [&](const unsigned char* stage, int b, int j) __attribute__((always_inline)) {
+        fb[b][j] = *reinterpret_cast<lds_f16x8*>((const lds_u8*)(stage) + b_row0 + j * 16 * S::ROW);
     };
 
     // The accumulators get their first value from the first matrix
     // instruction, with an inline-constant zero as its addend.
-    f32x16 acc[S::FM][S::FN];
-    constexpr int NMF = S::FM * S::FN;
-    constexpr int NFR = S::FM + S::FN;
-    auto mfmas = [&](int ks, auto first) __attribute__((always_inline)) {
-        const f32x16 zero = {};
+    f32x4 acc[GFM][GFN];
+    auto mfma_rows = [&](int i0, int i1, int b, auto first) __attribute__((always_inline)) {
+        const f32x4 zero = {};
 #pragma unroll
-        for (int i = 0; i < S::FM; ++i)
+        for (int i = i0; i < i1; ++i)
 #pragma unroll
-            for (int j = 0; j < S::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    fa[ks][i], fb[ks][j], decltype(first)::value ? zero : acc[i][j], 0, 0, 0);
+            for (int j = 0; j < GFN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    fa[i], fb[b][j], decltype(first)::value ? zero : acc[i][j], 0, 0, 0);
     };
     // one matrix instruction, then one fragment read, while reads remain
-    auto interleave = [&]() __attribute__((always_inline)) {
+    auto interleave = [&](auto nmf_c, auto nrd_c) __attribute__((always_inline)) {
+        constexpr int nmf = decltype(nmf_c)::value, nrd = decltype(nrd_c)::value;
 #pragma unroll
-        for (int m = 0; m < NMF; ++m) {
+        for (int m = 0; m < nmf; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (m < NFR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (m < nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
     };
 
-    // One panel in stage `cur`: fill panel kt_fill into `freed` (the stage of
-    // the previous panel, which every wave finished reading before the last
-    // barrier), step 0 beside the reads of step 1, wait for this wave's fills
-    // of the next panel, barrier, step 1 beside the first reads of `next`.
+    // One panel in stage `cur`, its B fragments in fb[b]: fill panel kt_fill
+    // into `freed` (the stage of the previous panel, which every wave finished
+    // reading before the last barrier), then the two halves described above.
     // Fills past the last panel reload the last panel into a stage nobody
     // reads again, so the count of outstanding fills is the same every panel.
     auto panel = [&](const unsigned char* cur, unsigned char* freed, const unsigned char* next,
-                     int kt_fill, auto first) __attribute__((always_inline)) {
+                     int kt_fill, auto b_c, auto first) __attribute__((always_inline)) {
+        constexpr int b = decltype(b_c)::value;
         fill(freed, kt_fill);
-        frags(cur, 1);
-        mfmas(0, first);
+#pragma unroll
+        for (int i = H; i < GFM; ++i) read_a(cur, i);
+        mfma_rows(0, H, b, first);
         __builtin_amdgcn_sched_group_barrier(0x020, S::FILLS, 0);
-        interleave();
+        interleave(std::integral_constant<int, H * GFN>{}, std::integral_constant<int, GFM - H>{});
         wait_vmcnt<(NS - 2) * S::FILLS>();
         ring_barrier();
-        frags(next, 0);
-        mfmas(1, std::false_type{});
-        interleave();
+#pragma unroll
+        for (int j = 0; j < GFN; ++j) read_b(next, b ^ 1, j);
+#pragma unroll
+        for (int i = 0; i < H; ++i) read_a(next, i);
+        mfma_rows(H, GFM, b, first);
+        interleave(std::integral_constant<int, (GFM - H) * GFN>{},
+                   std::integral_constant<int, GFN + H>{});
+    };
+    // Panel kt + u of an unrolled step: stage (kt + u) % NS with kt a multiple
+    // of U, and the B buffer alternates with the panel's parity.
+    auto step = [&](int kt, auto u_c, auto first) __attribute__((always_inline)) {
+        constexpr int u = decltype(u_c)::value;
+        panel(stage_of(u % NS), stage_of((u + NS - 1) % NS), stage_of((u + 1) % NS),
+              min(kt + u + NS - 1, nk - 1), std::integral_constant<int, u & 1>{}, first);
     };
 
-    // Prologue: panels 0 .. NS-2 into stages 0 .. NS-2; wait for panel 0.
+    // Prologue: panels 0 .. NS-2 into stages 0 .. NS-2; wait for panel 0 and
+    // read its first fragments.
 #pragma unroll
     for (int i = 0; i + 1 < NS; ++i) fill(stage_of(i), min(i, nk - 1));
     wait_vmcnt<(NS - 2) * S::FILLS>();
     ring_barrier();
-    frags(stage_of(0), 0);
+#pragma unroll
+    for (int j = 0; j < GFN; ++j) read_b(stage_of(0), 0, j);
+#pragma unroll
+    for (int i = 0; i < H; ++i) read_a(stage_of(0), i);
 
-    panel(stage_of(0), stage_of(NS - 1), stage_of(1), min(NS - 1, nk - 1), std::true_type{});
-#pragma unroll
-    for (int u = 1; u < NS; ++u)
-        if (u < nk)
-            panel(stage_of(u), stage_of(u - 1), stage_of((u + 1) % NS), min(u + NS - 1, nk - 1),
-                  std::false_type{});
-    for (int kt = NS; kt < nk; kt += NS) {
-#pragma unroll
-        for (int u = 0; u < NS; ++u) {
-            if (u == 0 || kt + u < nk)
-                panel(stage_of(u), stage_of((u + NS - 1) % NS), stage_of((u + 1) % NS),
-                      min(kt + u + NS - 1, nk - 1), std::false_type{});
-        }
+    step(0, std::integral_constant<int, 0>{}, std::true_type{});
+    static_for<U - 1>([&](auto v_c) __attribute__((always_inline)) {
+        constexpr int u = decltype(v_c)::value + 1;
+        if (u < nk) step(0, std::integral_constant<int, u>{}, std::false_type{});
+    });
+    for (int kt = U; kt < nk; kt += U) {
+        static_for<U>([&](auto u_c) __attribute__((always_inline)) {
+            if (decltype(u_c)::value == 0 || kt + decltype(u_c)::value < nk)
+                step(kt, u_c, std::false_type{});
+        });
     }
     wait_vmcnt<0>();   // no fill may still be landing in LDS when the workgroup ends
 
     if constexpr (OUT16)
-        store_tile16<S::FM, S::FN, MASKED>(acc, p.C16, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN,
-                                           p.M, p.N, p.alpha, p.beta, lane);
+        store_tile_m16<GFM, GFN, MASKED, true>(acc, p.C16, p.ldc, m0 + wr * S::TM,
+                                               n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta, lane);
     else
-        store_tile<S::FM, S::FN, MASKED>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M,
-                                         p.N, p.alpha, p.beta, lane);
+        store_tile_m16<GFM, GFN, MASKED, false>(acc, p.C, p.ldc, m0 + wr * S::TM,
+                                                n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta, lane);
 }
 
 // One configuration, both masking variants, f32 (OUT16 false) or binary16 C.
