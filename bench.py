@@ -223,8 +223,11 @@ def measure_roofs(g, torch, dev, seconds):
     return out
 
 
-def steady(fn, torch, seconds=0.5, min_calls=3):
-    """Median seconds per call after settling (the lab's steady())."""
+def steady(fn, torch, seconds=0.5, min_calls=3, batch=1):
+    """Median seconds per call after settling (the lab's steady()).  With
+    batch > 1 each sample times `batch` back-to-back calls between two events
+    and divides: for calls of a few microseconds, the GPU time per call in a
+    stream of calls, without the host's per-call launch latency."""
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds / 2:
         fn()
@@ -233,10 +236,11 @@ def steady(fn, torch, seconds=0.5, min_calls=3):
     ts, t0 = [], time.perf_counter()
     while time.perf_counter() - t0 < seconds or len(ts) < min_calls:
         s_ev.record()
-        fn()
+        for _ in range(batch):
+            fn()
         e_ev.record()
         e_ev.synchronize()
-        ts.append(s_ev.elapsed_time(e_ev) / 1e3)
+        ts.append(s_ev.elapsed_time(e_ev) / 1e3 / batch)
     return float(np.median(ts))
 
 
@@ -576,6 +580,7 @@ def precision_study(g, torch, dev, out):
 # f32 storage; below the ridge the HBM roof bounds the call.
 # ---------------------------------------------------------------------------
 SKINNY_M = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048]
+SKINNY_BATCH = 20   # calls per timed sample: the calls take microseconds
 
 
 def skinny_sweep(g, torch, dev, out, repeats):
@@ -597,7 +602,7 @@ def skinny_sweep(g, torch, dev, out, repeats):
         tA, tC = torch.from_numpy(A).to(dev), torch.from_numpy(C).to(dev)
         for mode in ("f32", "f16r"):
             ref, W = oracle.entries(mode, A, B, C, 1.0, 0.0, r, c)
-            for kind in ("tuned", "no split-K"):
+            for kind in ("tuned", "split-K", "rows", "no split-K"):
                 cases.append((mode, M, kind, tA, tC, r, c, ref, W))
     calls, tiles = {}, {}
     for (mode, M, kind, tA, tC, r, c, ref, W) in cases:
@@ -607,6 +612,16 @@ def skinny_sweep(g, torch, dev, out, repeats):
             g.tune(mode, tA, tB, tC, beta=0.0)
             tiles[key] = g.get_config(mode, M, N, K, beta=0.0)
             call = (lambda fn=fn, tA=tA, tC=tC: fn(tA, tB, tC, 1.0, 0.0))
+        elif kind in ("split-K", "rows"):
+            cfg = g.parse_config(mode, "KS=1" if kind == "split-K" else "KS=2")
+            tiles[key] = cfg
+
+            def call(fn=fn, tA=tA, tC=tC, mode=mode, cfg=cfg):
+                g.set_config(mode, cfg)
+                try:
+                    fn(tA, tB, tC, 1.0, 0.0)
+                finally:
+                    g.set_config(mode, None)
         else:
             # the library's best configuration without split-K (tuned over the rest)
             best, best_t = None, 1e30
@@ -615,7 +630,8 @@ def skinny_sweep(g, torch, dev, out, repeats):
                     continue
                 g.set_config(mode, cfg)
                 try:
-                    t = steady(lambda fn=fn, tA=tA, tC=tC: fn(tA, tB, tC, 1.0, 0.0), torch, 0.05)
+                    t = steady(lambda fn=fn, tA=tA, tC=tC: fn(tA, tB, tC, 1.0, 0.0), torch, 0.05,
+                               batch=SKINNY_BATCH)
                 finally:
                     g.set_config(mode, None)
                 if t < best_t:
@@ -640,7 +656,7 @@ def skinny_sweep(g, torch, dev, out, repeats):
         order = list(calls)
         rng.shuffle(order)
         for k in order:
-            times[k].append(steady(calls[k], torch, seconds=0.2))
+            times[k].append(steady(calls[k], torch, seconds=0.2, batch=SKINNY_BATCH))
         log(f"skinny: round {rnd + 1} of {repeats} done")
     rows = []
     hbm = roofs["hbm_read_gbs"] * 1e9
@@ -659,12 +675,17 @@ def skinny_sweep(g, torch, dev, out, repeats):
              "Command:", "", "```", "python bench.py --skinny profiles/skinny_m.md", "```", "",
              "A (M x K), B (K x N), C iid N(0,1); alpha = 1, beta = 0.  Every case is checked "
              "against the oracle on 256 sampled elements before it is timed; the time is the "
-             f"median of {repeats} shuffled rounds of steady() (0.2 s).  Bytes are the f32 "
+             f"median of {repeats} shuffled rounds of steady() (0.2 s), each sample "
+             f"{SKINNY_BATCH} back-to-back calls between two events (GPU time per call in a "
+             "stream of calls: at M = 1 a call takes ~15 us, less than the host's per-call "
+             "launch latency, which a single-call sample would add).  Bytes are the f32 "
              "storage the call must move at least once, 4(MK + KN + MN); the roof is "
              "min(measured matrix-core roof of the mode, intensity x measured HBM read roof "
-             f"{roofs['hbm_read_gbs']:.0f} GB/s).  `tuned` is the library's own choice (the "
-             "split-K configuration is one of the candidates); `no split-K` is the fastest "
-             "configuration without it.", "",
+             f"{roofs['hbm_read_gbs']:.0f} GB/s).  `tuned` is the library's own choice (all "
+             "configurations are candidates); `split-K` is the 32x128-tile split-K "
+             "configuration (KS=1), `rows` the few-rows configuration (KS=2: B streamed into "
+             "registers, 16x16x4 matrix instructions, k split within and across workgroups); "
+             "`no split-K` is the fastest configuration of neither kind.", "",
              "| mode | M | choice | TFLOP/s | GB/s | FLOP/B | bound | of roof | tile |",
              "|---|---:|---|---:|---:|---:|---|---:|---|"]
     for r_ in sorted(rows, key=lambda r_: (r_["mode"], r_["M"], r_["kind"])):
@@ -683,7 +704,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "f32": ["gemm_tiled_amd/csrc/gemm_f32.hip", "gemm_tiled_amd/csrc/f32_kernel.hpp",
             "gemm_tiled_amd/csrc/internal.hpp"],
-    "f16r": ["gemm_tiled_amd/csrc/gemm_f16r.hip", "gemm_tiled_amd/csrc/internal.hpp"],
+    "f16r": ["gemm_tiled_amd/csrc/gemm_f16r.hip", "gemm_tiled_amd/csrc/f16_kernel.hpp",
+             "gemm_tiled_amd/csrc/internal.hpp"],
 }
 
 

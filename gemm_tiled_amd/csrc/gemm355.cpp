@@ -37,7 +37,9 @@ bool log_debug() {
 
 const char* mode_name(int mode) { return mode == GEMM355_MODE_F32 ? "f32" : "f16r"; }
 
-// Up to this many rows of C the heuristic picks the split-K configuration.
+// Up to this many rows of C the heuristic picks the few-rows configuration,
+// and up to kSplitKRows the split-K configuration.
+constexpr int64_t kRowsRows = 16;
 constexpr int64_t kSplitKRows = 64;
 // Compute units of the MI355X (gfx950).
 constexpr int64_t kCUs = 256;
@@ -46,6 +48,8 @@ constexpr int64_t kCUs = 256;
 constexpr int64_t kSplitKTarget = 3 * kCUs;
 constexpr int64_t kSplitKMinDepth = 128;
 constexpr int64_t kSplitKMaxBytes = int64_t{1} << 30;
+// Most workgroups (of four waves) a few-rows launch splits K into.
+constexpr int64_t kRowsMaxWgs = 8 * kCUs;
 
 // ---------------------------------------------------------------------------
 // Instances and configuration strings.
@@ -61,6 +65,7 @@ std::vector<TileConfig> configs_of(int mode) {
         for (int i = 0; i < n; ++i) out.push_back(t[i].cfg);
     }
     out.push_back(splitk_config(mode));
+    out.push_back(rows_config(mode));
     return out;
 }
 
@@ -200,7 +205,9 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // efficiency of the tile), the trade-off of the phobos "Tuning" section:
 // larger tiles reuse more, but leave fewer workgroups to fill the chip.
 TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K) {
-    // a few rows of C: the split-K configuration (memory-bound, too few tiles)
+    // a few rows of C (memory-bound, too few tiles): the few-rows
+    // configuration up to one 16-row group, then the split-K tiles
+    if (M <= kRowsRows) return rows_config(mode);
     if (M <= kSplitKRows) return splitk_config(mode);
     const std::vector<TileConfig> all = configs_of(mode);
     double best = 1e300;
@@ -290,6 +297,40 @@ hipError_t workspace(hipStream_t s, size_t bytes, void** out) {
     return hipSuccess;
 }
 
+// Arrival counters of the few-rows configuration: one zeroed buffer per
+// (device, stream), grown on demand (zeroed again when it grows).  The kernel
+// leaves every counter it uses at zero.
+std::map<WsKey, Ws> g_counts;
+
+hipError_t counters(hipStream_t s, size_t n, unsigned** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    Ws& w = g_counts[WsKey{dev, s}];
+    const size_t bytes = n * sizeof(unsigned);
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            e = hipStreamSynchronize(s);
+            if (e != hipSuccess) return e;
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        const size_t grown = std::max<size_t>(bytes, 4096);
+        e = hipMalloc(&w.ptr, grown);
+        if (e == hipSuccess) e = hipMemsetAsync(w.ptr, 0, grown, s);
+        if (e != hipSuccess) {
+            if (w.ptr) (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            return e;
+        }
+        w.bytes = grown;
+    }
+    *out = static_cast<unsigned*>(w.ptr);
+    return hipSuccess;
+}
+
 // ---------------------------------------------------------------------------
 // Argument checks (BLAS xerbla numbering) and the dispatch of one call.
 // ---------------------------------------------------------------------------
@@ -364,9 +405,59 @@ int launch_splitk(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_
                                           C, ldc, s));
 }
 
+// The few-rows configuration: slices of K so that column groups x row groups
+// x slices reaches kRowsTarget workgroups, each slice a whole number of
+// rows_depth_unit() (every wave at least one 64-deep chunk), the partial
+// tiles within kSplitKMaxBytes.  Shapes whose B cannot be read 16 bytes at a
+// time take the split-K configuration instead.
+int launch_rows(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
+                const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                int64_t ldc, hipStream_t s, uint16_t* C16) {
+    const bool ta = (trans & 1) != 0, tb = (trans & 2) != 0;
+    if (!rows_supported(ta, tb, B, lda, ldb, static_cast<int>(M), static_cast<int>(N),
+                        static_cast<int>(K)))
+        return launch_splitk(splitk_config(cfg.mode), trans, M, N, K, alpha, A, lda, B, ldb, beta,
+                             C, ldc, s, C16);
+    // Slice depth: two 64-deep chunks per wave (one pass of the kernel) when
+    // that gives at least one workgroup per CU, one chunk when the grid would
+    // be smaller; deeper slices when there would be more than kRowsMaxWgs
+    // workgroups or the partial tiles would pass kSplitKMaxBytes.
+    const int64_t unit = rows_depth_unit();
+    const int64_t group = rows_group(static_cast<int>(M));
+    const int64_t wgs = ((N + 63) / 64) * ((M + group - 1) / group);
+    int64_t depth = 2 * unit;
+    if (wgs * ((K + depth - 1) / depth) < kCUs) depth = unit;
+    const int64_t max_slices = std::max<int64_t>(
+        1, std::min(kRowsMaxWgs / wgs, kSplitKMaxBytes / std::max<int64_t>(1, M * round_up(N, 4) * 4)));
+    if ((K + depth - 1) / depth > max_slices) depth = round_up((K + max_slices - 1) / max_slices, unit);
+    const int64_t slices = (K + depth - 1) / depth;
+    const bool r16 = cfg.mode == GEMM355_MODE_F16R;
+    if (log_debug())
+        std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=rows x%lld (k %lld)%s\n",
+                     layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
+                     (long long)K, format_config(cfg).c_str(), (long long)slices,
+                     (long long)depth, C16 ? " f16-out" : "");
+    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    float* P = nullptr;
+    unsigned* counts = nullptr;
+    if (slices > 1) {
+        void* ws = nullptr;
+        // partial rows are N rounded up to 4 floats apart
+        hipError_t e = workspace(s, static_cast<size_t>(slices * M * round_up(N, 4)) * 4, &ws);
+        if (e == hipSuccess) e = counters(s, static_cast<size_t>(rows_counters(m, n)), &counts);
+        if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
+        P = static_cast<float*>(ws);
+    }
+    return status_of(launch_f32_rows(A, lda, ta, B, ldb, tb, r16, C, C16, ldc, m, n, k, alpha,
+                                     beta, static_cast<int>(depth), static_cast<int>(slices), P,
+                                     counts, s));
+}
+
 int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
                 int64_t ldc, hipStream_t s, uint16_t* C16) {
+    if (cfg.ks == 2)
+        return launch_rows(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
     if (cfg.ks)
         return launch_splitk(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
     const int tiles_m = static_cast<int>((M + cfg.bm - 1) / cfg.bm);

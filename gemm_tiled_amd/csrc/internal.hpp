@@ -110,6 +110,24 @@ hipError_t launch_splitk_reduce16(const float* P, int S, int M, int N, float alp
 TileConfig splitk_config(int mode);
 hipError_t launch_f32_splitk(const F32Args& a, F32Variant v, hipStream_t s);
 
+// The few-rows configuration (KS=2, gemm_rows.hip): B streamed from memory
+// into registers, k split within and across workgroups.  Needs 16-byte loads
+// of B: B aligned, ldb % 4 == 0, and N % 4 == 0 (B is K x N) or K % 4 == 0
+// (B stored N x K).  depth is the k per slice, a multiple of
+// rows_depth_unit(); with slices > 1 the workgroups store partial tiles in P
+// and the last one of each column of workgroups (counted in `counts`, zero
+// before and after the launch) adds them in slice order and writes C.
+TileConfig rows_config(int mode);
+int rows_depth_unit();
+int rows_group(int M);
+bool rows_supported(bool ta, bool tb, const float* B, int64_t lda, int64_t ldb, int M, int N,
+                    int K);
+int rows_counters(int M, int N);
+hipError_t launch_f32_rows(const float* A, int64_t lda, bool ta, const float* B, int64_t ldb,
+                           bool tb, bool r16, float* C, uint16_t* C16, int64_t ldc, int M, int N,
+                           int K, float alpha, float beta, int depth, int slices, float* P,
+                           unsigned* counts, hipStream_t s);
+
 // Measurement kernels.
 hipError_t launch_roof_mfma(int mode, int64_t iters, int blocks, float* sink, double* flops,
                             hipStream_t s);

@@ -88,7 +88,9 @@ def test_f16out_beta_only_and_few_rows():
     got16 = run16(A, B, C16, 0.0, -0.5)
     assert np.array_equal(got16.view(np.uint16),
                           (np.float32(-0.5) * C16.astype(np.float32)).astype(np.float16).view(np.uint16))
-    say("[f16-out] split-K, 16 rows")
-    assert "KS=1" in g.get_config("f16r", 16, 4096, 4096, beta=0.25)
-    got16 = run16(A, B, C16, 1.0, 0.25)
-    assert inside_bound(A, B, C16, 1.0, 0.25, got16)
+    for cfg in ("BM=32 BN=128 BK=32 KS=1", "BM=16 BN=64 BK=64 KS=2"):
+        say(f"[f16-out] 16 rows, {cfg}")
+        with pinned("f16r", cfg):
+            got16 = run16(A, B, C16, 1.0, 0.25)
+        assert inside_bound(A, B, C16, 1.0, 0.25, got16)
+    assert "KS=2" in g.get_config("f16r", 16, 4096, 4096, beta=0.25)

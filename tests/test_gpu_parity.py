@@ -144,11 +144,84 @@ def test_splitk_small_integers_exact_and_beta_zero(mode):
         assert np.array_equal(got, exact.astype(np.float32))
 
 
+ROWS = "BM=16 BN=64 BK=64 KS=2"
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("M,N,K,lds", [
+    (1, 4096, 4096, {}),
+    (16, 4096, 4096, {}),
+    (17, 1000, 4093, {}),                     # 32-row group, ragged K and N
+    (64, 4096, 4096, {}),
+    (65, 516, 777, {"lda": 779, "ldc": 517}),   # two 64-row groups, odd lda/ldc
+    (5, 4100, 300, {"ldb": 4104}),            # one slice: the epilogue in the kernel
+    (3, 514, 1024, {}),                       # N % 4 != 0: falls back to split-K
+])
+def test_rows_against_the_oracle(mode, M, N, K, lds):
+    A, B, C = make_inputs(M, N, K, "normal", seed=15, **lds)
+    with pinned(mode, ROWS):
+        say(f"[rows] {mode} {M}x{N}x{K} {lds}")
+        got = run(mode, A, B, C, 1.25, -0.5)
+        again = run(mode, A, B, C, 1.25, -0.5)
+    assert_parity(mode, A, B, C, 1.25, -0.5, got)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))   # fixed slice order
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("M", [1, 9, 32, 48])
+def test_rows_small_integers_exact_and_beta_zero(mode, M):
+    N, K = 2048, 4096
+    A, B, C = small_integers(M, N, K, seed=16)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned(mode, ROWS):
+        say(f"[rows exact] {mode} {M}x{N}x{K}")
+        got = run(mode, A, B, C, -2.0, 0.5)
+        assert np.array_equal(got, (-2.0 * exact + 0.5 * C.astype(np.float64)).astype(np.float32))
+        Cn = np.full((M, N), np.nan, dtype=np.float32)
+        got = run(mode, A, B, Cn, 1.0, 0.0)
+        assert np.array_equal(got, exact.astype(np.float32))
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("ta,tb,N", [(True, False, 1028), (False, True, 1028), (True, True, 1028),
+                                     (False, True, 1027), (True, True, 61)])
+def test_rows_layouts(mode, ta, tb, N):
+    M, K = 24, 2052
+    A, B, C = make_inputs(M, N, K, "uniform", seed=17)
+    tA = to_device(np.ascontiguousarray(A.T) if ta else A)
+    tB = to_device(np.ascontiguousarray(B.T) if tb else B)
+    tC = to_device(C)
+    with pinned(mode, ROWS):
+        say(f"[rows layout] {mode} ta={ta} tb={tb} {M}x{N}x{K}")  # B^T: any N
+        g.gemm(mode, tA, tB, tC, 0.5, 2.0, transa=ta, transb=tb)
+        torch.cuda.synchronize()
+    assert_parity(mode, A, B, C, 0.5, 2.0, tC.cpu().numpy())
+
+
+def test_rows_f16_output():
+    M, N, K = 12, 2048, 4096
+    A, B, C = make_inputs(M, N, K, "normal", seed=18)
+    C16 = C.astype(np.float16)
+    tA, tB = to_device(A), to_device(B)
+    t16 = torch.from_numpy(C16.copy()).to("cuda")
+    t32 = to_device(C16.astype(np.float32))
+    with pinned("f16r", ROWS):
+        say(f"[rows f16-out] {M}x{N}x{K}")
+        g.gemm_f16r_f16out(tA, tB, t16, 0.75, -0.25)
+        g.gemm("f16r", tA, tB, t32, 0.75, -0.25)
+        torch.cuda.synchronize()
+    want = t32.cpu().numpy().astype(np.float16)
+    got = t16.cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
 def test_splitk_is_the_default_for_few_rows():
     for mode in MODES:
-        assert g.get_config(mode, 16, 4096, 4096).startswith("BM=32 BN=128 BK=32")
-        assert "KS=1" in g.get_config(mode, 16, 4096, 4096)
-        assert "KS=1" not in g.get_config(mode, 4096, 4096, 4096)
+        assert "KS=2" in g.get_config(mode, 1, 4096, 4096)
+        assert "KS=2" in g.get_config(mode, 16, 4096, 4096)
+        assert g.get_config(mode, 17, 4096, 4096).startswith("BM=32 BN=128 BK=32")
+        assert "KS=1" in g.get_config(mode, 64, 4096, 4096)
+        assert "KS=" not in g.get_config(mode, 4096, 4096, 4096)
 
 
 # ---------------------------------------------------------------------------
