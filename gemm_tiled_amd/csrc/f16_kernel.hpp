@@ -464,17 +464,94 @@ __device__ __forceinline__ void store_tile_m16(const f32x4 (&acc)[FM][FN], CT* _
     }
 }
 
+// The staged epilogue's shared memory per wave: 16 rows of TN floats, rows
+// TN + 4 floats apart (the four lane quarters of a block write four rows at
+// once; the padding puts them in different banks).
+template <int TN>
+struct StagedRows {
+    static constexpr int RS = TN + 4;
+    static constexpr int BYTES = 16 * RS * 4;
+};
+
+// Epilogue through shared memory for f32 C with 16-byte aligned rows and a
+// whole tile: one 16-row band of the wave's tile at a time is written to the
+// wave's own shared memory in the matrix-instruction layout and read back as
+// float4 along rows, so C is read (beta != 0) and written in whole 128-byte
+// row segments instead of the 64-byte ones of the block layout.  The same
+// value as store_tile: fma(alpha, acc, beta*c).  A wave's shared-memory
+// instructions complete in order, so no wait separates the write of a band,
+// its read-back and the next band's write.
+template <int FM, int FN, int TN>
+__device__ __forceinline__ void store_tile_m16_staged(const f32x4 (&acc)[FM][FN],
+                                                      float* __restrict__ C, int64_t ldc,
+                                                      int row0, int col0, float alpha, float beta,
+                                                      int lane, unsigned char* stage) {
+    using R = StagedRows<TN>;
+    static_assert(FN * 16 == TN, "a band is the wave tile's width");
+    constexpr int LPR = TN / 4;        // lanes per staged row (one float4 each)
+    constexpr int RPI = 64 / LPR;      // rows per read-back instruction
+    constexpr int IT = 16 / RPI;
+    typedef __attribute__((address_space(3))) float lds_f32;
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    lds_f32* st = (lds_f32*)(stage);
+    const int q = lane >> 4, r16 = lane & 15;
+    const int rr0 = lane / LPR, c4 = lane % LPR;
+    auto c_at = [&](int i, int it) { return C + (int64_t)(row0 + 16 * i + it * RPI + rr0) * ldc + col0 + 4 * c4; };
+    auto stage_band = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[(4 * q + e) * R::RS + 16 * j + r16] = acc[i][j][e];
+    };
+    auto staged = [&](int it) __attribute__((always_inline)) {
+        return *(const lds_f32x4*)(st + (it * RPI + rr0) * R::RS + 4 * c4);
+    };
+    if (beta == 0.f) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            stage_band(i);
+#pragma unroll
+            for (int it = 0; it < IT; ++it)
+                __builtin_nontemporal_store(alpha * staged(it), reinterpret_cast<f32x4*>(c_at(i, it)));
+        }
+        return;
+    }
+    // the C loads of band i + 1 are issued before band i is written
+    f32x4 old[2][IT];
+    auto load_band = [&](int i, f32x4(&d)[IT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+            d[it] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(c_at(i, it)));
+    };
+    load_band(0, old[0]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        if (i + 1 < FM) load_band(i + 1, old[(i + 1) & 1]);
+        stage_band(i);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const f32x4 v = staged(it);
+            f32x4 out;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) out[x] = __builtin_fmaf(alpha, v[x], beta * old[i & 1][it][x]);
+            __builtin_nontemporal_store(out, reinterpret_cast<f32x4*>(c_at(i, it)));
+        }
+    }
+}
+
 template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED, bool OUT16>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_ring_kernel(F16Args p) {
     using S = RingShape<BM, BN, NS, WM, WN>;
+    static_assert(S::NW * StagedRows<S::TN>::BYTES <= NS * S::STAGE, "staged epilogue fits the ring");
     constexpr int D = S::BK;
     constexpr int GFM = S::GFM, GFN = S::GFN, H = S::H;
     constexpr int U = 2 * NS;   // panels per unrolled step: every stage, both B buffers
-    __shared__ __attribute__((aligned(1024))) unsigned char st0[S::STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char st1[S::STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char st2[S::STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char st3[NS > 3 ? S::STAGE : 16];
-    __shared__ __attribute__((aligned(1024))) unsigned char st4[NS > 4 ? S::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * S::STAGE];
+    unsigned char* const st0 = ring;
+    unsigned char* const st1 = ring + S::STAGE;
+    unsigned char* const st2 = ring + 2 * S::STAGE;
+    unsigned char* const st3 = ring + (NS > 3 ? 3 : 0) * S::STAGE;
+    unsigned char* const st4 = ring + (NS > 4 ? 4 : 0) * S::STAGE;
 
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM, tm, tn);
@@ -603,12 +680,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_ring_kernel(F16Args p) 
     }
     wait_vmcnt<0>();   // no fill may still be landing in LDS when the workgroup ends
 
-    if constexpr (OUT16)
+    if constexpr (OUT16) {
         store_tile_m16<GFM, GFN, MASKED, true>(acc, p.C16, p.ldc, m0 + wr * S::TM,
                                                n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta, lane);
-    else
+    } else if (!MASKED && p.ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0) {
+        // every wave is past its last fragment read once all have arrived here
+        __syncthreads();
+        store_tile_m16_staged<GFM, GFN, S::TN>(
+            acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.alpha, p.beta, lane,
+            ring + wave * StagedRows<S::TN>::BYTES);
+    } else {
         store_tile_m16<GFM, GFN, MASKED, false>(acc, p.C, p.ldc, m0 + wr * S::TM,
                                                 n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta, lane);
+    }
 }
 
 // One configuration, both masking variants, f32 (OUT16 false) or binary16 C.
