@@ -473,30 +473,57 @@ struct StagedRows {
     static constexpr int BYTES = 16 * RS * 4;
 };
 
-// Epilogue through shared memory for f32 C with 16-byte aligned rows and a
-// whole tile: one 16-row band of the wave's tile at a time is written to the
-// wave's own shared memory in the matrix-instruction layout and read back as
-// float4 along rows, so C is read (beta != 0) and written in whole 128-byte
-// row segments instead of the 64-byte ones of the block layout.  The same
-// value as store_tile: fma(alpha, acc, beta*c).  A wave's shared-memory
-// instructions complete in order, so no wait separates the write of a band,
-// its read-back and the next band's write.
-template <int FM, int FN, int TN>
+// Epilogue through shared memory for a whole tile whose C rows allow
+// vector accesses (f32: 16-byte aligned rows; binary16: 8-byte aligned): one
+// 16-row band of the wave's tile at a time is written to the wave's own
+// shared memory in the matrix-instruction layout and read back as four
+// consecutive columns per lane, so C is read (beta != 0) and written in whole
+// 128-byte row segments instead of the 64-byte (f32) or 32-byte (binary16)
+// ones of the block layout.  The same value as store_tile / store_tile16:
+// fma(alpha, acc, beta*c), binary16 C widened exactly and the result rounded
+// once to nearest even.  A wave's shared-memory instructions complete in
+// order, so no wait separates the write of a band, its read-back and the next
+// band's write.
+template <int FM, int FN, int TN, bool OUT16, typename CT>
 __device__ __forceinline__ void store_tile_m16_staged(const f32x4 (&acc)[FM][FN],
-                                                      float* __restrict__ C, int64_t ldc,
+                                                      CT* __restrict__ C, int64_t ldc,
                                                       int row0, int col0, float alpha, float beta,
                                                       int lane, unsigned char* stage) {
     using R = StagedRows<TN>;
     static_assert(FN * 16 == TN, "a band is the wave tile's width");
-    constexpr int LPR = TN / 4;        // lanes per staged row (one float4 each)
+    constexpr int LPR = TN / 4;        // lanes per staged row (four columns each)
     constexpr int RPI = 64 / LPR;      // rows per read-back instruction
     constexpr int IT = 16 / RPI;
     typedef __attribute__((address_space(3))) float lds_f32;
     typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
     lds_f32* st = (lds_f32*)(stage);
     const int q = lane >> 4, r16 = lane & 15;
     const int rr0 = lane / LPR, c4 = lane % LPR;
-    auto c_at = [&](int i, int it) { return C + (int64_t)(row0 + 16 * i + it * RPI + rr0) * ldc + col0 + 4 * c4; };
+    auto c_at = [&](int i, int it) {
+        return C + (int64_t)(row0 + 16 * i + it * RPI + rr0) * ldc + col0 + 4 * c4;
+    };
+    auto load4 = [&](int i, int it) -> f32x4 {
+        if constexpr (OUT16) {
+            const u16x4 h = *reinterpret_cast<const u16x4*>(c_at(i, it));
+            f32x4 v;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) v[x] = static_cast<float>(__builtin_bit_cast(_Float16, h[x]));
+            return v;
+        } else {
+            return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(c_at(i, it)));
+        }
+    };
+    auto store4 = [&](int i, int it, f32x4 v) {
+        if constexpr (OUT16) {
+            u16x4 h;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) h[x] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[x]));
+            *reinterpret_cast<u16x4*>(c_at(i, it)) = h;
+        } else {
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(c_at(i, it)));
+        }
+    };
     auto stage_band = [&](int i) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
@@ -511,8 +538,7 @@ __device__ __forceinline__ void store_tile_m16_staged(const f32x4 (&acc)[FM][FN]
         for (int i = 0; i < FM; ++i) {
             stage_band(i);
 #pragma unroll
-            for (int it = 0; it < IT; ++it)
-                __builtin_nontemporal_store(alpha * staged(it), reinterpret_cast<f32x4*>(c_at(i, it)));
+            for (int it = 0; it < IT; ++it) store4(i, it, alpha * staged(it));
         }
         return;
     }
@@ -520,8 +546,7 @@ __device__ __forceinline__ void store_tile_m16_staged(const f32x4 (&acc)[FM][FN]
     f32x4 old[2][IT];
     auto load_band = [&](int i, f32x4(&d)[IT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int it = 0; it < IT; ++it)
-            d[it] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(c_at(i, it)));
+        for (int it = 0; it < IT; ++it) d[it] = load4(i, it);
     };
     load_band(0, old[0]);
 #pragma unroll
@@ -534,7 +559,7 @@ __device__ __forceinline__ void store_tile_m16_staged(const f32x4 (&acc)[FM][FN]
             f32x4 out;
 #pragma unroll
             for (int x = 0; x < 4; ++x) out[x] = __builtin_fmaf(alpha, v[x], beta * old[i & 1][it][x]);
-            __builtin_nontemporal_store(out, reinterpret_cast<f32x4*>(c_at(i, it)));
+            store4(i, it, out);
         }
     }
 }
@@ -680,15 +705,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_ring_kernel(F16Args p) 
     }
     wait_vmcnt<0>();   // no fill may still be landing in LDS when the workgroup ends
 
-    if constexpr (OUT16) {
-        store_tile_m16<GFM, GFN, MASKED, true>(acc, p.C16, p.ldc, m0 + wr * S::TM,
-                                               n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta, lane);
-    } else if (!MASKED && p.ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0) {
+    // vector rows of C: f32 16-byte aligned, binary16 8-byte aligned
+    const uintptr_t c_addr = OUT16 ? reinterpret_cast<uintptr_t>(p.C16) : reinterpret_cast<uintptr_t>(p.C);
+    const bool staged = !MASKED && p.ldc % 4 == 0 && (c_addr & (OUT16 ? 7 : 15)) == 0;
+    if (staged) {
         // every wave is past its last fragment read once all have arrived here
         __syncthreads();
-        store_tile_m16_staged<GFM, GFN, S::TN>(
-            acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.alpha, p.beta, lane,
-            ring + wave * StagedRows<S::TN>::BYTES);
+        unsigned char* mine = ring + wave * StagedRows<S::TN>::BYTES;
+        if constexpr (OUT16)
+            store_tile_m16_staged<GFM, GFN, S::TN, true>(acc, p.C16, p.ldc, m0 + wr * S::TM,
+                                                         n0 + wc * S::TN, p.alpha, p.beta, lane, mine);
+        else
+            store_tile_m16_staged<GFM, GFN, S::TN, false>(acc, p.C, p.ldc, m0 + wr * S::TM,
+                                                          n0 + wc * S::TN, p.alpha, p.beta, lane, mine);
+    } else if constexpr (OUT16) {
+        store_tile_m16<GFM, GFN, MASKED, true>(acc, p.C16, p.ldc, m0 + wr * S::TM,
+                                               n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta, lane);
     } else {
         store_tile_m16<GFM, GFN, MASKED, false>(acc, p.C, p.ldc, m0 + wr * S::TM,
                                                 n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta, lane);

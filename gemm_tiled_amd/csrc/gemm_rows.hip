@@ -56,15 +56,6 @@ __device__ __forceinline__ float rn16(float x) {
     return static_cast<float>(static_cast<_Float16>(x));
 }
 
-// One 64-deep chunk of a wave: B as float4 per (step, t), A per (step, mb, t).
-// Every load has an in-range address: rows of A past M and columns of B past
-// N are clamped to the last ones, which only feeds rows and columns of the
-// accumulators that are never stored.  Rows of k past the wave's range must
-// contribute zero: with KTAIL (K not a multiple of the chunk) their A values
-// are replaced by zero; otherwise every chunk that is multiplied is whole.
-// Nothing else touches the loaded values before the matrix instructions, so
-// all loads of a chunk stay in flight together while the other chunk is
-// multiplied.
 // How a chunk reads A: row-major four k at a time (lda % 4 == 0, A aligned,
 // K % 4 == 0), row-major one value at a time, or stored K x M.
 enum AMode { kAVec = 0, kARow = 1, kACol = 2 };
@@ -86,12 +77,18 @@ constexpr int kRsrcFlags = 0x00020000;
 // offset.  Nothing touches the loaded values before the matrix instructions,
 // so a chunk's loads stay in flight together while the other chunk is
 // multiplied.
-template <int MB, int AM, bool TB, bool KTAIL>
+//
+// VR = 0: the matrix-instruction form above (lane row c of each 16-row block).
+// VR > 0 (at most VR rows, one group; VR = 1 or 2): every lane holds A rows
+// 0 .. VR-1 at its own k and multiplies with vector FMAs; 16-row matrix
+// instructions would waste 15/16 of their work on a single row.
+template <int MB, int AM, bool TB, bool KTAIL, int VR>
 struct Chunk {
+    static constexpr int NA = VR > 0 ? VR : MB;   // A registers per step
     // B: without TB bv[s][t] holds row kk + t, columns col .. col + 3; with
     // TB bv[s][j] holds column col + j, rows kk .. kk + 3 (as stored).
     f32x4 bv[4][4];
-    f32x4 av[4][MB];   // rows of A, k = kk .. kk + 3
+    f32x4 av[4][NA];   // rows of A, k = kk .. kk + 3
 
     __device__ __forceinline__ void load(const RowsArgs& p, __amdgpu_buffer_rsrc_t ra,
                                          __amdgpu_buffer_rsrc_t rb, int k, int col, int m0, int q,
@@ -130,8 +127,8 @@ struct Chunk {
             }
         }
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int rc = min(m0 + 16 * mb + c, p.M - 1);
+        for (int mb = 0; mb < NA; ++mb) {
+            const int rc = min(VR > 0 ? mb : m0 + 16 * mb + c, p.M - 1);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int kk = kq + 16 * s;
@@ -157,6 +154,28 @@ struct Chunk {
         }
     }
 
+    // vector form: accv[r] += A[r][k] * B[k][col .. col + 3] over the lane's k
+    template <bool R16>
+    __device__ __forceinline__ void multiply_rows(f32x4 (&accv)[NA]) const {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                f32x4 b;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float x = TB ? bv[s][j][t] : bv[s][t][j];
+                    b[j] = R16 ? rn16(x) : x;
+                }
+#pragma unroll
+                for (int r = 0; r < NA; ++r) {
+                    const float a = R16 ? rn16(av[s][r][t]) : av[s][r][t];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) accv[r][j] = __builtin_fmaf(a, b[j], accv[r][j]);
+                }
+            }
+    }
+
     template <bool R16>
     __device__ __forceinline__ void multiply(f32x4 (&acc)[MB][4]) const {
 #pragma unroll
@@ -180,9 +199,13 @@ struct Chunk {
     }
 };
 
-template <int MB, int AM, bool TB, bool R16, bool KTAIL>
+template <int MB, int AM, bool TB, bool R16, bool KTAIL, int VR>
 __global__ __launch_bounds__(kWaves * 64) void gemm_rows_kernel(RowsArgs p) {
-    __shared__ f32x4 red[kWaves][16 * MB][kCols / 4];
+    static_assert(VR == 0 || MB == 1, "the vector form covers one row group");
+    // per-wave sums: [wave][row][column quad]; the vector form has one more
+    // level, the lane quarter, whose k subsets are added too
+    constexpr int RED_ROWS = VR > 0 ? 4 * VR : 16 * MB;
+    __shared__ f32x4 red[kWaves][RED_ROWS][kCols / 4];
     __shared__ unsigned last;
 
     const int lane = threadIdx.x & 63;
@@ -201,6 +224,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_rows_kernel(RowsArgs p) {
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 accv[VR > 0 ? VR : 1];
+#pragma unroll
+    for (int r = 0; r < (VR > 0 ? VR : 1); ++r) accv[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Buffer descriptors over A and B (their byte extents fit 32-bit offsets).
     const int64_t a_bytes = AM == kACol ? ((int64_t)(p.K - 1) * p.lda + p.M) * 4
@@ -217,34 +243,56 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_rows_kernel(RowsArgs p) {
     // wave's range is usually exactly one pass (128 k): straight-line code,
     // every load in flight at once.  The scheduling barriers keep the
     // compiler from sinking each load next to its use.
-    Chunk<MB, AM, TB, KTAIL> x, y;
+    Chunk<MB, AM, TB, KTAIL, VR> x, y;
     for (int k = k_lo; k < k_hi; k += 2 * kChunk) {
         __builtin_amdgcn_sched_barrier(0);
         x.load(p, ra, rb, k, col, m0, q, c);
         y.load(p, ra, rb, k + kChunk, col, m0, q, c);
         __builtin_amdgcn_sched_barrier(0);
-        x.template multiply<R16>(acc);
-        if (k + kChunk < k_hi) y.template multiply<R16>(acc);
+        if constexpr (VR > 0) {
+            x.template multiply_rows<R16>(accv);
+            if (k + kChunk < k_hi) y.template multiply_rows<R16>(accv);
+        } else {
+            x.template multiply<R16>(acc);
+            if (k + kChunk < k_hi) y.template multiply<R16>(acc);
+        }
     }
 
-    // the four waves' sums, added in wave order
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            red[wave][16 * mb + 4 * q + e][c] =
-                f32x4{acc[mb][0][e], acc[mb][1][e], acc[mb][2][e], acc[mb][3][e]};
-    __syncthreads();
+    // the four waves' sums (and, in the vector form, the four lane quarters'),
+    // added in a fixed order
     const int t = threadIdx.x;
     const int c4 = t % (kCols / 4);
     const int cc = n0 + 4 * c4;
     f32x4 sum[MB];
+    if constexpr (VR > 0) {
 #pragma unroll
-    for (int r = 0; r < MB; ++r) {
-        const int rr = t / (kCols / 4) + 16 * r;   // row within the group
-        sum[r] = red[0][rr][c4];
+        for (int r = 0; r < VR; ++r) red[wave][4 * r + q][c] = accv[r];
+        __syncthreads();
+        const int rr = t / (kCols / 4);            // row (threads of rows >= VR idle)
+        sum[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (rr < VR) {
+            sum[0] = red[0][4 * rr][c4];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) sum[r] += red[w][rr][c4];
+            for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq)
+                    if (w || qq) sum[0] += red[w][4 * rr + qq][c4];
+        }
+    } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                red[wave][16 * mb + 4 * q + e][c] =
+                    f32x4{acc[mb][0][e], acc[mb][1][e], acc[mb][2][e], acc[mb][3][e]};
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < MB; ++r) {
+            const int rr = t / (kCols / 4) + 16 * r;   // row within the group
+            sum[r] = red[0][rr][c4];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) sum[r] += red[w][rr][c4];
+        }
     }
 
     if (p.slices > 1) {
@@ -315,10 +363,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_rows_kernel(RowsArgs p) {
     }
 }
 
-template <int MB, bool KTAIL>
+template <int MB, bool KTAIL, int VR = 0>
 hipError_t launch_mb(const RowsArgs& a, int am, bool tb, bool r16, dim3 grid, hipStream_t s) {
     const dim3 block(kWaves * 64);
-#define G355_ROWS_LAUNCH(AM, TB, R16) gemm_rows_kernel<MB, AM, TB, R16, KTAIL><<<grid, block, 0, s>>>(a)
+#define G355_ROWS_LAUNCH(AM, TB, R16) gemm_rows_kernel<MB, AM, TB, R16, KTAIL, VR><<<grid, block, 0, s>>>(a)
 #define G355_ROWS_AM(TB, R16)                                \
     do {                                                     \
         if (am == kAVec) G355_ROWS_LAUNCH(kAVec, TB, R16);   \
@@ -377,6 +425,9 @@ hipError_t launch_f32_rows(const float* A, int64_t lda, bool ta, const float* B,
     const bool tail = K % kChunk != 0;
     const bool a_vec = !ta && lda % 4 == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0 && K % 4 == 0;
     const int am = ta ? kACol : a_vec ? kAVec : kARow;
+    // one or two rows (and K a whole number of chunks): the vector form
+    if (M == 1 && !tail) return launch_mb<1, false, 1>(a, am, tb, r16, grid, s);
+    if (M == 2 && !tail) return launch_mb<1, false, 2>(a, am, tb, r16, grid, s);
     if (group == 16) return tail ? launch_mb<1, true>(a, am, tb, r16, grid, s)
                                  : launch_mb<1, false>(a, am, tb, r16, grid, s);
     if (group == 32) return tail ? launch_mb<2, true>(a, am, tb, r16, grid, s)

@@ -168,7 +168,7 @@ def test_rows_against_the_oracle(mode, M, N, K, lds):
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("M", [1, 9, 32, 48])
+@pytest.mark.parametrize("M", [1, 2, 9, 32, 48])
 def test_rows_small_integers_exact_and_beta_zero(mode, M):
     N, K = 2048, 4096
     A, B, C = small_integers(M, N, K, seed=16)
@@ -196,6 +196,24 @@ def test_rows_layouts(mode, ta, tb, N):
         g.gemm(mode, tA, tB, tC, 0.5, 2.0, transa=ta, transb=tb)
         torch.cuda.synchronize()
     assert_parity(mode, A, B, C, 0.5, 2.0, tC.cpu().numpy())
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("ta,tb,N", [(False, False, 1028), (True, False, 1028), (False, True, 1027),
+                                     (True, True, 1027)])
+def test_rows_vector_form(mode, M, ta, tb, N):
+    """One or two rows with K a multiple of 64 take the vector-FMA form."""
+    K = 2048
+    A, B, C = make_inputs(M, N, K, "normal", seed=19)
+    tA = to_device(np.ascontiguousarray(A.T) if ta else A)
+    tB = to_device(np.ascontiguousarray(B.T) if tb else B)
+    tC = to_device(C)
+    with pinned(mode, ROWS):
+        say(f"[rows vector] {mode} M={M} ta={ta} tb={tb} {M}x{N}x{K}")
+        g.gemm(mode, tA, tB, tC, -0.75, 0.5, transa=ta, transb=tb)
+        torch.cuda.synchronize()
+    assert_parity(mode, A, B, C, -0.75, 0.5, tC.cpu().numpy())
 
 
 def test_rows_f16_output():
