@@ -22,8 +22,8 @@ __global__ __launch_bounds__(256) void scale_c_kernel(float* __restrict__ C, int
 __device__ __forceinline__ float h2f(uint16_t b) {
     return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
-__device__ __forceinline__ uint16_t f2h(float x) {   // round to nearest even
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+__device__ __forceinline__ uint16_t f2h(float x) {   // round to nearest even, once
+    return f32_to_f16_bits(x);
 }
 
 // C = beta*C on binary16 storage (the f16-output variant's beta-only path).

@@ -426,7 +426,7 @@ __device__ __forceinline__ void store_tile_m16(const f32x4 (&acc)[FM][FN], CT* _
     };
     auto st = [&](int row, int col, float v) {
         if constexpr (OUT16)
-            C[(int64_t)row * ldc + col] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+            C[(int64_t)row * ldc + col] = f32_to_f16_bits(v);
         else
             __builtin_nontemporal_store(v, C + (int64_t)row * ldc + col);
     };
@@ -496,30 +496,31 @@ __device__ __forceinline__ void store_tile_m16_staged(const f32x4 (&acc)[FM][FN]
     constexpr int IT = 16 / RPI;
     typedef __attribute__((address_space(3))) float lds_f32;
     typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-    typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     lds_f32* st = (lds_f32*)(stage);
     const int q = lane >> 4, r16 = lane & 15;
     const int rr0 = lane / LPR, c4 = lane % LPR;
     auto c_at = [&](int i, int it) {
         return C + (int64_t)(row0 + 16 * i + it * RPI + rr0) * ldc + col0 + 4 * c4;
     };
+    // binary16 C: four values as two 32-bit words (low half first)
+    auto h2f = [](uint32_t bits) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+    };
     auto load4 = [&](int i, int it) -> f32x4 {
         if constexpr (OUT16) {
-            const u16x4 h = *reinterpret_cast<const u16x4*>(c_at(i, it));
-            f32x4 v;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) v[x] = static_cast<float>(__builtin_bit_cast(_Float16, h[x]));
-            return v;
+            const u32x2 w = *reinterpret_cast<const u32x2*>(c_at(i, it));
+            return f32x4{h2f(w[0] & 0xffffu), h2f(w[0] >> 16), h2f(w[1] & 0xffffu), h2f(w[1] >> 16)};
         } else {
             return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(c_at(i, it)));
         }
     };
     auto store4 = [&](int i, int it, f32x4 v) {
         if constexpr (OUT16) {
-            u16x4 h;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) h[x] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[x]));
-            *reinterpret_cast<u16x4*>(c_at(i, it)) = h;
+            u32x2 w;
+            w[0] = uint32_t{f32_to_f16_bits(v[0])} | (uint32_t{f32_to_f16_bits(v[1])} << 16);
+            w[1] = uint32_t{f32_to_f16_bits(v[2])} | (uint32_t{f32_to_f16_bits(v[3])} << 16);
+            *reinterpret_cast<u32x2*>(c_at(i, it)) = w;
         } else {
             __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(c_at(i, it)));
         }

@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_rows_kernel(RowsArgs p) {
                                                 : static_cast<float>(__builtin_bit_cast(_Float16, p.C16[at]));
                 const float v = p.beta == 0.f ? p.alpha * sum[r][j]
                                               : __builtin_fmaf(p.alpha, sum[r][j], p.beta * old);
-                p.C16[at] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+                p.C16[at] = f32_to_f16_bits(v);
             } else {
                 p.C[at] = p.beta == 0.f ? p.alpha * sum[r][j]
                                         : __builtin_fmaf(p.alpha, sum[r][j], p.beta * p.C[at]);

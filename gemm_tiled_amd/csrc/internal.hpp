@@ -156,6 +156,17 @@ __device__ __forceinline__ void tile_of_block(int g, int G, int tiles_m, int til
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// An f32 result rounded to binary16 (nearest even) as a step of its own: the
+// empty asm makes the value opaque, so the compiler cannot fold the rounding
+// into the multiply-add that produced it (a mixed-precision FMA rounds the
+// exact result to binary16 once, which differs from rounding the f32 value
+// when that value is a binary16 tie).  Every binary16 result of the library
+// is the f32 result of the same call with f32 output, rounded once.
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    asm volatile("" : "+v"(x));
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
 // Epilogue shared by the GEMM kernels (phobos docs, "gemm, f32", section "The
 // epilogue": C = alpha*acc + beta*C over the tile, C read in place).  A wave
 // holds FM x FN accumulator blocks of 32x32; element e of lane l in a block
@@ -222,7 +233,7 @@ __device__ __forceinline__ void store_tile16(const f32x16 (&acc)[FM][FN], uint16
     auto row_of = [&](int i, int e) { return row0 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3); };
     auto col_of = [&](int j) { return col0 + j * 32 + r32; };
     auto inside = [&](int row, int col) { return !MASKED || (row < M && col < N); };
-    auto to16 = [](float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); };
+    auto to16 = [](float x) { return f32_to_f16_bits(x); };
     auto to32 = [](uint16_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); };
 #pragma unroll
     for (int b = 0; b < FM * FN; ++b) {

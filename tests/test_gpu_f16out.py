@@ -60,15 +60,18 @@ def test_f16out_is_the_rounded_f32_result(M, N, K):
         assert inside_bound(A, B, C16, alpha, beta, got16)
 
 
-def test_f16out_every_config():
-    M, N, K = 257, 129, 67
+@pytest.mark.parametrize("M,N,K", [(257, 129, 67),     # ragged: masked epilogues
+                                   (512, 512, 256)])   # whole tiles: the staged epilogue
+def test_f16out_every_config(M, N, K):
     A, B, C = make_inputs(M, N, K, "uniform", seed=32)
     C16 = C.astype(np.float16)
     for cfg in g.list_configs("f16r"):
         with pinned("f16r", cfg):
-            say(f"[f16-out] every config {cfg}")
+            say(f"[f16-out] every config {cfg} {M}x{N}x{K}")
             got16 = run16(A, B, C16, 1.5, 0.5)
+            got32 = run("f16r", A, B, C16.astype(np.float32), 1.5, 0.5)
         assert inside_bound(A, B, C16, 1.5, 0.5, got16), cfg
+        assert np.array_equal(got16.view(np.uint16), got32.astype(np.float16).view(np.uint16)), cfg
 
 
 def test_f16out_small_integers_exact():

@@ -53,6 +53,7 @@ def assert_sampled(mode, A, B, C, alpha, beta, got, n=4096, seed=1):
 def test_every_config_aligned_and_ragged(mode):
     shapes = [
         (512, 512, 256, {}),                                    # whole tiles
+        (512, 512, 256, {"ldc": 514}),                          # whole tiles, C rows 8-byte aligned
         (300, 200, 150, {}),                                    # ragged in M, N, K
         (257, 129, 67, {"lda": 68, "ldb": 132, "ldc": 131}),    # ragged, padded lds
         (129, 77, 45, {"lda": 47, "ldb": 79, "ldc": 77}),       # odd lds: 4-byte rows
