@@ -243,18 +243,30 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_rows_kernel(RowsArgs p) {
     // wave's range is usually exactly one pass (128 k): straight-line code,
     // every load in flight at once.  The scheduling barriers keep the
     // compiler from sinking each load next to its use.
-    Chunk<MB, AM, TB, KTAIL, VR> x, y;
-    for (int k = k_lo; k < k_hi; k += 2 * kChunk) {
-        __builtin_amdgcn_sched_barrier(0);
-        x.load(p, ra, rb, k, col, m0, q, c);
-        y.load(p, ra, rb, k + kChunk, col, m0, q, c);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (VR > 0) {
-            x.template multiply_rows<R16>(accv);
-            if (k + kChunk < k_hi) y.template multiply_rows<R16>(accv);
-        } else {
+    // With 32 or 64 rows (MB > 1) one chunk is in registers at a time, which
+    // keeps two waves per SIMD (the other wave's loads cover the wait).
+    if constexpr (MB > 1) {
+        Chunk<MB, AM, TB, KTAIL, VR> x;
+        for (int k = k_lo; k < k_hi; k += kChunk) {
+            __builtin_amdgcn_sched_barrier(0);
+            x.load(p, ra, rb, k, col, m0, q, c);
+            __builtin_amdgcn_sched_barrier(0);
             x.template multiply<R16>(acc);
-            if (k + kChunk < k_hi) y.template multiply<R16>(acc);
+        }
+    } else {
+        Chunk<MB, AM, TB, KTAIL, VR> x, y;
+        for (int k = k_lo; k < k_hi; k += 2 * kChunk) {
+            __builtin_amdgcn_sched_barrier(0);
+            x.load(p, ra, rb, k, col, m0, q, c);
+            y.load(p, ra, rb, k + kChunk, col, m0, q, c);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (VR > 0) {
+                x.template multiply_rows<R16>(accv);
+                if (k + kChunk < k_hi) y.template multiply_rows<R16>(accv);
+            } else {
+                x.template multiply<R16>(acc);
+                if (k + kChunk < k_hi) y.template multiply<R16>(acc);
+            }
         }
     }
 
