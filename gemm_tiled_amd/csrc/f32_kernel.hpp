@@ -23,6 +23,8 @@
 // instructions four k at a time (16-byte reads), the others one k at a time.
 #pragma once
 
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace g355 {
@@ -37,6 +39,16 @@ namespace g355 {
     X(128, 64, 16, 2, 2, 8)   \
     X(64, 64, 16, 2, 2, 8)    \
     X(64, 64, 32, 2, 2, 8)
+
+// The direct-to-LDS ring (gemm_f32_ring.hip): X(BM, BN, NS, WM, WN, GM),
+// BK = 16, NS stages; whole tiles of the plain layout only (other calls with
+// these tiles run the register-staged kernel).
+#define G355_F32_RING_CONFIGS(X) \
+    X(256, 256, 3, 2, 4, 8)      \
+    X(256, 256, 4, 2, 4, 8)      \
+    X(256, 256, 4, 4, 2, 8)      \
+    X(128, 256, 4, 2, 4, 8)      \
+    X(128, 256, 6, 2, 4, 8)
 
 template <int BM, int BN, int BK, int WM, int WN, bool TA, bool TB>
 struct F32Shape {
@@ -292,5 +304,9 @@ hipError_t launch_f32_layout(const F32Args& a, F32Variant v, hipStream_t s) {
 // The transposed layouts (defined in gemm_f32_t.hip).
 template <int BM, int BN, int BK, int WM, int WN, int GM>
 hipError_t launch_f32_transposed(const F32Args& a, F32Variant v, hipStream_t s);
+
+// The ring configurations (defined in gemm_f32_ring.hip).
+template <int BM, int BN, int NS, int WM, int WN, int GM>
+hipError_t launch_f32_ring(const F32Args& a, F32Variant v, hipStream_t s);
 
 }  // namespace g355

@@ -17,7 +17,14 @@ hipError_t launch_f32(const F32Args& a, F32Variant v, hipStream_t s) {
 #define G355_F32_INSTANCE(BM, BN, BK, WM, WN, GM) \
     {{GEMM355_MODE_F32, BM, BN, BK, 2, WM, WN, GM}, &launch_f32<BM, BN, BK, WM, WN, GM>},
 
-const F32Instance kF32Instances[] = {G355_F32_CONFIGS(G355_F32_INSTANCE)};
+#define G355_F32_RING_INSTANCE(BM, BN, NS, WM, WN, GM) \
+    {{GEMM355_MODE_F32, BM, BN, 16, NS, WM, WN, GM}, &launch_f32_ring<BM, BN, NS, WM, WN, GM>},
+
+// The rings come first: the heuristic takes the first of equally priced
+// tiles, and a ring configuration runs the register-staged kernel of its tile
+// wherever the ring does not apply.
+const F32Instance kF32Instances[] = {G355_F32_RING_CONFIGS(G355_F32_RING_INSTANCE)
+                                         G355_F32_CONFIGS(G355_F32_INSTANCE)};
 
 }  // namespace
 

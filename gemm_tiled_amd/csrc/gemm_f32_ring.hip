@@ -1,0 +1,218 @@
+// gemm_f32_ring.hip -- the f32 GEMM on a ring of direct-to-LDS panels, for
+// whole tiles of row-major A and B with 16-byte aligned rows.
+//
+// Same computation as gemm_f32_kernel (the phobos "gemm, f32" page: one output
+// tile per workgroup, a K loop over BK-deep panels staged in shared memory,
+// the alpha/beta epilogue over the tile), on v_mfma_f32_32x32x2_f32 at full
+// f32 precision.  What differs is how the panels reach shared memory: instead
+// of every thread loading its part of the next panel into registers and
+// storing it after the math of the current one (one panel ahead, a barrier
+// per panel with the copy in between), each wave issues global->LDS copies
+// (global_load_lds_dwordx4, 1 KB per instruction) into a ring of NS stages,
+// NS - 1 panels ahead, as in the f16 ring kernel.
+//
+// Panel layout (BK = 16 floats of k):
+//   A: BM rows of 64 bytes (four 16-byte chunks of 4 k); chunk c of row r sits
+//      at position c ^ ((r / 4) % 4), so the 16 lanes that read one chunk of 16
+//      consecutive rows hit 16 different bank groups.  A copy instruction
+//      fills 16 rows; lane l fetches the global chunk that belongs at its
+//      destination position.
+//   B: 16 k-rows of BN = 256 floats (one copy instruction each), rows
+//      1024 + 16 bytes apart: the two lane halves, which read rows 8 apart,
+//      then fall in opposite halves of the 64 banks.
+// Matrix instructions: lane (h, r32) feeds k = 8h + s in step s (s = 0..7) to
+// A (row r32 of its block) and B (column r32) alike, so every instruction
+// pairs matching k; its A values for steps 4q..4q+3 are one 16-byte read
+// (chunk 2h + q), its B values single reads of four k-rows.
+//
+// Each panel is two halves of four steps with the barrier between them, as in
+// the f16 ring: the first half multiplies fragments read before it while this
+// wave reads the second half's and issues its copies; the wave waits for its
+// copies of the next panel, passes the barrier, and the second half
+// multiplies while the next panel's first fragments are read.
+#include "f32_kernel.hpp"
+
+namespace g355 {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const f32x4 lds_f32x4c;
+typedef __attribute__((address_space(3))) const float lds_f32c;
+
+template <int BM, int BN, int NS, int WM, int WN>
+struct F32RingShape {
+    static constexpr int BK = 16;
+    static constexpr int NW = WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int A_BYTES = BM * BK * 4;      // rows of 64 bytes
+    static constexpr int B_ROW = BN * 4 + 16;        // bytes per padded k-row
+    static constexpr int STAGE = A_BYTES + BK * B_ROW;
+    static constexpr int A_INS = BM / 16 / NW;       // copies of 16 A rows per wave per panel
+    static constexpr int B_INS = BK / NW;            // copies of one B k-row per wave per panel
+    static constexpr int FILLS = A_INS + B_INS;
+    static_assert(BN == 256, "one k-row of B is one 1 KB copy");
+    static_assert(A_INS >= 1 && A_INS * 16 * NW == BM && B_INS >= 1 && B_INS * NW == BK,
+                  "copies split evenly over the waves");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(NS >= 3 && NS * STAGE <= 160 * 1024, "LDS budget of one CU");
+    static_assert((NS - 2) * FILLS < 64, "vmcnt range");
+};
+
+template <int BM, int BN, int NS, int WM, int WN, int GM>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) {
+    using S = F32RingShape<BM, BN, NS, WM, WN>;
+    constexpr int FM = S::FM, FN = S::FN;
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * S::STAGE];
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave / WN, wc = wave % WN;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int nk = p.K / S::BK;
+
+    // Copy sources.  A copy j of this wave fills panel rows 16 (wave + NW j)
+    // .. +15 (bytes (wave + NW j) KB of the stage); lane l takes row l / 4 of
+    // them and position l % 4, which holds global chunk (l % 4) ^ swz(row);
+    // rows start at multiples of 16, so swz(row) = (l / 16) % 4.  B copy j
+    // fills k-row wave + NW j, lane l its floats 4l .. 4l + 3.
+    const int arow = lane >> 2;
+    const int achunk = (lane & 3) ^ ((arow >> 2) & 3);
+    const float* a_src = p.A + (int64_t)(m0 + wave * 16 + arow) * p.lda + achunk * 4;
+    const float* b_src = p.B + (int64_t)wave * p.ldb + n0 + lane * 4;
+    const int64_t a_step = (int64_t)S::NW * 16 * p.lda;   // next copy of this wave
+    const int64_t b_step = (int64_t)S::NW * p.ldb;
+    const int64_t b_panel = (int64_t)S::BK * p.ldb;
+
+    auto stage_of = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+        return ring + i * S::STAGE;
+    };
+    auto fill = [&](unsigned char* stage, int kt) __attribute__((always_inline)) {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage));
+#pragma unroll
+        for (int j = 0; j < S::A_INS; ++j)
+            lds_copy16(a_src + j * a_step + kt * S::BK, base + (wave + S::NW * j) * 1024);
+#pragma unroll
+        for (int j = 0; j < S::B_INS; ++j)
+            lds_copy16(b_src + j * b_step + kt * b_panel,
+                       base + S::A_BYTES + (wave + S::NW * j) * S::B_ROW);
+    };
+
+    // Fragments of half q (steps 4q .. 4q + 3): A block i one 16-byte read at
+    // chunk 2h + q of its row; B block j four single reads at k-rows 8h + 4q + t.
+    const int sw = (r32 >> 2) & 3;
+    const int a_off = (wr * S::TM + r32) * 64;
+    const int b_off = S::A_BYTES + (8 * h) * S::B_ROW + (wc * S::TN + r32) * 4;
+    f32x4 fa[2][FM];
+    float fb[2][FN][4];
+    auto frags = [&](const unsigned char* stage, int q) __attribute__((always_inline)) {
+        const lds_u8* base = (const lds_u8*)(stage);
+        const int chunk = ((2 * h + q) ^ sw) << 4;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            fa[q][i] = *reinterpret_cast<lds_f32x4c*>(base + a_off + i * 32 * 64 + chunk);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                fb[q][j][t] = *reinterpret_cast<lds_f32c*>(base + b_off + (4 * q + t) * S::B_ROW +
+                                                           j * 32 * 4);
+    };
+
+    f32x16 acc[FM][FN];
+    auto mfmas = [&](int q, auto first) __attribute__((always_inline)) {
+        const f32x16 zero = {};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        fa[q][i][t], fb[q][j][t],
+                        (decltype(first)::value && t == 0) ? zero : acc[i][j], 0, 0, 0);
+    };
+    constexpr int NMF = 4 * FM * FN;      // matrix instructions per half
+    constexpr int NRD = FM + 4 * FN;      // fragment reads per half
+    auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < NMF; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (m < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+
+    // One panel in `cur`: copy panel kt_fill into `freed` (the previous
+    // panel's stage, which every wave finished reading before the last
+    // barrier); first half beside the reads of the second half's fragments;
+    // wait for this wave's copies of the next panel; barrier; second half
+    // beside the reads of the next panel's first fragments.  Copies past the
+    // last panel reload the last one into a stage nobody reads again, so the
+    // count of outstanding copies is the same every panel.
+    auto panel = [&](const unsigned char* cur, unsigned char* freed, const unsigned char* next,
+                     int kt_fill, auto first) __attribute__((always_inline)) {
+        fill(freed, kt_fill);
+        frags(cur, 1);
+        mfmas(0, first);
+        __builtin_amdgcn_sched_group_barrier(0x020, S::FILLS, 0);
+        interleave();
+        wait_vmcnt<(NS - 2) * S::FILLS>();
+        ring_barrier();
+        frags(next, 0);
+        mfmas(1, std::false_type{});
+        interleave();
+    };
+
+#pragma unroll
+    for (int i = 0; i + 1 < NS; ++i) fill(stage_of(i), min(i, nk - 1));
+    wait_vmcnt<(NS - 2) * S::FILLS>();
+    ring_barrier();
+    frags(stage_of(0), 0);
+
+    panel(stage_of(0), stage_of(NS - 1), stage_of(1), min(NS - 1, nk - 1), std::true_type{});
+#pragma unroll
+    for (int u = 1; u < NS; ++u)
+        if (u < nk)
+            panel(stage_of(u), stage_of(u - 1), stage_of((u + 1) % NS), min(u + NS - 1, nk - 1),
+                  std::false_type{});
+    for (int kt = NS; kt < nk; kt += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u)
+            if (u == 0 || kt + u < nk)
+                panel(stage_of(u), stage_of((u + NS - 1) % NS), stage_of((u + 1) % NS),
+                      min(kt + u + NS - 1, nk - 1), std::false_type{});
+    }
+    wait_vmcnt<0>();   // no copy may still be landing in LDS when the workgroup ends
+
+    store_tile<FM, FN, false>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N,
+                              p.alpha, p.beta, lane);
+}
+
+}  // namespace
+
+// The ring handles whole tiles of the plain layout with 16-byte aligned rows
+// and K a multiple of 16; anything else (ragged shapes, odd leading
+// dimensions, transposed operands, split-K slices) runs the register-staged
+// kernel with the same BM x BN tile (BK = 16, 2 x 2 waves).
+template <int BM, int BN, int NS, int WM, int WN, int GM>
+hipError_t launch_f32_ring(const F32Args& a, F32Variant v, hipStream_t s) {
+    const bool whole = !v.masked && v.vec && !v.ta && !v.tb && a.ksplit == 0 && !v.r16 &&
+                       a.M % BM == 0 && a.N % BN == 0 && a.K % 16 == 0 && a.K > 0;
+    if (!whole) {
+        if (v.ta || v.tb) return launch_f32_transposed<BM, BN, 16, 2, 2, GM>(a, v, s);
+        return launch_f32_layout<BM, BN, 16, 2, 2, GM, false, false>(a, v, s);
+    }
+    const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
+    gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM><<<grid, block, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+#define G355_F32_RING_INSTANTIATE(BM, BN, NS, WM, WN, GM) \
+    template hipError_t launch_f32_ring<BM, BN, NS, WM, WN, GM>(const F32Args&, F32Variant, hipStream_t);
+G355_F32_RING_CONFIGS(G355_F32_RING_INSTANTIATE)
+
+}  // namespace g355

@@ -156,6 +156,48 @@ __device__ __forceinline__ void tile_of_block(int g, int G, int tiles_m, int til
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// ----------------------------------------------------------------------------
+// Shared-memory rings filled by direct global->LDS copies (the f16 ring and
+// the f32 ring kernels).
+// ----------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt vmcnt(N) with N a compile-time constant (at most 63).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for the panel ring.  __syncthreads() carries a workgroup
+// fence, for which the compiler waits until every outstanding global->LDS fill
+// of the wave has landed; that would cap the ring at one panel in flight.  The
+// ring orders its fills itself (wait_vmcnt before this barrier), so a bare
+// s_barrier suffices; this wave's own LDS reads are drained first so no other
+// wave can refill a stage under them, and the asm is a compiler memory barrier.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One direct global->LDS copy of a wave: lane l copies the 16 bytes at `src`
+// (its own address) to LDS byte address lds_base + 16 l.  Written as assembly
+// so that the compiler does not track these copies: it cannot always tell
+// which stage a shared-memory read may alias and would then wait for every
+// copy in flight before the read, which serialises the ring.  The ring waits
+// for its copies itself (wait_vmcnt before each barrier).  M0 carries the
+// wave's LDS base (the compiler writes it before the statement); the copy
+// needs one wait state after a write of M0.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds_base) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_base)
+                 : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* generic_lds_ptr) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)(generic_lds_ptr)));
+}
+
+
 // An f32 result rounded to binary16 (nearest even) as a step of its own: the
 // empty asm makes the value opaque, so the compiler cannot fold the rounding
 // into the multiply-add that produced it (a mixed-precision FMA rounds the
