@@ -21,6 +21,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -309,7 +310,7 @@ def bench_workload(g, torch, dev, w, args, roofs, workload_inputs, sample_indice
     peak = PEAK_TFLOPS[w.mode]
     roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": None,
-            "kernel": "gemm_f32_kernel" if w.mode == "f32" else
+            "kernel": f32_kernel_name(tile) if w.mode == "f32" else
             "pack_kernel + gemm_f16_kernel (whole call)",
             "per_launch_flops": flops}
     res = {
@@ -737,12 +738,20 @@ def source_hash(mode):
     return h.hexdigest()[:16]
 
 
+def f32_kernel_name(tile):
+    """The f32 kernel a configuration string runs on whole tiles: the
+    direct-to-LDS ring for the configurations with three or more stages,
+    the register-staged kernel otherwise."""
+    m = re.search(r"ST=(\d+)", tile or "")
+    return "gemm_f32_ring_kernel" if m and int(m.group(1)) >= 3 else "gemm_f32_kernel"
+
+
 def committed_traffic(mode, workload, tile):
     """HBM bytes per launch from the committed counter summary of this
     workload and tile, if it was taken on the current kernel sources; else None."""
     import glob
     import re
-    for path in glob.glob(os.path.join(PROFILES, "*traffic*.md")):
+    for path in sorted(glob.glob(os.path.join(PROFILES, "**", "*traffic*.md"), recursive=True)):
         text = open(path).read()
         m = re.search(r"```json\n(.*?)\n```", text, re.S)
         if not m:
