@@ -703,8 +703,8 @@ def skinny_sweep(g, torch, dev, out, repeats):
 COPY_BYTES = 256 << 20          # one direction of the calibration copy
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
-    "f32": ["gemm_tiled_amd/csrc/gemm_f32.hip", "gemm_tiled_amd/csrc/f32_kernel.hpp",
-            "gemm_tiled_amd/csrc/internal.hpp"],
+    "f32": ["gemm_tiled_amd/csrc/gemm_f32.hip", "gemm_tiled_amd/csrc/gemm_f32_ring.hip",
+            "gemm_tiled_amd/csrc/f32_kernel.hpp", "gemm_tiled_amd/csrc/internal.hpp"],
     "f16r": ["gemm_tiled_amd/csrc/gemm_f16r.hip", "gemm_tiled_amd/csrc/f16_kernel.hpp",
              "gemm_tiled_amd/csrc/internal.hpp"],
 }
@@ -751,7 +751,7 @@ def committed_traffic(mode, workload, tile):
     workload and tile, if it was taken on the current kernel sources; else None."""
     import glob
     import re
-    for path in sorted(glob.glob(os.path.join(PROFILES, "**", "*traffic*.md"), recursive=True)):
+    for path in sorted(glob.glob(os.path.join(PROFILES, "traffic", "*.md"))):
         text = open(path).read()
         m = re.search(r"```json\n(.*?)\n```", text, re.S)
         if not m:
