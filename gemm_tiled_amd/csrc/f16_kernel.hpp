@@ -22,15 +22,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // of kPackRows, depth in blocks of D values (D = 64 or 32, the depth of the
 // panel the GEMM configuration multiplies from).  Block (xb, kb) starts at
 // element ((xb * nkb) + kb) * kPackRows * D.  Inside it, row r holds its D
-// values as D/8 chunks of 8, logical chunk c at position c ^ swz(r), where the
-// key runs through all D/8 chunk positions as r steps through the rows that
-// share one 256-byte window of shared-memory banks:
-//   D = 64 (128-byte rows, 2 per window): swz(r) = (r / 2) % 8
-//   D = 32 ( 64-byte rows, 4 per window): swz(r) = (r / 4) % 4
-// A 16-byte shared-memory read is served 16 lanes at a time from 64 four-byte
-// banks (256 bytes); the 16 lanes of a fragment read take 16 consecutive rows
-// at one logical chunk, and the swizzle puts them in 16 different 16-byte
-// slots.
+// values as D/8 chunks of 8, logical chunk c at position c ^ swz(r):
+//   D = 64 (128-byte rows): swz(r) = (r / 2) % 8
+//   D = 32 ( 64-byte rows): swz(r) = (r / 2) % 4
+// so that rows r and r + 2 never hold a logical chunk at the same position.
+// A fragment read has 16 lanes take 16 consecutive rows at one logical chunk
+// (ds_read_b128).  Measured on gfx950 (a probe timing 16-byte LDS reads of
+// fixed lane patterns): both keys read at the full 16-byte rate; 64-byte rows
+// keyed by (r / 4) % 4 -- distinct 16-byte slots within every 256 bytes, but
+// rows r and r + 2 alike -- take two passes per read, as do unswizzled rows.
 // ----------------------------------------------------------------------------
 constexpr int kPackRows = 256;
 constexpr int kPackK = 64;   // the padded depth is a multiple of this for every D
@@ -38,8 +38,7 @@ constexpr int kPackK = 64;   // the padded depth is a multiple of this for every
 template <int D>
 __device__ __forceinline__ int swz(int r) {
     static_assert(D == 32 || D == 64, "panel depth");
-    constexpr int cpr = D / 8;             // chunks per row
-    return (r / (16 / cpr)) % cpr;
+    return (r / 2) % (D / 8);
 }
 
 template <int D>
@@ -578,8 +577,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_ring_kernel(F16Args p) 
 
     // Fragment reads: lane (q, r16) reads row r16 of a 16-row block at logical
     // chunk q, the 8 k values [8q, 8q + 8) of the panel, to A and B alike.
-    // Blocks start at multiples of 16 rows, a whole swizzle period, so the key
-    // is swz(r16); the 16 lanes of a quarter hit 16 different 16-byte slots.
+    // Blocks start at multiples of 16 rows, whole swizzle periods, so the key
+    // is swz(r16).
     const int r16 = lane & 15, q = lane >> 4;
     const int chunk = (q ^ swz<D>(r16)) << 4;
     const int a_row0 = (wr * S::TM + r16) * S::ROW + chunk;
