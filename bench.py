@@ -603,7 +603,8 @@ def skinny_sweep(g, torch, dev, out, repeats):
         tA, tC = torch.from_numpy(A).to(dev), torch.from_numpy(C).to(dev)
         for mode in ("f32", "f16r"):
             ref, W = oracle.entries(mode, A, B, C, 1.0, 0.0, r, c)
-            for kind in ("tuned", "split-K", "rows", "no split-K"):
+            kinds = ("tuned", "split-K", "rows", "no split-K") + (("round on load",) if mode == "f16r" else ())
+            for kind in kinds:
                 cases.append((mode, M, kind, tA, tC, r, c, ref, W))
     calls, tiles = {}, {}
     for (mode, M, kind, tA, tC, r, c, ref, W) in cases:
@@ -624,10 +625,12 @@ def skinny_sweep(g, torch, dev, out, repeats):
                 finally:
                     g.set_config(mode, None)
         else:
-            # the library's best configuration without split-K (tuned over the rest)
+            # the library's best configuration without split-K (tuned over the
+            # rest), or the best of the f16r configurations that round the
+            # operands as they stage them (KS=3)
             best, best_t = None, 1e30
             for cfg in g.list_configs(mode):
-                if "KS=" in cfg:
+                if ("KS=3" not in cfg) if kind == "round on load" else ("KS=" in cfg):
                     continue
                 g.set_config(mode, cfg)
                 try:
@@ -686,7 +689,9 @@ def skinny_sweep(g, torch, dev, out, repeats):
              "configurations are candidates); `split-K` is the 32x128-tile split-K "
              "configuration (KS=1), `rows` the few-rows configuration (KS=2: B streamed into "
              "registers, 16x16x4 matrix instructions, k split within and across workgroups); "
-             "`no split-K` is the fastest configuration of neither kind.", "",
+             "`round on load` (f16r) the fastest of the configurations that round A and B to "
+             "binary16 as they stage them for the binary16 matrix instruction (KS=3, no packing "
+             "pass); `no split-K` is the fastest configuration of none of these kinds.", "",
              "| mode | M | choice | TFLOP/s | GB/s | FLOP/B | bound | of roof | tile |",
              "|---|---:|---|---:|---:|---:|---|---:|---|"]
     for r_ in sorted(rows, key=lambda r_: (r_["mode"], r_["M"], r_["kind"])):

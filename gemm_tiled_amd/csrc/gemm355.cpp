@@ -38,8 +38,10 @@ bool log_debug() {
 const char* mode_name(int mode) { return mode == GEMM355_MODE_F32 ? "f32" : "f16r"; }
 
 // Up to this many rows of C the heuristic picks the few-rows configuration,
-// and up to kSplitKRows the split-K configuration.
+// then, in the f16r mode up to kDirectRows, a configuration that rounds the
+// operands as it stages them, and up to kSplitKRows the split-K configuration.
 constexpr int64_t kRowsRows = 16;
+constexpr int64_t kDirectRows = 384;
 constexpr int64_t kSplitKRows = 64;
 // Compute units of the MI355X (gfx950).
 constexpr int64_t kCUs = 256;
@@ -48,6 +50,8 @@ constexpr int64_t kCUs = 256;
 constexpr int64_t kSplitKTarget = 3 * kCUs;
 constexpr int64_t kSplitKMinDepth = 128;
 constexpr int64_t kSplitKMaxBytes = int64_t{1} << 30;
+// Least k per slice of the KS=3 configurations.
+constexpr int64_t kDirectMinDepth = 512;
 // Most workgroups (of four waves) a few-rows launch splits K into.
 constexpr int64_t kRowsMaxWgs = 8 * kCUs;
 
@@ -63,6 +67,8 @@ std::vector<TileConfig> configs_of(int mode) {
     } else {
         const F16Instance* t = f16_instances(&n);
         for (int i = 0; i < n; ++i) out.push_back(t[i].cfg);
+        const DirectInstance* d = direct_instances(&n);
+        for (int i = 0; i < n; ++i) out.push_back(d[i].cfg);
     }
     out.push_back(splitk_config(mode));
     out.push_back(rows_config(mode));
@@ -208,6 +214,14 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K) {
     // a few rows of C (memory-bound, too few tiles): the few-rows
     // configuration up to one 16-row group, then the split-K tiles
     if (M <= kRowsRows) return rows_config(mode);
+    if (mode == GEMM355_MODE_F16R && M <= kDirectRows) {
+        // rounding on load: no packing pass, whose cost grows with N x K
+        const int bm = M <= 48 ? 32 : M <= 160 ? 64 : 128;
+        int n = 0;
+        const DirectInstance* d = direct_instances(&n);
+        for (int i = 0; i < n; ++i)
+            if (d[i].cfg.bm == bm && d[i].cfg.bn == (bm == 128 ? 128 : 64)) return d[i].cfg;
+    }
     if (M <= kSplitKRows) return splitk_config(mode);
     const std::vector<TileConfig> all = configs_of(mode);
     double best = 1e300;
@@ -453,11 +467,62 @@ int launch_rows(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
                                      counts, s));
 }
 
+// The configurations that round the operands as they stage them (KS=3):
+// slices of K so that the grid reaches one round of resident workgroups
+// (as many per CU as their shared memory allows), each slice at least
+// kDirectMinDepth deep (a multiple of 64), the partial tiles within
+// kSplitKMaxBytes.
+int launch_direct(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
+                  const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                  int64_t ldc, hipStream_t s, uint16_t* C16) {
+    int n = 0;
+    const DirectInstance* t = direct_instances(&n);
+    const DirectInstance* inst = nullptr;
+    for (int i = 0; i < n; ++i)
+        if (t[i].cfg == cfg) inst = &t[i];
+    if (!inst) return GEMM355_ERR_CONFIG;
+    const int64_t tiles_m = (M + cfg.bm - 1) / cfg.bm, tiles_n = (N + cfg.bn - 1) / cfg.bn;
+    const int64_t tiles = tiles_m * tiles_n;
+    // resident workgroups per CU: two stages of LDS each, at most four waves
+    // per SIMD
+    const int64_t lds_bytes = 2 * int64_t{cfg.bm + cfg.bn} * 128;
+    const int64_t per_cu = std::max<int64_t>(
+        1, std::min<int64_t>((160 * 1024) / lds_bytes, 4 * 4 / (cfg.wm * cfg.wn)));
+    const int64_t tile_bytes = int64_t{cfg.bm} * cfg.bn * 4;
+    int64_t slices = std::max<int64_t>(1, (kCUs * per_cu + tiles - 1) / tiles);
+    slices = std::min(slices, std::max<int64_t>(1, K / kDirectMinDepth));
+    slices = std::min(slices, std::max<int64_t>(1, kSplitKMaxBytes / (tiles * tile_bytes)));
+    const int64_t depth = round_up((K + slices - 1) / slices, 64);
+    slices = (K + depth - 1) / depth;
+    const bool ta = (trans & 1) != 0, tb = (trans & 2) != 0;
+    const bool masked = !vec_ok(A, lda) || !vec_ok(B, ldb) || (M % cfg.bm) || (N % cfg.bn) ||
+                        (K % 64);
+    if (log_debug())
+        std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=direct x%lld (k %lld)%s\n",
+                     layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
+                     (long long)K, format_config(cfg).c_str(), (long long)slices,
+                     (long long)depth, masked ? " masked" : "");
+    DirectArgs a{A, B, C, C16, nullptr, nullptr, lda, ldb, ldc, static_cast<int>(M),
+                 static_cast<int>(N), static_cast<int>(K), alpha, beta,
+                 static_cast<int>(tiles_m), static_cast<int>(tiles_n),
+                 static_cast<int>(depth), static_cast<int>(slices)};
+    if (slices > 1) {
+        void* ws = nullptr;
+        hipError_t e = workspace(s, static_cast<size_t>(slices * tiles * tile_bytes), &ws);
+        if (e == hipSuccess) e = counters(s, static_cast<size_t>(tiles), &a.counts);
+        if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
+        a.P = static_cast<float*>(ws);
+    }
+    return status_of(inst->launch(a, ta, tb, masked, s));
+}
+
 int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
                 int64_t ldc, hipStream_t s, uint16_t* C16) {
     if (cfg.ks == 2)
         return launch_rows(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
+    if (cfg.ks == 3)
+        return launch_direct(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
     if (cfg.ks)
         return launch_splitk(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
     const int tiles_m = static_cast<int>((M + cfg.bm - 1) / cfg.bm);

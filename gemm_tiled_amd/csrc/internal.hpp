@@ -16,7 +16,9 @@ namespace g355 {
 // rasterised tile order (L2 reuse).
 // KS = 1 names the split-K configuration for few rows of C (the f32 kernel
 // over slices of K, partial tiles summed by a second pass; in the f16r mode it
-// rounds the operands as it loads them, with no packing pass).
+// rounds the operands as it loads them, with no packing pass); KS = 2 the
+// few-rows configuration; KS = 3 the f16r configurations that round the
+// operands as they stage them for the binary16 matrix instruction.
 struct TileConfig {
     int mode;  // GEMM355_MODE_*
     int bm, bn, bk, st, wm, wn, gm;
@@ -127,6 +129,33 @@ hipError_t launch_f32_rows(const float* A, int64_t lda, bool ta, const float* B,
                            bool tb, bool r16, float* C, uint16_t* C16, int64_t ldc, int M, int N,
                            int K, float alpha, float beta, int depth, int slices, float* P,
                            unsigned* counts, hipStream_t s);
+
+// The configurations that round the operands to binary16 as they stage them
+// (KS=3, gemm_f16r_direct.hip): f16r only, no packing pass; K is split over
+// blockIdx.y in slices of `depth` (a multiple of 64) and, with slices > 1,
+// the workgroups of a tile store their accumulators in P (slices x tiles x
+// BM x BN floats, below 2^31 bytes) and the last one to arrive (counted in
+// counts[tile], zero before and after the launch) adds them in slice order
+// and writes C (f32) or C16 (binary16, when C16 is not null).
+struct DirectArgs {
+    const float* A;
+    const float* B;
+    float* C;
+    uint16_t* C16;
+    float* P;
+    unsigned* counts;
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+    float alpha, beta;
+    int tiles_m, tiles_n;
+    int depth, slices;
+};
+using DirectLaunch = hipError_t (*)(const DirectArgs&, bool ta, bool tb, bool masked, hipStream_t);
+struct DirectInstance {
+    TileConfig cfg;
+    DirectLaunch launch;
+};
+const DirectInstance* direct_instances(int* count);
 
 // Measurement kernels.
 hipError_t launch_roof_mfma(int mode, int64_t iters, int blocks, float* sink, double* flops,

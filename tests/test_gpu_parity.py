@@ -238,9 +238,15 @@ def test_splitk_is_the_default_for_few_rows():
     for mode in MODES:
         assert "KS=2" in g.get_config(mode, 1, 4096, 4096)
         assert "KS=2" in g.get_config(mode, 16, 4096, 4096)
-        assert g.get_config(mode, 17, 4096, 4096).startswith("BM=32 BN=128 BK=32")
-        assert "KS=1" in g.get_config(mode, 64, 4096, 4096)
         assert "KS=" not in g.get_config(mode, 4096, 4096, 4096)
+    assert g.get_config("f32", 17, 4096, 4096).startswith("BM=32 BN=128 BK=32")
+    assert "KS=1" in g.get_config("f32", 64, 4096, 4096)
+    # f16r: the configurations that round on load, up to 384 rows
+    assert g.get_config("f16r", 17, 4096, 4096).startswith("BM=32 BN=64 BK=64")
+    assert g.get_config("f16r", 64, 4096, 4096).startswith("BM=64 BN=64 BK=64")
+    assert g.get_config("f16r", 384, 4096, 4096).startswith("BM=128 BN=128 BK=64")
+    assert all("KS=3" in g.get_config("f16r", m, 4096, 4096) for m in (17, 64, 384))
+    assert "KS=" not in g.get_config("f16r", 385, 4096, 4096)
 
 
 # ---------------------------------------------------------------------------
