@@ -73,7 +73,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / WN, wc = wave % WN;
     const int h = lane >> 5, r32 = lane & 31;
-    const int nk = p.K / S::BK;
+    // this workgroup's slice of K (the whole of K without a split)
+    const int slice = blockIdx.y;
+    const int k_lo = p.ring_slices > 1 ? slice * p.ring_depth : 0;
+    const int k_hi = p.ring_slices > 1 ? min(p.K, k_lo + p.ring_depth) : p.K;
+    const int nk = (k_hi - k_lo) / S::BK;
 
     // Copy sources.  A copy j of this wave fills panel rows 16 (wave + NW j)
     // .. +15 (bytes (wave + NW j) KB of the stage); lane l takes row l / 4 of
@@ -82,8 +86,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) 
     // fills k-row wave + NW j, lane l its floats 4l .. 4l + 3.
     const int arow = lane >> 2;
     const int achunk = (lane & 3) ^ ((arow >> 2) & 3);
-    const float* a_src = p.A + (int64_t)(m0 + wave * 16 + arow) * p.lda + achunk * 4;
-    const float* b_src = p.B + (int64_t)wave * p.ldb + n0 + lane * 4;
+    const float* a_src = p.A + (int64_t)(m0 + wave * 16 + arow) * p.lda + k_lo + achunk * 4;
+    const float* b_src = p.B + (int64_t)(k_lo + wave) * p.ldb + n0 + lane * 4;
     const int64_t a_step = (int64_t)S::NW * 16 * p.lda;   // next copy of this wave
     const int64_t b_step = (int64_t)S::NW * p.ldb;
     const int64_t b_panel = (int64_t)S::BK * p.ldb;
@@ -188,6 +192,71 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) 
     }
     wait_vmcnt<0>();   // no copy may still be landing in LDS when the workgroup ends
 
+    if (p.ring_slices > 1) {
+        // Split K: store this slice's accumulators in register order (16
+        // floats per block and lane, four 16-byte device-scope stores, each
+        // instruction of a wave one contiguous kilobyte), wait for them, pass
+        // a barrier and count in; the last workgroup of the tile reads every
+        // slice back and adds them in slice order, so the sum does not depend
+        // on which workgroup arrives last.
+        constexpr int kSC1 = 1 << 4;          // cache-policy bit of the buffer intrinsics
+        constexpr int kRsrc = 0x00020000;     // raw buffer, 32-bit data format
+        constexpr int NB = FM * FN;
+        constexpr int TILE_BYTES = BM * BN * 4;
+        const int tiles = gridDim.x;
+        const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+            p.P, (short)0, static_cast<int>((int64_t)p.ring_slices * tiles * TILE_BYTES), kRsrc);
+        auto at = [&](int z, int b, int q) {   // quarter q of block b of this lane, slice z
+            return static_cast<int>(((int64_t)z * tiles + blockIdx.x) * TILE_BYTES +
+                                    (((wave * NB + b) * 4 + q) * 64 + lane) * 16);
+        };
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v = {acc[b / FN][b % FN][4 * q], acc[b / FN][b % FN][4 * q + 1],
+                                 acc[b / FN][b % FN][4 * q + 2], acc[b / FN][b % FN][4 * q + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp,
+                                                       at(slice, b, q), 0, kSC1);
+            }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();   // every wave is past its last panel read and its stores are done
+        unsigned* count = p.counts + blockIdx.x;
+        int* flag = reinterpret_cast<int*>(ring);
+        if (threadIdx.x == 0)
+            *flag = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    static_cast<unsigned>(p.ring_slices - 1);
+        __syncthreads();
+        if (!*flag) return;
+        if (threadIdx.x == 0) __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // one block at a time, the loads of up to four slices in flight together
+        constexpr int ZG = 4;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            for (int z0 = 0; z0 < p.ring_slices; z0 += ZG) {
+                f32x4 t[ZG][4];
+#pragma unroll
+                for (int zz = 0; zz < ZG; ++zz) {
+                    const int z = min(z0 + zz, p.ring_slices - 1);   // past the last: unused reload
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        t[zz][q] = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, at(z, b, q), 0, kSC1));
+                }
+#pragma unroll
+                for (int zz = 0; zz < ZG; ++zz) {
+                    if (z0 + zz >= p.ring_slices) break;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const float a = acc[b / FN][b % FN][e];
+                        acc[b / FN][b % FN][e] =
+                            z0 + zz == 0 ? t[zz][e / 4][e % 4] : a + t[zz][e / 4][e % 4];
+                    }
+                }
+            }
+        }
+    }
     store_tile<FM, FN, false>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N,
                               p.alpha, p.beta, lane);
 }
@@ -198,15 +267,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) 
 // and K a multiple of 16; anything else (ragged shapes, odd leading
 // dimensions, transposed operands, split-K slices) runs the register-staged
 // kernel with the same BM x BN tile (BK = 16, 2 x 2 waves).
+namespace {
+bool ring_whole(int bm, int bn, const F32Args& a, const F32Variant& v) {
+    return !v.masked && v.vec && !v.ta && !v.tb && a.ksplit == 0 && !v.r16 && a.M % bm == 0 &&
+           a.N % bn == 0 && a.K % 16 == 0 && a.K > 0;
+}
+}  // namespace
+
+bool f32_ring_takes(const TileConfig& cfg, const F32Args& a, const F32Variant& v) {
+    return ring_whole(cfg.bm, cfg.bn, a, v);
+}
+
 template <int BM, int BN, int NS, int WM, int WN, int GM>
 hipError_t launch_f32_ring(const F32Args& a, F32Variant v, hipStream_t s) {
-    const bool whole = !v.masked && v.vec && !v.ta && !v.tb && a.ksplit == 0 && !v.r16 &&
-                       a.M % BM == 0 && a.N % BN == 0 && a.K % 16 == 0 && a.K > 0;
-    if (!whole) {
+    if (!ring_whole(BM, BN, a, v)) {
         if (v.ta || v.tb) return launch_f32_transposed<BM, BN, 16, 2, 2, GM>(a, v, s);
         return launch_f32_layout<BM, BN, 16, 2, 2, GM, false, false>(a, v, s);
     }
-    const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
+    if (a.ring_slices > 1 &&
+        (!a.P || !a.counts || a.ring_depth <= 0 || a.ring_depth % 16 != 0 ||
+         (int64_t)(a.ring_slices - 1) * a.ring_depth >= a.K || (int64_t)a.ring_slices * a.ring_depth < a.K))
+        return hipErrorInvalidValue;
+    const dim3 grid(a.tiles_m * a.tiles_n, a.ring_slices > 1 ? a.ring_slices : 1), block(WM * WN * 64);
     gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM><<<grid, block, 0, s>>>(a);
     return hipGetLastError();
 }

@@ -43,6 +43,15 @@ struct F32Args {
     float alpha, beta;
     int tiles_m, tiles_n;
     int ksplit = 0;   // k per slice (multiple of BK); 0 = no split
+    // The f32 ring only (gemm_f32_ring.hip): K split over blockIdx.y into
+    // ring_slices slices of ring_depth k (a multiple of 16).  With more than
+    // one slice the workgroups of a tile store their accumulators in P
+    // (ring_slices x tiles x BM x BN floats, below 2^31 bytes) and the last
+    // one to arrive (counted in counts[tile], zero before and after the
+    // launch) adds them in slice order and applies the epilogue.
+    int ring_slices = 1, ring_depth = 0;
+    float* P = nullptr;
+    unsigned* counts = nullptr;
 };
 
 // Arguments of one f16 GEMM launch on rounded, packed operands: A16 holds A
@@ -69,6 +78,12 @@ struct F32Variant {
     bool tb = false;   // op(B) = B^T: B is stored N x K
     bool r16 = false;  // round A and B to binary16 (RNE) on load: the f16r mode
 };
+
+// Whether a call with ring configuration cfg runs the f32 ring (whole tiles
+// of the plain layout, 16-byte aligned rows, K a multiple of 16, no split-K
+// slices of the F32Args::ksplit kind); otherwise the register-staged kernel
+// of the same tile runs it.
+bool f32_ring_takes(const TileConfig& cfg, const F32Args& a, const F32Variant& v);
 
 using F32Launch = hipError_t (*)(const F32Args&, F32Variant, hipStream_t);
 using F16Launch = hipError_t (*)(const F16Args&, hipStream_t);

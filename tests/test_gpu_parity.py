@@ -454,3 +454,63 @@ def test_tuner_leaves_c_alone_and_its_choice_is_correct(mode):
         assert_parity(mode, A, B, C, 1.0, 0.5, tC.cpu().numpy())
     finally:
         g.cache_clear()
+
+
+# ---------------------------------------------------------------------------
+# The f32 ring splits K over workgroups when its tiles leave CUs idle; the
+# last workgroup of a tile adds the slices in slice order.
+# ---------------------------------------------------------------------------
+RINGS = [c for c in g.list_configs("f32") if "BK=16" in c and int(c.split("ST=")[1].split()[0]) >= 3]
+
+
+@pytest.mark.parametrize("cfg", RINGS)
+@pytest.mark.parametrize("M,N,K", [(256, 4096, 4096), (512, 1024, 8192), (2048, 2048, 1024),
+                                   (256, 512, 1040)])
+def test_ring_split_against_the_oracle(cfg, M, N, K):
+    A, B, C = make_inputs(M, N, K, "normal", seed=31)
+    with pinned("f32", cfg):
+        say(f"[ring split] {cfg} {M}x{N}x{K}")
+        got = run("f32", A, B, C, 1.25, -0.5)
+        again = run("f32", A, B, C, 1.25, -0.5)
+    assert_parity("f32", A, B, C, 1.25, -0.5, got)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))   # fixed slice order
+
+
+@pytest.mark.parametrize("cfg", RINGS[:1] + RINGS[-1:])
+def test_ring_split_small_integers_exact_and_beta_zero(cfg):
+    M, N, K = 256, 2048, 4096
+    A, B, C = small_integers(M, N, K, seed=32)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned("f32", cfg):
+        say(f"[ring split exact] {cfg} {M}x{N}x{K}")
+        got = run("f32", A, B, C, -2.0, 0.5)
+        assert np.array_equal(got, (-2.0 * exact + 0.5 * C.astype(np.float64)).astype(np.float32))
+        Cn = np.full((M, N), np.nan, dtype=np.float32)
+        got = run("f32", A, B, Cn, 1.0, 0.0)
+        assert np.array_equal(got, exact.astype(np.float32))
+
+
+def test_ring_split_graph_capture_replays():
+    M, N, K = 256, 512, 4096
+    A, B, C = make_inputs(M, N, K, "uniform", seed=33)
+    tA, tB, tC = to_device(A), to_device(B), to_device(C)
+    C0 = tC.clone()
+    s = torch.cuda.Stream()
+    with pinned("f32", RINGS[0]):
+        say(f"[graph ring split] {RINGS[0]} {M}x{N}x{K}")
+        with torch.cuda.stream(s):
+            g.gemm("f32", tA, tB, tC, 1.25, 0.5)     # eager; creates the workspace and counters
+        s.synchronize()
+        eager = tC.clone()
+        graph = torch.cuda.CUDAGraph()
+        tC.copy_(C0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            g.gemm("f32", tA, tB, tC, 1.25, 0.5)
+        for _ in range(3):
+            tC.copy_(C0)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(tC, eager)
+    assert_parity("f32", A, B, C, 1.25, 0.5, tC.cpu().numpy())
