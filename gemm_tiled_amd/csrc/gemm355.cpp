@@ -71,6 +71,8 @@ std::vector<TileConfig> configs_of(int mode) {
         for (int i = 0; i < n; ++i) out.push_back(t[i].cfg);
         const DirectInstance* d = direct_instances(&n);
         for (int i = 0; i < n; ++i) out.push_back(d[i].cfg);
+        d = f16_from_f32_ring_instances(&n);
+        for (int i = 0; i < n; ++i) out.push_back(d[i].cfg);
     }
     out.push_back(splitk_config(mode));
     out.push_back(rows_config(mode));
@@ -496,33 +498,46 @@ int launch_rows(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
 // The configurations that round the operands as they stage them (KS=3):
 // slices of K so that the grid reaches one round of resident workgroups
 // (as many per CU as their shared memory allows), each slice at least
-// kDirectMinDepth deep (a multiple of 64), the partial tiles within
+// kDirectMinDepth deep (a multiple of the panel depth), the partial tiles within
 // kSplitKMaxBytes.
-int launch_direct(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
-                  const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
-                  int64_t ldc, hipStream_t s, uint16_t* C16) {
+int launch_direct(const TileConfig& cfg_in, int trans, int64_t M, int64_t N, int64_t K,
+                  float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                  float beta, float* C, int64_t ldc, hipStream_t s, uint16_t* C16) {
+    TileConfig cfg = cfg_in;
+    const bool ta = (trans & 1) != 0, tb = (trans & 2) != 0;
+    // the f32-panel ring (BK = 16) hands the shapes it does not take to the
+    // register-staged kernel of the 64 x 64 tile
+    if (cfg.bk == 16 && !f16_from_f32_ring_takes(ta, tb, A, lda, B, ldb, N, K)) {
+        TileConfig fb;
+        if (!parse_config(cfg.mode, "BM=64 BN=64 BK=64 KS=3", &fb)) return GEMM355_ERR_CONFIG;
+        cfg = fb;
+    }
     int n = 0;
-    const DirectInstance* t = direct_instances(&n);
     const DirectInstance* inst = nullptr;
+    const DirectInstance* t = direct_instances(&n);
+    for (int i = 0; i < n; ++i)
+        if (t[i].cfg == cfg) inst = &t[i];
+    t = f16_from_f32_ring_instances(&n);
     for (int i = 0; i < n; ++i)
         if (t[i].cfg == cfg) inst = &t[i];
     if (!inst) return GEMM355_ERR_CONFIG;
     const int64_t tiles_m = (M + cfg.bm - 1) / cfg.bm, tiles_n = (N + cfg.bn - 1) / cfg.bn;
     const int64_t tiles = tiles_m * tiles_n;
-    // resident workgroups per CU: two stages of LDS each, at most four waves
+    // resident workgroups per CU: the LDS of the stages, at most four waves
     // per SIMD
-    const int64_t lds_bytes = 2 * int64_t{cfg.bm + cfg.bn} * 128;
+    const int64_t lds_bytes = cfg.bk == 16
+                                  ? int64_t{cfg.st} * (cfg.bm * 64 + 16 * (cfg.bn * 4 + 16))
+                                  : 2 * int64_t{cfg.bm + cfg.bn} * 128;
     const int64_t per_cu = std::max<int64_t>(
         1, std::min<int64_t>((160 * 1024) / lds_bytes, 4 * 4 / (cfg.wm * cfg.wn)));
     const int64_t tile_bytes = int64_t{cfg.bm} * cfg.bn * 4;
     int64_t slices = std::max<int64_t>(1, (kCUs * per_cu + tiles - 1) / tiles);
     slices = std::min(slices, std::max<int64_t>(1, K / kDirectMinDepth));
     slices = std::min(slices, std::max<int64_t>(1, kSplitKMaxBytes / (tiles * tile_bytes)));
-    const int64_t depth = round_up((K + slices - 1) / slices, 64);
+    const int64_t depth = round_up((K + slices - 1) / slices, cfg.bk);
     slices = (K + depth - 1) / depth;
-    const bool ta = (trans & 1) != 0, tb = (trans & 2) != 0;
     const bool masked = !vec_ok(A, lda) || !vec_ok(B, ldb) || (M % cfg.bm) || (N % cfg.bn) ||
-                        (K % 64);
+                        (K % cfg.bk);
     if (log_debug())
         std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=direct x%lld (k %lld)%s\n",
                      layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,

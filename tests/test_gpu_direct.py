@@ -24,7 +24,11 @@ import gemm_tiled_amd as g  # noqa: E402
 from tests.gpu_helpers import pinned, run, say, to_device  # noqa: E402
 
 DIRECT = ["BM=64 BN=64 BK=64 KS=3", "BM=32 BN=64 BK=64 KS=3", "BM=128 BN=128 BK=64 KS=3",
-          "BM=64 BN=256 BK=64 KS=3"]
+          "BM=64 BN=256 BK=64 KS=3",
+          # f32 panels through a ring of direct-to-LDS copies, rounded as read
+          "BM=64 BN=256 BK=16 ST=3 KS=3", "BM=64 BN=256 BK=16 ST=6 KS=3",
+          "BM=32 BN=256 BK=16 ST=6 KS=3", "BM=128 BN=256 BK=16 ST=4 KS=3"]
+RINGS = [c for c in DIRECT if "BK=16" in c]
 
 
 def assert_parity(A, B, C, alpha, beta, got):
@@ -51,6 +55,26 @@ def test_direct_against_the_oracle(cfg, M, N, K, lds):
     assert np.array_equal(got.view(np.uint32), again.view(np.uint32))   # fixed slice order
 
 
+@pytest.mark.parametrize("cfg", RINGS)
+@pytest.mark.parametrize("M,N,K,lds", [
+    (17, 1000, 4096, {}),                           # ragged M and N (N % 4 == 0), many slices
+    (300, 520, 2096, {"lda": 2100, "ldb": 524, "ldc": 521}),   # padded 16-byte rows, odd ldc
+    (1000, 300, 784, {}),                           # many tile rows, one or two slices
+    (64, 4096, 4096, {}),                           # whole tiles
+    (33, 256, 16, {}),                              # one panel
+])
+def test_direct_ring_shapes(cfg, M, N, K, lds):
+    """The shapes the f32-panel ring takes itself (16-byte rows, N % 4 == 0,
+    K % 16 == 0), ragged in M and N."""
+    A, B, C = make_inputs(M, N, K, "normal", seed=25, **lds)
+    with pinned("f16r", cfg):
+        say(f"[direct ring] {cfg} {M}x{N}x{K} {lds}")
+        got = run("f16r", A, B, C, -0.75, 1.5)
+        again = run("f16r", A, B, C, -0.75, 1.5)
+    assert_parity(A, B, C, -0.75, 1.5, got)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+
+
 @pytest.mark.parametrize("cfg", DIRECT)
 @pytest.mark.parametrize("M", [1, 40, 200])
 def test_direct_small_integers_exact_and_beta_zero(cfg, M):
@@ -66,7 +90,7 @@ def test_direct_small_integers_exact_and_beta_zero(cfg, M):
         assert np.array_equal(got, exact.astype(np.float32))
 
 
-@pytest.mark.parametrize("cfg", DIRECT[:2])
+@pytest.mark.parametrize("cfg", DIRECT[:2] + RINGS[:1])
 @pytest.mark.parametrize("ta,tb,M,N", [(True, False, 96, 1028), (False, True, 96, 1027),
                                        (True, True, 70, 1027), (True, False, 33, 61),
                                        (False, True, 128, 512)])
