@@ -50,8 +50,10 @@ constexpr int64_t kCUs = 256;
 constexpr int64_t kSplitKTarget = 3 * kCUs;
 constexpr int64_t kSplitKMinDepth = 128;
 constexpr int64_t kSplitKMaxBytes = int64_t{1} << 30;
-// Least k per slice of a split f32 ring call.
-constexpr int64_t kRingMinDepth = 512;
+// Least run of a stream-K f32 ring call (16-deep panels), and the panels its
+// partial sums are counted as in the choice of the run.
+constexpr int64_t kRingMinPanels = 32;
+constexpr int64_t kRingSkOverhead = 12;
 // Least k per slice of the KS=3 configurations.
 constexpr int64_t kDirectMinDepth = 512;
 // Most workgroups (of four waves) a few-rows launch splits K into.
@@ -211,19 +213,25 @@ bool vec_ok(const float* p, int64_t ld) {
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // The f32 ring configurations (direct-to-LDS copies, BK = 16, three or more
-// stages) and the number of K slices a ring call takes: as many as still fit
-// one workgroup per CU when the tiles alone leave CUs idle (a second round
-// would gain nothing), each slice at least kRingMinDepth deep, the partial
-// tiles within kSplitKMaxBytes.
+// stages) and their stream-K run length: when whole rounds of tiles would
+// leave CUs idle, the (tile, 16-deep panel) units of the call are dealt to the
+// CUs in equal runs of at least kRingMinPanels units, if that beats the whole
+// rounds by 5% counting kRingSkOverhead panels for the split tiles' partial
+// sums; 0 = one tile per workgroup.
 bool is_f32_ring(const TileConfig& c) {
     return c.mode == GEMM355_MODE_F32 && c.bk == 16 && c.st >= 3 && c.ks == 0;
 }
 
-int64_t ring_slices(const TileConfig& c, int64_t M, int64_t N, int64_t K) {
+int64_t ring_sk_q(const TileConfig& c, int64_t M, int64_t N, int64_t K) {
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    int64_t slices = std::min<int64_t>(kCUs / tiles, K / kRingMinDepth);
-    slices = std::min(slices, kSplitKMaxBytes / (tiles * c.bm * c.bn * 4));
-    return std::max<int64_t>(1, slices);
+    const int64_t nkt = K / 16, units = tiles * nkt;
+    if (tiles % kCUs == 0 || units >= (int64_t{1} << 31)) return 0;
+    const int64_t q = std::max<int64_t>((units + kCUs - 1) / kCUs, kRingMinPanels);
+    const int64_t whole = (tiles + kCUs - 1) / kCUs * nkt;
+    if (static_cast<double>(q + kRingSkOverhead) >= 0.95 * static_cast<double>(whole)) return 0;
+    const int64_t grid = (units + q - 1) / q;
+    if (grid * 2 * c.bm * c.bn * 4 > kSplitKMaxBytes) return 0;
+    return q;
 }
 
 // Heuristic when nothing is pinned or tuned: estimate the time of each
@@ -250,19 +258,18 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K) {
         if (c.ks) continue;
         const double tiles = static_cast<double>((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
         const double per_cu = (c.bm * c.bn >= 256 * 128) ? 1.0 : 2.0;
-        // a ring call on whole tiles splits K over idle CUs (each slice's
-        // partial tile written, and read back by the tile's last workgroup);
-        // it also stages its panels about 10% faster than the register-staged
-        // kernel
+        // a ring call on whole tiles deals its work in equal runs when whole
+        // rounds would leave CUs idle (stream-K, runs counted in panels plus
+        // the partial sums' overhead); it also stages its panels faster than
+        // the register-staged kernel (10-20% measured, counted as 20%)
         const bool ring = is_f32_ring(c) && M % c.bm == 0 && N % c.bn == 0 && K % 16 == 0;
-        const double slices = ring ? static_cast<double>(ring_slices(c, M, N, K)) : 1.0;
-        const double rounds = std::ceil(tiles * slices / (256.0 * per_cu));
-        const double reuse = static_cast<double>(c.bm) * c.bn / (c.bm + c.bn);   // flop per loaded element
-        const double eff = reuse / (reuse + 6.5) * (ring ? 1.1 : 1.0);
+        const int64_t q = ring ? ring_sk_q(c, M, N, K) : 0;
         const double kpad = static_cast<double>(round_up(K, c.bk));
-        const double partials = slices > 1 ? 8.0 * slices : 0.0;
-        const double cost =
-            rounds * per_cu * c.bm * c.bn * (kpad / slices / eff + partials);
+        const double rounds = q > 0 ? static_cast<double>(q + kRingSkOverhead) / (K / 16)
+                                    : std::ceil(tiles / (256.0 * per_cu));
+        const double reuse = static_cast<double>(c.bm) * c.bn / (c.bm + c.bn);   // flop per loaded element
+        const double eff = reuse / (reuse + 6.5) * (ring ? 1.2 : 1.0);
+        const double cost = rounds * per_cu * c.bm * c.bn * kpad / eff;
         if (cost < best * 0.999) {
             best = cost;
             pick = c;
@@ -580,27 +587,25 @@ int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
             v.ta = (trans & 1) != 0;
             v.tb = (trans & 2) != 0;
             v.masked = !v.vec || (M % cfg.bm) || (N % cfg.bn) || (K % cfg.bk);
-            // a ring configuration splits K when its tiles leave CUs idle
-            const int64_t slices = is_f32_ring(cfg) && f32_ring_takes(cfg, a, v)
-                                       ? ring_slices(cfg, M, N, K) : 1;
-            if (slices > 1) {
-                const int64_t depth = round_up((K + slices - 1) / slices, 16);
+            // a ring configuration deals its work to the CUs in equal runs
+            // (stream-K) when whole rounds of tiles would leave CUs idle
+            const int64_t q = is_f32_ring(cfg) && f32_ring_takes(cfg, a, v) ? ring_sk_q(cfg, M, N, K) : 0;
+            if (q > 0) {
                 const int64_t tiles = int64_t{tiles_m} * tiles_n;
-                a.ring_slices = static_cast<int>((K + depth - 1) / depth);
-                a.ring_depth = static_cast<int>(depth);
+                const int64_t grid = (tiles * (K / 16) + q - 1) / q;
+                a.sk_q = static_cast<int>(q);
                 void* ws = nullptr;
-                hipError_t e = workspace(
-                    s, static_cast<size_t>(a.ring_slices * tiles * cfg.bm * cfg.bn) * 4, &ws);
+                hipError_t e = workspace(s, static_cast<size_t>(grid * 2 * cfg.bm * cfg.bn) * 4, &ws);
                 if (e == hipSuccess) e = counters(s, static_cast<size_t>(tiles), &a.counts);
                 if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
                 a.P = static_cast<float*>(ws);
             }
             if (log_debug())
-                std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=%s%s x%d\n",
+                std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=%s%s run %d\n",
                              layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
                              (long long)K, format_config(cfg).c_str(),
                              v.masked ? "masked" : "aligned", v.vec ? "" : " scalar-loads",
-                             a.ring_slices);
+                             a.sk_q);
             return status_of(t[i].launch(a, v, s));
         }
         return GEMM355_ERR_CONFIG;

@@ -59,206 +59,249 @@ struct F32RingShape {
     static_assert((NS - 2) * FILLS < 64, "vmcnt range");
 };
 
-template <int BM, int BN, int NS, int WM, int WN, int GM>
+template <int BM, int BN, int NS, int WM, int WN, int GM, bool SK>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) {
     using S = F32RingShape<BM, BN, NS, WM, WN>;
     constexpr int FM = S::FM, FN = S::FN;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * S::STAGE];
 
-    int tm, tn;
-    tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / WN, wc = wave % WN;
     const int h = lane >> 5, r32 = lane & 31;
-    // this workgroup's slice of K (the whole of K without a split)
-    const int slice = blockIdx.y;
-    const int k_lo = p.ring_slices > 1 ? slice * p.ring_depth : 0;
-    const int k_hi = p.ring_slices > 1 ? min(p.K, k_lo + p.ring_depth) : p.K;
-    const int nk = (k_hi - k_lo) / S::BK;
+    const int nkt = p.K / S::BK;   // panels of a whole tile
 
-    // Copy sources.  A copy j of this wave fills panel rows 16 (wave + NW j)
-    // .. +15 (bytes (wave + NW j) KB of the stage); lane l takes row l / 4 of
-    // them and position l % 4, which holds global chunk (l % 4) ^ swz(row);
-    // rows start at multiples of 16, so swz(row) = (l / 16) % 4.  B copy j
-    // fills k-row wave + NW j, lane l its floats 4l .. 4l + 3.
-    const int arow = lane >> 2;
-    const int achunk = (lane & 3) ^ ((arow >> 2) & 3);
-    const float* a_src = p.A + (int64_t)(m0 + wave * 16 + arow) * p.lda + k_lo + achunk * 4;
-    const float* b_src = p.B + (int64_t)(k_lo + wave) * p.ldb + n0 + lane * 4;
-    const int64_t a_step = (int64_t)S::NW * 16 * p.lda;   // next copy of this wave
-    const int64_t b_step = (int64_t)S::NW * p.ldb;
-    const int64_t b_panel = (int64_t)S::BK * p.ldb;
+    // Work of this workgroup: one whole tile, or (stream-K) the run of
+    // (tile, panel) units [u, u_end), workgroups numbered so that the runs
+    // of one XCD are consecutive.
+    constexpr bool sk = SK;   // the host sets p.sk_q > 0 exactly for SK launches
+    const int tiles = p.tiles_m * p.tiles_n;
+    int g = 0, u = 0, u_end = 0;
+    if constexpr (sk) {
+        const int G = gridDim.x, xcd = blockIdx.x & 7, q8 = G >> 3, r8 = G & 7;
+        g = xcd * q8 + (xcd < r8 ? xcd : r8) + (blockIdx.x >> 3);
+        u = g * p.sk_q;
+        u_end = min(tiles * nkt, u + p.sk_q);
+    }
 
     auto stage_of = [&](int i) __attribute__((always_inline)) -> unsigned char* {
         return ring + i * S::STAGE;
     };
-    auto fill = [&](unsigned char* stage, int kt) __attribute__((always_inline)) {
-        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage));
-#pragma unroll
-        for (int j = 0; j < S::A_INS; ++j)
-            lds_copy16(a_src + j * a_step + kt * S::BK, base + (wave + S::NW * j) * 1024);
-#pragma unroll
-        for (int j = 0; j < S::B_INS; ++j)
-            lds_copy16(b_src + j * b_step + kt * b_panel,
-                       base + S::A_BYTES + (wave + S::NW * j) * S::B_ROW);
-    };
-
-    // Fragments of half q (steps 4q .. 4q + 3): A block i one 16-byte read at
-    // chunk 2h + q of its row; B block j four single reads at k-rows 8h + 4q + t.
     const int sw = (r32 >> 2) & 3;
     const int a_off = (wr * S::TM + r32) * 64;
     const int b_off = S::A_BYTES + (8 * h) * S::B_ROW + (wc * S::TN + r32) * 4;
-    f32x4 fa[2][FM];
-    float fb[2][FN][4];
-    auto frags = [&](const unsigned char* stage, int q) __attribute__((always_inline)) {
-        const lds_u8* base = (const lds_u8*)(stage);
-        const int chunk = ((2 * h + q) ^ sw) << 4;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-            fa[q][i] = *reinterpret_cast<lds_f32x4c*>(base + a_off + i * 32 * 64 + chunk);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                fb[q][j][t] = *reinterpret_cast<lds_f32c*>(base + b_off + (4 * q + t) * S::B_ROW +
-                                                           j * 32 * 4);
-    };
+    const int arow = lane >> 2;
+    const int achunk = (lane & 3) ^ ((arow >> 2) & 3);
 
-    f32x16 acc[FM][FN];
-    auto mfmas = [&](int q, auto first) __attribute__((always_inline)) {
-        const f32x16 zero = {};
+    for (;;) {
+        int tm, tn, kp0, nk;
+        if constexpr (!sk) {
+            tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM, tm, tn);
+            kp0 = 0;
+            nk = nkt;
+        } else {
+            if (u >= u_end) break;
+            const int t = u / nkt;
+            kp0 = u - t * nkt;
+            nk = min(nkt - kp0, u_end - u);
+            // tile t in groups of GM tile rows, column by column in a group
+            const int per_group = GM * p.tiles_n;
+            const int group = t / per_group, first_m = group * GM;
+            const int rows = min(p.tiles_m - first_m, GM);
+            const int in_group = t - group * per_group;
+            tm = first_m + in_group % rows;
+            tn = in_group / rows;
+        }
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int k_lo = kp0 * S::BK;
+
+        // Copy sources.  A copy j of this wave fills panel rows 16 (wave + NW j)
+        // .. +15 (bytes (wave + NW j) KB of the stage); lane l takes row l / 4
+        // of them and position l % 4, which holds global chunk (l % 4) ^
+        // swz(row); rows start at multiples of 16, so swz(row) = (l / 16) % 4.
+        // B copy j fills k-row wave + NW j, lane l its floats 4l .. 4l + 3.
+        const float* a_src = p.A + (int64_t)(m0 + wave * 16 + arow) * p.lda + k_lo + achunk * 4;
+        const float* b_src = p.B + (int64_t)(k_lo + wave) * p.ldb + n0 + lane * 4;
+        const int64_t a_step = (int64_t)S::NW * 16 * p.lda;   // next copy of this wave
+        const int64_t b_step = (int64_t)S::NW * p.ldb;
+        const int64_t b_panel = (int64_t)S::BK * p.ldb;
+        auto fill = [&](unsigned char* stage, int kt) __attribute__((always_inline)) {
+            const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage));
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+            for (int j = 0; j < S::A_INS; ++j)
+                lds_copy16(a_src + j * a_step + kt * S::BK, base + (wave + S::NW * j) * 1024);
+#pragma unroll
+            for (int j = 0; j < S::B_INS; ++j)
+                lds_copy16(b_src + j * b_step + kt * b_panel,
+                           base + S::A_BYTES + (wave + S::NW * j) * S::B_ROW);
+        };
+
+        // Fragments of half q (steps 4q .. 4q + 3): A block i one 16-byte read
+        // at chunk 2h + q of its row; B block j four single reads at k-rows
+        // 8h + 4q + t.
+        f32x4 fa[2][FM];
+        float fb[2][FN][4];
+        auto frags = [&](const unsigned char* stage, int q) __attribute__((always_inline)) {
+            const lds_u8* base = (const lds_u8*)(stage);
+            const int chunk = ((2 * h + q) ^ sw) << 4;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
+                fa[q][i] = *reinterpret_cast<lds_f32x4c*>(base + a_off + i * 32 * 64 + chunk);
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                        fa[q][i][t], fb[q][j][t],
-                        (decltype(first)::value && t == 0) ? zero : acc[i][j], 0, 0, 0);
-    };
-    constexpr int NMF = 4 * FM * FN;      // matrix instructions per half
-    constexpr int NRD = FM + 4 * FN;      // fragment reads per half
-    auto interleave = [&]() __attribute__((always_inline)) {
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int m = 0; m < NMF; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (m < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-    };
+                for (int t = 0; t < 4; ++t)
+                    fb[q][j][t] = *reinterpret_cast<lds_f32c*>(base + b_off + (4 * q + t) * S::B_ROW +
+                                                               j * 32 * 4);
+        };
 
-    // One panel in `cur`: copy panel kt_fill into `freed` (the previous
-    // panel's stage, which every wave finished reading before the last
-    // barrier); first half beside the reads of the second half's fragments;
-    // wait for this wave's copies of the next panel; barrier; second half
-    // beside the reads of the next panel's first fragments.  Copies past the
-    // last panel reload the last one into a stage nobody reads again, so the
-    // count of outstanding copies is the same every panel.
-    auto panel = [&](const unsigned char* cur, unsigned char* freed, const unsigned char* next,
-                     int kt_fill, auto first) __attribute__((always_inline)) {
-        fill(freed, kt_fill);
-        frags(cur, 1);
-        mfmas(0, first);
-        __builtin_amdgcn_sched_group_barrier(0x020, S::FILLS, 0);
-        interleave();
+        f32x16 acc[FM][FN];
+        auto mfmas = [&](int q, auto first) __attribute__((always_inline)) {
+            const f32x16 zero = {};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            fa[q][i][t], fb[q][j][t],
+                            (decltype(first)::value && t == 0) ? zero : acc[i][j], 0, 0, 0);
+        };
+        constexpr int NMF = 4 * FM * FN;      // matrix instructions per half
+        constexpr int NRD = FM + 4 * FN;      // fragment reads per half
+        auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int m = 0; m < NMF; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (m < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        };
+
+        // One panel in `cur`: copy panel kt_fill into `freed` (the previous
+        // panel's stage, which every wave finished reading before the last
+        // barrier); first half beside the reads of the second half's
+        // fragments; wait for this wave's copies of the next panel; barrier;
+        // second half beside the reads of the next panel's first fragments.
+        // Copies past the last panel reload the last one into a stage nobody
+        // reads again, so the count of outstanding copies is the same every
+        // panel.
+        auto panel = [&](const unsigned char* cur, unsigned char* freed, const unsigned char* next,
+                         int kt_fill, auto first) __attribute__((always_inline)) {
+            fill(freed, kt_fill);
+            frags(cur, 1);
+            mfmas(0, first);
+            __builtin_amdgcn_sched_group_barrier(0x020, S::FILLS, 0);
+            interleave();
+            wait_vmcnt<(NS - 2) * S::FILLS>();
+            ring_barrier();
+            frags(next, 0);
+            mfmas(1, std::false_type{});
+            interleave();
+        };
+
+#pragma unroll
+        for (int i = 0; i + 1 < NS; ++i) fill(stage_of(i), min(i, nk - 1));
         wait_vmcnt<(NS - 2) * S::FILLS>();
         ring_barrier();
-        frags(next, 0);
-        mfmas(1, std::false_type{});
-        interleave();
-    };
+        frags(stage_of(0), 0);
 
+        panel(stage_of(0), stage_of(NS - 1), stage_of(1), min(NS - 1, nk - 1), std::true_type{});
 #pragma unroll
-    for (int i = 0; i + 1 < NS; ++i) fill(stage_of(i), min(i, nk - 1));
-    wait_vmcnt<(NS - 2) * S::FILLS>();
-    ring_barrier();
-    frags(stage_of(0), 0);
+        for (int v = 1; v < NS; ++v)
+            if (v < nk)
+                panel(stage_of(v), stage_of(v - 1), stage_of((v + 1) % NS), min(v + NS - 1, nk - 1),
+                      std::false_type{});
+        for (int kt = NS; kt < nk; kt += NS) {
+#pragma unroll
+            for (int v = 0; v < NS; ++v)
+                if (v == 0 || kt + v < nk)
+                    panel(stage_of(v), stage_of((v + NS - 1) % NS), stage_of((v + 1) % NS),
+                          min(kt + v + NS - 1, nk - 1), std::false_type{});
+        }
+        wait_vmcnt<0>();   // no copy may still be landing in LDS when the segment ends
 
-    panel(stage_of(0), stage_of(NS - 1), stage_of(1), min(NS - 1, nk - 1), std::true_type{});
+        bool finish = true;
+        if (sk && nk < nkt) {
+            // A part of the tile: store the accumulators in register order
+            // (16 floats per block and lane, four 16-byte device-scope
+            // stores, each instruction of a wave one contiguous kilobyte) in
+            // this workgroup's slot for the tile (0: the tile its run starts
+            // in, 1: the tile it ends in), wait for them, pass a barrier and
+            // count in.  The last workgroup of the tile to arrive reads every
+            // part back and adds them in k order (part s comes from workgroup
+            // g_first + s), so the sum does not depend on the arrival order.
+            constexpr int kSC1 = 1 << 4;          // cache-policy bit of the buffer intrinsics
+            constexpr int kRsrc = 0x00020000;     // raw buffer, 32-bit data format
+            constexpr int NB = FM * FN;
+            constexpr int TILE_BYTES = BM * BN * 4;
+            const int t = u / nkt;
+            const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+                p.P, (short)0, static_cast<int>((int64_t)gridDim.x * 2 * TILE_BYTES), kRsrc);
+            auto slot_of = [&](int wg) { return (wg * p.sk_q) / nkt == t ? 0 : 1; };
+            auto at = [&](int wg, int b, int q) {   // quarter q of block b of this lane
+                return static_cast<int>(((int64_t)wg * 2 + slot_of(wg)) * TILE_BYTES +
+                                        (((wave * NB + b) * 4 + q) * 64 + lane) * 16);
+            };
+            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int u = 1; u < NS; ++u)
-        if (u < nk)
-            panel(stage_of(u), stage_of(u - 1), stage_of((u + 1) % NS), min(u + NS - 1, nk - 1),
-                  std::false_type{});
-    for (int kt = NS; kt < nk; kt += NS) {
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int u = 0; u < NS; ++u)
-            if (u == 0 || kt + u < nk)
-                panel(stage_of(u), stage_of((u + NS - 1) % NS), stage_of((u + 1) % NS),
-                      min(kt + u + NS - 1, nk - 1), std::false_type{});
-    }
-    wait_vmcnt<0>();   // no copy may still be landing in LDS when the workgroup ends
-
-    if (p.ring_slices > 1) {
-        // Split K: store this slice's accumulators in register order (16
-        // floats per block and lane, four 16-byte device-scope stores, each
-        // instruction of a wave one contiguous kilobyte), wait for them, pass
-        // a barrier and count in; the last workgroup of the tile reads every
-        // slice back and adds them in slice order, so the sum does not depend
-        // on which workgroup arrives last.
-        constexpr int kSC1 = 1 << 4;          // cache-policy bit of the buffer intrinsics
-        constexpr int kRsrc = 0x00020000;     // raw buffer, 32-bit data format
-        constexpr int NB = FM * FN;
-        constexpr int TILE_BYTES = BM * BN * 4;
-        const int tiles = gridDim.x;
-        const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-            p.P, (short)0, static_cast<int>((int64_t)p.ring_slices * tiles * TILE_BYTES), kRsrc);
-        auto at = [&](int z, int b, int q) {   // quarter q of block b of this lane, slice z
-            return static_cast<int>(((int64_t)z * tiles + blockIdx.x) * TILE_BYTES +
-                                    (((wave * NB + b) * 4 + q) * 64 + lane) * 16);
-        };
-        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 v = {acc[b / FN][b % FN][4 * q], acc[b / FN][b % FN][4 * q + 1],
-                                 acc[b / FN][b % FN][4 * q + 2], acc[b / FN][b % FN][4 * q + 3]};
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp,
-                                                       at(slice, b, q), 0, kSC1);
-            }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();   // every wave is past its last panel read and its stores are done
-        unsigned* count = p.counts + blockIdx.x;
-        int* flag = reinterpret_cast<int*>(ring);
-        if (threadIdx.x == 0)
-            *flag = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                    static_cast<unsigned>(p.ring_slices - 1);
-        __syncthreads();
-        if (!*flag) return;
-        if (threadIdx.x == 0) __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // one block at a time, the loads of up to four slices in flight together
-        constexpr int ZG = 4;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            for (int z0 = 0; z0 < p.ring_slices; z0 += ZG) {
-                f32x4 t[ZG][4];
-#pragma unroll
-                for (int zz = 0; zz < ZG; ++zz) {
-                    const int z = min(z0 + zz, p.ring_slices - 1);   // past the last: unused reload
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        t[zz][q] = __builtin_bit_cast(
-                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, at(z, b, q), 0, kSC1));
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = {acc[b / FN][b % FN][4 * q], acc[b / FN][b % FN][4 * q + 1],
+                                     acc[b / FN][b % FN][4 * q + 2], acc[b / FN][b % FN][4 * q + 3]};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp,
+                                                           at(g, b, q), 0, kSC1);
                 }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();   // every wave is past its last panel read and its stores are done
+            const int g_first = (t * nkt) / p.sk_q;
+            const int parts = (t * nkt + nkt - 1) / p.sk_q - g_first + 1;
+            unsigned* count = p.counts + t;
+            int* flag = reinterpret_cast<int*>(ring);
+            if (threadIdx.x == 0)
+                *flag = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                        static_cast<unsigned>(parts - 1);
+            __syncthreads();
+            finish = *flag != 0;
+            if (finish) {
+                if (threadIdx.x == 0) __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // one block at a time, the loads of up to four parts (two for
+                // the larger wave tiles, for registers) in flight together
+                constexpr int ZG = NB >= 8 ? 2 : 4;
 #pragma unroll
-                for (int zz = 0; zz < ZG; ++zz) {
-                    if (z0 + zz >= p.ring_slices) break;
+                for (int b = 0; b < NB; ++b) {
+                    for (int s0 = 0; s0 < parts; s0 += ZG) {
+                        f32x4 tv[ZG][4];
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const float a = acc[b / FN][b % FN][e];
-                        acc[b / FN][b % FN][e] =
-                            z0 + zz == 0 ? t[zz][e / 4][e % 4] : a + t[zz][e / 4][e % 4];
+                        for (int ss = 0; ss < ZG; ++ss) {
+                            const int wg = g_first + min(s0 + ss, parts - 1);   // past the last: unused reload
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                tv[ss][q] = __builtin_bit_cast(
+                                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, at(wg, b, q), 0, kSC1));
+                        }
+#pragma unroll
+                        for (int ss = 0; ss < ZG; ++ss) {
+                            if (s0 + ss >= parts) break;
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) {
+                                const float a = acc[b / FN][b % FN][e];
+                                acc[b / FN][b % FN][e] =
+                                    s0 + ss == 0 ? tv[ss][e / 4][e % 4] : a + tv[ss][e / 4][e % 4];
+                            }
+                        }
                     }
                 }
             }
         }
+        if (finish)
+            store_tile<FM, FN, false>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N,
+                                      p.alpha, p.beta, lane);
+        if constexpr (!sk) break;
+        u += nk;
+        ring_barrier();   // every wave is done with the ring before the next run refills it
     }
-    store_tile<FM, FN, false>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N,
-                              p.alpha, p.beta, lane);
 }
 
 }  // namespace
@@ -284,12 +327,16 @@ hipError_t launch_f32_ring(const F32Args& a, F32Variant v, hipStream_t s) {
         if (v.ta || v.tb) return launch_f32_transposed<BM, BN, 16, 2, 2, GM>(a, v, s);
         return launch_f32_layout<BM, BN, 16, 2, 2, GM, false, false>(a, v, s);
     }
-    if (a.ring_slices > 1 &&
-        (!a.P || !a.counts || a.ring_depth <= 0 || a.ring_depth % 16 != 0 ||
-         (int64_t)(a.ring_slices - 1) * a.ring_depth >= a.K || (int64_t)a.ring_slices * a.ring_depth < a.K))
+    const int64_t units = int64_t{a.tiles_m} * a.tiles_n * (a.K / 16);
+    if (a.sk_q > 0 && (!a.P || !a.counts || units > 0x7fffffff))
         return hipErrorInvalidValue;
-    const dim3 grid(a.tiles_m * a.tiles_n, a.ring_slices > 1 ? a.ring_slices : 1), block(WM * WN * 64);
-    gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM><<<grid, block, 0, s>>>(a);
+    const dim3 block(WM * WN * 64);
+    if (a.sk_q > 0)
+        gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM, true>
+            <<<dim3(static_cast<unsigned>((units + a.sk_q - 1) / a.sk_q)), block, 0, s>>>(a);
+    else
+        gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM, false>
+            <<<dim3(static_cast<unsigned>(a.tiles_m * a.tiles_n)), block, 0, s>>>(a);
     return hipGetLastError();
 }
 

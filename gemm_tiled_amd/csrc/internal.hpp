@@ -43,13 +43,15 @@ struct F32Args {
     float alpha, beta;
     int tiles_m, tiles_n;
     int ksplit = 0;   // k per slice (multiple of BK); 0 = no split
-    // The f32 ring only (gemm_f32_ring.hip): K split over blockIdx.y into
-    // ring_slices slices of ring_depth k (a multiple of 16).  With more than
-    // one slice the workgroups of a tile store their accumulators in P
-    // (ring_slices x tiles x BM x BN floats, below 2^31 bytes) and the last
-    // one to arrive (counted in counts[tile], zero before and after the
-    // launch) adds them in slice order and applies the epilogue.
-    int ring_slices = 1, ring_depth = 0;
+    // The f32 ring only (gemm_f32_ring.hip): with sk_q > 0 the launch is a
+    // stream-K one.  The (tile, 16-deep panel) units of the call, tile-major,
+    // are dealt in runs of sk_q to the workgroups (grid = ceil(units / sk_q));
+    // a tile whose panels span several runs is finished by the last of its
+    // workgroups to arrive (counted in counts[tile], zero before and after
+    // the launch), which adds the partial tiles the others stored in P (two
+    // BM x BN slots per workgroup, gridDim.x x 2 x BM x BN floats, below 2^31
+    // bytes) in k order.
+    int sk_q = 0;
     float* P = nullptr;
     unsigned* counts = nullptr;
 };
