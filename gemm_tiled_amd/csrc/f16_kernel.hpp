@@ -528,7 +528,13 @@ __device__ __forceinline__ void store_tile_m16_staged(const f32x4 (&acc)[FM][FN]
     }
 }
 
-template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED, bool OUT16>
+// SK: a data-parallel + stream-K launch (p.sk_q > 0): the workgroups first
+// take p.sk_dp whole rounds of tiles, then the (tile, panel) units of the
+// remaining tiles, tile-major, in runs of sk_q (workgroups of one XCD get
+// consecutive runs); a workgroup walks its run tile by tile, and a tile split
+// over several workgroups is finished by the last of them to arrive, which
+// adds the parts the others stored in P in k order.
+template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED, bool OUT16, bool SK>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_ring_kernel(F16Args p) {
     using S = RingShape<BM, BN, NS, WM, WN>;
     static_assert(S::NW * StagedRows<S::TN>::BYTES <= NS * S::STAGE, "staged epilogue fits the ring");
@@ -542,162 +548,283 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_ring_kernel(F16Args p) 
     unsigned char* const st3 = ring + (NS > 3 ? 3 : 0) * S::STAGE;
     unsigned char* const st4 = ring + (NS > 4 ? 4 : 0) * S::STAGE;
 
-    int tm, tn;
-    tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / WN, wc = wave % WN;
-    const int nk = static_cast<int>(p.nkb);
+    const int nkt = static_cast<int>(p.nkb);   // panels of a whole tile
+    const int dp_tiles = SK ? p.sk_dp * gridDim.x : 0;
+    int g = 0, u = 0, u_end = 0, r = 0;
+    if constexpr (SK) {
+        const int G = gridDim.x, xcd = blockIdx.x & 7, q8 = G >> 3, r8 = G & 7;
+        g = xcd * q8 + (xcd < r8 ? xcd : r8) + (blockIdx.x >> 3);
+        u = g * p.sk_q;
+        u_end = min((p.tiles_m * p.tiles_n - dp_tiles) * nkt, u + p.sk_q);
+    }
 
-    // Panel kt of this tile's A rows is the BM-row slice at row m0 % 256 of
-    // packed block (m0 / 256, kt); consecutive kt are consecutive blocks.
-    const int lane_ofs = wave * 1024 + lane * 16;
-    const unsigned char* a_src = reinterpret_cast<const unsigned char*>(
-        p.A16 + ((int64_t)(m0 / kPackRows) * p.nkb * kPackRows + m0 % kPackRows) * D) + lane_ofs;
-    const unsigned char* b_src = reinterpret_cast<const unsigned char*>(
-        p.B16t + ((int64_t)(n0 / kPackRows) * p.nkb * kPackRows + n0 % kPackRows) * D) + lane_ofs;
-    constexpr int64_t kBlockBytes = int64_t{kPackRows} * D * 2;
-
-    auto stage_of = [&](int i) __attribute__((always_inline)) -> unsigned char* {
-        return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : i == 3 ? st3 : st4;
-    };
-    auto fill = [&](unsigned char* stage, int kt) __attribute__((always_inline)) {
-        const uint32_t as = __builtin_amdgcn_readfirstlane(lds_addr(stage) + wave * 1024);
-        const uint32_t bs = as + S::A_BYTES;
-        const int64_t kofs = (int64_t)kt * kBlockBytes;
-#pragma unroll
-        for (int j = 0; j < S::A_INS; ++j)
-            lds_copy16(a_src + kofs + j * S::NW * 1024, as + j * S::NW * 1024);
-#pragma unroll
-        for (int j = 0; j < S::B_INS; ++j)
-            lds_copy16(b_src + kofs + j * S::NW * 1024, bs + j * S::NW * 1024);
-    };
-
-    // Fragment reads: lane (q, r16) reads row r16 of a 16-row block at logical
-    // chunk q, the 8 k values [8q, 8q + 8) of the panel, to A and B alike.
-    // Blocks start at multiples of 16 rows, whole swizzle periods, so the key
-    // is swz(r16).
-    const int r16 = lane & 15, q = lane >> 4;
-    const int chunk = (q ^ swz<D>(r16)) << 4;
-    const int a_row0 = (wr * S::TM + r16) * S::ROW + chunk;
-    const int b_row0 = S::A_BYTES + (wc * S::TN + r16) * S::ROW + chunk;
-    f16x8 fa[GFM], fb[2][GFN];
-    auto read_a = [&](const unsigned char* stage, int i) __attribute__((always_inline)) {
-        fa[i] = *reinterpret_cast<lds_f16x8*>((const lds_u8*)(stage) + a_row0 + i * 16 * S::ROW);
-    };
-    auto read_b = [&](const unsigned char* stage, int b, int j) __attribute__((always_inline)) {
-        fb[b][j] = *reinterpret_cast<lds_f16x8*>((const lds_u8*)(stage) + b_row0 + j * 16 * S::ROW);
-    };
-
-    // The accumulators get their first value from the first matrix
-    // instruction, with an inline-constant zero as its addend.
-    f32x4 acc[GFM][GFN];
-    auto mfma_rows = [&](int i0, int i1, int b, auto first) __attribute__((always_inline)) {
-        const f32x4 zero = {};
-#pragma unroll
-        for (int i = i0; i < i1; ++i)
-#pragma unroll
-            for (int j = 0; j < GFN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    fa[i], fb[b][j], decltype(first)::value ? zero : acc[i][j], 0, 0, 0);
-    };
-    // one matrix instruction, then one fragment read, while reads remain
-    auto interleave = [&](auto nmf_c, auto nrd_c) __attribute__((always_inline)) {
-        constexpr int nmf = decltype(nmf_c)::value, nrd = decltype(nrd_c)::value;
-#pragma unroll
-        for (int m = 0; m < nmf; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (m < nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (;;) {
+        int tm, tn, kp0, nk;
+        bool dp_item = false;
+        if constexpr (!SK) {
+            tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM, tm, tn);
+            kp0 = 0;
+            nk = nkt;
+        } else if (r < p.sk_dp) {
+            tile_of_block(r * gridDim.x + blockIdx.x, dp_tiles, p.tiles_m, p.tiles_n, GM, tm, tn);
+            kp0 = 0;
+            nk = nkt;
+            dp_item = true;
+        } else {
+            if (u >= u_end) break;
+            const int t = u / nkt;
+            kp0 = u - t * nkt;
+            nk = min(nkt - kp0, u_end - u);
+            raster_tile(dp_tiles + t, p.tiles_m, p.tiles_n, GM, tm, tn);
         }
-    };
+        const int m0 = tm * BM, n0 = tn * BN;
 
-    // One panel in stage `cur`, its B fragments in fb[b]: fill panel kt_fill
-    // into `freed` (the stage of the previous panel, which every wave finished
-    // reading before the last barrier), then the two halves described above.
-    // Fills past the last panel reload the last panel into a stage nobody
-    // reads again, so the count of outstanding fills is the same every panel.
-    auto panel = [&](const unsigned char* cur, unsigned char* freed, const unsigned char* next,
-                     int kt_fill, auto b_c, auto first) __attribute__((always_inline)) {
-        constexpr int b = decltype(b_c)::value;
-        fill(freed, kt_fill);
-#pragma unroll
-        for (int i = H; i < GFM; ++i) read_a(cur, i);
-        mfma_rows(0, H, b, first);
-        __builtin_amdgcn_sched_group_barrier(0x020, S::FILLS, 0);
-        interleave(std::integral_constant<int, H * GFN>{}, std::integral_constant<int, GFM - H>{});
+        // Panel kt of this tile's A rows is the BM-row slice at row m0 % 256 of
+        // packed block (m0 / 256, kt); consecutive kt are consecutive blocks.
+        constexpr int64_t kBlockBytes = int64_t{kPackRows} * D * 2;
+        const int lane_ofs = wave * 1024 + lane * 16;
+        const unsigned char* a_src = reinterpret_cast<const unsigned char*>(
+            p.A16 + ((int64_t)(m0 / kPackRows) * p.nkb * kPackRows + m0 % kPackRows) * D) + lane_ofs +
+            kp0 * kBlockBytes;
+        const unsigned char* b_src = reinterpret_cast<const unsigned char*>(
+            p.B16t + ((int64_t)(n0 / kPackRows) * p.nkb * kPackRows + n0 % kPackRows) * D) + lane_ofs +
+            kp0 * kBlockBytes;
+
+        auto stage_of = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+            return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : i == 3 ? st3 : st4;
+        };
+        auto fill = [&](unsigned char* stage, int kt) __attribute__((always_inline)) {
+            const uint32_t as = __builtin_amdgcn_readfirstlane(lds_addr(stage) + wave * 1024);
+            const uint32_t bs = as + S::A_BYTES;
+            const int64_t kofs = (int64_t)kt * kBlockBytes;
+    #pragma unroll
+            for (int j = 0; j < S::A_INS; ++j)
+                lds_copy16(a_src + kofs + j * S::NW * 1024, as + j * S::NW * 1024);
+    #pragma unroll
+            for (int j = 0; j < S::B_INS; ++j)
+                lds_copy16(b_src + kofs + j * S::NW * 1024, bs + j * S::NW * 1024);
+        };
+
+        // Fragment reads: lane (q, r16) reads row r16 of a 16-row block at logical
+        // chunk q, the 8 k values [8q, 8q + 8) of the panel, to A and B alike.
+        // Blocks start at multiples of 16 rows, whole swizzle periods, so the key
+        // is swz(r16).
+        const int r16 = lane & 15, q = lane >> 4;
+        const int chunk = (q ^ swz<D>(r16)) << 4;
+        const int a_row0 = (wr * S::TM + r16) * S::ROW + chunk;
+        const int b_row0 = S::A_BYTES + (wc * S::TN + r16) * S::ROW + chunk;
+        f16x8 fa[GFM], fb[2][GFN];
+        auto read_a = [&](const unsigned char* stage, int i) __attribute__((always_inline)) {
+            fa[i] = *reinterpret_cast<lds_f16x8*>((const lds_u8*)(stage) + a_row0 + i * 16 * S::ROW);
+        };
+        auto read_b = [&](const unsigned char* stage, int b, int j) __attribute__((always_inline)) {
+            fb[b][j] = *reinterpret_cast<lds_f16x8*>((const lds_u8*)(stage) + b_row0 + j * 16 * S::ROW);
+        };
+
+        // The accumulators get their first value from the first matrix
+        // instruction, with an inline-constant zero as its addend.
+        f32x4 acc[GFM][GFN];
+        auto mfma_rows = [&](int i0, int i1, int b, auto first) __attribute__((always_inline)) {
+            const f32x4 zero = {};
+    #pragma unroll
+            for (int i = i0; i < i1; ++i)
+    #pragma unroll
+                for (int j = 0; j < GFN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        fa[i], fb[b][j], decltype(first)::value ? zero : acc[i][j], 0, 0, 0);
+        };
+        // one matrix instruction, then one fragment read, while reads remain
+        auto interleave = [&](auto nmf_c, auto nrd_c) __attribute__((always_inline)) {
+            constexpr int nmf = decltype(nmf_c)::value, nrd = decltype(nrd_c)::value;
+    #pragma unroll
+            for (int m = 0; m < nmf; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (m < nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        };
+
+        // One panel in stage `cur`, its B fragments in fb[b]: fill panel kt_fill
+        // into `freed` (the stage of the previous panel, which every wave finished
+        // reading before the last barrier), then the two halves described above.
+        // Fills past the last panel reload the last panel into a stage nobody
+        // reads again, so the count of outstanding fills is the same every panel.
+        auto panel = [&](const unsigned char* cur, unsigned char* freed, const unsigned char* next,
+                         int kt_fill, auto b_c, auto first) __attribute__((always_inline)) {
+            constexpr int b = decltype(b_c)::value;
+            fill(freed, kt_fill);
+    #pragma unroll
+            for (int i = H; i < GFM; ++i) read_a(cur, i);
+            mfma_rows(0, H, b, first);
+            __builtin_amdgcn_sched_group_barrier(0x020, S::FILLS, 0);
+            interleave(std::integral_constant<int, H * GFN>{}, std::integral_constant<int, GFM - H>{});
+            wait_vmcnt<(NS - 2) * S::FILLS>();
+            ring_barrier();
+    #pragma unroll
+            for (int j = 0; j < GFN; ++j) read_b(next, b ^ 1, j);
+    #pragma unroll
+            for (int i = 0; i < H; ++i) read_a(next, i);
+            mfma_rows(H, GFM, b, first);
+            interleave(std::integral_constant<int, (GFM - H) * GFN>{},
+                       std::integral_constant<int, GFN + H>{});
+        };
+        // Panel kt + u of an unrolled step: stage (kt + u) % NS with kt a multiple
+        // of U, and the B buffer alternates with the panel's parity.
+        auto step = [&](int kt, auto u_c, auto first) __attribute__((always_inline)) {
+            constexpr int u = decltype(u_c)::value;
+            panel(stage_of(u % NS), stage_of((u + NS - 1) % NS), stage_of((u + 1) % NS),
+                  min(kt + u + NS - 1, nk - 1), std::integral_constant<int, u & 1>{}, first);
+        };
+
+        // Prologue: panels 0 .. NS-2 into stages 0 .. NS-2; wait for panel 0 and
+        // read its first fragments.
+    #pragma unroll
+        for (int i = 0; i + 1 < NS; ++i) fill(stage_of(i), min(i, nk - 1));
         wait_vmcnt<(NS - 2) * S::FILLS>();
         ring_barrier();
-#pragma unroll
-        for (int j = 0; j < GFN; ++j) read_b(next, b ^ 1, j);
-#pragma unroll
-        for (int i = 0; i < H; ++i) read_a(next, i);
-        mfma_rows(H, GFM, b, first);
-        interleave(std::integral_constant<int, (GFM - H) * GFN>{},
-                   std::integral_constant<int, GFN + H>{});
-    };
-    // Panel kt + u of an unrolled step: stage (kt + u) % NS with kt a multiple
-    // of U, and the B buffer alternates with the panel's parity.
-    auto step = [&](int kt, auto u_c, auto first) __attribute__((always_inline)) {
-        constexpr int u = decltype(u_c)::value;
-        panel(stage_of(u % NS), stage_of((u + NS - 1) % NS), stage_of((u + 1) % NS),
-              min(kt + u + NS - 1, nk - 1), std::integral_constant<int, u & 1>{}, first);
-    };
+    #pragma unroll
+        for (int j = 0; j < GFN; ++j) read_b(stage_of(0), 0, j);
+    #pragma unroll
+        for (int i = 0; i < H; ++i) read_a(stage_of(0), i);
 
-    // Prologue: panels 0 .. NS-2 into stages 0 .. NS-2; wait for panel 0 and
-    // read its first fragments.
-#pragma unroll
-    for (int i = 0; i + 1 < NS; ++i) fill(stage_of(i), min(i, nk - 1));
-    wait_vmcnt<(NS - 2) * S::FILLS>();
-    ring_barrier();
-#pragma unroll
-    for (int j = 0; j < GFN; ++j) read_b(stage_of(0), 0, j);
-#pragma unroll
-    for (int i = 0; i < H; ++i) read_a(stage_of(0), i);
-
-    step(0, std::integral_constant<int, 0>{}, std::true_type{});
-    static_for<U - 1>([&](auto v_c) __attribute__((always_inline)) {
-        constexpr int u = decltype(v_c)::value + 1;
-        if (u < nk) step(0, std::integral_constant<int, u>{}, std::false_type{});
-    });
-    for (int kt = U; kt < nk; kt += U) {
-        static_for<U>([&](auto u_c) __attribute__((always_inline)) {
-            if (decltype(u_c)::value == 0 || kt + decltype(u_c)::value < nk)
-                step(kt, u_c, std::false_type{});
+        step(0, std::integral_constant<int, 0>{}, std::true_type{});
+        static_for<U - 1>([&](auto v_c) __attribute__((always_inline)) {
+            constexpr int u = decltype(v_c)::value + 1;
+            if (u < nk) step(0, std::integral_constant<int, u>{}, std::false_type{});
         });
-    }
-    wait_vmcnt<0>();   // no fill may still be landing in LDS when the workgroup ends
+        for (int kt = U; kt < nk; kt += U) {
+            static_for<U>([&](auto u_c) __attribute__((always_inline)) {
+                if (decltype(u_c)::value == 0 || kt + decltype(u_c)::value < nk)
+                    step(kt, u_c, std::false_type{});
+            });
+        }
+        wait_vmcnt<0>();   // no fill may still be landing in LDS when the tile's work ends
+
+        bool finish = true;
+        if (SK && nk < nkt) {
+            // A part of the tile: store the accumulators in register order (one
+            // 16-byte device-scope store per block and lane) in this workgroup's
+            // slot for the tile (0: the tile its run starts in, 1: the one it ends
+            // in), wait for them, pass a barrier and count in; the last workgroup
+            // of the tile reads every part back in k order (part s comes from
+            // workgroup g_first + s) and applies the epilogue.
+            constexpr int kSC1 = 1 << 4;          // cache-policy bit of the buffer intrinsics
+            constexpr int kRsrc = 0x00020000;     // raw buffer, 32-bit data format
+            constexpr int NB = GFM * GFN;
+            constexpr int TILE_BYTES = BM * BN * 4;
+            const int t = u / nkt;
+            const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+                p.P, (short)0, static_cast<int>((int64_t)gridDim.x * 2 * TILE_BYTES), kRsrc);
+            auto at = [&](int wg, int b) {
+                const int slot = (wg * p.sk_q) / nkt == t ? 0 : 1;
+                return static_cast<int>(((int64_t)wg * 2 + slot) * TILE_BYTES +
+                                        ((wave * NB + b) * 64 + lane) * 16);
+            };
+    #pragma unroll
+            for (int b = 0; b < NB; ++b)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[b / GFN][b % GFN]),
+                                                       rp, at(g, b), 0, kSC1);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();   // every wave is past its last fragment read and its stores are done
+            const int g_first = (t * nkt) / p.sk_q;
+            const int parts = (t * nkt + nkt - 1) / p.sk_q - g_first + 1;
+            unsigned* count = p.counts + t;
+            int* flag = reinterpret_cast<int*>(ring);
+            if (threadIdx.x == 0)
+                *flag = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                        static_cast<unsigned>(parts - 1);
+            __syncthreads();
+            finish = *flag != 0;
+            if (finish) {
+                if (threadIdx.x == 0) __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // four blocks at a time, the loads of up to four parts in
+                // flight together, added in k order
+                constexpr int CB = 4, ZG = 4;
+                static_assert(NB % CB == 0, "blocks in chunks of four");
+#pragma unroll
+                for (int b0 = 0; b0 < NB; b0 += CB) {
+                    for (int s0 = 0; s0 < parts; s0 += ZG) {
+                        f32x4 tv[ZG][CB];
+#pragma unroll
+                        for (int ss = 0; ss < ZG; ++ss) {
+                            const int wg = g_first + min(s0 + ss, parts - 1);   // past the last: unused reload
+#pragma unroll
+                            for (int c = 0; c < CB; ++c)
+                                tv[ss][c] = __builtin_bit_cast(
+                                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, at(wg, b0 + c), 0, kSC1));
+                        }
+#pragma unroll
+                        for (int ss = 0; ss < ZG; ++ss) {
+                            if (s0 + ss >= parts) break;
+#pragma unroll
+                            for (int c = 0; c < CB; ++c) {
+                                const int b = b0 + c;
+                                const f32x4 a = acc[b / GFN][b % GFN];
+                                acc[b / GFN][b % GFN] = s0 + ss == 0 ? tv[ss][c] : a + tv[ss][c];
+                            }
+                        }
+                    }
+                }
+            }
+        }
 
     // vector rows of C: f32 16-byte aligned, binary16 8-byte aligned
-    const uintptr_t c_addr = OUT16 ? reinterpret_cast<uintptr_t>(p.C16) : reinterpret_cast<uintptr_t>(p.C);
-    const bool staged = !MASKED && p.ldc % 4 == 0 && (c_addr & (OUT16 ? 7 : 15)) == 0;
-    if (staged) {
-        // every wave is past its last fragment read once all have arrived here
-        __syncthreads();
-        unsigned char* mine = ring + wave * StagedRows<S::TN>::BYTES;
-        if constexpr (OUT16)
-            store_tile_m16_staged<GFM, GFN, S::TN, true>(acc, p.C16, p.ldc, m0 + wr * S::TM,
-                                                         n0 + wc * S::TN, p.alpha, p.beta, lane, mine);
-        else
-            store_tile_m16_staged<GFM, GFN, S::TN, false>(acc, p.C, p.ldc, m0 + wr * S::TM,
-                                                          n0 + wc * S::TN, p.alpha, p.beta, lane, mine);
-    } else if constexpr (OUT16) {
-        store_tile_m16<GFM, GFN, MASKED, true>(acc, p.C16, p.ldc, m0 + wr * S::TM,
-                                               n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta, lane);
-    } else {
-        store_tile_m16<GFM, GFN, MASKED, false>(acc, p.C, p.ldc, m0 + wr * S::TM,
-                                                n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta, lane);
+        const uintptr_t c_addr = OUT16 ? reinterpret_cast<uintptr_t>(p.C16) : reinterpret_cast<uintptr_t>(p.C);
+        const bool staged = !MASKED && p.ldc % 4 == 0 && (c_addr & (OUT16 ? 7 : 15)) == 0;
+        if (!finish) {
+            // another workgroup finishes this tile
+        } else if (staged) {
+            // every wave is past its last fragment read once all have arrived here
+            __syncthreads();
+            unsigned char* mine = ring + wave * StagedRows<S::TN>::BYTES;
+            if constexpr (OUT16)
+                store_tile_m16_staged<GFM, GFN, S::TN, true>(acc, p.C16, p.ldc, m0 + wr * S::TM,
+                                                             n0 + wc * S::TN, p.alpha, p.beta, lane, mine);
+            else
+                store_tile_m16_staged<GFM, GFN, S::TN, false>(acc, p.C, p.ldc, m0 + wr * S::TM,
+                                                              n0 + wc * S::TN, p.alpha, p.beta, lane, mine);
+        } else if constexpr (OUT16) {
+            store_tile_m16<GFM, GFN, MASKED, true>(acc, p.C16, p.ldc, m0 + wr * S::TM,
+                                                   n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta, lane);
+        } else {
+            store_tile_m16<GFM, GFN, MASKED, false>(acc, p.C, p.ldc, m0 + wr * S::TM,
+                                                    n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta, lane);
+        }
+        if constexpr (!SK) break;
+        if (dp_item) ++r;
+        else u += nk;
+        ring_barrier();   // every wave is done with the ring before the next tile refills it
     }
+}
+
+// Whether a half-depth ring configuration has a stream-K form: not for wave
+// tiles of 128 x 128, whose 256 accumulator registers leave no room for the
+// partial sums.  (The host's stream-K rule leaves them out too.)
+constexpr bool ring_takes_sk(int bm, int bn, int wm, int wn) {
+    return (bm / wm) * (bn / wn) < 128 * 128;
 }
 
 // One configuration, both masking variants, f32 (OUT16 false) or binary16 C.
 template <int BM, int BN, int NS, int WM, int WN, int GM, bool OUT16>
 hipError_t launch_f16_ring_out(const F16Args& a, hipStream_t s) {
-    const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
+    const dim3 block(WM * WN * 64);
     const bool masked = (a.M % BM) != 0 || (a.N % BN) != 0;
-    if (masked) gemm_f16_ring_kernel<BM, BN, NS, WM, WN, GM, true, OUT16><<<grid, block, 0, s>>>(a);
-    else gemm_f16_ring_kernel<BM, BN, NS, WM, WN, GM, false, OUT16><<<grid, block, 0, s>>>(a);
+    if constexpr (!ring_takes_sk(BM, BN, WM, WN)) {
+        if (a.sk_q > 0) return hipErrorInvalidValue;
+    } else if (a.sk_q > 0) {
+        const int grid = ring_sk_grid(int64_t{a.tiles_m} * a.tiles_n, a.nkb, a.sk_q, a.sk_dp,
+                                      a.sk_grid, a.P, a.counts);
+        if (grid <= 0) return hipErrorInvalidValue;
+        // the stream-K form always guards its stores (whole tiles too): the
+        // compiler keeps that variant's loop in registers better
+        gemm_f16_ring_kernel<BM, BN, NS, WM, WN, GM, true, OUT16, true><<<dim3(grid), block, 0, s>>>(a);
+        return hipGetLastError();
+    }
+    const dim3 grid(a.tiles_m * a.tiles_n);
+    if (masked) gemm_f16_ring_kernel<BM, BN, NS, WM, WN, GM, true, OUT16, false><<<grid, block, 0, s>>>(a);
+    else gemm_f16_ring_kernel<BM, BN, NS, WM, WN, GM, false, OUT16, false><<<grid, block, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -212,26 +212,54 @@ bool vec_ok(const float* p, int64_t ld) {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// The f32 ring configurations (direct-to-LDS copies, BK = 16, three or more
-// stages) and their stream-K run length: when whole rounds of tiles would
-// leave CUs idle, the (tile, 16-deep panel) units of the call are dealt to the
-// CUs in equal runs of at least kRingMinPanels units, if that beats the whole
-// rounds by 5% counting kRingSkOverhead panels for the split tiles' partial
-// sums; 0 = one tile per workgroup.
+// The ring configurations -- f32 (direct-to-LDS copies, BK = 16, three or
+// more stages) and f16r half-depth (BK = 32) -- and their stream-K form: when
+// whole rounds of tiles would leave resident slots idle, the slots take the
+// whole rounds they can fill (data-parallel, in the usual tile order) and
+// then the (tile, panel) units of the remaining tiles in equal runs of at
+// least kRingMinPanels units, if that beats the whole rounds by 5% counting
+// kRingSkOverhead panels for the split tiles' partial sums.  Runs that start
+// at different depths of their tiles share no operand panels in the cache,
+// which is why the remaining tiles alone are dealt this way.
 bool is_f32_ring(const TileConfig& c) {
     return c.mode == GEMM355_MODE_F32 && c.bk == 16 && c.st >= 3 && c.ks == 0;
 }
+bool is_f16_ring(const TileConfig& c) {
+    return c.mode == GEMM355_MODE_F16R && c.bk == 32 && c.ks == 0;
+}
 
-int64_t ring_sk_q(const TileConfig& c, int64_t M, int64_t N, int64_t K) {
+struct RingSk {
+    int64_t q = 0, dp = 0, grid = 0;   // q = 0: one tile per workgroup
+    double panels = 0;                 // estimated panels per slot
+};
+
+RingSk ring_sk(const TileConfig& c, int64_t M, int64_t N, int64_t K) {
+    RingSk out;
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    const int64_t nkt = K / 16, units = tiles * nkt;
-    if (tiles % kCUs == 0 || units >= (int64_t{1} << 31)) return 0;
-    const int64_t q = std::max<int64_t>((units + kCUs - 1) / kCUs, kRingMinPanels);
-    const int64_t whole = (tiles + kCUs - 1) / kCUs * nkt;
-    if (static_cast<double>(q + kRingSkOverhead) >= 0.95 * static_cast<double>(whole)) return 0;
-    const int64_t grid = (units + q - 1) / q;
-    if (grid * 2 * c.bm * c.bn * 4 > kSplitKMaxBytes) return 0;
-    return q;
+    const int64_t nkt = c.mode == GEMM355_MODE_F32 ? K / 16 : round_up(K, 64) / 32;
+    // LDS of one workgroup: NS stages of BM x BK A rows and BK x BN B values
+    // (f32 B rows padded by 16 bytes), binary16 or f32
+    const int64_t lds = c.mode == GEMM355_MODE_F32
+                            ? int64_t{c.st} * (c.bm * 64 + 16 * (c.bn * 4 + 16))
+                            : int64_t{c.st} * (c.bm + c.bn) * 64;
+    const int64_t slots = kCUs * std::max<int64_t>(1, (160 * 1024) / lds);
+    const int64_t whole = (tiles + slots - 1) / slots * nkt;
+    out.panels = static_cast<double>(whole);
+    if (tiles % slots == 0 || tiles * nkt >= (int64_t{1} << 31)) return out;
+    // a binary16 ring with 128 x 128 wave tiles has no stream-K form
+    if (c.mode == GEMM355_MODE_F16R && (c.bm / c.wm) * (c.bn / c.wn) >= 128 * 128) return out;
+    const int64_t dp = tiles / slots;
+    const int64_t rest = (tiles - dp * slots) * nkt;
+    const int64_t q = std::max<int64_t>((rest + slots - 1) / slots, kRingMinPanels);
+    const double panels = static_cast<double>(dp * nkt + q + kRingSkOverhead);
+    if (panels >= 0.95 * static_cast<double>(whole)) return out;
+    const int64_t grid = dp > 0 ? slots : (rest + q - 1) / q;
+    if (grid * 2 * c.bm * c.bn * 4 > kSplitKMaxBytes) return out;
+    out.q = q;
+    out.dp = dp;
+    out.grid = grid;
+    out.panels = panels;
+    return out;
 }
 
 // Heuristic when nothing is pinned or tuned: estimate the time of each
@@ -263,10 +291,9 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K) {
         // the partial sums' overhead); it also stages its panels faster than
         // the register-staged kernel (10-20% measured, counted as 20%)
         const bool ring = is_f32_ring(c) && M % c.bm == 0 && N % c.bn == 0 && K % 16 == 0;
-        const int64_t q = ring ? ring_sk_q(c, M, N, K) : 0;
+        const RingSk sk = ring || is_f16_ring(c) ? ring_sk(c, M, N, K) : RingSk{};
         const double kpad = static_cast<double>(round_up(K, c.bk));
-        const double rounds = q > 0 ? static_cast<double>(q + kRingSkOverhead) / (K / 16)
-                                    : std::ceil(tiles / (256.0 * per_cu));
+        const double rounds = sk.q > 0 ? sk.panels / (kpad / c.bk) : std::ceil(tiles / (256.0 * per_cu));
         const double reuse = static_cast<double>(c.bm) * c.bn / (c.bm + c.bn);   // flop per loaded element
         const double eff = reuse / (reuse + 6.5) * (ring ? 1.2 : 1.0);
         const double cost = rounds * per_cu * c.bm * c.bn * kpad / eff;
@@ -589,13 +616,15 @@ int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
             v.masked = !v.vec || (M % cfg.bm) || (N % cfg.bn) || (K % cfg.bk);
             // a ring configuration deals its work to the CUs in equal runs
             // (stream-K) when whole rounds of tiles would leave CUs idle
-            const int64_t q = is_f32_ring(cfg) && f32_ring_takes(cfg, a, v) ? ring_sk_q(cfg, M, N, K) : 0;
-            if (q > 0) {
+            const RingSk sk =
+                is_f32_ring(cfg) && f32_ring_takes(cfg, a, v) ? ring_sk(cfg, M, N, K) : RingSk{};
+            if (sk.q > 0) {
                 const int64_t tiles = int64_t{tiles_m} * tiles_n;
-                const int64_t grid = (tiles * (K / 16) + q - 1) / q;
-                a.sk_q = static_cast<int>(q);
+                a.sk_q = static_cast<int>(sk.q);
+                a.sk_dp = static_cast<int>(sk.dp);
+                a.sk_grid = static_cast<int>(sk.grid);
                 void* ws = nullptr;
-                hipError_t e = workspace(s, static_cast<size_t>(grid * 2 * cfg.bm * cfg.bn) * 4, &ws);
+                hipError_t e = workspace(s, static_cast<size_t>(sk.grid * 2 * cfg.bm * cfg.bn) * 4, &ws);
                 if (e == hipSuccess) e = counters(s, static_cast<size_t>(tiles), &a.counts);
                 if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
                 a.P = static_cast<float*>(ws);
@@ -611,12 +640,21 @@ int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
         return GEMM355_ERR_CONFIG;
     }
     int n = 0;
+    unsigned* counts = nullptr;
     const F16Instance* t = f16_instances(&n);
     for (int i = 0; i < n; ++i) {
         if (!(t[i].cfg == cfg)) continue;
         const int64_t mp = round_up(M, 256), np = round_up(N, 256), kp = round_up(K, 64);
+        // a half-depth ring deals its work in equal runs (stream-K) when whole
+        // rounds of tiles would leave slots idle; its partial tiles follow the
+        // packed operands in the workspace
+        const RingSk sk = is_f16_ring(cfg) ? ring_sk(cfg, M, N, K) : RingSk{};
+        const int64_t q = sk.q;
+        const int64_t packed_bytes = round_up((mp + np) * kp * 2, 256);
         void* ws = nullptr;
-        hipError_t e = workspace(s, static_cast<size_t>((mp + np) * kp) * 2, &ws);
+        hipError_t e = workspace(
+            s, static_cast<size_t>(packed_bytes + sk.grid * 2 * cfg.bm * cfg.bn * 4), &ws);
+        if (e == hipSuccess && q > 0) e = counters(s, static_cast<size_t>(tiles_m) * tiles_n, &counts);
         if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
         uint16_t* A16 = static_cast<uint16_t*>(ws);
         uint16_t* B16t = A16 + mp * kp;
@@ -627,12 +665,19 @@ int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
         F16Args a{A16, B16t, C, kp / cfg.bk, ldc, static_cast<int>(M), static_cast<int>(N), alpha,
                   beta, tiles_m, tiles_n};
         a.C16 = C16;
+        if (q > 0) {
+            a.sk_q = static_cast<int>(q);
+            a.sk_dp = static_cast<int>(sk.dp);
+            a.sk_grid = static_cast<int>(sk.grid);
+            a.P = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + packed_bytes);
+            a.counts = counts;
+        }
         if (log_debug())
-            std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=%s%s\n",
+            std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=%s%s run %lld\n",
                          layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
                          (long long)K, format_config(cfg).c_str(),
                          ((M % cfg.bm) || (N % cfg.bn)) ? "masked-store" : "aligned",
-                         C16 ? " f16-out" : "");
+                         C16 ? " f16-out" : "", (long long)q);
         return status_of(t[i].launch(a, s));
     }
     return GEMM355_ERR_CONFIG;

@@ -71,17 +71,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) 
     const int h = lane >> 5, r32 = lane & 31;
     const int nkt = p.K / S::BK;   // panels of a whole tile
 
-    // Work of this workgroup: one whole tile, or (stream-K) the run of
-    // (tile, panel) units [u, u_end), workgroups numbered so that the runs
-    // of one XCD are consecutive.
+    // Work of this workgroup: one whole tile, or (stream-K) sk_dp whole tiles
+    // and then the run of (tile, panel) units [u, u_end) of the remaining
+    // tiles, workgroups numbered so that the runs of one XCD are consecutive.
     constexpr bool sk = SK;   // the host sets p.sk_q > 0 exactly for SK launches
     const int tiles = p.tiles_m * p.tiles_n;
-    int g = 0, u = 0, u_end = 0;
+    const int dp_tiles = sk ? p.sk_dp * gridDim.x : 0;
+    int g = 0, u = 0, u_end = 0, r = 0;
     if constexpr (sk) {
         const int G = gridDim.x, xcd = blockIdx.x & 7, q8 = G >> 3, r8 = G & 7;
         g = xcd * q8 + (xcd < r8 ? xcd : r8) + (blockIdx.x >> 3);
         u = g * p.sk_q;
-        u_end = min(tiles * nkt, u + p.sk_q);
+        u_end = min((tiles - dp_tiles) * nkt, u + p.sk_q);
     }
 
     auto stage_of = [&](int i) __attribute__((always_inline)) -> unsigned char* {
@@ -95,22 +96,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) 
 
     for (;;) {
         int tm, tn, kp0, nk;
+        bool dp_item = false;
         if constexpr (!sk) {
             tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM, tm, tn);
             kp0 = 0;
             nk = nkt;
+        } else if (r < p.sk_dp) {
+            tile_of_block(r * gridDim.x + blockIdx.x, dp_tiles, p.tiles_m, p.tiles_n, GM, tm, tn);
+            kp0 = 0;
+            nk = nkt;
+            dp_item = true;
         } else {
             if (u >= u_end) break;
             const int t = u / nkt;
             kp0 = u - t * nkt;
             nk = min(nkt - kp0, u_end - u);
-            // tile t in groups of GM tile rows, column by column in a group
-            const int per_group = GM * p.tiles_n;
-            const int group = t / per_group, first_m = group * GM;
-            const int rows = min(p.tiles_m - first_m, GM);
-            const int in_group = t - group * per_group;
-            tm = first_m + in_group % rows;
-            tn = in_group / rows;
+            raster_tile(dp_tiles + t, p.tiles_m, p.tiles_n, GM, tm, tn);
         }
         const int m0 = tm * BM, n0 = tn * BN;
         const int k_lo = kp0 * S::BK;
@@ -299,7 +300,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) 
             store_tile<FM, FN, false>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N,
                                       p.alpha, p.beta, lane);
         if constexpr (!sk) break;
-        u += nk;
+        if (dp_item) ++r;
+        else u += nk;
         ring_barrier();   // every wave is done with the ring before the next run refills it
     }
 }
@@ -327,13 +329,13 @@ hipError_t launch_f32_ring(const F32Args& a, F32Variant v, hipStream_t s) {
         if (v.ta || v.tb) return launch_f32_transposed<BM, BN, 16, 2, 2, GM>(a, v, s);
         return launch_f32_layout<BM, BN, 16, 2, 2, GM, false, false>(a, v, s);
     }
-    const int64_t units = int64_t{a.tiles_m} * a.tiles_n * (a.K / 16);
-    if (a.sk_q > 0 && (!a.P || !a.counts || units > 0x7fffffff))
-        return hipErrorInvalidValue;
     const dim3 block(WM * WN * 64);
-    if (a.sk_q > 0)
-        gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM, true>
-            <<<dim3(static_cast<unsigned>((units + a.sk_q - 1) / a.sk_q)), block, 0, s>>>(a);
+    if (a.sk_q > 0) {
+        const int grid = ring_sk_grid(int64_t{a.tiles_m} * a.tiles_n, a.K / 16, a.sk_q, a.sk_dp,
+                                      a.sk_grid, a.P, a.counts);
+        if (grid <= 0) return hipErrorInvalidValue;
+        gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM, true><<<dim3(grid), block, 0, s>>>(a);
+    }
     else
         gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM, false>
             <<<dim3(static_cast<unsigned>(a.tiles_m * a.tiles_n)), block, 0, s>>>(a);

@@ -44,14 +44,17 @@ struct F32Args {
     int tiles_m, tiles_n;
     int ksplit = 0;   // k per slice (multiple of BK); 0 = no split
     // The f32 ring only (gemm_f32_ring.hip): with sk_q > 0 the launch is a
-    // stream-K one.  The (tile, 16-deep panel) units of the call, tile-major,
-    // are dealt in runs of sk_q to the workgroups (grid = ceil(units / sk_q));
-    // a tile whose panels span several runs is finished by the last of its
-    // workgroups to arrive (counted in counts[tile], zero before and after
-    // the launch), which adds the partial tiles the others stored in P (two
-    // BM x BN slots per workgroup, gridDim.x x 2 x BM x BN floats, below 2^31
-    // bytes) in k order.
-    int sk_q = 0;
+    // data-parallel + stream-K one.  Its G workgroups first take sk_dp whole
+    // rounds of tiles (round r: the tile of block id r*G + blockIdx.x in the
+    // usual order over the first sk_dp*G raster positions, G a multiple of
+    // 8); the (tile, 16-deep panel) units of the remaining tiles, tile-major
+    // in raster order, are then dealt in runs of sk_q.  A tile whose panels
+    // span several runs is finished by the last of its workgroups to arrive
+    // (counted in counts[tile - sk_dp*G], zero before and after the launch),
+    // which adds the partial tiles the others stored in P (two BM x BN slots
+    // per workgroup, G x 2 x BM x BN floats, below 2^31 bytes) in k order.
+    // G = sk_grid.
+    int sk_q = 0, sk_dp = 0, sk_grid = 0;
     float* P = nullptr;
     unsigned* counts = nullptr;
 };
@@ -70,6 +73,11 @@ struct F16Args {
     float alpha, beta;
     int tiles_m, tiles_n;
     uint16_t* C16 = nullptr;   // binary16 output (then C is unused): the f16-output variant
+    // The half-depth ring only: data-parallel rounds and stream-K runs as in
+    // F32Args (P: gridDim.x x 2 x BM x BN floats; counts: one per tile).
+    int sk_q = 0, sk_dp = 0, sk_grid = 0;
+    float* P = nullptr;
+    unsigned* counts = nullptr;
 };
 
 // Which variant of a compiled configuration a launch needs.
@@ -80,6 +88,19 @@ struct F32Variant {
     bool tb = false;   // op(B) = B^T: B is stored N x K
     bool r16 = false;  // round A and B to binary16 (RNE) on load: the f16r mode
 };
+
+// The grid of a stream-K ring launch (F32Args / F16Args sk_*), checked: every
+// unit of the tiles left after the data-parallel rounds lies in some run, the
+// rounds use whole XCD groups of workgroups, the buffers are there.  0 when
+// the arguments do not describe such a launch.
+inline int ring_sk_grid(int64_t tiles, int64_t nkt, int q, int dp, int grid, const void* P,
+                        const void* counts) {
+    if (q <= 0 || dp < 0 || grid <= 0 || !P || !counts) return 0;
+    if (dp > 0 && (grid % 8 != 0 || int64_t{dp} * grid > tiles)) return 0;
+    const int64_t rest = (tiles - int64_t{dp} * grid) * nkt;
+    if (tiles * nkt >= (int64_t{1} << 31) || rest > int64_t{grid} * q) return 0;
+    return grid;
+}
 
 // Whether a call with ring configuration cfg runs the f32 ring (whole tiles
 // of the plain layout, 16-byte aligned rows, K a multiple of 16, no split-K
@@ -193,18 +214,25 @@ hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t 
 // each XCD one contiguous run of the rasterised order, so the tiles that
 // share an XCD's L2 also share A rows and B columns.  Within the run, tiles
 // go down GM tile rows before moving one tile column right.
+// Position pos of the rasterised tile order: groups of gm tile rows, column
+// by column inside a group.
+__device__ __forceinline__ void raster_tile(int pos, int tiles_m, int tiles_n, int gm, int& tm,
+                                            int& tn) {
+    const int per_group = gm * tiles_n;
+    const int group = pos / per_group;
+    const int first_m = group * gm;
+    const int rows = min(tiles_m - first_m, gm);
+    const int in_group = pos - group * per_group;
+    tm = first_m + in_group % rows;
+    tn = in_group / rows;
+}
+
 __device__ __forceinline__ void tile_of_block(int g, int G, int tiles_m, int tiles_n, int gm,
                                               int& tm, int& tn) {
     const int xcd = g & 7;
     const int q = G >> 3, r = G & 7;
     const int gg = xcd * q + (xcd < r ? xcd : r) + (g >> 3);
-    const int per_group = gm * tiles_n;
-    const int group = gg / per_group;
-    const int first_m = group * gm;
-    const int rows = min(tiles_m - first_m, gm);
-    const int in_group = gg - group * per_group;
-    tm = first_m + in_group % rows;
-    tn = in_group / rows;
+    raster_tile(gg, tiles_m, tiles_n, gm, tm, tn);
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -514,3 +514,48 @@ def test_ring_split_graph_capture_replays():
             torch.cuda.synchronize()
             assert torch.equal(tC, eager)
     assert_parity("f32", A, B, C, 1.25, 0.5, tC.cpu().numpy())
+
+
+# ---------------------------------------------------------------------------
+# The f16r half-depth ring takes the stream-K form when whole rounds of
+# tiles leave CUs idle (not with 128 x 128 wave tiles).
+# ---------------------------------------------------------------------------
+F16_RINGS = [c for c in g.list_configs("f16r")
+             if "BK=32" in c and "KS=" not in c and "BM=256 BN=256 BK=32 ST=5 WM=2 WN=2" not in c]
+
+
+@pytest.mark.parametrize("cfg", F16_RINGS)
+@pytest.mark.parametrize("M,N,K,full", [(1024, 4096, 4096, True), (1000, 3000, 2000, True),
+                                        (3072, 3072, 3072, False)])
+def test_f16_ring_stream_k_against_the_oracle(cfg, M, N, K, full):
+    A, B, C = make_inputs(M, N, K, "normal", seed=41)
+    with pinned("f16r", cfg):
+        say(f"[f16 ring stream-K] {cfg} {M}x{N}x{K}")
+        got = run("f16r", A, B, C, 0.75, -0.25)
+        again = run("f16r", A, B, C, 0.75, -0.25)
+    if full:
+        assert_parity("f16r", A, B, C, 0.75, -0.25, got)
+    else:
+        assert_sampled("f16r", A, B, C, 0.75, -0.25, got)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))   # parts added in k order
+
+
+@pytest.mark.parametrize("cfg", F16_RINGS[:1] + F16_RINGS[-1:])
+def test_f16_ring_stream_k_small_integers_and_f16_output(cfg):
+    M, N, K = 512, 2048, 4096
+    A, B, C = small_integers(M, N, K, seed=42)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned("f16r", cfg):
+        say(f"[f16 ring stream-K exact] {cfg} {M}x{N}x{K}")
+        got = run("f16r", A, B, C, -2.0, 0.5)
+        assert np.array_equal(got, (-2.0 * exact + 0.5 * C.astype(np.float64)).astype(np.float32))
+        A2, B2, C2 = make_inputs(M, N, K, "normal", seed=43)
+        C16 = C2.astype(np.float16)
+        tA, tB = to_device(A2), to_device(B2)
+        t16 = torch.from_numpy(C16.copy()).to("cuda")
+        t32 = to_device(C16.astype(np.float32))
+        g.gemm_f16r_f16out(tA, tB, t16, 0.75, -0.25)
+        g.gemm("f16r", tA, tB, t32, 0.75, -0.25)
+        torch.cuda.synchronize()
+    want = t32.cpu().numpy().astype(np.float16)
+    assert np.array_equal(t16.cpu().numpy().view(np.uint16), want.view(np.uint16))
