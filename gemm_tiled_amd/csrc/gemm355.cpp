@@ -262,11 +262,45 @@ RingSk ring_sk(const TileConfig& c, int64_t M, int64_t N, int64_t K) {
     return out;
 }
 
+// Estimated time of configuration c on an M x N x K call (arbitrary units):
+// rounds of workgroups over 256 CUs (two per CU for tiles under 256 x 128)
+// times the work of a tile, over the reuse efficiency r / (r + 6.5) of the
+// tile, r = BM BN / (BM + BN).  A ring call on whole tiles deals its work in
+// equal runs when whole rounds would leave CUs idle (stream-K, counted by
+// the panels of a slot plus the partial sums' overhead) and stages its
+// panels faster than the register-staged kernel (10-20% measured, counted as
+// 20%); a ragged ring call is its whole-tile block plus the strips (64 x 64).
+// vec: the plain layout with 16-byte aligned rows, which the f32 ring needs
+// (otherwise a ring configuration runs the register-staged kernel).
+double estimated_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, bool vec) {
+    const bool ring = vec && is_f32_ring(c) && M % c.bm == 0 && N % c.bn == 0 && K % 16 == 0;
+    if (vec && is_f32_ring(c) && !ring) {
+        const int64_t M0 = M / c.bm * c.bm, N0 = N / c.bn * c.bn, K16 = K / 16 * 16;
+        if (M0 > 0 && N0 > 0 && K16 > 0 && 4 * M0 * N0 >= 3 * M * N) {
+            TileConfig edge = c;
+            edge.bm = edge.bn = 64;
+            edge.st = 2;   // the register-staged tile (costed only)
+            double cost = estimated_cost(c, M0, N0, K16, vec);
+            if (N0 < N) cost += estimated_cost(edge, M, N - N0, K, vec);
+            if (M0 < M) cost += estimated_cost(edge, M - M0, N0, K, vec);
+            return cost;
+        }
+    }
+    const double tiles = static_cast<double>((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    const double per_cu = (c.bm * c.bn >= 256 * 128) ? 1.0 : 2.0;
+    const RingSk sk = ring || is_f16_ring(c) ? ring_sk(c, M, N, K) : RingSk{};
+    const double kpad = static_cast<double>(round_up(K, c.bk));
+    const double rounds = sk.q > 0 ? sk.panels / (kpad / c.bk) : std::ceil(tiles / (256.0 * per_cu));
+    const double reuse = static_cast<double>(c.bm) * c.bn / (c.bm + c.bn);   // flop per loaded element
+    const double eff = reuse / (reuse + 6.5) * (ring ? 1.2 : 1.0);
+    return rounds * per_cu * c.bm * c.bn * kpad / eff;
+}
+
 // Heuristic when nothing is pinned or tuned: estimate the time of each
 // instance as (rounds of workgroups over 256 CUs) x (work per tile) / (reuse
 // efficiency of the tile), the trade-off of the phobos "Tuning" section:
 // larger tiles reuse more, but leave fewer workgroups to fill the chip.
-TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K) {
+TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, bool vec) {
     // a few rows of C (memory-bound, too few tiles): the few-rows
     // configuration up to one 16-row group, then the split-K tiles
     if (M <= kRowsRows) return rows_config(mode);
@@ -284,19 +318,7 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K) {
     TileConfig pick = all.front();
     for (const TileConfig& c : all) {
         if (c.ks) continue;
-        const double tiles = static_cast<double>((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-        const double per_cu = (c.bm * c.bn >= 256 * 128) ? 1.0 : 2.0;
-        // a ring call on whole tiles deals its work in equal runs when whole
-        // rounds would leave CUs idle (stream-K, runs counted in panels plus
-        // the partial sums' overhead); it also stages its panels faster than
-        // the register-staged kernel (10-20% measured, counted as 20%)
-        const bool ring = is_f32_ring(c) && M % c.bm == 0 && N % c.bn == 0 && K % 16 == 0;
-        const RingSk sk = ring || is_f16_ring(c) ? ring_sk(c, M, N, K) : RingSk{};
-        const double kpad = static_cast<double>(round_up(K, c.bk));
-        const double rounds = sk.q > 0 ? sk.panels / (kpad / c.bk) : std::ceil(tiles / (256.0 * per_cu));
-        const double reuse = static_cast<double>(c.bm) * c.bn / (c.bm + c.bn);   // flop per loaded element
-        const double eff = reuse / (reuse + 6.5) * (ring ? 1.2 : 1.0);
-        const double cost = rounds * per_cu * c.bm * c.bn * kpad / eff;
+        const double cost = estimated_cost(c, M, N, K, vec);
         if (cost < best * 0.999) {
             best = cost;
             pick = c;
@@ -326,7 +348,7 @@ int select_config(int mode, int trans, int64_t M, int64_t N, int64_t K, const fl
         *src = Source::Tuned;
         return 0;
     }
-    *out = heuristic(mode, M, N, K);
+    *out = heuristic(mode, M, N, K, trans == 0 && vec_ok(A, lda) && vec_ok(B, ldb));
     *src = Source::Heuristic;
     return 0;
 }
@@ -600,6 +622,38 @@ int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
         return launch_direct(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
     if (cfg.ks)
         return launch_splitk(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
+    if (is_f32_ring(cfg) && trans == 0 && vec_ok(A, lda) && vec_ok(B, ldb)) {
+        // A ragged call of a ring configuration: the ring takes the block of
+        // whole tiles [0, M0) x [0, N0) over the first K16 = K - K % 16 k, when
+        // that block holds at least 3/4 of C; the register-staged 64 x 64 tile
+        // adds the k tail to that block (beta = 1), and the right and bottom
+        // strips go to the configuration of their shape: the few-rows one for
+        // up to 16 rows, split-K tiles for a thin strip (a strip of few
+        // columns is a long K loop per tile, so it needs K split), else the
+        // 64 x 64 tile.
+        const int64_t M0 = M / cfg.bm * cfg.bm, N0 = N / cfg.bn * cfg.bn, K16 = K / 16 * 16;
+        const bool whole = M0 == M && N0 == N && K16 == K;
+        if (!whole && M0 > 0 && N0 > 0 && K16 > 0 && 4 * M0 * N0 >= 3 * M * N) {
+            TileConfig edge;
+            if (!parse_config(cfg.mode, "BM=64 BN=64 BK=16 ST=2", &edge)) return GEMM355_ERR_CONFIG;
+            auto strip = [&](int64_t rows, int64_t cols) {
+                if (rows <= kRowsRows) return rows_config(cfg.mode);
+                if (rows <= 128 || cols <= 128) return splitk_config(cfg.mode);
+                return edge;
+            };
+            int rc = launch_with(cfg, 0, M0, N0, K16, alpha, A, lda, B, ldb, beta, C, ldc, s, nullptr);
+            if (rc == 0 && K16 < K)
+                rc = launch_with(edge, 0, M0, N0, K - K16, alpha, A + K16, lda, B + K16 * ldb, ldb,
+                                 1.0f, C, ldc, s, nullptr);
+            if (rc == 0 && N0 < N)
+                rc = launch_with(strip(M, N - N0), 0, M, N - N0, K, alpha, A, lda, B + N0, ldb, beta,
+                                 C + N0, ldc, s, nullptr);
+            if (rc == 0 && M0 < M)
+                rc = launch_with(strip(M - M0, N0), 0, M - M0, N0, K, alpha, A + M0 * lda, lda, B, ldb,
+                                 beta, C + M0 * ldc, ldc, s, nullptr);
+            return rc;
+        }
+    }
     const int tiles_m = static_cast<int>((M + cfg.bm - 1) / cfg.bm);
     const int tiles_n = static_cast<int>((N + cfg.bn - 1) / cfg.bn);
     if (cfg.mode == GEMM355_MODE_F32) {

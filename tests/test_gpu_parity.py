@@ -559,3 +559,43 @@ def test_f16_ring_stream_k_small_integers_and_f16_output(cfg):
         torch.cuda.synchronize()
     want = t32.cpu().numpy().astype(np.float16)
     assert np.array_equal(t16.cpu().numpy().view(np.uint16), want.view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# A ragged call of an f32 ring configuration: the ring takes the block of
+# whole tiles over K rounded down to 16, the register-staged tile the k tail
+# and the right and bottom strips.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", RINGS)
+@pytest.mark.parametrize("M,N,K,full", [(1000, 1030, 1000, True), (2100, 2090, 2070, True),
+                                        (4097, 4097, 4097, False)])
+def test_ring_ragged_decomposition(cfg, M, N, K, full):
+    A, B, C = make_inputs(M, N, K, "normal", seed=51)
+    with pinned("f32", cfg):
+        say(f"[ring ragged] {cfg} {M}x{N}x{K}")
+        got = run("f32", A, B, C, 1.25, -0.5)
+        again = run("f32", A, B, C, 1.25, -0.5)
+    if full:
+        assert_parity("f32", A, B, C, 1.25, -0.5, got)
+    else:
+        assert_sampled("f32", A, B, C, 1.25, -0.5, got)
+        # whole rows (every column, the right strip's too) at the edges of
+        # the parts: the first rows, both sides of row 3840 and of 4096
+        for band in [(0, 2), (254, 258), (3838, 3842), (4094, 4097)]:
+            st = oracle.check("f32", A, B, C, 1.25, -0.5, got, rows=band)
+            assert st["n_fail"] == 0, (band, st)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+
+
+@pytest.mark.parametrize("cfg", RINGS[:1] + RINGS[-1:])
+def test_ring_ragged_small_integers_exact_and_beta_zero(cfg):
+    M, N, K = 1000, 1030, 1000
+    A, B, C = small_integers(M, N, K, seed=52)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned("f32", cfg):
+        say(f"[ring ragged exact] {cfg} {M}x{N}x{K}")
+        got = run("f32", A, B, C, -2.0, 0.5)
+        assert np.array_equal(got, (-2.0 * exact + 0.5 * C.astype(np.float64)).astype(np.float32))
+        Cn = np.full((M, N), np.nan, dtype=np.float32)
+        got = run("f32", A, B, Cn, 1.0, 0.0)
+        assert np.array_equal(got, exact.astype(np.float32))
