@@ -567,10 +567,15 @@ def test_f16_ring_stream_k_small_integers_and_f16_output(cfg):
 # and the right and bottom strips.
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg", RINGS)
-@pytest.mark.parametrize("M,N,K,full", [(1000, 1030, 1000, True), (2100, 2090, 2070, True),
-                                        (4097, 4097, 4097, False)])
-def test_ring_ragged_decomposition(cfg, M, N, K, full):
-    A, B, C = make_inputs(M, N, K, "normal", seed=51)
+@pytest.mark.parametrize("M,N,K,full,lds", [
+    (1000, 1030, 1000, True, {"lda": 1000, "ldb": 1032, "ldc": 1030}),
+    (2100, 2090, 2070, True, {"lda": 2072, "ldb": 2092, "ldc": 2090}),
+    (4097, 4097, 4097, False, {"lda": 4100, "ldb": 4100, "ldc": 4100}),
+])
+def test_ring_ragged_decomposition(cfg, M, N, K, full, lds):
+    """16-byte aligned rows (lda, ldb % 4 == 0), so the ring takes the block of
+    whole tiles and the strips go to the other configurations."""
+    A, B, C = make_inputs(M, N, K, "normal", seed=51, **lds)
     with pinned("f32", cfg):
         say(f"[ring ragged] {cfg} {M}x{N}x{K}")
         got = run("f32", A, B, C, 1.25, -0.5)
@@ -589,7 +594,7 @@ def test_ring_ragged_decomposition(cfg, M, N, K, full):
 
 @pytest.mark.parametrize("cfg", RINGS[:1] + RINGS[-1:])
 def test_ring_ragged_small_integers_exact_and_beta_zero(cfg):
-    M, N, K = 1000, 1030, 1000
+    M, N, K = 1000, 1032, 1000     # N % 4 == 0: B's rows 16-byte aligned
     A, B, C = small_integers(M, N, K, seed=52)
     exact = A.astype(np.float64) @ B.astype(np.float64)
     with pinned("f32", cfg):
