@@ -405,7 +405,15 @@ def _path_of(mode, n, tile):
     """Which variant a square n^3 call with this tile runs (dense, 16-byte aligned rows)."""
     t = _tile_fields(tile)
     if mode == "f32":
+        if t.get("KS"):
+            return "split" if n % 4 else "split, 16-byte rows"
         ragged = n % t["BM"] or n % t["BN"] or n % t["BK"]
+        ring = t["BK"] == 16 and t["ST"] >= 3
+        if ring and ragged and n % 4 == 0 and n >= t["BM"] and n >= t["BN"]:
+            # the ring on the block of whole tiles, the strips on other tiles
+            m0, n0 = n // t["BM"] * t["BM"], n // t["BN"] * t["BN"]
+            if 4 * m0 * n0 >= 3 * n * n:
+                return "ring block + strips"
         return ("masked" if ragged else "aligned") + ("" if n % 4 == 0 else ", rows 4-byte aligned")
     return "masked store" if (n % t["BM"] or n % t["BN"]) else "aligned"
 
