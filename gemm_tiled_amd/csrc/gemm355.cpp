@@ -395,9 +395,10 @@ hipError_t workspace(hipStream_t s, size_t bytes, void** out) {
     return hipSuccess;
 }
 
-// Arrival counters of the few-rows configuration: one zeroed buffer per
-// (device, stream), grown on demand (zeroed again when it grows).  The kernel
-// leaves every counter it uses at zero.
+// Arrival counters of the configurations that split K over workgroups (few
+// rows, round-on-load, stream-K rings): one zeroed buffer per (device,
+// stream), grown on demand (zeroed again when it grows).  Every kernel leaves
+// each counter it uses at zero.
 std::map<WsKey, Ws> g_counts;
 
 hipError_t counters(hipStream_t s, size_t n, unsigned** out) {

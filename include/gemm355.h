@@ -23,10 +23,14 @@
  * Execution:
  *   - the work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and the call returns without waiting for it;
- *   - the f16r mode writes the rounded operands into a device workspace that
- *     the library allocates on first use and keeps per (device, stream); calls
- *     on one stream are ordered and share it; calls on different streams use
- *     different workspaces;
+ *   - the f16r mode writes the rounded operands, and configurations that
+ *     split K over workgroups (both modes) write partial tiles and per-tile
+ *     arrival counters, into a device workspace that the library allocates on
+ *     first use, grows when a call needs more (synchronising the stream
+ *     first), and keeps per (device, stream);
+ *     calls on one stream are ordered and share it; calls on different
+ *     streams use different workspaces; each launch leaves the counters it
+ *     used at zero;
  *   - every call is thread-safe.
  *
  * Special cases, decided on the host before any launch:
@@ -163,8 +167,17 @@ int gemm355_get_config_ex(int mode, int transa, int transb, int64_t M, int64_t N
  * Pin one tile configuration for every later call of `mode`, skipping the
  * search (phobos docs, "gemm, f32", section "Tuning", the pinned run).
  * Grammar: space-separated KEY=VALUE with keys BM|TILE_M, BN|TILE_N,
- * BK|TILE_K, ST|STAGES, WM, WN, GM; omitted keys take the first compiled instance that
- * matches the given ones.  NULL or "" clears the pin.  The environment
+ * BK|TILE_K, ST|STAGES, WM, WN, GM, KS|SPLITK; omitted keys take the first compiled
+ * instance that matches the given ones, except KS, whose absence selects the
+ * tiled configurations (KS=0).  KS=1: K split over workgroups, partial tiles
+ * summed by a second pass; KS=2: one wavefront per few rows of C; KS=3 (f16r
+ * only): the operands rounded to binary16 as they are staged (BK=64 through
+ * registers, BK=16 from a ring of f32 panels), K split over workgroups and
+ * the slices added in order by the tile's last workgroup, with no packing
+ * pass.  A ring configuration (direct-to-LDS copies) that a call's row
+ * alignment or shape rules out runs that call in a register-staged kernel
+ * instead: the f32 one of the same tile, or BM=64 BN=64 BK=64 KS=3 in f16r.
+ * NULL or "" clears the pin.  The environment
  * variables GEMM355_CONFIG_F32 / GEMM355_CONFIG_F16R set the initial pin.
  * Returns 0 or GEMM355_ERR_CONFIG (the pin is then unchanged).  Host only.
  */
