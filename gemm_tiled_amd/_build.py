@@ -24,7 +24,7 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
     # no packed f32 instructions on the device (the host pass warns it does not know the feature)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wshadow", "-Wno-unused-function",
 ]
 
 

@@ -221,6 +221,19 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // kRingSkOverhead panels for the split tiles' partial sums.  Runs that start
 // at different depths of their tiles share no operand panels in the cache,
 // which is why the remaining tiles alone are dealt this way.
+// What the f32 ring can take of a call: nothing (transposed operands, or
+// leading dimensions too large for the masked copies' 32-bit offsets), any
+// shape through its masked form, or also whole tiles unmasked (16-byte
+// aligned rows).
+enum class RingRows { None, Any, Aligned };
+RingRows ring_rows(int trans, const float* A, int64_t lda, const float* B, int64_t ldb) {
+    if (trans != 0 || lda >= (int64_t{1} << 20) || ldb >= (int64_t{1} << 24)) return RingRows::None;
+    return vec_ok(A, lda) && vec_ok(B, ldb) ? RingRows::Aligned : RingRows::Any;
+}
+// The masked ring's rate relative to the unmasked one (4-byte copies, rows
+// not 16-byte aligned): 4095^3 129 TFLOP/s against 145 for 4096^3.
+constexpr double kRingMaskedRate = 0.89;
+
 bool is_f32_ring(const TileConfig& c) {
     return c.mode == GEMM355_MODE_F32 && c.bk == 16 && c.st >= 3 && c.ks == 0;
 }
@@ -236,7 +249,7 @@ struct RingSk {
 RingSk ring_sk(const TileConfig& c, int64_t M, int64_t N, int64_t K) {
     RingSk out;
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    const int64_t nkt = c.mode == GEMM355_MODE_F32 ? K / 16 : round_up(K, 64) / 32;
+    const int64_t nkt = c.mode == GEMM355_MODE_F32 ? (K + 15) / 16 : round_up(K, 64) / 32;
     // LDS of one workgroup: NS stages of BM x BK A rows and BK x BN B values
     // (f32 B rows padded by 16 bytes), binary16 or f32
     const int64_t lds = c.mode == GEMM355_MODE_F32
@@ -262,45 +275,88 @@ RingSk ring_sk(const TileConfig& c, int64_t M, int64_t N, int64_t K) {
     return out;
 }
 
-// Estimated time of configuration c on an M x N x K call (arbitrary units):
-// rounds of workgroups over 256 CUs (two per CU for tiles under 256 x 128)
-// times the work of a tile, over the reuse efficiency r / (r + 6.5) of the
-// tile, r = BM BN / (BM + BN).  A ring call on whole tiles deals its work in
-// equal runs when whole rounds would leave CUs idle (stream-K, counted by
-// the panels of a slot plus the partial sums' overhead) and stages its
-// panels faster than the register-staged kernel (10-20% measured, counted as
-// 20%); a ragged ring call is its whole-tile block plus the strips (64 x 64).
-// vec: the plain layout with 16-byte aligned rows, which the f32 ring needs
-// (otherwise a ring configuration runs the register-staged kernel).
-double estimated_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, bool vec) {
-    const bool ring = vec && is_f32_ring(c) && M % c.bm == 0 && N % c.bn == 0 && K % 16 == 0;
-    if (vec && is_f32_ring(c) && !ring) {
-        const int64_t M0 = M / c.bm * c.bm, N0 = N / c.bn * c.bn, K16 = K / 16 * 16;
-        if (M0 > 0 && N0 > 0 && K16 > 0 && 4 * M0 * N0 >= 3 * M * N) {
-            TileConfig edge = c;
-            edge.bm = edge.bn = 64;
-            edge.st = 2;   // the register-staged tile (costed only)
-            double cost = estimated_cost(c, M0, N0, K16, vec);
-            if (N0 < N) cost += estimated_cost(edge, M, N - N0, K, vec);
-            if (M0 < M) cost += estimated_cost(edge, M - M0, N0, K, vec);
-            return cost;
-        }
-    }
+// Estimated time of configuration c on an M x N x K call run whole
+// (arbitrary units): rounds of workgroups over 256 CUs (two per CU for tiles
+// under 256 x 128) times the work of a tile, over the reuse efficiency r /
+// (r + 6.5) of the tile, r = BM BN / (BM + BN).  An f32 ring call deals its
+// work in equal runs when whole rounds would leave CUs idle (stream-K,
+// counted by the panels of a slot plus the partial sums' overhead) and stages
+// its panels faster than the register-staged kernel (10-20% measured, counted
+// as 20%), the masked form at kRingMaskedRate of that.
+double whole_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, RingRows rows) {
+    const bool ring = is_f32_ring(c) && rows != RingRows::None;
+    const bool whole = rows == RingRows::Aligned && M % c.bm == 0 && N % c.bn == 0 && K % 16 == 0;
     const double tiles = static_cast<double>((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
     const double per_cu = (c.bm * c.bn >= 256 * 128) ? 1.0 : 2.0;
     const RingSk sk = ring || is_f16_ring(c) ? ring_sk(c, M, N, K) : RingSk{};
     const double kpad = static_cast<double>(round_up(K, c.bk));
     const double rounds = sk.q > 0 ? sk.panels / (kpad / c.bk) : std::ceil(tiles / (256.0 * per_cu));
     const double reuse = static_cast<double>(c.bm) * c.bn / (c.bm + c.bn);   // flop per loaded element
-    const double eff = reuse / (reuse + 6.5) * (ring ? 1.2 : 1.0);
+    const double eff =
+        reuse / (reuse + 6.5) * (ring ? 1.2 * (whole ? 1.0 : kRingMaskedRate) : 1.0);
     return rounds * per_cu * c.bm * c.bn * kpad / eff;
+}
+
+// The configuration of a strip left over by a split ring call (RingBlock):
+// the few-rows one for up to 16 rows, split-K tiles for a thin strip (a strip
+// of few columns is a long K loop per tile, so it needs K split), else the
+// register-staged 64 x 64 tile.  Its cost in the units of whole_cost: a thin
+// strip its share of the chip's rounds, a wide one whole rounds of 64 x 64
+// tiles.
+TileConfig strip_config(int mode, int64_t rows, int64_t cols) {
+    if (rows <= kRowsRows) return rows_config(mode);
+    if (rows <= 128 || cols <= 128) return splitk_config(mode);
+    TileConfig edge;
+    parse_config(mode, "BM=64 BN=64 BK=16 ST=2", &edge);
+    return edge;
+}
+double strip_cost(int64_t rows, int64_t cols, int64_t k) {
+    const double tiles = static_cast<double>((rows + 63) / 64) * ((cols + 63) / 64);
+    const double rounds = rows <= 128 || cols <= 128 ? tiles / 512.0 : std::ceil(tiles / 512.0);
+    return rounds * 2.0 * 64 * 64 * static_cast<double>(round_up(k, 16)) / (32.0 / 38.5);
+}
+
+// The part of a ragged call that an f32 ring configuration runs itself: the
+// block [0, mb) x [0, nb) of C over k in [0, kb); the right strip [0, M) x
+// [nb, N), the bottom strip [mb, M) x [0, nb) and the k tail of the block go
+// to strip configurations.  Candidates: the whole call (masked ring, or the
+// unmasked one on whole tiles), the call without its last partial tile row,
+// column or both (that partial tile can cost a whole extra round or a share
+// of stream-K runs), and with 16-byte aligned rows the block of whole tiles
+// over K rounded down to 16 (the unmasked ring).  The cheapest by whole_cost
+// + strip_cost wins, the whole call on a near tie.
+struct RingBlock {
+    int64_t mb, nb, kb;
+    double cost;
+};
+RingBlock ring_block(const TileConfig& c, RingRows rows, int64_t M, int64_t N, int64_t K) {
+    RingBlock best{M, N, K, whole_cost(c, M, N, K, rows)};
+    if (!is_f32_ring(c) || rows == RingRows::None) return best;
+    const int64_t M0 = M / c.bm * c.bm, N0 = N / c.bn * c.bn, K16 = K / 16 * 16;
+    auto consider = [&](int64_t mb, int64_t nb, int64_t kb) {
+        if (mb <= 0 || nb <= 0 || kb <= 0 || (mb == M && nb == N && kb == K)) return;
+        double cost = whole_cost(c, mb, nb, kb, rows);
+        if (nb < N) cost += strip_cost(M, N - nb, K);
+        if (mb < M) cost += strip_cost(M - mb, nb, K);
+        if (kb < K) cost += strip_cost(mb, nb, K - kb);
+        if (cost < 0.99 * best.cost) best = RingBlock{mb, nb, kb, cost};
+    };
+    consider(M0, N, K);
+    consider(M, N0, K);
+    consider(M0, N0, K);
+    if (rows == RingRows::Aligned) consider(M0, N0, K16);
+    return best;
+}
+
+double estimated_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, RingRows rows) {
+    return ring_block(c, rows, M, N, K).cost;
 }
 
 // Heuristic when nothing is pinned or tuned: estimate the time of each
 // instance as (rounds of workgroups over 256 CUs) x (work per tile) / (reuse
 // efficiency of the tile), the trade-off of the phobos "Tuning" section:
 // larger tiles reuse more, but leave fewer workgroups to fill the chip.
-TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, bool vec) {
+TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
     // a few rows of C (memory-bound, too few tiles): the few-rows
     // configuration up to one 16-row group, then the split-K tiles
     if (M <= kRowsRows) return rows_config(mode);
@@ -318,7 +374,7 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, bool vec) {
     TileConfig pick = all.front();
     for (const TileConfig& c : all) {
         if (c.ks) continue;
-        const double cost = estimated_cost(c, M, N, K, vec);
+        const double cost = estimated_cost(c, M, N, K, rows);
         if (cost < best * 0.999) {
             best = cost;
             pick = c;
@@ -348,7 +404,7 @@ int select_config(int mode, int trans, int64_t M, int64_t N, int64_t K, const fl
         *src = Source::Tuned;
         return 0;
     }
-    *out = heuristic(mode, M, N, K, trans == 0 && vec_ok(A, lda) && vec_ok(B, ldb));
+    *out = heuristic(mode, M, N, K, ring_rows(trans, A, lda, B, ldb));
     *src = Source::Heuristic;
     return 0;
 }
@@ -614,46 +670,39 @@ int launch_direct(const TileConfig& cfg_in, int trans, int64_t M, int64_t N, int
     return status_of(inst->launch(a, ta, tb, masked, s));
 }
 
+// whole_call: run the call as one piece (a part of a split call).
 int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
-                int64_t ldc, hipStream_t s, uint16_t* C16) {
+                int64_t ldc, hipStream_t s, uint16_t* C16, bool whole_call = false) {
     if (cfg.ks == 2)
         return launch_rows(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
     if (cfg.ks == 3)
         return launch_direct(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
     if (cfg.ks)
         return launch_splitk(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
-    if (is_f32_ring(cfg) && trans == 0 && vec_ok(A, lda) && vec_ok(B, ldb)) {
-        // A ragged call of a ring configuration: the ring takes the block of
-        // whole tiles [0, M0) x [0, N0) over the first K16 = K - K % 16 k, when
-        // that block holds at least 3/4 of C; the register-staged 64 x 64 tile
-        // adds the k tail to that block (beta = 1), and the right and bottom
-        // strips go to the configuration of their shape: the few-rows one for
-        // up to 16 rows, split-K tiles for a thin strip (a strip of few
-        // columns is a long K loop per tile, so it needs K split), else the
-        // 64 x 64 tile.
-        const int64_t M0 = M / cfg.bm * cfg.bm, N0 = N / cfg.bn * cfg.bn, K16 = K / 16 * 16;
-        const bool whole = M0 == M && N0 == N && K16 == K;
-        if (!whole && M0 > 0 && N0 > 0 && K16 > 0 && 4 * M0 * N0 >= 3 * M * N) {
-            TileConfig edge;
-            if (!parse_config(cfg.mode, "BM=64 BN=64 BK=16 ST=2", &edge)) return GEMM355_ERR_CONFIG;
-            auto strip = [&](int64_t rows, int64_t cols) {
-                if (rows <= kRowsRows) return rows_config(cfg.mode);
-                if (rows <= 128 || cols <= 128) return splitk_config(cfg.mode);
-                return edge;
-            };
-            int rc = launch_with(cfg, 0, M0, N0, K16, alpha, A, lda, B, ldb, beta, C, ldc, s, nullptr);
-            if (rc == 0 && K16 < K)
-                rc = launch_with(edge, 0, M0, N0, K - K16, alpha, A + K16, lda, B + K16 * ldb, ldb,
-                                 1.0f, C, ldc, s, nullptr);
-            if (rc == 0 && N0 < N)
-                rc = launch_with(strip(M, N - N0), 0, M, N - N0, K, alpha, A, lda, B + N0, ldb, beta,
-                                 C + N0, ldc, s, nullptr);
-            if (rc == 0 && M0 < M)
-                rc = launch_with(strip(M - M0, N0), 0, M - M0, N0, K, alpha, A + M0 * lda, lda, B, ldb,
-                                 beta, C + M0 * ldc, ldc, s, nullptr);
-            return rc;
-        }
+    const RingBlock rb = whole_call ? RingBlock{M, N, K, 0.0}
+                                    : ring_block(cfg, ring_rows(trans, A, lda, B, ldb), M, N, K);
+    if (rb.mb < M || rb.nb < N || rb.kb < K) {
+        // A ragged call of a ring configuration split as ring_block chose:
+        // the ring runs the block (unmasked when it is whole tiles with
+        // 16-byte aligned rows), the register-staged 64 x 64 tile adds the k
+        // tail to the block (beta = 1), and the strips go to the
+        // configurations of their shapes.
+        TileConfig edge;
+        if (!parse_config(cfg.mode, "BM=64 BN=64 BK=16 ST=2", &edge)) return GEMM355_ERR_CONFIG;
+        int rc = launch_with(cfg, 0, rb.mb, rb.nb, rb.kb, alpha, A, lda, B, ldb, beta, C, ldc, s,
+                             nullptr, true);
+        if (rc == 0 && rb.kb < K)
+            rc = launch_with(edge, 0, rb.mb, rb.nb, K - rb.kb, alpha, A + rb.kb, lda,
+                             B + rb.kb * ldb, ldb, 1.0f, C, ldc, s, nullptr, true);
+        if (rc == 0 && rb.nb < N)
+            rc = launch_with(strip_config(cfg.mode, M, N - rb.nb), 0, M, N - rb.nb, K, alpha, A, lda,
+                             B + rb.nb, ldb, beta, C + rb.nb, ldc, s, nullptr, true);
+        if (rc == 0 && rb.mb < M)
+            rc = launch_with(strip_config(cfg.mode, M - rb.mb, rb.nb), 0, M - rb.mb, rb.nb, K, alpha,
+                             A + rb.mb * lda, lda, B, ldb, beta, C + rb.mb * ldc, ldc, s, nullptr,
+                             true);
+        return rc;
     }
     const int tiles_m = static_cast<int>((M + cfg.bm - 1) / cfg.bm);
     const int tiles_n = static_cast<int>((N + cfg.bn - 1) / cfg.bn);

@@ -1,5 +1,6 @@
 // gemm_f32_ring.hip -- the f32 GEMM on a ring of direct-to-LDS panels, for
-// whole tiles of row-major A and B with 16-byte aligned rows.
+// row-major A and B: whole tiles with 16-byte aligned rows, or (the masked
+// form) any shape and any leading dimensions.
 //
 // Same computation as gemm_f32_kernel (the phobos "gemm, f32" page: one output
 // tile per workgroup, a K loop over BK-deep panels staged in shared memory,
@@ -20,6 +21,13 @@
 //   B: 16 k-rows of BN = 256 floats (one copy instruction each), rows
 //      1024 + 16 bytes apart: the two lane halves, which read rows 8 apart,
 //      then fall in opposite halves of the 64 banks.
+// The masked form copies 4 bytes a lane through buffer loads (256 bytes per
+// instruction, four times the instructions, which the matrix work hides) into
+// the same layout: A copy j of wave w fills the 4 rows of instruction index
+// w + NW j, B copy j a quarter (256 bytes) of a k-row.  A lane whose element
+// lies past M, N or K gets an out-of-range offset and writes a zero, so both
+// operands are zero-filled at every edge and the epilogue masks its stores.
+//
 // Matrix instructions: lane (h, r32) feeds k = 8h + s in step s (s = 0..7) to
 // A (row r32 of its block) and B (column r32) alike, so every instruction
 // pairs matching k; its A values for steps 4q..4q+3 are one 16-byte read
@@ -39,7 +47,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const f32x4 lds_f32x4c;
 typedef __attribute__((address_space(3))) const float lds_f32c;
 
-template <int BM, int BN, int NS, int WM, int WN>
+template <int BM, int BN, int NS, int WM, int WN, bool MASKED>
 struct F32RingShape {
     static constexpr int BK = 16;
     static constexpr int NW = WM * WN;
@@ -48,20 +56,24 @@ struct F32RingShape {
     static constexpr int A_BYTES = BM * BK * 4;      // rows of 64 bytes
     static constexpr int B_ROW = BN * 4 + 16;        // bytes per padded k-row
     static constexpr int STAGE = A_BYTES + BK * B_ROW;
-    static constexpr int A_INS = BM / 16 / NW;       // copies of 16 A rows per wave per panel
-    static constexpr int B_INS = BK / NW;            // copies of one B k-row per wave per panel
+    // copies per wave per panel: of 16 A rows and one B k-row (1 KB each), or
+    // (masked) of 4 A rows and a quarter k-row (256 bytes each)
+    static constexpr int A_INS = MASKED ? BM / 4 / NW : BM / 16 / NW;
+    static constexpr int B_INS = MASKED ? 4 * BK / NW : BK / NW;
     static constexpr int FILLS = A_INS + B_INS;
-    static_assert(BN == 256, "one k-row of B is one 1 KB copy");
-    static_assert(A_INS >= 1 && A_INS * 16 * NW == BM && B_INS >= 1 && B_INS * NW == BK,
+    static_assert(BN == 256, "one k-row of B is 1 KB");
+    static_assert(A_INS >= 1 && A_INS * NW * (MASKED ? 4 : 16) == BM &&
+                      B_INS >= 1 && B_INS * NW == (MASKED ? 4 : 1) * BK,
                   "copies split evenly over the waves");
+    static_assert(!MASKED || NW % 4 == 0, "masked copies: a wave's A swizzle and B quarter are fixed");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(NS >= 3 && NS * STAGE <= 160 * 1024, "LDS budget of one CU");
     static_assert((NS - 2) * FILLS < 64, "vmcnt range");
 };
 
-template <int BM, int BN, int NS, int WM, int WN, int GM, bool SK>
+template <int BM, int BN, int NS, int WM, int WN, int GM, bool SK, bool MASKED>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) {
-    using S = F32RingShape<BM, BN, NS, WM, WN>;
+    using S = F32RingShape<BM, BN, NS, WM, WN, MASKED>;
     constexpr int FM = S::FM, FN = S::FN;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * S::STAGE];
 
@@ -69,7 +81,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / WN, wc = wave % WN;
     const int h = lane >> 5, r32 = lane & 31;
-    const int nkt = p.K / S::BK;   // panels of a whole tile
+    const int nkt = (p.K + S::BK - 1) / S::BK;   // panels of a tile (the last one short when masked)
 
     // Work of this workgroup: one whole tile, or (stream-K) sk_dp whole tiles
     // and then the run of (tile, panel) units [u, u_end) of the remaining
@@ -126,15 +138,49 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) 
         const int64_t a_step = (int64_t)S::NW * 16 * p.lda;   // next copy of this wave
         const int64_t b_step = (int64_t)S::NW * p.ldb;
         const int64_t b_panel = (int64_t)S::BK * p.ldb;
+        // Masked copies: A copy j fills panel rows 4 (wave + NW j) .. +3, lane
+        // l row 4 (wave + NW j) + l / 16 at word l % 16 of it, which holds k =
+        // 4 ((l % 16) / 4 ^ swz) + l % 4 with swz = (wave + NW j) % 4 = wave % 4.
+        // B copy j fills quarter wave % 4 of k-row wave / 4 + (NW / 4) j, lane
+        // l its float 64 (wave % 4) + l.  Offsets are bytes from the panel's
+        // first element (row m0, column n0, depth k of the panel).
+        const int a_row = 4 * wave + (lane >> 4);
+        const int a_kk = ((((lane & 15) >> 2) ^ (wave & 3)) << 2) | (lane & 3);
+        const uint32_t a_voff = static_cast<uint32_t>(((int64_t)a_row * p.lda + a_kk) * 4);
+        const uint32_t a_voff_step = static_cast<uint32_t>((int64_t)4 * S::NW * p.lda * 4);
+        const int b_q = wave & 3, b_kr = wave >> 2;
+        const bool b_col_in = n0 + 64 * b_q + lane < p.N;
+        const uint32_t b_voff = static_cast<uint32_t>(((int64_t)b_kr * p.ldb + 64 * b_q + lane) * 4);
+        const uint32_t b_voff_step = static_cast<uint32_t>((int64_t)(S::NW / 4) * p.ldb * 4);
         auto fill = [&](unsigned char* stage, int kt) __attribute__((always_inline)) {
             const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage));
+            if constexpr (MASKED) {
+                const int kp = k_lo + kt * S::BK;
+                const i32x4_rsrc ra = copy_rsrc(p.A + (int64_t)m0 * p.lda + kp);
+                const bool a_k_in = kp + a_kk < p.K;
 #pragma unroll
-            for (int j = 0; j < S::A_INS; ++j)
-                lds_copy16(a_src + j * a_step + kt * S::BK, base + (wave + S::NW * j) * 1024);
+                for (int j = 0; j < S::A_INS; ++j) {
+                    const bool in = a_k_in && m0 + a_row + 4 * S::NW * j < p.M;
+                    lds_copy4_masked(ra, in ? a_voff + j * a_voff_step : kLdsCopyOut,
+                                     base + (wave + S::NW * j) * 256);
+                }
+                const i32x4_rsrc rb = copy_rsrc(p.B + (int64_t)kp * p.ldb + n0);
 #pragma unroll
-            for (int j = 0; j < S::B_INS; ++j)
-                lds_copy16(b_src + j * b_step + kt * b_panel,
-                           base + S::A_BYTES + (wave + S::NW * j) * S::B_ROW);
+                for (int j = 0; j < S::B_INS; ++j) {
+                    const int kr = b_kr + (S::NW / 4) * j;
+                    const bool in = b_col_in && kp + kr < p.K;
+                    lds_copy4_masked(rb, in ? b_voff + j * b_voff_step : kLdsCopyOut,
+                                     base + S::A_BYTES + kr * S::B_ROW + b_q * 256);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < S::A_INS; ++j)
+                    lds_copy16(a_src + j * a_step + kt * S::BK, base + (wave + S::NW * j) * 1024);
+#pragma unroll
+                for (int j = 0; j < S::B_INS; ++j)
+                    lds_copy16(b_src + j * b_step + kt * b_panel,
+                               base + S::A_BYTES + (wave + S::NW * j) * S::B_ROW);
+            }
         };
 
         // Fragments of half q (steps 4q .. 4q + 3): A block i one 16-byte read
@@ -297,8 +343,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) 
             }
         }
         if (finish)
-            store_tile<FM, FN, false>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N,
-                                      p.alpha, p.beta, lane);
+            store_tile<FM, FN, MASKED>(acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N,
+                                       p.alpha, p.beta, lane);
         if constexpr (!sk) break;
         if (dp_item) ++r;
         else u += nk;
@@ -308,38 +354,51 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) 
 
 }  // namespace
 
-// The ring handles whole tiles of the plain layout with 16-byte aligned rows
-// and K a multiple of 16; anything else (ragged shapes, odd leading
-// dimensions, transposed operands, split-K slices) runs the register-staged
-// kernel with the same BM x BN tile (BK = 16, 2 x 2 waves).
+// The ring handles the plain layout: whole tiles with 16-byte aligned rows
+// and K a multiple of 16 in the unmasked form, any other shape in the masked
+// form while the copies' byte offsets within a panel (BM rows of A, 16
+// k-rows of B) stay below 2^30; transposed operands and split-K slices run
+// the register-staged kernel with the same BM x BN tile (BK = 16, 2 x 2
+// waves).
 namespace {
+bool ring_plain(const F32Args& a, const F32Variant& v) {
+    return !v.ta && !v.tb && a.ksplit == 0 && !v.r16 && a.M > 0 && a.N > 0 && a.K > 0;
+}
 bool ring_whole(int bm, int bn, const F32Args& a, const F32Variant& v) {
-    return !v.masked && v.vec && !v.ta && !v.tb && a.ksplit == 0 && !v.r16 && a.M % bm == 0 &&
-           a.N % bn == 0 && a.K % 16 == 0 && a.K > 0;
+    return ring_plain(a, v) && !v.masked && v.vec && a.M % bm == 0 && a.N % bn == 0 &&
+           a.K % 16 == 0;
+}
+bool ring_masked(int bm, const F32Args& a, const F32Variant& v) {
+    return ring_plain(a, v) && int64_t{bm} * a.lda < (int64_t{1} << 28) &&
+           int64_t{16} * a.ldb < (int64_t{1} << 28);
 }
 }  // namespace
 
 bool f32_ring_takes(const TileConfig& cfg, const F32Args& a, const F32Variant& v) {
-    return ring_whole(cfg.bm, cfg.bn, a, v);
+    return ring_whole(cfg.bm, cfg.bn, a, v) || ring_masked(cfg.bm, a, v);
+}
+
+template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED>
+hipError_t launch_ring_form(const F32Args& a, hipStream_t s) {
+    const dim3 block(WM * WN * 64);
+    if (a.sk_q > 0) {
+        const int grid = ring_sk_grid(int64_t{a.tiles_m} * a.tiles_n, (a.K + 15) / 16, a.sk_q,
+                                      a.sk_dp, a.sk_grid, a.P, a.counts);
+        if (grid <= 0) return hipErrorInvalidValue;
+        gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM, true, MASKED><<<dim3(grid), block, 0, s>>>(a);
+    } else {
+        gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM, false, MASKED>
+            <<<dim3(static_cast<unsigned>(a.tiles_m * a.tiles_n)), block, 0, s>>>(a);
+    }
+    return hipGetLastError();
 }
 
 template <int BM, int BN, int NS, int WM, int WN, int GM>
 hipError_t launch_f32_ring(const F32Args& a, F32Variant v, hipStream_t s) {
-    if (!ring_whole(BM, BN, a, v)) {
-        if (v.ta || v.tb) return launch_f32_transposed<BM, BN, 16, 2, 2, GM>(a, v, s);
-        return launch_f32_layout<BM, BN, 16, 2, 2, GM, false, false>(a, v, s);
-    }
-    const dim3 block(WM * WN * 64);
-    if (a.sk_q > 0) {
-        const int grid = ring_sk_grid(int64_t{a.tiles_m} * a.tiles_n, a.K / 16, a.sk_q, a.sk_dp,
-                                      a.sk_grid, a.P, a.counts);
-        if (grid <= 0) return hipErrorInvalidValue;
-        gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM, true><<<dim3(grid), block, 0, s>>>(a);
-    }
-    else
-        gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM, false>
-            <<<dim3(static_cast<unsigned>(a.tiles_m * a.tiles_n)), block, 0, s>>>(a);
-    return hipGetLastError();
+    if (ring_whole(BM, BN, a, v)) return launch_ring_form<BM, BN, NS, WM, WN, GM, false>(a, s);
+    if (ring_masked(BM, a, v)) return launch_ring_form<BM, BN, NS, WM, WN, GM, true>(a, s);
+    if (v.ta || v.tb) return launch_f32_transposed<BM, BN, 16, 2, 2, GM>(a, v, s);
+    return launch_f32_layout<BM, BN, 16, 2, 2, GM, false, false>(a, v, s);
 }
 
 #define G355_F32_RING_INSTANTIATE(BM, BN, NS, WM, WN, GM) \

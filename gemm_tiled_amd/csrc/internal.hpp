@@ -274,6 +274,26 @@ __device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds_base) {
                  : "memory");
 }
 
+// One masked direct copy of a wave, 4 bytes a lane: lane l copies the float at
+// byte offset voff of the raw buffer `rsrc` to LDS byte address lds_base + 4 l.
+// A lane whose offset lies past the buffer's record count (kLdsCopyOut) reads
+// zero, which is how the copies zero-fill rows, columns and k past the edge
+// of a matrix.  Untracked by the compiler for the reason given above.
+typedef int i32x4_rsrc __attribute__((ext_vector_type(4)));
+constexpr uint32_t kLdsCopyOut = 0x80000000u;
+__device__ __forceinline__ i32x4_rsrc copy_rsrc(const float* base) {
+    // raw buffer of 32-bit data, record count 2^31 - 1 (every offset the
+    // copies use for a lane inside the matrix stays below 2^30)
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const i32x4_rsrc r = {static_cast<int>(static_cast<uint32_t>(a)), static_cast<int>((a >> 32) & 0xffff),
+                          0x7fffffff, 0x00020000};
+    return r;
+}
+__device__ __forceinline__ void lds_copy4_masked(i32x4_rsrc rsrc, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_base)
+                 : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const unsigned char* generic_lds_ptr) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)(generic_lds_ptr)));
 }

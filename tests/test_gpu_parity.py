@@ -604,3 +604,65 @@ def test_ring_ragged_small_integers_exact_and_beta_zero(cfg):
         Cn = np.full((M, N), np.nan, dtype=np.float32)
         got = run("f32", A, B, Cn, 1.0, 0.0)
         assert np.array_equal(got, exact.astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# The masked form of the f32 ring: any shape and any leading dimensions, the
+# copies zero-filling A and B past M, N and K (4-byte copies, so rows need no
+# 16-byte alignment), stream-K when whole rounds of tiles leave CUs idle.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", RINGS)
+@pytest.mark.parametrize("M,N,K,lds", [
+    (1000, 1030, 1000, {}),                                  # ragged, 8-byte rows
+    (300, 517, 333, {"lda": 335, "ldb": 519, "ldc": 521}),   # odd lds: 4-byte rows
+    (1, 1, 1, {}),                                           # one element
+    (33, 300, 7, {}),                                        # K shorter than a panel
+    (256, 256, 4093, {}),                                    # one tile, long ragged K
+    (513, 2049, 1100, {"lda": 1101}),                        # stream-K over ragged tiles
+    (1000, 1025, 1001, {"lda": 1001}),                       # one column past whole tiles
+])
+def test_ring_masked_against_the_oracle(cfg, M, N, K, lds):
+    A, B, C = make_inputs(M, N, K, "normal", seed=61, **lds)
+    with pinned("f32", cfg):
+        say(f"[ring masked] {cfg} {M}x{N}x{K} {lds}")
+        got = run("f32", A, B, C, 1.25, -0.5)
+        again = run("f32", A, B, C, 1.25, -0.5)
+    assert_parity("f32", A, B, C, 1.25, -0.5, got)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+
+
+@pytest.mark.parametrize("cfg", RINGS[:1] + RINGS[-1:])
+def test_ring_masked_zero_fills_past_the_edges(cfg):
+    """NaN in the padding of A's rows (k >= K) and of B's rows (columns >= N),
+    and in the rows of B after K: a masked copy that read any of them would
+    put NaN into C, since NaN times the zero of the other operand is NaN."""
+    M, N, K, lda, ldb = 300, 517, 333, 337, 523
+    A, B, C = small_integers(M, N, K, seed=62)
+    fa = np.full((M, lda), np.nan, dtype=np.float32)
+    fa[:, :K] = A
+    fb = np.full((K + 40, ldb), np.nan, dtype=np.float32)
+    fb[:K, :N] = B
+    tA = torch.from_numpy(fa).to("cuda")[:, :K]
+    tB = torch.from_numpy(fb).to("cuda")[:K, :N]
+    tC = to_device(C)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned("f32", cfg):
+        say(f"[ring masked nan] {cfg} {M}x{N}x{K}")
+        g.gemm("f32", tA, tB, tC, 1.0, -1.0)
+        torch.cuda.synchronize()
+    got = tC.cpu().numpy()
+    assert np.array_equal(got, (exact - C.astype(np.float64)).astype(np.float32))
+
+
+@pytest.mark.parametrize("cfg", RINGS[:1] + RINGS[-1:])
+def test_ring_masked_small_integers_exact_and_beta_zero(cfg):
+    M, N, K = 4000, 4097, 1001    # rows of B and C start 16-byte aligned every fourth row
+    A, B, C = small_integers(M, N, K, seed=63)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned("f32", cfg):
+        say(f"[ring masked exact] {cfg} {M}x{N}x{K}")
+        got = run("f32", A, B, C, -2.0, 0.5)
+        assert np.array_equal(got, (-2.0 * exact + 0.5 * C.astype(np.float64)).astype(np.float32))
+        Cn = np.full((M, N), np.nan, dtype=np.float32)
+        got = run("f32", A, B, Cn, 1.0, 0.0)
+        assert np.array_equal(got, exact.astype(np.float32))
