@@ -401,21 +401,22 @@ def _tile_fields(tile):
                                     t.split("=")[1].isdigit())}
 
 
-def _path_of(mode, n, tile):
-    """Which variant a square n^3 call with this tile runs (dense, 16-byte aligned rows)."""
-    t = _tile_fields(tile)
-    if mode == "f32":
-        if t.get("KS"):
-            return "split" if n % 4 else "split, 16-byte rows"
-        ragged = n % t["BM"] or n % t["BN"] or n % t["BK"]
-        ring = t["BK"] == 16 and t["ST"] >= 3
-        if ring and ragged and n % 4 == 0 and n >= t["BM"] and n >= t["BN"]:
-            # the ring on the block of whole tiles, the strips on other tiles
-            m0, n0 = n // t["BM"] * t["BM"], n // t["BN"] * t["BN"]
-            if 4 * m0 * n0 >= 3 * n * n:
-                return "ring block + strips"
-        return ("masked" if ragged else "aligned") + ("" if n % 4 == 0 else ", rows 4-byte aligned")
-    return "masked store" if (n % t["BM"] or n % t["BN"]) else "aligned"
+def _plan_of(g, mode, n, pin=None):
+    """How a square n^3 call runs (the library's own plan, gemm355_get_plan_ex):
+    the kernel path and, when the ring runs only a block of C, that block."""
+    if pin:
+        g.set_config(mode, pin)
+    try:
+        plan = dict(kv.split("=") for kv in g.get_plan(mode, n, n, n, beta=0.0).split())
+    finally:
+        if pin:
+            g.set_config(mode, None)
+    text = plan["form"]
+    if plan["block"] != f"{n}x{n}x{n}":
+        text += f" on {plan['block']} + strips"
+    if "rows" in plan:
+        text += ", rows 4-byte aligned"
+    return text
 
 
 def shape_sweep(g, torch, dev, out, repeats):
@@ -437,7 +438,7 @@ def shape_sweep(g, torch, dev, out, repeats):
         del A, B, C
     log(f"sweep: {len(cases)} cases, {repeats} shuffled rounds")
 
-    tiles, calls = {}, {}
+    tiles, plans, calls = {}, {}, {}
     for case in cases:
         mode, n, kind = case
         tA, tB, tC, r, c, refs = inputs[n]
@@ -445,9 +446,11 @@ def shape_sweep(g, torch, dev, out, repeats):
         if kind == "tuned":
             g.tune(mode, tA, tB, tC, beta=0.0)
             tiles[case] = g.get_config(mode, n, n, n, beta=0.0)
+            plans[case] = _plan_of(g, mode, n)
             call = (lambda fn=fn, tA=tA, tB=tB, tC=tC: fn(tA, tB, tC, 1.0, 0.0))
         else:
             tiles[case] = FIXED_TILE[mode] + " source=pin"
+            plans[case] = _plan_of(g, mode, n, FIXED_TILE[mode])
 
             def call(fn=fn, tA=tA, tB=tB, tC=tC, mode=mode):
                 g.set_config(mode, FIXED_TILE[mode])
@@ -480,7 +483,7 @@ def shape_sweep(g, torch, dev, out, repeats):
         ts = times[case]
         med = float(np.median(ts))
         rows.append({"mode": mode, "n": n, "kind": kind, "tile": tiles[case].split(" source=")[0],
-                     "path": _path_of(mode, n, tiles[case]), "seconds": med,
+                     "path": plans[case], "seconds": med,
                      "seconds_min": min(ts), "seconds_max": max(ts),
                      "tflops": 2.0 * n ** 3 / med / 1e12})
     by = {(r["mode"], r["n"], r["kind"]): r for r in rows}

@@ -51,6 +51,8 @@ EXPORTS = {
                                           _f32, _p, ctypes.c_size_t]),
     "gemm355_get_config_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64,
                                              _i64, _i64, _i64, _i64, _f32, _p, ctypes.c_size_t]),
+    "gemm355_get_plan_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64,
+                                           _i64, _i64, _i64, _i64, _f32, _p, ctypes.c_size_t]),
     "gemm355_set_config": (ctypes.c_int, [ctypes.c_int, _cp]),
     "gemm355_parse_config": (ctypes.c_int, [ctypes.c_int, _cp, _p, ctypes.c_size_t]),
     "gemm355_list_configs": (ctypes.c_int, [ctypes.c_int, _p, ctypes.c_size_t]),
@@ -219,6 +221,19 @@ def get_config(mode, M, N, K, lda=None, ldb=None, ldc=None, beta=0.0, transa=Fal
                                      lda, ldb, ldc or max(N, 1), float(beta), buf, 256)
     if st != 0:
         raise Gemm355Error(st, "gemm355_get_config_ex")
+    return buf.value.decode()
+
+
+def get_plan(mode, M, N, K, lda=None, ldb=None, ldc=None, beta=0.0, transa=False,
+             transb=False) -> str:
+    """How the call would run: "form=... block=MBxNBxKB" (see gemm355_get_plan_ex)."""
+    buf = ctypes.create_string_buffer(256)
+    lda = lda or max(M if transa else K, 1)
+    ldb = ldb or max(K if transb else N, 1)
+    st = lib().gemm355_get_plan_ex(_mode(mode), int(bool(transa)), int(bool(transb)), M, N, K,
+                                   lda, ldb, ldc or max(N, 1), float(beta), buf, 256)
+    if st != 0:
+        raise Gemm355Error(st, "gemm355_get_plan_ex")
     return buf.value.decode()
 
 

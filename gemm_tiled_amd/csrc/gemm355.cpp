@@ -1091,6 +1091,37 @@ int gemm355_get_config_ex(int mode, int transa, int transb, int64_t M, int64_t N
     return copy_out(format_config(cfg) + " source=" + sname, buf, len);
 }
 
+int gemm355_get_plan_ex(int mode, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc, float beta, char* buf, size_t len) {
+    if (mode != GEMM355_MODE_F32 && mode != GEMM355_MODE_F16R) return GEMM355_ERR_MODE;
+    int trans = 0;
+    if (const int bad = trans_of(transa, transb, &trans)) return bad;
+    const float* aligned = reinterpret_cast<const float*>(uintptr_t{256});
+    const int bad = check_args(trans, M, N, K, 1.0f, aligned, lda, aligned, ldb, aligned, ldc);
+    if (bad) return shift_ex(bad);
+    TileConfig cfg;
+    Source src;
+    const int rc =
+        select_config(mode, trans, M, N, K, aligned, lda, aligned, ldb, beta, &cfg, &src);
+    if (rc) return rc;
+    const RingRows rows = ring_rows(trans, aligned, lda, aligned, ldb);
+    const RingBlock b = ring_block(cfg, rows, M, N, K);
+    const bool vec = vec_ok(aligned, lda) && vec_ok(aligned, ldb);
+    std::string form;
+    if (cfg.ks == 1) form = "split-k";
+    else if (cfg.ks == 2) form = "rows";
+    else if (cfg.ks == 3) form = "round-on-load";
+    else if (mode == GEMM355_MODE_F16R) form = (M % cfg.bm || N % cfg.bn) ? "packed-masked" : "packed";
+    else if (is_f32_ring(cfg) && rows != RingRows::None)
+        form = rows == RingRows::Aligned && b.mb % cfg.bm == 0 && b.nb % cfg.bn == 0 && b.kb % 16 == 0
+                   ? "ring" : "ring-masked";
+    else form = (!vec || M % cfg.bm || N % cfg.bn || K % cfg.bk) ? "tiles-masked" : "tiles";
+    const std::string out = "form=" + form + " block=" + std::to_string(b.mb) + "x" +
+                            std::to_string(b.nb) + "x" + std::to_string(b.kb) +
+                            (vec ? "" : " rows=4-byte");
+    return copy_out(out, buf, len);
+}
+
 int gemm355_get_config(int mode, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                        int64_t ldc, float beta, char* buf, size_t len) {
     const int rc = gemm355_get_config_ex(mode, 0, 0, M, N, K, lda, ldb, ldc, beta, buf, len);

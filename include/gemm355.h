@@ -164,6 +164,24 @@ int gemm355_get_config_ex(int mode, int transa, int transb, int64_t M, int64_t N
                           char* buf, size_t len);
 
 /*
+ * How a call with these arguments (operand pointers taken as 256-byte
+ * aligned) would run, written into buf as "form=F block=MBxNBxKB" plus
+ * " rows=4-byte" when a leading dimension keeps rows from being 16-byte
+ * aligned.  F names the kernel path of the configuration gemm355_get_config_ex
+ * reports: ring / ring-masked (the f32 ring of direct-to-LDS panel copies, on
+ * whole tiles or in its zero-filling form), tiles / tiles-masked (the
+ * register-staged f32 kernel), packed / packed-masked (the f16r packing pass
+ * and binary16 kernel, masked stores at ragged edges), split-k, rows,
+ * round-on-load.  The block is the part of C (MB x NB, over the first KB of
+ * K) that configuration runs itself; when it is smaller than the call, the
+ * right strip, the bottom strip and the k tail run in the few-rows, split-K
+ * or 64 x 64 configurations.  Host only; no GPU call.  Returns as
+ * gemm355_get_config_ex.
+ */
+int gemm355_get_plan_ex(int mode, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc, float beta, char* buf, size_t len);
+
+/*
  * Pin one tile configuration for every later call of `mode`, skipping the
  * search (phobos docs, "gemm, f32", section "Tuning", the pinned run).
  * Grammar: space-separated KEY=VALUE with keys BM|TILE_M, BN|TILE_N,

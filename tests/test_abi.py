@@ -256,3 +256,28 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(g, "_HERE", str(tmp_path))
     with pytest.raises(ImportError):
         g.lib()
+
+
+def test_plan_names_the_path_and_the_ring_block():
+    """Host-only: gemm355_get_plan_ex.  A ring configuration runs whole tiles
+    unmasked; with 16-byte rows a call one element past whole tiles gives the
+    ring the block of whole tiles and the strips to other configurations; with
+    rows that are not 16-byte aligned the masked ring runs the call, here
+    without the last partial tile column (one column of C)."""
+    ring = "BM=256 BN=256 BK=16 ST=3 WM=2 WN=4 GM=8"
+    g.set_config("f32", ring)
+    try:
+        assert g.get_plan("f32", 4096, 4096, 4096) == "form=ring block=4096x4096x4096"
+        assert g.get_plan("f32", 4100, 4100, 4100) == "form=ring block=4096x4096x4096"
+        plan = g.get_plan("f32", 4000, 4097, 4093)
+        assert plan == "form=ring-masked block=4000x4096x4093 rows=4-byte", plan
+        assert g.get_plan("f32", 300, 517, 333, lda=335, ldb=519, ldc=521) == \
+            "form=ring-masked block=300x517x333 rows=4-byte"
+        # transposed operands: the register-staged kernel of the same tile
+        assert g.get_plan("f32", 4096, 4096, 4096, transa=True).startswith("form=tiles")
+    finally:
+        g.set_config("f32", None)
+    assert g.get_plan("f32", 8, 4096, 4096) == "form=rows block=8x4096x4096"
+    assert g.get_plan("f16r", 8192, 8192, 8192).startswith("form=packed block=8192x8192x8192")
+    with pytest.raises(g.Gemm355Error):
+        g.get_plan("f32", -1, 4, 4)
