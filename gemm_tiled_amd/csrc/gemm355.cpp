@@ -1111,7 +1111,7 @@ int gemm355_get_plan_ex(int mode, int transa, int transb, int64_t M, int64_t N, 
     if (cfg.ks == 1) form = "split-k";
     else if (cfg.ks == 2) form = "rows";
     else if (cfg.ks == 3) form = "round-on-load";
-    else if (mode == GEMM355_MODE_F16R) form = (M % cfg.bm || N % cfg.bn) ? "packed-masked" : "packed";
+    else if (mode == GEMM355_MODE_F16R) form = (b.mb % cfg.bm || b.nb % cfg.bn) ? "packed-masked" : "packed";
     else if (is_f32_ring(cfg) && rows != RingRows::None)
         form = rows == RingRows::Aligned && b.mb % cfg.bm == 0 && b.nb % cfg.bn == 0 && b.kb % 16 == 0
                    ? "ring" : "ring-masked";
