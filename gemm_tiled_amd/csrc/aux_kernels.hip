@@ -193,6 +193,21 @@ hipError_t launch_roof_hbm(const void* buf, int64_t bytes, int blocks, float* si
     return hipGetLastError();
 }
 
+// p[i] = value for i < n: clears arrival counters with a kernel (a memset
+// recorded into a captured graph is a node of another kind).
+__global__ void __launch_bounds__(256) fill_u32_kernel(unsigned* p, int64_t n, unsigned value) {
+    const int64_t stride = int64_t{gridDim.x} * blockDim.x;
+    for (int64_t i = int64_t{blockIdx.x} * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = value;
+}
+
+hipError_t launch_fill_u32(unsigned* p, int64_t n, unsigned value, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t want = (n + 255) / 256;
+    const int blocks = static_cast<int>(want < 1024 ? want : 1024);
+    fill_u32_kernel<<<blocks, 256, 0, s>>>(p, n, value);
+    return hipGetLastError();
+}
+
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s) {
     const int64_t n4 = n / 4;
     if (n4 > 0) {

@@ -18,6 +18,7 @@
 
 #include "gemm355.h"
 #include "internal.hpp"
+#include "workspace.hpp"
 
 namespace g355 {
 namespace {
@@ -410,81 +411,125 @@ int select_config(int mode, int trans, int64_t M, int64_t N, int64_t K, const fl
 }
 
 // ---------------------------------------------------------------------------
-// The f16r workspace: one device buffer per (device, stream), grown on demand.
-// Calls on one stream run in order, so they can share it.
+// Device scratch of a call: the packed binary16 operands of the f16r mode,
+// the partial tiles of the configurations that split K over workgroups and
+// their arrival counters.  The entry points that may allocate lease it from
+// a pool per device (workspace.hpp: the lease lasts from the call's first
+// request until its last launch is enqueued; growth is stream-ordered, the
+// host never waits).
+// Every call is first planned with a DryScratch (no launch), which records
+// what it will ask for, so a failure to allocate is reported before any
+// kernel is enqueued.
 // ---------------------------------------------------------------------------
-struct WsKey {
-    int dev;
-    hipStream_t s;
-    bool operator<(const WsKey& o) const { return std::tie(dev, s) < std::tie(o.dev, o.s); }
-};
-struct Ws {
-    void* ptr = nullptr;
-    size_t bytes = 0;
-};
-std::mutex g_ws_mu;
-std::map<WsKey, Ws> g_ws;
+int status_of(hipError_t e) { return e == hipSuccess ? 0 : static_cast<int>(e); }
 
-hipError_t workspace(hipStream_t s, size_t bytes, void** out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_ws_mu);
-    Ws& w = g_ws[WsKey{dev, s}];
-    if (w.bytes < bytes) {
-        if (w.ptr) {
-            // earlier work on this stream may still read the old buffer
-            e = hipStreamSynchronize(s);
-            if (e != hipSuccess) return e;
-            (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        e = hipMalloc(&w.ptr, bytes);
-        if (e != hipSuccess) {
-            w.ptr = nullptr;
-            return e;
-        }
-        w.bytes = bytes;
+struct HipBackend {
+    using Stream = hipStream_t;
+    using Event = hipEvent_t;
+    int alloc(void** p, size_t bytes, hipStream_t s) {
+        const hipError_t e = hipMallocAsync(p, bytes, s);
+        return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
     }
-    *out = w.ptr;
-    return hipSuccess;
+    int release(void* p, hipStream_t s) { return status_of(hipFreeAsync(p, s)); }
+    int zero_u32(unsigned* p, size_t n, hipStream_t s) {
+        return status_of(launch_fill_u32(p, static_cast<int64_t>(n), 0u, s));
+    }
+    int event_create(hipEvent_t* e) {
+        return status_of(hipEventCreateWithFlags(e, hipEventDisableTiming));
+    }
+    void event_destroy(hipEvent_t e) { (void)hipEventDestroy(e); }
+    int record(hipEvent_t e, hipStream_t s) { return status_of(hipEventRecord(e, s)); }
+    bool idle(hipEvent_t e) { return hipEventQuery(e) == hipSuccess; }
+    // an error of the query counts as capturing: the call then only reuses
+    // what its stream already holds and allocates nothing
+    bool capturing(hipStream_t s) {
+        hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+        return hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone;
+    }
+};
+
+// Slots kept per device (each as large as the largest call it served).
+constexpr size_t kPoolSlots = 8;
+using Pool = ScratchPool<HipBackend>;
+
+Pool* pool_of(int dev) {
+    static std::mutex mu;
+    static std::map<int, Pool*> pools;     // never destroyed: calls may run until exit
+    static HipBackend* backend = new HipBackend();
+    std::lock_guard<std::mutex> lock(mu);
+    Pool*& p = pools[dev];
+    if (!p) p = new Pool(*backend, kPoolSlots);
+    return p;
 }
 
-// Arrival counters of the configurations that split K over workgroups (few
-// rows, round-on-load, stream-K rings): one zeroed buffer per (device,
-// stream), grown on demand (zeroed again when it grows).  Every kernel leaves
-// each counter it uses at zero.
-std::map<WsKey, Ws> g_counts;
-
-hipError_t counters(hipStream_t s, size_t n, unsigned** out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_ws_mu);
-    Ws& w = g_counts[WsKey{dev, s}];
-    const size_t bytes = n * sizeof(unsigned);
-    if (w.bytes < bytes) {
-        if (w.ptr) {
-            e = hipStreamSynchronize(s);
-            if (e != hipSuccess) return e;
-            (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        const size_t grown = std::max<size_t>(bytes, 4096);
-        e = hipMalloc(&w.ptr, grown);
-        if (e == hipSuccess) e = hipMemsetAsync(w.ptr, 0, grown, s);
-        if (e != hipSuccess) {
-            if (w.ptr) (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            return e;
-        }
-        w.bytes = grown;
+class Scratch {
+public:
+    virtual ~Scratch() = default;
+    // A buffer of at least `bytes` bytes and n zeroed arrival counters for
+    // the launches of this call; 0 or a status.
+    virtual int workspace(size_t bytes, void** out) = 0;
+    virtual int counters(size_t n, unsigned** out) = 0;
+    // Planning pass: the launch functions return right before launching.
+    bool dry() const { return dry_; }
+    // Obtain, before anything is launched, what a dry pass recorded.
+    virtual int reserve(size_t bytes, size_t n) {
+        void* w = nullptr;
+        unsigned* c = nullptr;
+        int rc = bytes ? workspace(bytes, &w) : 0;
+        if (rc == 0 && n) rc = counters(n, &c);
+        return rc;
     }
-    *out = static_cast<unsigned*>(w.ptr);
-    return hipSuccess;
-}
+
+protected:
+    bool dry_ = false;
+};
+
+// Records the largest requests of a call; hands out a stand-in pointer that
+// no kernel ever sees (nothing is launched in a dry pass).
+class DryScratch : public Scratch {
+public:
+    DryScratch() { dry_ = true; }
+    int workspace(size_t bytes, void** out) override {
+        ws = std::max(ws, bytes);
+        *out = reinterpret_cast<void*>(uintptr_t{4096});
+        return 0;
+    }
+    int counters(size_t n, unsigned** out) override {
+        cnt = std::max(cnt, n);
+        *out = reinterpret_cast<unsigned*>(uintptr_t{4096});
+        return 0;
+    }
+    size_t ws = 0, cnt = 0;
+};
+
+class PoolScratch : public Scratch {
+public:
+    explicit PoolScratch(hipStream_t s) : s_(s) {}
+    int workspace(size_t bytes, void** out) override {
+        if (const int rc = take()) return rc;
+        return mapped(lease_.workspace(bytes, out));
+    }
+    int counters(size_t n, unsigned** out) override {
+        if (const int rc = take()) return rc;
+        return mapped(lease_.counters(n, out));
+    }
+
+private:
+    int take() {
+        if (!have_) {
+            int dev = 0;
+            const hipError_t e = hipGetDevice(&dev);
+            if (e != hipSuccess) return status_of(e);
+            lease_ = pool_of(dev)->lease(s_);
+            have_ = true;
+        }
+        return mapped(lease_.status());
+    }
+    static int mapped(int rc) { return rc == Pool::kNeedsAlloc ? GEMM355_ERR_CAPTURE : rc; }
+    hipStream_t s_;
+    bool have_ = false;
+    Pool::Lease lease_;
+};
 
 // ---------------------------------------------------------------------------
 // Argument checks (BLAS xerbla numbering) and the dispatch of one call.
@@ -508,15 +553,13 @@ int check_args(int trans, int64_t M, int64_t N, int64_t K, float alpha, const fl
     return 0;
 }
 
-int status_of(hipError_t e) { return e == hipSuccess ? 0 : static_cast<int>(e); }
-
 // The split-K configuration: slices of K chosen so that tiles x slices reaches
 // kSplitKTarget workgroups, each slice at least kSplitKMinDepth deep (a
 // multiple of BK), the partial tiles within kSplitKMaxBytes.  One slice runs
 // the normal epilogue; more go through the workspace and the reduction.
 int launch_splitk(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
                   const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
-                  int64_t ldc, hipStream_t s, uint16_t* C16) {
+                  int64_t ldc, hipStream_t s, uint16_t* C16, Scratch& sc) {
     const int tiles_m = static_cast<int>((M + cfg.bm - 1) / cfg.bm);
     const int tiles_n = static_cast<int>((N + cfg.bn - 1) / cfg.bn);
     const int64_t tiles = int64_t{tiles_m} * tiles_n;
@@ -535,21 +578,21 @@ int launch_splitk(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_
     v.ta = (trans & 1) != 0;
     v.tb = (trans & 2) != 0;
     v.r16 = cfg.mode == GEMM355_MODE_F16R;
-    if (log_debug())
+    if (log_debug() && !sc.dry())
         std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=split-K x%lld (k %lld)%s\n",
                      layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
                      (long long)K, format_config(cfg).c_str(), (long long)slices,
                      (long long)depth, v.masked ? " masked" : "");
     // binary16 output always goes through the reduction, which rounds
-    if (slices == 1 && !C16) return status_of(launch_f32_splitk(a, v, s));
+    if (slices == 1 && !C16) return sc.dry() ? 0 : status_of(launch_f32_splitk(a, v, s));
     void* ws = nullptr;
-    hipError_t e = workspace(s, static_cast<size_t>(slices * M * N) * 4, &ws);
-    if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
+    if (const int rc = sc.workspace(static_cast<size_t>(slices * M * N) * 4, &ws)) return rc;
+    if (sc.dry()) return 0;
     a.C = static_cast<float*>(ws);
     a.ldc = N;
     a.ksplit = static_cast<int>(depth);   // one slice too, when the output is binary16
     // the slices of a ragged split write partial tiles masked to M x N
-    e = launch_f32_splitk(a, v, s);
+    hipError_t e = launch_f32_splitk(a, v, s);
     if (e != hipSuccess) return status_of(e);
     if (C16)
         return status_of(launch_splitk_reduce16(static_cast<const float*>(ws),
@@ -567,12 +610,12 @@ int launch_splitk(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_
 // time take the split-K configuration instead.
 int launch_rows(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
-                int64_t ldc, hipStream_t s, uint16_t* C16) {
+                int64_t ldc, hipStream_t s, uint16_t* C16, Scratch& sc) {
     const bool ta = (trans & 1) != 0, tb = (trans & 2) != 0;
     if (!rows_supported(ta, tb, B, lda, ldb, static_cast<int>(M), static_cast<int>(N),
                         static_cast<int>(K)))
         return launch_splitk(splitk_config(cfg.mode), trans, M, N, K, alpha, A, lda, B, ldb, beta,
-                             C, ldc, s, C16);
+                             C, ldc, s, C16, sc);
     // Slice depth: two 64-deep chunks per wave (one pass of the kernel) when
     // that gives at least one workgroup per CU, one chunk when the grid would
     // be smaller; deeper slices when there would be more than kRowsMaxWgs
@@ -587,7 +630,7 @@ int launch_rows(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
     if ((K + depth - 1) / depth > max_slices) depth = round_up((K + max_slices - 1) / max_slices, unit);
     const int64_t slices = (K + depth - 1) / depth;
     const bool r16 = cfg.mode == GEMM355_MODE_F16R;
-    if (log_debug())
+    if (log_debug() && !sc.dry())
         std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=rows x%lld (k %lld)%s\n",
                      layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
                      (long long)K, format_config(cfg).c_str(), (long long)slices,
@@ -598,11 +641,12 @@ int launch_rows(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
     if (slices > 1) {
         void* ws = nullptr;
         // partial rows are N rounded up to 4 floats apart
-        hipError_t e = workspace(s, static_cast<size_t>(slices * M * round_up(N, 4)) * 4, &ws);
-        if (e == hipSuccess) e = counters(s, static_cast<size_t>(rows_counters(m, n)), &counts);
-        if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
+        int rc = sc.workspace(static_cast<size_t>(slices * M * round_up(N, 4)) * 4, &ws);
+        if (rc == 0) rc = sc.counters(static_cast<size_t>(rows_counters(m, n)), &counts);
+        if (rc) return rc;
         P = static_cast<float*>(ws);
     }
+    if (sc.dry()) return 0;
     return status_of(launch_f32_rows(A, lda, ta, B, ldb, tb, r16, C, C16, ldc, m, n, k, alpha,
                                      beta, static_cast<int>(depth), static_cast<int>(slices), P,
                                      counts, s));
@@ -615,7 +659,7 @@ int launch_rows(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
 // kSplitKMaxBytes.
 int launch_direct(const TileConfig& cfg_in, int trans, int64_t M, int64_t N, int64_t K,
                   float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
-                  float beta, float* C, int64_t ldc, hipStream_t s, uint16_t* C16) {
+                  float beta, float* C, int64_t ldc, hipStream_t s, uint16_t* C16, Scratch& sc) {
     TileConfig cfg = cfg_in;
     const bool ta = (trans & 1) != 0, tb = (trans & 2) != 0;
     // the f32-panel ring (BK = 16) hands the shapes it does not take to the
@@ -651,7 +695,7 @@ int launch_direct(const TileConfig& cfg_in, int trans, int64_t M, int64_t N, int
     slices = (K + depth - 1) / depth;
     const bool masked = !vec_ok(A, lda) || !vec_ok(B, ldb) || (M % cfg.bm) || (N % cfg.bn) ||
                         (K % cfg.bk);
-    if (log_debug())
+    if (log_debug() && !sc.dry())
         std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=direct x%lld (k %lld)%s\n",
                      layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
                      (long long)K, format_config(cfg).c_str(), (long long)slices,
@@ -662,24 +706,25 @@ int launch_direct(const TileConfig& cfg_in, int trans, int64_t M, int64_t N, int
                  static_cast<int>(depth), static_cast<int>(slices)};
     if (slices > 1) {
         void* ws = nullptr;
-        hipError_t e = workspace(s, static_cast<size_t>(slices * tiles * tile_bytes), &ws);
-        if (e == hipSuccess) e = counters(s, static_cast<size_t>(tiles), &a.counts);
-        if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
+        int rc = sc.workspace(static_cast<size_t>(slices * tiles * tile_bytes), &ws);
+        if (rc == 0) rc = sc.counters(static_cast<size_t>(tiles), &a.counts);
+        if (rc) return rc;
         a.P = static_cast<float*>(ws);
     }
+    if (sc.dry()) return 0;
     return status_of(inst->launch(a, ta, tb, masked, s));
 }
 
 // whole_call: run the call as one piece (a part of a split call).
 int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
-                int64_t ldc, hipStream_t s, uint16_t* C16, bool whole_call = false) {
+                int64_t ldc, hipStream_t s, uint16_t* C16, Scratch& sc, bool whole_call = false) {
     if (cfg.ks == 2)
-        return launch_rows(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
+        return launch_rows(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16, sc);
     if (cfg.ks == 3)
-        return launch_direct(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
+        return launch_direct(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16, sc);
     if (cfg.ks)
-        return launch_splitk(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
+        return launch_splitk(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16, sc);
     const RingBlock rb = whole_call ? RingBlock{M, N, K, 0.0}
                                     : ring_block(cfg, ring_rows(trans, A, lda, B, ldb), M, N, K);
     if (rb.mb < M || rb.nb < N || rb.kb < K) {
@@ -691,17 +736,17 @@ int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
         TileConfig edge;
         if (!parse_config(cfg.mode, "BM=64 BN=64 BK=16 ST=2", &edge)) return GEMM355_ERR_CONFIG;
         int rc = launch_with(cfg, 0, rb.mb, rb.nb, rb.kb, alpha, A, lda, B, ldb, beta, C, ldc, s,
-                             nullptr, true);
+                             nullptr, sc, true);
         if (rc == 0 && rb.kb < K)
             rc = launch_with(edge, 0, rb.mb, rb.nb, K - rb.kb, alpha, A + rb.kb, lda,
-                             B + rb.kb * ldb, ldb, 1.0f, C, ldc, s, nullptr, true);
+                             B + rb.kb * ldb, ldb, 1.0f, C, ldc, s, nullptr, sc, true);
         if (rc == 0 && rb.nb < N)
             rc = launch_with(strip_config(cfg.mode, M, N - rb.nb), 0, M, N - rb.nb, K, alpha, A, lda,
-                             B + rb.nb, ldb, beta, C + rb.nb, ldc, s, nullptr, true);
+                             B + rb.nb, ldb, beta, C + rb.nb, ldc, s, nullptr, sc, true);
         if (rc == 0 && rb.mb < M)
             rc = launch_with(strip_config(cfg.mode, M - rb.mb, rb.nb), 0, M - rb.mb, rb.nb, K, alpha,
                              A + rb.mb * lda, lda, B, ldb, beta, C + rb.mb * ldc, ldc, s, nullptr,
-                             true);
+                             sc, true);
         return rc;
     }
     const int tiles_m = static_cast<int>((M + cfg.bm - 1) / cfg.bm);
@@ -728,11 +773,12 @@ int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
                 a.sk_dp = static_cast<int>(sk.dp);
                 a.sk_grid = static_cast<int>(sk.grid);
                 void* ws = nullptr;
-                hipError_t e = workspace(s, static_cast<size_t>(sk.grid * 2 * cfg.bm * cfg.bn) * 4, &ws);
-                if (e == hipSuccess) e = counters(s, static_cast<size_t>(tiles), &a.counts);
-                if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
+                int rc = sc.workspace(static_cast<size_t>(sk.grid * 2 * cfg.bm * cfg.bn) * 4, &ws);
+                if (rc == 0) rc = sc.counters(static_cast<size_t>(tiles), &a.counts);
+                if (rc) return rc;
                 a.P = static_cast<float*>(ws);
             }
+            if (sc.dry()) return 0;
             if (log_debug())
                 std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=%s%s run %d\n",
                              layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
@@ -756,13 +802,14 @@ int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
         const int64_t q = sk.q;
         const int64_t packed_bytes = round_up((mp + np) * kp * 2, 256);
         void* ws = nullptr;
-        hipError_t e = workspace(
-            s, static_cast<size_t>(packed_bytes + sk.grid * 2 * cfg.bm * cfg.bn * 4), &ws);
-        if (e == hipSuccess && q > 0) e = counters(s, static_cast<size_t>(tiles_m) * tiles_n, &counts);
-        if (e != hipSuccess) return e == hipErrorOutOfMemory ? GEMM355_ERR_ALLOC : status_of(e);
+        int rc = sc.workspace(static_cast<size_t>(packed_bytes + sk.grid * 2 * cfg.bm * cfg.bn * 4),
+                              &ws);
+        if (rc == 0 && q > 0) rc = sc.counters(static_cast<size_t>(tiles_m) * tiles_n, &counts);
+        if (rc) return rc;
+        if (sc.dry()) return 0;
         uint16_t* A16 = static_cast<uint16_t*>(ws);
         uint16_t* B16t = A16 + mp * kp;
-        e = launch_pack(A, lda, (trans & 1) != 0, B, ldb, (trans & 2) != 0, static_cast<int>(M),
+        hipError_t e = launch_pack(A, lda, (trans & 1) != 0, B, ldb, (trans & 2) != 0, static_cast<int>(M),
                         static_cast<int>(N), static_cast<int>(K), A16, B16t, mp, np, kp, cfg.bk,
                         s);
         if (e != hipSuccess) return status_of(e);
@@ -789,9 +836,10 @@ int launch_with(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
 
 // C16 != NULL: the f16-output variant (f16r mode only): C is stored as
 // binary16 in C16 and the f32 result is rounded to nearest even; C is unused.
+// sc: where the call's scratch comes from (NULL: a lease of the device's pool).
 int gemm(int mode, int trans, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
          int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream,
-         const TileConfig* force, uint16_t* C16) {
+         const TileConfig* force, uint16_t* C16, Scratch* sc = nullptr) {
     const float* c_arg = C16 ? reinterpret_cast<const float*>(C16) : C;
     const int bad = check_args(trans, M, N, K, alpha, A, lda, B, ldb, c_arg, ldc);
     if (bad) return bad;
@@ -816,7 +864,18 @@ int gemm(int mode, int trans, int64_t M, int64_t N, int64_t K, float alpha, cons
         const int rc = select_config(mode, trans, M, N, K, A, lda, B, ldb, beta, &cfg, &src);
         if (rc) return rc;
     }
-    return launch_with(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16);
+    // plan (nothing launched), take the scratch the plan needs, then launch:
+    // a failure to obtain scratch leaves C untouched
+    DryScratch plan;
+    int rc = launch_with(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16, plan);
+    if (rc) return rc;
+    PoolScratch pooled(s);
+    Scratch& use = sc ? *sc : pooled;
+    if (plan.ws || plan.cnt) {
+        rc = use.reserve(plan.ws, plan.cnt);
+        if (rc) return rc;
+    }
+    return launch_with(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16, use);
 }
 
 // ---------------------------------------------------------------------------
@@ -1203,6 +1262,9 @@ const char* gemm355_strerror(int status) {
         case GEMM355_ERR_MODE: return "unknown mode";
         case GEMM355_ERR_BUFFER: return "output buffer too small or file error";
         case GEMM355_ERR_INTERNAL: return "internal error";
+        case GEMM355_ERR_CAPTURE:
+            return "the call needs device scratch that is not allocated yet, and the stream is "
+                   "being captured (run the call once on that stream before capturing)";
         default: break;
     }
     if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

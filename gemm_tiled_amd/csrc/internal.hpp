@@ -208,6 +208,8 @@ hipError_t launch_roof_mfma(int mode, int64_t iters, int blocks, float* sink, do
 hipError_t launch_roof_hbm(const void* buf, int64_t bytes, int blocks, float* sink,
                            hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
+// p[0..n) = value on stream s (a kernel, never a memset).
+hipError_t launch_fill_u32(unsigned* p, int64_t n, unsigned value, hipStream_t s);
 
 // The workgroup -> tile mapping used by every GEMM kernel.  Consecutive
 // workgroup ids are dealt to the 8 XCDs of the chip in turn; the remap gives

@@ -25,12 +25,21 @@
  *     stream) and the call returns without waiting for it;
  *   - the f16r mode writes the rounded operands, and configurations that
  *     split K over workgroups (both modes) write partial tiles and per-tile
- *     arrival counters, into a device workspace that the library allocates on
- *     first use, grows when a call needs more (synchronising the stream
- *     first), and keeps per (device, stream);
- *     calls on one stream are ordered and share it; calls on different
- *     streams use different workspaces; each launch leaves the counters it
- *     used at zero;
+ *     arrival counters, into device scratch that the library keeps in a pool
+ *     per device (at most 8 buffers kept, each as large as the largest call it
+ *     served).  A call holds one pool buffer from its first launch until its
+ *     last launch is enqueued, so calls from several host threads never share
+ *     one in between.  A buffer goes to a later call on the same stream at
+ *     once (stream order), to a call on another stream only once the work of
+ *     its last call has completed.  Buffers are allocated and freed
+ *     stream-ordered (hipMallocAsync / hipFreeAsync on the call's stream): no
+ *     call waits on the host.  Each call works out how much scratch it needs
+ *     before it launches anything, so a failed allocation (GEMM355_ERR_ALLOC)
+ *     leaves C untouched;
+ *   - under stream capture a call allocates nothing: it uses a pool buffer of
+ *     its stream that is already large enough (run the call once on that
+ *     stream first), else it returns GEMM355_ERR_CAPTURE; that buffer then
+ *     belongs to the graph and is never reused or freed;
  *   - every call is thread-safe.
  *
  * Special cases, decided on the host before any launch:
@@ -66,6 +75,7 @@ extern "C" {
 #define GEMM355_ERR_MODE (-103)     /* mode is neither F32 nor F16R */
 #define GEMM355_ERR_BUFFER (-104)   /* output buffer too small */
 #define GEMM355_ERR_INTERNAL (-105) /* no kernel instance fits (library bug) */
+#define GEMM355_ERR_CAPTURE (-106)  /* scratch would have to be allocated during stream capture */
 
 /*
  * C = alpha*A@B + beta*C in f32.  Arguments:

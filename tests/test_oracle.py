@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from tests import oracle_pins as pins
-from workloads import make_inputs
+from workloads import make_inputs, small_integers
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -208,6 +208,46 @@ def test_check_accepts_rounded_reference_and_flags_planted_errors(mode):
     assert st["n_fail"] == 2 and np.isinf(st["max_ratio"])
     band = oracle.check(mode, A, B, C, 1.5, 0.5, bad, rows=(0, 3))
     assert band["n_fail"] == 0
+
+
+def test_check_error_summaries_hand_example():
+    """The lab's two error summaries on a case worked by hand: A = I, B =
+    diag(3, 4), C = 0, alpha 1, beta 0, so the reference is diag(3, 4); one
+    element off by 1 gives max|err| / max|ref| = 1/4 and
+    ||err||_F / ||ref||_F = 1 / sqrt(9 + 16) = 1/5."""
+    A = np.eye(2, dtype=np.float32)
+    B = np.array([[3.0, 0.0], [0.0, 4.0]], dtype=np.float32)
+    C = np.zeros((2, 2), dtype=np.float32)
+    got = np.array([[3.0, 1.0], [0.0, 4.0]], dtype=np.float32)
+    for mode in MODES:
+        st = oracle.check(mode, A, B, C, 1.0, 0.0, got, tol=1.0)
+        assert st["err_max_norm"] == 0.25, st
+        assert st["err_fro"] == 0.2, st
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_check_error_summaries_match_numpy_norms(mode):
+    """err_max_norm and err_fro against numpy's norms of planted errors, on
+    small-integer inputs whose exact product numpy's float64 matmul gives
+    (every partial sum is an integer below 2^53), so the reference side is
+    independent of the oracle."""
+    A, B, C = small_integers(37, 29, 53, seed=21)
+    alpha, beta = 2.0, -0.5
+    ref = alpha * (A.astype(np.float64) @ B.astype(np.float64)) + beta * C.astype(np.float64)
+    rng = np.random.default_rng(22)
+    d = np.zeros_like(ref)
+    pos = rng.integers(0, ref.size, size=40)
+    d.flat[pos] = rng.uniform(-3.0, 3.0, size=40)
+    got = (ref + d).astype(np.float32)
+    d = got.astype(np.float64) - ref            # the error actually planted, after rounding
+    st = oracle.check(mode, A, B, C, alpha, beta, got, tol=1.0)
+    want_max = np.abs(d).max() / np.abs(ref).max()
+    want_fro = np.linalg.norm(d) / np.linalg.norm(ref)
+    assert st["err_max_norm"] == pytest.approx(want_max, rel=1e-12)
+    assert st["err_fro"] == pytest.approx(want_fro, rel=1e-12)
+    # a reference without error reads zero in both
+    st0 = oracle.check(mode, A, B, C, alpha, beta, ref.astype(np.float32), tol=1.0)
+    assert st0["err_max_norm"] == 0.0 and st0["err_fro"] == 0.0
 
 
 def test_check_requires_exact_zero_where_w_is_zero():
