@@ -18,7 +18,7 @@ import os
 
 __all__ = [
     "MODE_F32", "MODE_F16R", "Gemm355Error", "lib", "library_path", "gemm", "gemm_f32",
-    "gemm_f16r_f32acc", "tune", "get_config", "set_config", "parse_config", "list_configs",
+    "gemm_f16r_f32acc", "gemm_noalloc", "tune", "get_config", "set_config", "parse_config", "list_configs",
     "cache_load", "cache_save", "cache_clear", "strerror", "version", "EXPORTS",
 ]
 
@@ -43,6 +43,8 @@ EXPORTS = {
                                            _i64, _p, _i64, _f32, _p, _i64, _p]),
     "gemm_f16r_f16out": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _f32, _p,
                                         _i64, _p, _i64, _f32, _p, _i64, _p]),
+    "gemm355_gemm_noalloc": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64,
+                                            _i64, _f32, _p, _i64, _p, _i64, _f32, _p, _i64, _p]),
     "gemm355_tune": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p, _i64, _f32,
                                     _i64, _p]),
     "gemm355_tune_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64, _i64,
@@ -168,6 +170,22 @@ def gemm(mode, A, B, C, alpha=1.0, beta=0.0, stream=None, transa=False, transb=F
         st = getattr(lib(), name)(M, N, K, *ptrs)
     if st != 0:
         raise Gemm355Error(st, name)
+    return C
+
+
+def gemm_noalloc(mode, A, B, C, alpha=1.0, beta=0.0, stream=None, transa=False, transb=False):
+    """gemm() through gemm355_gemm_noalloc: the same result, with the library's
+    scratch taken from its fixed per-GPU array instead of allocated memory
+    (calls that overlap on one GPU race; see include/gemm355.h)."""
+    M, N, K, lda, ldb, ldc = _operands(A, B, C, transa, transb)
+    if (A.numel() and A.device != C.device) or (B.numel() and B.device != C.device):
+        raise ValueError("A, B and C must be on the same device")
+    st = lib().gemm355_gemm_noalloc(_mode(mode), int(bool(transa)), int(bool(transb)), M, N, K,
+                                    float(alpha), A.data_ptr() or None, lda, B.data_ptr() or None,
+                                    ldb, float(beta), C.data_ptr() or None, ldc,
+                                    _stream_ptr(stream))
+    if st != 0:
+        raise Gemm355Error(st, "gemm355_gemm_noalloc")
     return C
 
 

@@ -416,10 +416,10 @@ int select_config(int mode, int trans, int64_t M, int64_t N, int64_t K, const fl
 // their arrival counters.  The entry points that may allocate lease it from
 // a pool per device (workspace.hpp: the lease lasts from the call's first
 // request until its last launch is enqueued; growth is stream-ordered, the
-// host never waits).
+// host never waits); gemm355_gemm_noalloc takes it from a fixed device array.
 // Every call is first planned with a DryScratch (no launch), which records
-// what it will ask for, so a failure to allocate is reported before any
-// kernel is enqueued.
+// what it will ask for, so a failure to allocate, or a call larger than the
+// fixed array, is reported before any kernel is enqueued.
 // ---------------------------------------------------------------------------
 int status_of(hipError_t e) { return e == hipSuccess ? 0 : static_cast<int>(e); }
 
@@ -1119,6 +1119,96 @@ int gemm_f16r_f16out(int transa, int transb, int64_t M, int64_t N, int64_t K, fl
                          ldc, stream, nullptr, C16));
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing (gemm355_gemm_noalloc): its scratch
+// is this file-scope device array, one copy per GPU, held until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// names a stand-in, not device memory): the first call on a device looks up
+// the device address of that GPU's copy once, and every launch takes that.
+// Layout: kFixedCounters arrival counters, then the workspace.
+// ---------------------------------------------------------------------------
+namespace g355 {
+namespace {
+constexpr size_t kFixedScratchBytes = size_t{160} << 20;
+constexpr size_t kFixedCounters = 16384;
+constexpr size_t kFixedCounterBytes = kFixedCounters * sizeof(unsigned);   // 64 KiB
+}  // namespace
+}  // namespace g355
+
+static __device__ __align__(256) unsigned char scratch[g355::kFixedScratchBytes];
+
+namespace g355 {
+namespace {
+
+// The device address of this GPU's copy of `scratch`, looked up once per
+// device with that device current.
+int fixed_scratch_base(unsigned char** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return status_of(e);
+    static std::mutex mu;
+    static std::map<int, unsigned char*> base;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = base.find(dev);
+    if (it == base.end()) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return status_of(e);
+        if (!ptr) return GEMM355_ERR_INTERNAL;
+        it = base.emplace(dev, static_cast<unsigned char*>(ptr)).first;
+    }
+    *out = it->second;
+    return 0;
+}
+
+class FixedScratch : public Scratch {
+public:
+    FixedScratch(unsigned char* base, hipStream_t s) : base_(base), s_(s) {}
+    int workspace(size_t bytes, void** out) override {
+        if (bytes > kFixedScratchBytes - kFixedCounterBytes) return GEMM355_ERR_SCRATCH;
+        *out = base_ + kFixedCounterBytes;
+        return 0;
+    }
+    int counters(size_t n, unsigned** out) override {
+        if (n > kFixedCounters) return GEMM355_ERR_SCRATCH;
+        *out = reinterpret_cast<unsigned*>(base_);
+        return 0;
+    }
+    // the array keeps the last call's contents: the counters this call uses
+    // are cleared (by a kernel on the call's stream) before its launches
+    int reserve(size_t bytes, size_t n) override {
+        if (bytes > kFixedScratchBytes - kFixedCounterBytes || n > kFixedCounters)
+            return GEMM355_ERR_SCRATCH;
+        if (n == 0) return 0;
+        return status_of(launch_fill_u32(reinterpret_cast<unsigned*>(base_),
+                                         static_cast<int64_t>(n), 0u, s_));
+    }
+
+private:
+    unsigned char* base_;
+    hipStream_t s_;
+};
+
+}  // namespace
+}  // namespace g355
+
+extern "C" {
+
+int gemm355_gemm_noalloc(int mode, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                         float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                         float beta, float* C, int64_t ldc, void* stream) {
+    if (mode != GEMM355_MODE_F32 && mode != GEMM355_MODE_F16R) return GEMM355_ERR_MODE;
+    int trans = 0;
+    if (const int bad = trans_of(transa, transb, &trans)) return bad;
+    unsigned char* base = nullptr;
+    if (const int rc = fixed_scratch_base(&base)) return rc;
+    FixedScratch fixed(base, static_cast<hipStream_t>(stream));
+    return shift_ex(gemm(mode, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                         nullptr, nullptr, &fixed));
+}
+
 int gemm355_tune(int mode, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                  const float* B, int64_t ldb, float beta, int64_t ldc, void* stream) {
     return tune(mode, 0, M, N, K, A, lda, B, ldb, beta, ldc, stream);
@@ -1264,7 +1354,10 @@ const char* gemm355_strerror(int status) {
         case GEMM355_ERR_INTERNAL: return "internal error";
         case GEMM355_ERR_CAPTURE:
             return "the call needs device scratch that is not allocated yet, and the stream is "
-                   "being captured (run the call once on that stream before capturing)";
+                   "being captured (run the call once before capturing, or use "
+                   "gemm355_gemm_noalloc)";
+        case GEMM355_ERR_SCRATCH:
+            return "the call needs more scratch than the fixed array of gemm355_gemm_noalloc holds";
         default: break;
     }
     if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

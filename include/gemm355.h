@@ -39,7 +39,8 @@
  *   - under stream capture a call allocates nothing: it uses a pool buffer of
  *     its stream that is already large enough (run the call once on that
  *     stream first), else it returns GEMM355_ERR_CAPTURE; that buffer then
- *     belongs to the graph and is never reused or freed;
+ *     belongs to the graph and is never reused or freed (gemm355_gemm_noalloc
+ *     captures without this cost);
  *   - every call is thread-safe.
  *
  * Special cases, decided on the host before any launch:
@@ -76,6 +77,7 @@ extern "C" {
 #define GEMM355_ERR_BUFFER (-104)   /* output buffer too small */
 #define GEMM355_ERR_INTERNAL (-105) /* no kernel instance fits (library bug) */
 #define GEMM355_ERR_CAPTURE (-106)  /* scratch would have to be allocated during stream capture */
+#define GEMM355_ERR_SCRATCH (-107)  /* larger than the fixed scratch of gemm355_gemm_noalloc */
 
 /*
  * C = alpha*A@B + beta*C in f32.  Arguments:
@@ -139,6 +141,29 @@ int gemm_f16r_f32acc_ex(int transa, int transb, int64_t M, int64_t N, int64_t K,
 int gemm_f16r_f16out(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
                      const float* A, int64_t lda, const float* B, int64_t ldb,
                      float beta, uint16_t* C16, int64_t ldc, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * variant of gemm_f32_ex (mode GEMM355_MODE_F32) and gemm_f16r_f32acc_ex
+ * (mode GEMM355_MODE_F16R) that allocates no device memory.  Arguments,
+ * special cases, results and return codes are those of the _ex entry point
+ * of the mode (an invalid mode returns GEMM355_ERR_MODE).  Its scratch is one
+ * fixed device array per GPU of 160 MiB (64 KiB of arrival counters, the rest
+ * for packed operands and partial tiles), held from the first call on that
+ * GPU until the process ends; the first call on a GPU looks up the array's
+ * address there.  A call needing more returns GEMM355_ERR_SCRATCH with
+ * nothing launched: the f16r mode packs 2 (M + N) K bytes of binary16
+ * operands (M, N rounded up to 256, K to 64), and calls that split K over
+ * workgroups keep up to 128 MiB of partial tiles (f16r 8192^3 or 3072^3, for
+ * example, do not fit; 4096^3 does).  Every call on a GPU shares its
+ * array, which keeps the last call's contents (the counters a call uses are
+ * cleared by a kernel on its stream first): calls that overlap on one GPU,
+ * from any stream or thread, race and must be ordered by the caller.
+ */
+int gemm355_gemm_noalloc(int mode, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                         float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                         float beta, float* C, int64_t ldc, void* stream);
 
 /*
  * Per-shape tile autotuning (phobos docs, "gemm, f32", section "Tuning": time
