@@ -1,28 +1,38 @@
 """Benchmark of libgemm355 on one MI355X: TFLOP/s = 2MNK/t of C = alpha*A@B + beta*C.
 
 One "step" is one library call over the whole path (for f16r: the operand
-rounding passes and the GEMM).  The headline workload is the f32 GEMM at
+rounding pass and the GEMM).  The headline workload is the f32 GEMM at
 M = N = K = 4096 (alpha 1, beta 0); the line also carries the beta = 1 run and
 the f16r GEMM at 8192^3 (alpha 0.75, beta -0.25), each with its fraction of the
-matrix-core roof re-measured on this chip (the Matrix Multiplication lab,
-"Part 1 -- the two roofs, again"), and the CPU oracle timed on host cores.
+matrix-core roof re-measured on this chip in the same run (the Matrix
+Multiplication lab, "Part 1 -- the two roofs, again"), the shader clocks,
+board power and temperature sampled while it ran, and the CPU oracle timed on
+the host cores (the lab, "Part 2 -- the ladder": every rung checked and timed
+in the same run).
 
-Protocol (the lab's helpers): every result is checked against the oracle before
-it is timed; clocks are settled with synchronised calls for a quarter second;
-then exactly --steps calls are timed between two device synchronisations, with
-an event pair around every call on the stream the library launches on.
+Protocol: every result is checked against the oracle before it is timed; the
+clocks are brought to their working level with synchronised calls first; then
+exactly --steps calls are timed between two device synchronisations, with an
+event pair around every call on the stream the library launches on.  Tiles are
+the library's own choice (its heuristic), the same choice a profiled run of the
+same command makes; --tune runs the library's autotuner first.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--workloads a,b,...] [--no-tune] [--json-out path]
+                       [--workloads a,b,...] [--tune] [--json-out path]
+       python bench.py --profile WORKLOAD [--calls N] [--calibrate-copy]
+       python bench.py --summarize-trace DIR --out FILE --cmd "..."
+       python bench.py --summarize-counters WORKLOAD DIR [DIR ...] --out FILE --cmd "..."
 Prints progress on stderr and ONE JSON line on stdout.
 """
 from __future__ import annotations
 
 import argparse
+import collections
 import json
 import os
 import re
 import sys
+import threading
 import time
 
 import numpy as np
@@ -38,6 +48,9 @@ SCORED = ["f32_4096_a1_b0", "f32_4096_a1_b1", "f16r_8192_a0.75_b-0.25"]
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
 PEAK_TFLOPS = {"f32": 157.3, "f16r": 2500.0}
 PEAK_HBM_GBS = 8000.0
+# Matrix instruction forms of the roof kernel (gemm355_roof_mfma's `form`).
+ROOF_FORMS = {"f32": {0: "v_mfma_f32_32x32x2_f32", 1: "v_mfma_f32_16x16x4_f32"},
+              "f16r": {0: "v_mfma_f32_32x32x16_f16", 1: "v_mfma_f32_16x16x32_f16"}}
 
 
 def log(msg):
@@ -51,20 +64,26 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workloads", default=",".join(SCORED))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-tune", action="store_true")
+    ap.add_argument("--tune", action="store_true",
+                    help="run the library's autotuner for each workload before timing it")
     ap.add_argument("--no-roofs", action="store_true")
     ap.add_argument("--roof-seconds", type=float, default=2.0)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle sample")
+    ap.add_argument("--sustain-seconds", type=float, default=1.5,
+                    help="back-to-back calls of each workload with the clocks and power sampled")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="target CPU time of each oracle sample")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--profile", metavar="WORKLOAD", default=None,
+                    help="run only this workload's call --calls times (for a profiler)")
+    ap.add_argument("--calls", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB copy kernel (byte-counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR", default=None,
-                    help="write a markdown summary of a rocprofv3 --kernel-trace --stats run")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
-                    help="summarise FETCH_SIZE / WRITE_SIZE runs into an HBM-traffic table")
+                    help="markdown summary of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ARG", default=None,
+                    help="WORKLOAD DIR [DIR ...]: markdown summary of rocprofv3 --pmc runs")
     ap.add_argument("--out", default=None, help="output file of the --summarize-* modes")
-    ap.add_argument("--cmd", default="", help="the command that produced the profile")
+    ap.add_argument("--cmd", default="", help="the commands that produced the profile")
     ap.add_argument("--sweep", metavar="OUT_MD", default=None,
                     help="shape and alignment sweep of both modes (sizes 128..8192, n = "
                          "4088..4104 and 2048..2304, fixed-tile steps); markdown to OUT_MD")
@@ -80,8 +99,11 @@ def main():
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, args.cmd)
         return
-    if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.out, args.cmd)
+    if args.summarize_counters:
+        if len(args.summarize_counters) < 2:
+            raise SystemExit("--summarize-counters WORKLOAD DIR [DIR ...]")
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1:], args.out,
+                           args.cmd)
         return
 
     if args.gpus != 1:
@@ -95,7 +117,7 @@ def main():
     import torch
 
     import gemm_tiled_amd as g
-    from workloads import WORKLOADS, sample_indices, workload_inputs
+    from workloads import WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -106,9 +128,11 @@ def main():
     log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), "
         f"{props.multi_processor_count} CUs; libgemm355 {g.version()}")
 
+    if args.profile:
+        profile_run(g, torch, dev, WORKLOADS[args.profile], args.calls, args.calibrate_copy)
+        return
     if args.calibrate_copy:
         copy_calibration(g, torch, dev)
-
     if args.sweep:
         shape_sweep(g, torch, dev, args.sweep, args.sweep_repeats)
         return
@@ -123,25 +147,20 @@ def main():
     roofs = {}
     if not args.no_roofs:
         roofs = measure_roofs(g, torch, dev, args.roof_seconds)
-        log(f"measured roofs: {json.dumps(roofs)}")
+        log("measured roofs: " + json.dumps({k: v for k, v in roofs.items() if k != "forms"}))
 
     # -------------------------------------------------------------- workloads
     names = [n for n in args.workloads.split(",") if n]
-    runs = {}
-    for name in names:
-        w = WORKLOADS[name]
-        runs[name] = bench_workload(g, torch, dev, w, args, roofs, workload_inputs,
-                                    sample_indices)
+    runs = {name: bench_workload(g, torch, dev, WORKLOADS[name], args, roofs) for name in names}
+
+    # ------------------------------------------- the oracle on the host cores
+    if not args.no_cpu_baseline:
+        for name in names:
+            runs[name]["oracle"] = oracle_rate(WORKLOADS[name], args.cpu_seconds)
 
     primary = PRIMARY if PRIMARY in runs else names[0]
     pr = runs[primary]
     w = WORKLOADS[primary]
-
-    # --------------------------------------------------------- CPU baseline
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_seconds, workload_inputs)
-
     line = {
         "metric": METRIC,
         "value": pr["tflops_job"],
@@ -158,7 +177,7 @@ def main():
         "config": {"workload": primary, "mode": w.mode, "M": w.M, "N": w.N, "K": w.K,
                    "alpha": w.alpha, "beta": w.beta, "tile": pr["tile"]},
         "roofline": pr["roofline"],
-        "cpu_baseline": cpu,
+        "cpu_baseline": pr.get("oracle"),
         "measured_roof": roofs or None,
         "frac_of_measured_roof": pr.get("frac_of_measured_roof"),
         "workloads": runs,
@@ -170,42 +189,193 @@ def main():
     print(text, flush=True)
 
 
+# ---------------------------------------------------------------------------
+# Clocks, power and temperature while the GPU works (the lab's "Setup" keeps a
+# sampler beside every sustained run: a roof or a timing means little without
+# the clock it ran at).  Read through the amdsmi module of the ROCm install.
+# ---------------------------------------------------------------------------
+_AMDSMI = None
+
+
+def _amdsmi_handle():
+    """(module, processor handle) of the GPU, or None when amdsmi is missing."""
+    global _AMDSMI
+    if _AMDSMI is not None:
+        return _AMDSMI or None
+    try:
+        rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+        path = os.path.join(rocm, "share", "amd_smi")
+        if os.path.isdir(path) and path not in sys.path:
+            sys.path.append(path)
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        _AMDSMI = (amdsmi, handles[0]) if handles else False
+    except Exception as e:   # noqa: BLE001 -- the sampler is optional
+        log(f"amdsmi unavailable ({e}); clocks and power are not recorded")
+        _AMDSMI = False
+    return _AMDSMI or None
+
+
+class GpuSampler:
+    """Background thread reading the shader clock of every XCD, the socket
+    power and the hotspot temperature every `period` seconds while the block
+    it guards runs; summary() gives medians and extremes."""
+
+    def __init__(self, period=0.05):
+        self.period = period
+        self.rows = []
+        self._stop = threading.Event()
+        self._thread = None
+
+    def _read(self, smi, h):
+        m = smi.amdsmi_get_gpu_metrics_info(h)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float))
+                and 0 < c < 10000]
+        power = m.get("current_socket_power")
+        temp = m.get("temperature_hotspot")
+        return (float(np.mean(clks)) if clks else None,
+                float(power) if isinstance(power, (int, float)) else None,
+                float(temp) if isinstance(temp, (int, float)) else None)
+
+    def _loop(self, smi, h):
+        while not self._stop.is_set():
+            try:
+                self.rows.append(self._read(smi, h))
+            except Exception:   # noqa: BLE001 -- a failed read is skipped
+                pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        got = _amdsmi_handle()
+        if got:
+            self._thread = threading.Thread(target=self._loop, args=got, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.rows:
+            return None
+        out = {"samples": len(self.rows), "period_s": self.period, "source": "amdsmi"}
+        for idx, key in ((0, "gfx_mhz"), (1, "power_w"), (2, "hotspot_c")):
+            vals = [r[idx] for r in self.rows if r[idx] is not None]
+            if vals:
+                out[f"{key}_median"] = round(float(np.median(vals)), 1)
+                out[f"{key}_min"] = round(float(np.min(vals)), 1)
+                out[f"{key}_max"] = round(float(np.max(vals)), 1)
+        return out
+
+
+# ---------------------------------------------------------------------------
+# GPU timing.
+# ---------------------------------------------------------------------------
+def warm_clocks(call, torch, seconds=0.25):
+    """Synchronised calls for `seconds`, so the clocks sit at the level the
+    work itself holds them at before anything is timed."""
+    until = time.perf_counter() + seconds
+    while True:
+        call()
+        torch.cuda.synchronize()
+        if time.perf_counter() >= until:
+            return
+
+
+def call_times(call, torch, seconds=0.5, at_least=3, per_sample=1, chunk=8):
+    """GPU seconds per call, one sample per event pair: chunks of `chunk`
+    samples are queued back to back (each sample `per_sample` calls between its
+    two events) and read after one synchronisation per chunk, until `seconds`
+    have passed and at least `at_least` samples exist.  Warm the clocks first."""
+    stream = torch.cuda.current_stream()
+    out = []
+    until = time.perf_counter() + seconds
+    while len(out) < at_least or time.perf_counter() < until:
+        marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(chunk)]
+        for begin, end in marks:
+            begin.record(stream)
+            for _ in range(per_sample):
+                call()
+            end.record(stream)
+        marks[-1][1].synchronize()
+        out.extend(b.elapsed_time(e) * 1e-3 / per_sample for b, e in marks)
+    return out
+
+
+def median_call_time(call, torch, seconds=0.5, per_sample=1):
+    warm_clocks(call, torch, min(0.25, seconds / 2))
+    return float(np.median(call_times(call, torch, seconds, per_sample=per_sample)))
+
+
+def sustained(launch, torch, seconds, in_flight=4):
+    """Keep up to `in_flight` launches queued for `seconds`; returns (launches,
+    GPU seconds between an event before the first and one after the last)."""
+    stream = torch.cuda.current_stream()
+    first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    queued = collections.deque()
+    first.record(stream)
+    launches = 0
+    until = time.perf_counter() + seconds
+    while time.perf_counter() < until:
+        launch()
+        launches += 1
+        done = torch.cuda.Event()
+        done.record(stream)
+        queued.append(done)
+        if len(queued) > in_flight:
+            queued.popleft().synchronize()
+    last.record(stream)
+    last.synchronize()
+    return launches, first.elapsed_time(last) * 1e-3
+
+
+# ---------------------------------------------------------------------------
+# Roofs (the lab's "Part 1 -- the two roofs, again"): a kernel of nothing but
+# independent matrix instructions, in each instruction form of the mode, run
+# for `seconds` with the clocks sampled; the fastest form is the mode's roof.
+# The HBM read roof: a 16-byte grid-stride read of 4 GiB (beyond the 256 MB
+# memory-side cache).
+# ---------------------------------------------------------------------------
 def measure_roofs(g, torch, dev, seconds):
     import ctypes
 
     L = g.lib()
-    out = {}
-    stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
+    out = {"forms": {}}
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     blocks = 256 * 4   # four workgroups of four waves per CU
     sink = torch.empty(blocks * 256, device=dev, dtype=torch.float32)
     for mode, name in ((0, "f32"), (1, "f16r")):
-        iters = 2000 if mode == 0 else 4000
-        flops = ctypes.c_double(0)
+        best = None
+        for form, instr in ROOF_FORMS[name].items():
+            iters = 2000 if mode == 0 else 4000
+            flops = ctypes.c_double(0)
 
-        def launch():
-            st = L.gemm355_roof_mfma(mode, iters, blocks, ctypes.c_void_p(sink.data_ptr()),
-                                     ctypes.byref(flops), sp)
-            if st != 0:
-                raise g.Gemm355Error(st, "gemm355_roof_mfma")
+            def launch(mode=mode, form=form, iters=iters, flops=flops):
+                st = L.gemm355_roof_mfma(mode, form, iters, blocks,
+                                         ctypes.c_void_p(sink.data_ptr()), ctypes.byref(flops), sp)
+                if st != 0:
+                    raise g.Gemm355Error(st, "gemm355_roof_mfma")
 
-        launch()
-        torch.cuda.synchronize()
-        # sustained: back-to-back launches for `seconds`, synchronising every 4 calls
-        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s_ev.record()
-        n, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < seconds:
             launch()
-            n += 1
-            if n % 4 == 0:
-                torch.cuda.synchronize()
-        e_ev.record()
-        e_ev.synchronize()
-        t = s_ev.elapsed_time(e_ev) / 1e3 / n
-        out[f"mfma_{name}_tflops"] = flops.value / t / 1e12
+            torch.cuda.synchronize()
+            with GpuSampler() as smp:
+                n, span = sustained(launch, torch, seconds)
+            rate = flops.value * n / span / 1e12
+            out["forms"][f"{name}:{instr}"] = {"tflops": round(rate, 2), "launches": n,
+                                               "seconds": round(span, 3), "gpu": smp.summary()}
+            log(f"roof {name} {instr}: {rate:.1f} TFLOP/s over {span:.2f} s"
+                + (f" at {smp.summary()['gfx_mhz_median']} MHz" if smp.summary() else ""))
+            if best is None or rate > best[0]:
+                best = (rate, instr, smp.summary())
+        out[f"mfma_{name}_tflops"] = best[0]
+        out[f"mfma_{name}_form"] = best[1]
+        out[f"mfma_{name}_gpu"] = best[2]
         out[f"mfma_{name}_published_tflops"] = PEAK_TFLOPS[name]
-    # HBM read roof: 4 GiB, beyond the 256 MB last-level cache
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, device=dev, dtype=torch.float32)
     sink1 = torch.zeros(1, device=dev, dtype=torch.float32)
@@ -216,53 +386,40 @@ def measure_roofs(g, torch, dev, seconds):
         if st != 0:
             raise g.Gemm355Error(st, "gemm355_roof_hbm")
 
-    t = steady(read, torch, 0.5)
+    with GpuSampler() as smp:
+        t = median_call_time(read, torch, 0.5)
     out["hbm_read_gbs"] = nbytes / t / 1e9
+    out["hbm_gpu"] = smp.summary()
     out["hbm_published_gbs"] = PEAK_HBM_GBS
     del buf
     torch.cuda.empty_cache()
     return out
 
 
-def steady(fn, torch, seconds=0.5, min_calls=3, batch=1):
-    """Median seconds per call after settling (the lab's steady()).  With
-    batch > 1 each sample times `batch` back-to-back calls between two events
-    and divides: for calls of a few microseconds, the GPU time per call in a
-    stream of calls, without the host's per-call launch latency."""
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds / 2:
-        fn()
-        torch.cuda.synchronize()
-    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ts, t0 = [], time.perf_counter()
-    while time.perf_counter() - t0 < seconds or len(ts) < min_calls:
-        s_ev.record()
-        for _ in range(batch):
-            fn()
-        e_ev.record()
-        e_ev.synchronize()
-        ts.append(s_ev.elapsed_time(e_ev) / 1e3 / batch)
-    return float(np.median(ts))
+# ---------------------------------------------------------------------------
+# One workload: check, then time exactly --steps calls.
+# ---------------------------------------------------------------------------
+def _workload_tensors(w, torch, dev):
+    from workloads import workload_inputs
+    A, B, C = workload_inputs(w)
+    return (A, B, C), (torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev),
+                       torch.from_numpy(C).to(dev))
 
 
-def bench_workload(g, torch, dev, w, args, roofs, workload_inputs, sample_indices):
+def bench_workload(g, torch, dev, w, args, roofs):
     import oracle   # correctness check before timing (CPU, test infrastructure)
+    from workloads import sample_indices
 
     log(f"{w.name}: generating inputs")
-    A, B, C = workload_inputs(w)
-    tA = torch.from_numpy(A).to(dev)
-    tB = torch.from_numpy(B).to(dev)
-    tC0 = torch.from_numpy(C).to(dev)
-    tC = tC0.clone()
+    (A, B, C), (tA, tB, tC) = _workload_tensors(w, torch, dev)
     fn = g.gemm_f32 if w.mode == "f32" else g.gemm_f16r_f32acc
-
-    if not args.no_tune:
+    if args.tune:
         log(f"{w.name}: tuning")
         g.tune(w.mode, tA, tB, tC, beta=w.beta)
     tile = g.get_config(w.mode, w.M, w.N, w.K, beta=w.beta)
     log(f"{w.name}: tile {tile}")
 
-    # correctness first: one call on a fresh C, sampled oracle elements
+    # correctness first: one call on the workload's C, oracle-sampled elements
     fn(tA, tB, tC, w.alpha, w.beta)
     torch.cuda.synchronize()
     got = tC.cpu().numpy()
@@ -278,110 +435,136 @@ def bench_workload(g, torch, dev, w, args, roofs, workload_inputs, sample_indice
     del got
 
     stream = torch.cuda.current_stream()
-    call = lambda: fn(tA, tB, tC, w.alpha, w.beta)   # noqa: E731  (C drifts; timing is data-independent)
+
+    def call():   # C drifts from call to call when beta != 0; the timing does not depend on it
+        fn(tA, tB, tC, w.alpha, w.beta)
 
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    # settle the clocks (synchronised calls, a quarter second)
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < 0.25:
-        call()
-        torch.cuda.synchronize()
+    warm_clocks(call, torch, 0.25)
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s_ev, e_ev in evs:
-        s_ev.record(stream)
-        call()
-        e_ev.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = np.array([s.elapsed_time(e) / 1e3 for s, e in evs])
-    gpu_total = float(per.sum())
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    with GpuSampler(period=0.01) as smp:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for begin, end in marks:
+            begin.record(stream)
+            call()
+            end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    per = np.array([b.elapsed_time(e) * 1e-3 for b, e in marks])
+    # The timed steps last tens of milliseconds, about the update interval of
+    # the board's power reading: the clocks and power of the call are sampled
+    # over a sustained stretch of back-to-back calls as well.
+    with GpuSampler() as held:
+        n_held, span_held = sustained(call, torch, args.sustain_seconds)
 
     flops = w.flops
-    tflops_job = flops * args.steps / wall / 1e12
-    tflops_med = flops / float(np.median(per)) / 1e12
     avg = float(per.mean())
     achieved = flops / avg / 1e12
     peak = PEAK_TFLOPS[w.mode]
     roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": None,
-            "kernel": f32_kernel_name(tile) if w.mode == "f32" else
-            "pack_kernel + gemm_f16_kernel (whole call)",
-            "per_launch_flops": flops}
+            "kernel": dominant_kernel(w.mode, tile),
+            "per_launch_flops": flops,
+            "timed_as": "mean of the event-timed library calls (one launch for the f32 ring; "
+                        "the packing pass plus the GEMM launch for f16r)"}
     res = {
         "mode": w.mode, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
         "tile": tile,
         "ms_per_step": wall / args.steps * 1e3,
         "ms_median_call": float(np.median(per)) * 1e3,
         "ms_mean_call": avg * 1e3,
-        "gpu_busy_frac": gpu_total / wall,
-        "tflops_job": tflops_job,
-        "tflops_median_call": tflops_med,
+        "gpu_busy_frac": float(per.sum()) / wall,
+        "tflops_job": flops * args.steps / wall / 1e12,
+        "tflops_median_call": flops / float(np.median(per)) / 1e12,
         "parity_max_ratio_sampled": ratio,
+        "gpu_timed_steps": smp.summary(),
+        "sustained": {"tflops": w.flops * n_held / span_held / 1e12, "calls": n_held,
+                      "seconds": round(span_held, 3), "gpu": held.summary()},
         "roofline": roof,
     }
     tr = committed_traffic(w.mode, w.name, tile)
     if tr is not None:
         roof["traffic"] = tr["traffic_bytes_per_launch"]
         roof["traffic_source"] = tr["source"]
-    key = "mfma_f32_tflops" if w.mode == "f32" else "mfma_f16r_tflops"
+    key = f"mfma_{w.mode}_tflops"
     if roofs.get(key):
-        res["frac_of_measured_roof"] = round(tflops_med / roofs[key], 4)
-    log(f"{w.name}: {tflops_job:.2f} TFLOP/s over {args.steps} steps "
-        f"({res['ms_per_step']:.4f} ms/step, median call {res['ms_median_call']:.4f} ms, "
-        f"{tflops_med:.2f} TFLOP/s median); frac of published peak {roof['frac']:.3f}"
-        + (f", of measured roof {res['frac_of_measured_roof']:.3f}" if "frac_of_measured_roof" in res
-           else ""))
-    del tA, tB, tC, tC0
+        res["frac_of_measured_roof"] = round(res["tflops_median_call"] / roofs[key], 4)
+    gpu = res["sustained"]["gpu"] or {}
+    log(f"{w.name}: {res['tflops_job']:.2f} TFLOP/s over {args.steps} steps "
+        f"({res['ms_per_step']:.4f} ms/step, median call {res['ms_median_call']:.4f} ms); "
+        f"of published peak {roof['frac']:.3f}"
+        + (f", of measured roof {res['frac_of_measured_roof']:.3f}"
+           if "frac_of_measured_roof" in res else "")
+        + (f"; sustained {res['sustained']['tflops']:.1f} TFLOP/s at {gpu.get('gfx_mhz_median')} MHz, "
+           f"{gpu.get('power_w_median')} W" if gpu else ""))
+    del tA, tB, tC
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(w, target_seconds, workload_inputs):
-    """The oracle as it stands, timed on the host cores over the whole workload
-    when that fits in ~30 s, else over a band of output rows sized to about
-    target_seconds; throughput in TFLOP/s (2*rows*N*K / t)."""
+def oracle_rate(w, target_seconds):
+    """The oracle as it stands (float64 triple loop, the bound alongside),
+    timed on the host cores over the whole workload when that fits in ~30 s,
+    else over a band of output rows sized to about target_seconds; the rate
+    in TFLOP/s (2 * rows * N * K / t)."""
     import oracle
+    from workloads import workload_inputs
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
     os.environ["OMP_NUM_THREADS"] = str(threads)
     A, B, C = workload_inputs(w)
 
-    def timed(rows):
+    def run(rows):
         t0 = time.perf_counter()
         oracle.check(w.mode, A, B, C, w.alpha, w.beta, C, rows=(0, rows))
         return time.perf_counter() - t0
 
-    # per-row cost from two probes (the widening of A and B is a fixed cost)
-    t16, t64 = timed(16), timed(64)
-    per_row = max((t64 - t16) / 48.0, 1e-6)
-    fixed = max(t16 - 16 * per_row, 0.0)
-    if fixed + per_row * w.M <= 30.0:
-        rows = w.M
-    else:
-        rows = int(min(w.M, max(64, (target_seconds - fixed) / per_row)))
-    t = timed(rows)
-    flops = 2.0 * rows * w.N * w.K
+    # cost per row from two short bands (widening A and B is a fixed cost)
+    t_a, t_b = run(16), run(64)
+    per_row = max((t_b - t_a) / 48.0, 1e-6)
+    fixed = max(t_a - 16 * per_row, 0.0)
+    rows = w.M if fixed + per_row * w.M <= 30.0 else \
+        int(min(w.M, max(64, (target_seconds - fixed) / per_row)))
+    t = run(rows)
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
-            for ln in f:
-                if ln.startswith("model name"):
-                    cpu_model = ln.split(":", 1)[1].strip()
-                    break
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), "")
     except OSError:
         pass
     what = "the whole workload" if rows == w.M else f"{rows} of {w.M} output rows"
-    res = {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    res = {"value": 2.0 * rows * w.N * w.K / t / 1e12, "unit": "TFLOP/s", "cores": threads,
+           "kind": "oracle", "seconds": round(t, 2),
            "sample": f"{what} of {w.name} (float64 triple loop incl. operand widening and "
                      f"the bound), {t:.1f} s", "cpu": cpu_model}
-    log(f"cpu baseline: {res['value'] * 1e3:.2f} GFLOP/s on {threads} threads ({res['sample']})")
+    log(f"oracle {w.name}: {res['value'] * 1e3:.2f} GFLOP/s on {threads} threads "
+        f"({res['sample']})")
     return res
+
+
+def profile_run(g, torch, dev, w, calls, calibrate):
+    """The workload's call, `calls` times after 3 untimed ones, with the tile
+    the benchmark uses (nothing else runs on the GPU besides the optional
+    calibration copy): what a profiler of this command sees."""
+    (_, _, _), (tA, tB, tC) = _workload_tensors(w, torch, dev)
+    fn = g.gemm_f32 if w.mode == "f32" else g.gemm_f16r_f32acc
+    tile = g.get_config(w.mode, w.M, w.N, w.K, beta=w.beta)
+    log(f"profile {w.name}: tile {tile}, {calls} calls")
+    for _ in range(3):
+        fn(tA, tB, tC, w.alpha, w.beta)
+    torch.cuda.synchronize()
+    for _ in range(calls):
+        fn(tA, tB, tC, w.alpha, w.beta)
+    torch.cuda.synchronize()
+    if calibrate:
+        copy_calibration(g, torch, dev)
+    print(json.dumps({"profile": w.name, "tile": tile, "calls": calls}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -394,11 +577,6 @@ SWEEP_QUANT = list(range(4088, 4105)) + [2048, 2049, 2056, 2064, 2080, 2112, 217
 SWEEP_FIXED = [2048, 2049, 4096, 4097]
 FIXED_TILE = {"f32": "BM=128 BN=128 BK=32 ST=2 WM=2 WN=2 GM=8",
               "f16r": "BM=128 BN=128 BK=64 ST=1 WM=2 WN=2 GM=8"}
-
-
-def _tile_fields(tile):
-    return {k: int(v) for k, v in (t.split("=") for t in tile.split() if "=" in t and
-                                    t.split("=")[1].isdigit())}
 
 
 def _plan_of(g, mode, n, pin=None):
@@ -474,7 +652,7 @@ def shape_sweep(g, torch, dev, out, repeats):
         order = list(cases)
         rng.shuffle(order)
         for case in order:
-            times[case].append(steady(calls[case], torch, seconds=0.3))
+            times[case].append(median_call_time(calls[case], torch, 0.3))
         log(f"sweep: round {rnd + 1} of {repeats} done")
 
     rows = []
@@ -496,7 +674,8 @@ def shape_sweep(g, torch, dev, out, repeats):
              "Command:", "", "```", "python bench.py --sweep profiles/sweep_shapes.md", "```", "",
              "Square n x n x n, A, B, C iid N(0,1) (seed n), alpha = 1, beta = 0.  Every case is "
              "checked against the oracle on 256 sampled elements before it is timed; each time "
-             f"is the median of {repeats} shuffled rounds of the lab's steady() (0.3 s each).  "
+             f"is the median of {repeats} shuffled rounds, each the median of event-timed calls "
+             "over 0.3 s after warming the clocks.  "
              "`tuned` lets the library's tuner pick the tile per shape; `fixed` pins one 128 x 128 "
              "tile, so its step isolates the cost of the ragged edge.", ""]
     lines += ["## One-element steps", "", "| mode | tiling | 2048 -> 2049 time | 4096 -> 4097 time |",
@@ -552,7 +731,7 @@ def precision_study(g, torch, dev, out):
             vs64 = oracle.check("f32", A, B, zeros, 1.0, 0.0, got, tol=1.0)
             # and against the float64 product of the binary16-rounded inputs
             vsr = oracle.check("f16r", A, B, zeros, 1.0, 0.0, got, tol=1.0)
-            t = steady(fn, torch, 0.5)
+            t = median_call_time(fn, torch, 0.5)
             rows.append({"n": n, "variant": label, "seconds": t,
                          "tflops": 2.0 * n ** 3 / t / 1e12, "bytes_per_element": nbytes,
                          "err_max_norm": vs64["err_max_norm"], "err_fro": vs64["err_fro"],
@@ -572,7 +751,7 @@ def precision_study(g, torch, dev, out):
              "max error max|C - ref| / max|ref| and relative Frobenius error "
              "||C - ref|| / ||ref||.  The last two columns measure the same against the float64 "
              "product of the binary16-rounded inputs, which separates the rounding of the "
-             "operands (and of the output) from the f32 accumulation.  Times: steady(), "
+             "operands (and of the output) from the f32 accumulation.  Times: event-timed calls, "
              "median over 0.5 s.", "",
              "| n | variant | TFLOP/s | speedup vs f32 | bytes/element of C | max err (norm.) | "
              "Frobenius | max err vs rounded inputs | Frobenius vs rounded inputs |",
@@ -645,8 +824,8 @@ def skinny_sweep(g, torch, dev, out, repeats):
                     continue
                 g.set_config(mode, cfg)
                 try:
-                    t = steady(lambda fn=fn, tA=tA, tC=tC: fn(tA, tB, tC, 1.0, 0.0), torch, 0.05,
-                               batch=SKINNY_BATCH)
+                    t = median_call_time(lambda fn=fn, tA=tA, tC=tC: fn(tA, tB, tC, 1.0, 0.0),
+                                         torch, 0.05, per_sample=SKINNY_BATCH)
                 finally:
                     g.set_config(mode, None)
                 if t < best_t:
@@ -671,7 +850,7 @@ def skinny_sweep(g, torch, dev, out, repeats):
         order = list(calls)
         rng.shuffle(order)
         for k in order:
-            times[k].append(steady(calls[k], torch, seconds=0.2, batch=SKINNY_BATCH))
+            times[k].append(median_call_time(calls[k], torch, 0.2, per_sample=SKINNY_BATCH))
         log(f"skinny: round {rnd + 1} of {repeats} done")
     rows = []
     hbm = roofs["hbm_read_gbs"] * 1e9
@@ -690,7 +869,7 @@ def skinny_sweep(g, torch, dev, out, repeats):
              "Command:", "", "```", "python bench.py --skinny profiles/skinny_m.md", "```", "",
              "A (M x K), B (K x N), C iid N(0,1); alpha = 1, beta = 0.  Every case is checked "
              "against the oracle on 256 sampled elements before it is timed; the time is the "
-             f"median of {repeats} shuffled rounds of steady() (0.2 s), each sample "
+             f"median of {repeats} shuffled rounds of event-timed samples (0.2 s), each sample "
              f"{SKINNY_BATCH} back-to-back calls between two events (GPU time per call in a "
              "stream of calls: at M = 1 a call takes ~15 us, less than the host's per-call "
              "launch latency, which a single-call sample would add).  Bytes are the f32 "
@@ -714,7 +893,9 @@ def skinny_sweep(g, torch, dev, out, repeats):
 
 
 # ---------------------------------------------------------------------------
-# Profile evidence: byte-counter calibration, committed summaries.
+# Profile evidence: byte-counter calibration and the committed summaries of
+# rocprofv3 runs (profiles/).  Every summary embeds the exact commands that
+# produced it; the summarisers refuse to write one without them.
 # ---------------------------------------------------------------------------
 COPY_BYTES = 256 << 20          # one direction of the calibration copy
 PROFILES = os.path.join(ROOT, "profiles")
@@ -754,20 +935,28 @@ def source_hash(mode):
     return h.hexdigest()[:16]
 
 
-def f32_kernel_name(tile):
-    """The f32 kernel a configuration string runs on whole tiles: the
-    direct-to-LDS ring for the configurations with three or more stages,
-    the register-staged kernel otherwise."""
-    m = re.search(r"ST=(\d+)", tile or "")
-    return "gemm_f32_ring_kernel" if m and int(m.group(1)) >= 3 else "gemm_f32_kernel"
+def _tile_fields(tile):
+    return {k: int(v) for k, v in (t.split("=") for t in (tile or "").split()
+                                   if "=" in t and t.split("=")[1].isdigit())}
+
+
+def dominant_kernel(mode, tile):
+    """The kernel that does the work of a call with this tile, by the name
+    prefix rocprofv3 shows (for f16r, after its packing pass)."""
+    f = _tile_fields(tile)
+    if mode == "f32":
+        ring = f.get("ST", 0) >= 3 and f.get("BK") == 16 and "KS" not in f
+        return "gemm_f32_ring_kernel" if ring else "gemm_f32_kernel"
+    if f.get("KS") == 3:
+        return "gemm_f16_direct_kernel or gemm_f16_f32ring_kernel (no packing pass)"
+    return "pack_kernel + " + ("gemm_f16_ring_kernel" if f.get("BK") == 32 else "gemm_f16_kernel")
 
 
 def committed_traffic(mode, workload, tile):
-    """HBM bytes per launch from the committed counter summary of this
-    workload and tile, if it was taken on the current kernel sources; else None."""
+    """HBM bytes per call from the committed counter summary of this workload
+    and tile, if it was taken on the current kernel sources; else None."""
     import glob
-    import re
-    for path in sorted(glob.glob(os.path.join(PROFILES, "traffic", "*.md"))):
+    for path in sorted(glob.glob(os.path.join(PROFILES, "counters", "*.md"))):
         text = open(path).read()
         m = re.search(r"```json\n(.*?)\n```", text, re.S)
         if not m:
@@ -782,7 +971,7 @@ def committed_traffic(mode, workload, tile):
             continue
         if d.get("source_hash") != source_hash(mode):
             return None          # the kernel changed since the counters were taken
-        return {"traffic_bytes_per_launch": d["traffic_bytes_per_launch"],
+        return {"traffic_bytes_per_launch": d["traffic_bytes_per_call"],
                 "source": os.path.relpath(path, ROOT)}
     return None
 
@@ -790,94 +979,172 @@ def committed_traffic(mode, workload, tile):
 def _csv_rows(directory, suffix):
     import csv
     import glob
-    files = glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)
     rows = []
-    for f in files:
+    for f in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
         with open(f) as fh:
             rows.extend(csv.DictReader(fh))
     return rows
 
 
-def summarize_trace(directory, out, cmd):
-    rows = _csv_rows(directory, "kernel_stats.csv")
-    if not rows:
-        raise SystemExit(f"no kernel_stats.csv under {directory}")
-    lines = ["# Kernel trace summary", "", "Command:", "", "```", cmd, "```", "",
-             "| kernel | calls | average us | min us | max us | share of GPU time |",
-             "|---|---:|---:|---:|---:|---:|"]
-    for r in rows:
-        name = r["Name"].replace("|", "/")
-        lines.append(f"| `{name[:150]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
-                     f"{float(r['Percentage']):.1f}% |")
-    text = "\n".join(lines) + "\n"
-    _write(out, text)
+def _short(name, n=110):
+    name = name.replace("|", "/").replace("g355::(anonymous namespace)::", "").replace("g355::", "")
+    return name if len(name) <= n else name[:n] + "..."
 
 
-def _per_dispatch(rows, counter):
-    import collections
-    per = collections.defaultdict(float)
-    names = {}
-    for r in rows:
-        if r["Counter_Name"] != counter:
-            continue
-        per[r["Dispatch_Id"]] += float(r["Counter_Value"])
-        names[r["Dispatch_Id"]] = r["Kernel_Name"]
+def _commands_block(cmd):
+    if not cmd.strip():
+        raise SystemExit("a profile summary needs the commands that made it (--cmd)")
+    return ["Commands (run from the repository root; rocprofv3 writes under gpurun_out/):", "",
+            "```", cmd.strip(), "```", ""]
+
+
+def _dispatch_runs(trace_rows, gap_s=0.1):
+    """Dispatches of each kernel split into runs wherever the same kernel was
+    idle for more than gap_s (the phases of a benchmark: roofs, each
+    workload's check + warm-up + timed calls, tuning): (kernel, durations in
+    us, start ns) per run, in time order."""
     by_kernel = collections.defaultdict(list)
-    for d, v in per.items():
-        by_kernel[names[d]].append(v)
-    return {k: (sum(v) / len(v), len(v)) for k, v in by_kernel.items()}
+    for r in trace_rows:
+        by_kernel[r["Kernel_Name"]].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    runs = []
+    for k, ds in by_kernel.items():
+        ds.sort()
+        cur = [ds[0]]
+        for d in ds[1:]:
+            if d[0] - cur[-1][1] > gap_s * 1e9:
+                runs.append((k, [(e - s) / 1e3 for s, e in cur], cur[0][0]))
+                cur = []
+            cur.append(d)
+        runs.append((k, [(e - s) / 1e3 for s, e in cur], cur[0][0]))
+    runs.sort(key=lambda r: r[2])
+    return runs
 
 
-def summarize_pmc(fetch_dir, write_dir, out, cmd):
-    fetch = _per_dispatch(_csv_rows(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
-    write = _per_dispatch(_csv_rows(write_dir, "counter_collection.csv"), "WRITE_SIZE")
-    copy_f = [v[0] for k, v in fetch.items() if "copy_f32_kernel" in k]
-    copy_w = [v[0] for k, v in write.items() if "copy_f32_kernel" in k]
-    if not copy_f or not copy_w:
-        raise SystemExit("no calibration copy kernel in the counter runs (--calibrate-copy)")
+def summarize_trace(directory, out, cmd):
+    stats = _csv_rows(directory, "kernel_stats.csv")
+    trace = _csv_rows(directory, "kernel_trace.csv")
+    if not stats or not trace:
+        raise SystemExit(f"no kernel_stats.csv / kernel_trace.csv under {directory}")
+    lines = ["# Kernel trace summary", ""] + _commands_block(cmd)
+    lines += ["## Runs of each kernel, in time order", "",
+              "A run is the dispatches of one kernel with no gap above 0.1 s (the benchmark's "
+              "phases: roof kernels, then for each workload its check, warm-up and timed "
+              "calls).  Runs of 5 or more dispatches:", "",
+              "| # | kernel | dispatches | mean us | median us | min us | max us |",
+              "|---:|---|---:|---:|---:|---:|---:|"]
+    n = 0
+    for k, durs, _ in _dispatch_runs(trace):
+        if len(durs) < 5:
+            continue
+        n += 1
+        lines.append(f"| {n} | `{_short(k)}` | {len(durs)} | {np.mean(durs):.1f} | "
+                     f"{np.median(durs):.1f} | {np.min(durs):.1f} | {np.max(durs):.1f} |")
+    lines += ["", "## Every kernel (rocprofv3 --stats)", "",
+              "| kernel | calls | average us | min us | max us | share of GPU time |",
+              "|---|---:|---:|---:|---:|---:|"]
+    for r in stats:
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    _write(out, "\n".join(lines) + "\n")
+
+
+def _counter_table(dirs):
+    """Per kernel: the mean per dispatch of every counter found in the
+    counter_collection.csv files of dirs, and the mean duration (us) of the
+    same dispatches from the kernel traces of those runs."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    dur = {}
+    for d in dirs:
+        tag = os.path.abspath(d)
+        for r in _csv_rows(d, "counter_collection.csv"):
+            key = (tag, r["Dispatch_Id"])
+            per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[key] = r["Kernel_Name"]
+        for r in _csv_rows(d, "kernel_trace.csv"):
+            dur[(tag, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    table = collections.defaultdict(lambda: collections.defaultdict(list))
+    for key, vals in per.items():
+        for c, v in vals.items():
+            table[names[key]][c].append(v)
+        if key in dur:
+            table[names[key]]["duration_us"].append(dur[key])
+    return {k: {c: float(np.mean(v)) for c, v in cs.items()} for k, cs in table.items()}
+
+
+def summarize_counters(workload, dirs, out, cmd):
+    from workloads import WORKLOADS
+    w = WORKLOADS[workload]
+    tab = _counter_table(dirs)
+    copy = next((v for k, v in tab.items() if "copy_f32_kernel" in k), None)
+    if not copy or "FETCH_SIZE" not in copy or "WRITE_SIZE" not in copy:
+        raise SystemExit("no calibration copy kernel with FETCH_SIZE and WRITE_SIZE "
+                         "(run the profile with --calibrate-copy)")
     kib = COPY_BYTES / 1024
-    f_fac, w_fac = kib / copy_f[0], kib / copy_w[0]
-    lines = ["# HBM traffic per launch (FETCH_SIZE, WRITE_SIZE)", "", "Commands:", "", "```",
-             cmd, "```", "",
-             f"Calibration: the plain copy of {COPY_BYTES >> 20} MiB read FETCH_SIZE "
-             f"{copy_f[0]:.0f} KiB and WRITE_SIZE {copy_w[0]:.0f} KiB per launch against "
-             f"{kib:.0f} KiB moved each way, so the factors are {f_fac:.4f} (fetch) and "
-             f"{w_fac:.4f} (write).", "",
-             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | calibrated bytes |",
-             "|---|---:|---:|---:|"]
-    best = None
-    for k in sorted(set(fetch) | set(write)):
-        fb = fetch.get(k, (0.0, 0))[0] * f_fac * 1024
-        wb = write.get(k, (0.0, 0))[0] * w_fac * 1024
-        lines.append(f"| `{k[:150]}` | {fetch.get(k, (0.0, 0))[0]:.0f} | "
-                     f"{write.get(k, (0.0, 0))[0]:.0f} | {fb + wb:.4g} |")
-        calls = fetch.get(k, (0.0, 0))[1]
-        if "gemm_" in k and (best is None or calls > best[2]):
-            best = (k, fb + wb, calls)
-    text = "\n".join(lines) + "\n"
-    if best is not None:
-        mode = "f32" if "gemm_f32" in best[0] else "f16r"
-        kernel, total = best[0], best[1]
-        if mode == "f16r":
-            # one f16r call is one packing launch plus one GEMM launch; the
-            # roofline of that mode is priced on the whole call, so is its traffic
-            for k in set(fetch) | set(write):
-                if "pack_kernel" in k:
-                    total += (fetch.get(k, (0.0, 0))[0] * f_fac +
-                              write.get(k, (0.0, 0))[0] * w_fac) * 1024
-                    kernel = "pack_kernel + " + kernel
-        meta = {"workload": os.environ.get("TRAFFIC_WORKLOAD", ""),
-                "tile": os.environ.get("TRAFFIC_TILE", ""), "mode": mode, "kernel": kernel,
-                "traffic_bytes_per_launch": total, "source_hash": source_hash(mode),
-                "fetch_factor": f_fac, "write_factor": w_fac}
-        text += "\nMachine-readable (read by bench.py while the kernel sources are unchanged):\n"
-        text += "\n```json\n" + json.dumps(meta) + "\n```\n"
-    _write(out, text)
+    f_fac, w_fac = kib / copy["FETCH_SIZE"], kib / copy["WRITE_SIZE"]
+    mine = {k: v for k, v in tab.items() if "gemm_" in k or "pack_kernel" in k}
+    import gemm_tiled_amd as g   # the tile the profiled run used: the library's own choice
+    tile = g.get_config(w.mode, w.M, w.N, w.K, beta=w.beta).split(" source=")[0]
+    lines = [f"# Counters of the {workload} call ({w.mode}, {w.M}x{w.N}x{w.K}, "
+             f"alpha {w.alpha}, beta {w.beta})", ""] + _commands_block(cmd)
+    lines += [f"Tile: `{tile}` (the benchmark's own choice for this workload).", "",
+              f"Byte calibration: the plain copy of {COPY_BYTES >> 20} MiB each way read "
+              f"FETCH_SIZE {copy['FETCH_SIZE']:.0f} KiB and WRITE_SIZE {copy['WRITE_SIZE']:.0f} "
+              f"KiB per launch, so HBM bytes = FETCH_SIZE x {f_fac:.4f} + WRITE_SIZE x "
+              f"{w_fac:.4f} (KiB x 1024).", "",
+              "Definitions (rocprofv3's own metrics on gfx950): MfmaUtil = matrix-unit busy "
+              "cycles over (GRBM_GUI_ACTIVE x 1024 SIMDs); LdsBankConflict = bank-conflict "
+              "cycles per LDS-active cycle not stalled (conflicts per access); LdsUtil = "
+              "LDS-active cycles over (GUI-active cycles x 256 CUs); L2 hit = TCC_HIT / "
+              "(TCC_HIT + TCC_MISS); cycles = GRBM_GUI_ACTIVE per XCD (the counter sums the 8 "
+              "XCDs), over the kernel's duration in the same counted run for the clock (a "
+              "counted dispatch runs longer than an uncounted one: divide the cycles by the "
+              "kernel trace's duration for the clock of an ordinary run).", "",
+              "| kernel | duration us | cycles/XCD (M) | clock MHz | MfmaUtil % | "
+              "LdsBankConflict | LdsUtil % | L2 hit | HBM read MB | HBM write MB |",
+              "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    meta_k = {}
+    for k, v in sorted(mine.items(), key=lambda kv: -kv[1].get("duration_us", 0)):
+        du = v.get("duration_us")
+        clk = v["GRBM_GUI_ACTIVE"] / 8 / du if du and "GRBM_GUI_ACTIVE" in v else None
+        hit = v.get("TCC_HIT_sum")
+        miss = v.get("TCC_MISS_sum")
+        l2 = hit / (hit + miss) if hit is not None and miss is not None and hit + miss > 0 else None
+        rd = v["FETCH_SIZE"] * f_fac * 1024 if "FETCH_SIZE" in v else None
+        wr = v["WRITE_SIZE"] * w_fac * 1024 if "WRITE_SIZE" in v else None
+
+        def fmt(x, f):
+            return "" if x is None else format(x, f)
+        cyc = v["GRBM_GUI_ACTIVE"] / 8 / 1e6 if "GRBM_GUI_ACTIVE" in v else None
+        lines.append(f"| `{_short(k)}` | {fmt(du, '.1f')} | {fmt(cyc, '.3f')} | {fmt(clk, '.0f')} | "
+                     f"{fmt(v.get('MfmaUtil'), '.1f')} | {fmt(v.get('LdsBankConflict'), '.3f')} | "
+                     f"{fmt(v.get('LdsUtil'), '.1f')} | {fmt(l2, '.3f')} | "
+                     f"{fmt(rd and rd / 1e6, '.1f')} | {fmt(wr and wr / 1e6, '.1f')} |")
+        meta_k[k] = {"duration_us": du, "cycles_per_xcd": cyc and cyc * 1e6, "clock_mhz": clk,
+                     "mfma_util_pct": v.get("MfmaUtil"),
+                     "lds_bank_conflict_per_access": v.get("LdsBankConflict"),
+                     "lds_util_pct": v.get("LdsUtil"), "l2_hit": l2, "hbm_read_bytes": rd,
+                     "hbm_write_bytes": wr, "raw": dict(v)}
+    flops = 2.0 * w.M * w.N * w.K
+    compulsory = 4.0 * (w.M * w.K + w.K * w.N) + 4.0 * w.M * w.N * (2 if w.beta != 0 else 1)
+    traffic = sum((m["hbm_read_bytes"] or 0) + (m["hbm_write_bytes"] or 0) for m in meta_k.values())
+    lines += ["", f"Per call (every kernel above): HBM traffic {traffic / 1e6:.1f} MB against "
+              f"{compulsory / 1e6:.1f} MB compulsory (4(MK + KN) + 4MN read + 4MN written when "
+              f"beta != 0, else written only): {traffic / compulsory:.2f}x; "
+              f"{flops / max(traffic, 1):.0f} FLOP per HBM byte.", ""]
+    meta = {"workload": workload, "mode": w.mode, "tile": tile,
+            "traffic_bytes_per_call": traffic, "compulsory_bytes": compulsory,
+            "source_hash": source_hash(w.mode), "fetch_factor": f_fac, "write_factor": w_fac,
+            "kernels": meta_k}
+    lines += ["Machine-readable (bench.py reads `traffic_bytes_per_call` while the kernel "
+              "sources hash to `source_hash`):", "", "```json", json.dumps(meta), "```", ""]
+    _write(out, "\n".join(lines))
 
 
 def _write(out, text):
     if out:
+        os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
         with open(out, "w") as f:
             f.write(text)
     print(text)

@@ -1,4 +1,6 @@
 // aux_kernels.hip -- the beta-only update and the measurement kernels.
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace g355 {
@@ -72,50 +74,69 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 // Matrix-core roofs (the lab's "Part 1": a kernel of nothing but independent
-// multiply-adds).  Each wave keeps 8 independent accumulator blocks so the
-// matrix unit never waits on a previous result.
+// multiply-adds), one per matrix instruction form.  Each wave keeps NB
+// independent accumulator blocks (8 of 32x32, 16 of 16x16) so the matrix unit
+// never waits on a previous result.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int FORM>   // 0: v_mfma_f32_32x32x2_f32, 1: v_mfma_f32_16x16x4_f32
 __global__ __launch_bounds__(256) void roof_mfma_f32_kernel(int64_t iters, float* sink) {
+    using Acc = typename std::conditional<FORM == 0, f32x16, f32x4>::type;
+    constexpr int NB = FORM == 0 ? 8 : 16;
+    constexpr int NE = FORM == 0 ? 16 : 4;
     const float a = 1e-3f * (threadIdx.x & 7), b = 1e-3f * (threadIdx.x >> 3);
-    f32x16 acc[8];
+    Acc acc[NB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+        for (int e = 0; e < NE; ++e) acc[i][e] = 0.f;
     for (int64_t it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[i], 0, 0, 0);
+        for (int i = 0; i < NB; ++i) {
+            if constexpr (FORM == 0)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[i], 0, 0, 0);
+            else
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[i], 0, 0, 0);
+        }
     }
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s += acc[i][e];
+        for (int e = 0; e < NE; ++e) s += acc[i][e];
     sink[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+template <int FORM>   // 0: v_mfma_f32_32x32x16_f16, 1: v_mfma_f32_16x16x32_f16
 __global__ __launch_bounds__(256) void roof_mfma_f16_kernel(int64_t iters, float* sink) {
+    using Acc = typename std::conditional<FORM == 0, f32x16, f32x4>::type;
+    constexpr int NB = FORM == 0 ? 8 : 16;
+    constexpr int NE = FORM == 0 ? 16 : 4;
     f16x8 a, b;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         a[e] = static_cast<_Float16>(1e-3f * ((threadIdx.x + e) & 7));
         b[e] = static_cast<_Float16>(1e-3f * ((threadIdx.x >> 3) + e));
     }
-    f32x16 acc[8];
+    Acc acc[NB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+        for (int e = 0; e < NE; ++e) acc[i][e] = 0.f;
     for (int64_t it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[i], 0, 0, 0);
+        for (int i = 0; i < NB; ++i) {
+            if constexpr (FORM == 0)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[i], 0, 0, 0);
+            else
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[i], 0, 0, 0);
+        }
     }
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s += acc[i][e];
+        for (int e = 0; e < NE; ++e) s += acc[i][e];
     sink[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
@@ -174,16 +195,25 @@ hipError_t launch_scale_c(float* C, int64_t ldc, int M, int N, float beta, hipSt
     return hipGetLastError();
 }
 
-hipError_t launch_roof_mfma(int mode, int64_t iters, int blocks, float* sink, double* flops,
-                            hipStream_t s) {
+hipError_t launch_roof_mfma(int mode, int form, int64_t iters, int blocks, float* sink,
+                            double* flops, hipStream_t s) {
     const double waves = static_cast<double>(blocks) * 4.0;
-    if (mode == GEMM355_MODE_F32) {
-        roof_mfma_f32_kernel<<<blocks, 256, 0, s>>>(iters, sink);
-        *flops = waves * static_cast<double>(iters) * 8.0 * (2.0 * 32 * 32 * 2);
+    // instructions per wave per iteration x flops per instruction (2 m n k)
+    double per_iter = 0.0;
+    if (mode == GEMM355_MODE_F32 && form == 0) {
+        roof_mfma_f32_kernel<0><<<blocks, 256, 0, s>>>(iters, sink);
+        per_iter = 8.0 * (2.0 * 32 * 32 * 2);
+    } else if (mode == GEMM355_MODE_F32) {
+        roof_mfma_f32_kernel<1><<<blocks, 256, 0, s>>>(iters, sink);
+        per_iter = 16.0 * (2.0 * 16 * 16 * 4);
+    } else if (form == 0) {
+        roof_mfma_f16_kernel<0><<<blocks, 256, 0, s>>>(iters, sink);
+        per_iter = 8.0 * (2.0 * 32 * 32 * 16);
     } else {
-        roof_mfma_f16_kernel<<<blocks, 256, 0, s>>>(iters, sink);
-        *flops = waves * static_cast<double>(iters) * 8.0 * (2.0 * 32 * 32 * 16);
+        roof_mfma_f16_kernel<1><<<blocks, 256, 0, s>>>(iters, sink);
+        per_iter = 16.0 * (2.0 * 16 * 16 * 32);
     }
+    *flops = waves * static_cast<double>(iters) * per_iter;
     return hipGetLastError();
 }
 

@@ -1366,12 +1366,13 @@ const char* gemm355_strerror(int status) {
 
 const char* gemm355_version(void) { return "0.1.0"; }
 
-int gemm355_roof_mfma(int mode, int64_t iters, int blocks, float* sink, double* flops_out,
-                      void* stream) {
+int gemm355_roof_mfma(int mode, int form, int64_t iters, int blocks, float* sink,
+                      double* flops_out, void* stream) {
     if (mode != GEMM355_MODE_F32 && mode != GEMM355_MODE_F16R) return GEMM355_ERR_MODE;
-    if (iters < 1 || blocks < 1 || !sink || !flops_out) return GEMM355_ERR_BUFFER;
-    return status_of(
-        launch_roof_mfma(mode, iters, blocks, sink, flops_out, static_cast<hipStream_t>(stream)));
+    if ((form != 0 && form != 1) || iters < 1 || blocks < 1 || !sink || !flops_out)
+        return GEMM355_ERR_BUFFER;
+    return status_of(launch_roof_mfma(mode, form, iters, blocks, sink, flops_out,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int gemm355_roof_hbm(const void* buf, int64_t bytes, int blocks, float* sink, void* stream) {

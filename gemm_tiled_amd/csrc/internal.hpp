@@ -203,7 +203,7 @@ bool f16_from_f32_ring_takes(bool ta, bool tb, const float* A, int64_t lda, cons
                              int64_t ldb, int64_t N, int64_t K);
 
 // Measurement kernels.
-hipError_t launch_roof_mfma(int mode, int64_t iters, int blocks, float* sink, double* flops,
+hipError_t launch_roof_mfma(int mode, int form, int64_t iters, int blocks, float* sink, double* flops,
                             hipStream_t s);
 hipError_t launch_roof_hbm(const void* buf, int64_t bytes, int blocks, float* sink,
                            hipStream_t s);

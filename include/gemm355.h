@@ -271,10 +271,12 @@ const char* gemm355_version(void);
  * nothing but independent multiply-adds, and a streaming read).
  *
  * gemm355_roof_mfma: enqueue `blocks` workgroups of 256 threads, each wave
- * issuing `iters` rounds of 8 independent matrix instructions of the mode
- * (F32: 32x32x2 f32; F16R: 32x32x16 f16 with f32 accumulators) into `sink`
- * (device, >= blocks*256 floats).  *flops_out receives the flop count of the
- * launch (2*m*n*k per instruction).
+ * issuing `iters` rounds of independent matrix instructions of the mode in
+ * one form (form 0: 8 instructions of 32x32 blocks per round, F32
+ * v_mfma_f32_32x32x2_f32, F16R v_mfma_f32_32x32x16_f16; form 1: 16 of 16x16
+ * blocks, v_mfma_f32_16x16x4_f32 / v_mfma_f32_16x16x32_f16, f32
+ * accumulators) into `sink` (device, >= blocks*256 floats).  *flops_out
+ * receives the flop count of the launch (2*m*n*k per instruction).
  *
  * gemm355_roof_hbm: enqueue a grid-stride 16-byte read of `bytes` bytes
  * (multiple of 16) from device pointer `buf`, with `blocks` workgroups of 256
@@ -283,8 +285,8 @@ const char* gemm355_version(void);
  * gemm355_copy_f32: enqueue dst[i] = src[i] for n floats (a plain copy
  * kernel of known traffic, for calibrating hardware byte counters).
  */
-int gemm355_roof_mfma(int mode, int64_t iters, int blocks, float* sink, double* flops_out,
-                      void* stream);
+int gemm355_roof_mfma(int mode, int form, int64_t iters, int blocks, float* sink,
+                      double* flops_out, void* stream);
 int gemm355_roof_hbm(const void* buf, int64_t bytes, int blocks, float* sink, void* stream);
 int gemm355_copy_f32(const float* src, float* dst, int64_t n, void* stream);
 

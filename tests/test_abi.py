@@ -235,8 +235,9 @@ def test_tuning_cache_roundtrip_and_corrupt_lines(tmp_path):
 def test_roof_and_copy_reject_bad_buffers_before_launch():
     L = g.lib()
     flops = ctypes.c_double(0)
-    assert L.gemm355_roof_mfma(5, 10, 1, FAKE, ctypes.byref(flops), None) == -103
-    assert L.gemm355_roof_mfma(0, 0, 1, FAKE, ctypes.byref(flops), None) == -104
+    assert L.gemm355_roof_mfma(5, 0, 10, 1, FAKE, ctypes.byref(flops), None) == -103
+    assert L.gemm355_roof_mfma(0, 0, 0, 1, FAKE, ctypes.byref(flops), None) == -104
+    assert L.gemm355_roof_mfma(1, 2, 10, 1, FAKE, ctypes.byref(flops), None) == -104
     assert L.gemm355_roof_hbm(FAKE, 17, 1, FAKE, None) == -104
     assert L.gemm355_roof_hbm(ctypes.c_void_p((1 << 40) + 4), 32, 1, FAKE, None) == -104
     assert L.gemm355_copy_f32(None, FAKE, 4, None) == -104
