@@ -660,6 +660,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_ring_kernel(F16Args p) 
             mfma_rows(0, H, b, first);
             __builtin_amdgcn_sched_group_barrier(0x020, S::FILLS, 0);
             interleave(std::integral_constant<int, H * GFN>{}, std::integral_constant<int, GFM - H>{});
+            // The first half's matrix instructions stay ahead of the wait and
+            // the barrier: they touch no memory, so without this fence the
+            // scheduler moves most of them past the barrier, and every panel
+            // then waits for its last fragment reads and for the other waves
+            // with almost no matrix work queued.
+            __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<(NS - 2) * S::FILLS>();
             ring_barrier();
     #pragma unroll
