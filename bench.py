@@ -376,6 +376,23 @@ def measure_roofs(g, torch, dev, seconds):
         out[f"mfma_{name}_form"] = best[1]
         out[f"mfma_{name}_gpu"] = best[2]
         out[f"mfma_{name}_published_tflops"] = PEAK_TFLOPS[name]
+    # the vector FMA roof (the lab's fma_peak), the cross-check of the f32 matrix
+    # roof: one FMA per element, since no packed f32 instruction is built here
+    fflops = ctypes.c_double(0)
+
+    def launch_fma():
+        st = L.gemm355_roof_fma(20000, blocks, ctypes.c_void_p(sink.data_ptr()),
+                                ctypes.byref(fflops), sp)
+        if st != 0:
+            raise g.Gemm355Error(st, "gemm355_roof_fma")
+
+    launch_fma()
+    torch.cuda.synchronize()
+    with GpuSampler() as smp:
+        n, span = sustained(launch_fma, torch, seconds)
+    out["fma_f32_tflops"] = fflops.value * n / span / 1e12
+    out["fma_f32_gpu"] = smp.summary()
+    log(f"roof f32 vector FMA (v_fma_f32): {out['fma_f32_tflops']:.1f} TFLOP/s over {span:.2f} s")
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, device=dev, dtype=torch.float32)
     sink1 = torch.zeros(1, device=dev, dtype=torch.float32)
@@ -645,6 +662,7 @@ def shape_sweep(g, torch, dev, out, repeats):
         if not np.all(err <= oracle.TOL[mode] * W):
             raise SystemExit(f"sweep {case}: outside the parity bound")
         calls[case] = call
+        log(f"sweep: {mode} {n} {kind}: {tiles[case].split(' source=')[0]} ({plans[case]})")
 
     times = {case: [] for case in cases}
     rng = random.Random(0)
@@ -671,7 +689,7 @@ def shape_sweep(g, torch, dev, out, repeats):
         return 100 * (rb["seconds"] / ra["seconds"] - 1), 100 * (1 - rb["tflops"] / ra["tflops"])
 
     lines = ["# Shape and alignment sweep (both modes, one MI355X)", "",
-             "Command:", "", "```", "python bench.py --sweep profiles/sweep_shapes.md", "```", "",
+             "Command:", "", "```", f"python bench.py --sweep {out}", "```", "",
              "Square n x n x n, A, B, C iid N(0,1) (seed n), alpha = 1, beta = 0.  Every case is "
              "checked against the oracle on 256 sampled elements before it is timed; each time "
              f"is the median of {repeats} shuffled rounds, each the median of event-timed calls "
@@ -745,7 +763,7 @@ def precision_study(g, torch, dev, out):
         base = next(x for x in rows if x["n"] == r_["n"] and x["variant"] == "f32")
         r_["speedup_vs_f32"] = r_["tflops"] / base["tflops"]
     lines = ["# Precision: f32, f16r and f16r with binary16 output (one MI355X)", "",
-             "Command:", "", "```", "python bench.py --precision profiles/precision.md", "```", "",
+             "Command:", "", "```", f"python bench.py --precision {out}", "```", "",
              "A, B = U[0,1) - 0.5 (float32, seed 0), C = A @ B (alpha 1, beta 0).  Errors against "
              "the float64 product of the unrounded inputs, computed by the oracle: normalised "
              "max error max|C - ref| / max|ref| and relative Frobenius error "
@@ -844,6 +862,7 @@ def skinny_sweep(g, torch, dev, out, repeats):
         if not np.all(np.abs(got.astype(np.float64) - ref) <= oracle.TOL[mode] * W):
             raise SystemExit(f"skinny {key}: outside the parity bound")
         calls[key] = call
+        log(f"skinny: {mode} M={M} {kind}: {tiles[key].split(' source=')[0]}")
     times = {k: [] for k in calls}
     rng = random.Random(1)
     for rnd in range(repeats):
@@ -866,7 +885,7 @@ def skinny_sweep(g, torch, dev, out, repeats):
             "gbs": nbytes / t / 1e9, "intensity": intensity, "roof_tflops": roof / 1e12,
             "bound": "hbm" if intensity * hbm < mfma else "mfma", "frac_of_roof": flops / t / roof})
     lines = ["# Few rows of C: M = 1 .. 2048 at K = N = 4096 (both modes, one MI355X)", "",
-             "Command:", "", "```", "python bench.py --skinny profiles/skinny_m.md", "```", "",
+             "Command:", "", "```", f"python bench.py --skinny {out}", "```", "",
              "A (M x K), B (K x N), C iid N(0,1); alpha = 1, beta = 0.  Every case is checked "
              "against the oracle on 256 sampled elements before it is timed; the time is the "
              f"median of {repeats} shuffled rounds of event-timed samples (0.2 s), each sample "

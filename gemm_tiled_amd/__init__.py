@@ -65,6 +65,7 @@ EXPORTS = {
     "gemm355_version": (_cp, []),
     "gemm355_roof_mfma": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, ctypes.c_int, _p,
                                          ctypes.POINTER(ctypes.c_double), _p]),
+    "gemm355_roof_fma": (ctypes.c_int, [_i64, ctypes.c_int, _p, ctypes.POINTER(ctypes.c_double), _p]),
     "gemm355_roof_hbm": (ctypes.c_int, [_p, _i64, ctypes.c_int, _p, _p]),
     "gemm355_copy_f32": (ctypes.c_int, [_p, _p, _i64, _p]),
 }

@@ -140,6 +140,25 @@ __global__ __launch_bounds__(256) void roof_mfma_f16_kernel(int64_t iters, float
     sink[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// Vector FMA roof (the lab's fma_peak): every thread runs 8 independent
+// chains of f32 fused multiply-adds (one v_fma_f32 per element; packed f32
+// instructions are not built here).  a stays just below 1 and b small, so
+// the chains stay finite.
+__global__ __launch_bounds__(256) void roof_fma_f32_kernel(int64_t iters, float* sink) {
+    const float a = 0.999f - 1e-6f * (threadIdx.x & 31), b = 1e-3f * (threadIdx.x >> 5);
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 1e-2f * i;
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(acc[i], a, b);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += acc[i];
+    sink[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 // HBM read roof (the lab's streaming read): grid-stride 16-byte loads.
 __global__ __launch_bounds__(256) void roof_hbm_kernel(const float4* __restrict__ x, int64_t n4,
                                                        float* sink) {
@@ -214,6 +233,12 @@ hipError_t launch_roof_mfma(int mode, int form, int64_t iters, int blocks, float
         per_iter = 16.0 * (2.0 * 16 * 16 * 32);
     }
     *flops = waves * static_cast<double>(iters) * per_iter;
+    return hipGetLastError();
+}
+
+hipError_t launch_roof_fma(int64_t iters, int blocks, float* sink, double* flops, hipStream_t s) {
+    roof_fma_f32_kernel<<<blocks, 256, 0, s>>>(iters, sink);
+    *flops = static_cast<double>(blocks) * 256.0 * static_cast<double>(iters) * 8.0 * 2.0;
     return hipGetLastError();
 }
 

@@ -1375,6 +1375,11 @@ int gemm355_roof_mfma(int mode, int form, int64_t iters, int blocks, float* sink
                                       static_cast<hipStream_t>(stream)));
 }
 
+int gemm355_roof_fma(int64_t iters, int blocks, float* sink, double* flops_out, void* stream) {
+    if (iters < 1 || blocks < 1 || !sink || !flops_out) return GEMM355_ERR_BUFFER;
+    return status_of(launch_roof_fma(iters, blocks, sink, flops_out, static_cast<hipStream_t>(stream)));
+}
+
 int gemm355_roof_hbm(const void* buf, int64_t bytes, int blocks, float* sink, void* stream) {
     if (!buf || !sink || bytes < 16 || bytes % 16 || blocks < 1 ||
         (reinterpret_cast<uintptr_t>(buf) & 15))

@@ -205,6 +205,7 @@ bool f16_from_f32_ring_takes(bool ta, bool tb, const float* A, int64_t lda, cons
 // Measurement kernels.
 hipError_t launch_roof_mfma(int mode, int form, int64_t iters, int blocks, float* sink, double* flops,
                             hipStream_t s);
+hipError_t launch_roof_fma(int64_t iters, int blocks, float* sink, double* flops, hipStream_t s);
 hipError_t launch_roof_hbm(const void* buf, int64_t bytes, int blocks, float* sink,
                            hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);

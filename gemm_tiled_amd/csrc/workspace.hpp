@@ -15,7 +15,11 @@
 //   * A slot is leased again only when that use is ordered after the work of
 //     its last lease: by a call on the same stream (stream order), or, on
 //     another stream, once the event recorded when the last lease ended has
-//     completed.
+//     completed.  That event is recorded only while the pool holds `cap`
+//     slots (an event in the stream costs each call a few microseconds of GPU
+//     time): below the cap a call on a new stream gets a slot of its own, and
+//     a slot whose last lease recorded no event is never handed to another
+//     stream.
 //   * Buffers are allocated and freed stream-ordered on the stream of the
 //     call that leases them (the stream of their last use, or any stream
 //     once they are idle), so nothing waits on the host.
@@ -68,6 +72,8 @@ public:
         size_t withdrawn = 0;   // slots a captured call withdrew
         size_t leased = 0;      // slots leased now
         size_t bytes = 0;       // device bytes held by kept and withdrawn slots
+        uint64_t leases = 0;    // leases ended (outside capture)
+        uint64_t records = 0;   // of which recorded an event
     };
 
     ScratchPool(Backend& b, size_t cap) : b_(b), cap_(cap ? cap : 1) {}
@@ -245,6 +251,8 @@ public:
             if (sp->transient && sp->leased) ++st.leased;
         st.withdrawn = withdrawn_.size();
         st.bytes = bytes_.load();
+        st.leases = leases_;
+        st.records = records_;
         return st;
     }
     size_t cap() const { return cap_; }
@@ -287,10 +295,14 @@ private:
         }
         sl->last = s;
         sl->used = sl->ws || sl->cnt;   // a slot without buffers is idle for any stream
-        sl->recorded = false;
-        if (sl->used) {
+        sl->recorded = false;           // an older event says nothing about this lease
+        ++leases_;
+        if (sl->used && slots_.size() - transients_ >= cap_) {
             if (!sl->has_event && b_.event_create(&sl->ev) == 0) sl->has_event = true;
-            if (sl->has_event && b_.record(sl->ev, s) == 0) sl->recorded = true;
+            if (sl->has_event && b_.record(sl->ev, s) == 0) {
+                sl->recorded = true;
+                ++records_;
+            }
         }
         sl->leased = false;
     }
@@ -302,6 +314,7 @@ private:
     std::vector<std::unique_ptr<Slot>> withdrawn_;
     size_t transients_ = 0;
     std::atomic<size_t> bytes_{0};
+    uint64_t leases_ = 0, records_ = 0;
     uint64_t tick_ = 0;
 };
 

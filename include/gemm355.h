@@ -278,6 +278,11 @@ const char* gemm355_version(void);
  * accumulators) into `sink` (device, >= blocks*256 floats).  *flops_out
  * receives the flop count of the launch (2*m*n*k per instruction).
  *
+ * gemm355_roof_fma: the same with vector f32 fused multiply-adds instead of
+ * matrix instructions (8 independent chains per thread, one FMA per element:
+ * no packed f32 instructions), the cross-check of the f32 matrix roof;
+ * *flops_out receives 2 per FMA.
+ *
  * gemm355_roof_hbm: enqueue a grid-stride 16-byte read of `bytes` bytes
  * (multiple of 16) from device pointer `buf`, with `blocks` workgroups of 256
  * threads; `sink` is a device float written only to keep the loads alive.
@@ -287,6 +292,7 @@ const char* gemm355_version(void);
  */
 int gemm355_roof_mfma(int mode, int form, int64_t iters, int blocks, float* sink,
                       double* flops_out, void* stream);
+int gemm355_roof_fma(int64_t iters, int blocks, float* sink, double* flops_out, void* stream);
 int gemm355_roof_hbm(const void* buf, int64_t bytes, int blocks, float* sink, void* stream);
 int gemm355_copy_f32(const float* src, float* dst, int64_t n, void* stream);
 

@@ -238,6 +238,8 @@ def test_roof_and_copy_reject_bad_buffers_before_launch():
     assert L.gemm355_roof_mfma(5, 0, 10, 1, FAKE, ctypes.byref(flops), None) == -103
     assert L.gemm355_roof_mfma(0, 0, 0, 1, FAKE, ctypes.byref(flops), None) == -104
     assert L.gemm355_roof_mfma(1, 2, 10, 1, FAKE, ctypes.byref(flops), None) == -104
+    assert L.gemm355_roof_fma(0, 1, FAKE, ctypes.byref(flops), None) == -104
+    assert L.gemm355_roof_fma(10, 0, FAKE, ctypes.byref(flops), None) == -104
     assert L.gemm355_roof_hbm(FAKE, 17, 1, FAKE, None) == -104
     assert L.gemm355_roof_hbm(ctypes.c_void_p((1 << 40) + 4), 32, 1, FAKE, None) == -104
     assert L.gemm355_copy_f32(None, FAKE, 4, None) == -104

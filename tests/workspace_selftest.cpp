@@ -116,9 +116,15 @@ struct MockDevice {
         return capturing_streams.count(s) != 0;
     }
 
-    // The simulated calls' launches.
+    // The simulated calls' launches.  A buffer may have queued launches on
+    // one stream at a time: on two, their order is unknown (a race).
     void launch(uintptr_t b, Stream s, long call) {
         std::lock_guard<std::mutex> lock(mu);
+        for (auto& kv : q)
+            if (kv.first != s)
+                for (const Op& o : kv.second)
+                    if (o.kind == Op::Use && o.buf == b)
+                        fail("a buffer has queued launches on two streams");
         q[s].push_back(Op{Op::Use, b, 0, call});
     }
     // Host-side bracket of one call's launches on a buffer: no other call
@@ -359,6 +365,58 @@ void scenario_cap() {
     if (dev.frees < 4) fail("cap: transient slots not freed");
 }
 
+// Events are recorded only while the pool is full: one stream, or fewer
+// streams than the cap, records none (each stream keeps its own slot); at
+// the cap, leases record events and idle slots move between streams.
+void scenario_events() {
+    std::mt19937 rng(11);
+    {
+        MockDevice dev;
+        Pool pool(dev, 4);
+        for (long c = 0; c < 200; ++c) one_call(pool, dev, 0, c, 1 << (12 + c % 10), c % 3 ? 0 : 50, 2);
+        for (long c = 200; c < 400; ++c) one_call(pool, dev, static_cast<int>(c % 3), c, 1 << 16, 0, 1);
+        dev.drain(rng);
+        const Pool::Stats st = pool.stats();
+        if (st.records != 0) fail("events recorded below the cap");
+        if (st.kept != 3) fail("three streams below the cap should keep three slots");
+    }
+    {
+        MockDevice dev;
+        Pool pool(dev, 2);
+        {
+        // events recorded at the cap, then a capture withdraws a slot (the pool
+        // drops below the cap and later leases record no event): the older
+        // event of the other slot must not make it look idle to a third stream
+        MockDevice dev;
+        Pool pool(dev, 2);
+        for (long c = 0; c < 10; ++c) one_call(pool, dev, static_cast<int>(c % 2), c, 1 << 20, 0, 1);
+        dev.drain(rng);
+        dev.capturing_streams.insert(1);
+        {
+            Pool::Lease l = pool.lease(1);
+            void* p = nullptr;
+            if (l.workspace(1 << 20, &p) != 0) fail("events: capture lease");
+            dev.launch(reinterpret_cast<uintptr_t>(p), 1, 50);
+        }
+        dev.capturing_streams.clear();
+        dev.drain(rng);
+        one_call(pool, dev, 0, 60, 1 << 20, 0, 2);   // queued, not run: below the cap, no event
+        one_call(pool, dev, 5, 61, 1 << 20, 0, 1);   // must not take stream 0's slot
+        dev.drain(rng);
+    }
+    // fill the pool: two streams, then calls that record
+        for (long c = 0; c < 40; ++c) one_call(pool, dev, static_cast<int>(c % 2), c, 1 << 20, 0, 1);
+        if (pool.stats().records == 0) fail("no events recorded at the cap");
+        dev.drain(rng);
+        // a third stream finds an idle slot of another stream and reuses it
+        const long allocs = dev.allocs;
+        one_call(pool, dev, 7, 100, 1 << 20, 0, 1);
+        if (dev.allocs != allocs) fail("an idle slot at the cap was not reused across streams");
+        if (pool.stats().kept != 2) fail("cap: kept slots");
+        dev.drain(rng);
+    }
+}
+
 }  // namespace
 
 int main() {
@@ -367,6 +425,7 @@ int main() {
     scenario_capture();
     scenario_alloc_failure();
     scenario_cap();
+    scenario_events();
     if (g_fail) {
         std::fprintf(stderr, "%d failure(s)\n", g_fail);
         return 1;
