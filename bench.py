@@ -508,6 +508,7 @@ def bench_workload(g, torch, dev, w, args, roofs):
     if tr is not None:
         roof["traffic"] = tr["traffic_bytes_per_launch"]
         roof["traffic_source"] = tr["source"]
+        res["counters"] = {"source": tr["source"], "kernels": tr["kernels"]}
     key = f"mfma_{w.mode}_tflops"
     if roofs.get(key):
         res["frac_of_measured_roof"] = round(res["tflops_median_call"] / roofs[key], 4)
@@ -972,8 +973,9 @@ def dominant_kernel(mode, tile):
 
 
 def committed_traffic(mode, workload, tile):
-    """HBM bytes per call from the committed counter summary of this workload
-    and tile, if it was taken on the current kernel sources; else None."""
+    """HBM bytes per call and the per-kernel counters from the committed
+    counter summary of this workload and tile, if it was taken on the current
+    kernel sources; else None."""
     import glob
     for path in sorted(glob.glob(os.path.join(PROFILES, "counters", "*.md"))):
         text = open(path).read()
@@ -990,8 +992,12 @@ def committed_traffic(mode, workload, tile):
             continue
         if d.get("source_hash") != source_hash(mode):
             return None          # the kernel changed since the counters were taken
+        keep = ("duration_us", "cycles_per_xcd", "mfma_util_pct", "lds_bank_conflict_per_access",
+                "lds_util_pct", "l2_hit", "hbm_read_bytes", "hbm_write_bytes")
+        kernels = {_short(k, 80): {f: v.get(f) for f in keep}
+                   for k, v in d.get("kernels", {}).items()}
         return {"traffic_bytes_per_launch": d["traffic_bytes_per_call"],
-                "source": os.path.relpath(path, ROOT)}
+                "source": os.path.relpath(path, ROOT), "kernels": kernels}
     return None
 
 

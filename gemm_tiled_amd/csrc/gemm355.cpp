@@ -462,6 +462,17 @@ Pool* pool_of(int dev) {
     return p;
 }
 
+// The device a stream's work runs on (the current device for the null
+// stream): scratch must live there, whichever device is current.
+int device_of(hipStream_t s, int* dev) {
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice(s, &d) == hipSuccess) {
+        *dev = static_cast<int>(d);
+        return 0;
+    }
+    return status_of(hipGetDevice(dev));
+}
+
 class Scratch {
 public:
     virtual ~Scratch() = default;
@@ -518,8 +529,7 @@ private:
     int take() {
         if (!have_) {
             int dev = 0;
-            const hipError_t e = hipGetDevice(&dev);
-            if (e != hipSuccess) return status_of(e);
+            if (const int rc = device_of(s_, &dev)) return rc;
             lease_ = pool_of(dev)->lease(s_);
             have_ = true;
         }
@@ -1142,19 +1152,23 @@ static __device__ __align__(256) unsigned char scratch[g355::kFixedScratchBytes]
 namespace g355 {
 namespace {
 
-// The device address of this GPU's copy of `scratch`, looked up once per
-// device with that device current.
-int fixed_scratch_base(unsigned char** out) {
+// The device address of the copy of `scratch` on the device of stream s,
+// looked up once per device with that device current (the caller's current
+// device is restored).
+int fixed_scratch_base(hipStream_t s, unsigned char** out) {
     int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return status_of(e);
+    if (const int rc = device_of(s, &dev)) return rc;
     static std::mutex mu;
     static std::map<int, unsigned char*> base;
     std::lock_guard<std::mutex> lock(mu);
     auto it = base.find(dev);
     if (it == base.end()) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
         void* ptr = nullptr;
-        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
         if (e != hipSuccess) return status_of(e);
         if (!ptr) return GEMM355_ERR_INTERNAL;
         it = base.emplace(dev, static_cast<unsigned char*>(ptr)).first;
@@ -1203,7 +1217,7 @@ int gemm355_gemm_noalloc(int mode, int transa, int transb, int64_t M, int64_t N,
     int trans = 0;
     if (const int bad = trans_of(transa, transb, &trans)) return bad;
     unsigned char* base = nullptr;
-    if (const int rc = fixed_scratch_base(&base)) return rc;
+    if (const int rc = fixed_scratch_base(static_cast<hipStream_t>(stream), &base)) return rc;
     FixedScratch fixed(base, static_cast<hipStream_t>(stream));
     return shift_ex(gemm(mode, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
                          nullptr, nullptr, &fixed));
