@@ -39,9 +39,12 @@ bool log_debug() {
 const char* mode_name(int mode) { return mode == GEMM355_MODE_F32 ? "f32" : "f16r"; }
 
 // Up to this many rows of C the heuristic picks the few-rows configuration,
-// then, in the f16r mode up to kDirectRows, a configuration that rounds the
-// operands as it stages them, and up to kSplitKRows the split-K configuration.
+// then, in the f16r mode, a configuration that rounds the operands as it
+// stages them (up to kRingRows the f32-panel ring where it takes the shape,
+// up to twice that when N x K is at most 2^22; else up to kDirectRows the
+// register-staged one), and up to kSplitKRows the split-K configuration.
 constexpr int64_t kRowsRows = 16;
+constexpr int64_t kRingRows = 512;
 constexpr int64_t kDirectRows = 384;
 constexpr int64_t kSplitKRows = 128;
 // Compute units of the MI355X (gfx950).
@@ -353,6 +356,49 @@ double estimated_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, Ring
     return ring_block(c, rows, M, N, K).cost;
 }
 
+// The grid of a KS=3 launch: its tiles, the workgroups a CU holds at once
+// (the LDS of the stages, at most four waves per SIMD), and K in slices so
+// that the grid reaches one round of resident workgroups, each slice at least
+// kDirectMinDepth deep (a multiple of the panel depth), the partial tiles
+// within kSplitKMaxBytes.
+struct DirectGrid {
+    int64_t tiles_m, tiles_n, per_cu, slices, depth;
+};
+DirectGrid direct_grid(const TileConfig& cfg, int64_t M, int64_t N, int64_t K) {
+    DirectGrid d{};
+    d.tiles_m = (M + cfg.bm - 1) / cfg.bm;
+    d.tiles_n = (N + cfg.bn - 1) / cfg.bn;
+    const int64_t tiles = d.tiles_m * d.tiles_n;
+    const int64_t lds_bytes = cfg.bk == 32 ? int64_t{cfg.st} * (cfg.bm * 128 + 32 * cfg.bn * 4)
+                                           : 2 * int64_t{cfg.bm + cfg.bn} * 128;
+    d.per_cu = std::max<int64_t>(1, std::min<int64_t>((160 * 1024) / lds_bytes, 4 * 4 / (cfg.wm * cfg.wn)));
+    const int64_t tile_bytes = int64_t{cfg.bm} * cfg.bn * 4;
+    int64_t slices = std::max<int64_t>(1, (kCUs * d.per_cu + tiles - 1) / tiles);
+    slices = std::min(slices, std::max<int64_t>(1, K / kDirectMinDepth));
+    slices = std::min(slices, std::max<int64_t>(1, kSplitKMaxBytes / (tiles * tile_bytes)));
+    d.depth = round_up((K + slices - 1) / slices, cfg.bk);
+    d.slices = (K + d.depth - 1) / d.depth;
+    return d;
+}
+
+// The f32-panel ring configuration (KS=3, BK=32) for an f16r call whose shape
+// that ring takes: the tile by the rows of C (at N = K = 4096 measured best:
+// 32 x 64 up to 64 rows, 64 x 64 up to 160, 128 x 128 up to 256, 128 x 256
+// beyond), a smaller one while the call's workgroups (tiles x K slices) would
+// not fill one round of the CUs.
+TileConfig ring_rows_config(int64_t M, int64_t N, int64_t K) {
+    static const char* const kLadder[] = {
+        "BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 GM=8 KS=3", "BM=64 BN=64 BK=32 ST=4 WM=4 WN=1 GM=8 KS=3",
+        "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3", "BM=128 BN=256 BK=32 ST=3 WM=2 WN=4 GM=8 KS=3"};
+    TileConfig c{};
+    for (int i = M <= 64 ? 0 : M <= 160 ? 1 : M <= 256 ? 2 : 3; i >= 0; --i) {
+        parse_config(GEMM355_MODE_F16R, kLadder[i], &c);
+        const DirectGrid d = direct_grid(c, M, N, K);
+        if (d.tiles_m * d.tiles_n * d.slices >= kCUs * d.per_cu) break;
+    }
+    return c;
+}
+
 // Heuristic when nothing is pinned or tuned: estimate the time of each
 // instance as (rounds of workgroups over 256 CUs) x (work per tile) / (reuse
 // efficiency of the tile), the trade-off of the phobos "Tuning" section:
@@ -361,6 +407,11 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
     // a few rows of C (memory-bound, too few tiles): the few-rows
     // configuration up to one 16-row group, then the split-K tiles
     if (M <= kRowsRows) return rows_config(mode);
+    // (from 512 rows on the packed path wins once N x K is large: 768 x 4096^2
+    // 60 us packed against 79 us on the ring, 1024 x 8192^2 193 against 220)
+    if (mode == GEMM355_MODE_F16R && rows == RingRows::Aligned && N % 4 == 0 && K % 32 == 0 &&
+        (M <= kRingRows || (M <= 2 * kRingRows && N * K <= (int64_t{1} << 22))))
+        return ring_rows_config(M, N, K);
     if (mode == GEMM355_MODE_F16R && M <= kDirectRows) {
         // rounding on load: no packing pass, whose cost grows with N x K
         const int bm = M <= 48 ? 32 : M <= 160 ? 64 : 128;
@@ -662,19 +713,16 @@ int launch_rows(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
                                      counts, s));
 }
 
-// The configurations that round the operands as they stage them (KS=3):
-// slices of K so that the grid reaches one round of resident workgroups
-// (as many per CU as their shared memory allows), each slice at least
-// kDirectMinDepth deep (a multiple of the panel depth), the partial tiles within
-// kSplitKMaxBytes.
+// The configurations that round the operands as they stage them (KS=3), on
+// the grid of direct_grid.
 int launch_direct(const TileConfig& cfg_in, int trans, int64_t M, int64_t N, int64_t K,
                   float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
                   float beta, float* C, int64_t ldc, hipStream_t s, uint16_t* C16, Scratch& sc) {
     TileConfig cfg = cfg_in;
     const bool ta = (trans & 1) != 0, tb = (trans & 2) != 0;
-    // the f32-panel ring (BK = 16) hands the shapes it does not take to the
+    // the f32-panel ring (BK = 32) hands the shapes it does not take to the
     // register-staged kernel of the 64 x 64 tile
-    if (cfg.bk == 16 && !f16_from_f32_ring_takes(ta, tb, A, lda, B, ldb, N, K)) {
+    if (cfg.bk == 32 && !f16_from_f32_ring_takes(ta, tb, A, lda, B, ldb, N, K)) {
         TileConfig fb;
         if (!parse_config(cfg.mode, "BM=64 BN=64 BK=64 KS=3", &fb)) return GEMM355_ERR_CONFIG;
         cfg = fb;
@@ -688,21 +736,10 @@ int launch_direct(const TileConfig& cfg_in, int trans, int64_t M, int64_t N, int
     for (int i = 0; i < n; ++i)
         if (t[i].cfg == cfg) inst = &t[i];
     if (!inst) return GEMM355_ERR_CONFIG;
-    const int64_t tiles_m = (M + cfg.bm - 1) / cfg.bm, tiles_n = (N + cfg.bn - 1) / cfg.bn;
-    const int64_t tiles = tiles_m * tiles_n;
-    // resident workgroups per CU: the LDS of the stages, at most four waves
-    // per SIMD
-    const int64_t lds_bytes = cfg.bk == 16
-                                  ? int64_t{cfg.st} * (cfg.bm * 64 + 16 * (cfg.bn * 4 + 16))
-                                  : 2 * int64_t{cfg.bm + cfg.bn} * 128;
-    const int64_t per_cu = std::max<int64_t>(
-        1, std::min<int64_t>((160 * 1024) / lds_bytes, 4 * 4 / (cfg.wm * cfg.wn)));
+    const DirectGrid dg = direct_grid(cfg, M, N, K);
+    const int64_t tiles_m = dg.tiles_m, tiles_n = dg.tiles_n, tiles = tiles_m * tiles_n;
+    const int64_t slices = dg.slices, depth = dg.depth;
     const int64_t tile_bytes = int64_t{cfg.bm} * cfg.bn * 4;
-    int64_t slices = std::max<int64_t>(1, (kCUs * per_cu + tiles - 1) / tiles);
-    slices = std::min(slices, std::max<int64_t>(1, K / kDirectMinDepth));
-    slices = std::min(slices, std::max<int64_t>(1, kSplitKMaxBytes / (tiles * tile_bytes)));
-    const int64_t depth = round_up((K + slices - 1) / slices, cfg.bk);
-    slices = (K + depth - 1) / depth;
     const bool masked = !vec_ok(A, lda) || !vec_ok(B, ldb) || (M % cfg.bm) || (N % cfg.bn) ||
                         (K % cfg.bk);
     if (log_debug() && !sc.dry())

@@ -1,29 +1,18 @@
 // gemm_f16r_ring.hip -- f16r with the operands rounded to binary16 as the
-// matrix instruction's fragments are read (KS=3 configurations with BK = 16):
+// matrix instruction's fragments are read (KS=3 configurations with BK = 32):
 // the f32 panels reach shared memory through direct global->LDS copies into a
 // ring of NS stages, as in the f32 ring kernel, so many panels are in flight
 // per workgroup without holding them in registers; each fragment is read in
 // f32, rounded to binary16 (nearest even) in registers and multiplied on
-// v_mfma_f32_16x16x16_f16 with f32 accumulation.  For few rows of C the call
-// streams B once from memory and the matrix work is small, so what matters is
-// keeping enough copies in flight to reach the memory roof; the packing pass
-// of the packed path (read, round and write all of B, then read it again) and
-// the one-panel-ahead register staging of the other KS=3 kernel both fall
-// short of it there.
-//
-// Panel layout (BK = 16 floats of k), as in the f32 ring but keyed for the
-// 16-lane fragment reads of this instruction:
-//   A: BM rows of 64 bytes (four 16-byte chunks of 4 k); chunk c of row r sits
-//      at position c ^ ((r / 2) % 4); a copy instruction fills 16 rows, lane l
-//      fetching the global chunk that belongs at its position.
-//   B: 16 k-rows of BN = 256 floats, 1024 + 16 bytes apart.
-// Fragments: lane (q, r16) takes row r16 of a 16-row A block at chunk q (one
-// 16-byte read) and column r16 of a 16-column B block at k-rows 4q .. 4q + 3
-// (four 4-byte reads); the four lane quarters read k-rows 4 apart, which the
-// 16-byte row padding puts in different banks.
+// v_mfma_f32_16x16x32_f16 with f32 accumulation.  For a few hundred rows of C
+// the call streams B once from memory and the matrix work is small, so what
+// matters is keeping enough copies in flight to reach the memory roof; the
+// packing pass of the packed path (read, round and write all of B, then read
+// it again) and the one-panel-ahead register staging of the other KS=3 kernel
+// both fall short of it there.
 //
 // Shapes: the plain layout with 16-byte aligned rows, N % 4 == 0 and
-// K % 16 == 0 (M and N need not be tile multiples: copies of rows past M read
+// K % 32 == 0 (M and N need not be tile multiples: copies of rows past M read
 // row M - 1 and of columns past N column n0, values that only reach outputs
 // the masked epilogue never stores).  K is split over blockIdx.y as in the
 // other KS=3 kernel, the last workgroup of a tile adding the slices' partial
@@ -32,55 +21,246 @@
 
 // X(BM, BN, NS, WM, WN, GM): the compiled configurations.
 #define G355_F16_FROM_F32_RING_CONFIGS(X) \
-    X(64, 256, 3, 1, 4, 8)                \
-    X(64, 256, 6, 1, 4, 8)                \
-    X(32, 256, 6, 1, 2, 8)                \
-    X(128, 256, 4, 2, 4, 8)
+    X(32, 64, 4, 2, 1, 8)                 \
+    X(32, 128, 4, 2, 2, 8)                \
+    X(64, 64, 4, 4, 1, 8)                 \
+    X(64, 128, 3, 2, 2, 8)                \
+    X(128, 128, 3, 4, 2, 8)               \
+    X(128, 256, 3, 2, 4, 8)               \
+    X(256, 128, 3, 4, 2, 8)
 
 namespace g355 {
 namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const f32x4v lds_f32x4c;
-typedef __attribute__((address_space(3))) const float lds_f32c;
 
+// A K slice of a split call: the workgroup stores its partial tile in P
+// (slices x tiles x TILE_BYTES; within a tile, wave-major, block-major, lane
+// by lane, 16 bytes each), and the last workgroup of the tile to arrive
+// (counted in counts[tile]) adds the slices' partial tiles in slice order into
+// acc and returns true; the others return false.  The counter is zero again
+// when the last one leaves.  `flag` is 4 bytes of the workgroup's shared
+// memory that no wave reads any more.
+template <int GFM, int GFN, int TILE_BYTES>
+__device__ __forceinline__ bool last_slice_adds(f32x4v (&acc)[GFM][GFN], const DirectArgs& p,
+                                                int wave, int lane, unsigned char* flag_lds) {
+    constexpr int kSC1 = 1 << 4;             // cache-policy bit of the buffer intrinsics
+    constexpr int kRsrc = 0x00020000;        // raw buffer, 32-bit data format
+    constexpr int NB = GFM * GFN;
+    const int tiles = gridDim.x, slice = blockIdx.y;
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        p.P, (short)0, static_cast<int>((int64_t)p.slices * tiles * TILE_BYTES), kRsrc);
+    auto at = [&](int z, int b) {
+        return static_cast<int>(((int64_t)z * tiles + blockIdx.x) * TILE_BYTES +
+                                ((wave * NB + b) * 64 + lane) * 16);
+    };
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[b / GFN][b % GFN]), rp,
+                                               at(slice, b), 0, kSC1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // every wave is past its last panel read and its stores are done
+    unsigned* count = p.counts + blockIdx.x;
+    int* flag = reinterpret_cast<int*>(flag_lds);
+    if (threadIdx.x == 0)
+        *flag = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                static_cast<unsigned>(p.slices - 1);
+    __syncthreads();
+    if (!*flag) return false;
+    if (threadIdx.x == 0) __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    constexpr int ZG = 4;
+    for (int z0 = 0; z0 < p.slices; z0 += ZG) {
+        f32x4v t[ZG][NB];
+#pragma unroll
+        for (int zz = 0; zz < ZG; ++zz) {
+            const int z = min(z0 + zz, p.slices - 1);   // past the last slice: a reload, unused
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                t[zz][b] = __builtin_bit_cast(
+                    f32x4v, __builtin_amdgcn_raw_buffer_load_b128(rp, at(z, b), 0, kSC1));
+        }
+#pragma unroll
+        for (int zz = 0; zz < ZG; ++zz) {
+            if (z0 + zz >= p.slices) break;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const f32x4v a = acc[b / GFN][b % GFN];
+                acc[b / GFN][b % GFN] = z0 + zz == 0 ? t[zz][b] : a + t[zz][b];
+            }
+        }
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Panel layout:
+//   A: BM rows of 128 bytes (eight 16-byte chunks of 4 k); chunk c of row r
+//      sits at position c ^ key32(r), key32(r) = (r % 8) ^ ((r / 8) % 2), so
+//      that rows r, r + 1 .. r + 7 and rows r and r + 8 never hold a logical
+//      chunk at the same position; a copy instruction fills 8 rows, lane l
+//      fetching the global chunk that belongs at its position.
+//   B: 32 k-rows of BN floats, BN * 4 bytes apart; a copy instruction fills
+//      1024 / (4 BN) whole k-rows.
+// The instruction's sum runs over its 32 k in any order, so lane quarter q
+// takes k in {4q .. 4q + 3} and {16 + 4q .. 16 + 4q + 3}, for A and B alike:
+// two 16-byte reads of an A row.  Columns: the wave tile's columns are dealt
+// to its 16-column blocks four at a time -- lane column r16 of block 4g + jj
+// is column 64g + 4 r16 + jj of the wave tile -- so one 16-byte read of a B
+// k-row gives a lane its value for four blocks (eight reads: four blocks'
+// fragments, 16 lanes reading 256 contiguous bytes), and in the epilogue a
+// lane holds four consecutive columns of a row, which it reads (beta != 0)
+// and writes as one piece.
+// ---------------------------------------------------------------------------
 template <int BM, int BN, int NS, int WM, int WN>
 struct F16RingShape {
-    static constexpr int BK = 16;
+    static constexpr int BK = 32;
     static constexpr int NW = WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int GFM = TM / 16, GFN = TN / 16;
-    static constexpr int A_BYTES = BM * BK * 4;
-    static constexpr int B_ROW = BN * 4 + 16;
+    static constexpr int A_ROW = BK * 4;
+    static constexpr int A_BYTES = BM * A_ROW;
+    static constexpr int B_ROW = BN * 4;
     static constexpr int STAGE = A_BYTES + BK * B_ROW;
-    static constexpr int A_INS = BM / 16 / NW;
-    static constexpr int B_INS = BK / NW;
+    static constexpr int A_INS = A_BYTES / (1024 * NW);
+    static constexpr int B_INS = BK * B_ROW / (1024 * NW);
     static constexpr int FILLS = A_INS + B_INS;
-    static_assert(BN == 256, "one k-row of B is one 1 KB copy");
-    static_assert(A_INS >= 1 && A_INS * 16 * NW == BM && B_INS >= 1 && B_INS * NW == BK,
+    static_assert(BN == 64 || BN == 128 || BN == 256, "whole k-rows per copy instruction");
+    static_assert(A_INS >= 1 && A_INS * NW * 1024 == A_BYTES && B_INS >= 1 &&
+                      B_INS * NW * 1024 == BK * B_ROW,
                   "copies split evenly over the waves");
-    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile of whole 16 x 16 blocks");
+    static_assert(TM % 16 == 0 && TN % 64 == 0, "wave tile of 16-row blocks and 64-column groups");
     static_assert(NS >= 3 && NS * STAGE <= 160 * 1024, "LDS budget of one CU");
     static_assert((NS - 2) * FILLS < 64, "vmcnt range");
 };
 
-__device__ __forceinline__ f16x4 rn4(f32x4v v) {
-    return f16x4{static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1]),
-                 static_cast<_Float16>(v[2]), static_cast<_Float16>(v[3])};
+__device__ __forceinline__ int key32(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ f16x8 rn8(f32x4v lo, f32x4v hi) {
+    return f16x8{static_cast<_Float16>(lo[0]), static_cast<_Float16>(lo[1]),
+                 static_cast<_Float16>(lo[2]), static_cast<_Float16>(lo[3]),
+                 static_cast<_Float16>(hi[0]), static_cast<_Float16>(hi[1]),
+                 static_cast<_Float16>(hi[2]), static_cast<_Float16>(hi[3])};
+}
+
+// Epilogue of the column-dealt blocks: element e of lane (q, r16) in block
+// (i, 4g + jj) is C[row0 + 16 i + 4 q + e][col0 + 64 g + 4 r16 + jj].  The
+// value is fma(alpha, acc, beta*c) as in every epilogue of the library (f32,
+// or binary16 C widened and the result rounded once to nearest even); beta ==
+// 0 never reads C.  When C's rows allow it (f32: 16-byte aligned, binary16:
+// 8-byte aligned, ldc % 4 == 0) a lane's four columns are one access, and the
+// C reads of a row of blocks are issued before the previous row's stores;
+// otherwise element by element.  N % 4 == 0, so a lane's four columns are all
+// inside or all past the edge.
+template <int GFM, int GFN, bool MASKED, bool OUT16, typename CT>
+__device__ __forceinline__ void store_tile_dealt(const f32x4v (&acc)[GFM][GFN], CT* __restrict__ C,
+                                                 int64_t ldc, int row0, int col0, int M, int N,
+                                                 float alpha, float beta, int lane) {
+    constexpr int GG = GFN / 4;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const int q = lane >> 4, r16 = lane & 15;
+    auto row_of = [&](int i, int e) { return row0 + 16 * i + 4 * q + e; };
+    auto col_of = [&](int g) { return col0 + 64 * g + 4 * r16; };
+    auto inside = [&](int row, int col) { return !MASKED || (row < M && col < N); };
+    auto h2f = [](uint32_t bits) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+    };
+    const bool vec = ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(C) & (OUT16 ? 7 : 15)) == 0;
+    if (!vec) {
+#pragma unroll
+        for (int i = 0; i < GFM; ++i)
+#pragma unroll
+            for (int g = 0; g < GG; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = row_of(i, e), col = col_of(g);
+                    if (!inside(row, col)) continue;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        CT* at = C + (int64_t)row * ldc + col + jj;
+                        const float a = acc[i][4 * g + jj][e];
+                        if constexpr (OUT16) {
+                            const float v = beta == 0.f ? alpha * a
+                                                        : __builtin_fmaf(alpha, a, beta * h2f(*at));
+                            *at = f32_to_f16_bits(v);
+                        } else {
+                            *at = beta == 0.f ? alpha * a : __builtin_fmaf(alpha, a, beta * *at);
+                        }
+                    }
+                }
+        return;
+    }
+    auto load4 = [&](int row, int col) -> f32x4v {
+        if constexpr (OUT16) {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(C + (int64_t)row * ldc + col);
+            return f32x4v{h2f(w[0] & 0xffffu), h2f(w[0] >> 16), h2f(w[1] & 0xffffu), h2f(w[1] >> 16)};
+        } else {
+            return __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4v*>(C + (int64_t)row * ldc + col));
+        }
+    };
+    auto store4 = [&](int row, int col, f32x4v v) {
+        if constexpr (OUT16) {
+            u32x2 w;
+            w[0] = uint32_t{f32_to_f16_bits(v[0])} | (uint32_t{f32_to_f16_bits(v[1])} << 16);
+            w[1] = uint32_t{f32_to_f16_bits(v[2])} | (uint32_t{f32_to_f16_bits(v[3])} << 16);
+            *reinterpret_cast<u32x2*>(C + (int64_t)row * ldc + col) = w;
+        } else {
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4v*>(C + (int64_t)row * ldc + col));
+        }
+    };
+    auto quad = [&](int i, int g, int e) {
+        return f32x4v{acc[i][4 * g][e], acc[i][4 * g + 1][e], acc[i][4 * g + 2][e],
+                      acc[i][4 * g + 3][e]};
+    };
+    if (beta == 0.f) {
+#pragma unroll
+        for (int i = 0; i < GFM; ++i)
+#pragma unroll
+            for (int g = 0; g < GG; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (inside(row_of(i, e), col_of(g))) store4(row_of(i, e), col_of(g), alpha * quad(i, g, e));
+        return;
+    }
+    f32x4v old[2][GG * 4];
+    auto load_row = [&](int i, f32x4v(&d)[GG * 4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < GG; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                d[g * 4 + e] = inside(row_of(i, e), col_of(g)) ? load4(row_of(i, e), col_of(g))
+                                                               : f32x4v{0.f, 0.f, 0.f, 0.f};
+    };
+    load_row(0, old[0]);
+#pragma unroll
+    for (int i = 0; i < GFM; ++i) {
+        if (i + 1 < GFM) load_row(i + 1, old[(i + 1) & 1]);
+#pragma unroll
+        for (int g = 0; g < GG; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (!inside(row_of(i, e), col_of(g))) continue;
+                const f32x4v a = quad(i, g, e), c = old[i & 1][g * 4 + e];
+                f32x4v out;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) out[x] = __builtin_fmaf(alpha, a[x], beta * c[x]);
+                store4(row_of(i, e), col_of(g), out);
+            }
+        asm volatile("" ::: "memory");
+    }
 }
 
 template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED, bool OUT16>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_f32ring_kernel(DirectArgs p) {
     using S = F16RingShape<BM, BN, NS, WM, WN>;
-    constexpr int GFM = S::GFM, GFN = S::GFN;
+    constexpr int GFM = S::GFM, GFN = S::GFN, GG = GFN / 4;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * S::STAGE];
 
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int slice = blockIdx.y;
-    const int k_lo = slice * p.depth;
+    const int k_lo = blockIdx.y * p.depth;
     const int k_hi = min(p.K, k_lo + p.depth);
     const int nk = (k_hi - k_lo) / S::BK;
 
@@ -88,21 +268,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_f32ring_kernel(DirectAr
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / WN, wc = wave % WN;
 
-    // Copy sources.  A copy j of this wave fills panel rows 16 (wave + NW j)
-    // .. +15; lane l takes row l / 4 of them at position l % 4, which holds
-    // global chunk (l % 4) ^ ((row / 2) % 4) = (l % 4) ^ ((l / 8) % 4).  B copy
-    // j fills k-row wave + NW j, lane l its floats 4l .. 4l + 3.
-    const int arow = lane >> 2;
-    const int achunk = (lane & 3) ^ ((lane >> 3) & 3);
+    // Copy sources.  A copy j of this wave fills the panel rows 8u .. 8u + 7,
+    // u = wave + NW j: lane l takes row 8u + l / 8 at position l % 8, which
+    // holds global chunk (l % 8) ^ key32(row); rows past M read row M - 1.  B
+    // copy j fills bytes 1024u .. 1024u + 1023 of the B panel: lane l the four
+    // floats at byte 1024u + 16l, i.e. k-row (1024u + 16l) / B_ROW from column
+    // ((1024u + 16l) % B_ROW) / 4 on (columns past N read column n0); copy j
+    // is copy 0 moved down 1024 NW / B_ROW k-rows.
     const float* a_src[S::A_INS];
 #pragma unroll
     for (int j = 0; j < S::A_INS; ++j) {
-        const int row = min(m0 + (wave + S::NW * j) * 16 + arow, p.M - 1);
-        a_src[j] = p.A + (int64_t)row * p.lda + k_lo + achunk * 4;
+        const int row = 8 * (wave + S::NW * j) + (lane >> 3);
+        const int chunk = (lane & 7) ^ key32(row & 15);
+        a_src[j] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + k_lo + chunk * 4;
     }
-    const int bcol = n0 + lane * 4 < p.N ? n0 + lane * 4 : n0;
-    const float* b_src = p.B + (int64_t)(k_lo + wave) * p.ldb + bcol;
-    const int64_t b_step = (int64_t)S::NW * p.ldb;
+    const int b_byte = 1024 * wave + 16 * lane;
+    const int bcol = n0 + (b_byte % S::B_ROW) / 4;
+    const float* b_src = p.B + (int64_t)(k_lo + b_byte / S::B_ROW) * p.ldb + (bcol < p.N ? bcol : n0);
+    const int64_t b_step = (int64_t)(1024 / S::B_ROW) * S::NW * p.ldb;
     const int64_t b_panel = (int64_t)S::BK * p.ldb;
 
     auto stage_of = [&](int i) __attribute__((always_inline)) -> unsigned char* {
@@ -115,13 +298,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_f32ring_kernel(DirectAr
             lds_copy16(a_src[j] + kt * S::BK, base + (wave + S::NW * j) * 1024);
 #pragma unroll
         for (int j = 0; j < S::B_INS; ++j)
-            lds_copy16(b_src + j * b_step + kt * b_panel,
-                       base + S::A_BYTES + (wave + S::NW * j) * S::B_ROW);
+            lds_copy16(b_src + j * b_step + kt * b_panel, base + S::A_BYTES + (wave + S::NW * j) * 1024);
     };
 
+    // Fragment reads of lane (q, r16): A row r16 of a block at logical chunks
+    // q and q + 4; B k-rows 4q .. 4q + 3 and 16 + 4q .. 16 + 4q + 3 at the
+    // lane's four columns of a 64-column group.
     const int r16 = lane & 15, q = lane >> 4;
-    const int a_off = (wr * S::TM + r16) * 64 + ((q ^ ((r16 >> 1) & 3)) << 4);
-    const int b_off = S::A_BYTES + (4 * q) * S::B_ROW + (wc * S::TN + r16) * 4;
+    const int a_row = (wr * S::TM + r16) * S::A_ROW;
+    const int a_off0 = a_row + ((q ^ key32(r16)) << 4);
+    const int a_off1 = a_row + (((q + 4) ^ key32(r16)) << 4);
+    const int b_off = S::A_BYTES + 4 * q * S::B_ROW + (wc * S::TN + 4 * r16) * 4;
 
     f32x4v acc[GFM][GFN];
 #pragma unroll
@@ -140,87 +327,45 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_f32ring_kernel(DirectAr
         ring_barrier();
         fill(stage_of((kt + NS - 1) % NS), min(kt + NS - 1, nk - 1));
         const lds_u8* st = (const lds_u8*)(stage_of(kt % NS));
-        f16x4 fa[GFM], fb[GFN];
+        f16x8 fa[GFM], fb[GFN];
 #pragma unroll
         for (int i = 0; i < GFM; ++i)
-            fa[i] = rn4(*reinterpret_cast<lds_f32x4c*>(st + a_off + i * 16 * 64));
+            fa[i] = rn8(*reinterpret_cast<lds_f32x4c*>(st + a_off0 + i * 16 * S::A_ROW),
+                        *reinterpret_cast<lds_f32x4c*>(st + a_off1 + i * 16 * S::A_ROW));
 #pragma unroll
-        for (int j = 0; j < GFN; ++j) {
-            f32x4v v;
+        for (int g = 0; g < GG; ++g) {
+            f32x4v v[8];
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                v[t] = *reinterpret_cast<lds_f32c*>(st + b_off + t * S::B_ROW + j * 16 * 4);
-            fb[j] = rn4(v);
+            for (int t = 0; t < 8; ++t)
+                v[t] = *reinterpret_cast<lds_f32x4c*>(st + b_off + (t < 4 ? t : t + 12) * S::B_ROW +
+                                                      g * 256);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                fb[4 * g + jj] = rn8(f32x4v{v[0][jj], v[1][jj], v[2][jj], v[3][jj]},
+                                     f32x4v{v[4][jj], v[5][jj], v[6][jj], v[7][jj]});
         }
 #pragma unroll
         for (int i = 0; i < GFM; ++i)
 #pragma unroll
             for (int j = 0; j < GFN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
     wait_vmcnt<0>();   // no copy may still be landing in LDS when the workgroup ends
 
+    if (p.slices > 1 && !last_slice_adds<GFM, GFN, BM * BN * 4>(acc, p, wave, lane, ring)) return;
     const int row0 = m0 + wr * S::TM, col0 = n0 + wc * S::TN;
-    if (p.slices > 1) {
-        constexpr int kSC1 = 1 << 4;             // cache-policy bit of the buffer intrinsics
-        constexpr int kRsrc = 0x00020000;        // raw buffer, 32-bit data format
-        constexpr int NB = GFM * GFN;
-        constexpr int TILE_BYTES = BM * BN * 4;
-        const int tiles = gridDim.x;
-        const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-            p.P, (short)0, static_cast<int>((int64_t)p.slices * tiles * TILE_BYTES), kRsrc);
-        auto at = [&](int z, int b) {
-            return static_cast<int>(((int64_t)z * tiles + blockIdx.x) * TILE_BYTES +
-                                    ((wave * NB + b) * 64 + lane) * 16);
-        };
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[b / GFN][b % GFN]),
-                                                   rp, at(slice, b), 0, kSC1);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();   // every wave is past its last panel read and its stores are done
-        unsigned* count = p.counts + blockIdx.x;
-        int* flag = reinterpret_cast<int*>(ring);
-        if (threadIdx.x == 0)
-            *flag = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                    static_cast<unsigned>(p.slices - 1);
-        __syncthreads();
-        if (!*flag) return;
-        if (threadIdx.x == 0) __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        constexpr int ZG = 4;
-        for (int z0 = 0; z0 < p.slices; z0 += ZG) {
-            f32x4v t[ZG][NB];
-#pragma unroll
-            for (int zz = 0; zz < ZG; ++zz) {
-                const int z = min(z0 + zz, p.slices - 1);   // past the last slice: a reload, unused
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    t[zz][b] = __builtin_bit_cast(
-                        f32x4v, __builtin_amdgcn_raw_buffer_load_b128(rp, at(z, b), 0, kSC1));
-            }
-#pragma unroll
-            for (int zz = 0; zz < ZG; ++zz) {
-                if (z0 + zz >= p.slices) break;
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const f32x4v a = acc[b / GFN][b % GFN];
-                    acc[b / GFN][b % GFN] = z0 + zz == 0 ? t[zz][b] : a + t[zz][b];
-                }
-            }
-        }
-    }
     if constexpr (OUT16)
-        store_tile_m16<GFM, GFN, MASKED, true>(acc, p.C16, p.ldc, row0, col0, p.M, p.N, p.alpha,
-                                               p.beta, lane);
+        store_tile_dealt<GFM, GFN, MASKED, true>(acc, p.C16, p.ldc, row0, col0, p.M, p.N, p.alpha,
+                                                 p.beta, lane);
     else
-        store_tile_m16<GFM, GFN, MASKED, false>(acc, p.C, p.ldc, row0, col0, p.M, p.N, p.alpha,
-                                                p.beta, lane);
+        store_tile_dealt<GFM, GFN, MASKED, false>(acc, p.C, p.ldc, row0, col0, p.M, p.N, p.alpha,
+                                                  p.beta, lane);
 }
 
 template <int BM, int BN, int NS, int WM, int WN, int GM>
 hipError_t launch_f32ring(const DirectArgs& a, bool ta, bool tb, bool masked, hipStream_t s) {
     // the host hands only the shapes this kernel takes (f16_from_f32_ring_takes)
-    if (ta || tb || a.N % 4 != 0 || a.K % 16 != 0 || a.depth % 16 != 0 || a.K <= 0)
+    if (ta || tb || a.N % 4 != 0 || a.K % 32 != 0 || a.depth % 32 != 0 || a.K <= 0)
         return hipErrorInvalidValue;
     const dim3 grid(a.tiles_m * a.tiles_n, a.slices), block(WM * WN * 64);
     const bool edge = masked || a.M % BM != 0 || a.N % BN != 0;
@@ -235,7 +380,7 @@ hipError_t launch_f32ring(const DirectArgs& a, bool ta, bool tb, bool masked, hi
 }
 
 #define G355_F32RING_INSTANCE(BM, BN, NS, WM, WN, GM) \
-    {{GEMM355_MODE_F16R, BM, BN, 16, NS, WM, WN, GM, 3}, &launch_f32ring<BM, BN, NS, WM, WN, GM>},
+    {{GEMM355_MODE_F16R, BM, BN, 32, NS, WM, WN, GM, 3}, &launch_f32ring<BM, BN, NS, WM, WN, GM>},
 
 const DirectInstance kF32RingInstances[] = {G355_F16_FROM_F32_RING_CONFIGS(G355_F32RING_INSTANCE)};
 
@@ -251,7 +396,7 @@ bool f16_from_f32_ring_takes(bool ta, bool tb, const float* A, int64_t lda, cons
     auto vec = [](const float* p, int64_t ld) {
         return ld % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0;
     };
-    return !ta && !tb && vec(A, lda) && vec(B, ldb) && N % 4 == 0 && K % 16 == 0 && K > 0;
+    return !ta && !tb && vec(A, lda) && vec(B, ldb) && N % 4 == 0 && K % 32 == 0 && K > 0;
 }
 
 }  // namespace g355

@@ -194,10 +194,11 @@ struct DirectInstance {
     DirectLaunch launch;
 };
 const DirectInstance* direct_instances(int* count);
-// The KS=3 configurations with BK = 16 (gemm_f16r_ring.hip): f32 panels in a
-// ring of direct-to-LDS copies, rounded as the fragments are read.  They take
-// the plain layout with 16-byte aligned rows, N % 4 == 0 and K % 16 == 0
-// (f16_from_f32_ring_takes), slices of K a multiple of 16 deep.
+// The KS=3 configurations with BK = 32 (gemm_f16r_ring.hip): f32 panels in a
+// ring of direct-to-LDS copies, rounded as the fragments are read for
+// v_mfma_f32_16x16x32_f16.  They take the plain layout with 16-byte aligned
+// rows, N % 4 == 0 and K % 32 == 0 (f16_from_f32_ring_takes), slices of K a
+// multiple of 32 deep.
 const DirectInstance* f16_from_f32_ring_instances(int* count);
 bool f16_from_f32_ring_takes(bool ta, bool tb, const float* A, int64_t lda, const float* B,
                              int64_t ldb, int64_t N, int64_t K);

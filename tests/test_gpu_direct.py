@@ -26,9 +26,11 @@ from tests.gpu_helpers import pinned, run, say, to_device  # noqa: E402
 DIRECT = ["BM=64 BN=64 BK=64 KS=3", "BM=32 BN=64 BK=64 KS=3", "BM=128 BN=128 BK=64 KS=3",
           "BM=64 BN=256 BK=64 KS=3",
           # f32 panels through a ring of direct-to-LDS copies, rounded as read
-          "BM=64 BN=256 BK=16 ST=3 KS=3", "BM=64 BN=256 BK=16 ST=6 KS=3",
-          "BM=32 BN=256 BK=16 ST=6 KS=3", "BM=128 BN=256 BK=16 ST=4 KS=3"]
-RINGS = [c for c in DIRECT if "BK=16" in c]
+          "BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 KS=3", "BM=32 BN=128 BK=32 ST=4 WM=2 WN=2 KS=3",
+          "BM=64 BN=64 BK=32 ST=4 WM=4 WN=1 KS=3", "BM=64 BN=128 BK=32 ST=3 WM=2 WN=2 KS=3",
+          "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 KS=3", "BM=128 BN=256 BK=32 ST=3 WM=2 WN=4 KS=3",
+          "BM=256 BN=128 BK=32 ST=3 WM=4 WN=2 KS=3"]
+RINGS = [c for c in DIRECT if "ST=" in c]
 
 
 def assert_parity(A, B, C, alpha, beta, got):
@@ -58,14 +60,15 @@ def test_direct_against_the_oracle(cfg, M, N, K, lds):
 @pytest.mark.parametrize("cfg", RINGS)
 @pytest.mark.parametrize("M,N,K,lds", [
     (17, 1000, 4096, {}),                           # ragged M and N (N % 4 == 0), many slices
-    (300, 520, 2096, {"lda": 2100, "ldb": 524, "ldc": 521}),   # padded 16-byte rows, odd ldc
-    (1000, 300, 784, {}),                           # many tile rows, one or two slices
+    (300, 520, 2112, {"lda": 2116, "ldb": 524, "ldc": 521}),   # padded 16-byte rows, odd ldc
+    (1000, 300, 800, {}),                           # many tile rows, one or two slices
     (64, 4096, 4096, {}),                           # whole tiles
-    (33, 256, 16, {}),                              # one panel
+    (33, 256, 32, {}),                              # one panel
+    (130, 2052, 1024, {"ldc": 2056}),               # a column group past N in a ragged tile
 ])
 def test_direct_ring_shapes(cfg, M, N, K, lds):
     """The shapes the f32-panel ring takes itself (16-byte rows, N % 4 == 0,
-    K % 16 == 0), ragged in M and N."""
+    K % 32 == 0), ragged in M and N."""
     A, B, C = make_inputs(M, N, K, "normal", seed=25, **lds)
     with pinned("f16r", cfg):
         say(f"[direct ring] {cfg} {M}x{N}x{K} {lds}")
@@ -73,6 +76,34 @@ def test_direct_ring_shapes(cfg, M, N, K, lds):
         again = run("f16r", A, B, C, -0.75, 1.5)
     assert_parity(A, B, C, -0.75, 1.5, got)
     assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+
+
+@pytest.mark.parametrize("cfg", RINGS)
+@pytest.mark.parametrize("ldc_pad", [0, 2])
+def test_ring32_epilogue_paths(cfg, ldc_pad):
+    """The 32-deep ring's epilogue, bit-exact on small integers: a lane's four
+    columns as one access when C's rows allow it (ldc % 4 == 0), element by
+    element otherwise (ldc = N + 2); f32 C with beta != 0 and with beta = 0
+    (NaN in C, never read), binary16 C as the f32 result rounded once."""
+    M, N, K = 150, 1000, 1024
+    A, B, C = small_integers(M, N, K, seed=26, ldc=N + ldc_pad)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    Cn = np.full((M, N + ldc_pad), np.nan, dtype=np.float32)[:, :N]
+    with pinned("f16r", cfg):
+        say(f"[ring32 epilogue] {cfg} {M}x{N}x{K} ldc={N + ldc_pad}")
+        got = run("f16r", A, B, C, -2.0, 0.5)
+        assert np.array_equal(got, (-2.0 * exact + 0.5 * C.astype(np.float64)).astype(np.float32))
+        got = run("f16r", A, B, Cn, 1.0, 0.0)
+        assert np.array_equal(got, exact.astype(np.float32))
+        tA, tB = to_device(A), to_device(B)
+        t16 = torch.zeros((M, N + ldc_pad), dtype=torch.float16, device="cuda")[:, :N]
+        t16.copy_(torch.from_numpy(C.astype(np.float16)))
+        t32 = to_device(C.astype(np.float16).astype(np.float32))
+        g.gemm_f16r_f16out(tA, tB, t16, 0.75, -0.25)
+        g.gemm("f16r", tA, tB, t32, 0.75, -0.25)
+        torch.cuda.synchronize()
+    want = t32.cpu().numpy().astype(np.float16)
+    assert np.array_equal(t16.cpu().numpy().view(np.uint16), want.view(np.uint16))
 
 
 @pytest.mark.parametrize("cfg", DIRECT)

@@ -241,12 +241,21 @@ def test_splitk_is_the_default_for_few_rows():
         assert "KS=" not in g.get_config(mode, 4096, 4096, 4096)
     assert g.get_config("f32", 17, 4096, 4096).startswith("BM=32 BN=128 BK=32")
     assert "KS=1" in g.get_config("f32", 64, 4096, 4096)
-    # f16r: the configurations that round on load, up to 384 rows
-    assert g.get_config("f16r", 17, 4096, 4096).startswith("BM=32 BN=64 BK=64")
-    assert g.get_config("f16r", 64, 4096, 4096).startswith("BM=64 BN=64 BK=64")
-    assert g.get_config("f16r", 384, 4096, 4096).startswith("BM=128 BN=128 BK=64")
-    assert all("KS=3" in g.get_config("f16r", m, 4096, 4096) for m in (17, 64, 384))
-    assert "KS=" not in g.get_config("f16r", 385, 4096, 4096)
+    # f16r: the configurations that round on load -- the f32-panel ring up to
+    # 512 rows where it takes the shape (K % 32 == 0; up to 1024 rows for a
+    # small N x K), else the register-staged one up to 384 rows
+    assert g.get_config("f16r", 17, 4096, 4096).startswith("BM=32 BN=64 BK=32")
+    assert g.get_config("f16r", 64, 4096, 4096).startswith("BM=32 BN=64 BK=32")
+    assert g.get_config("f16r", 128, 4096, 4096).startswith("BM=64 BN=64 BK=32")
+    assert g.get_config("f16r", 256, 4096, 4096).startswith("BM=128 BN=128 BK=32")
+    assert g.get_config("f16r", 512, 4096, 4096).startswith("BM=128 BN=256 BK=32")
+    assert g.get_config("f16r", 512, 2048, 2048).startswith("BM=128 BN=128 BK=32")
+    assert g.get_config("f16r", 1024, 1024, 1024).startswith("BM=64 BN=64 BK=32")
+    assert all("KS=3" in g.get_config("f16r", m, 4096, 4096) for m in (17, 64, 384, 512))
+    assert "KS=" not in g.get_config("f16r", 513, 4096, 4096)
+    assert g.get_config("f16r", 64, 4096, 4080).startswith("BM=64 BN=64 BK=64")
+    assert g.get_config("f16r", 384, 4096, 4080).startswith("BM=128 BN=128 BK=64")
+    assert "KS=" not in g.get_config("f16r", 385, 4096, 4080)
 
 
 # ---------------------------------------------------------------------------
