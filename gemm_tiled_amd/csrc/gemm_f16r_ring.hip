@@ -96,10 +96,12 @@ __device__ __forceinline__ bool last_slice_adds(f32x4v (&acc)[GFM][GFN], const D
 // ---------------------------------------------------------------------------
 // Panel layout:
 //   A: BM rows of 128 bytes (eight 16-byte chunks of 4 k); chunk c of row r
-//      sits at position c ^ key32(r), key32(r) = (r % 8) ^ ((r / 8) % 2), so
-//      that rows r, r + 1 .. r + 7 and rows r and r + 8 never hold a logical
-//      chunk at the same position; a copy instruction fills 8 rows, lane l
-//      fetching the global chunk that belongs at its position.
+//      sits at position c ^ swz<64>(r) = c ^ ((r / 2) % 8), the key of the
+//      packed image's 128-byte rows; a copy instruction fills 8 rows, lane l
+//      fetching the global chunk that belongs at its position.  Measured
+//      (LdsBankConflict): no conflicts with this key or with r % 8, while
+//      (r % 8) ^ ((r / 8) % 2) made every A fragment read a two-way conflict
+//      (2-4% of the call's time at 256-512 rows).
 //   B: 32 k-rows of BN floats, BN * 4 bytes apart; a copy instruction fills
 //      1024 / (4 BN) whole k-rows.
 // The instruction's sum runs over its 32 k in any order, so lane quarter q
@@ -133,8 +135,6 @@ struct F16RingShape {
     static_assert(NS >= 3 && NS * STAGE <= 160 * 1024, "LDS budget of one CU");
     static_assert((NS - 2) * FILLS < 64, "vmcnt range");
 };
-
-__device__ __forceinline__ int key32(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ f16x8 rn8(f32x4v lo, f32x4v hi) {
     return f16x8{static_cast<_Float16>(lo[0]), static_cast<_Float16>(lo[1]),
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_f32ring_kernel(DirectAr
 
     // Copy sources.  A copy j of this wave fills the panel rows 8u .. 8u + 7,
     // u = wave + NW j: lane l takes row 8u + l / 8 at position l % 8, which
-    // holds global chunk (l % 8) ^ key32(row); rows past M read row M - 1.  B
+    // holds global chunk (l % 8) ^ swz<64>(row); rows past M read row M - 1.  B
     // copy j fills bytes 1024u .. 1024u + 1023 of the B panel: lane l the four
     // floats at byte 1024u + 16l, i.e. k-row (1024u + 16l) / B_ROW from column
     // ((1024u + 16l) % B_ROW) / 4 on (columns past N read column n0); copy j
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_f32ring_kernel(DirectAr
 #pragma unroll
     for (int j = 0; j < S::A_INS; ++j) {
         const int row = 8 * (wave + S::NW * j) + (lane >> 3);
-        const int chunk = (lane & 7) ^ key32(row & 15);
+        const int chunk = (lane & 7) ^ swz<64>(row & 15);
         a_src[j] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + k_lo + chunk * 4;
     }
     const int b_byte = 1024 * wave + 16 * lane;
@@ -306,8 +306,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_f32ring_kernel(DirectAr
     // lane's four columns of a 64-column group.
     const int r16 = lane & 15, q = lane >> 4;
     const int a_row = (wr * S::TM + r16) * S::A_ROW;
-    const int a_off0 = a_row + ((q ^ key32(r16)) << 4);
-    const int a_off1 = a_row + (((q + 4) ^ key32(r16)) << 4);
+    const int a_off0 = a_row + ((q ^ swz<64>(r16)) << 4);
+    const int a_off1 = a_row + (((q + 4) ^ swz<64>(r16)) << 4);
     const int b_off = S::A_BYTES + 4 * q * S::B_ROW + (wc * S::TN + 4 * r16) * 4;
 
     f32x4v acc[GFM][GFN];
