@@ -812,7 +812,8 @@ def skinny_sweep(g, torch, dev, out, repeats):
         tA, tC = torch.from_numpy(A).to(dev), torch.from_numpy(C).to(dev)
         for mode in ("f32", "f16r"):
             ref, W = oracle.entries(mode, A, B, C, 1.0, 0.0, r, c)
-            kinds = ("tuned", "split-K", "rows", "no split-K") + (("round on load",) if mode == "f16r" else ())
+            kinds = ("tuned", "split-K", "rows", "no split-K",
+                     "round on load" if mode == "f16r" else "panel ring")
             for kind in kinds:
                 cases.append((mode, M, kind, tA, tC, r, c, ref, W))
     calls, tiles = {}, {}
@@ -835,11 +836,11 @@ def skinny_sweep(g, torch, dev, out, repeats):
                     g.set_config(mode, None)
         else:
             # the library's best configuration without split-K (tuned over the
-            # rest), or the best of the f16r configurations that round the
-            # operands as they stage them (KS=3)
+            # rest), or the best of the KS=3 configurations (f16r: those that
+            # round the operands as they stage them; f32: the f32-panel ring)
             best, best_t = None, 1e30
             for cfg in g.list_configs(mode):
-                if ("KS=3" not in cfg) if kind == "round on load" else ("KS=" in cfg):
+                if ("KS=3" not in cfg) if kind in ("round on load", "panel ring") else ("KS=" in cfg):
                     continue
                 g.set_config(mode, cfg)
                 try:
@@ -901,7 +902,9 @@ def skinny_sweep(g, torch, dev, out, repeats):
              "registers, 16x16x4 matrix instructions, k split within and across workgroups); "
              "`round on load` (f16r) the fastest of the configurations that round A and B to "
              "binary16 as they stage them for the binary16 matrix instruction (KS=3, no packing "
-             "pass); `no split-K` is the fastest configuration of none of these kinds.", "",
+             "pass), `panel ring` (f32) the fastest of the f32-panel ring's configurations (KS=3: "
+             "direct-to-LDS f32 panels, K split, slices added in order by the tile's last "
+             "workgroup); `no split-K` is the fastest configuration of none of these kinds.", "",
              "| mode | M | choice | TFLOP/s | GB/s | FLOP/B | bound | of roof | tile |",
              "|---|---:|---|---:|---:|---:|---|---:|---|"]
     for r_ in sorted(rows, key=lambda r_: (r_["mode"], r_["M"], r_["kind"])):

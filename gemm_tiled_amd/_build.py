@@ -16,7 +16,7 @@ OUT = os.path.join(HERE, "libgemm355.so")
 BUILD = os.path.join(ROOT, "_build", "gemm355")
 
 SOURCES = ["gemm_f32.hip", "gemm_f32_t.hip", "gemm_f32_ring.hip", "gemm_splitk.hip", "gemm_rows.hip", "gemm_f16r.hip",
-           "gemm_f16r_o16.hip", "gemm_f16r_direct.hip", "gemm_f16r_ring.hip", "aux_kernels.hip", "gemm355.cpp"]
+           "gemm_f16r_o16.hip", "gemm_f16r_direct.hip", "gemm_panel_ring.hip", "aux_kernels.hip", "gemm355.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

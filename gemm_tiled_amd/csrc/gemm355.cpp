@@ -39,12 +39,13 @@ bool log_debug() {
 const char* mode_name(int mode) { return mode == GEMM355_MODE_F32 ? "f32" : "f16r"; }
 
 // Up to this many rows of C the heuristic picks the few-rows configuration,
-// then, in the f16r mode, a configuration that rounds the operands as it
-// stages them (up to kRingRows the f32-panel ring where it takes the shape,
-// up to twice that when N x K is at most 2^22; else up to kDirectRows the
-// register-staged one), and up to kSplitKRows the split-K configuration.
+// then the f32-panel ring where it takes the shape (f16r: up to kRingRows, or
+// twice that when N x K is at most 2^22; f32: up to kPanelRowsF32), else in
+// the f16r mode the register-staged configuration that rounds on load up to
+// kDirectRows, and up to kSplitKRows the split-K configuration.
 constexpr int64_t kRowsRows = 16;
 constexpr int64_t kRingRows = 512;
+constexpr int64_t kPanelRowsF32 = 256;
 constexpr int64_t kDirectRows = 384;
 constexpr int64_t kSplitKRows = 128;
 // Compute units of the MI355X (gfx950).
@@ -77,9 +78,9 @@ std::vector<TileConfig> configs_of(int mode) {
         for (int i = 0; i < n; ++i) out.push_back(t[i].cfg);
         const DirectInstance* d = direct_instances(&n);
         for (int i = 0; i < n; ++i) out.push_back(d[i].cfg);
-        d = f16_from_f32_ring_instances(&n);
-        for (int i = 0; i < n; ++i) out.push_back(d[i].cfg);
     }
+    const DirectInstance* d = panel_ring_instances(mode, &n);
+    for (int i = 0; i < n; ++i) out.push_back(d[i].cfg);
     out.push_back(splitk_config(mode));
     out.push_back(rows_config(mode));
     return out;
@@ -381,20 +382,31 @@ DirectGrid direct_grid(const TileConfig& cfg, int64_t M, int64_t N, int64_t K) {
     return d;
 }
 
-// The f32-panel ring configuration (KS=3, BK=32) for an f16r call whose shape
-// that ring takes: the tile by the rows of C (at N = K = 4096 measured best:
-// 32 x 64 up to 64 rows, 64 x 64 up to 160, 128 x 128 up to 256, 128 x 256
-// beyond), a smaller one while the call's workgroups (tiles x K slices) would
-// not fill one round of the CUs.
-TileConfig ring_rows_config(int64_t M, int64_t N, int64_t K) {
-    static const char* const kLadder[] = {
+// The f32-panel ring configuration (KS=3, BK=32) for a call whose shape that
+// ring takes: the tile by the rows of C, measured best at N = K = 4096 --
+// f16r: 32 x 64 up to 64 rows, 64 x 64 up to 160, 128 x 128 up to 256,
+// 128 x 256 beyond; f32: 32 x 128 up to 32 rows, 64 x 64 up to 128, 64 x 128
+// beyond -- then a smaller tile of the mode's ladder while the call's
+// workgroups (tiles x K slices) would not fill one round of the CUs (f16r) or
+// half a round (f32: there 32 x 128 at 17 rows, 256 workgroups, beat 32 x 64
+// with 512, 21 against 27 us, while f16r's 1024^3 took 64 x 64 at 13 us over
+// 128 x 128's half round at 16 us).
+TileConfig panel_ring_config(int mode, int64_t M, int64_t N, int64_t K) {
+    static const char* const kF16r[] = {
         "BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 GM=8 KS=3", "BM=64 BN=64 BK=32 ST=4 WM=4 WN=1 GM=8 KS=3",
         "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3", "BM=128 BN=256 BK=32 ST=3 WM=2 WN=4 GM=8 KS=3"};
+    static const char* const kF32[] = {
+        "BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 GM=8 KS=3", "BM=32 BN=128 BK=32 ST=4 WM=2 WN=2 GM=8 KS=3",
+        "BM=64 BN=64 BK=32 ST=4 WM=4 WN=1 GM=8 KS=3", "BM=64 BN=128 BK=32 ST=3 WM=2 WN=2 GM=8 KS=3"};
+    const bool f32 = mode == GEMM355_MODE_F32;
+    const char* const* ladder = f32 ? kF32 : kF16r;
+    int i = f32 ? (M <= 32 ? 1 : M <= 128 ? 2 : 3) : (M <= 64 ? 0 : M <= 160 ? 1 : M <= 256 ? 2 : 3);
+    const int64_t fill = f32 ? 2 : 1;   // workgroups x fill >= one round
     TileConfig c{};
-    for (int i = M <= 64 ? 0 : M <= 160 ? 1 : M <= 256 ? 2 : 3; i >= 0; --i) {
-        parse_config(GEMM355_MODE_F16R, kLadder[i], &c);
+    for (; i >= 0; --i) {
+        parse_config(mode, ladder[i], &c);
         const DirectGrid d = direct_grid(c, M, N, K);
-        if (d.tiles_m * d.tiles_n * d.slices >= kCUs * d.per_cu) break;
+        if (fill * d.tiles_m * d.tiles_n * d.slices >= kCUs * d.per_cu) break;
     }
     return c;
 }
@@ -409,9 +421,11 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
     if (M <= kRowsRows) return rows_config(mode);
     // (from 512 rows on the packed path wins once N x K is large: 768 x 4096^2
     // 60 us packed against 79 us on the ring, 1024 x 8192^2 193 against 220)
-    if (mode == GEMM355_MODE_F16R && rows == RingRows::Aligned && N % 4 == 0 && K % 32 == 0 &&
+    const bool panels = rows == RingRows::Aligned && N % 4 == 0 && K % 32 == 0;
+    if (panels && mode == GEMM355_MODE_F16R &&
         (M <= kRingRows || (M <= 2 * kRingRows && N * K <= (int64_t{1} << 22))))
-        return ring_rows_config(M, N, K);
+        return panel_ring_config(mode, M, N, K);
+    if (panels && mode == GEMM355_MODE_F32 && M <= kPanelRowsF32) return panel_ring_config(mode, M, N, K);
     if (mode == GEMM355_MODE_F16R && M <= kDirectRows) {
         // rounding on load: no packing pass, whose cost grows with N x K
         const int bm = M <= 48 ? 32 : M <= 160 ? 64 : 128;
@@ -721,20 +735,26 @@ int launch_direct(const TileConfig& cfg_in, int trans, int64_t M, int64_t N, int
     TileConfig cfg = cfg_in;
     const bool ta = (trans & 1) != 0, tb = (trans & 2) != 0;
     // the f32-panel ring (BK = 32) hands the shapes it does not take to the
-    // register-staged kernel of the 64 x 64 tile
-    if (cfg.bk == 32 && !f16_from_f32_ring_takes(ta, tb, A, lda, B, ldb, N, K)) {
+    // register-staged kernel of the 64 x 64 tile (f16r) or to the split-K
+    // tiles (f32)
+    if (cfg.bk == 32 && !panel_ring_takes(ta, tb, A, lda, B, ldb, N, K)) {
+        if (cfg.mode == GEMM355_MODE_F32)
+            return launch_splitk(splitk_config(cfg.mode), trans, M, N, K, alpha, A, lda, B, ldb,
+                                 beta, C, ldc, s, C16, sc);
         TileConfig fb;
         if (!parse_config(cfg.mode, "BM=64 BN=64 BK=64 KS=3", &fb)) return GEMM355_ERR_CONFIG;
         cfg = fb;
     }
     int n = 0;
     const DirectInstance* inst = nullptr;
-    const DirectInstance* t = direct_instances(&n);
+    const DirectInstance* t = panel_ring_instances(cfg.mode, &n);
     for (int i = 0; i < n; ++i)
         if (t[i].cfg == cfg) inst = &t[i];
-    t = f16_from_f32_ring_instances(&n);
-    for (int i = 0; i < n; ++i)
-        if (t[i].cfg == cfg) inst = &t[i];
+    if (cfg.mode == GEMM355_MODE_F16R) {
+        t = direct_instances(&n);
+        for (int i = 0; i < n; ++i)
+            if (t[i].cfg == cfg) inst = &t[i];
+    }
     if (!inst) return GEMM355_ERR_CONFIG;
     const DirectGrid dg = direct_grid(cfg, M, N, K);
     const int64_t tiles_m = dg.tiles_m, tiles_n = dg.tiles_n, tiles = tiles_m * tiles_n;
@@ -983,11 +1003,20 @@ int save_cache_locked(State& st, const char* path) {
 // ---------------------------------------------------------------------------
 // The autotuner (phobos docs, "gemm, f32", section "Tuning"): stage 1 times
 // every compiled configuration a few times and drops those that fail; stage 2
-// re-times the fastest few over shuffled rounds, one launch of each per round,
-// so the finalists see the same clocks (the lab's sweep() helper).
+// re-times the fastest few over shuffled rounds, one sample of each per round,
+// so the finalists see the same clocks (the lab's sweep() helper).  A sample
+// of a short call is several back-to-back calls between two events (as many
+// as fill kTuneSampleMs, at most kTuneMaxReps), per call: the time of a call
+// in a stream of calls, which a single call would overstate by the host's
+// launch work (a few microseconds, more for calls of several launches) when
+// that is not hidden behind the previous call.
 // ---------------------------------------------------------------------------
+constexpr float kTuneSampleMs = 0.2f;
+constexpr int kTuneMaxReps = 16;
+
 struct Timed {
     TileConfig cfg;
+    int reps = 1;
     std::vector<float> ms;
     float median() const {
         std::vector<float> v = ms;
@@ -996,16 +1025,21 @@ struct Timed {
     }
 };
 
+// One sample: `reps` calls of `cfg` between two events; *ms = time per call.
 int time_once(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, const float* A,
               int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
-              hipStream_t s, hipEvent_t e0, hipEvent_t e1, float* ms) {
+              hipStream_t s, hipEvent_t e0, hipEvent_t e1, int reps, float* ms) {
     hipError_t e = hipEventRecord(e0, s);
     if (e != hipSuccess) return status_of(e);
-    int rc = gemm(cfg.mode, trans, M, N, K, 1.0f, A, lda, B, ldb, beta, C, ldc, s, &cfg, nullptr);
-    if (rc) return rc;
+    for (int i = 0; i < reps; ++i) {
+        const int rc = gemm(cfg.mode, trans, M, N, K, 1.0f, A, lda, B, ldb, beta, C, ldc, s, &cfg,
+                            nullptr);
+        if (rc) return rc;
+    }
     e = hipEventRecord(e1, s);
     if (e == hipSuccess) e = hipEventSynchronize(e1);
     if (e == hipSuccess) e = hipEventElapsedTime(ms, e0, e1);
+    *ms /= static_cast<float>(reps);
     return status_of(e);
 }
 
@@ -1029,11 +1063,15 @@ int tune(int mode, int trans, int64_t M, int64_t N, int64_t K, const float* A, i
     std::vector<Timed> ok;
     if (rc == 0) {
         for (const TileConfig& cfg : configs_of(mode)) {
-            Timed t{cfg, {}};
+            Timed t{cfg, 1, {}};
             float ms = 0.f;
-            int r = time_once(cfg, trans, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, &ms);  // warm-up
+            // warm-up, then the sample size from a second single call
+            int r = time_once(cfg, trans, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, 1, &ms);
+            if (r == 0) r = time_once(cfg, trans, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, 1, &ms);
+            if (r == 0 && ms > 0.f && ms < kTuneSampleMs)
+                t.reps = std::min(kTuneMaxReps, static_cast<int>(std::ceil(kTuneSampleMs / ms)));
             for (int i = 0; i < 3 && r == 0; ++i) {
-                r = time_once(cfg, trans, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, &ms);
+                r = time_once(cfg, trans, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, t.reps, &ms);
                 if (r == 0) t.ms.push_back(ms);
             }
             if (r != 0) {
@@ -1059,7 +1097,8 @@ int tune(int mode, int trans, int64_t M, int64_t N, int64_t K, const float* A, i
             }
             for (size_t i : order) {
                 float ms = 0.f;
-                if (time_once(ok[i].cfg, trans, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1, &ms) == 0)
+                if (time_once(ok[i].cfg, trans, M, N, K, A, lda, B, ldb, beta, C, ldc, s, e0, e1,
+                              ok[i].reps, &ms) == 0)
                     ok[i].ms.push_back(ms);
             }
         }
@@ -1310,7 +1349,7 @@ int gemm355_get_plan_ex(int mode, int transa, int transb, int64_t M, int64_t N, 
     std::string form;
     if (cfg.ks == 1) form = "split-k";
     else if (cfg.ks == 2) form = "rows";
-    else if (cfg.ks == 3) form = "round-on-load";
+    else if (cfg.ks == 3) form = mode == GEMM355_MODE_F16R ? "round-on-load" : "panel-ring";
     else if (mode == GEMM355_MODE_F16R) form = (b.mb % cfg.bm || b.nb % cfg.bn) ? "packed-masked" : "packed";
     else if (is_f32_ring(cfg) && rows != RingRows::None)
         form = rows == RingRows::Aligned && b.mb % cfg.bm == 0 && b.nb % cfg.bn == 0 && b.kb % 16 == 0

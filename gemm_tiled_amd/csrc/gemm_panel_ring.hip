@@ -1,33 +1,40 @@
-// gemm_f16r_ring.hip -- f16r with the operands rounded to binary16 as the
-// matrix instruction's fragments are read (KS=3 configurations with BK = 32):
-// the f32 panels reach shared memory through direct global->LDS copies into a
-// ring of NS stages, as in the f32 ring kernel, so many panels are in flight
-// per workgroup without holding them in registers; each fragment is read in
-// f32, rounded to binary16 (nearest even) in registers and multiplied on
-// v_mfma_f32_16x16x32_f16 with f32 accumulation.  For a few hundred rows of C
-// the call streams B once from memory and the matrix work is small, so what
-// matters is keeping enough copies in flight to reach the memory roof; the
-// packing pass of the packed path (read, round and write all of B, then read
-// it again) and the one-panel-ahead register staging of the other KS=3 kernel
-// both fall short of it there.
+// gemm_panel_ring.hip -- the f32-panel ring with K split over workgroups
+// (KS=3 configurations with BK = 32), in both modes: the f32 panels of A and
+// B reach shared memory through direct global->LDS copies into a ring of NS
+// stages, as in the f32 ring kernel, so many panels are in flight per
+// workgroup without holding them in registers; each fragment is read in f32
+// and, in the f16r mode, rounded to binary16 (nearest even) in registers and
+// multiplied on v_mfma_f32_16x16x32_f16, in the f32 mode multiplied as read on
+// v_mfma_f32_16x16x4_f32, with f32 accumulation either way.  For up to a few
+// hundred rows of C the call streams B once from memory and the matrix work is
+// small, so what matters is keeping enough copies in flight to reach the
+// memory roof; in f16r the packing pass of the packed path (read, round and
+// write all of B, then read it again) and the one-panel-ahead register
+// staging of the other KS=3 kernel both fall short of it there, in f32 the
+// split-K tiles (KS=1: partial tiles summed by a second pass).
 //
 // Shapes: the plain layout with 16-byte aligned rows, N % 4 == 0 and
 // K % 32 == 0 (M and N need not be tile multiples: copies of rows past M read
 // row M - 1 and of columns past N column n0, values that only reach outputs
-// the masked epilogue never stores).  K is split over blockIdx.y as in the
-// other KS=3 kernel, the last workgroup of a tile adding the slices' partial
-// tiles in slice order.
+// the masked epilogue never stores).  K is split over blockIdx.y, the last
+// workgroup of a tile adding the slices' partial tiles in slice order.
 #include "f16_kernel.hpp"
 
-// X(BM, BN, NS, WM, WN, GM): the compiled configurations.
-#define G355_F16_FROM_F32_RING_CONFIGS(X) \
-    X(32, 64, 4, 2, 1, 8)                 \
-    X(32, 128, 4, 2, 2, 8)                \
-    X(64, 64, 4, 4, 1, 8)                 \
-    X(64, 128, 3, 2, 2, 8)                \
-    X(128, 128, 3, 4, 2, 8)               \
-    X(128, 256, 3, 2, 4, 8)               \
+// X(BM, BN, NS, WM, WN, GM): the compiled configurations of each mode.
+#define G355_PANEL_RING_F16R_CONFIGS(X) \
+    X(32, 64, 4, 2, 1, 8)               \
+    X(32, 128, 4, 2, 2, 8)              \
+    X(64, 64, 4, 4, 1, 8)               \
+    X(64, 128, 3, 2, 2, 8)              \
+    X(128, 128, 3, 4, 2, 8)             \
+    X(128, 256, 3, 2, 4, 8)             \
     X(256, 128, 3, 4, 2, 8)
+#define G355_PANEL_RING_F32_CONFIGS(X) \
+    X(32, 64, 4, 2, 1, 8)              \
+    X(32, 128, 4, 2, 2, 8)             \
+    X(64, 64, 4, 4, 1, 8)              \
+    X(64, 128, 3, 2, 2, 8)             \
+    X(128, 128, 3, 4, 2, 8)
 
 namespace g355 {
 namespace {
@@ -104,9 +111,12 @@ __device__ __forceinline__ bool last_slice_adds(f32x4v (&acc)[GFM][GFN], const D
 //      (2-4% of the call's time at 256-512 rows).
 //   B: 32 k-rows of BN floats, BN * 4 bytes apart; a copy instruction fills
 //      1024 / (4 BN) whole k-rows.
-// The instruction's sum runs over its 32 k in any order, so lane quarter q
-// takes k in {4q .. 4q + 3} and {16 + 4q .. 16 + 4q + 3}, for A and B alike:
-// two 16-byte reads of an A row.  Columns: the wave tile's columns are dealt
+// A panel's sum over its 32 k may run in any order, so lane quarter q takes
+// k in {4q .. 4q + 3} and {16 + 4q .. 16 + 4q + 3}, for A and B alike: two
+// 16-byte reads of an A row.  In f16r these eight k are the lane's eight
+// operands of one v_mfma_f32_16x16x32_f16; in f32, step t of eight
+// v_mfma_f32_16x16x4_f32 takes the t-th of them from every lane quarter, so
+// each step sums four distinct k and the eight steps all 32.  Columns: the wave tile's columns are dealt
 // to its 16-column blocks four at a time -- lane column r16 of block 4g + jj
 // is column 64g + 4 r16 + jj of the wave tile -- so one 16-byte read of a B
 // k-row gives a lane its value for four blocks (eight reads: four blocks'
@@ -115,7 +125,7 @@ __device__ __forceinline__ bool last_slice_adds(f32x4v (&acc)[GFM][GFN], const D
 // and writes as one piece.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int NS, int WM, int WN>
-struct F16RingShape {
+struct PanelRingShape {
     static constexpr int BK = 32;
     static constexpr int NW = WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;
@@ -251,9 +261,13 @@ __device__ __forceinline__ void store_tile_dealt(const f32x4v (&acc)[GFM][GFN], 
     }
 }
 
-template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED, bool OUT16>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_f16_f32ring_kernel(DirectArgs p) {
-    using S = F16RingShape<BM, BN, NS, WM, WN>;
+// F16: round to binary16 and multiply on v_mfma_f32_16x16x32_f16 (f16r);
+// otherwise multiply the f32 values on v_mfma_f32_16x16x4_f32, eight steps a
+// panel, step s taking from lane quarter q the s-th of its eight k (so the
+// same fragment reads serve both modes).
+template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED, bool OUT16, bool F16>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_panel_ring_kernel(DirectArgs p) {
+    using S = PanelRingShape<BM, BN, NS, WM, WN>;
     constexpr int GFM = S::GFM, GFN = S::GFN, GG = GFN / 4;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * S::STAGE];
 
@@ -327,28 +341,51 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_f32ring_kernel(DirectAr
         ring_barrier();
         fill(stage_of((kt + NS - 1) % NS), min(kt + NS - 1, nk - 1));
         const lds_u8* st = (const lds_u8*)(stage_of(kt % NS));
-        f16x8 fa[GFM], fb[GFN];
+        f32x4v a0[GFM], a1[GFM];
 #pragma unroll
-        for (int i = 0; i < GFM; ++i)
-            fa[i] = rn8(*reinterpret_cast<lds_f32x4c*>(st + a_off0 + i * 16 * S::A_ROW),
-                        *reinterpret_cast<lds_f32x4c*>(st + a_off1 + i * 16 * S::A_ROW));
-#pragma unroll
-        for (int g = 0; g < GG; ++g) {
-            f32x4v v[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                v[t] = *reinterpret_cast<lds_f32x4c*>(st + b_off + (t < 4 ? t : t + 12) * S::B_ROW +
-                                                      g * 256);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                fb[4 * g + jj] = rn8(f32x4v{v[0][jj], v[1][jj], v[2][jj], v[3][jj]},
-                                     f32x4v{v[4][jj], v[5][jj], v[6][jj], v[7][jj]});
+        for (int i = 0; i < GFM; ++i) {
+            a0[i] = *reinterpret_cast<lds_f32x4c*>(st + a_off0 + i * 16 * S::A_ROW);
+            a1[i] = *reinterpret_cast<lds_f32x4c*>(st + a_off1 + i * 16 * S::A_ROW);
         }
+        if constexpr (F16) {
+            f16x8 fa[GFM], fb[GFN];
 #pragma unroll
-        for (int i = 0; i < GFM; ++i)
+            for (int i = 0; i < GFM; ++i) fa[i] = rn8(a0[i], a1[i]);
 #pragma unroll
-            for (int j = 0; j < GFN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            for (int g = 0; g < GG; ++g) {
+                f32x4v v[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    v[t] = *reinterpret_cast<lds_f32x4c*>(st + b_off + (t < 4 ? t : t + 12) * S::B_ROW +
+                                                          g * 256);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    fb[4 * g + jj] = rn8(f32x4v{v[0][jj], v[1][jj], v[2][jj], v[3][jj]},
+                                         f32x4v{v[4][jj], v[5][jj], v[6][jj], v[7][jj]});
+            }
+#pragma unroll
+            for (int i = 0; i < GFM; ++i)
+#pragma unroll
+                for (int j = 0; j < GFN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int g = 0; g < GG; ++g) {
+                f32x4v v[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    v[t] = *reinterpret_cast<lds_f32x4c*>(st + b_off + (t < 4 ? t : t + 12) * S::B_ROW +
+                                                          g * 256);
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int i = 0; i < GFM; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            acc[i][4 * g + jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                t < 4 ? a0[i][t] : a1[i][t - 4], v[t][jj], acc[i][4 * g + jj], 0, 0, 0);
+            }
+        }
     }
     wait_vmcnt<0>();   // no copy may still be landing in LDS when the workgroup ends
 
@@ -362,37 +399,47 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_f32ring_kernel(DirectAr
                                                   p.beta, lane);
 }
 
-template <int BM, int BN, int NS, int WM, int WN, int GM>
-hipError_t launch_f32ring(const DirectArgs& a, bool ta, bool tb, bool masked, hipStream_t s) {
-    // the host hands only the shapes this kernel takes (f16_from_f32_ring_takes)
-    if (ta || tb || a.N % 4 != 0 || a.K % 32 != 0 || a.depth % 32 != 0 || a.K <= 0)
+template <int BM, int BN, int NS, int WM, int WN, int GM, bool F16>
+hipError_t launch_panel_ring(const DirectArgs& a, bool ta, bool tb, bool masked, hipStream_t s) {
+    // the host hands only the shapes this kernel takes (panel_ring_takes)
+    if (ta || tb || a.N % 4 != 0 || a.K % 32 != 0 || a.depth % 32 != 0 || a.K <= 0 ||
+        (!F16 && a.C16))
         return hipErrorInvalidValue;
     const dim3 grid(a.tiles_m * a.tiles_n, a.slices), block(WM * WN * 64);
     const bool edge = masked || a.M % BM != 0 || a.N % BN != 0;
-    if (a.C16) {
-        if (edge) gemm_f16_f32ring_kernel<BM, BN, NS, WM, WN, GM, true, true><<<grid, block, 0, s>>>(a);
-        else gemm_f16_f32ring_kernel<BM, BN, NS, WM, WN, GM, false, true><<<grid, block, 0, s>>>(a);
-    } else {
-        if (edge) gemm_f16_f32ring_kernel<BM, BN, NS, WM, WN, GM, true, false><<<grid, block, 0, s>>>(a);
-        else gemm_f16_f32ring_kernel<BM, BN, NS, WM, WN, GM, false, false><<<grid, block, 0, s>>>(a);
+    if constexpr (F16) {
+        if (a.C16) {
+            if (edge) gemm_panel_ring_kernel<BM, BN, NS, WM, WN, GM, true, true, true><<<grid, block, 0, s>>>(a);
+            else gemm_panel_ring_kernel<BM, BN, NS, WM, WN, GM, false, true, true><<<grid, block, 0, s>>>(a);
+            return hipGetLastError();
+        }
     }
+    if (edge) gemm_panel_ring_kernel<BM, BN, NS, WM, WN, GM, true, false, F16><<<grid, block, 0, s>>>(a);
+    else gemm_panel_ring_kernel<BM, BN, NS, WM, WN, GM, false, false, F16><<<grid, block, 0, s>>>(a);
     return hipGetLastError();
 }
 
-#define G355_F32RING_INSTANCE(BM, BN, NS, WM, WN, GM) \
-    {{GEMM355_MODE_F16R, BM, BN, 32, NS, WM, WN, GM, 3}, &launch_f32ring<BM, BN, NS, WM, WN, GM>},
+#define G355_PANEL_RING_F16R(BM, BN, NS, WM, WN, GM) \
+    {{GEMM355_MODE_F16R, BM, BN, 32, NS, WM, WN, GM, 3}, &launch_panel_ring<BM, BN, NS, WM, WN, GM, true>},
+#define G355_PANEL_RING_F32(BM, BN, NS, WM, WN, GM) \
+    {{GEMM355_MODE_F32, BM, BN, 32, NS, WM, WN, GM, 3}, &launch_panel_ring<BM, BN, NS, WM, WN, GM, false>},
 
-const DirectInstance kF32RingInstances[] = {G355_F16_FROM_F32_RING_CONFIGS(G355_F32RING_INSTANCE)};
+const DirectInstance kF16rInstances[] = {G355_PANEL_RING_F16R_CONFIGS(G355_PANEL_RING_F16R)};
+const DirectInstance kF32Instances[] = {G355_PANEL_RING_F32_CONFIGS(G355_PANEL_RING_F32)};
 
 }  // namespace
 
-const DirectInstance* f16_from_f32_ring_instances(int* count) {
-    *count = static_cast<int>(sizeof(kF32RingInstances) / sizeof(kF32RingInstances[0]));
-    return kF32RingInstances;
+const DirectInstance* panel_ring_instances(int mode, int* count) {
+    if (mode == GEMM355_MODE_F32) {
+        *count = static_cast<int>(sizeof(kF32Instances) / sizeof(kF32Instances[0]));
+        return kF32Instances;
+    }
+    *count = static_cast<int>(sizeof(kF16rInstances) / sizeof(kF16rInstances[0]));
+    return kF16rInstances;
 }
 
-bool f16_from_f32_ring_takes(bool ta, bool tb, const float* A, int64_t lda, const float* B,
-                             int64_t ldb, int64_t N, int64_t K) {
+bool panel_ring_takes(bool ta, bool tb, const float* A, int64_t lda, const float* B, int64_t ldb,
+                      int64_t N, int64_t K) {
     auto vec = [](const float* p, int64_t ld) {
         return ld % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0;
     };

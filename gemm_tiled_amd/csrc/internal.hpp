@@ -169,8 +169,9 @@ hipError_t launch_f32_rows(const float* A, int64_t lda, bool ta, const float* B,
                            unsigned* counts, hipStream_t s);
 
 // The configurations that round the operands to binary16 as they stage them
-// (KS=3, gemm_f16r_direct.hip): f16r only, no packing pass; K is split over
-// blockIdx.y in slices of `depth` (a multiple of 64) and, with slices > 1,
+// through registers (KS=3, BK=64, gemm_f16r_direct.hip): f16r only, no
+// packing pass; K is split over blockIdx.y in slices of `depth` (a multiple
+// of the panel depth) and, with slices > 1,
 // the workgroups of a tile store their accumulators in P (slices x tiles x
 // BM x BN floats, below 2^31 bytes) and the last one to arrive (counted in
 // counts[tile], zero before and after the launch) adds them in slice order
@@ -194,14 +195,15 @@ struct DirectInstance {
     DirectLaunch launch;
 };
 const DirectInstance* direct_instances(int* count);
-// The KS=3 configurations with BK = 32 (gemm_f16r_ring.hip): f32 panels in a
-// ring of direct-to-LDS copies, rounded as the fragments are read for
-// v_mfma_f32_16x16x32_f16.  They take the plain layout with 16-byte aligned
-// rows, N % 4 == 0 and K % 32 == 0 (f16_from_f32_ring_takes), slices of K a
-// multiple of 32 deep.
-const DirectInstance* f16_from_f32_ring_instances(int* count);
-bool f16_from_f32_ring_takes(bool ta, bool tb, const float* A, int64_t lda, const float* B,
-                             int64_t ldb, int64_t N, int64_t K);
+// The KS=3 configurations with BK = 32 (gemm_panel_ring.hip), in both modes:
+// f32 panels in a ring of direct-to-LDS copies, each fragment read in f32 and
+// multiplied on v_mfma_f32_16x16x4_f32 (f32) or rounded to binary16 for
+// v_mfma_f32_16x16x32_f16 (f16r).  They take the plain layout with 16-byte
+// aligned rows, N % 4 == 0 and K % 32 == 0 (panel_ring_takes), slices of K a
+// multiple of 32 deep; binary16 C in f16r only.
+const DirectInstance* panel_ring_instances(int mode, int* count);
+bool panel_ring_takes(bool ta, bool tb, const float* A, int64_t lda, const float* B, int64_t ldb,
+                      int64_t N, int64_t K);
 
 // Measurement kernels.
 hipError_t launch_roof_mfma(int mode, int form, int64_t iters, int blocks, float* sink, double* flops,

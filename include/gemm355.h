@@ -168,7 +168,9 @@ int gemm355_gemm_noalloc(int mode, int transa, int transb, int64_t M, int64_t N,
 /*
  * Per-shape tile autotuning (phobos docs, "gemm, f32", section "Tuning": time
  * every configuration briefly, skip those that fail, then re-time the fastest
- * few over interleaved rounds under the same clocks).  Runs the candidates on
+ * few over interleaved rounds under the same clocks; a call under 0.2 ms is
+ * timed as a batch of back-to-back calls, the time of a call in a stream of
+ * calls).  Runs the candidates on
  * the caller's A and B and on a scratch C the library allocates and frees
  * (the caller's C is not touched), synchronises `stream`, and stores the
  * winner in the per-shape cache used by later calls with the same key
@@ -223,13 +225,16 @@ int gemm355_get_plan_ex(int mode, int transa, int transb, int64_t M, int64_t N, 
  * BK|TILE_K, ST|STAGES, WM, WN, GM, KS|SPLITK; omitted keys take the first compiled
  * instance that matches the given ones, except KS, whose absence selects the
  * tiled configurations (KS=0).  KS=1: K split over workgroups, partial tiles
- * summed by a second pass; KS=2: one wavefront per few rows of C; KS=3 (f16r
- * only): the operands rounded to binary16 as they are staged (BK=64 through
- * registers, BK=16 from a ring of f32 panels), K split over workgroups and
- * the slices added in order by the tile's last workgroup, with no packing
- * pass.  A ring configuration (direct-to-LDS copies) that a call's row
- * alignment or shape rules out runs that call in a register-staged kernel
- * instead: the f32 one of the same tile, or BM=64 BN=64 BK=64 KS=3 in f16r.
+ * summed by a second pass; KS=2: one wavefront per few rows of C; KS=3: K
+ * split over workgroups and the slices added in order by the tile's last
+ * workgroup, the operands staged as f32 panels from a ring of direct-to-LDS
+ * copies (BK=32, both modes; in f16r rounded to binary16 as the fragments
+ * are read, with no packing pass) or, in f16r only, rounded to binary16
+ * through registers (BK=64).  A ring configuration (direct-to-LDS copies)
+ * that a call's row alignment or shape rules out runs that call in a
+ * register-staged kernel instead: the f32 one of the same tile, BM=64 BN=64
+ * BK=64 KS=3 for the f16r panel ring, the split-K tiles (KS=1) for the f32
+ * one.
  * NULL or "" clears the pin.  The environment
  * variables GEMM355_CONFIG_F32 / GEMM355_CONFIG_F16R set the initial pin.
  * Returns 0 or GEMM355_ERR_CONFIG (the pin is then unchanged).  Host only.

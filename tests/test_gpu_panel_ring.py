@@ -1,0 +1,103 @@
+"""GPU parity tests of the f32-panel ring in the f32 mode (KS=3, BK=32: f32
+panels through direct-to-LDS copies, multiplied as read on the f32 matrix
+instruction, K split over workgroups with the last workgroup of a tile adding
+the slices in order).
+
+Same bound as the other f32 parity tests against the float64 oracle; exact
+results on small integers; bitwise repeatability (the slice order is fixed);
+the shapes the ring does not take (K % 32 != 0, unaligned rows, transposed
+operands) handed to the split-K tiles.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_inputs, small_integers
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():   # collected on CPU-only hosts, never run there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gemm_tiled_amd as g  # noqa: E402
+from tests.gpu_helpers import pinned, run, say, to_device  # noqa: E402
+
+RINGS = ["BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 KS=3", "BM=32 BN=128 BK=32 ST=4 WM=2 WN=2 KS=3",
+         "BM=64 BN=64 BK=32 ST=4 WM=4 WN=1 KS=3", "BM=64 BN=128 BK=32 ST=3 WM=2 WN=2 KS=3",
+         "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 KS=3"]
+
+
+def assert_parity(A, B, C, alpha, beta, got):
+    st = oracle.check("f32", A, B, C, alpha, beta, got)
+    assert st["n_fail"] == 0, st
+
+
+@pytest.mark.parametrize("cfg", RINGS)
+@pytest.mark.parametrize("M,N,K,lds", [
+    (17, 1000, 4096, {}),                           # ragged M and N (N % 4 == 0), many slices
+    (300, 520, 2112, {"lda": 2116, "ldb": 524, "ldc": 521}),   # padded 16-byte rows, odd ldc
+    (1000, 300, 800, {}),                           # many tile rows, one or two slices
+    (64, 4096, 4096, {}),                           # whole tiles
+    (33, 256, 32, {}),                              # one panel
+    (130, 2052, 1024, {"ldc": 2056}),               # a column group past N in a ragged tile
+])
+def test_panel_ring_against_the_oracle(cfg, M, N, K, lds):
+    A, B, C = make_inputs(M, N, K, "normal", seed=31, **lds)
+    with pinned("f32", cfg):
+        say(f"[panel ring f32] {cfg} {M}x{N}x{K} {lds}")
+        got = run("f32", A, B, C, -0.75, 1.5)
+        again = run("f32", A, B, C, -0.75, 1.5)
+    assert_parity(A, B, C, -0.75, 1.5, got)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+
+
+@pytest.mark.parametrize("cfg", RINGS)
+@pytest.mark.parametrize("M,ldc_pad", [(1, 0), (40, 2), (200, 0)])
+def test_panel_ring_small_integers_exact(cfg, M, ldc_pad):
+    """Exact on small integers, with the epilogue's vector path (ldc % 4 == 0)
+    and its element-by-element one (ldc = N + 2); beta = 0 never reads C (NaN
+    there)."""
+    N, K = 2048, 4096
+    A, B, C = small_integers(M, N, K, seed=32, ldc=N + ldc_pad)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    Cn = np.full((M, N + ldc_pad), np.nan, dtype=np.float32)[:, :N]
+    with pinned("f32", cfg):
+        say(f"[panel ring f32 exact] {cfg} {M}x{N}x{K} ldc={N + ldc_pad}")
+        got = run("f32", A, B, C, -2.0, 0.5)
+        assert np.array_equal(got, (-2.0 * exact + 0.5 * C.astype(np.float64)).astype(np.float32))
+        got = run("f32", A, B, Cn, 1.0, 0.0)
+        assert np.array_equal(got, exact.astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K,lds,trans", [
+    (64, 1024, 4080, {}, (False, False)),           # K % 32 != 0
+    (64, 1022, 2048, {}, (False, False)),           # N % 4 != 0
+    (64, 1024, 2048, {"lda": 2049}, (False, False)),   # rows not 16-byte aligned
+    (64, 1024, 2048, {}, (True, False)),            # A stored transposed
+    (64, 1024, 2048, {}, (False, True)),            # B stored transposed
+])
+def test_panel_ring_hands_other_shapes_to_split_k(M, N, K, lds, trans):
+    A, B, C = make_inputs(M, N, K, "uniform", seed=33, **lds)
+    ta, tb = trans
+    tA = to_device(np.ascontiguousarray(A.T) if ta else A)
+    tB = to_device(np.ascontiguousarray(B.T) if tb else B)
+    tC = to_device(C)
+    with pinned("f32", RINGS[0]):
+        say(f"[panel ring f32 hand-off] {M}x{N}x{K} {lds} ta={ta} tb={tb}")
+        g.gemm("f32", tA, tB, tC, 0.5, 2.0, transa=ta, transb=tb)
+        torch.cuda.synchronize()
+    assert_parity(A, B, C, 0.5, 2.0, tC.cpu().numpy())
+
+
+def test_panel_ring_counters_reset_between_shapes():
+    """Calls of different tile counts in a row share the arrival counters: each
+    launch must leave every counter it used at zero."""
+    with pinned("f32", RINGS[2]):
+        for (M, N, K) in [(64, 4096, 4096), (200, 1024, 3008), (64, 4096, 4096), (20, 300, 8000)]:
+            A, B, C = make_inputs(M, N, K, "normal", seed=M + N)
+            say(f"[panel ring f32 counters] {M}x{N}x{K}")
+            got = run("f32", A, B, C, 1.0, 1.0)
+            assert_parity(A, B, C, 1.0, 1.0, got)

@@ -239,8 +239,14 @@ def test_splitk_is_the_default_for_few_rows():
         assert "KS=2" in g.get_config(mode, 1, 4096, 4096)
         assert "KS=2" in g.get_config(mode, 16, 4096, 4096)
         assert "KS=" not in g.get_config(mode, 4096, 4096, 4096)
-    assert g.get_config("f32", 17, 4096, 4096).startswith("BM=32 BN=128 BK=32")
-    assert "KS=1" in g.get_config("f32", 64, 4096, 4096)
+    # f32: the f32-panel ring up to 256 rows where it takes the shape, else
+    # the split-K tiles up to 128 rows
+    assert g.get_config("f32", 17, 4096, 4096).startswith("BM=32 BN=128 BK=32 ST=4")
+    assert g.get_config("f32", 64, 4096, 4096).startswith("BM=64 BN=64 BK=32 ST=4")
+    assert g.get_config("f32", 256, 4096, 4096).startswith("BM=64 BN=128 BK=32 ST=3")
+    assert all("KS=3" in g.get_config("f32", m, 4096, 4096) for m in (17, 64, 256))
+    assert "KS=" not in g.get_config("f32", 257, 4096, 4096)
+    assert "KS=1" in g.get_config("f32", 64, 4096, 4080)
     # f16r: the configurations that round on load -- the f32-panel ring up to
     # 512 rows where it takes the shape (K % 32 == 0; up to 1024 rows for a
     # small N x K), else the register-staged one up to 384 rows
