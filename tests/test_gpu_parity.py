@@ -421,13 +421,16 @@ def test_non_default_stream(mode):
     assert_parity(mode, A, B, C, 1.0, 0.5, tC.cpu().numpy())
 
 
-@pytest.mark.parametrize("mode,M,K", [("f32", 640, 512), ("f16r", 640, 512), ("f16r", 16, 4096),
-                                      ("f32", 16, 4096)])
+@pytest.mark.parametrize("mode,M,K", [("f32", 640, 512), ("f16r", 640, 512), ("f16r", 1280, 512),
+                                      ("f16r", 16, 4096), ("f32", 16, 4096), ("f16r", 64, 4096),
+                                      ("f32", 64, 4096)])
 def test_graph_capture_replays(mode, M, K):
     """The calls enqueue kernels only (no allocation once the stream's workspace
     exists, no memset), so they can be captured into a HIP graph; every replay,
     with eager work and synchronisations in between, matches the eager call bit
-    for bit.  M = 16 takes the split-K path (partials + reduction)."""
+    for bit.  M = 16 takes the few-rows path (partials + counters), M = 64 the
+    f32-panel ring split over K (partials + counters), f16r 1280 rows the
+    packed path (packed operands in scratch)."""
     N = 384
     A, B, C = make_inputs(M, N, K, "uniform", seed=14)
     tA, tB, tC = to_device(A), to_device(B), to_device(C)
