@@ -967,11 +967,16 @@ def dominant_kernel(mode, tile):
     """The kernel that does the work of a call with this tile, by the name
     prefix rocprofv3 shows (for f16r, after its packing pass)."""
     f = _tile_fields(tile)
+    ks = f.get("KS", 0)
+    if ks == 2:
+        return "gemm_rows_kernel"
+    if ks == 3:
+        if f.get("BK") == 32:
+            return "gemm_panel_ring_kernel" + (" (no packing pass)" if mode == "f16r" else "")
+        return "gemm_f16_direct_kernel (no packing pass)"
     if mode == "f32":
-        ring = f.get("ST", 0) >= 3 and f.get("BK") == 16 and "KS" not in f
+        ring = f.get("ST", 0) >= 3 and f.get("BK") == 16 and ks == 0
         return "gemm_f32_ring_kernel" if ring else "gemm_f32_kernel"
-    if f.get("KS") == 3:
-        return "gemm_f16_direct_kernel or gemm_f16_f32ring_kernel (no packing pass)"
     return "pack_kernel + " + ("gemm_f16_ring_kernel" if f.get("BK") == 32 else "gemm_f16_kernel")
 
 
