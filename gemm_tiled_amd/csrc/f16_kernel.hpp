@@ -436,22 +436,28 @@ struct StagedRows {
     static constexpr int BYTES = 16 * RS * 4;
 };
 
-// Epilogue through shared memory for a whole tile whose C rows allow
-// vector accesses (f32: 16-byte aligned rows; binary16: 8-byte aligned): one
-// 16-row band of the wave's tile at a time is written to the wave's own
-// shared memory in the matrix-instruction layout and read back as four
-// consecutive columns per lane, so C is read (beta != 0) and written in whole
-// 128-byte row segments instead of the 64-byte (f32) or 32-byte (binary16)
-// ones of the block layout.  The same value as store_tile / store_tile16:
-// fma(alpha, acc, beta*c), binary16 C widened exactly and the result rounded
-// once to nearest even.  A wave's shared-memory instructions complete in
-// order, so no wait separates the write of a band, its read-back and the next
-// band's write.
-template <int FM, int FN, int TN, bool OUT16, typename CT>
+// Epilogue through shared memory for a tile whose C rows allow vector
+// accesses (f32: 16-byte aligned rows; binary16: 8-byte aligned): one 16-row
+// band of the wave's tile at a time is written to the wave's own shared
+// memory in the matrix-instruction layout and read back as four consecutive
+// columns per lane, so C is read (beta != 0) and written in whole 128-byte
+// row segments instead of the 64-byte (f32) or 32-byte (binary16) ones of the
+// block layout.  The same value as store_tile / store_tile16: fma(alpha, acc,
+// beta*c), binary16 C widened exactly and the result rounded once to nearest
+// even.  A wave's shared-memory instructions complete in order, so no wait
+// separates the write of a band, its read-back and the next band's write.
+// MASKED (a tile of a ragged launch) skips rows >= M and columns >= N: a lane
+// whose four columns all lie inside keeps its one access, the lane across the
+// edge goes element by element.  Rows that do not allow vector accesses
+// (!vec) are read back one column per lane instead, 64 lanes on 64
+// consecutive columns of a row: single-element accesses, still whole row
+// segments per instruction.
+template <int FM, int FN, int TN, bool OUT16, bool MASKED, typename CT>
 __device__ __forceinline__ void store_tile_m16_staged(const f32x4 (&acc)[FM][FN],
                                                       CT* __restrict__ C, int64_t ldc,
-                                                      int row0, int col0, float alpha, float beta,
-                                                      int lane, unsigned char* stage) {
+                                                      int row0, int col0, int M, int N, float alpha,
+                                                      float beta, int lane, unsigned char* stage,
+                                                      bool vec) {
     using R = StagedRows<TN>;
     static_assert(FN * 16 == TN, "a band is the wave tile's width");
     constexpr int LPR = TN / 4;        // lanes per staged row (four columns each)
@@ -466,26 +472,51 @@ __device__ __forceinline__ void store_tile_m16_staged(const f32x4 (&acc)[FM][FN]
     auto c_at = [&](int i, int it) {
         return C + (int64_t)(row0 + 16 * i + it * RPI + rr0) * ldc + col0 + 4 * c4;
     };
+    // how many of the lane's four columns of staged row (i, it) are inside
+    // C: 4 (one access), 1..3 (element by element) or 0
+    auto inside = [&](int i, int it) -> int {
+        if constexpr (!MASKED) return 4;
+        const int row = row0 + 16 * i + it * RPI + rr0, col = col0 + 4 * c4;
+        return row < M ? max(0, min(4, N - col)) : 0;
+    };
     // binary16 C: four values as two 32-bit words (low half first)
     auto h2f = [](uint32_t bits) {
         return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
     };
     auto load4 = [&](int i, int it) -> f32x4 {
-        if constexpr (OUT16) {
-            const u32x2 w = *reinterpret_cast<const u32x2*>(c_at(i, it));
-            return f32x4{h2f(w[0] & 0xffffu), h2f(w[0] >> 16), h2f(w[1] & 0xffffu), h2f(w[1] >> 16)};
-        } else {
-            return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(c_at(i, it)));
+        const int n = inside(i, it);
+        if (n == 4) {
+            if constexpr (OUT16) {
+                const u32x2 w = *reinterpret_cast<const u32x2*>(c_at(i, it));
+                return f32x4{h2f(w[0] & 0xffffu), h2f(w[0] >> 16), h2f(w[1] & 0xffffu),
+                             h2f(w[1] >> 16)};
+            } else {
+                return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(c_at(i, it)));
+            }
         }
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < n; ++e) {
+            if constexpr (OUT16) v[e] = h2f(c_at(i, it)[e]);
+            else v[e] = c_at(i, it)[e];
+        }
+        return v;
     };
     auto store4 = [&](int i, int it, f32x4 v) {
-        if constexpr (OUT16) {
-            u32x2 w;
-            w[0] = uint32_t{f32_to_f16_bits(v[0])} | (uint32_t{f32_to_f16_bits(v[1])} << 16);
-            w[1] = uint32_t{f32_to_f16_bits(v[2])} | (uint32_t{f32_to_f16_bits(v[3])} << 16);
-            *reinterpret_cast<u32x2*>(c_at(i, it)) = w;
-        } else {
-            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(c_at(i, it)));
+        const int n = inside(i, it);
+        if (n == 4) {
+            if constexpr (OUT16) {
+                u32x2 w;
+                w[0] = uint32_t{f32_to_f16_bits(v[0])} | (uint32_t{f32_to_f16_bits(v[1])} << 16);
+                w[1] = uint32_t{f32_to_f16_bits(v[2])} | (uint32_t{f32_to_f16_bits(v[3])} << 16);
+                *reinterpret_cast<u32x2*>(c_at(i, it)) = w;
+            } else {
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(c_at(i, it)));
+            }
+            return;
+        }
+        for (int e = 0; e < n; ++e) {
+            if constexpr (OUT16) c_at(i, it)[e] = f32_to_f16_bits(v[e]);
+            else c_at(i, it)[e] = v[e];
         }
     };
     auto stage_band = [&](int i) __attribute__((always_inline)) {
@@ -497,6 +528,55 @@ __device__ __forceinline__ void store_tile_m16_staged(const f32x4 (&acc)[FM][FN]
     auto staged = [&](int it) __attribute__((always_inline)) {
         return *(const lds_f32x4*)(st + (it * RPI + rr0) * R::RS + 4 * c4);
     };
+    if (!vec) {
+        // one column per lane: staged row rr, columns 64 h + lane
+        constexpr int H = TN / 64;
+        static_assert(TN % 64 == 0, "whole 64-column groups");
+        auto at = [&](int i, int rr, int h) {
+            return C + (int64_t)(row0 + 16 * i + rr) * ldc + col0 + 64 * h + lane;
+        };
+        auto in = [&](int i, int rr, int h) {
+            return !MASKED || (row0 + 16 * i + rr < M && col0 + 64 * h + lane < N);
+        };
+        auto ld1 = [&](const CT* a) -> float {
+            if constexpr (OUT16) return h2f(*a);
+            else return __builtin_nontemporal_load(a);
+        };
+        auto st1 = [&](CT* a, float v) {
+            if constexpr (OUT16) *a = f32_to_f16_bits(v);
+            else __builtin_nontemporal_store(v, a);
+        };
+        // a band's staged values are all read back before its first store,
+        // and its C values (beta != 0) all loaded, so each kind of access is
+        // waited for once per band
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            stage_band(i);
+            float v[16][H], c[16][H];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+                for (int h = 0; h < H; ++h) v[rr][h] = st[rr * R::RS + 64 * h + lane];
+            if (beta != 0.f) {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+                    for (int h = 0; h < H; ++h) c[rr][h] = in(i, rr, h) ? ld1(at(i, rr, h)) : 0.f;
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+                    for (int h = 0; h < H; ++h)
+                        if (in(i, rr, h)) st1(at(i, rr, h), __builtin_fmaf(alpha, v[rr][h], beta * c[rr][h]));
+            } else {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+                    for (int h = 0; h < H; ++h)
+                        if (in(i, rr, h)) st1(at(i, rr, h), alpha * v[rr][h]);
+            }
+        }
+        return;
+    }
     if (beta == 0.f) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -783,25 +863,21 @@ void gemm_f16_ring_kernel(F16Args p) {
 
     // vector rows of C: f32 16-byte aligned, binary16 8-byte aligned
         const uintptr_t c_addr = OUT16 ? reinterpret_cast<uintptr_t>(p.C16) : reinterpret_cast<uintptr_t>(p.C);
-        const bool staged = !MASKED && p.ldc % 4 == 0 && (c_addr & (OUT16 ? 7 : 15)) == 0;
+        const bool vec = p.ldc % 4 == 0 && (c_addr & (OUT16 ? 7 : 15)) == 0;
         if (!finish) {
             // another workgroup finishes this tile
-        } else if (staged) {
+        } else {
             // every wave is past its last fragment read once all have arrived here
             __syncthreads();
             unsigned char* mine = ring + wave * StagedRows<S::TN>::BYTES;
             if constexpr (OUT16)
-                store_tile_m16_staged<GFM, GFN, S::TN, true>(acc, p.C16, p.ldc, m0 + wr * S::TM,
-                                                             n0 + wc * S::TN, p.alpha, p.beta, lane, mine);
+                store_tile_m16_staged<GFM, GFN, S::TN, true, MASKED>(
+                    acc, p.C16, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta,
+                    lane, mine, vec);
             else
-                store_tile_m16_staged<GFM, GFN, S::TN, false>(acc, p.C, p.ldc, m0 + wr * S::TM,
-                                                              n0 + wc * S::TN, p.alpha, p.beta, lane, mine);
-        } else if constexpr (OUT16) {
-            store_tile_m16<GFM, GFN, MASKED, true>(acc, p.C16, p.ldc, m0 + wr * S::TM,
-                                                   n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta, lane);
-        } else {
-            store_tile_m16<GFM, GFN, MASKED, false>(acc, p.C, p.ldc, m0 + wr * S::TM,
-                                                    n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta, lane);
+                store_tile_m16_staged<GFM, GFN, S::TN, false, MASKED>(
+                    acc, p.C, p.ldc, m0 + wr * S::TM, n0 + wc * S::TN, p.M, p.N, p.alpha, p.beta,
+                    lane, mine, vec);
         }
         if constexpr (!SK) break;
         if (dp_item) ++r;
