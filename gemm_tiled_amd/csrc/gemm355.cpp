@@ -267,9 +267,17 @@ RingSk ring_sk(const TileConfig& c, int64_t M, int64_t N, int64_t K) {
     // a binary16 ring with 128 x 128 wave tiles has no stream-K form
     if (c.mode == GEMM355_MODE_F16R && (c.bm / c.wm) * (c.bn / c.wn) >= 128 * 128) return out;
     const int64_t dp = tiles / slots;
+    // A binary16 call with no whole round: its runs all start at different
+    // depths, so no two share operand panels in the cache and the call is
+    // bound by memory -- measured worse than the tiles alone once they fill a
+    // quarter of the slots (3072^3 on 256^2 tiles, 144 of 256 slots: 134 us
+    // against 88 us), better below (2048 x 2048 x 8192, 64 tiles: 131 against
+    // 172 us), and counted at twice its panels.
+    const bool f16_alone = c.mode == GEMM355_MODE_F16R && dp == 0;
+    if (f16_alone && tiles * 4 > slots) return out;
     const int64_t rest = (tiles - dp * slots) * nkt;
     const int64_t q = std::max<int64_t>((rest + slots - 1) / slots, kRingMinPanels);
-    const double panels = static_cast<double>(dp * nkt + q + kRingSkOverhead);
+    const double panels = static_cast<double>(dp * nkt + q + kRingSkOverhead) * (f16_alone ? 2 : 1);
     if (panels >= 0.95 * static_cast<double>(whole)) return out;
     const int64_t grid = dp > 0 ? slots : (rest + q - 1) / q;
     if (grid * 2 * c.bm * c.bn * 4 > kSplitKMaxBytes) return out;
@@ -297,6 +305,23 @@ double whole_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, RingRows
     const double kpad = static_cast<double>(round_up(K, c.bk));
     const double rounds = sk.q > 0 ? sk.panels / (kpad / c.bk) : std::ceil(tiles / (256.0 * per_cu));
     const double reuse = static_cast<double>(c.bm) * c.bn / (c.bm + c.bn);   // flop per loaded element
+    if (c.mode == GEMM355_MODE_F16R) {
+        // f16r: a CU's time is the tiles (or stream-K panels of its slots) it
+        // runs, whatever their number at once, over a reuse efficiency that
+        // falls much faster with the tile than in f32, the half-depth rings
+        // counted 1.2 times as efficient as the full-depth panels (measured
+        // at 1024 x 4096^2, 1536 x 4096^2, 2048^3, 2048^2 x 8192, 2560^3,
+        // 3072^3, 5120^3 and 6144^3: 128^2 rings against 256^2 tiles 1.2-1.6
+        // times less work per CU-microsecond, the ring at a tile 1.1-1.4
+        // times faster than the panels)
+        const double eff16 = reuse / (reuse + 85.0) * (is_f16_ring(c) ? 1.2 : 1.0);
+        double cu_tiles = std::ceil(tiles / 256.0);
+        if (sk.q > 0) {
+            const double lds = static_cast<double>(c.st) * (c.bm + c.bn) * 64;
+            cu_tiles = std::max(1.0, std::floor(160.0 * 1024 / lds)) * sk.panels / (kpad / c.bk);
+        }
+        return cu_tiles * c.bm * c.bn * kpad / eff16;
+    }
     const double eff =
         reuse / (reuse + 6.5) * (ring ? 1.2 * (whole ? 1.0 : kRingMaskedRate) : 1.0);
     return rounds * per_cu * c.bm * c.bn * kpad / eff;
