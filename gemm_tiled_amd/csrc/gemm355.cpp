@@ -267,14 +267,17 @@ RingSk ring_sk(const TileConfig& c, int64_t M, int64_t N, int64_t K) {
     // a binary16 ring with 128 x 128 wave tiles has no stream-K form
     if (c.mode == GEMM355_MODE_F16R && (c.bm / c.wm) * (c.bn / c.wn) >= 128 * 128) return out;
     const int64_t dp = tiles / slots;
-    // A binary16 call with no whole round: its runs all start at different
-    // depths, so no two share operand panels in the cache and the call is
-    // bound by memory -- measured worse than the tiles alone once they fill a
-    // quarter of the slots (3072^3 on 256^2 tiles, 144 of 256 slots: 134 us
-    // against 88 us), better below (2048 x 2048 x 8192, 64 tiles: 131 against
-    // 172 us), and counted at twice its panels.
+    // In binary16 the runs start at different depths, so no two share operand
+    // panels in the cache and that phase is bound by memory: measured worse
+    // than whole rounds once the tiles left after them fill more than a
+    // quarter of the slots (3072^3 on 256^2 tiles, 144 of 256 slots and no
+    // whole round: 134 us against 88 us; 5120^3, one round and 144 tiles
+    // left: 356 against 283 us), better below (2048 x 2048 x 8192, 64 tiles:
+    // 131 against 172 us; 6144^3, two rounds and 64 tiles left: 455 against
+    // 529 us on the 256^2 panels).  With no whole round the call is counted at
+    // twice its panels.
     const bool f16_alone = c.mode == GEMM355_MODE_F16R && dp == 0;
-    if (f16_alone && tiles * 4 > slots) return out;
+    if (c.mode == GEMM355_MODE_F16R && (tiles - dp * slots) * 4 > slots) return out;
     const int64_t rest = (tiles - dp * slots) * nkt;
     const int64_t q = std::max<int64_t>((rest + slots - 1) / slots, kRingMinPanels);
     const double panels = static_cast<double>(dp * nkt + q + kRingSkOverhead) * (f16_alone ? 2 : 1);
