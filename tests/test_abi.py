@@ -284,3 +284,39 @@ def test_plan_names_the_path_and_the_ring_block():
     assert g.get_plan("f16r", 8192, 8192, 8192).startswith("form=packed block=8192x8192x8192")
     with pytest.raises(g.Gemm355Error):
         g.get_plan("f32", -1, 4, 4)
+
+
+# The heuristic's choices where the configurations were timed against each
+# other on an MI355X (host only: no kernel runs).  Each row: mode, shape, the
+# configuration the measurements favour (prefix), and what was measured.
+HEURISTIC_PICKS = [
+    # f32 scored shapes: the 256^2 ring (the tuner's winner within 2%)
+    ("f32", (4096, 4096, 4096), "BM=256 BN=256 BK=16 ST=3 WM=2 WN=4"),
+    # f32 few rows: the few-rows configuration up to 16 rows, then the
+    # f32-panel ring (32 rows: 32 x 128, 20 us against 22 us split-K tiles;
+    # 128 rows: 64 x 64, 42 against 54 us; 256 rows: 64 x 128, 73 against 79)
+    ("f32", (16, 4096, 4096), "BM=16 BN=64 BK=64"),
+    ("f32", (32, 4096, 4096), "BM=32 BN=128 BK=32 ST=4"),
+    ("f32", (128, 4096, 4096), "BM=64 BN=64 BK=32 ST=4"),
+    ("f32", (256, 4096, 4096), "BM=64 BN=128 BK=32 ST=3"),
+    # f16r scored shape: the 256^2 half-depth ring
+    ("f16r", (8192, 8192, 8192), "BM=256 BN=256 BK=32 ST=5 WM=4 WN=2"),
+    # f16r few rows: the f32-panel ring rounding on load (64 rows: 32 x 64,
+    # 17.5 us against 24 us before it; 512 rows: 128 x 256, 38 against 54)
+    ("f16r", (64, 4096, 4096), "BM=32 BN=64 BK=32 ST=4"),
+    ("f16r", (512, 4096, 4096), "BM=128 BN=256 BK=32 ST=3"),
+    # f16r mid sizes on the packed path (the fastest of eight tiles timed,
+    # or within 5%): 128^2 ring 60 us at 1024 x 4096^2, 100 us at 2048^2 x
+    # 8192, 54 us at 2560^3; 256^2 ring without stream-K 84-88 us at 3072^3
+    ("f16r", (1024, 4096, 4096), "BM=128 BN=128 BK=32 ST=5 WM=2 WN=2"),
+    ("f16r", (2048, 2048, 8192), "BM=128 BN=128 BK=32 ST=5 WM=2 WN=2"),
+    ("f16r", (2560, 2560, 2560), "BM=128 BN=128 BK=32 ST=5 WM=2 WN=2"),
+    ("f16r", (3072, 3072, 3072), "BM=256 BN=256 BK=32 ST=5 WM=4 WN=2"),
+]
+
+
+@pytest.mark.parametrize("mode,shape,want", HEURISTIC_PICKS)
+def test_heuristic_picks_the_measured_best(mode, shape, want):
+    g.cache_clear()
+    got = g.get_config(mode, *shape, beta=0.0)
+    assert got.endswith("source=heuristic") and got.startswith(want), (mode, shape, got)
