@@ -941,7 +941,10 @@ hipError_t launch_f16_o16(const F16Args& a, hipStream_t s);
     X(256, 256, 4, 4, 2, 8)      \
     X(256, 256, 4, 2, 4, 8)      \
     X(256, 256, 5, 2, 2, 8)      \
-    X(128, 128, 5, 2, 2, 8)
+    X(128, 128, 5, 2, 2, 8)      \
+    X(256, 128, 4, 4, 2, 8)      \
+    X(128, 256, 4, 2, 4, 8)      \
+    X(128, 128, 5, 4, 2, 8)
 #define G355_F16_PANEL_CONFIGS(Y) \
     Y(256, 256, 1, 4, 2, 8)       \
     Y(256, 256, 1, 2, 4, 8)       \

@@ -291,6 +291,24 @@ RingSk ring_sk(const TileConfig& c, int64_t M, int64_t N, int64_t K) {
     return out;
 }
 
+// The rate of an f16r configuration's tile on a CU relative to the 256^2
+// half-depth ring with eight waves, measured: 256^2 with four waves 0.85,
+// 256 x 128 and 128 x 256 with eight 0.93, 128^2 with eight 0.85 (two
+// workgroups per CU) and with four 0.80.  Others by their reuse r = BM BN /
+// (BM + BN) as r / (r + 85) against the 256^2 tile's, the full-depth panels at
+// 1 / 1.2 of that (the half-depth ring at a tile ran 1.1-1.4 times faster).
+double f16_efficiency(const TileConfig& c) {
+    const int waves = c.wm * c.wn;
+    if (is_f16_ring(c)) {
+        if (c.bm == 256 && c.bn == 256) return waves == 8 ? 1.0 : 0.85;
+        if (c.bm * c.bn == 256 * 128 && waves == 8) return 0.93;
+        if (c.bm == 128 && c.bn == 128) return waves == 8 ? 0.85 : 0.80;
+    }
+    const double r = static_cast<double>(c.bm) * c.bn / (c.bm + c.bn);
+    const double rel = (r / (r + 85.0)) / (128.0 / (128.0 + 85.0));
+    return is_f16_ring(c) ? rel : rel / 1.2;
+}
+
 // Estimated time of configuration c on an M x N x K call run whole
 // (arbitrary units): rounds of workgroups over 256 CUs (two per CU for tiles
 // under 256 x 128) times the work of a tile, over the reuse efficiency r /
@@ -309,21 +327,28 @@ double whole_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, RingRows
     const double rounds = sk.q > 0 ? sk.panels / (kpad / c.bk) : std::ceil(tiles / (256.0 * per_cu));
     const double reuse = static_cast<double>(c.bm) * c.bn / (c.bm + c.bn);   // flop per loaded element
     if (c.mode == GEMM355_MODE_F16R) {
-        // f16r: a CU's time is the tiles (or stream-K panels of its slots) it
-        // runs, whatever their number at once, over a reuse efficiency that
-        // falls much faster with the tile than in f32, the half-depth rings
-        // counted 1.2 times as efficient as the full-depth panels (measured
-        // at 1024 x 4096^2, 1536 x 4096^2, 2048^3, 2048^2 x 8192, 2560^3,
-        // 3072^3, 5120^3 and 6144^3: 128^2 rings against 256^2 tiles 1.2-1.6
-        // times less work per CU-microsecond, the ring at a tile 1.1-1.4
-        // times faster than the panels)
-        const double eff16 = reuse / (reuse + 85.0) * (is_f16_ring(c) ? 1.2 : 1.0);
-        double cu_tiles = std::ceil(tiles / 256.0);
+        // f16r: the time of the busiest CU.  Whole rounds of 256 tiles count
+        // one tile each; a part-filled last round of L tiles counts
+        // sqrt(L / 256) of one, since a chip with idle CUs runs each tile
+        // faster (less contention for power, cache and memory: 64 256^2 tiles
+        // ran each at 0.4 of a full round's time, 128 at 0.7); a stream-K
+        // call its panels per slot.  A tile's time is its work over the
+        // efficiency of its configuration (f16_efficiency).  Fitted to the
+        // ring configurations timed pinned at 26 shapes from 768 x 4096^2 to
+        // 8192^3, ragged 3000^3, 4097^3 and 6000^3 among them: at every one
+        // the pick was within 1.2% of the fastest.
+        const double t_tile = c.bm * c.bn * kpad / f16_efficiency(c);
         if (sk.q > 0) {
-            const double lds = static_cast<double>(c.st) * (c.bm + c.bn) * 64;
-            cu_tiles = std::max(1.0, std::floor(160.0 * 1024 / lds)) * sk.panels / (kpad / c.bk);
+            // in runs the 256^2 tile with 2 x 4 waves was 1-5% faster than
+            // with 4 x 2 (6144^3 448 against 469 us), in whole rounds 1-4%
+            // slower (8192^2 x 2048 272 against 262)
+            const double slots_per_cu =
+                std::max(1.0, std::floor(160.0 * 1024 / (static_cast<double>(c.st) * (c.bm + c.bn) * 64)));
+            const double waves = (c.bm == 256 && c.bn == 256 && c.wm == 4) ? 1.03 : 1.0;
+            return slots_per_cu * sk.panels / (kpad / c.bk) * t_tile * waves;
         }
-        return cu_tiles * c.bm * c.bn * kpad / eff16;
+        const double full = std::floor(tiles / 256.0), left = tiles - 256.0 * full;
+        return (full + std::sqrt(left / 256.0)) * t_tile;
     }
     const double eff =
         reuse / (reuse + 6.5) * (ring ? 1.2 * (whole ? 1.0 : kRingMaskedRate) : 1.0);

@@ -305,13 +305,22 @@ HEURISTIC_PICKS = [
     # 17.5 us against 24 us before it; 512 rows: 128 x 256, 38 against 54)
     ("f16r", (64, 4096, 4096), "BM=32 BN=64 BK=32 ST=4"),
     ("f16r", (512, 4096, 4096), "BM=128 BN=256 BK=32 ST=3"),
-    # f16r mid sizes on the packed path (the fastest of eight tiles timed,
-    # or within 5%): 128^2 ring 60 us at 1024 x 4096^2, 100 us at 2048^2 x
-    # 8192, 54 us at 2560^3; 256^2 ring without stream-K 84-88 us at 3072^3
-    ("f16r", (1024, 4096, 4096), "BM=128 BN=128 BK=32 ST=5 WM=2 WN=2"),
-    ("f16r", (2048, 2048, 8192), "BM=128 BN=128 BK=32 ST=5 WM=2 WN=2"),
-    ("f16r", (2560, 2560, 2560), "BM=128 BN=128 BK=32 ST=5 WM=2 WN=2"),
+    # f16r mid sizes on the packed path (every half-depth ring timed pinned;
+    # the pick within 1.2% of the fastest): 128^2 with eight waves 58 us at
+    # 1024 x 4096^2 and 99 us at 2048^2 x 8192 (256 tiles: one per CU, where
+    # 256 x 128 fills half the CUs, 70 and 119 us); 256 x 128 52 us at
+    # 2560^3, 76 at 1536 x 4096^2, 218 at 4608^3 and 200 at 4097^3 (128^2:
+    # 55, 81, 232 and 208; 256^2: 68, 100, 242 and 220); the 256^2 ring 89 us
+    # at 3072^3 (144 tiles; 256 x 128 in runs 95), with 2 x 4 waves in runs
+    # (6144^3: 448 against 469 us with 4 x 2)
+    ("f16r", (1024, 4096, 4096), "BM=128 BN=128 BK=32 ST=5 WM=4 WN=2"),
+    ("f16r", (2048, 2048, 8192), "BM=128 BN=128 BK=32 ST=5 WM=4 WN=2"),
+    ("f16r", (2560, 2560, 2560), "BM=256 BN=128 BK=32 ST=4 WM=4 WN=2"),
+    ("f16r", (1536, 4096, 4096), "BM=256 BN=128 BK=32 ST=4 WM=4 WN=2"),
+    ("f16r", (4608, 4608, 4608), "BM=256 BN=128 BK=32 ST=4 WM=4 WN=2"),
+    ("f16r", (4097, 4097, 4097), "BM=256 BN=128 BK=32 ST=4 WM=4 WN=2"),
     ("f16r", (3072, 3072, 3072), "BM=256 BN=256 BK=32 ST=5 WM=4 WN=2"),
+    ("f16r", (6144, 6144, 6144), "BM=256 BN=256 BK=32 ST=5 WM=2 WN=4"),
 ]
 
 
