@@ -40,7 +40,9 @@ const char* mode_name(int mode) { return mode == GEMM355_MODE_F32 ? "f32" : "f16
 
 // Up to this many rows of C the heuristic picks the few-rows configuration,
 // then the f32-panel ring where it takes the shape (f16r: up to kRingRows, or
-// twice that when N x K is at most 2^22; f32: up to kPanelRowsF32), else in
+// twice that when N x K is at most 2^22; f32: up to kPanelRowsF32, or four
+// times that when N x K is at most 2^21: 1024^3 in 26 us against 29 us on the
+// best tile that does not split K), else in
 // the f16r mode the register-staged configuration that rounds on load up to
 // kDirectRows, and up to kSplitKRows the split-K configuration.
 constexpr int64_t kRowsRows = 16;
@@ -235,9 +237,17 @@ RingRows ring_rows(int trans, const float* A, int64_t lda, const float* B, int64
     if (trans != 0 || lda >= (int64_t{1} << 20) || ldb >= (int64_t{1} << 24)) return RingRows::None;
     return vec_ok(A, lda) && vec_ok(B, ldb) ? RingRows::Aligned : RingRows::Any;
 }
-// The masked ring's rate relative to the unmasked one (4-byte copies, rows
-// not 16-byte aligned): 4095^3 129 TFLOP/s against 145 for 4096^3.
-constexpr double kRingMaskedRate = 0.89;
+// The masked ring's rate relative to the unmasked one (4-byte copies, edge
+// tiles), with the reuse constant kReuseF32 of whole_cost and the strips'
+// efficiency kStripRate fitted to every f32 configuration timed pinned at 29
+// shapes from 512 x 4096^2 to 6144^3, 15 of them ragged (1000^3 to 6000^3,
+// 4000 x 4097 x 4093): the pick within 2.2% of the fastest at all but 1000^3
+// (4.6%) and 3500^3 (3.7%), and every timed configuration keeping its plan
+// (whole call, or block and strips); at 18 more shapes timed after the fit,
+// within 1% at 13 of them and 6.8% at worst (1000 x 8000 x 4000).
+constexpr double kRingMaskedRate = 0.93;
+constexpr double kReuseF32 = 10.0;
+constexpr double kStripRate = 0.95;
 
 bool is_f32_ring(const TileConfig& c) {
     return c.mode == GEMM355_MODE_F32 && c.bk == 16 && c.st >= 3 && c.ks == 0;
@@ -292,9 +302,10 @@ RingSk ring_sk(const TileConfig& c, int64_t M, int64_t N, int64_t K) {
 }
 
 // The rate of an f16r configuration's tile on a CU relative to the 256^2
-// half-depth ring with eight waves, measured: 256^2 with four waves 0.85,
-// 256 x 128 and 128 x 256 with eight 0.93, 128^2 with eight 0.85 (two
-// workgroups per CU) and with four 0.80.  Others by their reuse r = BM BN /
+// half-depth ring with eight waves, fitted (with the rest of the f16r cost
+// in whole_cost) to timings: 256^2 with four waves 0.85, 256 x 128 and
+// 128 x 256 with eight 0.93, 128^2 (two workgroups per CU) with four 0.86
+// and with eight 0.82.  Others by their reuse r = BM BN /
 // (BM + BN) as r / (r + 85) against the 256^2 tile's, the full-depth panels at
 // 1 / 1.2 of that (the half-depth ring at a tile ran 1.1-1.4 times faster).
 double f16_efficiency(const TileConfig& c) {
@@ -302,7 +313,7 @@ double f16_efficiency(const TileConfig& c) {
     if (is_f16_ring(c)) {
         if (c.bm == 256 && c.bn == 256) return waves == 8 ? 1.0 : 0.85;
         if (c.bm * c.bn == 256 * 128 && waves == 8) return 0.93;
-        if (c.bm == 128 && c.bn == 128) return waves == 8 ? 0.85 : 0.80;
+        if (c.bm == 128 && c.bn == 128) return waves == 8 ? 0.82 : 0.86;
     }
     const double r = static_cast<double>(c.bm) * c.bn / (c.bm + c.bn);
     const double rel = (r / (r + 85.0)) / (128.0 / (128.0 + 85.0));
@@ -312,7 +323,7 @@ double f16_efficiency(const TileConfig& c) {
 // Estimated time of configuration c on an M x N x K call run whole
 // (arbitrary units): rounds of workgroups over 256 CUs (two per CU for tiles
 // under 256 x 128) times the work of a tile, over the reuse efficiency r /
-// (r + 6.5) of the tile, r = BM BN / (BM + BN).  An f32 ring call deals its
+// (r + kReuseF32) of the tile, r = BM BN / (BM + BN).  An f32 ring call deals its
 // work in equal runs when whole rounds would leave CUs idle (stream-K,
 // counted by the panels of a slot plus the partial sums' overhead) and stages
 // its panels faster than the register-staged kernel (10-20% measured, counted
@@ -329,14 +340,16 @@ double whole_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, RingRows
     if (c.mode == GEMM355_MODE_F16R) {
         // f16r: the time of the busiest CU.  Whole rounds of 256 tiles count
         // one tile each; a part-filled last round of L tiles counts
-        // sqrt(L / 256) of one, since a chip with idle CUs runs each tile
+        // (L / 256)^0.4 of one, since a chip with idle CUs runs each tile
         // faster (less contention for power, cache and memory: 64 256^2 tiles
-        // ran each at 0.4 of a full round's time, 128 at 0.7); a stream-K
-        // call its panels per slot.  A tile's time is its work over the
+        // ran each at 0.4 of a full round's time, 128 at 0.7).  A stream-K
+        // call counts its panels per slot, the panels of the runs 2.5 times
+        // (runs at different depths share no operand panels in the cache, so
+        // that phase is bound by memory).  A tile's time is its work over the
         // efficiency of its configuration (f16_efficiency).  Fitted to the
-        // ring configurations timed pinned at 26 shapes from 768 x 4096^2 to
-        // 8192^3, ragged 3000^3, 4097^3 and 6000^3 among them: at every one
-        // the pick was within 1.2% of the fastest.
+        // ring configurations timed pinned at 43 shapes from 768 x 4096^2 to
+        // 8192^3, 15 of them ragged: the pick within 2.4% of the fastest at
+        // all but 2048^3 (3%) and 7000^3 (4.2%).
         const double t_tile = c.bm * c.bn * kpad / f16_efficiency(c);
         if (sk.q > 0) {
             // in runs the 256^2 tile with 2 x 4 waves was 1-5% faster than
@@ -345,13 +358,17 @@ double whole_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, RingRows
             const double slots_per_cu =
                 std::max(1.0, std::floor(160.0 * 1024 / (static_cast<double>(c.st) * (c.bm + c.bn) * 64)));
             const double waves = (c.bm == 256 && c.bn == 256 && c.wm == 4) ? 1.03 : 1.0;
-            return slots_per_cu * sk.panels / (kpad / c.bk) * t_tile * waves;
+            const double nkt = kpad / c.bk;
+            const double panels = (static_cast<double>(sk.dp) * nkt +
+                                   2.5 * static_cast<double>(sk.q + kRingSkOverhead)) *
+                                  (sk.dp == 0 ? 2.0 : 1.0);
+            return slots_per_cu * panels / nkt * t_tile * waves;
         }
         const double full = std::floor(tiles / 256.0), left = tiles - 256.0 * full;
-        return (full + std::sqrt(left / 256.0)) * t_tile;
+        return (full + std::pow(left / 256.0, 0.4)) * t_tile;
     }
     const double eff =
-        reuse / (reuse + 6.5) * (ring ? 1.2 * (whole ? 1.0 : kRingMaskedRate) : 1.0);
+        reuse / (reuse + kReuseF32) * (ring ? 1.2 * (whole ? 1.0 : kRingMaskedRate) : 1.0);
     return rounds * per_cu * c.bm * c.bn * kpad / eff;
 }
 
@@ -360,7 +377,7 @@ double whole_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, RingRows
 // of few columns is a long K loop per tile, so it needs K split), else the
 // register-staged 64 x 64 tile.  Its cost in the units of whole_cost: a thin
 // strip its share of the chip's rounds, a wide one whole rounds of 64 x 64
-// tiles.
+// tiles, at the efficiency kStripRate.
 TileConfig strip_config(int mode, int64_t rows, int64_t cols) {
     if (rows <= kRowsRows) return rows_config(mode);
     if (rows <= 128 || cols <= 128) return splitk_config(mode);
@@ -371,7 +388,7 @@ TileConfig strip_config(int mode, int64_t rows, int64_t cols) {
 double strip_cost(int64_t rows, int64_t cols, int64_t k) {
     const double tiles = static_cast<double>((rows + 63) / 64) * ((cols + 63) / 64);
     const double rounds = rows <= 128 || cols <= 128 ? tiles / 512.0 : std::ceil(tiles / 512.0);
-    return rounds * 2.0 * 64 * 64 * static_cast<double>(round_up(k, 16)) / (32.0 / 38.5);
+    return rounds * 2.0 * 64 * 64 * static_cast<double>(round_up(k, 16)) / kStripRate;
 }
 
 // The part of a ragged call that an f32 ring configuration runs itself: the
@@ -478,7 +495,9 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
     if (panels && mode == GEMM355_MODE_F16R &&
         (M <= kRingRows || (M <= 2 * kRingRows && N * K <= (int64_t{1} << 22))))
         return panel_ring_config(mode, M, N, K);
-    if (panels && mode == GEMM355_MODE_F32 && M <= kPanelRowsF32) return panel_ring_config(mode, M, N, K);
+    if (panels && mode == GEMM355_MODE_F32 &&
+        (M <= kPanelRowsF32 || (M <= 4 * kPanelRowsF32 && N * K <= (int64_t{1} << 21))))
+        return panel_ring_config(mode, M, N, K);
     if (mode == GEMM355_MODE_F16R && M <= kDirectRows) {
         // rounding on load: no packing pass, whose cost grows with N x K
         const int bm = M <= 48 ? 32 : M <= 160 ? 64 : 128;

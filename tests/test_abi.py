@@ -299,6 +299,14 @@ HEURISTIC_PICKS = [
     ("f32", (32, 4096, 4096), "BM=32 BN=128 BK=32 ST=4"),
     ("f32", (128, 4096, 4096), "BM=64 BN=64 BK=32 ST=4"),
     ("f32", (256, 4096, 4096), "BM=64 BN=128 BK=32 ST=3"),
+    # f32 mid sizes (every configuration timed pinned): the f32-panel ring
+    # at 1024^3 (26 us against 29 on the best tile that does not split K),
+    # the 128 x 256 ring at 2000^3 (154 us; the register-staged 128 x 64
+    # tile chosen before, 185), the masked 256^2 ring at 3000^3 (463 us;
+    # 128 x 256 on a block plus strips, chosen before, 511)
+    ("f32", (1024, 1024, 1024), "BM=64 BN=128 BK=32 ST=3 WM=2 WN=2 GM=8 KS=3"),
+    ("f32", (2000, 2000, 2000), "BM=128 BN=256 BK=16 ST=4 WM=2 WN=4"),
+    ("f32", (3000, 3000, 3000), "BM=256 BN=256 BK=16 ST=3 WM=2 WN=4"),
     # f16r scored shape: the 256^2 half-depth ring
     ("f16r", (8192, 8192, 8192), "BM=256 BN=256 BK=32 ST=5 WM=4 WN=2"),
     # f16r few rows: the f32-panel ring rounding on load (64 rows: 32 x 64,
@@ -306,21 +314,21 @@ HEURISTIC_PICKS = [
     ("f16r", (64, 4096, 4096), "BM=32 BN=64 BK=32 ST=4"),
     ("f16r", (512, 4096, 4096), "BM=128 BN=256 BK=32 ST=3"),
     # f16r mid sizes on the packed path (every half-depth ring timed pinned;
-    # the pick within 1.2% of the fastest): 128^2 with eight waves 58 us at
-    # 1024 x 4096^2 and 99 us at 2048^2 x 8192 (256 tiles: one per CU, where
-    # 256 x 128 fills half the CUs, 70 and 119 us); 256 x 128 52 us at
-    # 2560^3, 76 at 1536 x 4096^2, 218 at 4608^3 and 200 at 4097^3 (128^2:
-    # 55, 81, 232 and 208; 256^2: 68, 100, 242 and 220); the 256^2 ring 89 us
-    # at 3072^3 (144 tiles; 256 x 128 in runs 95), with 2 x 4 waves in runs
-    # (6144^3: 448 against 469 us with 4 x 2)
-    ("f16r", (1024, 4096, 4096), "BM=128 BN=128 BK=32 ST=5 WM=4 WN=2"),
-    ("f16r", (2048, 2048, 8192), "BM=128 BN=128 BK=32 ST=5 WM=4 WN=2"),
+    # the pick within 2.3% of the fastest): 128^2 60 us at 1024 x 4096^2,
+    # 100 at 2048^2 x 8192 and 194 at 4352^3 (256 x 128 70, 119 and 205);
+    # 256 x 128 52 us at 2560^3, 76 at 1536 x 4096^2, 219 at 4608^3, 200 at
+    # 4097^3 and 458 at 6144^3 (128^2: 55, 81, 232, 208, 465; 256^2: 68, 100,
+    # 242, 220, 448); the 256^2 ring 89 us at 3072^3 (144 tiles; 256 x 128 in
+    # runs 95)
+    ("f16r", (1024, 4096, 4096), "BM=128 BN=128 BK=32 ST=5 WM=2 WN=2"),
+    ("f16r", (2048, 2048, 8192), "BM=128 BN=128 BK=32 ST=5 WM=2 WN=2"),
+    ("f16r", (4352, 4352, 4352), "BM=128 BN=128 BK=32 ST=5 WM=2 WN=2"),
     ("f16r", (2560, 2560, 2560), "BM=256 BN=128 BK=32 ST=4 WM=4 WN=2"),
     ("f16r", (1536, 4096, 4096), "BM=256 BN=128 BK=32 ST=4 WM=4 WN=2"),
     ("f16r", (4608, 4608, 4608), "BM=256 BN=128 BK=32 ST=4 WM=4 WN=2"),
     ("f16r", (4097, 4097, 4097), "BM=256 BN=128 BK=32 ST=4 WM=4 WN=2"),
+    ("f16r", (6144, 6144, 6144), "BM=256 BN=128 BK=32 ST=4 WM=4 WN=2"),
     ("f16r", (3072, 3072, 3072), "BM=256 BN=256 BK=32 ST=5 WM=4 WN=2"),
-    ("f16r", (6144, 6144, 6144), "BM=256 BN=256 BK=32 ST=5 WM=2 WN=4"),
 ]
 
 
