@@ -91,6 +91,9 @@ def main():
     ap.add_argument("--precision", metavar="OUT_MD", default=None,
                     help="precision study (the lab's Part 4): f32, f16r and f16r with binary16 "
                          "output against float64 of the unrounded inputs; markdown to OUT_MD")
+    ap.add_argument("--choice", metavar="OUT_MD", default=None,
+                    help="the untuned choice against every configuration timed pinned, at "
+                         "square, few-row and ragged shapes of both modes; markdown to OUT_MD")
     ap.add_argument("--skinny", metavar="OUT_MD", default=None,
                     help="few-rows sweep (M = 1..2048 at K = N = 4096, both modes) against "
                          "the HBM and matrix-core roofs; markdown to OUT_MD")
@@ -138,6 +141,9 @@ def main():
         return
     if args.skinny:
         skinny_sweep(g, torch, dev, args.skinny, args.sweep_repeats)
+        return
+    if args.choice:
+        choice_study(g, torch, dev, args.choice, args.sweep_repeats)
         return
     if args.precision:
         precision_study(g, torch, dev, args.precision)
@@ -714,6 +720,120 @@ def shape_sweep(g, torch, dev, out, repeats):
                          f"{r['seconds_min'] * 1e3:.3f}..{r['seconds_max'] * 1e3:.3f} | "
                          f"{r['tile']} | {r['path']} |")
     lines += ["", "```json", json.dumps(rows), "```", ""]
+    _write(out, "\n".join(lines))
+
+
+# ---------------------------------------------------------------------------
+# The untuned choice (the phobos "gemm, f32" page, "Tuning": the best tile
+# depends on the card and the sizes).  At each shape every configuration the
+# heuristic weighs there is timed pinned -- in f32 every one that does not
+# split K for few rows, in f16r the half-depth rings -- and the library's own
+# choice without tuning is set beside the fastest.
+# ---------------------------------------------------------------------------
+CHOICE_SHAPES = {
+    "f32": [(n, n, n) for n in (1024, 1536, 1792, 2048, 2304, 2560, 2816, 3072, 3328, 3584,
+                                4096, 4608, 5120, 5632, 6144)] +
+           [(n, n, n) for n in (1000, 1500, 1800, 2000, 2049, 2300, 2500, 2800, 3000, 3300,
+                                3500, 4000, 4097, 4100, 4600, 5000, 5500, 6000, 7000)] +
+           [(512, 4096, 4096), (768, 4096, 4096), (1024, 4096, 4096), (1536, 4096, 4096),
+            (2048, 4096, 4096), (2048, 2048, 8192), (4096, 4096, 1024), (4000, 4097, 4093),
+            (3000, 5000, 2000), (1000, 8000, 4000), (768, 1024, 1024), (1024, 512, 2048),
+            (2000, 3000, 1000)],
+    "f16r": [(n, n, n) for n in (1792, 2048, 2304, 2560, 2816, 3072, 3328, 3584, 3840, 4096,
+                                 4352, 4608, 5120, 5632, 6144, 6656, 7168, 7680, 8192)] +
+            [(n, n, n) for n in (1800, 2300, 2800, 3000, 3300, 4097, 4600, 5500, 6000, 7000)] +
+            [(768, 4096, 4096), (1024, 4096, 4096), (1280, 4096, 4096), (1536, 4096, 4096),
+             (2048, 4096, 4096), (3072, 4096, 4096), (2048, 2048, 8192), (4096, 4096, 1024),
+             (8192, 8192, 2048), (4096, 8192, 4096), (1024, 8192, 8192), (3000, 5000, 2000),
+             (1000, 8000, 4000), (2000, 3000, 1000)],
+}
+
+
+def _choice_candidates(g, mode):
+    if mode == "f32":
+        return [c for c in g.list_configs(mode) if "KS=1" not in c and "KS=2" not in c]
+    return [c for c in g.list_configs(mode) if "BK=32" in c and "KS=" not in c]
+
+
+def choice_study(g, torch, dev, out, repeats):
+    import random
+
+    import oracle
+    from workloads import make_inputs, sample_indices
+
+    g.cache_clear()
+    rows = []
+    for mode in ("f32", "f16r"):
+        cands = _choice_candidates(g, mode)
+        for (M, N, K) in CHOICE_SHAPES[mode]:
+            A, B, C = make_inputs(M, N, K, "normal", seed=M + 3 * N + 7 * K)
+            r, c = sample_indices(M, N, 64, seed=3)
+            ref, W = oracle.entries(mode, A, B, C, 1.0, 0.0, r, c)
+            tA, tB, tC = (torch.from_numpy(x).to(dev) for x in (A, B, C))
+            del A, B, C
+            heur = g.get_config(mode, M, N, K, beta=0.0).split(" source=")[0]
+            plan = g.get_plan(mode, M, N, K, beta=0.0)
+            fn = g.gemm_f32 if mode == "f32" else g.gemm_f16r_f32acc
+            cfgs = list(dict.fromkeys(cands + [heur]))
+            calls, reps = {}, {}
+            for cfg in cfgs:
+                def call(fn=fn, cfg=cfg):
+                    g.set_config(mode, cfg)
+                    try:
+                        fn(tA, tB, tC, 1.0, 0.0)
+                    finally:
+                        g.set_config(mode, None)
+                call()
+                torch.cuda.synchronize()
+                got = tC[torch.as_tensor(r, device=dev), torch.as_tensor(c, device=dev)].cpu().numpy()
+                if not np.all(np.abs(got.astype(np.float64) - ref) <= oracle.TOL[mode] * W):
+                    raise SystemExit(f"choice {mode} {M}x{N}x{K} {cfg}: outside the parity bound")
+                calls[cfg] = call
+                t0 = median_call_time(call, torch, 0.02)
+                reps[cfg] = max(1, min(10, int(2e-4 / max(t0, 1e-6))))
+            times = {cfg: [] for cfg in cfgs}
+            rng = random.Random(M * N + K)
+            for _ in range(repeats):
+                order = list(cfgs)
+                rng.shuffle(order)
+                for cfg in order:
+                    times[cfg].append(median_call_time(calls[cfg], torch, 0.04, per_sample=reps[cfg]))
+            med = {cfg: float(np.median(v)) for cfg, v in times.items()}
+            best = min(med, key=med.get)
+            rows.append({"mode": mode, "M": M, "N": N, "K": K, "heuristic": heur, "plan": plan,
+                         "heuristic_s": med[heur], "best": best, "best_s": med[best],
+                         "ratio": med[heur] / med[best], "times": med})
+            log(f"choice: {mode} {M}x{N}x{K}: {heur} {med[heur] * 1e6:.1f} us, fastest {best} "
+                f"{med[best] * 1e6:.1f} us ({med[heur] / med[best]:.3f})")
+            del tA, tB, tC
+            torch.cuda.empty_cache()
+
+    lines = ["# The untuned choice against every configuration timed pinned (one MI355X)", "",
+             "Command:", "", "```", f"python bench.py --choice {out}", "```", "",
+             "A, B, C iid N(0,1), alpha = 1, beta = 0.  At each shape every candidate is checked "
+             "against the oracle on 64 sampled elements, then timed pinned: the median of "
+             f"{repeats} shuffled rounds, each the median of event-timed calls over 0.04 s after "
+             "warming the clocks (calls under 0.2 ms in batches).  Candidates: in f32 every "
+             "configuration that does not split K for few rows (the rings, the register-staged "
+             "tiles and the f32-panel ring), in f16r the half-depth rings.  `ratio` is the "
+             "untuned choice's time over the fastest candidate's.", ""]
+    for mode in ("f32", "f16r"):
+        sel = [r for r in rows if r["mode"] == mode]
+        ratios = [r["ratio"] for r in sel]
+        lines += [f"## {mode}", "",
+                  f"{len(sel)} shapes: the untuned choice within 2% of the fastest at "
+                  f"{sum(x <= 1.02 for x in ratios)}, within 5% at {sum(x <= 1.05 for x in ratios)}; "
+                  f"mean ratio {np.mean(ratios):.3f}, worst {max(ratios):.3f}.", "",
+                  "| M x N x K | untuned choice | plan | us | fastest pinned | us | ratio |",
+                  "|---|---|---|---:|---|---:|---:|"]
+        for r in sel:
+            lines.append(f"| {r['M']}x{r['N']}x{r['K']} | {r['heuristic']} | {r['plan']} | "
+                         f"{r['heuristic_s'] * 1e6:.1f} | {r['best']} | {r['best_s'] * 1e6:.1f} | "
+                         f"{r['ratio']:.3f} |")
+        lines.append("")
+    brief = [{k: (round(v * 1e6, 1) if k.endswith("_s") else v) for k, v in r.items()
+              if k != "times"} for r in rows]
+    lines += ["```json", json.dumps(brief), "```", ""]
     _write(out, "\n".join(lines))
 
 
