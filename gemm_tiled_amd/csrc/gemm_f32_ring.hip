@@ -47,7 +47,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const f32x4 lds_f32x4c;
 typedef __attribute__((address_space(3))) const float lds_f32c;
 
-template <int BM, int BN, int NS, int WM, int WN, bool MASKED>
+// NARROW: the masked copies of 4 bytes a lane (any shape and leading
+// dimension); otherwise copies of 16 bytes a lane (whole tiles, or masked ones
+// whose chunks of four lie wholly inside or outside the matrix).
+template <int BM, int BN, int NS, int WM, int WN, bool NARROW>
 struct F32RingShape {
     static constexpr int BK = 16;
     static constexpr int NW = WM * WN;
@@ -58,22 +61,25 @@ struct F32RingShape {
     static constexpr int STAGE = A_BYTES + BK * B_ROW;
     // copies per wave per panel: of 16 A rows and one B k-row (1 KB each), or
     // (masked) of 4 A rows and a quarter k-row (256 bytes each)
-    static constexpr int A_INS = MASKED ? BM / 4 / NW : BM / 16 / NW;
-    static constexpr int B_INS = MASKED ? 4 * BK / NW : BK / NW;
+    static constexpr int A_INS = NARROW ? BM / 4 / NW : BM / 16 / NW;
+    static constexpr int B_INS = NARROW ? 4 * BK / NW : BK / NW;
     static constexpr int FILLS = A_INS + B_INS;
     static_assert(BN == 256, "one k-row of B is 1 KB");
-    static_assert(A_INS >= 1 && A_INS * NW * (MASKED ? 4 : 16) == BM &&
-                      B_INS >= 1 && B_INS * NW == (MASKED ? 4 : 1) * BK,
+    static_assert(A_INS >= 1 && A_INS * NW * (NARROW ? 4 : 16) == BM &&
+                      B_INS >= 1 && B_INS * NW == (NARROW ? 4 : 1) * BK,
                   "copies split evenly over the waves");
-    static_assert(!MASKED || NW % 4 == 0, "masked copies: a wave's A swizzle and B quarter are fixed");
+    static_assert(!NARROW || NW % 4 == 0, "masked copies: a wave's A swizzle and B quarter are fixed");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(NS >= 3 && NS * STAGE <= 160 * 1024, "LDS budget of one CU");
     static_assert((NS - 2) * FILLS < 64, "vmcnt range");
 };
 
-template <int BM, int BN, int NS, int WM, int WN, int GM, bool SK, bool MASKED>
+// MASKED with WIDE: 16-byte masked copies (16-byte aligned rows, N and K
+// multiples of 4), which take a quarter of the 4-byte ones' instructions.
+template <int BM, int BN, int NS, int WM, int WN, int GM, bool SK, bool MASKED, bool WIDE = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) {
-    using S = F32RingShape<BM, BN, NS, WM, WN, MASKED>;
+    static_assert(!WIDE || MASKED, "16-byte masked copies are a masked form");
+    using S = F32RingShape<BM, BN, NS, WM, WN, MASKED && !WIDE>;
     constexpr int FM = S::FM, FN = S::FN;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * S::STAGE];
 
@@ -152,9 +158,34 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f32_ring_kernel(F32Args p) 
         const bool b_col_in = n0 + 64 * b_q + lane < p.N;
         const uint32_t b_voff = static_cast<uint32_t>(((int64_t)b_kr * p.ldb + 64 * b_q + lane) * 4);
         const uint32_t b_voff_step = static_cast<uint32_t>((int64_t)(S::NW / 4) * p.ldb * 4);
+        // 16-byte masked copies: the lanes and destinations of the unmasked
+        // copies, a lane outside the matrix (row >= M, k >= K or columns >= N;
+        // K and N multiples of 4, so a chunk is wholly in or out) reading zero.
+        const uint32_t a16_voff = static_cast<uint32_t>(((int64_t)(wave * 16 + arow) * p.lda + achunk * 4) * 4);
+        const uint32_t a16_step = static_cast<uint32_t>(a_step * 4);
+        const bool b16_col_in = n0 + 4 * lane < p.N;
+        const uint32_t b16_voff = static_cast<uint32_t>(((int64_t)wave * p.ldb + 4 * lane) * 4);
+        const uint32_t b16_step = static_cast<uint32_t>(b_step * 4);
         auto fill = [&](unsigned char* stage, int kt) __attribute__((always_inline)) {
             const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage));
-            if constexpr (MASKED) {
+            if constexpr (WIDE) {
+                const int kp = k_lo + kt * S::BK;
+                const i32x4_rsrc ra = copy_rsrc(p.A + (int64_t)m0 * p.lda + kp);
+                const bool a_k_in = kp + achunk * 4 < p.K;
+#pragma unroll
+                for (int j = 0; j < S::A_INS; ++j) {
+                    const bool in = a_k_in && m0 + wave * 16 + arow + S::NW * 16 * j < p.M;
+                    lds_copy16_masked(ra, in ? a16_voff + j * a16_step : kLdsCopyOut,
+                                      base + (wave + S::NW * j) * 1024);
+                }
+                const i32x4_rsrc rb = copy_rsrc(p.B + (int64_t)kp * p.ldb + n0);
+#pragma unroll
+                for (int j = 0; j < S::B_INS; ++j) {
+                    const bool in = b16_col_in && kp + wave + S::NW * j < p.K;
+                    lds_copy16_masked(rb, in ? b16_voff + j * b16_step : kLdsCopyOut,
+                                      base + S::A_BYTES + (wave + S::NW * j) * S::B_ROW);
+                }
+            } else if constexpr (MASKED) {
                 const int kp = k_lo + kt * S::BK;
                 const i32x4_rsrc ra = copy_rsrc(p.A + (int64_t)m0 * p.lda + kp);
                 const bool a_k_in = kp + a_kk < p.K;
@@ -378,16 +409,16 @@ bool f32_ring_takes(const TileConfig& cfg, const F32Args& a, const F32Variant& v
     return ring_whole(cfg.bm, cfg.bn, a, v) || ring_masked(cfg.bm, a, v);
 }
 
-template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED>
+template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED, bool WIDE = false>
 hipError_t launch_ring_form(const F32Args& a, hipStream_t s) {
     const dim3 block(WM * WN * 64);
     if (a.sk_q > 0) {
         const int grid = ring_sk_grid(int64_t{a.tiles_m} * a.tiles_n, (a.K + 15) / 16, a.sk_q,
                                       a.sk_dp, a.sk_grid, a.P, a.counts);
         if (grid <= 0) return hipErrorInvalidValue;
-        gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM, true, MASKED><<<dim3(grid), block, 0, s>>>(a);
+        gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM, true, MASKED, WIDE><<<dim3(grid), block, 0, s>>>(a);
     } else {
-        gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM, false, MASKED>
+        gemm_f32_ring_kernel<BM, BN, NS, WM, WN, GM, false, MASKED, WIDE>
             <<<dim3(static_cast<unsigned>(a.tiles_m * a.tiles_n)), block, 0, s>>>(a);
     }
     return hipGetLastError();
@@ -396,7 +427,12 @@ hipError_t launch_ring_form(const F32Args& a, hipStream_t s) {
 template <int BM, int BN, int NS, int WM, int WN, int GM>
 hipError_t launch_f32_ring(const F32Args& a, F32Variant v, hipStream_t s) {
     if (ring_whole(BM, BN, a, v)) return launch_ring_form<BM, BN, NS, WM, WN, GM, false>(a, s);
-    if (ring_masked(BM, a, v)) return launch_ring_form<BM, BN, NS, WM, WN, GM, true>(a, s);
+    if (ring_masked(BM, a, v)) {
+        // 16-byte chunks lie wholly inside or outside the matrix
+        if (v.vec && a.N % 4 == 0 && a.K % 4 == 0)
+            return launch_ring_form<BM, BN, NS, WM, WN, GM, true, true>(a, s);
+        return launch_ring_form<BM, BN, NS, WM, WN, GM, true>(a, s);
+    }
     if (v.ta || v.tb) return launch_f32_transposed<BM, BN, 16, 2, 2, GM>(a, v, s);
     return launch_f32_layout<BM, BN, 16, 2, 2, GM, false, false>(a, v, s);
 }

@@ -299,6 +299,12 @@ __device__ __forceinline__ void lds_copy4_masked(i32x4_rsrc rsrc, uint32_t voff,
     asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_base)
                  : "memory");
 }
+// The same with 16 bytes a lane (lane l to lds_base + 16 l): for operands whose
+// 16-byte chunks lie wholly inside or wholly outside the matrix.
+__device__ __forceinline__ void lds_copy16_masked(i32x4_rsrc rsrc, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_base)
+                 : "memory");
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const unsigned char* generic_lds_ptr) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)(generic_lds_ptr)));

@@ -675,6 +675,75 @@ def test_ring_masked_zero_fills_past_the_edges(cfg):
     assert np.array_equal(got, (exact - C.astype(np.float64)).astype(np.float32))
 
 
+# The masked f32 ring with 16-byte copies: 16-byte aligned rows (leading
+# dimensions multiples of 4) and N, K multiples of 4, so each lane's chunk of
+# four floats lies wholly inside or outside the matrix.  Every case checks that
+# the pinned ring runs the whole call masked with aligned rows (the plan).
+WIDE_CASES = [
+    (1000, 1000, 1000, {}),                                     # ragged M, N; K tail of 8
+    (1001, 1028, 1004, {}),                                     # odd M; K tail of 12
+    (700, 1020, 100, {"lda": 104, "ldb": 1024, "ldc": 1021}),   # padded lds, odd ldc
+    (4000, 4000, 4000, {}),                                     # stream-K over ragged tiles
+]
+
+
+@pytest.mark.parametrize("cfg", RINGS)
+@pytest.mark.parametrize("M,N,K,lds", WIDE_CASES)
+def test_ring_wide_masked_copies_against_the_oracle(cfg, M, N, K, lds):
+    A, B, C = make_inputs(M, N, K, "normal", seed=64, **lds)
+    with pinned("f32", cfg):
+        plan = g.get_plan("f32", M, N, K, beta=-0.5, **lds)
+        assert plan == f"form=ring-masked block={M}x{N}x{K}", plan
+        say(f"[ring wide masked] {cfg} {M}x{N}x{K} {lds}")
+        got = run("f32", A, B, C, 1.25, -0.5)
+        again = run("f32", A, B, C, 1.25, -0.5)
+    if M * N <= 2 ** 21:
+        assert_parity("f32", A, B, C, 1.25, -0.5, got)
+    else:
+        assert_sampled("f32", A, B, C, 1.25, -0.5, got)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+
+
+@pytest.mark.parametrize("cfg", RINGS[:1] + RINGS[-1:])
+def test_ring_wide_masked_zero_fills_past_the_edges(cfg):
+    """NaN in the padding of A's rows (k >= K), of B's rows (columns >= N) and
+    in the rows of B after K, with 16-byte copies: a chunk that read any of
+    them would put NaN into C.  Small integers, so the result is exact."""
+    M, N, K, lda, ldb = 1000, 1012, 332, 336, 1016
+    A, B, C = small_integers(M, N, K, seed=65)
+    fa = np.full((M, lda), np.nan, dtype=np.float32)
+    fa[:, :K] = A
+    fb = np.full((K + 40, ldb), np.nan, dtype=np.float32)
+    fb[:K, :N] = B
+    tA = torch.from_numpy(fa).to("cuda")[:, :K]
+    tB = torch.from_numpy(fb).to("cuda")[:K, :N]
+    tC = to_device(C)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned("f32", cfg):
+        plan = g.get_plan("f32", M, N, K, lda=lda, ldb=ldb, beta=-1.0)
+        assert plan == f"form=ring-masked block={M}x{N}x{K}", plan
+        say(f"[ring wide masked nan] {cfg} {M}x{N}x{K}")
+        g.gemm("f32", tA, tB, tC, 1.0, -1.0)
+        torch.cuda.synchronize()
+    got = tC.cpu().numpy()
+    assert np.array_equal(got, (exact - C.astype(np.float64)).astype(np.float32))
+
+
+@pytest.mark.parametrize("cfg", RINGS[:1] + RINGS[-1:])
+def test_ring_wide_masked_small_integers_exact_and_beta_zero(cfg):
+    M, N, K = 4000, 4092, 1004
+    A, B, C = small_integers(M, N, K, seed=66)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned("f32", cfg):
+        assert g.get_plan("f32", M, N, K, beta=0.5) == f"form=ring-masked block={M}x{N}x{K}"
+        say(f"[ring wide masked exact] {cfg} {M}x{N}x{K}")
+        got = run("f32", A, B, C, -2.0, 0.5)
+        assert np.array_equal(got, (-2.0 * exact + 0.5 * C.astype(np.float64)).astype(np.float32))
+        Cn = np.full((M, N), np.nan, dtype=np.float32)
+        got = run("f32", A, B, Cn, 1.0, 0.0)
+        assert np.array_equal(got, exact.astype(np.float32))
+
+
 @pytest.mark.parametrize("cfg", RINGS[:1] + RINGS[-1:])
 def test_ring_masked_small_integers_exact_and_beta_zero(cfg):
     M, N, K = 4000, 4097, 1001    # rows of B and C start 16-byte aligned every fourth row
