@@ -241,17 +241,16 @@ RingRows ring_rows(int trans, const float* A, int64_t lda, const float* B, int64
 // tiles), with the reuse constant kReuseF32 of whole_cost and the strips'
 // efficiency kStripRate fitted to every f32 configuration timed pinned at 29
 // shapes from 512 x 4096^2 to 6144^3, 15 of them ragged (1000^3 to 6000^3,
-// 4000 x 4097 x 4093): the pick within 2.2% of the fastest at all but 1000^3
-// (4.6%) and 3500^3 (3.7%), and every timed configuration keeping its plan
-// (whole call, or block and strips); at 18 more shapes timed after the fit,
-// within 1% at 13 of them and 6.8% at worst (1000 x 8000 x 4000).
+// 4000 x 4097 x 4093), so that every timed configuration kept its plan (whole
+// call, or block and strips) and the pick came within 2.2% of the fastest at
+// all but 1000^3 (4.6%) and 3500^3 (3.7%).
 constexpr double kRingMaskedRate = 0.93;
+constexpr double kReuseF32 = 10.0;
+constexpr double kStripRate = 0.95;
 // The masked ring with 16-byte copies (16-byte aligned rows, N and K multiples
 // of 4): 4088^3 in 951 us against 939 us for 4096^3, 2-3% below the unmasked
 // ring per flop (the 4-byte copies: 1019 us).
 constexpr double kRingWideRate = 0.98;
-constexpr double kReuseF32 = 10.0;
-constexpr double kStripRate = 0.95;
 
 bool is_f32_ring(const TileConfig& c) {
     return c.mode == GEMM355_MODE_F32 && c.bk == 16 && c.st >= 3 && c.ks == 0;
@@ -331,7 +330,8 @@ double f16_efficiency(const TileConfig& c) {
 // work in equal runs when whole rounds would leave CUs idle (stream-K,
 // counted by the panels of a slot plus the partial sums' overhead) and stages
 // its panels faster than the register-staged kernel (10-20% measured, counted
-// as 20%), the masked form at kRingMaskedRate of that.
+// as 20%), the masked form at kRingMaskedRate of that (kRingWideRate with
+// 16-byte copies).
 double whole_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, RingRows rows) {
     const bool ring = is_f32_ring(c) && rows != RingRows::None;
     const bool whole = rows == RingRows::Aligned && M % c.bm == 0 && N % c.bn == 0 && K % 16 == 0;
@@ -357,8 +357,9 @@ double whole_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, RingRows
         const double t_tile = c.bm * c.bn * kpad / f16_efficiency(c);
         if (sk.q > 0) {
             // in runs the 256^2 tile with 2 x 4 waves was 1-5% faster than
-            // with 4 x 2 (6144^3 448 against 469 us), in whole rounds 1-4%
-            // slower (8192^2 x 2048 272 against 262)
+            // with 4 x 2 (6144^3 448 against 469 us; the stream-K form of the
+            // 4 x 2 tile spills registers), in whole rounds 1-4% slower
+            // (8192^2 x 2048 272 against 262)
             const double slots_per_cu =
                 std::max(1.0, std::floor(160.0 * 1024 / (static_cast<double>(c.st) * (c.bm + c.bn) * 64)));
             const double waves = (c.bm == 256 && c.bn == 256 && c.wm == 4) ? 1.03 : 1.0;
