@@ -379,13 +379,14 @@ double whole_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, RingRows
 }
 
 // The configuration of a strip left over by a split ring call (RingBlock):
-// the few-rows one for up to 16 rows, split-K tiles for a thin strip (a strip
-// of few columns is a long K loop per tile, so it needs K split), else the
+// the few-rows one for up to 16 rows or (in its few-columns form) 16 columns,
+// split-K tiles for another thin strip (a strip of few columns is a long K
+// loop per tile, so it needs K split), else the
 // register-staged 64 x 64 tile.  Its cost in the units of whole_cost: a thin
 // strip its share of the chip's rounds, a wide one whole rounds of 64 x 64
 // tiles, at the efficiency kStripRate.
 TileConfig strip_config(int mode, int64_t rows, int64_t cols) {
-    if (rows <= kRowsRows) return rows_config(mode);
+    if (rows <= kRowsRows || cols <= kRowsRows) return rows_config(mode);
     if (rows <= 128 || cols <= 128) return splitk_config(mode);
     TileConfig edge;
     parse_config(mode, "BM=64 BN=64 BK=16 ST=2", &edge);
@@ -495,6 +496,11 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
     // a few rows of C (memory-bound, too few tiles): the few-rows
     // configuration up to one 16-row group, then the split-K tiles
     if (M <= kRowsRows) return rows_config(mode);
+    // a few columns of C: the same configuration on the transposed problem
+    // (f32 4096 x 16 x 4096 in 20 us against 81 us on the masked 128 x 256
+    // ring, 8192 x 1 x 8192 in 46 against 283 us; f16r 4096 x 16 x 4096 22
+    // against 54 us on the packed 64 x 64 tiles)
+    if (N <= kRowsRows) return rows_config(mode);
     // (from 512 rows on the packed path wins once N x K is large: 768 x 4096^2
     // 60 us packed against 79 us on the ring, 1024 x 8192^2 193 against 220)
     const bool panels = rows == RingRows::Aligned && N % 4 == 0 && K % 32 == 0;
@@ -760,15 +766,33 @@ int launch_splitk(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_
 // x slices reaches kRowsTarget workgroups, each slice a whole number of
 // rows_depth_unit() (every wave at least one 64-deep chunk), the partial
 // tiles within kSplitKMaxBytes.  Shapes whose B cannot be read 16 bytes at a
-// time take the split-K configuration instead.
+// time take the split-K configuration instead.  A call with few columns and
+// more rows (N <= kRowsRows < M) runs as the transposed problem C^T =
+// op(B)^T op(A)^T, whose few rows stream A, with C stored transposed: the
+// few-columns form.
 int launch_rows(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K, float alpha,
                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
                 int64_t ldc, hipStream_t s, uint16_t* C16, Scratch& sc) {
-    const bool ta = (trans & 1) != 0, tb = (trans & 2) != 0;
+    const bool ta_in = (trans & 1) != 0, tb_in = (trans & 2) != 0;
+    const bool tc = N <= kRowsRows && M > kRowsRows;
+    if (tc) {
+        // C^T (N x M) = op(B)^T (N x K) op(A)^T (K x M): op(B)^T is B read
+        // with the other layout flag, and likewise op(A)^T
+        std::swap(M, N);
+        std::swap(A, B);
+        std::swap(lda, ldb);
+    }
+    const bool ta = tc ? !tb_in : ta_in, tb = tc ? !ta_in : tb_in;
     if (!rows_supported(ta, tb, B, lda, ldb, static_cast<int>(M), static_cast<int>(N),
-                        static_cast<int>(K)))
+                        static_cast<int>(K))) {
+        if (tc) {
+            std::swap(M, N);
+            std::swap(A, B);
+            std::swap(lda, ldb);
+        }
         return launch_splitk(splitk_config(cfg.mode), trans, M, N, K, alpha, A, lda, B, ldb, beta,
                              C, ldc, s, C16, sc);
+    }
     // Slice depth: two 64-deep chunks per wave (one pass of the kernel) when
     // that gives at least one workgroup per CU, one chunk when the grid would
     // be smaller; deeper slices when there would be more than kRowsMaxWgs
@@ -785,9 +809,9 @@ int launch_rows(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
     const bool r16 = cfg.mode == GEMM355_MODE_F16R;
     if (log_debug() && !sc.dry())
         std::fprintf(stderr, "[gemm355] %s M=%lld N=%lld K=%lld %s path=rows x%lld (k %lld)%s\n",
-                     layout_name(cfg.mode, trans).c_str(), (long long)M, (long long)N,
-                     (long long)K, format_config(cfg).c_str(), (long long)slices,
-                     (long long)depth, C16 ? " f16-out" : "");
+                     layout_name(cfg.mode, trans).c_str(), (long long)(tc ? N : M),
+                     (long long)(tc ? M : N), (long long)K, format_config(cfg).c_str(),
+                     (long long)slices, (long long)depth, C16 ? " f16-out" : "");
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     float* P = nullptr;
     unsigned* counts = nullptr;
@@ -800,7 +824,7 @@ int launch_rows(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
         P = static_cast<float*>(ws);
     }
     if (sc.dry()) return 0;
-    return status_of(launch_f32_rows(A, lda, ta, B, ldb, tb, r16, C, C16, ldc, m, n, k, alpha,
+    return status_of(launch_f32_rows(A, lda, ta, B, ldb, tb, r16, C, C16, ldc, tc, m, n, k, alpha,
                                      beta, static_cast<int>(depth), static_cast<int>(slices), P,
                                      counts, s));
 }
@@ -1426,7 +1450,7 @@ int gemm355_get_plan_ex(int mode, int transa, int transb, int64_t M, int64_t N, 
     const bool vec = vec_ok(aligned, lda) && vec_ok(aligned, ldb);
     std::string form;
     if (cfg.ks == 1) form = "split-k";
-    else if (cfg.ks == 2) form = "rows";
+    else if (cfg.ks == 2) form = N <= kRowsRows && M > kRowsRows ? "columns" : "rows";
     else if (cfg.ks == 3) form = mode == GEMM355_MODE_F16R ? "round-on-load" : "panel-ring";
     else if (mode == GEMM355_MODE_F16R) form = (b.mb % cfg.bm || b.nb % cfg.bn) ? "packed-masked" : "packed";
     else if (is_f32_ring(cfg) && rows != RingRows::None)

@@ -50,6 +50,7 @@ struct RowsArgs {
     float alpha, beta;
     int depth;           // k per slice, a multiple of kWaves * kChunk
     int slices;
+    bool tc;             // C is stored transposed: element (row, col) at C[col * ldc + row]
 };
 
 __device__ __forceinline__ float rn16(float x) {
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_rows_kernel(RowsArgs p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (cc + j >= p.N) continue;
-            const int64_t at = (int64_t)row * p.ldc + cc + j;
+            const int64_t at = p.tc ? (int64_t)(cc + j) * p.ldc + row : (int64_t)row * p.ldc + cc + j;
             if (p.C16) {
                 const float old = p.beta == 0.f ? 0.f
                                                 : static_cast<float>(__builtin_bit_cast(_Float16, p.C16[at]));
@@ -419,19 +420,21 @@ bool rows_supported(bool ta, bool tb, const float* B, int64_t lda, int64_t ldb, 
     return aligned && (tb ? K % 4 == 0 : N % 4 == 0) && a_bytes < limit && b_bytes < limit;
 }
 
-// C (f32) or C16 (binary16) receives the result.  depth is the k per slice
+// C (f32) or C16 (binary16) receives the result (tc: stored transposed, the
+// few-columns form: the caller passes the transposed problem C^T = op(B)^T
+// op(A)^T).  depth is the k per slice
 // (a multiple of rows_depth_unit()); with slices > 1, P holds slices x M x NP
 // floats of partial tiles (NP = N rounded up to 4) and counts one zeroed
 // counter per workgroup column
 // (ceil(N/64) x row groups), which the kernel leaves zero again.
 hipError_t launch_f32_rows(const float* A, int64_t lda, bool ta, const float* B, int64_t ldb,
-                           bool tb, bool r16, float* C, uint16_t* C16, int64_t ldc, int M, int N,
-                           int K, float alpha, float beta, int depth, int slices, float* P,
+                           bool tb, bool r16, float* C, uint16_t* C16, int64_t ldc, bool tc, int M,
+                           int N, int K, float alpha, float beta, int depth, int slices, float* P,
                            unsigned* counts, hipStream_t s) {
     if (depth <= 0 || depth % rows_depth_unit() != 0) return hipErrorInvalidValue;
     if (!rows_supported(ta, tb, B, lda, ldb, M, N, K)) return hipErrorInvalidValue;
     if (slices > 1 && (!P || !counts)) return hipErrorInvalidValue;
-    const RowsArgs a{A, B, C, C16, P, counts, lda, ldb, ldc, M, N, K, alpha, beta, depth, slices};
+    const RowsArgs a{A, B, C, C16, P, counts, lda, ldb, ldc, M, N, K, alpha, beta, depth, slices, tc};
     const int group = rows_group(M);
     const dim3 grid((N + kCols - 1) / kCols, slices, (M + group - 1) / group);
     const bool tail = K % kChunk != 0;

@@ -163,9 +163,11 @@ int rows_group(int M);
 bool rows_supported(bool ta, bool tb, const float* B, int64_t lda, int64_t ldb, int M, int N,
                     int K);
 int rows_counters(int M, int N);
+// tc: C is stored transposed (the few-columns form, run as the few-rows one
+// on C^T = op(B)^T op(A)^T).
 hipError_t launch_f32_rows(const float* A, int64_t lda, bool ta, const float* B, int64_t ldb,
-                           bool tb, bool r16, float* C, uint16_t* C16, int64_t ldc, int M, int N,
-                           int K, float alpha, float beta, int depth, int slices, float* P,
+                           bool tb, bool r16, float* C, uint16_t* C16, int64_t ldc, bool tc, int M,
+                           int N, int K, float alpha, float beta, int depth, int slices, float* P,
                            unsigned* counts, hipStream_t s);
 
 // The configurations that round the operands to binary16 as they stage them

@@ -296,6 +296,10 @@ HEURISTIC_PICKS = [
     # f32-panel ring (32 rows: 32 x 128, 20 us against 22 us split-K tiles;
     # 128 rows: 64 x 64, 42 against 54 us; 256 rows: 64 x 128, 73 against 79)
     ("f32", (16, 4096, 4096), "BM=16 BN=64 BK=64"),
+    # few columns: the same configuration on the transposed problem (4096 x 16
+    # x 4096 in 20 us against 81 us on the 128 x 256 ring; f16r 22 against 54)
+    ("f32", (4096, 16, 4096), "BM=16 BN=64 BK=64"),
+    ("f16r", (4096, 1, 4096), "BM=16 BN=64 BK=64"),
     ("f32", (32, 4096, 4096), "BM=32 BN=128 BK=32 ST=4"),
     ("f32", (128, 4096, 4096), "BM=64 BN=64 BK=32 ST=4"),
     ("f32", (256, 4096, 4096), "BM=64 BN=128 BK=32 ST=3"),

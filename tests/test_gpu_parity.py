@@ -217,6 +217,78 @@ def test_rows_vector_form(mode, M, ta, tb, N):
     assert_parity(mode, A, B, C, -0.75, 0.5, tC.cpu().numpy())
 
 
+# The few-columns form of the same configuration: C with at most 16 columns
+# and more rows runs as C^T = op(B)^T op(A)^T on the few-rows kernel, which
+# then streams A, and stores C transposed.
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("M,N,K,lds", [
+    (4096, 1, 4096, {}),                            # one column (C^T: the vector form)
+    (4096, 16, 4096, {}),
+    (1000, 7, 1000, {}),                            # ragged M, odd N, K tail
+    (4100, 12, 1024, {"lda": 1028, "ldc": 13}),     # padded lda, ldc past N
+    (17, 16, 100, {}),                              # just past the few-rows sizes
+    (300, 3, 64, {"ldb": 5}),                       # odd ldb: B read element by element
+])
+def test_columns_against_the_oracle(mode, M, N, K, lds):
+    A, B, C = make_inputs(M, N, K, "normal", seed=20, **lds)
+    with pinned(mode, ROWS):
+        plan = g.get_plan(mode, M, N, K, beta=-0.5, **lds)
+        assert plan.startswith("form=columns"), plan
+        say(f"[columns] {mode} {M}x{N}x{K} {lds}")
+        got = run(mode, A, B, C, 1.25, -0.5)
+        again = run(mode, A, B, C, 1.25, -0.5)
+    assert_parity(mode, A, B, C, 1.25, -0.5, got)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))   # fixed slice order
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("N", [1, 2, 9, 16])
+def test_columns_small_integers_exact_and_beta_zero(mode, N):
+    M, K = 2048, 4096
+    A, B, C = small_integers(M, N, K, seed=21)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned(mode, ROWS):
+        say(f"[columns exact] {mode} {M}x{N}x{K}")
+        got = run(mode, A, B, C, -2.0, 0.5)
+        assert np.array_equal(got, (-2.0 * exact + 0.5 * C.astype(np.float64)).astype(np.float32))
+        Cn = np.full((M, N), np.nan, dtype=np.float32)
+        got = run(mode, A, B, Cn, 1.0, 0.0)
+        assert np.array_equal(got, exact.astype(np.float32))
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("ta,tb", [(True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("N", [1, 13])
+def test_columns_layouts(mode, ta, tb, N):
+    M, K = 2052, 1028
+    A, B, C = make_inputs(M, N, K, "uniform", seed=22)
+    tA = to_device(np.ascontiguousarray(A.T) if ta else A)
+    tB = to_device(np.ascontiguousarray(B.T) if tb else B)
+    tC = to_device(C)
+    with pinned(mode, ROWS):
+        say(f"[columns layout] {mode} ta={ta} tb={tb} {M}x{N}x{K}")
+        g.gemm(mode, tA, tB, tC, 0.5, 2.0, transa=ta, transb=tb)
+        torch.cuda.synchronize()
+    assert_parity(mode, A, B, C, 0.5, 2.0, tC.cpu().numpy())
+
+
+def test_columns_f16_output():
+    M, N, K = 2048, 12, 4096
+    A, B, C = make_inputs(M, N, K, "normal", seed=23)
+    C16 = C.astype(np.float16)
+    tA, tB = to_device(A), to_device(B)
+    t16 = torch.from_numpy(C16.copy()).to("cuda")
+    t32 = to_device(C16.astype(np.float32))
+    with pinned("f16r", ROWS):
+        say(f"[columns f16-out] {M}x{N}x{K}")
+        g.gemm_f16r_f16out(tA, tB, t16, 0.75, -0.25)
+        g.gemm("f16r", tA, tB, t32, 0.75, -0.25)
+        torch.cuda.synchronize()
+    want = t32.cpu().numpy().astype(np.float16)
+    got = t16.cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
 def test_rows_f16_output():
     M, N, K = 12, 2048, 4096
     A, B, C = make_inputs(M, N, K, "normal", seed=18)
