@@ -209,7 +209,8 @@ int gemm355_get_config_ex(int mode, int transa, int transb, int64_t M, int64_t N
  * whole tiles or in its zero-filling form), tiles / tiles-masked (the
  * register-staged f32 kernel), packed / packed-masked (the f16r packing pass
  * and binary16 kernel, masked stores at ragged edges), split-k, rows,
- * round-on-load.  The block is the part of C (MB x NB, over the first KB of
+ * columns (the few-rows configuration run on the transposed problem for a C
+ * of at most 16 columns), round-on-load, panel-ring.  The block is the part of C (MB x NB, over the first KB of
  * K) that configuration runs itself; when it is smaller than the call, the
  * right strip, the bottom strip and the k tail run in the few-rows, split-K
  * or 64 x 64 configurations.  Host only; no GPU call.  Returns as
@@ -225,7 +226,9 @@ int gemm355_get_plan_ex(int mode, int transa, int transb, int64_t M, int64_t N, 
  * BK|TILE_K, ST|STAGES, WM, WN, GM, KS|SPLITK; omitted keys take the first compiled
  * instance that matches the given ones, except KS, whose absence selects the
  * tiled configurations (KS=0).  KS=1: K split over workgroups, partial tiles
- * summed by a second pass; KS=2: one wavefront per few rows of C; KS=3: K
+ * summed by a second pass; KS=2: one wavefront per few rows of C (a C of at
+ * most 16 columns and more rows: per few columns, as the transposed problem
+ * with C stored transposed); KS=3: K
  * split over workgroups and the slices added in order by the tile's last
  * workgroup, the operands staged as f32 panels from a ring of direct-to-LDS
  * copies (BK=32, both modes; in f16r rounded to binary16 as the fragments
