@@ -94,6 +94,9 @@ def main():
     ap.add_argument("--choice", metavar="OUT_MD", default=None,
                     help="the untuned choice against every configuration timed pinned, at "
                          "square, few-row and ragged shapes of both modes; markdown to OUT_MD")
+    ap.add_argument("--thin", metavar="OUT_MD", default=None,
+                    help="few-columns sweep (N = 1..64 at M = K = 4096, both modes); markdown "
+                         "to OUT_MD")
     ap.add_argument("--skinny", metavar="OUT_MD", default=None,
                     help="few-rows sweep (M = 1..2048 at K = N = 4096, both modes) against "
                          "the HBM and matrix-core roofs; markdown to OUT_MD")
@@ -144,6 +147,9 @@ def main():
         return
     if args.choice:
         choice_study(g, torch, dev, args.choice, args.sweep_repeats)
+        return
+    if args.thin:
+        thin_sweep(g, torch, dev, args.thin, args.sweep_repeats)
         return
     if args.precision:
         precision_study(g, torch, dev, args.precision)
@@ -1032,6 +1038,116 @@ def skinny_sweep(g, torch, dev, out, repeats):
                      f"{r_['gbs']:.0f} | {r_['intensity']:.1f} | {r_['bound']} | "
                      f"{r_['frac_of_roof']:.2f} | {r_['tile']} |")
     lines += ["", "```json", json.dumps({"roofs": roofs, "rows": rows}), "```", ""]
+    _write(out, "\n".join(lines))
+
+
+THIN_N = [1, 2, 4, 8, 16, 32, 64]
+
+
+def thin_sweep(g, torch, dev, out, repeats):
+    """Few columns of C: N = 1 .. 64 at M = K = 4096.  The calls stream A
+    (64 MiB), so the bound is A's bytes over the HBM read roof; compared: the
+    library's tuned choice, the few-rows configuration pinned (for N <= 16 its
+    few-columns form, the transposed problem) and the fastest configuration of
+    any other kind."""
+    import random
+
+    import oracle
+    from workloads import make_inputs, sample_indices
+
+    roofs = measure_roofs(g, torch, dev, 1.0)
+    M = K = 4096
+    A = make_inputs(M, 1, K, "normal", seed=4097)[0]
+    tA = torch.from_numpy(A).to(dev)
+    calls, tiles, plans = {}, {}, {}
+    for N in THIN_N:
+        B = make_inputs(1, N, K, "normal", seed=N)[1]
+        C = make_inputs(M, N, 1, "normal", seed=N + 1)[2]
+        r, c = sample_indices(M, N, 256, seed=3)
+        tB, tC = torch.from_numpy(B).to(dev), torch.from_numpy(C).to(dev)
+        for mode in ("f32", "f16r"):
+            ref, W = oracle.entries(mode, A, B, C, 1.0, 0.0, r, c)
+            fn = g.gemm_f32 if mode == "f32" else g.gemm_f16r_f32acc
+            for kind in ("tuned", "rows", "other"):
+                key = (mode, N, kind)
+                if kind == "tuned":
+                    g.tune(mode, tA, tB, tC, beta=0.0)
+                    cfg = g.get_config(mode, M, N, K, beta=0.0).split(" source=")[0]
+                    pin = None
+                elif kind == "rows":
+                    cfg = pin = g.parse_config(mode, "KS=2")
+                else:
+                    best, best_t = None, 1e30
+                    for cand in g.list_configs(mode):
+                        if "KS=2" in cand:
+                            continue
+                        g.set_config(mode, cand)
+                        try:
+                            t = median_call_time(lambda fn=fn, tB=tB, tC=tC: fn(tA, tB, tC, 1.0, 0.0),
+                                                 torch, 0.05, per_sample=SKINNY_BATCH)
+                        finally:
+                            g.set_config(mode, None)
+                        if t < best_t:
+                            best, best_t = cand, t
+                    cfg = pin = best
+
+                def call(fn=fn, tB=tB, tC=tC, mode=mode, pin=pin):
+                    if pin:
+                        g.set_config(mode, pin)
+                    try:
+                        fn(tA, tB, tC, 1.0, 0.0)
+                    finally:
+                        if pin:
+                            g.set_config(mode, None)
+                call()
+                torch.cuda.synchronize()
+                got = tC[torch.as_tensor(r, device=dev), torch.as_tensor(c, device=dev)].cpu().numpy()
+                if not np.all(np.abs(got.astype(np.float64) - ref) <= oracle.TOL[mode] * W):
+                    raise SystemExit(f"thin {key}: outside the parity bound")
+                if pin:
+                    g.set_config(mode, pin)
+                try:
+                    plans[key] = g.get_plan(mode, M, N, K, beta=0.0).split()[0].split("=")[1]
+                finally:
+                    if pin:
+                        g.set_config(mode, None)
+                calls[key], tiles[key] = call, cfg
+                log(f"thin: {mode} N={N} {kind}: {cfg} ({plans[key]})")
+    times = {k: [] for k in calls}
+    rng = random.Random(2)
+    for rnd in range(repeats):
+        order = list(calls)
+        rng.shuffle(order)
+        for k in order:
+            times[k].append(median_call_time(calls[k], torch, 0.2, per_sample=SKINNY_BATCH))
+        log(f"thin: round {rnd + 1} of {repeats} done")
+    hbm = roofs["hbm_read_gbs"] * 1e9
+    rows = []
+    for (mode, N, kind), ts in times.items():
+        t = float(np.median(ts))
+        nbytes = 4.0 * (M * K + K * N + M * N)
+        rows.append({"mode": mode, "N": N, "kind": kind, "tile": tiles[(mode, N, kind)],
+                     "path": plans[(mode, N, kind)], "seconds": t, "gbs": nbytes / t / 1e9,
+                     "frac_of_hbm_roof": nbytes / t / hbm})
+    lines = ["# Few columns of C: N = 1 .. 64 at M = K = 4096 (both modes, one MI355X)", "",
+             "Command:", "", "```", f"python bench.py --thin {out}", "```", "",
+             "A (M x K), B (K x N), C iid N(0,1); alpha = 1, beta = 0.  Every case is checked "
+             "against the oracle on 256 sampled elements before it is timed; the time is the "
+             f"median of {repeats} shuffled rounds of event-timed samples (0.2 s), each sample "
+             f"{SKINNY_BATCH} back-to-back calls between two events.  Bytes are the f32 storage "
+             "the call must move at least once, 4(MK + KN + MN), against the measured HBM read "
+             f"roof {roofs['hbm_read_gbs']:.0f} GB/s.  `tuned` is the library's own choice after "
+             "tuning, `rows` the few-rows configuration pinned (KS=2: for N <= 16 its "
+             "few-columns form, the transposed problem C^T = B^T A^T, streaming A), `other` the "
+             "fastest configuration of any other kind.", "",
+             "| mode | N | choice | us | GB/s | of HBM roof | path | tile |",
+             "|---|---:|---|---:|---:|---:|---|---|"]
+    for r_ in sorted(rows, key=lambda r_: (r_["mode"], r_["N"], r_["kind"])):
+        lines.append(f"| {r_['mode']} | {r_['N']} | {r_['kind']} | {r_['seconds'] * 1e6:.1f} | "
+                     f"{r_['gbs']:.0f} | {r_['frac_of_hbm_roof']:.2f} | {r_['path']} | "
+                     f"{r_['tile']} |")
+    lines += ["", "```json", json.dumps({"hbm_read_gbs": roofs["hbm_read_gbs"], "rows": rows}),
+              "```", ""]
     _write(out, "\n".join(lines))
 
 
