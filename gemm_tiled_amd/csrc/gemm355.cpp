@@ -496,14 +496,30 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
     // a few rows of C (memory-bound, too few tiles): the few-rows
     // configuration up to one 16-row group, then the split-K tiles
     if (M <= kRowsRows) return rows_config(mode);
-    // a few columns of C: the same configuration on the transposed problem
-    // (f32 4096 x 16 x 4096 in 20 us against 81 us on the masked 128 x 256
-    // ring, 8192 x 1 x 8192 in 46 against 283 us; f16r 4096 x 16 x 4096 22
-    // against 54 us on the packed 64 x 64 tiles)
+    const bool panels = rows == RingRows::Aligned && N % 4 == 0 && K % 32 == 0;
+    // A few columns of C (measured at M = K = 4096): in f32 the same
+    // configuration on the transposed problem up to 16 columns (4096 x 16 x
+    // 4096 in 20 us against 81 us on the masked 128 x 256 ring, 8192 x 1 x
+    // 8192 in 46 against 283 us), then up to 64 columns the f32-panel ring on
+    // 64 x 64 tiles (26 us); in f16r the transposed few-rows form for one or
+    // two columns (18.5 us against 19.6) and from 4 to 64 columns the
+    // f32-panel ring on 32 x 64 tiles (16 us against 21 on the transposed
+    // form, 54 on the packed 64 x 64 tiles).
+    if (N <= 64 && M >= 4 * N) {
+        TileConfig thin;
+        if (panels && mode == GEMM355_MODE_F16R && N >= 4 &&
+            parse_config(mode, "BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 GM=8 KS=3", &thin))
+            return thin;
+        if (N <= kRowsRows) return rows_config(mode);
+        if (panels && parse_config(mode, mode == GEMM355_MODE_F32
+                                             ? "BM=64 BN=64 BK=32 ST=4 WM=4 WN=1 GM=8 KS=3"
+                                             : "BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 GM=8 KS=3",
+                                   &thin))
+            return thin;
+    }
     if (N <= kRowsRows) return rows_config(mode);
     // (from 512 rows on the packed path wins once N x K is large: 768 x 4096^2
     // 60 us packed against 79 us on the ring, 1024 x 8192^2 193 against 220)
-    const bool panels = rows == RingRows::Aligned && N % 4 == 0 && K % 32 == 0;
     if (panels && mode == GEMM355_MODE_F16R &&
         (M <= kRingRows || (M <= 2 * kRingRows && N * K <= (int64_t{1} << 22))))
         return panel_ring_config(mode, M, N, K);

@@ -296,10 +296,16 @@ HEURISTIC_PICKS = [
     # f32-panel ring (32 rows: 32 x 128, 20 us against 22 us split-K tiles;
     # 128 rows: 64 x 64, 42 against 54 us; 256 rows: 64 x 128, 73 against 79)
     ("f32", (16, 4096, 4096), "BM=16 BN=64 BK=64"),
-    # few columns: the same configuration on the transposed problem (4096 x 16
-    # x 4096 in 20 us against 81 us on the 128 x 256 ring; f16r 22 against 54)
+    # few columns (M = K = 4096): f32 the same configuration on the
+    # transposed problem up to 16 columns (4096 x 16 x 4096 in 20 us against
+    # 81 us on the 128 x 256 ring), then the f32-panel ring on 64 x 64 tiles
+    # (26 us at 64 columns); f16r the transposed form for one or two columns
+    # (18.5 us), the f32-panel ring on 32 x 64 tiles from 4 (16 us against 21)
     ("f32", (4096, 16, 4096), "BM=16 BN=64 BK=64"),
+    ("f32", (4096, 64, 4096), "BM=64 BN=64 BK=32 ST=4 WM=4 WN=1 GM=8 KS=3"),
     ("f16r", (4096, 1, 4096), "BM=16 BN=64 BK=64"),
+    ("f16r", (4096, 16, 4096), "BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 GM=8 KS=3"),
+    ("f16r", (4096, 64, 4096), "BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 GM=8 KS=3"),
     ("f32", (32, 4096, 4096), "BM=32 BN=128 BK=32 ST=4"),
     ("f32", (128, 4096, 4096), "BM=64 BN=64 BK=32 ST=4"),
     ("f32", (256, 4096, 4096), "BM=64 BN=128 BK=32 ST=3"),
