@@ -281,6 +281,11 @@ def test_plan_names_the_path_and_the_ring_block():
     finally:
         g.set_config("f32", None)
     assert g.get_plan("f32", 8, 4096, 4096) == "form=rows block=8x4096x4096"
+    # a few columns: the few-rows configuration on the transposed problem
+    assert g.get_plan("f32", 4096, 8, 4096) == "form=columns block=4096x8x4096"
+    assert g.get_plan("f16r", 4096, 1, 4096) == "form=columns block=4096x1x4096 rows=4-byte"
+    # 16-byte rows with N and K multiples of 4: the masked ring whole (16-byte copies)
+    assert g.get_plan("f32", 4000, 4000, 4000) == "form=ring-masked block=4000x4000x4000"
     assert g.get_plan("f16r", 8192, 8192, 8192).startswith("form=packed block=8192x8192x8192")
     with pytest.raises(g.Gemm355Error):
         g.get_plan("f32", -1, 4, 4)
