@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import make_inputs
+from workloads import make_inputs, sample_indices
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -78,3 +78,48 @@ def test_random_shape_against_the_oracle(mode, i, case):
     Cref = np.zeros((M, N), dtype=np.float32) if beta == 0.0 else C
     st = oracle.check(mode, A, B, Cref, alpha, beta, got)
     assert st["n_fail"] == 0, (case, plan, st)
+
+
+def _large_cases(n, seed):
+    """Larger shapes, where the rings, their stream-K and masked forms, the
+    f32-panel ring and the packed path run: each dimension uniform in
+    200..3000, a multiple of 4 half the time (16-byte rows with the matrix
+    width as leading dimension), otherwise padded by 0..3."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dims = []
+        for _ in range(3):
+            d = int(rng.integers(200, 3001))
+            dims.append(d - d % 4 if rng.random() < 0.5 else d)
+        pads = [int(rng.choice([0, 0, 1, 3])) for _ in range(3)]
+        beta = float(rng.choice([0.0, 1.0, -0.25]))
+        out.append((*dims, pads, beta))
+    return out
+
+
+LARGE = [(mode, i, c) for mode, seed in (("f32", 201), ("f16r", 202))
+         for i, c in enumerate(_large_cases(30, seed))]
+
+
+@pytest.mark.parametrize("mode,i,case", LARGE, ids=[f"{m}-{i}" for m, i, _ in LARGE])
+def test_random_large_shape_sampled(mode, i, case):
+    """The last row and column in full, plus sampled elements, against the
+    oracle (the full product is too long for the float64 oracle here)."""
+    M, N, K, pads, beta = case
+    A, B, C = make_inputs(M, N, K, "normal", seed=2000 + i,
+                          lda=K + pads[0], ldb=N + pads[1], ldc=N + pads[2])
+    Cin = np.full_like(C, np.nan) if beta == 0.0 else C
+    plan = g.get_plan(mode, M, N, K, lda=K + pads[0], ldb=N + pads[1], ldc=N + pads[2], beta=beta)
+    say(f"[random large] {mode} #{i} {M}x{N}x{K} pads={pads} beta={beta} {plan}")
+    tA, tB, tC = to_device(A), to_device(B), to_device(Cin)
+    g.gemm(mode, tA, tB, tC, 0.75, beta)
+    torch.cuda.synchronize()
+    got = tC.cpu().numpy()
+    Cref = np.zeros_like(C) if beta == 0.0 else C
+    r = np.concatenate([np.full(N, M - 1), np.arange(M), sample_indices(M, N, 2048, seed=i)[0]])
+    c = np.concatenate([np.arange(N), np.full(M, N - 1), sample_indices(M, N, 2048, seed=i)[1]])
+    ref, W = oracle.entries(mode, A, B, Cref, 0.75, beta, r, c)
+    err = np.abs(got[r, c].astype(np.float64) - ref)
+    bad = ~(err <= oracle.TOL[mode] * W)
+    assert not bad.any(), (case, plan, int(bad.sum()), r[bad][:5], c[bad][:5])
