@@ -1193,7 +1193,8 @@ COPY_BYTES = 256 << 20          # one direction of the calibration copy
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "f32": ["gemm_tiled_amd/csrc/gemm_f32.hip", "gemm_tiled_amd/csrc/gemm_f32_ring.hip",
-            "gemm_tiled_amd/csrc/f32_kernel.hpp", "gemm_tiled_amd/csrc/internal.hpp"],
+            "gemm_tiled_amd/csrc/f32_ring.hpp", "gemm_tiled_amd/csrc/f32_kernel.hpp",
+            "gemm_tiled_amd/csrc/internal.hpp"],
     "f16r": ["gemm_tiled_amd/csrc/gemm_f16r.hip", "gemm_tiled_amd/csrc/f16_kernel.hpp",
              "gemm_tiled_amd/csrc/internal.hpp"],
 }

@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libgemm355.so")
 BUILD = os.path.join(ROOT, "_build", "gemm355")
 
-SOURCES = ["gemm_f32.hip", "gemm_f32_t.hip", "gemm_f32_ring.hip", "gemm_splitk.hip", "gemm_rows.hip", "gemm_f16r.hip",
+SOURCES = ["gemm_f32.hip", "gemm_f32_t.hip", "gemm_f32_ring.hip", "gemm_f32_ring_tn.hip", "gemm_f32_ring_nt.hip",
+           "gemm_f32_ring_tt.hip", "gemm_splitk.hip", "gemm_rows.hip", "gemm_f16r.hip",
            "gemm_f16r_o16.hip", "gemm_f16r_direct.hip", "gemm_panel_ring.hip", "aux_kernels.hip", "gemm355.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -40,9 +40,9 @@ namespace g355 {
     X(64, 64, 16, 2, 2, 8)    \
     X(64, 64, 32, 2, 2, 8)
 
-// The direct-to-LDS ring (gemm_f32_ring.hip): X(BM, BN, NS, WM, WN, GM),
-// BK = 16, NS stages; whole tiles of the plain layout only (other calls with
-// these tiles run the register-staged kernel).
+// The direct-to-LDS ring (f32_ring.hpp): X(BM, BN, NS, WM, WN, GM), BK = 16,
+// NS stages, every operand layout (split-K slices and leading dimensions past
+// its copies' offsets run the register-staged kernel with these tiles).
 #define G355_F32_RING_CONFIGS(X) \
     X(256, 256, 3, 2, 4, 8)      \
     X(256, 256, 4, 2, 4, 8)      \

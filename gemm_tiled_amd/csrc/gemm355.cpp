@@ -228,14 +228,24 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // kRingSkOverhead panels for the split tiles' partial sums.  Runs that start
 // at different depths of their tiles share no operand panels in the cache,
 // which is why the remaining tiles alone are dealt this way.
-// What the f32 ring can take of a call: nothing (transposed operands, or
-// leading dimensions too large for the masked copies' 32-bit offsets), any
-// shape through its masked form, or also whole tiles unmasked (16-byte
-// aligned rows).
-enum class RingRows { None, Any, Aligned };
+// What the f32 ring can take of a call: nothing (leading dimensions too large
+// for the masked copies' 32-bit offsets: up to 256 stored rows of a panel of
+// an operand whose k runs along its rows, 16 of one whose k runs down them),
+// any shape through its masked form, or also whole tiles unmasked (16-byte
+// aligned rows); and the operand layouts (bit 0 op(A) = A^T, bit 1 op(B) =
+// B^T).
+struct RingRows {
+    enum Kind { None, Any, Aligned };
+    Kind kind = None;
+    int trans = 0;
+    bool none() const { return kind == None; }
+    bool aligned() const { return kind == Aligned; }
+};
 RingRows ring_rows(int trans, const float* A, int64_t lda, const float* B, int64_t ldb) {
-    if (trans != 0 || lda >= (int64_t{1} << 20) || ldb >= (int64_t{1} << 24)) return RingRows::None;
-    return vec_ok(A, lda) && vec_ok(B, ldb) ? RingRows::Aligned : RingRows::Any;
+    const int64_t a_lim = (trans & 1) ? int64_t{1} << 24 : int64_t{1} << 20;
+    const int64_t b_lim = (trans & 2) ? int64_t{1} << 20 : int64_t{1} << 24;
+    if (lda >= a_lim || ldb >= b_lim) return RingRows{RingRows::None, trans};
+    return RingRows{vec_ok(A, lda) && vec_ok(B, ldb) ? RingRows::Aligned : RingRows::Any, trans};
 }
 // The masked ring's rate relative to the unmasked one (4-byte copies, edge
 // tiles), with the reuse constant kReuseF32 of whole_cost and the strips'
@@ -333,8 +343,8 @@ double f16_efficiency(const TileConfig& c) {
 // as 20%), the masked form at kRingMaskedRate of that (kRingWideRate with
 // 16-byte copies).
 double whole_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, RingRows rows) {
-    const bool ring = is_f32_ring(c) && rows != RingRows::None;
-    const bool whole = rows == RingRows::Aligned && M % c.bm == 0 && N % c.bn == 0 && K % 16 == 0;
+    const bool ring = is_f32_ring(c) && !rows.none();
+    const bool whole = rows.aligned() && M % c.bm == 0 && N % c.bn == 0 && K % 16 == 0;
     const double tiles = static_cast<double>((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
     const double per_cu = (c.bm * c.bn >= 256 * 128) ? 1.0 : 2.0;
     const RingSk sk = ring || is_f16_ring(c) ? ring_sk(c, M, N, K) : RingSk{};
@@ -372,7 +382,10 @@ double whole_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, RingRows
         const double full = std::floor(tiles / 256.0), left = tiles - 256.0 * full;
         return (full + std::pow(left / 256.0, 0.4)) * t_tile;
     }
-    const bool wide = rows == RingRows::Aligned && N % 4 == 0 && K % 4 == 0;
+    // 16-byte masked copies: along each operand's contiguous dimension a
+    // multiple of 4 elements
+    const int64_t a_run = (rows.trans & 1) ? M : K, b_run = (rows.trans & 2) ? K : N;
+    const bool wide = rows.aligned() && a_run % 4 == 0 && b_run % 4 == 0;
     const double eff = reuse / (reuse + kReuseF32) *
                        (ring ? 1.2 * (whole ? 1.0 : wide ? kRingWideRate : kRingMaskedRate) : 1.0);
     return rounds * per_cu * c.bm * c.bn * kpad / eff;
@@ -413,7 +426,8 @@ struct RingBlock {
 };
 RingBlock ring_block(const TileConfig& c, RingRows rows, int64_t M, int64_t N, int64_t K) {
     RingBlock best{M, N, K, whole_cost(c, M, N, K, rows)};
-    if (!is_f32_ring(c) || rows == RingRows::None) return best;
+    // (the block and strips address the operands as stored: plain layout only)
+    if (!is_f32_ring(c) || rows.none() || rows.trans != 0) return best;
     const int64_t M0 = M / c.bm * c.bm, N0 = N / c.bn * c.bn, K16 = K / 16 * 16;
     auto consider = [&](int64_t mb, int64_t nb, int64_t kb) {
         if (mb <= 0 || nb <= 0 || kb <= 0 || (mb == M && nb == N && kb == K)) return;
@@ -426,7 +440,7 @@ RingBlock ring_block(const TileConfig& c, RingRows rows, int64_t M, int64_t N, i
     consider(M0, N, K);
     consider(M, N0, K);
     consider(M0, N0, K);
-    if (rows == RingRows::Aligned) consider(M0, N0, K16);
+    if (rows.aligned()) consider(M0, N0, K16);
     return best;
 }
 
@@ -496,7 +510,7 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
     // a few rows of C (memory-bound, too few tiles): the few-rows
     // configuration up to one 16-row group, then the split-K tiles
     if (M <= kRowsRows) return rows_config(mode);
-    const bool panels = rows == RingRows::Aligned && N % 4 == 0 && K % 32 == 0;
+    const bool panels = rows.aligned() && rows.trans == 0 && N % 4 == 0 && K % 32 == 0;
     // A few columns of C (measured at M = K = 4096): in f32 the same
     // configuration on the transposed problem up to 16 columns (4096 x 16 x
     // 4096 in 20 us against 81 us on the masked 128 x 256 ring, 8192 x 1 x
@@ -1469,8 +1483,8 @@ int gemm355_get_plan_ex(int mode, int transa, int transb, int64_t M, int64_t N, 
     else if (cfg.ks == 2) form = N <= kRowsRows && M > kRowsRows ? "columns" : "rows";
     else if (cfg.ks == 3) form = mode == GEMM355_MODE_F16R ? "round-on-load" : "panel-ring";
     else if (mode == GEMM355_MODE_F16R) form = (b.mb % cfg.bm || b.nb % cfg.bn) ? "packed-masked" : "packed";
-    else if (is_f32_ring(cfg) && rows != RingRows::None)
-        form = rows == RingRows::Aligned && b.mb % cfg.bm == 0 && b.nb % cfg.bn == 0 && b.kb % 16 == 0
+    else if (is_f32_ring(cfg) && !rows.none())
+        form = rows.aligned() && b.mb % cfg.bm == 0 && b.nb % cfg.bn == 0 && b.kb % 16 == 0
                    ? "ring" : "ring-masked";
     else form = (!vec || M % cfg.bm || N % cfg.bn || K % cfg.bk) ? "tiles-masked" : "tiles";
     const std::string out = "form=" + form + " block=" + std::to_string(b.mb) + "x" +

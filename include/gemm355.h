@@ -205,16 +205,16 @@ int gemm355_get_config_ex(int mode, int transa, int transb, int64_t M, int64_t N
  * aligned) would run, written into buf as "form=F block=MBxNBxKB" plus
  * " rows=4-byte" when a leading dimension keeps rows from being 16-byte
  * aligned.  F names the kernel path of the configuration gemm355_get_config_ex
- * reports: ring / ring-masked (the f32 ring of direct-to-LDS panel copies, on
- * whole tiles or in its zero-filling form), tiles / tiles-masked (the
+ * reports: ring / ring-masked (the f32 ring of direct-to-LDS panel copies, in
+ * every operand layout, on whole tiles or in its zero-filling form), tiles / tiles-masked (the
  * register-staged f32 kernel), packed / packed-masked (the f16r packing pass
  * and binary16 kernel, masked stores at ragged edges), split-k, rows,
  * columns (the few-rows configuration run on the transposed problem for a C
  * of at most 16 columns), round-on-load, panel-ring.  The block is the part
  * of C (MB x NB, over the first KB of K) that configuration runs itself; when
- * it is smaller than the call, the right strip, the bottom strip and the k
- * tail run in the few-rows (or few-columns), split-K or 64 x 64
- * configurations.  Host only; no GPU call.  Returns as
+ * it is smaller than the call (the f32 ring, plain layout only), the right
+ * strip, the bottom strip and the k tail run in the few-rows (or
+ * few-columns), split-K or 64 x 64 configurations.  Host only; no GPU call.  Returns as
  * gemm355_get_config_ex.
  */
 int gemm355_get_plan_ex(int mode, int transa, int transb, int64_t M, int64_t N, int64_t K,

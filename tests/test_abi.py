@@ -276,8 +276,21 @@ def test_plan_names_the_path_and_the_ring_block():
         assert plan == "form=ring-masked block=4000x4096x4093 rows=4-byte", plan
         assert g.get_plan("f32", 300, 517, 333, lda=335, ldb=519, ldc=521) == \
             "form=ring-masked block=300x517x333 rows=4-byte"
-        # transposed operands: the register-staged kernel of the same tile
-        assert g.get_plan("f32", 4096, 4096, 4096, transa=True).startswith("form=tiles")
+        # transposed operands: the ring too, copying each panel along the
+        # stored rows, and whole (the block and strips take the plain layout
+        # only); leading dimensions past its copies' 32-bit offsets (256
+        # stored rows of B^T, 16 of A^T) run the register-staged kernel
+        assert g.get_plan("f32", 4096, 4096, 4096, transa=True) == "form=ring block=4096x4096x4096"
+        assert g.get_plan("f32", 4100, 4100, 4100, transb=True) == \
+            "form=ring-masked block=4100x4100x4100"
+        assert g.get_plan("f32", 300, 517, 333, lda=301, ldb=335, transa=True, transb=True) == \
+            "form=ring-masked block=300x517x333 rows=4-byte"
+        assert g.get_plan("f32", 256, 512, 16, ldb=(1 << 20) + 4, transb=True) == \
+            "form=tiles block=256x512x16"
+        assert g.get_plan("f32", 256, 512, 16, lda=(1 << 20) + 4, transa=True) == \
+            "form=ring block=256x512x16"
+        assert g.get_plan("f32", 256, 512, 16, lda=(1 << 24) + 4, transa=True) == \
+            "form=tiles block=256x512x16"
     finally:
         g.set_config("f32", None)
     assert g.get_plan("f32", 8, 4096, 4096) == "form=rows block=8x4096x4096"

@@ -119,3 +119,98 @@ def test_layout_tuner_keys_the_layout(mode):
     assert g.get_config(mode, M, N, K, beta=0.5, transa=True).endswith("source=tuned")
     got = run_ex(mode, A, B, C, 1.0, 0.5, True, False)
     check(mode, A, B, C, 1.0, 0.5, got)
+
+
+# ---------------------------------------------------------------------------
+# The f32 ring of direct-to-LDS copies in the transposed layouts: a transposed
+# operand's panels are copied along its stored rows (k-rows of A^T; rows of
+# B^T, along which k runs), in every ring configuration and form -- whole tiles
+# in whole rounds or dealt to the CUs in runs (stream-K), the 16-byte masked
+# copies (16-byte aligned rows, each operand's contiguous extent a multiple of
+# 4) and the 4-byte ones.  The plan must name the ring for the whole call.
+# ---------------------------------------------------------------------------
+RINGS = [c for c in g.list_configs("f32") if "BK=16" in c and int(c.split("ST=")[1].split()[0]) >= 3]
+RING_CASES = [
+    (1024, 1024, 1024, 0, "ring"),          # whole tiles; few tiles: runs of panels
+    (4096, 4096, 64, 0, "ring"),            # whole tiles in whole rounds
+    (1000, 1004, 1008, 0, "ring-masked"),   # 16-byte masked copies
+    (300, 517, 333, 3, "ring-masked"),      # odd leading dimensions: 4-byte copies
+    (513, 2049, 1100, 1, "ring-masked"),    # runs over ragged tiles
+    (1, 1, 1, 0, "ring-masked"),            # one element
+    (33, 300, 7, 0, "ring-masked"),         # K shorter than a panel
+]
+
+
+def _lds(M, N, K, ta, tb, pad):
+    return ((M if ta else K) + pad if pad else None), ((K if tb else N) + pad if pad else None)
+
+
+@pytest.mark.parametrize("cfg", RINGS)
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[_name(*x) for x in LAYOUTS])
+@pytest.mark.parametrize("M,N,K,pad,form", RING_CASES)
+def test_ring_layouts_against_the_oracle(cfg, ta, tb, M, N, K, pad, form):
+    A, B, C = make_inputs(M, N, K, "normal", seed=71)
+    lda, ldb = _lds(M, N, K, ta, tb, pad)
+    with pinned("f32", cfg):
+        plan = g.get_plan("f32", M, N, K, lda=lda, ldb=ldb, beta=-0.5, transa=ta, transb=tb)
+        assert plan.startswith(f"form={form} block={M}x{N}x{K}"), plan
+        say(f"[ring layout] {_name(ta, tb)} {cfg} {M}x{N}x{K} lda={lda} ldb={ldb}")
+        got = run_ex("f32", A, B, C, 1.25, -0.5, ta, tb, lda, ldb)
+        again = run_ex("f32", A, B, C, 1.25, -0.5, ta, tb, lda, ldb)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+    if M * N <= 2 ** 21:
+        check("f32", A, B, C, 1.25, -0.5, got)
+    else:
+        check("f32", A, B, C, 1.25, -0.5, got, rows=(0, 48))
+        check("f32", A, B, C, 1.25, -0.5, got, rows=(M - 48, M))
+        r, c = sample_indices(M, N, 2048, seed=2)
+        ref, W = oracle.entries("f32", np.ascontiguousarray(A), np.ascontiguousarray(B), C, 1.25,
+                                -0.5, r, c)
+        assert np.all(np.abs(got[r, c].astype(np.float64) - ref) <= oracle.TOL["f32"] * W)
+
+
+def _nan_padded(op, t, ld, extra=40):
+    """op stored as itself or transposed, in a NaN-filled buffer with a padded
+    leading dimension and extra NaN rows after it; the view of the stored
+    array."""
+    st = op.T if t else op
+    buf = np.full((st.shape[0] + extra, ld), np.nan, dtype=np.float32)
+    buf[:st.shape[0], :st.shape[1]] = st
+    return torch.from_numpy(buf).to("cuda")[:st.shape[0], :st.shape[1]]
+
+
+@pytest.mark.parametrize("cfg", RINGS[:1] + RINGS[-1:])
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[_name(*x) for x in LAYOUTS])
+@pytest.mark.parametrize("M,N,K,pad", [(1000, 1012, 332, 4), (301, 517, 333, 3)])
+def test_ring_layouts_zero_fill_past_the_edges(cfg, ta, tb, M, N, K, pad):
+    """NaN in the padding of every stored row and in the rows after each
+    stored array: a masked copy (16-byte ones for the first shape, 4-byte ones
+    for the second) that read any of them would put NaN into C.  Small
+    integers, so the result is exact."""
+    A, B, C = small_integers(M, N, K, seed=72)
+    lda, ldb = _lds(M, N, K, ta, tb, pad)
+    tA, tB, tC = _nan_padded(A, ta, lda), _nan_padded(B, tb, ldb), to_device(C)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned("f32", cfg):
+        plan = g.get_plan("f32", M, N, K, lda=lda, ldb=ldb, beta=-1.0, transa=ta, transb=tb)
+        assert plan.startswith(f"form=ring-masked block={M}x{N}x{K}"), plan
+        say(f"[ring layout nan] {_name(ta, tb)} {cfg} {M}x{N}x{K}")
+        g.gemm("f32", tA, tB, tC, 1.0, -1.0, transa=ta, transb=tb)
+        torch.cuda.synchronize()
+    got = tC.cpu().numpy()
+    assert np.array_equal(got, (exact - C.astype(np.float64)).astype(np.float32))
+
+
+@pytest.mark.parametrize("cfg", RINGS[:1] + RINGS[-1:])
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[_name(*x) for x in LAYOUTS])
+@pytest.mark.parametrize("M,N,K", [(2048, 1024, 1024), (4000, 4092, 1004)])
+def test_ring_layouts_small_integers_exact_and_beta_zero(cfg, ta, tb, M, N, K):
+    A, B, C = small_integers(M, N, K, seed=73)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned("f32", cfg):
+        say(f"[ring layout exact] {_name(ta, tb)} {cfg} {M}x{N}x{K}")
+        got = run_ex("f32", A, B, C, -2.0, 0.5, ta, tb)
+        assert np.array_equal(got, (-2.0 * exact + 0.5 * C.astype(np.float64)).astype(np.float32))
+        Cn = np.full((M, N), np.nan, dtype=np.float32)
+        got = run_ex("f32", A, B, Cn, 1.0, 0.0, ta, tb)
+        assert np.array_equal(got, exact.astype(np.float32))
