@@ -725,16 +725,20 @@ def shape_sweep(g, torch, dev, out, repeats):
             lines.append(f"| {r['mode']} | {r['n']} | {r['tflops']:.1f} | "
                          f"{r['seconds_min'] * 1e3:.3f}..{r['seconds_max'] * 1e3:.3f} | "
                          f"{r['tile']} | {r['path']} |")
-    # operand layouts at the scored sizes: op(A) = A^T and/or op(B) = B^T,
-    # stored transposed, against the plain layout, the library's own choice
+    # operand layouts at the scored sizes and for few rows of C (K = N = 4096):
+    # op(A) = A^T and/or op(B) = B^T, stored transposed, against the plain
+    # layout, the library's own choice
     lay = []
-    for mode, n in (("f32", 4096), ("f16r", 8192)):
-        A, B, C = make_inputs(n, n, n, "normal", seed=n + 7)
-        r, c = sample_indices(n, n, 256, seed=4)
+    layout_shapes = [("f32", 4096, 4096, 4096), ("f16r", 8192, 8192, 8192)] + [
+        (mode, m, 4096, 4096) for mode in ("f32", "f16r") for m in (16, 128, 512)]
+    for mode, M, N, K in layout_shapes:
+        A, B, C = make_inputs(M, N, K, "normal", seed=M + 7)
+        r, c = sample_indices(M, N, 256, seed=4)
         ref, W = oracle.entries(mode, A, B, C, 1.0, 0.0, r, c)
         tA, tB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
         tAt, tBt = tA.t().contiguous(), tB.t().contiguous()
         tC = torch.from_numpy(C).to(dev)
+        batch = 1 if M * N * K >= 2 ** 36 else SKINNY_BATCH
         for ta, tb in ((False, False), (True, False), (False, True), (True, True)):
             def call(mode=mode, ta=ta, tb=tb, a=tAt if ta else tA, b=tBt if tb else tB, cc=tC):
                 g.gemm(mode, a, b, cc, 1.0, 0.0, transa=ta, transb=tb)
@@ -742,22 +746,30 @@ def shape_sweep(g, torch, dev, out, repeats):
             torch.cuda.synchronize()
             got = tC[torch.as_tensor(r, device=dev), torch.as_tensor(c, device=dev)].cpu().numpy()
             if not np.all(np.abs(got.astype(np.float64) - ref) <= oracle.TOL[mode] * W):
-                raise SystemExit(f"sweep layouts {mode} {n} ta={ta} tb={tb}: outside the parity bound")
-            t = float(np.median([median_call_time(call, torch, 0.3) for _ in range(repeats)]))
-            plan = g.get_plan(mode, n, n, n, beta=0.0, transa=ta, transb=tb).split()[0].split("=")[1]
-            lay.append({"mode": mode, "n": n, "ta": ta, "tb": tb, "seconds": t,
-                        "tflops": 2.0 * n ** 3 / t / 1e12, "path": plan})
-            log(f"sweep: layout {mode} {n} ta={ta} tb={tb}: {t * 1e3:.3f} ms ({plan})")
+                raise SystemExit(f"sweep layouts {mode} {M}x{N}x{K} ta={ta} tb={tb}: outside the "
+                                 "parity bound")
+            t = float(np.median([median_call_time(call, torch, 0.3, per_sample=batch)
+                                 for _ in range(repeats)]))
+            plan = g.get_plan(mode, M, N, K, beta=0.0, transa=ta, transb=tb).split()[0].split("=")[1]
+            tile = g.get_config(mode, M, N, K, beta=0.0, transa=ta, transb=tb).split(" source=")[0]
+            lay.append({"mode": mode, "M": M, "N": N, "K": K, "ta": ta, "tb": tb, "seconds": t,
+                        "tflops": 2.0 * M * N * K / t / 1e12, "path": plan, "tile": tile})
+            log(f"sweep: layout {mode} {M}x{N}x{K} ta={ta} tb={tb}: {t * 1e6:.1f} us ({plan})")
         del tA, tB, tAt, tBt, tC
         torch.cuda.empty_cache()
     lines += ["", "## Operand layouts (the library's own choice; op(X) = X^T stored transposed)", "",
-              "| mode | n | layout | ms | TFLOP/s | against NN | path |", "|---|---:|---|---:|---:|---:|---|"]
+              "Few-row calls are timed in samples of " + str(SKINNY_BATCH) + " back-to-back calls "
+              "(GPU time per call in a stream of calls).", "",
+              "| mode | M x N x K | layout | us | TFLOP/s | against NN | path | tile |",
+              "|---|---|---|---:|---:|---:|---|---|"]
     for r_ in lay:
-        nn = next(x for x in lay if x["mode"] == r_["mode"] and not x["ta"] and not x["tb"])
+        nn = next(x for x in lay if x["mode"] == r_["mode"] and x["M"] == r_["M"] and
+                  x["N"] == r_["N"] and not x["ta"] and not x["tb"])
         name = ("T" if r_["ta"] else "N") + ("T" if r_["tb"] else "N")
-        lines.append(f"| {r_['mode']} | {r_['n']} | {name} | {r_['seconds'] * 1e3:.3f} | "
-                     f"{r_['tflops']:.1f} | {100 * (r_['seconds'] / nn['seconds'] - 1):+.1f}% | "
-                     f"{r_['path']} |")
+        lines.append(f"| {r_['mode']} | {r_['M']}x{r_['N']}x{r_['K']} | {name} | "
+                     f"{r_['seconds'] * 1e6:.1f} | {r_['tflops']:.1f} | "
+                     f"{100 * (r_['seconds'] / nn['seconds'] - 1):+.1f}% | {r_['path']} | "
+                     f"{r_['tile']} |")
     lines += ["", "```json", json.dumps({"shapes": rows, "layouts": lay}), "```", ""]
     _write(out, "\n".join(lines))
 

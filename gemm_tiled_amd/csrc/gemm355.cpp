@@ -510,7 +510,10 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
     // a few rows of C (memory-bound, too few tiles): the few-rows
     // configuration up to one 16-row group, then the split-K tiles
     if (M <= kRowsRows) return rows_config(mode);
-    const bool panels = rows.aligned() && rows.trans == 0 && N % 4 == 0 && K % 32 == 0;
+    // (the f32-panel ring: 16-byte aligned rows, K % 32 == 0, and a multiple
+    // of 4 along B's rows as stored K x N and along A's as stored K x M)
+    const bool panels = rows.aligned() && K % 32 == 0 && ((rows.trans & 2) || N % 4 == 0) &&
+                        (!(rows.trans & 1) || M % 4 == 0);
     // A few columns of C (measured at M = K = 4096): in f32 the same
     // configuration on the transposed problem up to 16 columns (4096 x 16 x
     // 4096 in 20 us against 81 us on the masked 128 x 256 ring, 8192 x 1 x
@@ -869,7 +872,7 @@ int launch_direct(const TileConfig& cfg_in, int trans, int64_t M, int64_t N, int
     // the f32-panel ring (BK = 32) hands the shapes it does not take to the
     // register-staged kernel of the 64 x 64 tile (f16r) or to the split-K
     // tiles (f32)
-    if (cfg.bk == 32 && !panel_ring_takes(ta, tb, A, lda, B, ldb, N, K)) {
+    if (cfg.bk == 32 && !panel_ring_takes(ta, tb, A, lda, B, ldb, M, N, K)) {
         if (cfg.mode == GEMM355_MODE_F32)
             return launch_splitk(splitk_config(cfg.mode), trans, M, N, K, alpha, A, lda, B, ldb,
                                  beta, C, ldc, s, C16, sc);

@@ -13,11 +13,13 @@
 // staging of the other KS=3 kernel both fall short of it there, in f32 the
 // split-K tiles (KS=1: partial tiles summed by a second pass).
 //
-// Shapes: the plain layout with 16-byte aligned rows, N % 4 == 0 and
-// K % 32 == 0 (M and N need not be tile multiples: copies of rows past M read
-// row M - 1 and of columns past N column n0, values that only reach outputs
-// the masked epilogue never stores).  K is split over blockIdx.y, the last
-// workgroup of a tile adding the slices' partial tiles in slice order.
+// Shapes: every operand layout with 16-byte aligned rows and K % 32 == 0;
+// N % 4 == 0 where B is stored K x N and M % 4 == 0 where A is stored K x M
+// (M and N need not be tile multiples: copies of rows past M or N read the
+// last row, and of columns past them the tile's first column, values that
+// only reach outputs the masked epilogue never stores).  K is split over
+// blockIdx.y, the last workgroup of a tile adding the slices' partial tiles
+// in slice order.
 #include "f16_kernel.hpp"
 
 // X(BM, BN, NS, WM, WN, GM): the compiled configurations of each mode.
@@ -41,6 +43,7 @@ namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const f32x4v lds_f32x4c;
+typedef __attribute__((address_space(3))) const float lds_f32c;
 
 // A K slice of a split call: the workgroup stores its partial tile in P
 // (slices x tiles x TILE_BYTES; within a tile, wave-major, block-major, lane
@@ -101,47 +104,81 @@ __device__ __forceinline__ bool last_slice_adds(f32x4v (&acc)[GFM][GFN], const D
 }
 
 // ---------------------------------------------------------------------------
-// Panel layout:
-//   A: BM rows of 128 bytes (eight 16-byte chunks of 4 k); chunk c of row r
-//      sits at position c ^ swz<64>(r) = c ^ ((r / 2) % 8), the key of the
-//      packed image's 128-byte rows; a copy instruction fills 8 rows, lane l
-//      fetching the global chunk that belongs at its position.  Measured
-//      (LdsBankConflict): no conflicts with this key or with r % 8, while
-//      (r % 8) ^ ((r / 8) % 2) made every A fragment read a two-way conflict
-//      (2-4% of the call's time at 256-512 rows).
-//   B: 32 k-rows of BN floats, BN * 4 bytes apart; a copy instruction fills
-//      1024 / (4 BN) whole k-rows.
+// Panel layout (each operand copied along its stored rows and kept in that
+// orientation):
+//   A (as stored; B^T alike): BM rows of 128 bytes (eight 16-byte chunks of 4
+//      k); chunk c of row r sits at position c ^ swz<64>(r) = c ^ ((r / 2) %
+//      8), the key of the packed image's 128-byte rows; a copy instruction
+//      fills 8 rows, lane l fetching the global chunk that belongs at its
+//      position.  Measured (LdsBankConflict): no conflicts with this key or
+//      with r % 8, while (r % 8) ^ ((r / 8) % 2) made every A fragment read a
+//      two-way conflict (2-4% of the call's time at 256-512 rows).
+//   B (as stored): 32 k-rows of BN floats, BN * 4 bytes apart; a copy
+//      instruction fills 1024 / (4 BN) whole k-rows.
+//   A^T (A stored K x M): 32 k-rows of BM floats in groups of 256 / BM k-rows
+//      that one copy instruction fills, the groups 1 KB + PAD apart (KRowsPanel
+//      below), so that the four k-rows the lane quarters read at once (4
+//      apart) fall in four different quarters of the 64 banks.
 // A panel's sum over its 32 k may run in any order, so lane quarter q takes
 // k in {4q .. 4q + 3} and {16 + 4q .. 16 + 4q + 3}, for A and B alike: two
-// 16-byte reads of an A row.  In f16r these eight k are the lane's eight
-// operands of one v_mfma_f32_16x16x32_f16; in f32, step t of eight
-// v_mfma_f32_16x16x4_f32 takes the t-th of them from every lane quarter, so
-// each step sums four distinct k and the eight steps all 32.  Columns: the wave tile's columns are dealt
-// to its 16-column blocks four at a time -- lane column r16 of block 4g + jj
-// is column 64g + 4 r16 + jj of the wave tile -- so one 16-byte read of a B
-// k-row gives a lane its value for four blocks (eight reads: four blocks'
-// fragments, 16 lanes reading 256 contiguous bytes), and in the epilogue a
-// lane holds four consecutive columns of a row, which it reads (beta != 0)
-// and writes as one piece.
+// 16-byte reads of a row (A, B^T), or eight single reads of k-rows (A^T).  In
+// f16r these eight k are the lane's eight operands of one
+// v_mfma_f32_16x16x32_f16; in f32, step t of eight v_mfma_f32_16x16x4_f32
+// takes the t-th of them from every lane quarter, so each step sums four
+// distinct k and the eight steps all 32.  Columns (B as stored): the wave
+// tile's columns are dealt to its 16-column blocks four at a time -- lane
+// column r16 of block 4g + jj is column 64g + 4 r16 + jj of the wave tile --
+// so one 16-byte read of a B k-row gives a lane its value for four blocks
+// (eight reads: four blocks' fragments, 16 lanes reading 256 contiguous
+// bytes), and in the epilogue a lane holds four consecutive columns of a row,
+// which it reads (beta != 0) and writes as one piece.  With B^T the columns
+// are not dealt (lane column r16 of block j is column 16 j + r16, 16
+// consecutive rows of the B^T panel, as the A reads) and the epilogue is the
+// block layout's.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int NS, int WM, int WN>
+
+// The k-rows panel of A^T: 32 k-rows of EXT floats.  One 1 KB copy fills a
+// group of RPI = 256 / EXT k-rows; groups lie GROUP bytes apart.  The lane
+// quarters read k-rows 4q + t together (t fixed), 16 floats each: PAD puts
+// them 16 banks apart (RPI k-rows of a group are contiguous, so rows 4 apart
+// in one group sit a multiple of 128 floats apart; with RPI = 8 the slots of
+// a group are permuted, k-row r at slot 2 (r % 4) + (r / 4) % 2, so that rows
+// 4 apart land in slots of opposite parity, 32 banks apart).
+template <int EXT>
+struct KRowsPanel {
+    static_assert(EXT == 32 || EXT == 64 || EXT == 128 || EXT == 256, "panel extent");
+    static constexpr int RPI = 256 / EXT;
+    static constexpr int PAD = RPI == 1 ? 16 : RPI == 2 ? 32 : 64;
+    static constexpr int GROUP = 1024 + PAD;
+    static constexpr int BYTES = (32 / RPI) * GROUP;
+    __host__ __device__ static constexpr int slot(int r) { return RPI == 8 ? 2 * (r % 4) + (r / 4) % 2 : r; }
+    __host__ __device__ static constexpr int row_of_slot(int s) { return RPI == 8 ? s / 2 + 4 * (s % 2) : s; }
+    // byte offset of float e of k-row kr
+    __host__ __device__ static constexpr int at(int kr, int e) {
+        return (kr / RPI) * GROUP + slot(kr % RPI) * EXT * 4 + 4 * e;
+    }
+};
+
+template <int BM, int BN, int NS, int WM, int WN, bool TA, bool TB>
 struct PanelRingShape {
     static constexpr int BK = 32;
     static constexpr int NW = WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int GFM = TM / 16, GFN = TN / 16;
-    static constexpr int A_ROW = BK * 4;
-    static constexpr int A_BYTES = BM * A_ROW;
-    static constexpr int B_ROW = BN * 4;
-    static constexpr int STAGE = A_BYTES + BK * B_ROW;
-    static constexpr int A_INS = A_BYTES / (1024 * NW);
-    static constexpr int B_INS = BK * B_ROW / (1024 * NW);
+    static constexpr int A_ROW = BK * 4;                       // rows layout
+    static constexpr int A_BYTES = TA ? KRowsPanel<BM>::BYTES : BM * A_ROW;
+    static constexpr int B_ROW = TB ? BK * 4 : BN * 4;         // a B^T row, or a k-row of B
+    static constexpr int B_BYTES = TB ? BN * B_ROW : BK * B_ROW;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    // 1 KB copies per wave per panel (8 rows, or 1024 / (4 EXT) k-rows, each)
+    static constexpr int A_INS = BM / 8 / NW;
+    static constexpr int B_INS = BN / 8 / NW;
     static constexpr int FILLS = A_INS + B_INS;
     static_assert(BN == 64 || BN == 128 || BN == 256, "whole k-rows per copy instruction");
-    static_assert(A_INS >= 1 && A_INS * NW * 1024 == A_BYTES && B_INS >= 1 &&
-                      B_INS * NW * 1024 == BK * B_ROW,
+    static_assert(A_INS >= 1 && A_INS * NW * 8 == BM && B_INS >= 1 && B_INS * NW * 8 == BN,
                   "copies split evenly over the waves");
-    static_assert(TM % 16 == 0 && TN % 64 == 0, "wave tile of 16-row blocks and 64-column groups");
+    static_assert(TM % 16 == 0 && TN % (TB ? 16 : 64) == 0,
+                  "wave tile of 16-row blocks and (dealt) 64-column groups");
     static_assert(NS >= 3 && NS * STAGE <= 160 * 1024, "LDS budget of one CU");
     static_assert((NS - 2) * FILLS < 64, "vmcnt range");
 };
@@ -264,10 +301,13 @@ __device__ __forceinline__ void store_tile_dealt(const f32x4v (&acc)[GFM][GFN], 
 // F16: round to binary16 and multiply on v_mfma_f32_16x16x32_f16 (f16r);
 // otherwise multiply the f32 values on v_mfma_f32_16x16x4_f32, eight steps a
 // panel, step s taking from lane quarter q the s-th of its eight k (so the
-// same fragment reads serve both modes).
-template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED, bool OUT16, bool F16>
+// same fragment reads serve both modes).  TA: A stored K x M; TB: B stored
+// N x K.
+template <int BM, int BN, int NS, int WM, int WN, int GM, bool MASKED, bool OUT16, bool F16, bool TA,
+          bool TB>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_ring_kernel(DirectArgs p) {
-    using S = PanelRingShape<BM, BN, NS, WM, WN>;
+    using S = PanelRingShape<BM, BN, NS, WM, WN, TA, TB>;
+    using KA = KRowsPanel<BM>;
     constexpr int GFM = S::GFM, GFN = S::GFN, GG = GFN / 4;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * S::STAGE];
 
@@ -282,25 +322,48 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_ring_kernel(DirectArg
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / WN, wc = wave % WN;
 
-    // Copy sources.  A copy j of this wave fills the panel rows 8u .. 8u + 7,
-    // u = wave + NW j: lane l takes row 8u + l / 8 at position l % 8, which
-    // holds global chunk (l % 8) ^ swz<64>(row); rows past M read row M - 1.  B
-    // copy j fills bytes 1024u .. 1024u + 1023 of the B panel: lane l the four
-    // floats at byte 1024u + 16l, i.e. k-row (1024u + 16l) / B_ROW from column
-    // ((1024u + 16l) % B_ROW) / 4 on (columns past N read column n0); copy j
-    // is copy 0 moved down 1024 NW / B_ROW k-rows.
+    // Copy sources.  Rows layout (A, B^T): copy j of this wave fills the panel
+    // rows 8u .. 8u + 7, u = wave + NW j: lane l takes row 8u + l / 8 at
+    // position l % 8, which holds global chunk (l % 8) ^ swz<64>(row); rows
+    // past M (N) read row M - 1 (N - 1).  k-rows of A^T: copy j fills group u,
+    // lane l the four floats 4 (l % LPR) .. of the k-row in slot l / LPR (LPR
+    // lanes a k-row; columns past M read column m0).  B: copy j fills bytes
+    // 1024u .. 1024u + 1023 of the B panel: lane l the four floats at byte
+    // 1024u + 16l, i.e. k-row (1024u + 16l) / B_ROW from column ((1024u + 16l)
+    // % B_ROW) / 4 on (columns past N read column n0); copy j is copy 0 moved
+    // down 1024 NW / B_ROW k-rows.
     const float* a_src[S::A_INS];
 #pragma unroll
     for (int j = 0; j < S::A_INS; ++j) {
-        const int row = 8 * (wave + S::NW * j) + (lane >> 3);
-        const int chunk = (lane & 7) ^ swz<64>(row & 15);
-        a_src[j] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + k_lo + chunk * 4;
+        if constexpr (TA) {
+            constexpr int LPR = 64 / KA::RPI;
+            const int col = m0 + 4 * (lane % LPR);
+            const int kr = KA::RPI * (wave + S::NW * j) + KA::row_of_slot(lane / LPR);
+            a_src[j] = p.A + (int64_t)(k_lo + kr) * p.lda + (col < p.M ? col : m0);
+        } else {
+            const int row = 8 * (wave + S::NW * j) + (lane >> 3);
+            const int chunk = (lane & 7) ^ swz<64>(row & 15);
+            a_src[j] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + k_lo + chunk * 4;
+        }
     }
-    const int b_byte = 1024 * wave + 16 * lane;
-    const int bcol = n0 + (b_byte % S::B_ROW) / 4;
-    const float* b_src = p.B + (int64_t)(k_lo + b_byte / S::B_ROW) * p.ldb + (bcol < p.N ? bcol : n0);
-    const int64_t b_step = (int64_t)(1024 / S::B_ROW) * S::NW * p.ldb;
-    const int64_t b_panel = (int64_t)S::BK * p.ldb;
+    const int64_t a_panel = TA ? (int64_t)S::BK * p.lda : S::BK;
+    constexpr int A_DST = TA ? KA::GROUP : 1024;   // LDS bytes between copies
+    const float* b_src[TB ? S::B_INS : 1];
+    int64_t b_step = 0, b_panel = S::BK;
+    if constexpr (TB) {
+#pragma unroll
+        for (int j = 0; j < S::B_INS; ++j) {
+            const int row = 8 * (wave + S::NW * j) + (lane >> 3);
+            const int chunk = (lane & 7) ^ swz<64>(row & 15);
+            b_src[j] = p.B + (int64_t)min(n0 + row, p.N - 1) * p.ldb + k_lo + chunk * 4;
+        }
+    } else {
+        const int b_byte = 1024 * wave + 16 * lane;
+        const int bcol = n0 + (b_byte % S::B_ROW) / 4;
+        b_src[0] = p.B + (int64_t)(k_lo + b_byte / S::B_ROW) * p.ldb + (bcol < p.N ? bcol : n0);
+        b_step = (int64_t)(1024 / S::B_ROW) * S::NW * p.ldb;
+        b_panel = (int64_t)S::BK * p.ldb;
+    }
 
     auto stage_of = [&](int i) __attribute__((always_inline)) -> unsigned char* {
         return ring + i * S::STAGE;
@@ -309,20 +372,31 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_ring_kernel(DirectArg
         const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage));
 #pragma unroll
         for (int j = 0; j < S::A_INS; ++j)
-            lds_copy16(a_src[j] + kt * S::BK, base + (wave + S::NW * j) * 1024);
+            lds_copy16(a_src[j] + kt * a_panel, base + (wave + S::NW * j) * A_DST);
 #pragma unroll
-        for (int j = 0; j < S::B_INS; ++j)
-            lds_copy16(b_src + j * b_step + kt * b_panel, base + S::A_BYTES + (wave + S::NW * j) * 1024);
+        for (int j = 0; j < S::B_INS; ++j) {
+            if constexpr (TB)
+                lds_copy16(b_src[j] + kt * b_panel, base + S::A_BYTES + (wave + S::NW * j) * 1024);
+            else
+                lds_copy16(b_src[0] + j * b_step + kt * b_panel,
+                           base + S::A_BYTES + (wave + S::NW * j) * 1024);
+        }
     };
 
-    // Fragment reads of lane (q, r16): A row r16 of a block at logical chunks
-    // q and q + 4; B k-rows 4q .. 4q + 3 and 16 + 4q .. 16 + 4q + 3 at the
-    // lane's four columns of a 64-column group.
+    // Fragment reads of lane (q, r16): a row r16 of a block at logical chunks
+    // q and q + 4 (A; B^T at row r16 of a 16-column block); A^T k-rows 4q ..
+    // 4q + 3 and 16 + 4q .. 16 + 4q + 3 at column r16 of a block; B k-rows
+    // 4q .. 4q + 3 and 16 + 4q .. 16 + 4q + 3 at the lane's four columns of a
+    // 64-column group.
     const int r16 = lane & 15, q = lane >> 4;
     const int a_row = (wr * S::TM + r16) * S::A_ROW;
-    const int a_off0 = a_row + ((q ^ swz<64>(r16)) << 4);
-    const int a_off1 = a_row + (((q + 4) ^ swz<64>(r16)) << 4);
-    const int b_off = S::A_BYTES + 4 * q * S::B_ROW + (wc * S::TN + 4 * r16) * 4;
+    const int a_off0 = TA ? KA::at(4 * q, wr * S::TM + r16) : a_row + ((q ^ swz<64>(r16)) << 4);
+    const int a_off1 = TA ? KA::at(16 + 4 * q, wr * S::TM + r16)
+                          : a_row + (((q + 4) ^ swz<64>(r16)) << 4);
+    const int b_row = S::A_BYTES + (wc * S::TN + r16) * S::B_ROW;   // B^T
+    const int b_off = TB ? b_row + ((q ^ swz<64>(r16)) << 4)
+                         : S::A_BYTES + 4 * q * S::B_ROW + (wc * S::TN + 4 * r16) * 4;
+    const int b_off1 = b_row + (((q + 4) ^ swz<64>(r16)) << 4);
 
     f32x4v acc[GFM][GFN];
 #pragma unroll
@@ -344,10 +418,49 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_ring_kernel(DirectArg
         f32x4v a0[GFM], a1[GFM];
 #pragma unroll
         for (int i = 0; i < GFM; ++i) {
-            a0[i] = *reinterpret_cast<lds_f32x4c*>(st + a_off0 + i * 16 * S::A_ROW);
-            a1[i] = *reinterpret_cast<lds_f32x4c*>(st + a_off1 + i * 16 * S::A_ROW);
+            if constexpr (TA) {
+                // k-row offsets relative to k-row 4q (16 + 4q): KA::at is
+                // additive over whole multiples of RPI and 4q's own slot
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    a0[i][t] = *reinterpret_cast<lds_f32c*>(st + a_off0 + KA::at(t, 16 * i));
+                    a1[i][t] = *reinterpret_cast<lds_f32c*>(st + a_off1 + KA::at(t, 16 * i));
+                }
+            } else {
+                a0[i] = *reinterpret_cast<lds_f32x4c*>(st + a_off0 + i * 16 * S::A_ROW);
+                a1[i] = *reinterpret_cast<lds_f32x4c*>(st + a_off1 + i * 16 * S::A_ROW);
+            }
         }
-        if constexpr (F16) {
+        if constexpr (TB) {
+            f32x4v b0[GFN], b1[GFN];
+#pragma unroll
+            for (int j = 0; j < GFN; ++j) {
+                b0[j] = *reinterpret_cast<lds_f32x4c*>(st + b_off + j * 16 * S::B_ROW);
+                b1[j] = *reinterpret_cast<lds_f32x4c*>(st + b_off1 + j * 16 * S::B_ROW);
+            }
+            if constexpr (F16) {
+                f16x8 fa[GFM], fb[GFN];
+#pragma unroll
+                for (int i = 0; i < GFM; ++i) fa[i] = rn8(a0[i], a1[i]);
+#pragma unroll
+                for (int j = 0; j < GFN; ++j) fb[j] = rn8(b0[j], b1[j]);
+#pragma unroll
+                for (int i = 0; i < GFM; ++i)
+#pragma unroll
+                    for (int j = 0; j < GFN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int i = 0; i < GFM; ++i)
+#pragma unroll
+                        for (int j = 0; j < GFN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                t < 4 ? a0[i][t] : a1[i][t - 4], t < 4 ? b0[j][t] : b1[j][t - 4],
+                                acc[i][j], 0, 0, 0);
+            }
+        } else if constexpr (F16) {
             f16x8 fa[GFM], fb[GFN];
 #pragma unroll
             for (int i = 0; i < GFM; ++i) fa[i] = rn8(a0[i], a1[i]);
@@ -391,32 +504,50 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_ring_kernel(DirectArg
 
     if (p.slices > 1 && !last_slice_adds<GFM, GFN, BM * BN * 4>(acc, p, wave, lane, ring)) return;
     const int row0 = m0 + wr * S::TM, col0 = n0 + wc * S::TN;
-    if constexpr (OUT16)
+    if constexpr (TB) {
+        if constexpr (OUT16)
+            store_tile_m16<GFM, GFN, MASKED, true>(acc, p.C16, p.ldc, row0, col0, p.M, p.N, p.alpha,
+                                                   p.beta, lane);
+        else
+            store_tile_m16<GFM, GFN, MASKED, false>(acc, p.C, p.ldc, row0, col0, p.M, p.N, p.alpha,
+                                                    p.beta, lane);
+    } else if constexpr (OUT16) {
         store_tile_dealt<GFM, GFN, MASKED, true>(acc, p.C16, p.ldc, row0, col0, p.M, p.N, p.alpha,
                                                  p.beta, lane);
-    else
+    } else {
         store_tile_dealt<GFM, GFN, MASKED, false>(acc, p.C, p.ldc, row0, col0, p.M, p.N, p.alpha,
                                                   p.beta, lane);
+    }
+}
+
+template <int BM, int BN, int NS, int WM, int WN, int GM, bool F16, bool TA, bool TB>
+hipError_t launch_panel_ring_layout(const DirectArgs& a, bool masked, hipStream_t s) {
+    const dim3 grid(a.tiles_m * a.tiles_n, a.slices), block(WM * WN * 64);
+    const bool edge = masked || a.M % BM != 0 || a.N % BN != 0;
+    if constexpr (F16) {
+        if (a.C16) {
+            if (edge)
+                gemm_panel_ring_kernel<BM, BN, NS, WM, WN, GM, true, true, true, TA, TB><<<grid, block, 0, s>>>(a);
+            else
+                gemm_panel_ring_kernel<BM, BN, NS, WM, WN, GM, false, true, true, TA, TB><<<grid, block, 0, s>>>(a);
+            return hipGetLastError();
+        }
+    }
+    if (edge) gemm_panel_ring_kernel<BM, BN, NS, WM, WN, GM, true, false, F16, TA, TB><<<grid, block, 0, s>>>(a);
+    else gemm_panel_ring_kernel<BM, BN, NS, WM, WN, GM, false, false, F16, TA, TB><<<grid, block, 0, s>>>(a);
+    return hipGetLastError();
 }
 
 template <int BM, int BN, int NS, int WM, int WN, int GM, bool F16>
 hipError_t launch_panel_ring(const DirectArgs& a, bool ta, bool tb, bool masked, hipStream_t s) {
     // the host hands only the shapes this kernel takes (panel_ring_takes)
-    if (ta || tb || a.N % 4 != 0 || a.K % 32 != 0 || a.depth % 32 != 0 || a.K <= 0 ||
-        (!F16 && a.C16))
+    if ((!tb && a.N % 4 != 0) || (ta && a.M % 4 != 0) || a.K % 32 != 0 || a.depth % 32 != 0 ||
+        a.K <= 0 || (!F16 && a.C16))
         return hipErrorInvalidValue;
-    const dim3 grid(a.tiles_m * a.tiles_n, a.slices), block(WM * WN * 64);
-    const bool edge = masked || a.M % BM != 0 || a.N % BN != 0;
-    if constexpr (F16) {
-        if (a.C16) {
-            if (edge) gemm_panel_ring_kernel<BM, BN, NS, WM, WN, GM, true, true, true><<<grid, block, 0, s>>>(a);
-            else gemm_panel_ring_kernel<BM, BN, NS, WM, WN, GM, false, true, true><<<grid, block, 0, s>>>(a);
-            return hipGetLastError();
-        }
-    }
-    if (edge) gemm_panel_ring_kernel<BM, BN, NS, WM, WN, GM, true, false, F16><<<grid, block, 0, s>>>(a);
-    else gemm_panel_ring_kernel<BM, BN, NS, WM, WN, GM, false, false, F16><<<grid, block, 0, s>>>(a);
-    return hipGetLastError();
+    if (ta && tb) return launch_panel_ring_layout<BM, BN, NS, WM, WN, GM, F16, true, true>(a, masked, s);
+    if (ta) return launch_panel_ring_layout<BM, BN, NS, WM, WN, GM, F16, true, false>(a, masked, s);
+    if (tb) return launch_panel_ring_layout<BM, BN, NS, WM, WN, GM, F16, false, true>(a, masked, s);
+    return launch_panel_ring_layout<BM, BN, NS, WM, WN, GM, F16, false, false>(a, masked, s);
 }
 
 #define G355_PANEL_RING_F16R(BM, BN, NS, WM, WN, GM) \
@@ -439,11 +570,12 @@ const DirectInstance* panel_ring_instances(int mode, int* count) {
 }
 
 bool panel_ring_takes(bool ta, bool tb, const float* A, int64_t lda, const float* B, int64_t ldb,
-                      int64_t N, int64_t K) {
+                      int64_t M, int64_t N, int64_t K) {
     auto vec = [](const float* p, int64_t ld) {
         return ld % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0;
     };
-    return !ta && !tb && vec(A, lda) && vec(B, ldb) && N % 4 == 0 && K % 32 == 0 && K > 0;
+    return vec(A, lda) && vec(B, ldb) && (tb || N % 4 == 0) && (!ta || M % 4 == 0) && K % 32 == 0 &&
+           K > 0;
 }
 
 }  // namespace g355

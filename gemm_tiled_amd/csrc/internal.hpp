@@ -200,12 +200,13 @@ const DirectInstance* direct_instances(int* count);
 // The KS=3 configurations with BK = 32 (gemm_panel_ring.hip), in both modes:
 // f32 panels in a ring of direct-to-LDS copies, each fragment read in f32 and
 // multiplied on v_mfma_f32_16x16x4_f32 (f32) or rounded to binary16 for
-// v_mfma_f32_16x16x32_f16 (f16r).  They take the plain layout with 16-byte
-// aligned rows, N % 4 == 0 and K % 32 == 0 (panel_ring_takes), slices of K a
+// v_mfma_f32_16x16x32_f16 (f16r).  They take every operand layout with
+// 16-byte aligned rows and K % 32 == 0, N % 4 == 0 where B is stored K x N
+// and M % 4 == 0 where A is stored K x M (panel_ring_takes), slices of K a
 // multiple of 32 deep; binary16 C in f16r only.
 const DirectInstance* panel_ring_instances(int mode, int* count);
 bool panel_ring_takes(bool ta, bool tb, const float* A, int64_t lda, const float* B, int64_t ldb,
-                      int64_t N, int64_t K);
+                      int64_t M, int64_t N, int64_t K);
 
 // Measurement kernels.
 hipError_t launch_roof_mfma(int mode, int form, int64_t iters, int blocks, float* sink, double* flops,

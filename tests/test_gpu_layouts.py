@@ -214,3 +214,48 @@ def test_ring_layouts_small_integers_exact_and_beta_zero(cfg, ta, tb, M, N, K):
         Cn = np.full((M, N), np.nan, dtype=np.float32)
         got = run_ex("f32", A, B, Cn, 1.0, 0.0, ta, tb)
         assert np.array_equal(got, exact.astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# The f32-panel ring (KS=3, BK=32: f32 panels through direct-to-LDS copies,
+# rounded to binary16 as read in f16r, K split over workgroups) in the
+# transposed layouts: A^T staged as k-rows, B^T as swizzled rows read in the
+# block layout of the 16-column blocks, both modes, every configuration.
+# ---------------------------------------------------------------------------
+PANEL_RINGS = {m: [c for c in g.list_configs(m) if "KS=3" in c and "BK=32" in c] for m in MODES}
+PANEL_CASES = [
+    (20, 1000, 4096, 0),     # ragged M and N, many slices
+    (300, 520, 2112, 4),     # padded 16-byte rows
+    (64, 4096, 4096, 0),     # whole tiles
+    (36, 256, 32, 0),        # one panel
+    (128, 1001, 1024, 0),    # N % 4 != 0: B^T taken, B as stored handed to other tiles
+]
+
+
+@pytest.mark.parametrize("mode,cfg", [(m, c) for m in MODES for c in PANEL_RINGS[m]])
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[_name(*x) for x in LAYOUTS])
+@pytest.mark.parametrize("M,N,K,pad", PANEL_CASES)
+def test_panel_ring_layouts_against_the_oracle(mode, cfg, ta, tb, M, N, K, pad):
+    A, B, C = make_inputs(M, N, K, "normal", seed=74)
+    lda, ldb = _lds(M, N, K, ta, tb, pad)
+    with pinned(mode, cfg):
+        say(f"[panel ring layout] {mode} {_name(ta, tb)} {cfg} {M}x{N}x{K} lda={lda} ldb={ldb}")
+        got = run_ex(mode, A, B, C, -0.75, 1.5, ta, tb, lda, ldb)
+        again = run_ex(mode, A, B, C, -0.75, 1.5, ta, tb, lda, ldb)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+    check(mode, A, B, C, -0.75, 1.5, got)
+
+
+@pytest.mark.parametrize("mode,cfg", [(m, c) for m in MODES for c in PANEL_RINGS[m][:1] + PANEL_RINGS[m][-1:]])
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[_name(*x) for x in LAYOUTS])
+def test_panel_ring_layouts_small_integers_exact_and_beta_zero(mode, cfg, ta, tb):
+    M, N, K = 40, 2048, 4096
+    A, B, C = small_integers(M, N, K, seed=75)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned(mode, cfg):
+        say(f"[panel ring layout exact] {mode} {_name(ta, tb)} {cfg} {M}x{N}x{K}")
+        got = run_ex(mode, A, B, C, -2.0, 0.5, ta, tb)
+        assert np.array_equal(got, (-2.0 * exact + 0.5 * C.astype(np.float64)).astype(np.float32))
+        Cn = np.full((M, N), np.nan, dtype=np.float32)
+        got = run_ex(mode, A, B, Cn, 1.0, 0.0, ta, tb)
+        assert np.array_equal(got, exact.astype(np.float32))

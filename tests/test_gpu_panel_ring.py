@@ -5,8 +5,10 @@ the slices in order).
 
 Same bound as the other f32 parity tests against the float64 oracle; exact
 results on small integers; bitwise repeatability (the slice order is fixed);
-the shapes the ring does not take (K % 32 != 0, unaligned rows, transposed
-operands) handed to the split-K tiles.
+the shapes the ring does not take (K % 32 != 0, unaligned rows, N % 4 != 0
+for B stored K x N, M % 4 != 0 for A stored K x M) handed to the split-K
+tiles.  The transposed layouts of the ring are tested in
+test_gpu_layouts.py.
 """
 from __future__ import annotations
 
@@ -76,14 +78,21 @@ def test_panel_ring_small_integers_exact(cfg, M, ldc_pad):
     (64, 1024, 4080, {}, (False, False)),           # K % 32 != 0
     (64, 1022, 2048, {}, (False, False)),           # N % 4 != 0
     (64, 1024, 2048, {"lda": 2049}, (False, False)),   # rows not 16-byte aligned
-    (64, 1024, 2048, {}, (True, False)),            # A stored transposed
-    (64, 1024, 2048, {}, (False, True)),            # B stored transposed
+    (62, 1024, 2048, {}, (True, False)),            # A stored K x M with M % 4 != 0
+    (64, 1024, 2048, {"ldb": 2049}, (False, True)),    # B stored N x K, rows not 16-byte aligned
 ])
 def test_panel_ring_hands_other_shapes_to_split_k(M, N, K, lds, trans):
-    A, B, C = make_inputs(M, N, K, "uniform", seed=33, **lds)
     ta, tb = trans
-    tA = to_device(np.ascontiguousarray(A.T) if ta else A)
-    tB = to_device(np.ascontiguousarray(B.T) if tb else B)
+    A, B, C = make_inputs(M, N, K, "uniform", seed=33, **({} if tb else lds))
+
+    def stored(x, t, ld):
+        if not t:
+            return to_device(x)
+        buf = np.zeros((x.shape[1], ld or x.shape[0]), dtype=np.float32)
+        buf[:, :x.shape[0]] = x.T
+        return torch.from_numpy(buf).to("cuda")[:, :x.shape[0]]
+    tA = stored(A, ta, lds.get("lda") if ta else None)
+    tB = stored(B, tb, lds.get("ldb") if tb else None)
     tC = to_device(C)
     with pinned("f32", RINGS[0]):
         say(f"[panel ring f32 hand-off] {M}x{N}x{K} {lds} ta={ta} tb={tb}")
