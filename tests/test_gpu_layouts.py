@@ -259,3 +259,25 @@ def test_panel_ring_layouts_small_integers_exact_and_beta_zero(mode, cfg, ta, tb
         Cn = np.full((M, N), np.nan, dtype=np.float32)
         got = run_ex(mode, A, B, Cn, 1.0, 0.0, ta, tb)
         assert np.array_equal(got, exact.astype(np.float32))
+
+
+@pytest.mark.parametrize("mode,cfg", [(m, c) for m in MODES for c in PANEL_RINGS[m][:1] + PANEL_RINGS[m][-1:]])
+@pytest.mark.parametrize("ta,tb", [(False, False)] + LAYOUTS, ids=["NN"] + [_name(*x) for x in LAYOUTS])
+def test_panel_ring_layouts_never_read_past_the_matrix(mode, cfg, ta, tb):
+    """NaN in the padding of every stored row (16-byte aligned leading
+    dimensions) and in 40 rows after each stored array; M and N ragged
+    against the tiles.  The panel ring clamps every copy to the matrix, so a
+    read of any NaN would show in C.  Small integers: the result is exact."""
+    M, N, K = 44, 1000, 2048
+    A, B, C = small_integers(M, N, K, seed=76)
+    lda, ldb = _lds(M, N, K, ta, tb, 4)
+    tA, tB, tC = _nan_padded(A, ta, lda), _nan_padded(B, tb, ldb), to_device(C)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned(mode, cfg):
+        plan = g.get_plan(mode, M, N, K, lda=lda, ldb=ldb, beta=-1.0, transa=ta, transb=tb)
+        assert plan.split()[0] in ("form=panel-ring", "form=round-on-load"), plan
+        say(f"[panel ring layout nan] {mode} {_name(ta, tb)} {cfg} {M}x{N}x{K}")
+        g.gemm(mode, tA, tB, tC, 1.0, -1.0, transa=ta, transb=tb)
+        torch.cuda.synchronize()
+    got = tC.cpu().numpy()
+    assert np.array_equal(got, (exact - C.astype(np.float64)).astype(np.float32))
