@@ -507,13 +507,24 @@ TileConfig panel_ring_config(int mode, int64_t M, int64_t N, int64_t K) {
 // efficiency of the tile), the trade-off of the phobos "Tuning" section:
 // larger tiles reuse more, but leave fewer workgroups to fill the chip.
 TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
-    // a few rows of C (memory-bound, too few tiles): the few-rows
-    // configuration up to one 16-row group, then the split-K tiles
-    if (M <= kRowsRows) return rows_config(mode);
     // (the f32-panel ring: 16-byte aligned rows, K % 32 == 0, and a multiple
     // of 4 along B's rows as stored K x N and along A's as stored K x M)
     const bool panels = rows.aligned() && K % 32 == 0 && ((rows.trans & 2) || N % 4 == 0) &&
                         (!(rows.trans & 1) || M % 4 == 0);
+    // a few rows of C (memory-bound, too few tiles): the few-rows
+    // configuration up to one 16-row group, then the split-K tiles.  With B
+    // stored N x K the few-rows kernel's register layout reads B^T 16 stored
+    // rows per load, while the f32-panel ring copies whole 128-byte pieces of
+    // rows into its panels: at K = N = 4096 and 1 to 16 rows the ring on 32 x
+    // 128 tiles ran f16r in 16.3-16.8 us against 19.3-22.0, f32 in 19.0-19.5
+    // against 19.4-20.7.
+    if (M <= kRowsRows) {
+        TileConfig ring;
+        if ((rows.trans & 2) && panels && N >= 128 &&
+            parse_config(mode, "BM=32 BN=128 BK=32 ST=4 WM=2 WN=2 GM=8 KS=3", &ring))
+            return ring;
+        return rows_config(mode);
+    }
     // A few columns of C (measured at M = K = 4096): in f32 the same
     // configuration on the transposed problem up to 16 columns (4096 x 16 x
     // 4096 in 20 us against 81 us on the masked 128 x 256 ring, 8192 x 1 x
