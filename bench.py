@@ -19,7 +19,7 @@ same command makes; --tune runs the library's autotuner first.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--workloads a,b,...] [--tune] [--json-out path]
-       python bench.py --profile WORKLOAD [--calls N] [--calibrate-copy]
+       python bench.py --profile WORKLOAD [--layout TN] [--calls N] [--calibrate-copy]
        python bench.py --summarize-trace DIR --out FILE --cmd "..."
        python bench.py --summarize-counters WORKLOAD DIR [DIR ...] --out FILE --cmd "..."
 Prints progress on stderr and ONE JSON line on stdout.
@@ -74,7 +74,12 @@ def main():
                     help="target CPU time of each oracle sample")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--profile", metavar="WORKLOAD", default=None,
-                    help="run only this workload's call --calls times (for a profiler)")
+                    help="run only this workload's call --calls times (for a profiler); a "
+                         "workload name or mode:MxNxK (alpha 1, beta 0, U[-1,1] inputs)")
+    ap.add_argument("--layout", choices=("NN", "TN", "NT", "TT"), default="NN",
+                    help="operand layout of --profile and --summarize-counters: T stores "
+                         "that operand transposed (op(A) = A^T from a K x M array, op(B) = "
+                         "B^T from an N x K one)")
     ap.add_argument("--calls", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB copy kernel (byte-counter calibration)")
@@ -109,7 +114,7 @@ def main():
         if len(args.summarize_counters) < 2:
             raise SystemExit("--summarize-counters WORKLOAD DIR [DIR ...]")
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1:], args.out,
-                           args.cmd)
+                           args.cmd, args.layout)
         return
 
     if args.gpus != 1:
@@ -135,7 +140,8 @@ def main():
         f"{props.multi_processor_count} CUs; libgemm355 {g.version()}")
 
     if args.profile:
-        profile_run(g, torch, dev, WORKLOADS[args.profile], args.calls, args.calibrate_copy)
+        profile_run(g, torch, dev, profile_target(args.profile), args.calls, args.calibrate_copy,
+                    args.layout)
         return
     if args.calibrate_copy:
         copy_calibration(g, torch, dev)
@@ -578,23 +584,41 @@ def oracle_rate(w, target_seconds):
     return res
 
 
-def profile_run(g, torch, dev, w, calls, calibrate):
+def profile_target(spec):
+    """A scored workload by name, or mode:MxNxK (alpha 1, beta 0, U[-1,1])."""
+    from workloads import WORKLOADS, Workload
+    if spec in WORKLOADS:
+        return WORKLOADS[spec]
+    m = re.fullmatch(r"(f32|f16r):(\d+)x(\d+)x(\d+)", spec)
+    if not m:
+        raise SystemExit(f"unknown workload {spec!r}: a workload name or mode:MxNxK")
+    return Workload(spec, m.group(1), int(m.group(2)), int(m.group(3)), int(m.group(4)), 1.0,
+                    0.0, "uniform")
+
+
+def profile_run(g, torch, dev, w, calls, calibrate, layout="NN"):
     """The workload's call, `calls` times after 3 untimed ones, with the tile
     the benchmark uses (nothing else runs on the GPU besides the optional
-    calibration copy): what a profiler of this command sees."""
+    calibration copy): what a profiler of this command sees.  A transposed
+    layout stores that operand transposed (copied once, before the calls)."""
     (_, _, _), (tA, tB, tC) = _workload_tensors(w, torch, dev)
-    fn = g.gemm_f32 if w.mode == "f32" else g.gemm_f16r_f32acc
-    tile = g.get_config(w.mode, w.M, w.N, w.K, beta=w.beta)
-    log(f"profile {w.name}: tile {tile}, {calls} calls")
+    ta, tb = layout[0] == "T", layout[1] == "T"
+    if ta:
+        tA = tA.t().contiguous()
+    if tb:
+        tB = tB.t().contiguous()
+    tile = g.get_config(w.mode, w.M, w.N, w.K, beta=w.beta, transa=ta, transb=tb)
+    log(f"profile {w.name} {layout}: tile {tile}, {calls} calls")
     for _ in range(3):
-        fn(tA, tB, tC, w.alpha, w.beta)
+        g.gemm(w.mode, tA, tB, tC, w.alpha, w.beta, transa=ta, transb=tb)
     torch.cuda.synchronize()
     for _ in range(calls):
-        fn(tA, tB, tC, w.alpha, w.beta)
+        g.gemm(w.mode, tA, tB, tC, w.alpha, w.beta, transa=ta, transb=tb)
     torch.cuda.synchronize()
     if calibrate:
         copy_calibration(g, torch, dev)
-    print(json.dumps({"profile": w.name, "tile": tile, "calls": calls}), flush=True)
+    print(json.dumps({"profile": w.name, "layout": layout, "tile": tile, "calls": calls}),
+          flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -1276,7 +1300,7 @@ def committed_traffic(mode, workload, tile):
             d = json.loads(m.group(1))
         except ValueError:
             continue
-        if d.get("workload") != workload or d.get("mode") != mode:
+        if d.get("workload") != workload or d.get("mode") != mode or d.get("layout", "NN") != "NN":
             continue
         if d.get("tile", "").split(" source=")[0] != tile.split(" source=")[0]:
             continue
@@ -1388,9 +1412,9 @@ def _counter_table(dirs):
     return {k: {c: float(np.mean(v)) for c, v in cs.items()} for k, cs in table.items()}
 
 
-def summarize_counters(workload, dirs, out, cmd):
-    from workloads import WORKLOADS
-    w = WORKLOADS[workload]
+def summarize_counters(workload, dirs, out, cmd, layout="NN"):
+    w = profile_target(workload)
+    ta, tb = layout[0] == "T", layout[1] == "T"
     tab = _counter_table(dirs)
     copy = next((v for k, v in tab.items() if "copy_f32_kernel" in k), None)
     if not copy or "FETCH_SIZE" not in copy or "WRITE_SIZE" not in copy:
@@ -1400,10 +1424,13 @@ def summarize_counters(workload, dirs, out, cmd):
     f_fac, w_fac = kib / copy["FETCH_SIZE"], kib / copy["WRITE_SIZE"]
     mine = {k: v for k, v in tab.items() if "gemm_" in k or "pack_kernel" in k}
     import gemm_tiled_amd as g   # the tile the profiled run used: the library's own choice
-    tile = g.get_config(w.mode, w.M, w.N, w.K, beta=w.beta).split(" source=")[0]
+    tile = g.get_config(w.mode, w.M, w.N, w.K, beta=w.beta, transa=ta,
+                        transb=tb).split(" source=")[0]
+    what = "" if layout == "NN" else (f", layout {layout}: " + "; ".join(
+        x for x, t in (("A stored K x M", ta), ("B stored N x K", tb)) if t))
     lines = [f"# Counters of the {workload} call ({w.mode}, {w.M}x{w.N}x{w.K}, "
-             f"alpha {w.alpha}, beta {w.beta})", ""] + _commands_block(cmd)
-    lines += [f"Tile: `{tile}` (the benchmark's own choice for this workload).", "",
+             f"alpha {w.alpha}, beta {w.beta}{what})", ""] + _commands_block(cmd)
+    lines += [f"Tile: `{tile}` (the library's own choice for this call).", "",
               f"Byte calibration: the plain copy of {COPY_BYTES >> 20} MiB each way read "
               f"FETCH_SIZE {copy['FETCH_SIZE']:.0f} KiB and WRITE_SIZE {copy['WRITE_SIZE']:.0f} "
               f"KiB per launch, so HBM bytes = FETCH_SIZE x {f_fac:.4f} + WRITE_SIZE x "
@@ -1448,7 +1475,7 @@ def summarize_counters(workload, dirs, out, cmd):
               f"{compulsory / 1e6:.1f} MB compulsory (4(MK + KN) + 4MN read + 4MN written when "
               f"beta != 0, else written only): {traffic / compulsory:.2f}x; "
               f"{flops / max(traffic, 1):.0f} FLOP per HBM byte.", ""]
-    meta = {"workload": workload, "mode": w.mode, "tile": tile,
+    meta = {"workload": workload, "layout": layout, "mode": w.mode, "tile": tile,
             "traffic_bytes_per_call": traffic, "compulsory_bytes": compulsory,
             "source_hash": source_hash(w.mode), "fetch_factor": f_fac, "write_factor": w_fac,
             "kernels": meta_k}

@@ -107,3 +107,13 @@ def test_counter_summary_by_hand(tmp_path):
     # compulsory at 4096^3, beta = 0: 4(MK + KN) + 4MN = 3 x 64 MiB
     assert meta["compulsory_bytes"] == pytest.approx(3 * 64 * 2 ** 20)
     assert meta["fetch_factor"] == pytest.approx(2.0) and meta["write_factor"] == pytest.approx(1.0)
+
+
+def test_profile_target_names_a_workload_or_a_shape():
+    w = bench.profile_target("f32_4096_a1_b1")
+    assert (w.mode, w.M, w.N, w.K, w.beta) == ("f32", 4096, 4096, 4096, 1.0)
+    s = bench.profile_target("f16r:128x4096x2048")
+    assert (s.mode, s.M, s.N, s.K, s.alpha, s.beta) == ("f16r", 128, 4096, 2048, 1.0, 0.0)
+    for bad in ("f64:1x2x3", "f32:1x2", "nothing"):
+        with pytest.raises(SystemExit):
+            bench.profile_target(bad)
