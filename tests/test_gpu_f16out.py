@@ -97,3 +97,34 @@ def test_f16out_beta_only_and_few_rows():
             got16 = run16(A, B, C16, 1.0, 0.25)
         assert inside_bound(A, B, C16, 1.0, 0.25, got16)
     assert "KS=2" in g.get_config("f16r", 16, 4096, 4096, beta=0.25)
+
+
+@pytest.mark.parametrize("ta,tb", [(True, False), (False, True), (True, True)],
+                         ids=["TN", "NT", "TT"])
+@pytest.mark.parametrize("M,cfg", [
+    (16, None),                                           # the library's choice (B^T: panel ring)
+    (40, "BM=32 BN=128 BK=32 ST=4 WM=2 WN=2 KS=3"),       # f32-panel ring, ragged rows
+    (200, "BM=128 BN=256 BK=32 ST=3 WM=2 WN=4 KS=3"),
+])
+def test_f16out_layouts_on_the_panel_ring(ta, tb, M, cfg):
+    """The binary16 epilogues of the f32-panel ring in the transposed layouts
+    (the block-layout epilogue with B stored N x K, the column-dealt one
+    otherwise): bit for bit the rounding of the f32-output call, inside the
+    widened bound."""
+    N, K = 1000, 2048
+    A, B, C = make_inputs(M, N, K, "normal", seed=35)
+    C16 = C.astype(np.float16)
+    tA = to_device(np.ascontiguousarray(A.T) if ta else A)
+    tB = to_device(np.ascontiguousarray(B.T) if tb else B)
+    spec = cfg or g.get_config("f16r", M, N, K, beta=0.5, transa=ta, transb=tb).split(" source=")[0]
+    assert "KS=3" in spec or not tb, spec
+    with pinned("f16r", spec):
+        say(f"[f16-out layout] ta={ta} tb={tb} {M}x{N}x{K} {spec}")
+        t16 = torch.from_numpy(C16.copy()).to(DEV)
+        g.gemm_f16r_f16out(tA, tB, t16, 1.25, 0.5, transa=ta, transb=tb)
+        t32 = to_device(C16.astype(np.float32))
+        g.gemm("f16r", tA, tB, t32, 1.25, 0.5, transa=ta, transb=tb)
+        torch.cuda.synchronize()
+    got16, got32 = t16.cpu().numpy(), t32.cpu().numpy()
+    assert np.array_equal(got16.view(np.uint16), got32.astype(np.float16).view(np.uint16))
+    assert inside_bound(A, B, C16, 1.25, 0.5, got16)
