@@ -515,13 +515,13 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
     // configuration up to one 16-row group, then the split-K tiles.  With B
     // stored N x K the few-rows kernel's register layout reads B^T 16 stored
     // rows per load, while the f32-panel ring copies whole 128-byte pieces of
-    // rows into its panels: at K = N = 4096 and 1 to 16 rows the ring on 32 x
-    // 128 tiles ran f16r in 16.3-16.8 us against 19.3-22.0, f32 in 19.0-19.5
-    // against 19.4-20.7.
+    // rows into its panels: at K = N = 4096 and 1 to 16 rows the ring on 16 x
+    // 128 tiles ran f16r in 15.9-16.2 us against 19.3-21.9, f32 in 18.2-18.5
+    // against 19.3-20.6 (on 32 x 128 tiles 16.3-16.9 and 18.9-19.6).
     if (M <= kRowsRows) {
         TileConfig ring;
         if ((rows.trans & 2) && panels && N >= 128 &&
-            parse_config(mode, "BM=32 BN=128 BK=32 ST=4 WM=2 WN=2 GM=8 KS=3", &ring))
+            parse_config(mode, "BM=16 BN=128 BK=32 ST=4 WM=1 WN=2 GM=8 KS=3", &ring))
             return ring;
         return rows_config(mode);
     }

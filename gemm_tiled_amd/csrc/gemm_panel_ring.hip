@@ -24,6 +24,7 @@
 
 // X(BM, BN, NS, WM, WN, GM): the compiled configurations of each mode.
 #define G355_PANEL_RING_F16R_CONFIGS(X) \
+    X(16, 128, 4, 1, 2, 8)              \
     X(32, 64, 4, 2, 1, 8)               \
     X(32, 128, 4, 2, 2, 8)              \
     X(64, 64, 4, 4, 1, 8)               \
@@ -32,6 +33,7 @@
     X(128, 256, 3, 2, 4, 8)             \
     X(256, 128, 3, 4, 2, 8)
 #define G355_PANEL_RING_F32_CONFIGS(X) \
+    X(16, 128, 4, 1, 2, 8)             \
     X(32, 64, 4, 2, 1, 8)              \
     X(32, 128, 4, 2, 2, 8)             \
     X(64, 64, 4, 4, 1, 8)              \
@@ -139,20 +141,23 @@ __device__ __forceinline__ bool last_slice_adds(f32x4v (&acc)[GFM][GFN], const D
 
 // The k-rows panel of A^T: 32 k-rows of EXT floats.  One 1 KB copy fills a
 // group of RPI = 256 / EXT k-rows; groups lie GROUP bytes apart.  The lane
-// quarters read k-rows 4q + t together (t fixed), 16 floats each: PAD puts
-// them 16 banks apart (RPI k-rows of a group are contiguous, so rows 4 apart
-// in one group sit a multiple of 128 floats apart; with RPI = 8 the slots of
-// a group are permuted, k-row r at slot 2 (r % 4) + (r / 4) % 2, so that rows
-// 4 apart land in slots of opposite parity, 32 banks apart).
+// quarters read k-rows 4q + t together (t fixed), 16 floats each, which must
+// fall in four different quarters of the 64 banks.  Up to 4 k-rows a group,
+// PAD does it (the k-rows of a group are contiguous, so rows 4 apart in one
+// group sit a multiple of 128 floats apart); with 8 or 16 a group the slots
+// are permuted, k-row r at slot Q (r % 4) + (r / 4) % Q (Q = RPI / 4), so
+// that rows 4 apart land in slots that differ by one modulo Q: 32 banks
+// apart for 128-byte k-rows (plus PAD across groups), 16 for 64-byte ones.
 template <int EXT>
 struct KRowsPanel {
-    static_assert(EXT == 32 || EXT == 64 || EXT == 128 || EXT == 256, "panel extent");
+    static_assert(EXT == 16 || EXT == 32 || EXT == 64 || EXT == 128 || EXT == 256, "panel extent");
     static constexpr int RPI = 256 / EXT;
-    static constexpr int PAD = RPI == 1 ? 16 : RPI == 2 ? 32 : 64;
+    static constexpr int Q = RPI >= 8 ? RPI / 4 : 1;
+    static constexpr int PAD = RPI == 1 ? 16 : RPI == 2 ? 32 : RPI == 16 ? 0 : 64;
     static constexpr int GROUP = 1024 + PAD;
     static constexpr int BYTES = (32 / RPI) * GROUP;
-    __host__ __device__ static constexpr int slot(int r) { return RPI == 8 ? 2 * (r % 4) + (r / 4) % 2 : r; }
-    __host__ __device__ static constexpr int row_of_slot(int s) { return RPI == 8 ? s / 2 + 4 * (s % 2) : s; }
+    __host__ __device__ static constexpr int slot(int r) { return RPI >= 8 ? Q * (r % 4) + (r / 4) % Q : r; }
+    __host__ __device__ static constexpr int row_of_slot(int s) { return RPI >= 8 ? 4 * (s % Q) + s / Q : s; }
     // byte offset of float e of k-row kr
     __host__ __device__ static constexpr int at(int kr, int e) {
         return (kr / RPI) * GROUP + slot(kr % RPI) * EXT * 4 + 4 * e;

@@ -368,16 +368,16 @@ def test_heuristic_picks_the_measured_best(mode, shape, want):
 
 
 # Few rows with B stored N x K (op(B) = B^T) at K = N = 4096: the f32-panel
-# ring on 32 x 128 tiles (f16r 16.3-16.8 us against 19.3-22.0 on the few-rows
-# configuration at 1 to 16 rows, f32 19.0-19.5 against 19.4-20.7); with A
+# ring on 16 x 128 tiles (f16r 15.9-16.2 us against 19.3-21.9 on the few-rows
+# configuration at 1 to 16 rows, f32 18.2-18.5 against 19.3-20.6); with A
 # also stored transposed and M % 4 != 0 the ring does not take the call and
-# the few-rows configuration stays (f16r TT 1 row 18.8 us).
+# the few-rows configuration stays (f16r TT 1 row 18.9 us).
 @pytest.mark.parametrize("mode", ["f32", "f16r"])
 @pytest.mark.parametrize("M,ta,want", [
-    (1, False, "BM=32 BN=128 BK=32 ST=4 WM=2 WN=2 GM=8 KS=3"),
-    (16, False, "BM=32 BN=128 BK=32 ST=4 WM=2 WN=2 GM=8 KS=3"),
-    (8, True, "BM=32 BN=128 BK=32 ST=4 WM=2 WN=2 GM=8 KS=3"),
-    (2, True, "BM=16 BN=64 BK=64"),
+    (1, False, "BM=16 BN=128 BK=32 ST=4 WM=1 WN=2 GM=8 KS=3"),
+    (16, False, "BM=16 BN=128 BK=32 ST=4 WM=1 WN=2 GM=8 KS=3"),
+    (8, True, "BM=16 BN=128 BK=32 ST=4 WM=1 WN=2 GM=8 KS=3"),
+    (2, True, "BM=16 BN=64 BK=64 ST=1"),
 ])
 def test_heuristic_few_rows_with_b_transposed(mode, M, ta, want):
     g.cache_clear()
