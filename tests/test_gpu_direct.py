@@ -26,6 +26,7 @@ from tests.gpu_helpers import pinned, run, say, to_device  # noqa: E402
 DIRECT = ["BM=64 BN=64 BK=64 KS=3", "BM=32 BN=64 BK=64 KS=3", "BM=128 BN=128 BK=64 KS=3",
           "BM=64 BN=256 BK=64 KS=3",
           # f32 panels through a ring of direct-to-LDS copies, rounded as read
+          "BM=16 BN=128 BK=32 ST=4 WM=1 WN=2 KS=3",
           "BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 KS=3", "BM=32 BN=128 BK=32 ST=4 WM=2 WN=2 KS=3",
           "BM=64 BN=64 BK=32 ST=4 WM=4 WN=1 KS=3", "BM=64 BN=128 BK=32 ST=3 WM=2 WN=2 KS=3",
           "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 KS=3", "BM=128 BN=256 BK=32 ST=3 WM=2 WN=4 KS=3",

@@ -27,7 +27,8 @@ if not torch.cuda.is_available():   # collected on CPU-only hosts, never run the
 import gemm_tiled_amd as g  # noqa: E402
 from tests.gpu_helpers import pinned, run, say, to_device  # noqa: E402
 
-RINGS = ["BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 KS=3", "BM=32 BN=128 BK=32 ST=4 WM=2 WN=2 KS=3",
+RINGS = ["BM=16 BN=128 BK=32 ST=4 WM=1 WN=2 KS=3",
+         "BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 KS=3", "BM=32 BN=128 BK=32 ST=4 WM=2 WN=2 KS=3",
          "BM=64 BN=64 BK=32 ST=4 WM=4 WN=1 KS=3", "BM=64 BN=128 BK=32 ST=3 WM=2 WN=2 KS=3",
          "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 KS=3"]
 
@@ -104,7 +105,7 @@ def test_panel_ring_hands_other_shapes_to_split_k(M, N, K, lds, trans):
 def test_panel_ring_counters_reset_between_shapes():
     """Calls of different tile counts in a row share the arrival counters: each
     launch must leave every counter it used at zero."""
-    with pinned("f32", RINGS[2]):
+    with pinned("f32", RINGS[3]):
         for (M, N, K) in [(64, 4096, 4096), (200, 1024, 3008), (64, 4096, 4096), (20, 300, 8000)]:
             A, B, C = make_inputs(M, N, K, "normal", seed=M + N)
             say(f"[panel ring f32 counters] {M}x{N}x{K}")
