@@ -538,6 +538,14 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
         if (panels && mode == GEMM355_MODE_F16R && N >= 4 &&
             parse_config(mode, "BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 GM=8 KS=3", &thin))
             return thin;
+        // f32, at most 16 columns: the 16-row tile of the f32-panel ring on the
+        // transposed problem (4096 x 4..16 x 4096 in 18.3-18.7 us against
+        // 19.8-20.1 on the few-rows configuration's few-columns form), where
+        // that takes it
+        if (mode == GEMM355_MODE_F32 && N <= kRowsRows && !(rows.trans & 1) && rows.aligned() &&
+            K % 32 == 0 && ((rows.trans & 2) || N % 4 == 0) &&
+            parse_config(mode, "BM=16 BN=128 BK=32 ST=4 WM=1 WN=2 GM=8 KS=3", &thin))
+            return thin;
         if (N <= kRowsRows) return rows_config(mode);
         if (panels && parse_config(mode, mode == GEMM355_MODE_F32
                                              ? "BM=64 BN=64 BK=32 ST=4 WM=4 WN=1 GM=8 KS=3"
@@ -873,17 +881,52 @@ int launch_rows(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t 
                                      counts, s));
 }
 
+// Whether a KS=3 call runs as its transposed problem with C stored
+// transposed: the 16-row tile of the f32-panel ring, a C of at most 16
+// columns and more rows, A stored M x K, and a transposed problem the ring
+// takes (op(B)^T as A': 16-byte rows, and M' = N a multiple of 4 where it is
+// stored K x N).
+bool columns_form(const TileConfig& cfg, int trans, int64_t M, int64_t N, int64_t K,
+                  const float* A, int64_t lda, const float* B, int64_t ldb) {
+    const bool ta = (trans & 1) != 0, tb = (trans & 2) != 0;
+    return cfg.ks == 3 && cfg.bk == 32 && cfg.bm == 16 && N <= kRowsRows && M > kRowsRows && !ta &&
+           panel_ring_takes(!tb, true, B, ldb, A, lda, N, M, K);
+}
+
+// One KS=3 launch; tc: C stored transposed (the few-columns form).
+int run_direct(const TileConfig& cfg_in, int trans, int64_t M, int64_t N, int64_t K, float alpha,
+               const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+               int64_t ldc, hipStream_t s, uint16_t* C16, Scratch& sc, bool tc);
+
 // The configurations that round the operands as they stage them (KS=3), on
 // the grid of direct_grid.
 int launch_direct(const TileConfig& cfg_in, int trans, int64_t M, int64_t N, int64_t K,
                   float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
                   float beta, float* C, int64_t ldc, hipStream_t s, uint16_t* C16, Scratch& sc) {
     TileConfig cfg = cfg_in;
+    // The 16-row tile of the f32-panel ring runs a C of at most 16 columns
+    // and more rows as the transposed problem C^T = op(B)^T op(A)^T, whose few
+    // rows stream A (stored M x K, so op(A)^T is the ring's B^T layout, read
+    // in whole rows), with C stored transposed (the block-layout epilogue of
+    // that layout writes C^T[row][col] to C[col * ldc + row]).
+    if (columns_form(cfg, trans, M, N, K, A, lda, B, ldb)) {
+        const bool tb_in = (trans & 2) != 0;
+        return run_direct(cfg, (tb_in ? 0 : 1) | 2, N, M, K, alpha, B, ldb, A, lda, beta, C, ldc,
+                          s, C16, sc, true);
+    }
+    return run_direct(cfg, trans, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s, C16, sc, false);
+}
+
+int run_direct(const TileConfig& cfg_in, int trans, int64_t M, int64_t N, int64_t K, float alpha,
+               const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+               int64_t ldc, hipStream_t s, uint16_t* C16, Scratch& sc, bool tc) {
+    TileConfig cfg = cfg_in;
     const bool ta = (trans & 1) != 0, tb = (trans & 2) != 0;
     // the f32-panel ring (BK = 32) hands the shapes it does not take to the
     // register-staged kernel of the 64 x 64 tile (f16r) or to the split-K
     // tiles (f32)
     if (cfg.bk == 32 && !panel_ring_takes(ta, tb, A, lda, B, ldb, M, N, K)) {
+        if (tc) return GEMM355_ERR_CONFIG;   // columns_form checked the transposed problem
         if (cfg.mode == GEMM355_MODE_F32)
             return launch_splitk(splitk_config(cfg.mode), trans, M, N, K, alpha, A, lda, B, ldb,
                                  beta, C, ldc, s, C16, sc);
@@ -916,7 +959,7 @@ int launch_direct(const TileConfig& cfg_in, int trans, int64_t M, int64_t N, int
     DirectArgs a{A, B, C, C16, nullptr, nullptr, lda, ldb, ldc, static_cast<int>(M),
                  static_cast<int>(N), static_cast<int>(K), alpha, beta,
                  static_cast<int>(tiles_m), static_cast<int>(tiles_n),
-                 static_cast<int>(depth), static_cast<int>(slices)};
+                 static_cast<int>(depth), static_cast<int>(slices), tc};
     if (slices > 1) {
         void* ws = nullptr;
         int rc = sc.workspace(static_cast<size_t>(slices * tiles * tile_bytes), &ws);
@@ -1495,7 +1538,9 @@ int gemm355_get_plan_ex(int mode, int transa, int transb, int64_t M, int64_t N, 
     std::string form;
     if (cfg.ks == 1) form = "split-k";
     else if (cfg.ks == 2) form = N <= kRowsRows && M > kRowsRows ? "columns" : "rows";
-    else if (cfg.ks == 3) form = mode == GEMM355_MODE_F16R ? "round-on-load" : "panel-ring";
+    else if (cfg.ks == 3)
+        form = std::string(mode == GEMM355_MODE_F16R ? "round-on-load" : "panel-ring") +
+               (columns_form(cfg, trans, M, N, K, aligned, lda, aligned, ldb) ? "-columns" : "");
     else if (mode == GEMM355_MODE_F16R) form = (b.mb % cfg.bm || b.nb % cfg.bn) ? "packed-masked" : "packed";
     else if (is_f32_ring(cfg) && !rows.none())
         form = rows.aligned() && b.mb % cfg.bm == 0 && b.nb % cfg.bn == 0 && b.kb % 16 == 0

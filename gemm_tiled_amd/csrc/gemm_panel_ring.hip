@@ -303,6 +303,71 @@ __device__ __forceinline__ void store_tile_dealt(const f32x4v (&acc)[GFM][GFN], 
     }
 }
 
+// Epilogue of the 16 x 16 blocks into a C stored transposed (the few-columns
+// form: this workgroup computes C^T): element e of lane (q, r16) in block
+// (i, j) is C^T[row][col] with row = row0 + 16 i + 4 q + e, col = col0 + 16 j
+// + r16, stored at C[col * ldc + row], so a lane's four elements of a block
+// are four consecutive floats (binary16 values), one 16-byte (8-byte) access
+// when the rows of C allow it and all four lie inside.  Same value as the
+// other epilogues: fma(alpha, acc, beta*c), beta == 0 never reads C.
+template <int GFM, int GFN, bool OUT16, typename CT>
+__device__ __forceinline__ void store_tile_t(const f32x4v (&acc)[GFM][GFN], CT* __restrict__ C,
+                                             int64_t ldc, int row0, int col0, int M, int N,
+                                             float alpha, float beta, int lane) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const int q = lane >> 4, r16 = lane & 15;
+    auto h2f = [](uint32_t bits) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+    };
+    const bool vec = ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(C) & (OUT16 ? 7 : 15)) == 0;
+#pragma unroll
+    for (int i = 0; i < GFM; ++i)
+#pragma unroll
+        for (int j = 0; j < GFN; ++j) {
+            const int row = row0 + 16 * i + 4 * q, col = col0 + 16 * j + r16;
+            if (col >= N || row >= M) continue;
+            CT* at = C + (int64_t)col * ldc + row;
+            if (vec && row + 3 < M) {
+                f32x4v old = f32x4v{0.f, 0.f, 0.f, 0.f};
+                if (beta != 0.f) {
+                    if constexpr (OUT16) {
+                        const u32x2 w = *reinterpret_cast<const u32x2*>(at);
+                        old = f32x4v{h2f(w[0] & 0xffffu), h2f(w[0] >> 16), h2f(w[1] & 0xffffu),
+                                     h2f(w[1] >> 16)};
+                    } else {
+                        old = *reinterpret_cast<const f32x4v*>(at);
+                    }
+                }
+                f32x4v out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    out[e] = beta == 0.f ? alpha * acc[i][j][e]
+                                         : __builtin_fmaf(alpha, acc[i][j][e], beta * old[e]);
+                if constexpr (OUT16) {
+                    u32x2 w;
+                    w[0] = uint32_t{f32_to_f16_bits(out[0])} | (uint32_t{f32_to_f16_bits(out[1])} << 16);
+                    w[1] = uint32_t{f32_to_f16_bits(out[2])} | (uint32_t{f32_to_f16_bits(out[3])} << 16);
+                    *reinterpret_cast<u32x2*>(at) = w;
+                } else {
+                    *reinterpret_cast<f32x4v*>(at) = out;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (row + e >= M) break;
+                    const float a = acc[i][j][e];
+                    if constexpr (OUT16) {
+                        const float v = beta == 0.f ? alpha * a
+                                                    : __builtin_fmaf(alpha, a, beta * h2f(at[e]));
+                        at[e] = f32_to_f16_bits(v);
+                    } else {
+                        at[e] = beta == 0.f ? alpha * a : __builtin_fmaf(alpha, a, beta * at[e]);
+                    }
+                }
+            }
+        }
+}
+
 // F16: round to binary16 and multiply on v_mfma_f32_16x16x32_f16 (f16r);
 // otherwise multiply the f32 values on v_mfma_f32_16x16x4_f32, eight steps a
 // panel, step s taking from lane quarter q the s-th of its eight k (so the
@@ -510,12 +575,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_ring_kernel(DirectArg
     if (p.slices > 1 && !last_slice_adds<GFM, GFN, BM * BN * 4>(acc, p, wave, lane, ring)) return;
     const int row0 = m0 + wr * S::TM, col0 = n0 + wc * S::TN;
     if constexpr (TB) {
-        if constexpr (OUT16)
+        if (p.tc) {
+            if constexpr (OUT16)
+                store_tile_t<GFM, GFN, true>(acc, p.C16, p.ldc, row0, col0, p.M, p.N, p.alpha,
+                                             p.beta, lane);
+            else
+                store_tile_t<GFM, GFN, false>(acc, p.C, p.ldc, row0, col0, p.M, p.N, p.alpha,
+                                              p.beta, lane);
+        } else if constexpr (OUT16) {
             store_tile_m16<GFM, GFN, MASKED, true>(acc, p.C16, p.ldc, row0, col0, p.M, p.N, p.alpha,
                                                    p.beta, lane);
-        else
+        } else {
             store_tile_m16<GFM, GFN, MASKED, false>(acc, p.C, p.ldc, row0, col0, p.M, p.N, p.alpha,
                                                     p.beta, lane);
+        }
     } else if constexpr (OUT16) {
         store_tile_dealt<GFM, GFN, MASKED, true>(acc, p.C16, p.ldc, row0, col0, p.M, p.N, p.alpha,
                                                  p.beta, lane);
@@ -547,7 +620,7 @@ template <int BM, int BN, int NS, int WM, int WN, int GM, bool F16>
 hipError_t launch_panel_ring(const DirectArgs& a, bool ta, bool tb, bool masked, hipStream_t s) {
     // the host hands only the shapes this kernel takes (panel_ring_takes)
     if ((!tb && a.N % 4 != 0) || (ta && a.M % 4 != 0) || a.K % 32 != 0 || a.depth % 32 != 0 ||
-        a.K <= 0 || (!F16 && a.C16))
+        a.K <= 0 || (!F16 && a.C16) || (a.tc && !tb))
         return hipErrorInvalidValue;
     if (ta && tb) return launch_panel_ring_layout<BM, BN, NS, WM, WN, GM, F16, true, true>(a, masked, s);
     if (ta) return launch_panel_ring_layout<BM, BN, NS, WM, WN, GM, F16, true, false>(a, masked, s);

@@ -190,6 +190,7 @@ struct DirectArgs {
     float alpha, beta;
     int tiles_m, tiles_n;
     int depth, slices;
+    bool tc = false;   // C stored transposed: element (row, col) at C[col * ldc + row]
 };
 using DirectLaunch = hipError_t (*)(const DirectArgs&, bool ta, bool tb, bool masked, hipStream_t);
 struct DirectInstance {

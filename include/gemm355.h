@@ -210,7 +210,9 @@ int gemm355_get_config_ex(int mode, int transa, int transb, int64_t M, int64_t N
  * register-staged f32 kernel), packed / packed-masked (the f16r packing pass
  * and binary16 kernel, masked stores at ragged edges), split-k, rows,
  * columns (the few-rows configuration run on the transposed problem for a C
- * of at most 16 columns), round-on-load, panel-ring.  The block is the part
+ * of at most 16 columns), round-on-load, panel-ring, and round-on-load-columns
+ * / panel-ring-columns (the 16-row tile of the f32-panel ring run on the
+ * transposed problem for a C of at most 16 columns, A stored M x K).  The block is the part
  * of C (MB x NB, over the first KB of K) that configuration runs itself; when
  * it is smaller than the call (the f32 ring, plain layout only), the right
  * strip, the bottom strip and the k tail run in the few-rows (or
@@ -233,7 +235,9 @@ int gemm355_get_plan_ex(int mode, int transa, int transb, int64_t M, int64_t N, 
  * split over workgroups and the slices added in order by the tile's last
  * workgroup, the operands staged as f32 panels from a ring of direct-to-LDS
  * copies (BK=32, both modes; in f16r rounded to binary16 as the fragments
- * are read, with no packing pass) or, in f16r only, rounded to binary16
+ * are read, with no packing pass; its 16-row tile runs a C of at most 16
+ * columns and more rows, with A stored M x K, as the transposed problem with
+ * C stored transposed) or, in f16r only, rounded to binary16
  * through registers (BK=64).  A ring configuration (direct-to-LDS copies)
  * that a call's row alignment or shape rules out runs that call in a
  * register-staged kernel instead: the f32 one of the same tile, BM=64 BN=64

@@ -294,8 +294,12 @@ def test_plan_names_the_path_and_the_ring_block():
     finally:
         g.set_config("f32", None)
     assert g.get_plan("f32", 8, 4096, 4096) == "form=rows block=8x4096x4096"
-    # a few columns: the few-rows configuration on the transposed problem
-    assert g.get_plan("f32", 4096, 8, 4096) == "form=columns block=4096x8x4096"
+    # a few columns: the few-rows configuration on the transposed problem, or
+    # (f32, A stored M x K, N % 4 == 0 or B stored N x K) the 16-row tile of the
+    # f32-panel ring on it
+    assert g.get_plan("f32", 4096, 2, 4096) == "form=columns block=4096x2x4096 rows=4-byte"
+    assert g.get_plan("f32", 4096, 8, 4096) == "form=panel-ring-columns block=4096x8x4096"
+    assert g.get_plan("f32", 4096, 8, 4096, transa=True) == "form=columns block=4096x8x4096"
     assert g.get_plan("f16r", 4096, 1, 4096) == "form=columns block=4096x1x4096 rows=4-byte"
     # 16-byte rows with N and K multiples of 4: the masked ring whole (16-byte copies)
     assert g.get_plan("f32", 4000, 4000, 4000) == "form=ring-masked block=4000x4000x4000"
@@ -315,11 +319,13 @@ HEURISTIC_PICKS = [
     # 128 rows: 64 x 64, 42 against 54 us; 256 rows: 64 x 128, 73 against 79)
     ("f32", (16, 4096, 4096), "BM=16 BN=64 BK=64"),
     # few columns (M = K = 4096): f32 the same configuration on the
-    # transposed problem up to 16 columns (4096 x 16 x 4096 in 20 us against
+    # transposed problem for one or two columns (18.7 us), from 4 to 16 the
+    # f32-panel ring's 16-row tile on it (18.3-18.5 us against 19.8-20.1;
     # 81 us on the 128 x 256 ring), then the f32-panel ring on 64 x 64 tiles
     # (26 us at 64 columns); f16r the transposed form for one or two columns
     # (18.5 us), the f32-panel ring on 32 x 64 tiles from 4 (16 us against 21)
-    ("f32", (4096, 16, 4096), "BM=16 BN=64 BK=64"),
+    ("f32", (4096, 2, 4096), "BM=16 BN=64 BK=64"),
+    ("f32", (4096, 16, 4096), "BM=16 BN=128 BK=32 ST=4 WM=1 WN=2 GM=8 KS=3"),
     ("f32", (4096, 64, 4096), "BM=64 BN=64 BK=32 ST=4 WM=4 WN=1 GM=8 KS=3"),
     ("f16r", (4096, 1, 4096), "BM=16 BN=64 BK=64"),
     ("f16r", (4096, 16, 4096), "BM=32 BN=64 BK=32 ST=4 WM=2 WN=1 GM=8 KS=3"),

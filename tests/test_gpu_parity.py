@@ -289,6 +289,73 @@ def test_columns_f16_output():
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
 
 
+# The few-columns form of the f32-panel ring's 16-row tile: C with at most 16
+# columns and more rows, A stored M x K, runs as C^T = op(B)^T op(A)^T on the
+# ring (op(A)^T read as B^T, whole rows per copy) with C stored transposed.
+PR16 = "BM=16 BN=128 BK=32 ST=4 WM=1 WN=2 KS=3"
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("M,N,K,lds,tb", [
+    (4096, 16, 4096, {}, False),
+    (4096, 4, 4096, {}, False),
+    (1000, 8, 1024, {}, False),                             # ragged M (a partial 128-column tile)
+    (4100, 12, 1024, {"lda": 1028, "ldc": 13}, False),      # padded lda, odd ldc: element stores
+    (300, 3, 64, {}, True),                                 # B stored N x K: any N
+    (2052, 13, 2048, {"ldc": 16}, True),
+])
+def test_panel_ring_columns_against_the_oracle(mode, M, N, K, lds, tb):
+    A, B, C = make_inputs(M, N, K, "normal", seed=24, **lds)
+    tA = to_device(A)
+    tB = to_device(np.ascontiguousarray(B.T) if tb else B)
+    tC0 = to_device(C)
+    with pinned(mode, PR16):
+        plan = g.get_plan(mode, M, N, K, beta=-0.5, transb=tb, **lds)
+        assert plan.split()[0] in ("form=panel-ring-columns", "form=round-on-load-columns"), plan
+        say(f"[panel-ring columns] {mode} tb={tb} {M}x{N}x{K} {lds}")
+        outs = []
+        for _ in range(2):
+            tC = tC0.clone()
+            g.gemm(mode, tA, tB, tC, 1.25, -0.5, transb=tb)
+            torch.cuda.synchronize()
+            outs.append(tC.cpu().numpy())
+    assert_parity(mode, A, B, C, 1.25, -0.5, outs[0])
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("N", [4, 16])
+def test_panel_ring_columns_small_integers_exact_and_beta_zero(mode, N):
+    M, K = 2048, 4096
+    A, B, C = small_integers(M, N, K, seed=25)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    with pinned(mode, PR16):
+        assert g.get_plan(mode, M, N, K, beta=0.5).split()[0].endswith("-columns")
+        say(f"[panel-ring columns exact] {mode} {M}x{N}x{K}")
+        got = run(mode, A, B, C, -2.0, 0.5)
+        assert np.array_equal(got, (-2.0 * exact + 0.5 * C.astype(np.float64)).astype(np.float32))
+        Cn = np.full((M, N), np.nan, dtype=np.float32)
+        got = run(mode, A, B, Cn, 1.0, 0.0)
+        assert np.array_equal(got, exact.astype(np.float32))
+
+
+def test_panel_ring_columns_f16_output():
+    M, N, K = 2048, 12, 4096
+    A, B, C = make_inputs(M, N, K, "normal", seed=26)
+    C16 = C.astype(np.float16)
+    tA, tB = to_device(A), to_device(B)
+    t16 = torch.from_numpy(C16.copy()).to("cuda")
+    t32 = to_device(C16.astype(np.float32))
+    with pinned("f16r", PR16):
+        say(f"[panel-ring columns f16-out] {M}x{N}x{K}")
+        g.gemm_f16r_f16out(tA, tB, t16, 0.75, -0.25)
+        g.gemm("f16r", tA, tB, t32, 0.75, -0.25)
+        torch.cuda.synchronize()
+    want = t32.cpu().numpy().astype(np.float16)
+    got = t16.cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
 def test_rows_f16_output():
     M, N, K = 12, 2048, 4096
     A, B, C = make_inputs(M, N, K, "normal", seed=18)
