@@ -556,8 +556,19 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
     if (N <= kRowsRows) return rows_config(mode);
     // (from 512 rows on the packed path wins once N x K is large: 768 x 4096^2
     // 60 us packed against 79 us on the ring, 1024 x 8192^2 193 against 220)
+    // (and, measured, where the packed tiles are too few for a deep K, which
+    // the ring splits over workgroups -- M N <= 2^21, min(M, N) <= 1280, K >=
+    // 4096: 1024 x 2048 x 4096 41 us against 56, 1280^2 x 4096 49 against 54,
+    // 1280^2 x 8192 80 against 95; not 1448^2 x 4096, 60 against 47 on the
+    // packed path -- or where K is so shallow that the packing pass dominates
+    // -- K <= 512 with M, N <= 2048: 2048^2 x 512 12.8 us against 18.8,
+    // 2048^2 x 256 8.5 against 15.2; at K = 1024-2048 the packed path held
+    // its own or won: 1448^2 x 2048 29 against 39 us, 1792^2 x 1024 23
+    // against 27)
     if (panels && mode == GEMM355_MODE_F16R &&
-        (M <= kRingRows || (M <= 2 * kRingRows && N * K <= (int64_t{1} << 22))))
+        (M <= kRingRows || (M <= 2 * kRingRows && N * K <= (int64_t{1} << 22)) ||
+         (M * N <= (int64_t{1} << 21) && std::min(M, N) <= 1280 && K >= 4096) ||
+         (K <= 512 && M <= 2048 && N <= 2048)))
         return panel_ring_config(mode, M, N, K);
     if (panels && mode == GEMM355_MODE_F32 &&
         (M <= kPanelRowsF32 || (M <= 4 * kPanelRowsF32 && N * K <= (int64_t{1} << 21))))

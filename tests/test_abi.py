@@ -347,6 +347,14 @@ HEURISTIC_PICKS = [
     # 17.5 us against 24 us before it; 512 rows: 128 x 256, 38 against 54)
     ("f16r", (64, 4096, 4096), "BM=32 BN=64 BK=32 ST=4"),
     ("f16r", (512, 4096, 4096), "BM=128 BN=256 BK=32 ST=3"),
+    # f16r, few packed tiles for a deep K or a shallow K that the packing pass
+    # dominates: the f32-panel ring (A/B of the library before and after the
+    # rule: 1024 x 2048 x 4096 41 us against 56, 1024^2 x 8192 48 against 75,
+    # 2048^2 x 512 12.8 against 18.8); 1448^2 x 4096 stays packed (49 us
+    # against 60 on the ring)
+    ("f16r", (1024, 2048, 4096), "BM=128 BN=256 BK=32 ST=3 WM=2 WN=4 GM=8 KS=3"),
+    ("f16r", (2048, 2048, 512), "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3"),
+    ("f16r", (1448, 1448, 4096), "BM=128 BN=128 BK=32 ST=5"),
     # f16r mid sizes on the packed path (every half-depth ring timed pinned;
     # the pick within 2.3% of the fastest): 128^2 60 us at 1024 x 4096^2,
     # 100 at 2048^2 x 8192 and 194 at 4352^3 (256 x 128 70, 119 and 205);
