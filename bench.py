@@ -802,8 +802,8 @@ def shape_sweep(g, torch, dev, out, repeats):
 # The untuned choice (the phobos "gemm, f32" page, "Tuning": the best tile
 # depends on the card and the sizes).  At each shape every configuration the
 # heuristic weighs there is timed pinned -- in f32 every one that does not
-# split K for few rows, in f16r the half-depth rings -- and the library's own
-# choice without tuning is set beside the fastest.
+# split K for few rows, in f16r the half-depth rings and the f32-panel ring --
+# and the library's own choice without tuning is set beside the fastest.
 # ---------------------------------------------------------------------------
 CHOICE_SHAPES = {
     "f32": [(n, n, n) for n in (1024, 1536, 1792, 2048, 2304, 2560, 2816, 3072, 3328, 3584,
@@ -820,14 +820,20 @@ CHOICE_SHAPES = {
             [(768, 4096, 4096), (1024, 4096, 4096), (1280, 4096, 4096), (1536, 4096, 4096),
              (2048, 4096, 4096), (3072, 4096, 4096), (2048, 2048, 8192), (4096, 4096, 1024),
              (8192, 8192, 2048), (4096, 8192, 4096), (1024, 8192, 8192), (3000, 5000, 2000),
-             (1000, 8000, 4000), (2000, 3000, 1000)],
+             (1000, 8000, 4000), (2000, 3000, 1000),
+             # small products: few packed tiles for a deep K, or a shallow K
+             (1024, 2048, 4096), (1280, 1280, 4096), (1024, 1024, 8192), (1448, 1448, 4096),
+             (1280, 1280, 2048), (1536, 1536, 1024), (2048, 2048, 512), (1280, 1024, 512),
+             (2048, 2048, 1024)],
 }
 
 
 def _choice_candidates(g, mode):
     if mode == "f32":
         return [c for c in g.list_configs(mode) if "KS=1" not in c and "KS=2" not in c]
-    return [c for c in g.list_configs(mode) if "BK=32" in c and "KS=" not in c]
+    # the half-depth rings of the packed path and the f32-panel ring that
+    # rounds on load (no packing pass)
+    return [c for c in g.list_configs(mode) if "BK=32" in c and ("KS=" not in c or "KS=3" in c)]
 
 
 def choice_study(g, torch, dev, out, repeats):
@@ -890,7 +896,8 @@ def choice_study(g, torch, dev, out, repeats):
              f"{repeats} shuffled rounds, each the median of event-timed calls over 0.04 s after "
              "warming the clocks (calls under 0.2 ms in batches).  Candidates: in f32 every "
              "configuration that does not split K for few rows (the rings, the register-staged "
-             "tiles and the f32-panel ring), in f16r the half-depth rings.  `ratio` is the "
+             "tiles and the f32-panel ring), in f16r the half-depth rings of the packed path and "
+             "the f32-panel ring that rounds on load.  `ratio` is the "
              "untuned choice's time over the fastest candidate's.", ""]
     for mode in ("f32", "f16r"):
         sel = [r for r in rows if r["mode"] == mode]
