@@ -127,7 +127,7 @@ def test_capture_without_scratch_fails_and_launches_nothing():
     """A new stream holds no scratch: capturing an f16r call on it (which
     needs its packed operands) must return GEMM355_ERR_CAPTURE (-106) and
     leave C untouched; the same call runs eagerly afterwards."""
-    M, N, K = 1280, 384, 512    # the packed path: its binary16 operands live in scratch
+    M, N, K = 1280, 384, 1024   # the packed path: its binary16 operands live in scratch
     assert g.get_plan("f16r", M, N, K, beta=0.5).startswith("form=packed")
     A, B, C = make_inputs(M, N, K, "uniform", seed=81)
     tA, tB, tC = to_device(A), to_device(B), to_device(C)
