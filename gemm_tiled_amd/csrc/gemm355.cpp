@@ -318,15 +318,17 @@ RingSk ring_sk(const TileConfig& c, int64_t M, int64_t N, int64_t K) {
 // half-depth ring with eight waves, fitted (with the rest of the f16r cost
 // in whole_cost) to timings: 256^2 with four waves 0.85, 256 x 128 and
 // 128 x 256 with eight 0.93, 128^2 (two workgroups per CU) with four 0.86
-// and with eight 0.82.  Others by their reuse r = BM BN /
+// and with eight 0.87 on a grid of at most one round (512 tiles), 0.85 on a
+// larger one (eight waves 0.6-7% faster at 9 of 10 shapes of 100-256 tiles,
+// the tenth even, 0.4-1.3% slower at 4 of 5 of 676-3025).  Others by their reuse r = BM BN /
 // (BM + BN) as r / (r + 85) against the 256^2 tile's, the full-depth panels at
 // 1 / 1.2 of that (the half-depth ring at a tile ran 1.1-1.4 times faster).
-double f16_efficiency(const TileConfig& c) {
+double f16_efficiency(const TileConfig& c, double tiles) {
     const int waves = c.wm * c.wn;
     if (is_f16_ring(c)) {
         if (c.bm == 256 && c.bn == 256) return waves == 8 ? 1.0 : 0.85;
         if (c.bm * c.bn == 256 * 128 && waves == 8) return 0.93;
-        if (c.bm == 128 && c.bn == 128) return waves == 8 ? 0.82 : 0.86;
+        if (c.bm == 128 && c.bn == 128) return waves != 8 ? 0.86 : tiles <= 512 ? 0.87 : 0.85;
     }
     const double r = static_cast<double>(c.bm) * c.bn / (c.bm + c.bn);
     const double rel = (r / (r + 85.0)) / (128.0 / (128.0 + 85.0));
@@ -364,7 +366,7 @@ double whole_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, RingRows
         // ring configurations timed pinned at 43 shapes from 768 x 4096^2 to
         // 8192^3, 15 of them ragged: the pick within 2.4% of the fastest at
         // all but 2048^3 (3%) and 7000^3 (4.2%).
-        const double t_tile = c.bm * c.bn * kpad / f16_efficiency(c);
+        const double t_tile = c.bm * c.bn * kpad / f16_efficiency(c, tiles);
         if (sk.q > 0) {
             // in runs the 256^2 tile with 2 x 4 waves was 1-5% faster than
             // with 4 x 2 (6144^3 448 against 469 us; the stream-K form of the
