@@ -824,7 +824,8 @@ CHOICE_SHAPES = {
              # small products: few packed tiles for a deep K, or a shallow K
              (1024, 2048, 4096), (1280, 1280, 4096), (1024, 1024, 8192), (1448, 1448, 4096),
              (1280, 1280, 2048), (1536, 1536, 1024), (2048, 2048, 512), (1280, 1024, 512),
-             (2048, 2048, 1024)],
+             (2048, 2048, 1024), (1792, 1792, 1024), (1448, 1448, 2048), (1024, 1024, 2048),
+             (2048, 1024, 2048), (1280, 1280, 1024)],
 }
 
 

@@ -451,12 +451,22 @@ double estimated_cost(const TileConfig& c, int64_t M, int64_t N, int64_t K, Ring
 }
 
 // The grid of a KS=3 launch: its tiles, the workgroups a CU holds at once
-// (the LDS of the stages, at most four waves per SIMD), and K in slices so
-// that the grid reaches one round of resident workgroups, each slice at least
-// kDirectMinDepth deep (a multiple of the panel depth), the partial tiles
-// within kSplitKMaxBytes.
+// (the LDS of the stages, at most four waves per SIMD), and K in slices, each
+// at least kDirectMinDepth deep (a multiple of the panel depth), the partial
+// tiles within kSplitKMaxBytes.  Up to `reach` slices would take the grid to
+// one round of resident workgroups; of 1..reach the count taken is the one
+// that loads the busiest CU least (workgroups a CU x slice depth), on a tie
+// the fewer slices where one workgroup fills a CU and the more where several
+// share one (they hide each other's latency).  A grid of one-workgroup tiles
+// that cannot fill the CUs evenly so runs as one round of deeper slices
+// rather than a full round and a part-filled second one: f16r 128^2,
+// 1536^2 x 1024 (144 tiles) and 1792^2 x 1024 (196) in 18.7 and 20.0 us
+// against 25.9 and 28.6 on 288 and 392 workgroups of half depth; 128 x 256 at
+// 1280^2 x 4096 (50 tiles) 37.4 on 5 slices against 48.3 on 6.  f32 64 x 128
+// (two workgroups a CU) at 768 x 4096^2 keeps its 768 workgroups: on 384 it
+// ran in 260 us against 207.
 struct DirectGrid {
-    int64_t tiles_m, tiles_n, per_cu, slices, depth;
+    int64_t tiles_m, tiles_n, per_cu, slices, depth, reach;
 };
 DirectGrid direct_grid(const TileConfig& cfg, int64_t M, int64_t N, int64_t K) {
     DirectGrid d{};
@@ -467,9 +477,17 @@ DirectGrid direct_grid(const TileConfig& cfg, int64_t M, int64_t N, int64_t K) {
                                            : 2 * int64_t{cfg.bm + cfg.bn} * 128;
     d.per_cu = std::max<int64_t>(1, std::min<int64_t>((160 * 1024) / lds_bytes, 4 * 4 / (cfg.wm * cfg.wn)));
     const int64_t tile_bytes = int64_t{cfg.bm} * cfg.bn * 4;
-    int64_t slices = std::max<int64_t>(1, (kCUs * d.per_cu + tiles - 1) / tiles);
-    slices = std::min(slices, std::max<int64_t>(1, K / kDirectMinDepth));
-    slices = std::min(slices, std::max<int64_t>(1, kSplitKMaxBytes / (tiles * tile_bytes)));
+    const int64_t round = kCUs * d.per_cu;   // resident workgroups
+    int64_t reach = std::max<int64_t>(1, (round + tiles - 1) / tiles);
+    reach = std::min(reach, std::max<int64_t>(1, K / kDirectMinDepth));
+    reach = std::min(reach, std::max<int64_t>(1, kSplitKMaxBytes / (tiles * tile_bytes)));
+    d.reach = reach;
+    int64_t slices = 1;
+    for (int64_t s = 2; s <= reach; ++s) {   // busiest CU, K as the unit: ceil(tiles s / CUs) / s
+        const int64_t load_s = (tiles * s + kCUs - 1) / kCUs * slices;
+        const int64_t load_best = (tiles * slices + kCUs - 1) / kCUs * s;
+        if (load_s < load_best || (load_s == load_best && d.per_cu > 1)) slices = s;
+    }
     d.depth = round_up((K + slices - 1) / slices, cfg.bk);
     d.slices = (K + d.depth - 1) / d.depth;
     return d;
@@ -480,7 +498,8 @@ DirectGrid direct_grid(const TileConfig& cfg, int64_t M, int64_t N, int64_t K) {
 // f16r: 32 x 64 up to 64 rows, 64 x 64 up to 160, 128 x 128 up to 256,
 // 128 x 256 beyond; f32: 32 x 128 up to 32 rows, 64 x 64 up to 128, 64 x 128
 // beyond -- then a smaller tile of the mode's ladder while the call's
-// workgroups (tiles x K slices) would not fill one round of the CUs (f16r) or
+// workgroups (tiles x the most K slices it could take, the reach of
+// direct_grid) would not fill one round of the CUs (f16r) or
 // half a round (f32: there 32 x 128 at 17 rows, 256 workgroups, beat 32 x 64
 // with 512, 21 against 27 us, while f16r's 1024^3 took 64 x 64 at 13 us over
 // 128 x 128's half round at 16 us).
@@ -499,7 +518,7 @@ TileConfig panel_ring_config(int mode, int64_t M, int64_t N, int64_t K) {
     for (; i >= 0; --i) {
         parse_config(mode, ladder[i], &c);
         const DirectGrid d = direct_grid(c, M, N, K);
-        if (fill * d.tiles_m * d.tiles_n * d.slices >= kCUs * d.per_cu) break;
+        if (fill * d.tiles_m * d.tiles_n * d.reach >= kCUs * d.per_cu) break;
     }
     return c;
 }
@@ -559,19 +578,35 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
     // (from 512 rows on the packed path wins once N x K is large: 768 x 4096^2
     // 60 us packed against 79 us on the ring, 1024 x 8192^2 193 against 220)
     // (and, measured, where the packed tiles are too few for a deep K, which
-    // the ring splits over workgroups -- M N <= 2^21, min(M, N) <= 1280, K >=
-    // 4096: 1024 x 2048 x 4096 41 us against 56, 1280^2 x 4096 49 against 54,
-    // 1280^2 x 8192 80 against 95; not 1448^2 x 4096, 60 against 47 on the
-    // packed path -- or where K is so shallow that the packing pass dominates
-    // -- K <= 512 with M, N <= 2048: 2048^2 x 512 12.8 us against 18.8,
-    // 2048^2 x 256 8.5 against 15.2; at K = 1024-2048 the packed path held
-    // its own or won: 1448^2 x 2048 29 against 39 us, 1792^2 x 1024 23
-    // against 27)
+    // the ring splits over workgroups -- K >= 4096 with M N <= 2^21 and
+    // min(M, N) <= 1280, or M, N <= 1536: 1024 x 2048 x 4096 39 us against
+    // 56, 1280^2 x 4096 36 against 45, 1448^2 x 4096 43 against 46, 1536^2 x
+    // 4096 42 against 44; not 1792^2 x 4096, 54 against 46 on the packed
+    // path, nor 768 x 4096^2, 60 against 52, and even at 1800 x 1280 x 4096
+    // -- or where K is so shallow that the packing pass dominates -- K <= 512
+    // with M, N <= 2048: 2048^2 x 512 12.8 us against 18.8, 2048^2 x 256 8.5
+    // against 15.2)
+    const bool deep_few = K >= 4096 && ((M * N <= (int64_t{1} << 21) && std::min(M, N) <= 1280) ||
+                                        std::max(M, N) <= 1536);
     if (panels && mode == GEMM355_MODE_F16R &&
-        (M <= kRingRows || (M <= 2 * kRingRows && N * K <= (int64_t{1} << 22)) ||
-         (M * N <= (int64_t{1} << 21) && std::min(M, N) <= 1280 && K >= 4096) ||
+        (M <= kRingRows || (M <= 2 * kRingRows && N * K <= (int64_t{1} << 22)) || deep_few ||
          (K <= 512 && M <= 2048 && N <= 2048)))
         return panel_ring_config(mode, M, N, K);
+    // f16r, K = 513-2048: the 128^2 f32-panel ring where its grid, counted
+    // in 1024-deep slices, fits one round of the CUs (each tile then runs
+    // whole or in slices of at most 1024 in one round, with no packing pass):
+    // 1.07-1.37 times the packed path's speed at 17 shapes, K = 640-1024 and
+    // 100-256 tiles (1280^2 x 1024 16.2 us against 20.6, 2048^2 x 1024 21.9
+    // against 26.4, 4096 x 1024^2 21.8 against 26.0), K = 1536-2048 and
+    // 80-128 tiles (1280^2 x 2048 23.1 against 27.7).  Where a tile runs a
+    // whole K of 2048 the packed path wins: 1792^2 x 2048 28.2 against 31.8,
+    // 2048^2 x 2048 31.1 against 33.1.
+    if (panels && mode == GEMM355_MODE_F16R && K > 512 && K <= 2048 &&
+        ((M + 127) / 128) * ((N + 127) / 128) * ((K + 1023) / 1024) <= kCUs) {
+        TileConfig c{};
+        parse_config(mode, "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3", &c);
+        return c;
+    }
     if (panels && mode == GEMM355_MODE_F32 &&
         (M <= kPanelRowsF32 || (M <= 4 * kPanelRowsF32 && N * K <= (int64_t{1} << 21))))
         return panel_ring_config(mode, M, N, K);

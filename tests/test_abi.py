@@ -350,24 +350,32 @@ HEURISTIC_PICKS = [
     # f16r, few packed tiles for a deep K or a shallow K that the packing pass
     # dominates: the f32-panel ring (A/B of the library before and after the
     # rule: 1024 x 2048 x 4096 41 us against 56, 1024^2 x 8192 48 against 75,
-    # 2048^2 x 512 12.8 against 18.8); 1448^2 x 4096 stays packed (49 us
-    # against 60 on the ring)
+    # 2048^2 x 512 12.8 against 18.8, 1448^2 x 4096 43 against 46); 1792^2 x
+    # 4096 stays packed (46 us against 54 on the ring)
     ("f16r", (1024, 2048, 4096), "BM=128 BN=256 BK=32 ST=3 WM=2 WN=4 GM=8 KS=3"),
     ("f16r", (2048, 2048, 512), "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3"),
-    ("f16r", (1448, 1448, 4096), "BM=128 BN=128 BK=32 ST=5"),
+    ("f16r", (1448, 1448, 4096), "BM=128 BN=256 BK=32 ST=3 WM=2 WN=4 GM=8 KS=3"),
+    ("f16r", (1792, 1792, 4096), "BM=128 BN=128 BK=32 ST=5"),
+    # f16r, K = 513-2048 on a grid of 128^2 tiles that fits one round in
+    # 1024-deep slices: the 128^2 f32-panel ring (1792^2 x 1024 19.7 us
+    # against 23.8 packed, 1280^2 x 2048 23.1 against 27.7); a whole K of
+    # 2048 a tile stays packed (1792^2 x 2048 28 us against 32 on the ring)
+    ("f16r", (1792, 1792, 1024), "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3"),
+    ("f16r", (1280, 1280, 2048), "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3"),
+    ("f16r", (1792, 1792, 2048), "BM=128 BN=128 BK=32 ST=5"),
     # f16r mid sizes on the packed path (every half-depth ring timed pinned;
     # the pick within 2.3% of the fastest): 128^2 60 us at 1024 x 4096^2,
     # 100 at 2048^2 x 8192 and 194 at 4352^3 (256 x 128 70, 119 and 205),
-    # with eight waves on a grid of one round (up to 512 tiles: 1448^2 x 4096
-    # 44.6 us against 47.7 with four, 2048^3 33.2 against 34.6), four on a
-    # larger one (4352^3 193 against 195);
+    # with eight waves on a grid of one round (up to 512 tiles: 1792^3 29.7
+    # us against 30.8 with four, 2048^3 33.2 against 34.6), four on a larger
+    # one (4352^3 193 against 195);
     # 256 x 128 52 us at 2560^3, 76 at 1536 x 4096^2, 219 at 4608^3, 200 at
     # 4097^3 and 458 at 6144^3 (128^2: 55, 81, 232, 208, 465; 256^2: 68, 100,
     # 242, 220, 448); the 256^2 ring 89 us at 3072^3 (144 tiles; 256 x 128 in
     # runs 95)
     ("f16r", (1024, 4096, 4096), "BM=128 BN=128 BK=32 ST=5 WM=4 WN=2"),
     ("f16r", (2048, 2048, 8192), "BM=128 BN=128 BK=32 ST=5 WM=4 WN=2"),
-    ("f16r", (1448, 1448, 4096), "BM=128 BN=128 BK=32 ST=5 WM=4 WN=2"),
+    ("f16r", (1792, 1792, 1792), "BM=128 BN=128 BK=32 ST=5 WM=4 WN=2"),
     ("f16r", (2048, 2048, 2048), "BM=128 BN=128 BK=32 ST=5 WM=4 WN=2"),
     ("f16r", (4352, 4352, 4352), "BM=128 BN=128 BK=32 ST=5 WM=2 WN=2"),
     ("f16r", (2560, 2560, 2560), "BM=256 BN=128 BK=32 ST=4 WM=4 WN=2"),

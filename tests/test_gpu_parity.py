@@ -560,7 +560,7 @@ def test_non_default_stream(mode):
     assert_parity(mode, A, B, C, 1.0, 0.5, tC.cpu().numpy())
 
 
-@pytest.mark.parametrize("mode,M,K", [("f32", 640, 512), ("f16r", 640, 512), ("f16r", 1280, 512),
+@pytest.mark.parametrize("mode,M,K", [("f32", 640, 512), ("f16r", 640, 512), ("f16r", 1280, 3072),
                                       ("f16r", 16, 4096), ("f32", 16, 4096), ("f16r", 64, 4096),
                                       ("f32", 64, 4096)])
 def test_graph_capture_replays(mode, M, K):

@@ -32,7 +32,7 @@ from tests.gpu_helpers import say, to_device  # noqa: E402
 # (mode, M, N, K): f16r packed path (operands in scratch), f16r rounding on
 # load with K split (partials + counters), f32 few rows (partials + counters),
 # f32 split-K tiles (partials, second pass)
-CASES = [("f16r", 512, 768, 1024), ("f16r", 200, 1000, 3000), ("f32", 8, 4096, 4096),
+CASES = [("f16r", 1280, 384, 3072), ("f16r", 200, 1000, 3000), ("f32", 8, 4096, 4096),
          ("f32", 64, 2048, 4096), ("f16r", 1024, 1536, 640)]
 
 
@@ -127,7 +127,7 @@ def test_capture_without_scratch_fails_and_launches_nothing():
     """A new stream holds no scratch: capturing an f16r call on it (which
     needs its packed operands) must return GEMM355_ERR_CAPTURE (-106) and
     leave C untouched; the same call runs eagerly afterwards."""
-    M, N, K = 1280, 384, 1024   # the packed path: its binary16 operands live in scratch
+    M, N, K = 1280, 384, 3072   # the packed path: its binary16 operands live in scratch
     assert g.get_plan("f16r", M, N, K, beta=0.5).startswith("form=packed")
     A, B, C = make_inputs(M, N, K, "uniform", seed=81)
     tA, tB, tC = to_device(A), to_device(B), to_device(C)

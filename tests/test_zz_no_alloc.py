@@ -91,7 +91,7 @@ def test_noalloc_refuses_a_call_larger_than_its_array():
 
 
 @pytest.mark.parametrize("mode,M,N,K,cfg", [
-    ("f16r", 1280, 384, 512, None),           # packed operands
+    ("f16r", 1280, 384, 3072, None),          # packed operands
     ("f32", 16, 384, 4096, None),             # few rows: partials + counters
     ("f32", 2048, 2048, 1024, "BM=256 BN=256 BK=16 ST=4 WM=4 WN=2"),   # stream-K ring
 ])
