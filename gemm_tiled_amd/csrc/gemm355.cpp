@@ -518,6 +518,13 @@ TileConfig panel_ring_config(int mode, int64_t M, int64_t N, int64_t K) {
     for (; i >= 0; --i) {
         parse_config(mode, ladder[i], &c);
         const DirectGrid d = direct_grid(c, M, N, K);
+        // f16r 128 x 256 in 6 or more slices: the last workgroup of a tile
+        // adds many large partial tiles alone, so 128^2 is taken -- 1.11-1.49
+        // times faster at 7 shapes (512 x 1024 x 8192, 16 slices, 49.9 us
+        // against 33.5; 1024^2 x 4096, 8, 33.6 against 29.5; 640 x 2048 x
+        // 4096, 6, 32.5 against 28.3), 3% slower at 1024^2 x 8192; from 5
+        // slices 128^2 has too few workgroups (384 x 4096^2 35.8 against 39.8)
+        if (!f32 && c.bn == 256 && d.slices > 5) continue;
         if (fill * d.tiles_m * d.tiles_n * d.reach >= kCUs * d.per_cu) break;
     }
     return c;

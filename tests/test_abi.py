@@ -363,6 +363,11 @@ HEURISTIC_PICKS = [
     ("f16r", (1792, 1792, 1024), "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3"),
     ("f16r", (1280, 1280, 2048), "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3"),
     ("f16r", (1792, 1792, 2048), "BM=128 BN=128 BK=32 ST=5"),
+    # the f32-panel ring's 128 x 256 tile gives way to 128^2 from 6 slices
+    # (512 x 1024 x 8192: 16 slices 49.9 us, 128^2 in 8 33.5), not at 5
+    # (384 x 4096^2: 35.8 us against 39.8 on 128^2)
+    ("f16r", (512, 1024, 8192), "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3"),
+    ("f16r", (384, 4096, 4096), "BM=128 BN=256 BK=32 ST=3 WM=2 WN=4 GM=8 KS=3"),
     # f16r mid sizes on the packed path (every half-depth ring timed pinned;
     # the pick within 2.3% of the fastest): 128^2 60 us at 1024 x 4096^2,
     # 100 at 2048^2 x 8192 and 194 at 4352^3 (256 x 128 70, 119 and 205),
