@@ -320,9 +320,10 @@ RingSk ring_sk(const TileConfig& c, int64_t M, int64_t N, int64_t K) {
 // 128 x 256 with eight 0.93, 128^2 (two workgroups per CU) with four 0.86
 // and with eight 0.87 on a grid of at most one round (512 tiles), 0.85 on a
 // larger one (eight waves 0.6-7% faster at 9 of 10 shapes of 100-256 tiles,
-// the tenth even, 0.4-1.3% slower at 4 of 5 of 676-3025).  Others by their reuse r = BM BN /
-// (BM + BN) as r / (r + 85) against the 256^2 tile's, the full-depth panels at
-// 1 / 1.2 of that (the half-depth ring at a tile ran 1.1-1.4 times faster).
+// the tenth even, 0.4-1.3% slower at 4 of 5 of 676-3025).  Others by their
+// reuse r = BM BN / (BM + BN) as r / (r + 85) against the 256^2 tile's, the
+// full-depth panels at 1 / 1.2 of that (the half-depth ring at a tile ran
+// 1.1-1.4 times faster).
 double f16_efficiency(const TileConfig& c, double tiles) {
     const int waves = c.wm * c.wn;
     if (is_f16_ring(c)) {
@@ -588,8 +589,8 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
     // the ring splits over workgroups -- K >= 4096 with M N <= 2^21 and
     // min(M, N) <= 1280, or M, N <= 1536: 1024 x 2048 x 4096 39 us against
     // 56, 1280^2 x 4096 36 against 45, 1448^2 x 4096 43 against 46, 1536^2 x
-    // 4096 42 against 44; not 1792^2 x 4096, 54 against 46 on the packed
-    // path, nor 768 x 4096^2, 60 against 52, and even at 1800 x 1280 x 4096
+    // 4096 42 against 44; not 1792^2 x 4096 (54 against 46 on the packed
+    // path), 768 x 4096^2 (60 against 52) or 1800 x 1280 x 4096 (even)
     // -- or where K is so shallow that the packing pass dominates -- K <= 512
     // with M, N <= 2048: 2048^2 x 512 12.8 us against 18.8, 2048^2 x 256 8.5
     // against 15.2)
