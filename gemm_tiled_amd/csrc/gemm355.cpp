@@ -615,6 +615,18 @@ TileConfig heuristic(int mode, int64_t M, int64_t N, int64_t K, RingRows rows) {
         parse_config(mode, "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3", &c);
         return c;
     }
+    // (and at K = 513-1024 the 256 x 128 or 128 x 256 tile, its long side
+    // along the longer of M and N, where that grid fits one round: 1.05-1.33
+    // times the packed path's speed at 18 shapes, 2304^2 x 1024 28.0 us
+    // against 29.3, 8192 x 1024^2 28.5 against 32.4, 2560^2 x 640 19.3
+    // against 25.7; 3072^2 x 1024, 288 tiles, stays packed: 37 us against 50)
+    if (panels && mode == GEMM355_MODE_F16R && K > 512 && K <= 1024 &&
+        ((std::max(M, N) + 255) / 256) * ((std::min(M, N) + 127) / 128) <= kCUs) {
+        TileConfig c{};
+        parse_config(mode, M >= N ? "BM=256 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3"
+                                  : "BM=128 BN=256 BK=32 ST=3 WM=2 WN=4 GM=8 KS=3", &c);
+        return c;
+    }
     if (panels && mode == GEMM355_MODE_F32 &&
         (M <= kPanelRowsF32 || (M <= 4 * kPanelRowsF32 && N * K <= (int64_t{1} << 21))))
         return panel_ring_config(mode, M, N, K);

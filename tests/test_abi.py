@@ -363,6 +363,13 @@ HEURISTIC_PICKS = [
     ("f16r", (1792, 1792, 1024), "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3"),
     ("f16r", (1280, 1280, 2048), "BM=128 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3"),
     ("f16r", (1792, 1792, 2048), "BM=128 BN=128 BK=32 ST=5"),
+    # K <= 1024 past one round of 128^2 tiles: the 256 x 128 ring, its long
+    # side along the longer of M and N, while that grid fits one round
+    # (2560^2 x 1024 29.0 us against 30.9 packed, 2048 x 4096 x 1024 29.9
+    # against 32.1); 3072^2 x 1024 (288 tiles) stays packed (37 us against 50)
+    ("f16r", (2560, 2560, 1024), "BM=256 BN=128 BK=32 ST=3 WM=4 WN=2 GM=8 KS=3"),
+    ("f16r", (2048, 4096, 1024), "BM=128 BN=256 BK=32 ST=3 WM=2 WN=4 GM=8 KS=3"),
+    ("f16r", (3072, 3072, 1024), "BM=128 BN=128 BK=32 ST=5"),
     # the f32-panel ring's 128 x 256 tile gives way to 128^2 from 6 slices
     # (512 x 1024 x 8192: 16 slices 49.9 us, 128^2 in 8 33.5), not at 5
     # (384 x 4096^2: 35.8 us against 39.8 on 128^2)
